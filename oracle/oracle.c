@@ -1,0 +1,299 @@
+/*
+ * oracle.c -- CPU oracle for block-quantized decode GEMV.
+ *
+ * TEST INFRASTRUCTURE ONLY (see oracle.h).  Plain C, one weight at a time,
+ * fp64 accumulation.  Parity pins for every function live in
+ * tests/test_oracle_pins.py.
+ *
+ * What the pages fix, and what is a reading:
+ *  - larql "Architecture -> Metal shader map", dispatch predicate table: the
+ *    Q4_K weights larql reads directly from llama.cpp-saved GGUF files use
+ *    the 144-byte block.  Its Gemma 3 table runs Q4_K (Q, K, O, gate, up,
+ *    lm_head) and Q6_K (V, down) under the ollama Q4_K_M convention.
+ *  - dotLLM PR #320, commit on the Q8_0 GEMV row-stride fix: a Q8_0 block is
+ *    34 bytes (blocksPerRow * 34) and rows are packed without padding; the
+ *    commit on CPU Q8_0 kernels gives the 32-element block.
+ *  - The field lists and value formulas (w = d*sc*q - dmin*m for Q4_K,
+ *    w = d*scale*(q-32) for Q6_K, w = d*q for Q8_0) come with the workload
+ *    definitions this library is measured on.
+ *  - Reading: no page prints the bit placement inside a block.  The layout
+ *    below is the GGUF k-quant layout the larql page names, restated field by
+ *    field; little-endian throughout.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stddef.h>
+#include <stdlib.h>
+#include <string.h>
+
+int orc_block_elems(int fmt) {
+    switch (fmt) {
+    case ORC_Q4_K: return 256;
+    case ORC_Q6_K: return 256;
+    case ORC_Q8_0: return 32;
+    default: return 0;
+    }
+}
+
+int orc_block_bytes(int fmt) {
+    switch (fmt) {
+    case ORC_Q4_K: return 144;
+    case ORC_Q6_K: return 210;
+    case ORC_Q8_0: return 34;
+    default: return 0;
+    }
+}
+
+int64_t orc_row_bytes(int fmt, int64_t K) {
+    int qk = orc_block_elems(fmt);
+    if (qk == 0 || K <= 0 || K % qk != 0) return 0;
+    return (K / qk) * (int64_t)orc_block_bytes(fmt);
+}
+
+static uint16_t rd_u16(const uint8_t *p) {
+    return (uint16_t)(p[0] | (p[1] << 8));
+}
+
+/* binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+ * exponent 0 -> subnormal, value = fraction * 2^-24;
+ * exponent 31 -> infinity (fraction 0) or NaN;
+ * otherwise value = (1024 + fraction) * 2^(exponent - 25). */
+float orc_f16_to_f32(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 31;
+    int f = h & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + f), e - 25);
+    return (float)(sign ? -v : v);
+}
+
+/* bfloat16 keeps the top 16 bits of the fp32 encoding.  Round to nearest,
+ * ties to even, done on the value: find the two neighbouring bfloat16 values
+ * and pick the nearer one. */
+uint16_t orc_f32_to_bf16(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if (isnan(f)) return (uint16_t)((u >> 16) | 0x0040); /* quiet NaN */
+    if (isinf(f)) return (uint16_t)(u >> 16);
+    uint32_t lo = u & 0xFFFF0000u;             /* truncation toward zero */
+    uint32_t hi = lo + 0x00010000u;            /* next value away from zero */
+    float flo, fhi;
+    memcpy(&flo, &lo, 4);
+    memcpy(&fhi, &hi, 4);
+    double vlo = (double)flo;
+    /* past the largest finite bf16 the next value is 2^128, i.e. overflow to
+     * infinity; the distance is taken to 2^128 as IEEE rounding does */
+    double vhi = isinf(fhi) ? copysign(ldexp(1.0, 128), (double)f) : (double)fhi;
+    double dlo = fabs((double)f - vlo);
+    double dhi = fabs(vhi - (double)f);
+    if (dlo < dhi) return (uint16_t)(lo >> 16);
+    if (dhi < dlo) return (uint16_t)(hi >> 16);
+    /* exact tie: the even one (low bit of the bf16 fraction clear) */
+    return (uint16_t)((((lo >> 16) & 1) == 0) ? (lo >> 16) : (hi >> 16));
+}
+
+float orc_bf16_to_f32(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* ---------------------------------------------------------------- Q4_K ---
+ * 144 bytes:  [0,2) d (f16)   [2,4) dmin (f16)
+ *             [4,16) s[0..11]: eight 6-bit scales and eight 6-bit mins
+ *             [16,144) qs[0..127]: 256 four-bit quants
+ * Sub-block j (0..7) covers weights 32j..32j+31.
+ *  j < 4: scale = low 6 bits of s[j], min = low 6 bits of s[j+4].
+ *  j >= 4: scale = low nibble of s[j+4], with the top 2 bits of s[j-4] as
+ *          bits 4..5; min = high nibble of s[j+4], with the top 2 bits of
+ *          s[j] as bits 4..5.
+ * Quants: the 128 bytes form four runs of 32; run c holds weights
+ * 64c..64c+31 in its low nibbles and 64c+32..64c+63 in its high nibbles.
+ * Weight i = d*scale_j*q_i - dmin*min_j with j = i/32. */
+void orc_q4k_scale_min(const uint8_t *blk, int j, int *sc, int *m) {
+    const uint8_t *s = blk + 4;
+    if (j < 4) {
+        *sc = s[j] & 63;
+        *m = s[j + 4] & 63;
+    } else {
+        *sc = (s[j + 4] & 15) | ((s[j - 4] >> 6) << 4);
+        *m = (s[j + 4] >> 4) | ((s[j] >> 6) << 4);
+    }
+}
+
+void orc_dequant_q4k_block(const uint8_t *blk, float *w) {
+    double d = orc_f16_to_f32(rd_u16(blk));
+    double dmin = orc_f16_to_f32(rd_u16(blk + 2));
+    const uint8_t *qs = blk + 16;
+    for (int i = 0; i < 256; i++) {
+        int j = i / 32;
+        int run = i / 64;
+        int pos = i % 64;
+        uint8_t byte = qs[32 * run + pos % 32];
+        int q = (pos < 32) ? (byte & 15) : (byte >> 4);
+        int sc, m;
+        orc_q4k_scale_min(blk, j, &sc, &m);
+        /* d*sc*q has at most 11+6+4 significant bits and dmin*m at most
+         * 11+6, so both products are exact in fp64; the difference is exact
+         * unless the exponents are more than 32 apart, and then the larger
+         * term (exact in fp32) is the correctly rounded result either way.
+         * The cast to float is therefore the single correct rounding of the
+         * real value d*sc*q - dmin*m. */
+        w[i] = (float)(d * sc * q - dmin * m);
+    }
+}
+
+/* ---------------------------------------------------------------- Q6_K ---
+ * 210 bytes:  [0,128) ql: low 4 bits of each quant
+ *             [128,192) qh: high 2 bits of each quant
+ *             [192,208) sc[0..15]: int8 scales, one per 16 weights
+ *             [208,210) d (f16)
+ * The block is two halves of 128 weights.  In half h, weight
+ * 128h + 32g + l (g = 0..3, l = 0..31) takes
+ *   low 4 bits:  byte ql[64h + 32*(g%2) + l], low nibble for g < 2,
+ *                high nibble for g >= 2;
+ *   high 2 bits: bits 2g..2g+1 of byte qh[32h + l].
+ * q = low | high << 4 (0..63); weight i = d * sc[i/16] * (q - 32). */
+void orc_dequant_q6k_block(const uint8_t *blk, float *w) {
+    const uint8_t *ql = blk;
+    const uint8_t *qh = blk + 128;
+    const int8_t *sc = (const int8_t *)(blk + 192);
+    double d = orc_f16_to_f32(rd_u16(blk + 208));
+    for (int i = 0; i < 256; i++) {
+        int h = i / 128;
+        int g = (i % 128) / 32;
+        int l = i % 32;
+        uint8_t lbyte = ql[64 * h + 32 * (g % 2) + l];
+        int lo = (g < 2) ? (lbyte & 15) : (lbyte >> 4);
+        int hi = (qh[32 * h + l] >> (2 * g)) & 3;
+        int q = lo | (hi << 4);
+        /* 11 + 7 + 6 significant bits: exact in fp32 */
+        w[i] = (float)(d * sc[i / 16] * (q - 32));
+    }
+}
+
+/* ---------------------------------------------------------------- Q8_0 ---
+ * 34 bytes:  [0,2) d (f16)   [2,34) q[0..31] (int8)
+ * weight i = d * q_i. */
+void orc_dequant_q8_0_block(const uint8_t *blk, float *w) {
+    double d = orc_f16_to_f32(rd_u16(blk));
+    const int8_t *q = (const int8_t *)(blk + 2);
+    for (int i = 0; i < 32; i++) w[i] = (float)(d * q[i]);
+}
+
+static void dequant_block(int fmt, const uint8_t *blk, float *w) {
+    if (fmt == ORC_Q4_K) orc_dequant_q4k_block(blk, w);
+    else if (fmt == ORC_Q6_K) orc_dequant_q6k_block(blk, w);
+    else orc_dequant_q8_0_block(blk, w);
+}
+
+int orc_dequant_rows(int fmt, const uint8_t *W, int64_t K, int64_t n0,
+                     int64_t n1, float *out) {
+    int64_t rb = orc_row_bytes(fmt, K);
+    if (rb == 0 || n0 < 0 || n1 < n0) return -1;
+    int qk = orc_block_elems(fmt), bb = orc_block_bytes(fmt);
+    for (int64_t n = n0; n < n1; n++)
+        for (int64_t b = 0; b < K / qk; b++)
+            dequant_block(fmt, W + n * rb + b * bb, out + (n - n0) * K + b * qk);
+    return 0;
+}
+
+/* ----------------------------------------------------------------- GEMV ---
+ * The product every projection on the decode path computes: the larql
+ * Gemma 3 table's q4k_matvec (lm_head), q4k_matvec_8sg (O), q6k_matvec
+ * (down); dotLLM's matmul_q8_0 ("direct quantized GEMV against Q8_0-packed
+ * weights").  Written as the definition: decode row n, then sum w*x. */
+int orc_gemv(int fmt, const uint8_t *W, const float *x, int64_t N, int64_t K,
+             int batch, int64_t n0, int64_t n1, double *y64, double *S) {
+    int64_t rb = orc_row_bytes(fmt, K);
+    if (rb == 0 || batch < 1 || n0 < 0 || n1 < n0 || n1 > N) return -1;
+    float *w = (float *)malloc(sizeof(float) * (size_t)K);
+    if (!w) return -1;
+    for (int64_t n = n0; n < n1; n++) {
+        orc_dequant_rows(fmt, W, K, n, n + 1, w);
+        for (int b = 0; b < batch; b++) {
+            double acc = 0.0, acc_abs = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                double p = (double)w[k] * (double)x[(int64_t)b * K + k];
+                acc += p;
+                acc_abs += fabs(p);
+            }
+            if (y64) y64[(int64_t)b * N + n] = acc;
+            if (S) S[(int64_t)b * N + n] = acc_abs;
+        }
+    }
+    free(w);
+    return 0;
+}
+
+/* ------------------------------------------------------------- RMS-norm ---
+ * larql Gemma 3 table, "Input RMS-norm": standard RMS-norm with the weight
+ * offset baked into the stored weight, so the weight multiplies directly.
+ * x / sqrt(mean(x^2) + eps) * w, eps inside the square root. */
+void orc_rmsnorm(const float *x, const float *w, int64_t K, int batch,
+                 double eps, double *out) {
+    for (int b = 0; b < batch; b++) {
+        const float *xb = x + (int64_t)b * K;
+        double ss = 0.0;
+        for (int64_t k = 0; k < K; k++) ss += (double)xb[k] * (double)xb[k];
+        double inv = 1.0 / sqrt(ss / (double)K + eps);
+        for (int64_t k = 0; k < K; k++)
+            out[(int64_t)b * K + k] = (double)xb[k] * inv * (double)w[k];
+    }
+}
+
+/* ---------------------------------------------------------- Activations ---
+ * larql Gemma 3 table, "GEGLU activation": the GELU-tanh variant applied to
+ * gate, times up.  GELU with the tanh approximation (Hendrycks & Gimpel):
+ *   0.5 g (1 + tanh( sqrt(2/pi) (g + 0.044715 g^3) )).
+ * larql Llama table and the gerbil guide's SwiGLU MLP: SiLU on gate, times
+ * up.  SiLU(g) = g / (1 + exp(-g)). */
+double orc_gelu_tanh(double g) {
+    const double pi = 3.14159265358979323846;
+    const double k = sqrt(2.0 / pi);
+    return 0.5 * g * (1.0 + tanh(k * (g + 0.044715 * g * g * g)));
+}
+
+double orc_silu(double g) { return g / (1.0 + exp(-g)); }
+
+double orc_act(int act, double g) {
+    return act == ORC_ACT_SILU ? orc_silu(g) : orc_gelu_tanh(g);
+}
+
+/* -------------------------------------------------------- Prefill GEMM ---
+ * Multi-token prefill against quantized weights (dotLLM's tiled Q8_0 GEMM
+ * for prefill is the pages' instance).  Here the operands are bfloat16:
+ * each fp32 dequantised weight rounded to bf16, the activations given as
+ * bf16; products summed in fp64. */
+int orc_gemm_bf16(int fmt, const uint8_t *W, const uint16_t *X, int64_t M,
+                  int64_t N, int64_t K, int64_t m0, int64_t m1, int64_t n0,
+                  int64_t n1, double *Y64, double *S) {
+    int64_t rb = orc_row_bytes(fmt, K);
+    if (rb == 0 || m0 < 0 || m1 < m0 || m1 > M || n0 < 0 || n1 < n0 || n1 > N)
+        return -1;
+    float *w = (float *)malloc(sizeof(float) * (size_t)K);
+    if (!w) return -1;
+    for (int64_t n = n0; n < n1; n++) {
+        orc_dequant_rows(fmt, W, K, n, n + 1, w);
+        for (int64_t k = 0; k < K; k++) w[k] = orc_bf16_to_f32(orc_f32_to_bf16(w[k]));
+        for (int64_t m = m0; m < m1; m++) {
+            double acc = 0.0, acc_abs = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                double p = (double)w[k] * (double)orc_bf16_to_f32(X[m * K + k]);
+                acc += p;
+                acc_abs += fabs(p);
+            }
+            if (Y64) Y64[m * N + n] = acc;
+            if (S) S[m * N + n] = acc_abs;
+        }
+    }
+    free(w);
+    return 0;
+}
