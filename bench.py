@@ -1,0 +1,296 @@
+#!/usr/bin/env python3
+"""Benchmark: batch-1 k-quant decode FFN at Gemma-3-4B shape on one MI355X.
+
+One step = one pass of the decode hot path over one token:
+  qffn_gate_up_act   RMS-norm(x) -> gate/up GEMV (Q4_K, 10240 x 2560 each)
+                     -> GELU-tanh(gate) * up = h
+  qgemv_q6k          down GEMV (Q6_K, 2560 x 10240) on h
+Weights are seeded synthetic tensors with the workload's field distributions
+(no checkpoint is available); they rotate through enough distinct copies
+(>= 1 GiB) that neither the L2 nor the 256 MB Infinity Cache serves them.
+Inputs are resident in HBM before the timed region.
+
+Prints ONE JSON line on stdout.  `value` is weight GB/s of the whole step;
+`roofline` is for the dominant kernel (fused gate/up), timed with HIP events
+on the stream it runs on; `cpu_baseline` is the C oracle on the host cores.
+Other workloads (--workload) are for profiling and sweeps.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "batch-1 k-quant GEMV µs and weight GB/s (% of HBM peak), Gemma-3-4B FFN"
+ROTATE_BYTES = 1 << 30
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="gemma3_ffn",
+                   choices=["gemma3_ffn", "gemma4_ffn", "gemma4_ffn_b8", "lm_head_q4k",
+                            "lm_head_q8_0", "down_q6k", "gate_up_q4k", "copy"])
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="approximate CPU time budget of the oracle baseline (0 = skip)")
+    p.add_argument("--seed", type=int, default=0x5EED)
+    p.add_argument("--override", default="",
+                   help="p_in,p_out,nr launch-shape override (tuning only)")
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantized_decode_q4k_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel_key: str, alg_bytes: float):
+    """HBM bytes per launch from the committed PMC summary, if it was taken
+    on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    try:
+        d = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    e = d.get(kernel_key)
+    if not e or e.get("source_hash") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+class Workload:
+    """Weights (rotating copies), activations and the per-step launches."""
+
+    def __init__(self, name, seed, dev):
+        import torch
+        import synth
+        import quantized_decode_q4k_amd as qd
+        self.qd, self.torch, self.name = qd, torch, name
+        t = lambda a: torch.from_numpy(a).to(dev)
+        self.batch = 1
+        if name in ("gemma3_ffn", "gemma4_ffn", "gemma4_ffn_b8", "gate_up_q4k", "down_q6k"):
+            hidden, ff = (2560, 10240) if name in ("gemma3_ffn", "gate_up_q4k", "down_q6k") else (5376, 21504)
+            self.batch = 8 if name == "gemma4_ffn_b8" else 1
+            self.hidden, self.ff = hidden, ff
+            mats = {}
+            if name != "down_q6k":
+                mats["gate"] = synth.quant_weights("q4_k", ff, hidden, seed, tensor_id=41)
+                mats["up"] = synth.quant_weights("q4_k", ff, hidden, seed, tensor_id=42)
+            if name != "gate_up_q4k":
+                mats["down"] = synth.quant_weights("q6_k", hidden, ff, seed, tensor_id=45)
+            self.weight_bytes = sum(m.size for m in mats.values())
+            x = synth.normal((self.batch, hidden), seed, tensor_id=43)
+            nw = synth.normal((hidden,), seed, tensor_id=44, mean=1.0, std=0.1)
+            self.x = t(x)
+            self.nw = t(nw)
+            self.h = torch.empty((self.batch, ff), device=dev)
+            self.hin = t(synth.normal((self.batch, ff), seed, tensor_id=46))
+            self.y = torch.empty((self.batch, hidden), device=dev)
+            base = {k: t(v) for k, v in mats.items()}
+        elif name in ("lm_head_q4k", "lm_head_q8_0"):
+            fmt = "q4_k" if name == "lm_head_q4k" else "q8_0"
+            self.fmt = fmt
+            W = synth.quant_weights(fmt, 262144, 2560, seed, tensor_id=10)
+            self.weight_bytes = W.size
+            self.x = t(synth.normal((1, 2560), seed, tensor_id=5))
+            self.y = torch.empty((1, 262144), device=dev)
+            base = {"W": t(W)}
+        else:  # copy: plain device copy of 512 MiB, to calibrate counters
+            self.weight_bytes = 512 << 20
+            base = {"src": torch.empty(self.weight_bytes // 4, device=dev).fill_(1.0)}
+            self.dst = torch.empty_like(base["src"])
+        ncopy = max(2, math.ceil(ROTATE_BYTES / max(1, self.weight_bytes))) if name != "copy" else 1
+        self.copies = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(ncopy - 1)]
+        self.ncopy = ncopy
+        self.i = 0
+
+    def alg_bytes(self):
+        """(dominant kernel name, algorithmic bytes per launch of it)."""
+        b, n = self.batch, self.name
+        if n in ("gemma3_ffn", "gemma4_ffn", "gemma4_ffn_b8", "gate_up_q4k"):
+            w = 2 * self.ff * (self.hidden // 256) * 144
+            return "qffn_gate_up_act", w + 4 * (b * self.hidden + self.hidden + b * self.ff)
+        if n == "down_q6k":
+            return "qgemv_q6k", self.hidden * (self.ff // 256) * 210 + 4 * b * (self.ff + self.hidden)
+        if n.startswith("lm_head"):
+            return "qgemv", self.weight_bytes + 4 * (2560 + 262144)
+        return "copy", 2 * self.weight_bytes
+
+    def step(self, ev=None):
+        c = self.copies[self.i]
+        self.i = (self.i + 1) % self.ncopy
+        qd, n = self.qd, self.name
+        if n in ("gemma3_ffn", "gemma4_ffn", "gemma4_ffn_b8", "gate_up_q4k"):
+            if ev:
+                ev[0].record()
+            qd.qffn_gate_up_act("q4_k", c["gate"], c["up"], self.x, self.nw, 1e-6, "gelu_tanh", h=self.h)
+            if ev:
+                ev[1].record()
+            if n != "gate_up_q4k":
+                qd.qgemv_q6k(c["down"], self.h, self.y)
+        elif n == "down_q6k":
+            if ev:
+                ev[0].record()
+            qd.qgemv_q6k(c["down"], self.hin, self.y)
+            if ev:
+                ev[1].record()
+        elif n.startswith("lm_head"):
+            if ev:
+                ev[0].record()
+            qd.qgemv(self.fmt, c["W"], self.x, self.y)
+            if ev:
+                ev[1].record()
+        else:
+            if ev:
+                ev[0].record()
+            self.dst.copy_(c["src"])
+            if ev:
+                ev[1].record()
+
+
+def cpu_baseline(seed, budget_s):
+    """The C oracle on one FFN step of the same workload, rows split over the
+    host cores; repeated whole steps until about budget_s seconds."""
+    import numpy as np
+    import oracle
+    import synth
+    hidden, ff = 2560, 10240
+    Wg = synth.quant_weights("q4_k", ff, hidden, seed, tensor_id=41)
+    Wu = synth.quant_weights("q4_k", ff, hidden, seed, tensor_id=42)
+    Wd = synth.quant_weights("q6_k", hidden, ff, seed, tensor_id=45)
+    x = synth.normal((1, hidden), seed, tensor_id=43)
+    nw = synth.normal((hidden,), seed, tensor_id=44, mean=1.0, std=0.1)
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    threads = max(1, min(16, cores))
+    wbytes = Wg.size + Wu.size + Wd.size
+
+    def one():
+        xn = oracle.rmsnorm(x, nw, 1e-6).astype(np.float32)
+        g, _ = oracle.gemv_threaded("q4_k", Wg, xn, ff, hidden, threads)
+        u, _ = oracle.gemv_threaded("q4_k", Wu, xn, ff, hidden, threads)
+        h = (oracle.act_vec(oracle.ACT_GELU_TANH, g) * u).astype(np.float32)
+        oracle.gemv_threaded("q6_k", Wd, h, hidden, ff, threads)
+
+    t0 = time.perf_counter()
+    one()
+    first = time.perf_counter() - t0
+    reps = max(1, int(budget_s / max(first, 1e-3)) - 1)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        one()
+    dt = (time.perf_counter() - t0) / reps
+    return {"value": round(wbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "ms_per_step": round(dt * 1e3, 3),
+            "sample": f"{reps} full FFN steps (all 10240+10240+2560 rows, RMS-norm, GELU-tanh) after "
+                      f"1 untimed; rows split over {threads} host threads; fp64 accumulation"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this library has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import quantized_decode_q4k_amd as qd
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    qd.lib()
+    if args.override:
+        p_in, p_out, nr = (int(v) for v in args.override.split(","))
+        qd.set_launch_override(p_in, p_out, nr)
+
+    log(f"[bench] workload={args.workload} steps={args.steps} warmup={args.warmup}")
+    wl = Workload(args.workload, args.seed, dev)
+    log(f"[bench] weight bytes/step={wl.weight_bytes} rotating copies={wl.ncopy}")
+    for _ in range(args.warmup):
+        wl.step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(K):
+        wl.step(evs[s])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / K
+    kern_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    kern_avg = sum(kern_ms) / K
+    kname, alg = wl.alg_bytes()
+    achieved = alg / (kern_avg * 1e-3) / 1e9
+    log(f"[bench] step {ms_per_step * 1e3:.2f} us; {kname} avg {kern_avg * 1e3:.2f} us "
+        f"(median {kern_ms[K // 2] * 1e3:.2f}, min {kern_ms[0] * 1e3:.2f}) -> {achieved:.0f} GB/s")
+
+    value = wl.weight_bytes / (ms_per_step * 1e-3) / 1e9
+    out = {
+        "metric": METRIC if args.workload == "gemma3_ffn" else f"weight GB/s, {args.workload}",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": {
+                "gemma3_ffn": "Gemma-3-4B FFN decode step, batch 1: RMS-norm + fused gate/up Q4_K "
+                              "10240x2560 + GELU-tanh, then down Q6_K 2560x10240",
+            }.get(args.workload, args.workload),
+            "batch": wl.batch,
+            "weight_bytes_per_step": wl.weight_bytes,
+            "us_per_step": round(ms_per_step * 1e3, 3),
+            "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+            "rotating_weight_copies": wl.ncopy,
+            "seed": args.seed,
+        },
+        "roofline": {
+            "kernel": kname,
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_from_profiles(f"{args.workload}:{kname}", alg),
+            "alg_bytes_per_launch": alg,
+            "avg_launch_us": round(kern_avg * 1e3, 3),
+        },
+        "context": "pages' figure: ~1670 ms/token CPU-fallback decode of Gemma-4-E2B (larql); not a target",
+    }
+    if args.cpu_seconds > 0 and args.workload == "gemma3_ffn":
+        log("[bench] cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(args.seed, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,206 @@
+/*
+ * qdecode.h -- block-quantized matrix-vector products for transformer decode
+ * on AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * What is computed.  Every projection of a decoder layer in the engines the
+ * source pages describe streams a block-quantized weight matrix against an
+ * fp32 activation vector:
+ *   - larql "Architecture -> Metal shader map", Gemma 3 table: Q4_K for the
+ *     Q/K projections, O (q4k_matvec_8sg), FFN gate+up (q4k_ffn_gate_up_8sg,
+ *     followed by the GELU-tanh geglu) and lm_head (q4k_matvec); Q6_K for V
+ *     and FFN down (q6k_matvec).  Llama table: the same gate+up kernel with
+ *     SiLU instead of GELU-tanh.
+ *   - dotLLM PR #320: a direct Q8_0 GEMV (matmul_q8_0) and a tiled Q8_0 GEMM
+ *     for multi-token prefill.
+ * The kernel is chosen by the weight format (larql's "How dispatch happens
+ * today": format predicates, no per-architecture tables); here each format
+ * has its own entry point.
+ *
+ * Block formats (values / bytes per block):
+ *   Q4_K  256 / 144: f16 d, f16 dmin, 12 bytes of packed 6-bit scales and
+ *                    mins for 8 sub-blocks of 32, 128 bytes of 4-bit quants;
+ *                    w = d*scale*q - dmin*min.
+ *   Q6_K  256 / 210: 128 bytes low 4 bits, 64 bytes high 2 bits, 16 int8
+ *                    scales (one per 16 weights), f16 d; w = d*scale*(q-32).
+ *   Q8_0   32 /  34: f16 d, 32 int8 quants; w = d*q.
+ * Bit placement inside a block follows the GGUF k-quant layout that the larql
+ * page's dispatch table names for its 144-byte GGUF-direct Q4_K extracts.
+ *
+ * Matrix layout.  A weight matrix of N rows and K columns is N rows stored
+ * one after another; row n holds K/QK consecutive blocks and starts at byte
+ * n * qd_row_bytes(fmt, K).  There is no padding between rows (dotLLM PR
+ * #320, the Q8_0 GEMV row-stride fix: the stride is blocksPerRow * 34).
+ *
+ * Conventions for every call below.
+ *   - All array pointers are DEVICE pointers, owned by the caller, and must
+ *     stay valid until the work enqueued on `stream` has finished.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work and returns; nothing is synchronised.  Results are ready
+ *     when the stream has completed.
+ *   - Outputs are overwritten, never accumulated into.  Inputs are read-only.
+ *   - Arguments are checked on the host before anything is enqueued; a bad
+ *     argument returns an error code and enqueues nothing.  Launch failures
+ *     return QD_ELAUNCH.  A device fault surfaces at the caller's next
+ *     synchronisation of the stream.
+ *   - Shapes: N, M >= 1; batch in 1..QD_MAX_BATCH; K a positive multiple of
+ *     256 for Q4_K and Q6_K, of 32 for Q8_0 (dotLLM's CPU Q8_0 kernels reject
+ *     lengths that are not a multiple of the 32-element block).
+ *   - Alignment: weight pointers 16-byte aligned; fp32 and bf16 activation
+ *     pointers 16-byte aligned; output pointers 4-byte aligned.
+ *   - Outputs must not overlap inputs.
+ *   - Threads: calls may be made from any host thread.  Split-K launches use
+ *     a small per-(device, stream) workspace allocated on first use; calls on
+ *     the same stream are ordered by the stream, so they never share it
+ *     concurrently.
+ */
+#ifndef QDECODE_H
+#define QDECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qd_status {
+    QD_OK = 0,
+    QD_EINVAL = 1,       /* null pointer, unknown enum, aliasing outputs */
+    QD_ESHAPE = 2,       /* N, M, K or batch out of range */
+    QD_EALIGN = 3,       /* pointer not aligned as required */
+    QD_ELAUNCH = 4,      /* the HIP runtime refused the launch */
+    QD_EUNSUPPORTED = 5, /* valid arguments this build does not handle */
+    QD_ENOMEM = 6        /* workspace allocation failed */
+} qd_status;
+
+typedef enum qd_format { QD_Q4_K = 0, QD_Q6_K = 1, QD_Q8_0 = 2 } qd_format;
+
+/* FFN gate activation.  larql Gemma 3 table, "GEGLU activation": GELU with
+ * the tanh approximation applied to gate, times up; larql Llama table and
+ * the gerbil architecture guide's SwiGLU MLP: SiLU(gate) times up. */
+typedef enum qd_act { QD_ACT_GELU_TANH = 0, QD_ACT_SILU = 1 } qd_act;
+
+#define QD_MAX_BATCH 8
+
+/* Weights per block (256, 256, 32) and bytes per block (144, 210, 34);
+ * 0 for an unknown format. */
+int qd_block_elems(qd_format fmt);
+int qd_block_bytes(qd_format fmt);
+
+/* Bytes in one row of K weights, or 0 if K is not a positive multiple of the
+ * block size. */
+int64_t qd_row_bytes(qd_format fmt, int64_t K);
+
+/* Static description of a status code (never NULL). */
+const char *qd_status_str(qd_status status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int qd_version(void);
+
+/*
+ * y = W x  (batch-1 to batch-8 GEMV with in-register dequantisation)
+ *
+ * The decode-path projection: larql's q4k_matvec / q4k_matvec_8sg (Q4_K:
+ * Q, K, O, lm_head), q6k_matvec (Q6_K: V, down); dotLLM's matmul_q8_0 (Q8_0).
+ *
+ *   W      N x K quantized matrix in `fmt` blocks (layout above)
+ *   x      fp32 [batch][K], row-major
+ *   y      fp32 [batch][N], row-major; y[b][n] = sum_k w[n][k] * x[b][k]
+ *
+ * Accuracy: |y - y_exact| <= 1e-4 * sum_k |w[n][k] x[b][k]| + 1e-6, where w
+ * is the exactly dequantised weight.  For Q4_K the kernel applies the scale
+ * and the min per 32-weight sub-block (sum of q*x and sum of x); the bound
+ * holds whenever the two terms do not cancel to a row whose every weight is
+ * zero while scale and min are not.
+ */
+qd_status qgemv_q4k(const void *W, const float *x, float *y, int64_t N,
+                    int64_t K, int batch, void *stream);
+qd_status qgemv_q6k(const void *W, const float *x, float *y, int64_t N,
+                    int64_t K, int batch, void *stream);
+qd_status qgemv_q8_0(const void *W, const float *x, float *y, int64_t N,
+                     int64_t K, int batch, void *stream);
+
+/* Same as the three above with the format as an argument. */
+qd_status qgemv(qd_format fmt, const void *W, const float *x, float *y,
+                int64_t N, int64_t K, int batch, void *stream);
+
+/*
+ * h = act(Wg xn) * (Wu xn),  xn = RMSNorm(x) if norm_w != NULL else x
+ *
+ * The fused FFN gate+up of larql's q4k_ffn_gate_up_8sg with the geglu
+ * element-wise step folded into its epilogue, and the input RMS-norm of the
+ * larql Gemma 3 table folded into the staging of x.
+ *
+ *   fmt     format of both Wg and Wu (Q4_K in the Gemma FFN)
+ *   Wg, Wu  N_ff x K quantized matrices (gate, up)
+ *   x       fp32 [batch][K]
+ *   norm_w  fp32 [K] RMS-norm weight, or NULL for no norm.  The norm is
+ *           xn = x * norm_w / sqrt(mean(x^2) + eps): the weight multiplies
+ *           directly (larql: "weight offset baked into stored weight").
+ *   eps     added to mean(x^2) inside the square root (ignored without norm)
+ *   act     QD_ACT_GELU_TANH: 0.5 g (1 + tanh(sqrt(2/pi)(g + 0.044715 g^3)))
+ *           QD_ACT_SILU:      g / (1 + exp(-g))
+ *   h       fp32 [batch][N_ff]
+ *   g_out, u_out  optional fp32 [batch][N_ff] copies of the gate and up
+ *           projections (NULL = not written)
+ * Accuracy: g and u each meet the GEMV bound; h = act(g) * u evaluated in
+ * fp32 from them.
+ */
+qd_status qffn_gate_up_act(qd_format fmt, const void *Wg, const void *Wu,
+                           const float *x, const float *norm_w, float eps,
+                           qd_act act, float *h, float *g_out, float *u_out,
+                           int64_t N_ff, int64_t K, int batch, void *stream);
+
+/*
+ * Y = X W^T for a multi-token prefill (dequantise to bf16, MFMA, fp32
+ * accumulate).  dotLLM PR #320's tiled Q8_0 GEMM for prefill is the pages'
+ * instance; here any of the three formats.
+ *
+ *   W   N x K quantized matrix
+ *   X   bf16 bits [M][K], row-major
+ *   Y   fp32 [M][N], row-major; Y[m][n] = sum_k bf16(w[n][k]) * X[m][k]
+ *       where bf16(w) is the round-to-nearest-even bfloat16 of the fp32
+ *       dequantised weight.
+ * Accuracy: |Y - Y_exact| <= 1e-4 * sum_k |bf16(w) X| + 1e-6.
+ */
+qd_status qgemm_prefill(qd_format fmt, const void *W, const uint16_t *X,
+                        float *Y, int64_t M, int64_t N, int64_t K,
+                        void *stream);
+
+/*
+ * H = bf16( act(X Wg^T) * (X Wu^T) ) for a prefill FFN: two prefill GEMMs
+ * sharing X, with the activation product in the epilogue; H is rounded to
+ * bf16 (nearest-even) so it can feed qgemm_prefill for the down projection.
+ *
+ *   X   bf16 [M][K];  H  bf16 bits [M][N_ff]
+ *   g_out, u_out  optional fp32 [M][N_ff] gate and up products (NULL = no)
+ */
+qd_status qgemm_prefill_gate_up_act(qd_format fmt, const void *Wg,
+                                    const void *Wu, const uint16_t *X,
+                                    qd_act act, uint16_t *H, float *g_out,
+                                    float *u_out, int64_t M, int64_t N_ff,
+                                    int64_t K, void *stream);
+
+/*
+ * out = dequantised W, fp32 [N][K] (exact: the single rounding of the real
+ * value of each weight), or its round-to-nearest-even bf16 bits.  Used by
+ * tests to check the in-kernel decoders bit for bit.
+ */
+qd_status qdequant(qd_format fmt, const void *W, float *out, int64_t N,
+                   int64_t K, void *stream);
+qd_status qdequant_bf16(qd_format fmt, const void *W, uint16_t *out,
+                        int64_t N, int64_t K, void *stream);
+
+/*
+ * Launch-shape override for tuning sweeps (process-wide; 0 = automatic).
+ *   p_in   K-slices interleaved inside one workgroup (1, 2, 4, 8, 16)
+ *   p_out  K-slices across workgroups (>= 1; > 1 uses the split-K workspace)
+ *   nr     rows per lane group for plain GEMV (1 or 2)
+ * Returns QD_EINVAL for values outside these sets.
+ */
+qd_status qd_set_launch_override(int p_in, int p_out, int nr);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QDECODE_H */

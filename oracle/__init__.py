@@ -165,6 +165,23 @@ def gemv(fmt, W: np.ndarray, x: np.ndarray, N: int, K: int,
     return y, S
 
 
+def gemv_rows(fmt, W: np.ndarray, x: np.ndarray, N: int, K: int, rows):
+    """Same as gemv, computed only for the listed rows (others NaN)."""
+    fmt = _fmt(fmt)
+    W = np.ascontiguousarray(W, dtype=np.uint8)
+    x2 = np.ascontiguousarray(np.atleast_2d(x), dtype=np.float32)
+    batch = x2.shape[0]
+    assert x2.shape[1] == K
+    y = np.full((batch, N), np.nan, dtype=np.float64)
+    S = np.full((batch, N), np.nan, dtype=np.float64)
+    lib = _load()
+    pW, px, py, pS = _ptr(W), _ptr(x2), _ptr(y), _ptr(S)
+    for r in np.asarray(rows, dtype=np.int64):
+        if lib.orc_gemv(fmt, pW, px, N, K, batch, int(r), int(r) + 1, py, pS) != 0:
+            raise ValueError("orc_gemv failed")
+    return y, S
+
+
 def gemv_threaded(fmt, W, x, N, K, threads: int):
     """Same as gemv over all rows, rows split over `threads` host threads
     (ctypes releases the GIL during the C call)."""

@@ -1,0 +1,247 @@
+"""Block-quantized decode GEMV for AMD MI355X (gfx950) -- Python binding.
+
+This module only marshals arguments: it checks torch tensors, then passes
+their device pointers and the current HIP stream to the C ABI of
+``libqdecode.so`` (declared in ``include/qdecode.h``).  Every step of the
+computation runs in the library's HIP kernels.  There is no fallback: if the
+library is not built, or a tensor is not on the GPU, the call raises.
+
+Entry points (same names as the C ABI):
+    qgemv_q4k, qgemv_q6k, qgemv_q8_0, qgemv        y = W x, batch 1..8
+    qffn_gate_up_act                               h = act(Wg xn) * (Wu xn)
+    qgemm_prefill, qgemm_prefill_gate_up_act       bf16 MFMA prefill GEMMs
+    qdequant, qdequant_bf16                        decoded weights (tests)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqdecode.so")
+
+Q4_K, Q6_K, Q8_0 = 0, 1, 2
+FORMATS = {"q4_k": Q4_K, "q6_k": Q6_K, "q8_0": Q8_0}
+ACT_GELU_TANH, ACT_SILU = 0, 1
+ACTS = {"gelu_tanh": ACT_GELU_TANH, "silu": ACT_SILU}
+MAX_BATCH = 8
+
+QD_OK, QD_EINVAL, QD_ESHAPE, QD_EALIGN, QD_ELAUNCH, QD_EUNSUPPORTED, QD_ENOMEM = range(7)
+
+# Every function the header declares, with its ctypes signature.
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I = ctypes.c_int
+_F = ctypes.c_float
+SIGNATURES = {
+    "qd_block_elems": (_I, [_I]),
+    "qd_block_bytes": (_I, [_I]),
+    "qd_row_bytes": (_I64, [_I, _I64]),
+    "qd_status_str": (ctypes.c_char_p, [_I]),
+    "qd_version": (_I, []),
+    "qgemv_q4k": (_I, [_P, _P, _P, _I64, _I64, _I, _P]),
+    "qgemv_q6k": (_I, [_P, _P, _P, _I64, _I64, _I, _P]),
+    "qgemv_q8_0": (_I, [_P, _P, _P, _I64, _I64, _I, _P]),
+    "qgemv": (_I, [_I, _P, _P, _P, _I64, _I64, _I, _P]),
+    "qffn_gate_up_act": (_I, [_I, _P, _P, _P, _P, _F, _I, _P, _P, _P, _I64, _I64, _I, _P]),
+    "qgemm_prefill": (_I, [_I, _P, _P, _P, _I64, _I64, _I64, _P]),
+    "qgemm_prefill_gate_up_act": (_I, [_I, _P, _P, _P, _I, _P, _P, _P, _I64, _I64, _I64, _P]),
+    "qdequant": (_I, [_I, _P, _P, _I64, _I64, _P]),
+    "qdequant_bf16": (_I, [_I, _P, _P, _I64, _I64, _P]),
+    "qd_set_launch_override": (_I, [_I, _I, _I]),
+}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class QDError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = lib().qd_status_str(status).decode()
+        super().__init__(f"{fn} failed: status {status} ({msg})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libqdecode.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                    "(hipcc --offload-arch=gfx950) first")
+            L = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in SIGNATURES.items():
+                fn = getattr(L, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = L
+        return _lib
+
+
+def _fmt(fmt) -> int:
+    v = FORMATS[fmt.lower()] if isinstance(fmt, str) else int(fmt)
+    if v not in (Q4_K, Q6_K, Q8_0):
+        raise ValueError(f"unknown format {fmt!r}")
+    return v
+
+
+def _act(act) -> int:
+    return ACTS[act] if isinstance(act, str) else int(act)
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (no CPU path exists)")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _check(fn: str, status: int):
+    if status != QD_OK:
+        raise QDError(fn, status)
+
+
+def block_elems(fmt) -> int:
+    return lib().qd_block_elems(_fmt(fmt))
+
+
+def block_bytes(fmt) -> int:
+    return lib().qd_block_bytes(_fmt(fmt))
+
+
+def row_bytes(fmt, K: int) -> int:
+    return lib().qd_row_bytes(_fmt(fmt), K)
+
+
+def _rows(fmt: int, W: torch.Tensor, K: int) -> int:
+    rb = lib().qd_row_bytes(fmt, K)
+    if rb <= 0:
+        raise ValueError(f"K={K} is not a multiple of the block size")
+    if W.numel() % rb:
+        raise ValueError("weight bytes are not a whole number of rows")
+    return W.numel() // rb
+
+
+def qgemv(fmt, W: torch.Tensor, x: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
+    """y = W x.  W: uint8 (N rows of blocks); x: fp32 [K] or [batch, K]."""
+    f = _fmt(fmt)
+    K = x.shape[-1]
+    batch = 1 if x.dim() == 1 else x.shape[0]
+    N = _rows(f, W, K)
+    if y is None:
+        y = torch.empty((N,) if x.dim() == 1 else (batch, N), dtype=torch.float32, device=x.device)
+    st = lib().qgemv(f, _dev(W, "W", torch.uint8), _dev(x, "x", torch.float32),
+                     _dev(y, "y", torch.float32), N, K, batch, _stream())
+    _check("qgemv", st)
+    return y
+
+
+def qgemv_q4k(W, x, y=None):
+    return qgemv(Q4_K, W, x, y)
+
+
+def qgemv_q6k(W, x, y=None):
+    return qgemv(Q6_K, W, x, y)
+
+
+def qgemv_q8_0(W, x, y=None):
+    return qgemv(Q8_0, W, x, y)
+
+
+def qffn_gate_up_act(fmt, Wg: torch.Tensor, Wu: torch.Tensor, x: torch.Tensor,
+                     norm_w: torch.Tensor | None = None, eps: float = 1e-6, act="gelu_tanh",
+                     h: torch.Tensor | None = None, g_out: torch.Tensor | None = None,
+                     u_out: torch.Tensor | None = None) -> torch.Tensor:
+    """h = act(Wg xn) * (Wu xn) with xn = RMSNorm(x) (if norm_w) or x."""
+    f = _fmt(fmt)
+    K = x.shape[-1]
+    batch = 1 if x.dim() == 1 else x.shape[0]
+    N = _rows(f, Wg, K)
+    if _rows(f, Wu, K) != N:
+        raise ValueError("gate and up must have the same shape")
+    shape = (N,) if x.dim() == 1 else (batch, N)
+    if h is None:
+        h = torch.empty(shape, dtype=torch.float32, device=x.device)
+    nw = _dev(norm_w, "norm_w", torch.float32) if norm_w is not None else None
+    gp = _dev(g_out, "g_out", torch.float32) if g_out is not None else None
+    up = _dev(u_out, "u_out", torch.float32) if u_out is not None else None
+    st = lib().qffn_gate_up_act(f, _dev(Wg, "Wg", torch.uint8), _dev(Wu, "Wu", torch.uint8),
+                                _dev(x, "x", torch.float32), nw, float(eps), _act(act),
+                                _dev(h, "h", torch.float32), gp, up, N, K, batch, _stream())
+    _check("qffn_gate_up_act", st)
+    return h
+
+
+def qgemm_prefill(fmt, W: torch.Tensor, X: torch.Tensor, Y: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = X bf16(W)^T.  X: bf16 bits as int16/uint16 or torch.bfloat16 [M, K]."""
+    f = _fmt(fmt)
+    M, K = X.shape
+    N = _rows(f, W, K)
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    st = lib().qgemm_prefill(f, _dev(W, "W", torch.uint8), _dev(X, "X", X.dtype if X.dtype in
+                             (torch.bfloat16, torch.int16, torch.uint16) else torch.bfloat16),
+                             _dev(Y, "Y", torch.float32), M, N, K, _stream())
+    _check("qgemm_prefill", st)
+    return Y
+
+
+def qgemm_prefill_gate_up_act(fmt, Wg, Wu, X, act="gelu_tanh", H=None, g_out=None, u_out=None):
+    """H = bf16(act(X Wg^T) * (X Wu^T)); X and H bf16 [M, *]."""
+    f = _fmt(fmt)
+    M, K = X.shape
+    N = _rows(f, Wg, K)
+    if _rows(f, Wu, K) != N:
+        raise ValueError("gate and up must have the same shape")
+    if H is None:
+        H = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    xdt = X.dtype if X.dtype in (torch.bfloat16, torch.int16, torch.uint16) else torch.bfloat16
+    hdt = H.dtype if H.dtype in (torch.bfloat16, torch.int16, torch.uint16) else torch.bfloat16
+    gp = _dev(g_out, "g_out", torch.float32) if g_out is not None else None
+    up = _dev(u_out, "u_out", torch.float32) if u_out is not None else None
+    st = lib().qgemm_prefill_gate_up_act(f, _dev(Wg, "Wg", torch.uint8), _dev(Wu, "Wu", torch.uint8),
+                                         _dev(X, "X", xdt), _act(act), _dev(H, "H", hdt), gp, up,
+                                         M, N, K, _stream())
+    _check("qgemm_prefill_gate_up_act", st)
+    return H
+
+
+def qdequant(fmt, W: torch.Tensor, K: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """fp32 [N, K] dequantised weights."""
+    f = _fmt(fmt)
+    N = _rows(f, W, K)
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.float32, device=W.device)
+    st = lib().qdequant(f, _dev(W, "W", torch.uint8), _dev(out, "out", torch.float32), N, K, _stream())
+    _check("qdequant", st)
+    return out
+
+
+def qdequant_bf16(fmt, W: torch.Tensor, K: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """bf16 bits (int16 tensor) [N, K] of the dequantised weights."""
+    f = _fmt(fmt)
+    N = _rows(f, W, K)
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.int16, device=W.device)
+    st = lib().qdequant_bf16(f, _dev(W, "W", torch.uint8), _dev(out, "out", out.dtype), N, K, _stream())
+    _check("qdequant_bf16", st)
+    return out
+
+
+def set_launch_override(p_in: int = 0, p_out: int = 0, nr: int = 0):
+    """Force the GEMV launch shape for tuning sweeps (0 = automatic)."""
+    _check("qd_set_launch_override", lib().qd_set_launch_override(p_in, p_out, nr))

@@ -1,0 +1,332 @@
+// qd_abi.hip -- the C ABI of include/qdecode.h: argument checks, launch-shape
+// choice and the split-K workspace.  Every check runs on the host before any
+// HIP call, so a rejected call enqueues nothing.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "qd_internal.h"
+#include "qdecode.h"
+
+namespace {
+
+using qd::Shape;
+
+constexpr int kVersion = 10000;  // 1.0.0
+
+int block_elems(int fmt) {
+    switch (fmt) {
+    case QD_Q4_K: return 256;
+    case QD_Q6_K: return 256;
+    case QD_Q8_0: return 32;
+    default: return 0;
+    }
+}
+
+int block_bytes(int fmt) {
+    switch (fmt) {
+    case QD_Q4_K: return 144;
+    case QD_Q6_K: return 210;
+    case QD_Q8_0: return 34;
+    default: return 0;
+    }
+}
+
+int64_t row_bytes(int fmt, int64_t K) {
+    const int qk = block_elems(fmt);
+    if (qk == 0 || K <= 0 || K % qk != 0) return 0;
+    return (K / qk) * (int64_t)block_bytes(fmt);
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// [p, p + n) and [q, q + m) overlap?
+bool overlap(const void *p, size_t n, const void *q, size_t m) {
+    if (!p || !q || n == 0 || m == 0) return false;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+    return a < b + m && b < a + n;
+}
+
+// ------------------------------------------------------- launch shapes ---
+std::atomic<int> g_over_pin{0}, g_over_pout{0}, g_over_nr{0};
+
+constexpr int kTargetWorkgroups = 1024;  // ~4 per CU on 256 CUs
+constexpr int kMaxTiles = 1 << 16;       // split-K counters per workspace
+
+int lds_units_max(int fmt, int batch) {
+    // largest nk whose staging fits the per-workgroup LDS budget
+    int nk = 1;
+    while (qd::mv_lds_bytes(fmt, batch, nk + 1) <= (size_t)qd::kLdsBudgetBytes) nk++;
+    return nk;
+}
+
+struct Plan {
+    Shape s;
+    int nk;
+    int64_t tiles;
+};
+
+Plan make_plan(int fmt, int64_t N, int64_t K, int batch, bool ffn, Shape s) {
+    const int nb = (int)((K + qd::kSuper - 1) / qd::kSuper);
+    Plan p;
+    p.s = s;
+    p.nk = (nb + s.p_out - 1) / s.p_out;
+    p.s.p_out = (nb + p.nk - 1) / p.nk;  // every slice non-empty
+    const int rows_wg = (qd::kGroups / s.p_in) * (ffn ? 1 : s.nr);
+    p.tiles = (N + rows_wg - 1) / rows_wg;
+    return p;
+}
+
+Plan choose_plan(int fmt, int64_t N, int64_t K, int batch, bool ffn) {
+    const int nb = (int)((K + qd::kSuper - 1) / qd::kSuper);
+    const int max_nk = lds_units_max(fmt, batch);
+    Shape s{1, 1, ffn ? 2 : (N >= 16384 ? 2 : 1)};
+    s.p_out = (nb + max_nk - 1) / max_nk;  // LDS bound
+    Plan p = make_plan(fmt, N, K, batch, ffn, s);
+    // Add K-parallelism until the grid is large enough or each lane group is
+    // down to about two superunits: first inside the workgroup (no
+    // workspace), then across workgroups.
+    for (int iter = 0; iter < 16; iter++) {
+        const int64_t wgs = p.tiles * p.s.p_out;
+        const int steps = (p.nk + p.s.p_in - 1) / p.s.p_in;
+        if (wgs >= kTargetWorkgroups || steps <= 2) break;
+        Shape t = p.s;
+        if (t.p_in < 4 && p.nk / (t.p_in * 2) >= 2) t.p_in *= 2;
+        else if (p.nk >= 4 && p.tiles <= kMaxTiles) t.p_out = p.s.p_out * 2;
+        else if (t.p_in < 16 && p.nk / (t.p_in * 2) >= 1) t.p_in *= 2;
+        else break;
+        p = make_plan(fmt, N, K, batch, ffn, t);
+    }
+    // explicit overrides (tuning sweeps)
+    const int op = g_over_pin.load(), oq = g_over_pout.load(), onr = g_over_nr.load();
+    if (op || oq || onr) {
+        Shape t = p.s;
+        if (op) t.p_in = op;
+        if (oq) t.p_out = std::max(oq, (nb + max_nk - 1) / max_nk);
+        if (onr && !ffn) t.nr = onr;
+        p = make_plan(fmt, N, K, batch, ffn, t);
+    }
+    if (p.s.p_out > 1 && p.tiles > kMaxTiles) {  // fall back: no split across workgroups
+        Shape t = p.s;
+        t.p_out = (nb + max_nk - 1) / max_nk;
+        p = make_plan(fmt, N, K, batch, ffn, t);
+    }
+    return p;
+}
+
+// ---------------------------------------------------------- workspace ---
+// Split-K partial sums and per-tile counters, one block per (device, stream)
+// so that calls on different streams never share it.  Counters start at
+// zero and every kernel that uses one resets it before it ends.
+struct Workspace {
+    float *partials = nullptr;
+    unsigned *counters = nullptr;
+    size_t partial_floats = 0;
+};
+
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+constexpr size_t kInitialPartials = size_t(8) << 20;  // 32 MiB of floats
+
+qd_status get_workspace(hipStream_t st, size_t need_floats, Workspace *out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return QD_ELAUNCH;
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    Workspace &w = g_ws[{dev, st}];
+    if (w.partials == nullptr || w.partial_floats < need_floats) {
+        size_t n = std::max(kInitialPartials, need_floats);
+        float *p = nullptr;
+        unsigned *c = nullptr;
+        if (hipMalloc(&p, n * sizeof(float)) != hipSuccess) return QD_ENOMEM;
+        if (hipMalloc(&c, kMaxTiles * sizeof(unsigned)) != hipSuccess) {
+            (void)hipFree(p);
+            return QD_ENOMEM;
+        }
+        if (hipMemsetAsync(c, 0, kMaxTiles * sizeof(unsigned), st) != hipSuccess) {
+            (void)hipFree(p);
+            (void)hipFree(c);
+            return QD_ELAUNCH;
+        }
+        if (w.partials != nullptr) {
+            // an older, smaller block: wait for its users on this stream
+            (void)hipStreamSynchronize(st);
+            (void)hipFree(w.partials);
+            (void)hipFree(w.counters);
+        }
+        w.partials = p;
+        w.counters = c;
+        w.partial_floats = n;
+    }
+    *out = w;
+    return QD_OK;
+}
+
+// ------------------------------------------------------------- checks ---
+qd_status check_shape(int fmt, int64_t N, int64_t K, int batch) {
+    if (block_elems(fmt) == 0) return QD_EINVAL;
+    if (N < 1 || K < 1 || batch < 1 || batch > QD_MAX_BATCH) return QD_ESHAPE;
+    if (row_bytes(fmt, K) == 0) return QD_ESHAPE;
+    if (N > (int64_t(1) << 31) || K > (int64_t(1) << 24)) return QD_ESHAPE;
+    return QD_OK;
+}
+
+qd_status run_mv(int fmt, bool ffn, const void *W0, const void *W1, const float *x,
+                 const float *norm_w, float eps, int act, float *y, float *g_out, float *u_out,
+                 int64_t N, int64_t K, int batch, void *stream) {
+    qd_status st = check_shape(fmt, N, K, batch);
+    if (st != QD_OK) return st;
+    if (!W0 || !x || !y || (ffn && !W1)) return QD_EINVAL;
+    if (ffn && act != QD_ACT_GELU_TANH && act != QD_ACT_SILU) return QD_EINVAL;
+    if (!aligned(W0, 16) || (W1 && !aligned(W1, 16)) || !aligned(x, 16)) return QD_EALIGN;
+    if (norm_w && !aligned(norm_w, 16)) return QD_EALIGN;
+    if (!aligned(y, 4) || (g_out && !aligned(g_out, 4)) || (u_out && !aligned(u_out, 4)))
+        return QD_EALIGN;
+    const size_t xbytes = (size_t)batch * K * 4, ybytes = (size_t)batch * N * 4;
+    const size_t wbytes = (size_t)N * row_bytes(fmt, K);
+    const void *outs[3] = {y, g_out, u_out};
+    for (const void *o : outs) {
+        if (!o) continue;
+        if (overlap(o, ybytes, x, xbytes) || overlap(o, ybytes, W0, wbytes) ||
+            (W1 && overlap(o, ybytes, W1, wbytes)) || (norm_w && overlap(o, ybytes, norm_w, K * 4)))
+            return QD_EINVAL;
+    }
+    if (overlap(y, ybytes, g_out, ybytes) || overlap(y, ybytes, u_out, ybytes) ||
+        overlap(g_out, ybytes, u_out, ybytes))
+        return QD_EINVAL;
+
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    Plan p = choose_plan(fmt, N, K, batch, ffn);
+    qd::MvArgs a{};
+    a.W0 = static_cast<const uint8_t *>(W0);
+    a.W1 = static_cast<const uint8_t *>(W1);
+    a.x = x;
+    a.norm_w = norm_w;
+    a.y = y;
+    a.g_out = g_out;
+    a.u_out = u_out;
+    a.N = N;
+    a.K = K;
+    a.row_bytes = row_bytes(fmt, K);
+    a.nb = (int)((K + qd::kSuper - 1) / qd::kSuper);
+    a.nblk = (int)(K / block_elems(fmt));
+    a.nk = p.nk;
+    a.act = act;
+    a.eps = eps;
+    if (p.s.p_out > 1) {
+        Workspace w;
+        const size_t need = (size_t)p.s.p_out * batch * (ffn ? 2 : 1) * N;
+        qd_status ws = get_workspace(hs, need, &w);
+        if (ws != QD_OK) return ws;
+        a.partials = w.partials;
+        a.counters = w.counters;
+    }
+    hipError_t e = qd::launch_gemv(fmt, batch, ffn, a, p.s, hs);
+    return e == hipSuccess ? QD_OK : QD_ELAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qd_block_elems(qd_format fmt) { return block_elems(fmt); }
+int qd_block_bytes(qd_format fmt) { return block_bytes(fmt); }
+int64_t qd_row_bytes(qd_format fmt, int64_t K) { return row_bytes(fmt, K); }
+int qd_version(void) { return kVersion; }
+
+const char *qd_status_str(qd_status s) {
+    switch (s) {
+    case QD_OK: return "ok";
+    case QD_EINVAL: return "invalid argument (null pointer, unknown enum or overlapping buffers)";
+    case QD_ESHAPE: return "shape out of range (N, M, K or batch)";
+    case QD_EALIGN: return "pointer not aligned as required";
+    case QD_ELAUNCH: return "kernel launch failed";
+    case QD_EUNSUPPORTED: return "not supported by this build";
+    case QD_ENOMEM: return "workspace allocation failed";
+    default: return "unknown status";
+    }
+}
+
+qd_status qgemv(qd_format fmt, const void *W, const float *x, float *y, int64_t N, int64_t K,
+                int batch, void *stream) {
+    return run_mv(fmt, false, W, nullptr, x, nullptr, 0.f, 0, y, nullptr, nullptr, N, K, batch,
+                  stream);
+}
+
+qd_status qgemv_q4k(const void *W, const float *x, float *y, int64_t N, int64_t K, int batch,
+                    void *stream) {
+    return qgemv(QD_Q4_K, W, x, y, N, K, batch, stream);
+}
+
+qd_status qgemv_q6k(const void *W, const float *x, float *y, int64_t N, int64_t K, int batch,
+                    void *stream) {
+    return qgemv(QD_Q6_K, W, x, y, N, K, batch, stream);
+}
+
+qd_status qgemv_q8_0(const void *W, const float *x, float *y, int64_t N, int64_t K, int batch,
+                     void *stream) {
+    return qgemv(QD_Q8_0, W, x, y, N, K, batch, stream);
+}
+
+qd_status qffn_gate_up_act(qd_format fmt, const void *Wg, const void *Wu, const float *x,
+                           const float *norm_w, float eps, qd_act act, float *h, float *g_out,
+                           float *u_out, int64_t N_ff, int64_t K, int batch, void *stream) {
+    return run_mv(fmt, true, Wg, Wu, x, norm_w, eps, act, h, g_out, u_out, N_ff, K, batch, stream);
+}
+
+qd_status qdequant(qd_format fmt, const void *W, float *out, int64_t N, int64_t K, void *stream) {
+    qd_status st = check_shape(fmt, N, K, 1);
+    if (st != QD_OK) return st;
+    if (!W || !out) return QD_EINVAL;
+    if (!aligned(W, 16)) return QD_EALIGN;
+    if (!aligned(out, 4)) return QD_EALIGN;
+    if (overlap(out, (size_t)N * K * 4, W, (size_t)N * row_bytes(fmt, K))) return QD_EINVAL;
+    hipError_t e = qd::launch_dequant(fmt, static_cast<const uint8_t *>(W), out, nullptr, N, K,
+                                      reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? QD_OK : QD_ELAUNCH;
+}
+
+qd_status qdequant_bf16(qd_format fmt, const void *W, uint16_t *out, int64_t N, int64_t K,
+                        void *stream) {
+    qd_status st = check_shape(fmt, N, K, 1);
+    if (st != QD_OK) return st;
+    if (!W || !out) return QD_EINVAL;
+    if (!aligned(W, 16)) return QD_EALIGN;
+    if (!aligned(out, 2)) return QD_EALIGN;
+    if (overlap(out, (size_t)N * K * 2, W, (size_t)N * row_bytes(fmt, K))) return QD_EINVAL;
+    hipError_t e = qd::launch_dequant(fmt, static_cast<const uint8_t *>(W), nullptr, out, N, K,
+                                      reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? QD_OK : QD_ELAUNCH;
+}
+
+qd_status qgemm_prefill(qd_format fmt, const void *W, const uint16_t *X, float *Y, int64_t M,
+                        int64_t N, int64_t K, void *stream) {
+    (void)fmt; (void)W; (void)X; (void)Y; (void)M; (void)N; (void)K; (void)stream;
+    return QD_EUNSUPPORTED;
+}
+
+qd_status qgemm_prefill_gate_up_act(qd_format fmt, const void *Wg, const void *Wu,
+                                    const uint16_t *X, qd_act act, uint16_t *H, float *g_out,
+                                    float *u_out, int64_t M, int64_t N_ff, int64_t K,
+                                    void *stream) {
+    (void)fmt; (void)Wg; (void)Wu; (void)X; (void)act; (void)H; (void)g_out; (void)u_out;
+    (void)M; (void)N_ff; (void)K; (void)stream;
+    return QD_EUNSUPPORTED;
+}
+
+qd_status qd_set_launch_override(int p_in, int p_out, int nr) {
+    auto pow2_le16 = [](int v) { return v == 1 || v == 2 || v == 4 || v == 8 || v == 16; };
+    if (p_in != 0 && !pow2_le16(p_in)) return QD_EINVAL;
+    if (p_out < 0 || p_out > 256) return QD_EINVAL;
+    if (nr != 0 && nr != 1 && nr != 2) return QD_EINVAL;
+    g_over_pin.store(p_in);
+    g_over_pout.store(p_out);
+    g_over_nr.store(nr);
+    return QD_OK;
+}
+
+}  // extern "C"

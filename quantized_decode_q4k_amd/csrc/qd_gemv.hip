@@ -1,0 +1,491 @@
+// qd_gemv.hip -- batch-1..8 GEMV and fused FFN gate+up over Q4_K, Q6_K and
+// Q8_0 weights, dequantised in registers and fused into fp32 FMAs.
+//
+// What is computed: y[b][n] = sum_k w[n][k] x[b][k] for the decode-path
+// projections of the larql "Architecture -> Metal shader map" page (Gemma 3
+// table: q4k_matvec, q4k_matvec_8sg, q6k_matvec; q4k_ffn_gate_up_8sg + geglu)
+// and dotLLM PR #320's matmul_q8_0.  The Metal/Vulkan kernel shapes those
+// pages name (8 or 4 SIMD-groups per threadgroup, one row per threadgroup)
+// are not followed; the CDNA4 mapping is:
+//
+//  * A workgroup is 256 threads = 64 lane groups of 4 lanes.  A lane group
+//    owns one row (two for the fused gate/up, or for GEMV with nr = 2) and
+//    walks that row's superunits (256 weights: one Q4_K/Q6_K block or eight
+//    Q8_0 blocks).  Each lane takes 64 weights of the superunit, so the four
+//    lanes read the block bytes with 16-byte (Q4_K) or 4-byte-aligned dword
+//    (Q6_K, Q8_0: their 210- and 34-byte blocks start on 2-byte boundaries)
+//    loads and the row stream is read exactly once.
+//  * K is split p_in ways inside a workgroup (adjacent lane groups take
+//    interleaved superunits of the same row, so they read neighbouring
+//    blocks together) and p_out ways across workgroups (gridDim.y).  The
+//    split across workgroups ends in a deterministic reduction: partial sums
+//    go to a workspace and the last workgroup to finish a row tile sums them
+//    in slice order.
+//  * x (optionally RMS-normalised on the way in) is staged once per
+//    workgroup in LDS with a 16-byte skew every 64 floats, so the four lanes
+//    of a group, which read the same offsets 64 floats apart, hit different
+//    banks.  Q4_K also stages per-32 sums of x for its min term.
+//  * Decoding: Q4_K nibbles become floats through the fp8 converter (two
+//    per instruction, exact); Q6_K quants become signed (q - 32) bytes with a
+//    byte-permute lookup of the high bits, then one sign-extending convert;
+//    Q8_0 bytes take one sign-extending convert.  Scales are applied once per
+//    16 or 32 weights.
+//  * Per-lane partials are reduced across the 4*p_in lanes of a row with
+//    cross-lane shuffles; one lane writes each output (and, for the fused
+//    FFN, applies the GELU-tanh or SiLU product).
+#include "qd_decode.h"
+
+namespace qd {
+
+// LDS index of logical activation index k (16-byte skew every 64 floats).
+QD_DEV int xphys(int k) { return k + ((k >> 6) << 2); }
+// LDS floats per staged superunit per batch row.
+constexpr int kSuperPhys = kSuper + kSuper / 16;  // 272
+
+// ------------------------------------------------------------ per-step math ---
+// One superunit of NR row streams against B staged activation rows.
+
+// Q4_K.  xp: this lane's 64 activations (logical 256*tl + 64c, contiguous in
+// LDS); sp: the staged sums of x over sub-blocks 2c and 2c+1.  Accumulates,
+// per row stream and batch row,
+//   yq += d * (sc0 * sum(q x) over the low nibbles + sc1 * sum(q x) high)
+//         (in units of fp8_unit())
+//   ym += dmin * (m0 * X0 + m1 * X1)
+// so that the row result is yq / fp8_unit() - ym.
+template <int NR, int B>
+QD_DEV void q4k_step(const RawQ4K (&r)[NR], const float *__restrict__ xp, int xstride,
+                     const float *__restrict__ sp, int sstride, const Q4Lane &L,
+                     float (&yq)[NR][B], float (&ym)[NR][B]) {
+    float alo[NR][B], ahi[NR][B];
+#pragma unroll
+    for (int i = 0; i < NR; i++)
+#pragma unroll
+        for (int b = 0; b < B; b++) { alo[i][b] = 0.f; ahi[i][b] = 0.f; }
+
+#pragma unroll
+    for (int dw = 0; dw < 8; dw++) {
+        float4 xl[B], xh[B];
+#pragma unroll
+        for (int b = 0; b < B; b++) {
+            xl[b] = *reinterpret_cast<const float4 *>(xp + b * xstride + 4 * dw);
+            xh[b] = *reinterpret_cast<const float4 *>(xp + b * xstride + 32 + 4 * dw);
+        }
+#pragma unroll
+        for (int i = 0; i < NR; i++) {
+            const Q4Nibbles n = q4k_nibbles(r[i].q[dw]);
+#pragma unroll
+            for (int b = 0; b < B; b++) {
+                float s = alo[i][b];
+                s = fmaf(n.lo01.x, xl[b].x, s);
+                s = fmaf(n.lo01.y, xl[b].y, s);
+                s = fmaf(n.lo23.x, xl[b].z, s);
+                s = fmaf(n.lo23.y, xl[b].w, s);
+                alo[i][b] = s;
+                float u = ahi[i][b];
+                u = fmaf(n.hi01.x, xh[b].x, u);
+                u = fmaf(n.hi01.y, xh[b].y, u);
+                u = fmaf(n.hi23.x, xh[b].z, u);
+                u = fmaf(n.hi23.y, xh[b].w, u);
+                ahi[i][b] = u;
+            }
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < NR; i++) {
+        const Q4Scales s = q4k_scales(r[i], L);
+#pragma unroll
+        for (int b = 0; b < B; b++) {
+            const float2 X = *reinterpret_cast<const float2 *>(sp + b * sstride);
+            yq[i][b] = fmaf(s.d, fmaf(s.sc1, ahi[i][b], s.sc0 * alo[i][b]), yq[i][b]);
+            ym[i][b] = fmaf(s.dmin, fmaf(s.m1, X.y, s.m0 * X.x), ym[i][b]);
+        }
+    }
+}
+
+// Q6_K.  xg0..xg3: this lane's four runs of 16 activations (groups g).
+template <int NR, int B>
+QD_DEV void q6k_step(const RawQ6K (&r)[NR], const float *__restrict__ xg0,
+                     const float *__restrict__ xg1, const float *__restrict__ xg2,
+                     const float *__restrict__ xg3, int xstride, int j, float (&y)[NR][B]) {
+    float acc[NR][B][4];
+#pragma unroll
+    for (int i = 0; i < NR; i++)
+#pragma unroll
+        for (int b = 0; b < B; b++)
+#pragma unroll
+            for (int g = 0; g < 4; g++) acc[i][b][g] = 0.f;
+
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        float4 xv[B][4];
+#pragma unroll
+        for (int b = 0; b < B; b++) {
+            xv[b][0] = *reinterpret_cast<const float4 *>(xg0 + b * xstride + 4 * k);
+            xv[b][1] = *reinterpret_cast<const float4 *>(xg1 + b * xstride + 4 * k);
+            xv[b][2] = *reinterpret_cast<const float4 *>(xg2 + b * xstride + 4 * k);
+            xv[b][3] = *reinterpret_cast<const float4 *>(xg3 + b * xstride + 4 * k);
+        }
+#pragma unroll
+        for (int i = 0; i < NR; i++) {
+            uint32_t q[4];
+            q6k_qbytes(r[i], k, q);
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                const float w0 = sbyte(q[g], 0), w1 = sbyte(q[g], 1);
+                const float w2 = sbyte(q[g], 2), w3 = sbyte(q[g], 3);
+#pragma unroll
+                for (int b = 0; b < B; b++) {
+                    float s = acc[i][b][g];
+                    s = fmaf(w0, xv[b][g].x, s);
+                    s = fmaf(w1, xv[b][g].y, s);
+                    s = fmaf(w2, xv[b][g].z, s);
+                    s = fmaf(w3, xv[b][g].w, s);
+                    acc[i][b][g] = s;
+                }
+            }
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < NR; i++) {
+        const Q6Scales s = q6k_scales(r[i], j);
+#pragma unroll
+        for (int b = 0; b < B; b++) {
+            float u = s.sc[0] * acc[i][b][0];
+            u = fmaf(s.sc[1], acc[i][b][1], u);
+            u = fmaf(s.sc[2], acc[i][b][2], u);
+            u = fmaf(s.sc[3], acc[i][b][3], u);
+            y[i][b] = fmaf(s.d, u, y[i][b]);
+        }
+    }
+}
+
+// Q8_0.  xp: this lane's 64 activations (block A then block B).
+template <int NR, int B>
+QD_DEV void q80_step(const RawQ80 (&r)[NR], const float *__restrict__ xp, int xstride,
+                     float (&y)[NR][B]) {
+#pragma unroll
+    for (int i = 0; i < NR; i++) {
+        const float2 d = q80_d(r[i]);
+        float accA[B], accB[B];
+#pragma unroll
+        for (int b = 0; b < B; b++) { accA[b] = 0.f; accB[b] = 0.f; }
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            const uint2 v = q80_qdwords(r[i], k);
+#pragma unroll
+            for (int b = 0; b < B; b++) {
+                const float4 xa = *reinterpret_cast<const float4 *>(xp + b * xstride + 4 * k);
+                const float4 xb = *reinterpret_cast<const float4 *>(xp + b * xstride + 32 + 4 * k);
+                float s = accA[b];
+                s = fmaf(sbyte(v.x, 0), xa.x, s);
+                s = fmaf(sbyte(v.x, 1), xa.y, s);
+                s = fmaf(sbyte(v.x, 2), xa.z, s);
+                s = fmaf(sbyte(v.x, 3), xa.w, s);
+                accA[b] = s;
+                float u = accB[b];
+                u = fmaf(sbyte(v.y, 0), xb.x, u);
+                u = fmaf(sbyte(v.y, 1), xb.y, u);
+                u = fmaf(sbyte(v.y, 2), xb.z, u);
+                u = fmaf(sbyte(v.y, 3), xb.w, u);
+                accB[b] = u;
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < B; b++) y[i][b] = fmaf(d.y, accB[b], fmaf(d.x, accA[b], y[i][b]));
+    }
+}
+
+// ------------------------------------------------------------- the kernel ---
+QD_DEV float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+// FMT: block format; B: batch rows (1..8); NR: row streams per lane group
+// (FFN: 2 = gate, up); FFN: fused gate/up/activation epilogue.
+template <int FMT, int B, int NR, bool FFN>
+__global__ __launch_bounds__(kThreads) void mv_kernel(MvArgs a) {
+    extern __shared__ float smem[];
+    const int tid = threadIdx.x;
+    const int c = tid & 3;
+    const int grp = tid >> 2;
+    const int p_in = a.p_in;
+    const int rs = grp / p_in;            // row slot in this workgroup
+    const int pi = grp - rs * p_in;       // K-interleave index
+    const int RS = kGroups / p_in;        // row slots per workgroup
+    const int ks = blockIdx.y;            // K-slice of this workgroup
+    const int t_beg = ks * a.nk;
+    const int t_end = min(a.nb, t_beg + a.nk);
+    const int xstride = a.nk * kSuperPhys;
+    float *xl = smem;                                 // [B][nk * 272]
+    float *xsum = smem + B * xstride;                 // Q4_K: [B][nk * 8]
+    const int sstride = a.nk * 8;
+    float *red = xsum + (FMT == kQ4K ? B * sstride : 0);  // [4 waves][B], then [B]
+
+    // ---- rows of this lane group
+    const int64_t slot = (int64_t)blockIdx.x * RS + rs;
+    int64_t row[NR];
+    bool rvalid[NR];
+    const uint8_t *rowp[NR];
+#pragma unroll
+    for (int i = 0; i < NR; i++) {
+        row[i] = FFN ? slot : slot * NR + i;
+        rvalid[i] = row[i] < a.N;
+        int64_t rr = rvalid[i] ? row[i] : a.N - 1;
+        rowp[i] = ((FFN && i == 1) ? a.W1 : a.W0) + rr * a.row_bytes;
+    }
+
+    // ---- first weight loads go out before the staging work
+    using Raw = typename RawOf<FMT>::T;
+    Raw cur[NR];
+    int t = t_beg + pi;
+    {
+        int t0 = min(t, t_end - 1);
+#pragma unroll
+        for (int i = 0; i < NR; i++) load_unit<FMT>(cur[i], rowp[i], t0, c, a.nblk);
+    }
+
+    // ---- inverse RMS of each batch row (RMS-norm fused into staging)
+    const int64_t K = a.K;
+    float inv_rms[B];
+#pragma unroll
+    for (int b = 0; b < B; b++) inv_rms[b] = 1.0f;
+    if (a.norm_w != nullptr) {
+        const int wave = tid >> 6;
+#pragma unroll
+        for (int b = 0; b < B; b++) {
+            const float *xb = a.x + (int64_t)b * K;
+            float ss = 0.f;
+            for (int64_t k = 4 * tid; k < K; k += 4 * kThreads) {
+                float4 v = *reinterpret_cast<const float4 *>(xb + k);
+                ss = fmaf(v.x, v.x, ss);
+                ss = fmaf(v.y, v.y, ss);
+                ss = fmaf(v.z, v.z, ss);
+                ss = fmaf(v.w, v.w, ss);
+            }
+            ss = wave_sum(ss);
+            if ((tid & 63) == 0) red[wave * B + b] = ss;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int b = 0; b < B; b++) {
+            float ss = (red[b] + red[B + b]) + (red[2 * B + b] + red[3 * B + b]);
+            inv_rms[b] = 1.0f / sqrtf(ss / (float)K + a.eps);
+        }
+    }
+
+    // ---- stage x[b][t_beg*256 ...) into LDS (zero past K)
+    {
+        const int F = a.nk * (kSuper / 4);   // float4 per batch row in this slice
+        const int64_t k0 = (int64_t)t_beg * kSuper;
+        for (int f = tid; f < B * F; f += kThreads) {
+            int b = f / F;
+            int f4 = f - b * F;
+            int64_t k = k0 + 4 * f4;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (k < K) {
+                v = *reinterpret_cast<const float4 *>(a.x + (int64_t)b * K + k);
+                if (a.norm_w != nullptr) {
+                    float4 w = *reinterpret_cast<const float4 *>(a.norm_w + k);
+                    float ir = inv_rms[0];
+#pragma unroll
+                    for (int bb = 1; bb < B; bb++)
+                        if (bb == b) ir = inv_rms[bb];
+                    v.x = v.x * ir * w.x;
+                    v.y = v.y * ir * w.y;
+                    v.z = v.z * ir * w.z;
+                    v.w = v.w * ir * w.w;
+                }
+            }
+            *reinterpret_cast<float4 *>(xl + b * xstride + xphys(4 * f4)) = v;
+            if constexpr (FMT == kQ4K) {
+                // sum of each 32-run of x: 8 consecutive float4 live in 8
+                // consecutive lanes of one wave
+                float s = (v.x + v.y) + (v.z + v.w);
+                s += __shfl_xor(s, 1);
+                s += __shfl_xor(s, 2);
+                s += __shfl_xor(s, 4);
+                if ((tid & 7) == 0) xsum[b * sstride + (f4 >> 3)] = s;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- main loop over this group's superunits
+    float acc[NR][B], acc2[NR][B];
+#pragma unroll
+    for (int i = 0; i < NR; i++)
+#pragma unroll
+        for (int b = 0; b < B; b++) { acc[i][b] = 0.f; acc2[i][b] = 0.f; }
+
+    Q4Lane L4;
+    if constexpr (FMT == kQ4K) L4 = q4k_lane(c);
+
+    for (; t < t_end; t += p_in) {
+        Raw nxt[NR];
+        const int tn = min(t + p_in, t_end - 1);
+#pragma unroll
+        for (int i = 0; i < NR; i++) load_unit<FMT>(nxt[i], rowp[i], tn, c, a.nblk);
+
+        const int tl = t - t_beg;
+        if constexpr (FMT == kQ4K) {
+            const float *xp = xl + xphys(kSuper * tl + 64 * c);
+            const float *sp = xsum + 8 * tl + 2 * c;
+            q4k_step<NR, B>(cur, xp, xstride, sp, sstride, L4, acc, acc2);
+        } else if constexpr (FMT == kQ6K) {
+            const int h = c >> 1, j = c & 1;
+            const int base = kSuper * tl + 128 * h + 16 * j;
+            q6k_step<NR, B>(cur, xl + xphys(base), xl + xphys(base + 32), xl + xphys(base + 64),
+                            xl + xphys(base + 96), xstride, j, acc);
+        } else {
+            q80_step<NR, B>(cur, xl + xphys(kSuper * tl + 64 * c), xstride, acc);
+        }
+#pragma unroll
+        for (int i = 0; i < NR; i++) cur[i] = nxt[i];
+    }
+
+    // ---- combine per lane, then reduce over the 4 * p_in lanes of a row
+    float v[NR][B];
+    if constexpr (FMT == kQ4K) {
+        const float inv_unit = 1.0f / fp8_unit();  // exact power of two
+#pragma unroll
+        for (int i = 0; i < NR; i++)
+#pragma unroll
+            for (int b = 0; b < B; b++) v[i][b] = fmaf(acc[i][b], inv_unit, -acc2[i][b]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < NR; i++)
+#pragma unroll
+            for (int b = 0; b < B; b++) v[i][b] = acc[i][b];
+    }
+    for (int off = 1; off < 4 * p_in; off <<= 1) {
+#pragma unroll
+        for (int i = 0; i < NR; i++)
+#pragma unroll
+            for (int b = 0; b < B; b++) v[i][b] += __shfl_xor(v[i][b], off);
+    }
+    const bool leader = (pi == 0) && (c == 0);
+    const int64_t N = a.N;
+
+    if (gridDim.y == 1) {
+        if (leader) {
+            if constexpr (FFN) {
+                if (rvalid[0]) {
+#pragma unroll
+                    for (int b = 0; b < B; b++) {
+                        float gv = v[0][b], uv = v[1][b];
+                        a.y[(int64_t)b * N + row[0]] = act_apply(a.act, gv) * uv;
+                        if (a.g_out) a.g_out[(int64_t)b * N + row[0]] = gv;
+                        if (a.u_out) a.u_out[(int64_t)b * N + row[0]] = uv;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < NR; i++)
+                    if (rvalid[i])
+#pragma unroll
+                        for (int b = 0; b < B; b++) a.y[(int64_t)b * N + row[i]] = v[i][b];
+            }
+        }
+        return;
+    }
+
+    // ---- split-K: publish partials; the last workgroup of this row tile sums
+    constexpr int NP = FFN ? 2 : 1;  // partial planes per batch row
+    if (leader) {
+#pragma unroll
+        for (int i = 0; i < NR; i++)
+            if (rvalid[i])
+#pragma unroll
+                for (int b = 0; b < B; b++)
+                    a.partials[(((int64_t)ks * B + b) * NP + (FFN ? i : 0)) * N + row[i]] = v[i][b];
+    }
+    __threadfence();
+    __syncthreads();
+    __shared__ int s_last;
+    if (tid == 0) {
+        unsigned prev = atomicAdd(&a.counters[blockIdx.x], 1u);
+        s_last = (prev == gridDim.y - 1) ? 1 : 0;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    const int rows_here = FFN ? RS : RS * NR;
+    const int64_t row0 = (int64_t)blockIdx.x * rows_here;
+    for (int e = tid; e < rows_here * B; e += kThreads) {
+        const int b = e / rows_here;
+        const int64_t r = row0 + (e - b * rows_here);
+        if (r >= N) continue;
+        float s0 = 0.f, s1 = 0.f;
+        for (int k = 0; k < (int)gridDim.y; k++) {
+            const float *p = a.partials + (((int64_t)k * B + b) * NP) * N + r;
+            s0 += __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if constexpr (FFN) s1 += __hip_atomic_load(p + N, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if constexpr (FFN) {
+            a.y[(int64_t)b * N + r] = act_apply(a.act, s0) * s1;
+            if (a.g_out) a.g_out[(int64_t)b * N + r] = s0;
+            if (a.u_out) a.u_out[(int64_t)b * N + r] = s1;
+        } else {
+            a.y[(int64_t)b * N + r] = s0;
+        }
+    }
+    if (tid == 0) a.counters[blockIdx.x] = 0u;  // ready for the next call
+}
+
+// ------------------------------------------------------------ launchers ---
+size_t mv_lds_bytes(int fmt, int batch, int nk) {
+    size_t floats = (size_t)batch * nk * kSuperPhys;
+    if (fmt == kQ4K) floats += (size_t)batch * nk * 8;
+    floats += 4 * 8;  // cross-wave scratch: [4 waves][batch]
+    return floats * sizeof(float);
+}
+
+template <int FMT, int B, int NR, bool FFN>
+static hipError_t launch_one(const MvArgs &a, dim3 grid, hipStream_t st) {
+    size_t lds = mv_lds_bytes(FMT, B, a.nk);
+    hipLaunchKernelGGL((mv_kernel<FMT, B, NR, FFN>), grid, dim3(kThreads), lds, st, a);
+    return hipGetLastError();
+}
+
+template <int FMT, int B>
+static hipError_t launch_fb(const MvArgs &a, bool ffn, int nr, dim3 grid, hipStream_t st) {
+    if (ffn) return launch_one<FMT, B, 2, true>(a, grid, st);
+    if (nr == 2) return launch_one<FMT, B, 2, false>(a, grid, st);
+    return launch_one<FMT, B, 1, false>(a, grid, st);
+}
+
+template <int FMT>
+static hipError_t launch_f(const MvArgs &a, int batch, bool ffn, int nr, dim3 grid, hipStream_t st) {
+    switch (batch) {
+    case 1: return launch_fb<FMT, 1>(a, ffn, nr, grid, st);
+    case 2: return launch_fb<FMT, 2>(a, ffn, nr, grid, st);
+    case 3: return launch_fb<FMT, 3>(a, ffn, nr, grid, st);
+    case 4: return launch_fb<FMT, 4>(a, ffn, nr, grid, st);
+    case 5: return launch_fb<FMT, 5>(a, ffn, nr, grid, st);
+    case 6: return launch_fb<FMT, 6>(a, ffn, nr, grid, st);
+    case 7: return launch_fb<FMT, 7>(a, ffn, nr, grid, st);
+    case 8: return launch_fb<FMT, 8>(a, ffn, nr, grid, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_gemv(int fmt, int batch, bool ffn, MvArgs a, Shape s, hipStream_t st) {
+    a.p_in = s.p_in;
+    a.p_out = s.p_out;
+    const int nr = ffn ? 2 : s.nr;
+    const int rows_per_wg = (kGroups / s.p_in) * (ffn ? 1 : nr);
+    const int64_t tiles = (a.N + rows_per_wg - 1) / rows_per_wg;
+    dim3 grid((unsigned)tiles, (unsigned)s.p_out);
+    switch (fmt) {
+    case kQ4K: return launch_f<kQ4K>(a, batch, ffn, nr, grid, st);
+    case kQ6K: return launch_f<kQ6K>(a, batch, ffn, nr, grid, st);
+    case kQ80: return launch_f<kQ80>(a, batch, ffn, nr, grid, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace qd

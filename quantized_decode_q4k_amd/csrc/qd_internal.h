@@ -1,0 +1,72 @@
+// qd_internal.h -- declarations shared by the HIP translation units of the
+// library (launchers and argument blocks).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qd {
+
+enum Fmt : int { kQ4K = 0, kQ6K = 1, kQ80 = 2 };
+
+// Every format is processed in "superunits" of 256 weights: one Q4_K or Q6_K
+// block, or eight Q8_0 blocks.  Four lanes share a superunit, 64 weights each.
+constexpr int kSuper = 256;
+constexpr int kThreads = 256;            // threads per workgroup (4 waves)
+constexpr int kGroups = kThreads / 4;    // lane groups per workgroup
+constexpr int kLdsBudgetBytes = 65536 - 1024;  // dynamic LDS per workgroup (two fit on a CU)
+
+// Arguments of the GEMV / fused gate-up kernels.
+struct MvArgs {
+    const uint8_t *W0;      // row stream 0: the matrix (GEMV) or gate (FFN)
+    const uint8_t *W1;      // row stream 1: up (FFN); unused for GEMV
+    const float *x;         // [batch][K]
+    const float *norm_w;    // [K] or nullptr
+    float *y;               // GEMV: [batch][N]; FFN: h [batch][N]
+    float *g_out;           // FFN optional [batch][N]
+    float *u_out;           // FFN optional [batch][N]
+    float *partials;        // split-K: [p_out][batch][nr][N]
+    unsigned *counters;     // split-K: one per row tile, zero between calls
+    int64_t N;              // output rows
+    int64_t K;              // columns
+    int64_t row_bytes;      // bytes per weight row
+    int nb;                 // superunits per row, ceil(K / 256)
+    int nblk;               // format blocks per row (Q8_0: K / 32)
+    int nk;                 // superunits per K-slice (split across workgroups)
+    int p_in;               // K-interleave inside a workgroup
+    int p_out;              // K-slices across workgroups (gridDim.y)
+    int act;                // qd_act
+    float eps;
+};
+
+struct Shape {
+    int p_in;
+    int p_out;
+    int nr;   // row streams per lane group: 2 for FFN (gate, up); 1 or 2 for GEMV
+};
+
+// Launchers (qd_gemv.hip).
+// LDS bytes the GEMV kernel needs for `nk` staged superunits of `batch` rows.
+size_t mv_lds_bytes(int fmt, int batch, int nk);
+hipError_t launch_gemv(int fmt, int batch, bool ffn, MvArgs a, Shape s, hipStream_t st);
+
+// Dequantisers (qd_dequant.hip).
+hipError_t launch_dequant(int fmt, const uint8_t *W, float *out, uint16_t *out_bf16,
+                          int64_t N, int64_t K, hipStream_t st);
+
+// Prefill GEMM (qd_prefill.hip).
+struct GemmArgs {
+    const uint8_t *Wg;      // weights (or gate for the fused FFN)
+    const uint8_t *Wu;      // up (fused FFN) or nullptr
+    const uint16_t *X;      // bf16 [M][K]
+    float *Y;               // fp32 [M][N] (plain GEMM)
+    uint16_t *H;            // bf16 [M][N] (fused FFN)
+    float *g_out;
+    float *u_out;
+    int64_t M, N, K;
+    int64_t row_bytes;
+    int act;
+};
+hipError_t launch_gemm(int fmt, bool ffn, const GemmArgs &a, hipStream_t st);
+
+}  // namespace qd

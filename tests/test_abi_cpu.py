@@ -1,0 +1,122 @@
+"""The C ABI on the host: the library loads, exports every function the
+header declares, and rejects bad arguments before touching the GPU (every
+call below fails validation, so no HIP work is enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qdecode.h")
+
+
+def _lib():
+    import quantized_decode_q4k_amd as qd
+    if not os.path.exists(qd.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return qd, qd.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(n for n in names if n.startswith(("q", "qd_"))))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["qgemv_q4k", "qgemv_q6k", "qgemv_q8_0", "qffn_gate_up_act", "qgemm_prefill",
+              "qdequant", "qdequant_bf16", "qd_status_str", "qd_row_bytes"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    qd, L = _lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+        assert n in qd.SIGNATURES, n
+
+
+def test_block_sizes_and_row_bytes():
+    qd, L = _lib()
+    assert [L.qd_block_bytes(f) for f in (0, 1, 2)] == [144, 210, 34]
+    assert [L.qd_block_elems(f) for f in (0, 1, 2)] == [256, 256, 32]
+    assert L.qd_block_bytes(9) == 0
+    assert L.qd_row_bytes(0, 2560) == 1440
+    assert L.qd_row_bytes(1, 10240) == 8400
+    assert L.qd_row_bytes(2, 96) == 102
+    assert L.qd_row_bytes(0, 100) == 0
+    assert L.qd_row_bytes(2, 0) == 0
+    assert L.qd_version() >= 10000
+    for s in range(8):
+        assert isinstance(L.qd_status_str(s), bytes)
+
+
+# fake device pointers: never dereferenced because validation fails first
+A16 = 0x10000
+A16b = 0x20000
+A16c = 0x30000
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, A16, A16b, 4, 256, 1, None), 1),           # null W
+    ((A16, 0, A16b, 4, 256, 1, None), 1),           # null x
+    ((A16, A16b, 0, 4, 256, 1, None), 1),           # null y
+    ((A16, A16b, A16c, 0, 256, 1, None), 2),        # N = 0
+    ((A16, A16b, A16c, 4, 100, 1, None), 2),        # K not a multiple of 256
+    ((A16, A16b, A16c, 4, 256, 0, None), 2),        # batch 0
+    ((A16, A16b, A16c, 4, 256, 9, None), 2),        # batch 9
+    ((A16 + 4, A16b, A16c, 4, 256, 1, None), 3),    # W misaligned
+    ((A16, A16b + 4, A16c, 4, 256, 1, None), 3),    # x misaligned
+    ((A16, A16b, A16c + 2, 4, 256, 1, None), 3),    # y misaligned
+    ((A16, A16b, A16b + 512, 4, 256, 1, None), 1),  # y overlaps x
+])
+def test_gemv_validation(args, status):
+    _, L = _lib()
+    assert L.qgemv_q4k(*args) == status
+
+
+def test_q8_0_accepts_k_multiple_of_32_only_in_validation():
+    _, L = _lib()
+    assert L.qgemv_q8_0(A16, A16b, A16c, 4, 48, 1, None) == 2
+    assert L.qgemv(7, A16, A16b, A16c, 4, 256, 1, None) == 1
+
+
+def test_ffn_validation():
+    _, L = _lib()
+    f = L.qffn_gate_up_act
+    # null up
+    assert f(0, A16, 0, A16b, None, 1e-6, 0, A16c, None, None, 4, 256, 1, None) == 1
+    # bad activation
+    assert f(0, A16, A16 + 0x8000, A16b, None, 1e-6, 5, A16c, None, None, 4, 256, 1, None) == 1
+    # misaligned norm weight
+    assert f(0, A16, A16 + 0x8000, A16b, A16b + 0x1004, 1e-6, 0, A16c, None, None, 4, 256, 1, None) == 3
+    # h overlapping g_out
+    assert f(0, A16, A16 + 0x8000, A16b, None, 1e-6, 0, A16c, A16c + 4, None, 4, 256, 1, None) == 1
+
+
+def test_dequant_validation():
+    _, L = _lib()
+    assert L.qdequant(0, 0, A16b, 4, 256, None) == 1
+    assert L.qdequant(0, A16 + 1, A16b, 4, 256, None) == 3
+    assert L.qdequant_bf16(1, A16, A16b, 4, 300, None) == 2
+
+
+def test_launch_override_validation():
+    _, L = _lib()
+    assert L.qd_set_launch_override(3, 0, 0) == 1
+    assert L.qd_set_launch_override(0, 0, 5) == 1
+    assert L.qd_set_launch_override(0, 0, 0) == 0
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    qd, _ = _lib()
+    W = torch.zeros(144, dtype=torch.uint8)
+    x = torch.zeros(256, dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        qd.qgemv_q4k(W, x)
