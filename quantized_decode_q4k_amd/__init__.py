@@ -68,6 +68,8 @@ class QDError(RuntimeError):
 def lib() -> ctypes.CDLL:
     """The loaded libqdecode.so (raises if it has not been built)."""
     global _lib
+    if _lib is not None:
+        return _lib
     with _lock:
         if _lib is None:
             if not os.path.exists(LIB_PATH):

@@ -54,7 +54,7 @@ bool overlap(const void *p, size_t n, const void *q, size_t m) {
 // ------------------------------------------------------- launch shapes ---
 std::atomic<int> g_over_pin{0}, g_over_pout{0}, g_over_nr{0};
 
-constexpr int kTargetWorkgroups = 1024;  // ~4 per CU on 256 CUs
+constexpr int kTargetWorkgroups = 400;   // enough to keep every CU streaming
 constexpr int kMaxTiles = 1 << 16;       // split-K counters per workspace
 
 int lds_units_max(int fmt, int batch) {
@@ -84,35 +84,36 @@ Plan make_plan(int fmt, int64_t N, int64_t K, int batch, bool ffn, Shape s) {
 Plan choose_plan(int fmt, int64_t N, int64_t K, int batch, bool ffn) {
     const int nb = (int)((K + qd::kSuper - 1) / qd::kSuper);
     const int max_nk = lds_units_max(fmt, batch);
-    Shape s{1, 1, ffn ? 2 : (N >= 16384 ? 2 : 1)};
-    s.p_out = (nb + max_nk - 1) / max_nk;  // LDS bound
+    const int p_lds = (nb + max_nk - 1) / max_nk;  // K-slices the LDS budget forces
+    // Measured on MI355X (sweeps over p_in x p_out x nr for every workload
+    // shape): two lane groups per row is the best streaming shape; small-N
+    // shapes then need more K-parallelism inside the workgroup to fill the
+    // chip, and only then across workgroups.
+    Shape s{2, p_lds, 1};
     Plan p = make_plan(fmt, N, K, batch, ffn, s);
-    // Add K-parallelism until the grid is large enough or each lane group is
-    // down to about two superunits: first inside the workgroup (no
-    // workspace), then across workgroups.
     for (int iter = 0; iter < 16; iter++) {
         const int64_t wgs = p.tiles * p.s.p_out;
-        const int steps = (p.nk + p.s.p_in - 1) / p.s.p_in;
-        if (wgs >= kTargetWorkgroups || steps <= 2) break;
+        if (wgs >= kTargetWorkgroups) break;
         Shape t = p.s;
-        if (t.p_in < 4 && p.nk / (t.p_in * 2) >= 2) t.p_in *= 2;
-        else if (p.nk >= 4 && p.tiles <= kMaxTiles) t.p_out = p.s.p_out * 2;
-        else if (t.p_in < 16 && p.nk / (t.p_in * 2) >= 1) t.p_in *= 2;
+        if (t.p_in < 16 && (p.nk + 2 * t.p_in - 1) / (2 * t.p_in) >= 1) t.p_in *= 2;
+        else if (p.nk >= 2 && p.tiles <= kMaxTiles) t.p_out = p.s.p_out + 1;
         else break;
-        p = make_plan(fmt, N, K, batch, ffn, t);
+        Plan q = make_plan(fmt, N, K, batch, ffn, t);
+        if (q.s.p_out == p.s.p_out && q.s.p_in == p.s.p_in) break;
+        p = q;
     }
     // explicit overrides (tuning sweeps)
     const int op = g_over_pin.load(), oq = g_over_pout.load(), onr = g_over_nr.load();
     if (op || oq || onr) {
         Shape t = p.s;
         if (op) t.p_in = op;
-        if (oq) t.p_out = std::max(oq, (nb + max_nk - 1) / max_nk);
+        if (oq) t.p_out = std::max(oq, p_lds);
         if (onr && !ffn) t.nr = onr;
         p = make_plan(fmt, N, K, batch, ffn, t);
     }
     if (p.s.p_out > 1 && p.tiles > kMaxTiles) {  // fall back: no split across workgroups
         Shape t = p.s;
-        t.p_out = (nb + max_nk - 1) / max_nk;
+        t.p_out = p_lds;
         p = make_plan(fmt, N, K, batch, ffn, t);
     }
     return p;

@@ -37,6 +37,10 @@
 
 namespace qd {
 
+// Target of the ring's loads past the end of a K-slice (covers every byte a
+// lane reads of superunit 0: 144, 212 or 340 bytes).
+__device__ __attribute__((aligned(256))) uint8_t g_zero_block[512];
+
 // LDS index of logical activation index k (16-byte skew every 64 floats).
 QD_DEV int xphys(int k) { return k + ((k >> 6) << 2); }
 // LDS floats per staged superunit per batch row.
@@ -204,11 +208,21 @@ QD_DEV float wave_sum(float v) {
     return v;
 }
 
+// Superunits of loads kept in flight ahead of the one being multiplied.
+template <int FMT, int B, int NR>
+constexpr int lookahead() {
+#ifdef QD_LOOKAHEAD
+    return QD_LOOKAHEAD;
+#else
+    return (B * NR <= 2) ? 2 : 1;
+#endif
+}
+
 // FMT: block format; B: batch rows (1..8); NR: row streams per lane group
 // (FFN: 2 = gate, up); FFN: fused gate/up/activation epilogue.
 template <int FMT, int B, int NR, bool FFN>
 __global__ __launch_bounds__(kThreads) void mv_kernel(MvArgs a) {
-    extern __shared__ float smem[];
+    extern __shared__ __attribute__((aligned(16))) float smem[];
     const int tid = threadIdx.x;
     const int c = tid & 3;
     const int grp = tid >> 2;
@@ -238,14 +252,18 @@ __global__ __launch_bounds__(kThreads) void mv_kernel(MvArgs a) {
         rowp[i] = ((FFN && i == 1) ? a.W1 : a.W0) + rr * a.row_bytes;
     }
 
-    // ---- first weight loads go out before the staging work
+    // ---- the first D superunits' loads go out before the staging work
     using Raw = typename RawOf<FMT>::T;
-    Raw cur[NR];
-    int t = t_beg + pi;
-    {
-        int t0 = min(t, t_end - 1);
+    constexpr int D = lookahead<FMT, B, NR>();
+    Raw buf[D + 1][NR];
+    const int t0 = t_beg + pi;
 #pragma unroll
-        for (int i = 0; i < NR; i++) load_unit<FMT>(cur[i], rowp[i], t0, c, a.nblk);
+    for (int d = 0; d < D; d++) {
+        const int td = t0 + d * p_in;
+        const bool live = td < t_end;
+#pragma unroll
+        for (int i = 0; i < NR; i++)
+            load_unit<FMT>(buf[d][i], live ? rowp[i] : g_zero_block, live ? td : 0, c, a.nblk);
     }
 
     // ---- inverse RMS of each batch row (RMS-norm fused into staging)
@@ -324,27 +342,38 @@ __global__ __launch_bounds__(kThreads) void mv_kernel(MvArgs a) {
     Q4Lane L4;
     if constexpr (FMT == kQ4K) L4 = q4k_lane(c);
 
-    for (; t < t_end; t += p_in) {
-        Raw nxt[NR];
-        const int tn = min(t + p_in, t_end - 1);
+    // Ring of D + 1 load buffers: while superunit t is being multiplied, the
+    // loads of t + p_in .. t + D*p_in are in flight.  The inner loop is fully
+    // unrolled so every buffer index is a compile-time constant (no register
+    // copies, no wait for loads issued in the same iteration).
+    for (int t = t0; t < t_end; t += (D + 1) * p_in) {
 #pragma unroll
-        for (int i = 0; i < NR; i++) load_unit<FMT>(nxt[i], rowp[i], tn, c, a.nblk);
-
-        const int tl = t - t_beg;
-        if constexpr (FMT == kQ4K) {
-            const float *xp = xl + xphys(kSuper * tl + 64 * c);
-            const float *sp = xsum + 8 * tl + 2 * c;
-            q4k_step<NR, B>(cur, xp, xstride, sp, sstride, L4, acc, acc2);
-        } else if constexpr (FMT == kQ6K) {
-            const int h = c >> 1, j = c & 1;
-            const int base = kSuper * tl + 128 * h + 16 * j;
-            q6k_step<NR, B>(cur, xl + xphys(base), xl + xphys(base + 32), xl + xphys(base + 64),
-                            xl + xphys(base + 96), xstride, j, acc);
-        } else {
-            q80_step<NR, B>(cur, xl + xphys(kSuper * tl + 64 * c), xstride, acc);
+        for (int s = 0; s <= D; s++) {
+            const int ts = t + s * p_in;
+            if (ts >= t_end) break;
+            // issued on every path so the wait counts are the same on every
+            // path; past the end of the slice it reads a small zero block that
+            // stays in cache instead of weight bytes
+            const int tl = ts + D * p_in;
+            const bool live = tl < t_end;
+#pragma unroll
+            for (int i = 0; i < NR; i++)
+                load_unit<FMT>(buf[(s + D) % (D + 1)][i], live ? rowp[i] : g_zero_block,
+                               live ? tl : 0, c, a.nblk);
+            const int tlo = ts - t_beg;
+            if constexpr (FMT == kQ4K) {
+                const float *xp = xl + xphys(kSuper * tlo + 64 * c);
+                const float *sp = xsum + 8 * tlo + 2 * c;
+                q4k_step<NR, B>(buf[s], xp, xstride, sp, sstride, L4, acc, acc2);
+            } else if constexpr (FMT == kQ6K) {
+                const int h = c >> 1, j = c & 1;
+                const int base = kSuper * tlo + 128 * h + 16 * j;
+                q6k_step<NR, B>(buf[s], xl + xphys(base), xl + xphys(base + 32),
+                                xl + xphys(base + 64), xl + xphys(base + 96), xstride, j, acc);
+            } else {
+                q80_step<NR, B>(buf[s], xl + xphys(kSuper * tlo + 64 * c), xstride, acc);
+            }
         }
-#pragma unroll
-        for (int i = 0; i < NR; i++) cur[i] = nxt[i];
     }
 
     // ---- combine per lane, then reduce over the 4 * p_in lanes of a row
@@ -394,6 +423,11 @@ __global__ __launch_bounds__(kThreads) void mv_kernel(MvArgs a) {
     }
 
     // ---- split-K: publish partials; the last workgroup of this row tile sums
+    // them in slice order.  Partials are written and read with device-scope
+    // atomic stores and loads (write-through / L2-bypassing accesses), so no
+    // cache-wide writeback is needed: each wave waits until its stores have
+    // completed, the workgroup synchronises, and only then bumps the tile's
+    // counter with a device-scope atomic.
     constexpr int NP = FFN ? 2 : 1;  // partial planes per batch row
     if (leader) {
 #pragma unroll
@@ -401,18 +435,20 @@ __global__ __launch_bounds__(kThreads) void mv_kernel(MvArgs a) {
             if (rvalid[i])
 #pragma unroll
                 for (int b = 0; b < B; b++)
-                    a.partials[(((int64_t)ks * B + b) * NP + (FFN ? i : 0)) * N + row[i]] = v[i][b];
+                    __hip_atomic_store(
+                        a.partials + (((int64_t)ks * B + b) * NP + (FFN ? i : 0)) * N + row[i],
+                        v[i][b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    __threadfence();
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's stores are complete
     __syncthreads();
     __shared__ int s_last;
     if (tid == 0) {
-        unsigned prev = atomicAdd(&a.counters[blockIdx.x], 1u);
+        unsigned prev = __hip_atomic_fetch_add(a.counters + blockIdx.x, 1u, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
         s_last = (prev == gridDim.y - 1) ? 1 : 0;
     }
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
     const int rows_here = FFN ? RS : RS * NR;
     const int64_t row0 = (int64_t)blockIdx.x * rows_here;
     for (int e = tid; e < rows_here * B; e += kThreads) {
@@ -433,7 +469,8 @@ __global__ __launch_bounds__(kThreads) void mv_kernel(MvArgs a) {
             a.y[(int64_t)b * N + r] = s0;
         }
     }
-    if (tid == 0) a.counters[blockIdx.x] = 0u;  // ready for the next call
+    if (tid == 0)  // ready for the next call
+        __hip_atomic_store(a.counters + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------ launchers ---
