@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "batch-1 k-quant GEMV µs and weight GB/s (% of HBM peak), Gemma-3-4B FFN"
 ROTATE_BYTES = 1 << 30
+FFN_WORKLOADS = ("gemma3_ffn", "gemma3_ffn_2k", "gemma4_ffn", "gemma4_ffn_2k", "gemma4_ffn_b8")
 
 
 def parse():
@@ -39,7 +40,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="gemma3_ffn",
-                   choices=["gemma3_ffn", "gemma4_ffn", "gemma4_ffn_b8", "lm_head_q4k",
+                   choices=["gemma3_ffn", "gemma3_ffn_2k", "gemma4_ffn", "gemma4_ffn_2k",
+                            "gemma4_ffn_b8", "lm_head_q4k",
                             "lm_head_q8_0", "down_q6k", "gate_up_q4k", "copy"])
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="approximate CPU time budget of the oracle baseline (0 = skip)")
@@ -87,8 +89,9 @@ class Workload:
         self.qd, self.torch, self.name = qd, torch, name
         t = lambda a: torch.from_numpy(a).to(dev)
         self.batch = 1
-        if name in ("gemma3_ffn", "gemma4_ffn", "gemma4_ffn_b8", "gate_up_q4k", "down_q6k"):
-            hidden, ff = (2560, 10240) if name in ("gemma3_ffn", "gate_up_q4k", "down_q6k") else (5376, 21504)
+        if name in FFN_WORKLOADS + ("gate_up_q4k", "down_q6k"):
+            hidden, ff = (2560, 10240) if name in ("gemma3_ffn", "gemma3_ffn_2k", "gate_up_q4k",
+                                                   "down_q6k") else (5376, 21504)
             self.batch = 8 if name == "gemma4_ffn_b8" else 1
             self.hidden, self.ff = hidden, ff
             mats = {}
@@ -106,6 +109,7 @@ class Workload:
             self.hin = t(synth.normal((self.batch, ff), seed, tensor_id=46))
             self.y = torch.empty((self.batch, hidden), device=dev)
             base = {k: t(v) for k, v in mats.items()}
+            self.hidden = hidden
         elif name in ("lm_head_q4k", "lm_head_q8_0"):
             fmt = "q4_k" if name == "lm_head_q4k" else "q8_0"
             self.fmt = fmt
@@ -126,7 +130,10 @@ class Workload:
     def alg_bytes(self):
         """(dominant kernel name, algorithmic bytes per launch of it)."""
         b, n = self.batch, self.name
-        if n in ("gemma3_ffn", "gemma4_ffn", "gemma4_ffn_b8", "gate_up_q4k"):
+        if n in ("gemma3_ffn", "gemma4_ffn"):
+            # the whole FFN is one kernel: all weights, x, norm weight, y
+            return "qffn_decode", self.weight_bytes + 4 * (2 * b * self.hidden + self.hidden)
+        if n in ("gemma3_ffn_2k", "gemma4_ffn_2k", "gemma4_ffn_b8", "gate_up_q4k"):
             w = 2 * self.ff * (self.hidden // 256) * 144
             return "qffn_gate_up_act", w + 4 * (b * self.hidden + self.hidden + b * self.ff)
         if n == "down_q6k":
@@ -139,7 +146,14 @@ class Workload:
         c = self.copies[self.i]
         self.i = (self.i + 1) % self.ncopy
         qd, n = self.qd, self.name
-        if n in ("gemma3_ffn", "gemma4_ffn", "gemma4_ffn_b8", "gate_up_q4k"):
+        if n in ("gemma3_ffn", "gemma4_ffn"):
+            if ev:
+                ev[0].record()
+            qd.qffn_decode("q4_k", c["gate"], c["up"], "q6_k", c["down"], self.x, self.nw, 1e-6,
+                           "gelu_tanh", y=self.y)
+            if ev:
+                ev[1].record()
+        elif n in ("gemma3_ffn_2k", "gemma4_ffn_2k", "gemma4_ffn_b8", "gate_up_q4k"):
             if ev:
                 ev[0].record()
             qd.qffn_gate_up_act("q4_k", c["gate"], c["up"], self.x, self.nw, 1e-6, "gelu_tanh", h=self.h)
@@ -285,8 +299,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": {
-                "gemma3_ffn": "Gemma-3-4B FFN decode step, batch 1: RMS-norm + fused gate/up Q4_K "
-                              "10240x2560 + GELU-tanh, then down Q6_K 2560x10240",
+                "gemma3_ffn": "Gemma-3-4B FFN decode step, batch 1: RMS-norm + gate/up Q4_K "
+                              "10240x2560 + GELU-tanh + down Q6_K 2560x10240, one qffn_decode launch",
             }.get(args.workload, args.workload),
             "batch": wl.batch,
             "weight_bytes_per_step": wl.weight_bytes,

@@ -9,6 +9,7 @@ library is not built, or a tensor is not on the GPU, the call raises.
 Entry points (same names as the C ABI):
     qgemv_q4k, qgemv_q6k, qgemv_q8_0, qgemv        y = W x, batch 1..8
     qffn_gate_up_act                               h = act(Wg xn) * (Wu xn)
+    qffn_decode                                    y = Wd h (whole FFN, one launch)
     qgemm_prefill, qgemm_prefill_gate_up_act       bf16 MFMA prefill GEMMs
     qdequant, qdequant_bf16                        decoded weights (tests)
 """
@@ -47,11 +48,13 @@ SIGNATURES = {
     "qgemv_q8_0": (_I, [_P, _P, _P, _I64, _I64, _I, _P]),
     "qgemv": (_I, [_I, _P, _P, _P, _I64, _I64, _I, _P]),
     "qffn_gate_up_act": (_I, [_I, _P, _P, _P, _P, _F, _I, _P, _P, _P, _I64, _I64, _I, _P]),
+    "qffn_decode": (_I, [_I, _P, _P, _I, _P, _P, _P, _F, _I, _P, _P, _I64, _I64, _I, _P]),
     "qgemm_prefill": (_I, [_I, _P, _P, _P, _I64, _I64, _I64, _P]),
     "qgemm_prefill_gate_up_act": (_I, [_I, _P, _P, _P, _I, _P, _P, _P, _I64, _I64, _I64, _P]),
     "qdequant": (_I, [_I, _P, _P, _I64, _I64, _P]),
     "qdequant_bf16": (_I, [_I, _P, _P, _I64, _I64, _P]),
     "qd_set_launch_override": (_I, [_I, _I, _I]),
+    "qd_set_ffn_override": (_I, [_I, _I, _I]),
 }
 
 _lock = threading.Lock()
@@ -188,6 +191,28 @@ def qffn_gate_up_act(fmt, Wg: torch.Tensor, Wu: torch.Tensor, x: torch.Tensor,
     return h
 
 
+def qffn_decode(fmt_gu, Wg: torch.Tensor, Wu: torch.Tensor, fmt_down, Wd: torch.Tensor,
+                x: torch.Tensor, norm_w: torch.Tensor | None = None, eps: float = 1e-6,
+                act="gelu_tanh", y: torch.Tensor | None = None,
+                h_out: torch.Tensor | None = None) -> torch.Tensor:
+    """y = Wd (act(Wg xn) * (Wu xn)): the decode FFN of one layer."""
+    fg, fd = _fmt(fmt_gu), _fmt(fmt_down)
+    K = x.shape[-1]
+    batch = 1 if x.dim() == 1 else x.shape[0]
+    N = _rows(fg, Wg, K)
+    if _rows(fg, Wu, K) != N or _rows(fd, Wd, N) != K:
+        raise ValueError("gate/up must be N_ff x K and down K x N_ff")
+    if y is None:
+        y = torch.empty_like(x)
+    nw = _dev(norm_w, "norm_w", torch.float32) if norm_w is not None else None
+    hp = _dev(h_out, "h_out", torch.float32) if h_out is not None else None
+    st = lib().qffn_decode(fg, _dev(Wg, "Wg", torch.uint8), _dev(Wu, "Wu", torch.uint8), fd,
+                           _dev(Wd, "Wd", torch.uint8), _dev(x, "x", torch.float32), nw, float(eps),
+                           _act(act), _dev(y, "y", torch.float32), hp, N, K, batch, _stream())
+    _check("qffn_decode", st)
+    return y
+
+
 def qgemm_prefill(fmt, W: torch.Tensor, X: torch.Tensor, Y: torch.Tensor | None = None) -> torch.Tensor:
     """Y = X bf16(W)^T.  X: bf16 bits as int16/uint16 or torch.bfloat16 [M, K]."""
     f = _fmt(fmt)
@@ -242,6 +267,11 @@ def qdequant_bf16(fmt, W: torch.Tensor, K: int, out: torch.Tensor | None = None)
     st = lib().qdequant_bf16(f, _dev(W, "W", torch.uint8), _dev(out, "out", out.dtype), N, K, _stream())
     _check("qdequant_bf16", st)
     return out
+
+
+def set_ffn_override(p_in_a: int = 0, p_in_b: int = 0, p_out_b: int = 0):
+    """Force qffn_decode's launch shape for tuning sweeps (0 = automatic)."""
+    _check("qd_set_ffn_override", lib().qd_set_ffn_override(p_in_a, p_in_b, p_out_b))
 
 
 def set_launch_override(p_in: int = 0, p_out: int = 0, nr: int = 0):

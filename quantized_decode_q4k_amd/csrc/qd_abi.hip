@@ -53,9 +53,11 @@ bool overlap(const void *p, size_t n, const void *q, size_t m) {
 
 // ------------------------------------------------------- launch shapes ---
 std::atomic<int> g_over_pin{0}, g_over_pout{0}, g_over_nr{0};
+std::atomic<int> g_ffn_pin_a{0}, g_ffn_pin_b{0}, g_ffn_pout_b{0};
 
 constexpr int kTargetWorkgroups = 400;   // enough to keep every CU streaming
 constexpr int kMaxTiles = 1 << 16;       // split-K counters per workspace
+constexpr int kCtlSlots = qd::kFfnCtlWords;  // leading counters: the fused FFN's control block
 
 int lds_units_max(int fmt, int batch) {
     // largest nk whose staging fits the per-workgroup LDS budget
@@ -144,11 +146,11 @@ qd_status get_workspace(hipStream_t st, size_t need_floats, Workspace *out) {
         float *p = nullptr;
         unsigned *c = nullptr;
         if (hipMalloc(&p, n * sizeof(float)) != hipSuccess) return QD_ENOMEM;
-        if (hipMalloc(&c, kMaxTiles * sizeof(unsigned)) != hipSuccess) {
+        if (hipMalloc(&c, (kMaxTiles + kCtlSlots) * sizeof(unsigned)) != hipSuccess) {
             (void)hipFree(p);
             return QD_ENOMEM;
         }
-        if (hipMemsetAsync(c, 0, kMaxTiles * sizeof(unsigned), st) != hipSuccess) {
+        if (hipMemsetAsync(c, 0, (kMaxTiles + kCtlSlots) * sizeof(unsigned), st) != hipSuccess) {
             (void)hipFree(p);
             (void)hipFree(c);
             return QD_ELAUNCH;
@@ -178,7 +180,7 @@ qd_status check_shape(int fmt, int64_t N, int64_t K, int batch) {
 
 qd_status run_mv(int fmt, bool ffn, const void *W0, const void *W1, const float *x,
                  const float *norm_w, float eps, int act, float *y, float *g_out, float *u_out,
-                 int64_t N, int64_t K, int batch, void *stream) {
+                 int64_t N, int64_t K, int batch, void *stream, size_t ws_offset = 0) {
     qd_status st = check_shape(fmt, N, K, batch);
     if (st != QD_OK) return st;
     if (!W0 || !x || !y || (ffn && !W1)) return QD_EINVAL;
@@ -220,13 +222,133 @@ qd_status run_mv(int fmt, bool ffn, const void *W0, const void *W1, const float 
     a.eps = eps;
     if (p.s.p_out > 1) {
         Workspace w;
-        const size_t need = (size_t)p.s.p_out * batch * (ffn ? 2 : 1) * N;
+        const size_t need = ws_offset + (size_t)p.s.p_out * batch * (ffn ? 2 : 1) * N;
         qd_status ws = get_workspace(hs, need, &w);
         if (ws != QD_OK) return ws;
-        a.partials = w.partials;
-        a.counters = w.counters;
+        a.partials = w.partials + ws_offset;
+        a.counters = w.counters + kCtlSlots;
     }
     hipError_t e = qd::launch_gemv(fmt, batch, ffn, a, p.s, hs);
+    return e == hipSuccess ? QD_OK : QD_ELAUNCH;
+}
+
+// y = Wd (act(Wg xn) * (Wu xn)) in one launch when the shapes allow it,
+// else as the two calls qffn_gate_up_act + qgemv on the same stream.
+qd_status run_ffn_decode(int fmt_gu, const void *Wg, const void *Wu, int fmt_d, const void *Wd,
+                         const float *x, const float *norm_w, float eps, int act, float *y,
+                         float *h_out, int64_t N_ff, int64_t K, int batch, void *stream) {
+    qd_status st = check_shape(fmt_gu, N_ff, K, batch);
+    if (st != QD_OK) return st;
+    st = check_shape(fmt_d, K, N_ff, batch);
+    if (st != QD_OK) return st;
+    if (!Wg || !Wu || !Wd || !x || !y) return QD_EINVAL;
+    if (act != QD_ACT_GELU_TANH && act != QD_ACT_SILU) return QD_EINVAL;
+    if (!aligned(Wg, 16) || !aligned(Wu, 16) || !aligned(Wd, 16) || !aligned(x, 16)) return QD_EALIGN;
+    if ((norm_w && !aligned(norm_w, 16)) || !aligned(y, 4)) return QD_EALIGN;
+    if (h_out && !aligned(h_out, 16)) return QD_EALIGN;
+    const size_t xbytes = (size_t)batch * K * 4, hbytes = (size_t)batch * N_ff * 4;
+    const void *ins[5] = {Wg, Wu, Wd, x, norm_w};
+    const size_t insz[5] = {(size_t)N_ff * row_bytes(fmt_gu, K), (size_t)N_ff * row_bytes(fmt_gu, K),
+                            (size_t)K * row_bytes(fmt_d, N_ff), xbytes, (size_t)K * 4};
+    for (int i = 0; i < 5; i++) {
+        if (overlap(y, xbytes, ins[i], insz[i]) || (h_out && overlap(h_out, hbytes, ins[i], insz[i])))
+            return QD_EINVAL;
+    }
+    if (h_out && overlap(y, xbytes, h_out, hbytes)) return QD_EINVAL;
+
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    const size_t h_floats = h_out ? 0 : (((size_t)batch * N_ff + 63) / 64) * 64;
+
+    // phase A: gate/up with the whole of K in one workgroup
+    Plan pa = choose_plan(fmt_gu, N_ff, K, batch, true);
+    const int nb_a = (int)((K + qd::kSuper - 1) / qd::kSuper);
+    const bool fits = lds_units_max(fmt_gu, batch) >= nb_a;
+    // phase B: down tiles wait for their slice of h and stage it from
+    // memory, so h is split into slices of about five superunits and each
+    // workgroup takes many rows of one slice (h read once per row tile)
+    Plan pb;
+    {
+        const int nb_b = (int)((N_ff + qd::kSuper - 1) / qd::kSuper);
+        const int nk_b = std::min(lds_units_max(fmt_d, batch), 5);
+        Shape t{2, (nb_b + nk_b - 1) / nk_b, 1};
+        if (g_ffn_pin_b.load()) t.p_in = g_ffn_pin_b.load();
+        if (g_ffn_pout_b.load())
+            t.p_out = std::max(g_ffn_pout_b.load(), (nb_b + lds_units_max(fmt_d, batch) - 1) /
+                                                        lds_units_max(fmt_d, batch));
+        pb = make_plan(fmt_d, K, N_ff, batch, false, t);
+    }
+    const bool fused = fits && qd::ffn_fused_supported(fmt_gu, fmt_d) &&
+                       pb.s.p_out * 64 <= kCtlSlots && pb.tiles <= kMaxTiles;
+    if (!fused) {
+        // size the workspace once for h and both calls' split-K partials, so
+        // that neither call reallocates it under h
+        const Plan qa = choose_plan(fmt_gu, N_ff, K, batch, true);
+        const Plan qb = choose_plan(fmt_d, K, N_ff, batch, false);
+        const size_t need_a = qa.s.p_out > 1 ? (size_t)qa.s.p_out * batch * 2 * N_ff : 0;
+        const size_t need_b = qb.s.p_out > 1 ? (size_t)qb.s.p_out * batch * K : 0;
+        float *h = h_out;
+        if (h_floats + std::max(need_a, need_b) > 0) {
+            Workspace w;
+            st = get_workspace(hs, h_floats + std::max(need_a, need_b), &w);
+            if (st != QD_OK) return st;
+            if (!h) h = w.partials;
+        }
+        st = run_mv(fmt_gu, true, Wg, Wu, x, norm_w, eps, act, h, nullptr, nullptr, N_ff, K, batch,
+                    stream, h_floats);
+        if (st != QD_OK) return st;
+        return run_mv(fmt_d, false, Wd, nullptr, h, nullptr, 0.f, 0, y, nullptr, nullptr, K, N_ff,
+                      batch, stream, h_floats);
+    }
+    {
+        Shape t = pa.s;
+        t.p_out = 1;
+        if (g_ffn_pin_a.load()) t.p_in = g_ffn_pin_a.load();
+        pa = make_plan(fmt_gu, N_ff, K, batch, true, t);
+    }
+    Workspace w;
+    const size_t need = h_floats + (size_t)pb.s.p_out * batch * K;
+    st = get_workspace(hs, need, &w);
+    if (st != QD_OK) return st;
+    float *h = h_out ? h_out : w.partials;
+
+    qd::FfnArgs f{};
+    qd::MvArgs &a = f.a;
+    a.W0 = static_cast<const uint8_t *>(Wg);
+    a.W1 = static_cast<const uint8_t *>(Wu);
+    a.x = x;
+    a.norm_w = norm_w;
+    a.y = h;
+    a.N = N_ff;
+    a.K = K;
+    a.row_bytes = row_bytes(fmt_gu, K);
+    a.nb = nb_a;
+    a.nblk = (int)(K / block_elems(fmt_gu));
+    a.nk = pa.nk;
+    a.p_in = pa.s.p_in;
+    a.p_out = 1;
+    a.act = act;
+    a.eps = eps;
+    qd::MvArgs &b = f.b;
+    b.W0 = static_cast<const uint8_t *>(Wd);
+    b.x = h;
+    b.y = y;
+    b.partials = w.partials + h_floats;
+    b.counters = w.counters + kCtlSlots;
+    b.N = K;
+    b.K = N_ff;
+    b.row_bytes = row_bytes(fmt_d, N_ff);
+    b.nb = (int)((N_ff + qd::kSuper - 1) / qd::kSuper);
+    b.nblk = (int)(N_ff / block_elems(fmt_d));
+    b.nk = pb.nk;
+    b.p_in = pb.s.p_in;
+    b.p_out = pb.s.p_out;
+    f.ctl = w.counters;
+    f.nA = (int)pa.tiles;
+    f.nBx = (int)pb.tiles;
+    f.pB = pb.s.p_out;
+    f.rowsA = qd::kGroups / pa.s.p_in;
+    f.sliceRows = pb.nk * qd::kSuper;
+    hipError_t e = qd::launch_ffn(fmt_gu, fmt_d, batch, f, hs);
     return e == hipSuccess ? QD_OK : QD_ELAUNCH;
 }
 
@@ -279,6 +401,13 @@ qd_status qffn_gate_up_act(qd_format fmt, const void *Wg, const void *Wu, const 
     return run_mv(fmt, true, Wg, Wu, x, norm_w, eps, act, h, g_out, u_out, N_ff, K, batch, stream);
 }
 
+qd_status qffn_decode(qd_format fmt_gu, const void *Wg, const void *Wu, qd_format fmt_down,
+                      const void *Wd, const float *x, const float *norm_w, float eps, qd_act act,
+                      float *y, float *h_out, int64_t N_ff, int64_t K, int batch, void *stream) {
+    return run_ffn_decode(fmt_gu, Wg, Wu, fmt_down, Wd, x, norm_w, eps, act, y, h_out, N_ff, K,
+                          batch, stream);
+}
+
 qd_status qdequant(qd_format fmt, const void *W, float *out, int64_t N, int64_t K, void *stream) {
     qd_status st = check_shape(fmt, N, K, 1);
     if (st != QD_OK) return st;
@@ -317,6 +446,15 @@ qd_status qgemm_prefill_gate_up_act(qd_format fmt, const void *Wg, const void *W
     (void)fmt; (void)Wg; (void)Wu; (void)X; (void)act; (void)H; (void)g_out; (void)u_out;
     (void)M; (void)N_ff; (void)K; (void)stream;
     return QD_EUNSUPPORTED;
+}
+
+qd_status qd_set_ffn_override(int p_in_a, int p_in_b, int p_out_b) {
+    auto ok = [](int v) { return v == 0 || v == 1 || v == 2 || v == 4 || v == 8 || v == 16; };
+    if (!ok(p_in_a) || !ok(p_in_b) || p_out_b < 0 || p_out_b > kCtlSlots / 64) return QD_EINVAL;
+    g_ffn_pin_a.store(p_in_a);
+    g_ffn_pin_b.store(p_in_b);
+    g_ffn_pout_b.store(p_out_b);
+    return QD_OK;
 }
 
 qd_status qd_set_launch_override(int p_in, int p_out, int nr) {

@@ -35,6 +35,8 @@
 //    FFN, applies the GELU-tanh or SiLU product).
 #include "qd_decode.h"
 
+#include <algorithm>
+
 namespace qd {
 
 // Target of the ring's loads past the end of a K-slice (covers every byte a
@@ -218,11 +220,48 @@ constexpr int lookahead() {
 #endif
 }
 
-// FMT: block format; B: batch rows (1..8); NR: row streams per lane group
-// (FFN: 2 = gate, up); FFN: fused gate/up/activation epilogue.
-template <int FMT, int B, int NR, bool FFN>
-__global__ __launch_bounds__(kThreads) void mv_kernel(MvArgs a) {
-    extern __shared__ __attribute__((aligned(16))) float smem[];
+// Where a tile's activations come from and where its outputs go.
+enum : int {
+    kPlain = 0,     // ordinary loads / stores
+    kCoherent = 1,  // device-scope loads / stores: data produced or consumed by
+                    // other workgroups of the same launch (fused FFN)
+};
+
+template <int YM>
+QD_DEV void store_out(float *p, float v) {
+    if constexpr (YM == kCoherent) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *p = v;
+}
+
+// Bounded wait of thread 0 until *ctr >= target (device-scope loads).  The
+// bound is a safety net: the producers of every counter waited on here are
+// already running when the wait starts, so it ends long before the bound.
+QD_DEV void wait_counter(const unsigned *ctr, unsigned target) {
+    for (int it = 0; it < (1 << 20); it++) {
+        if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) return;
+        __builtin_amdgcn_s_sleep(4);
+    }
+}
+
+// One workgroup tile: rows [bx * rows_per_wg, ...) over K-slice ks of
+// p_out.  FMT: block format; B: batch rows (1..8); NR: row streams per lane
+// group (FFN: 2 = gate, up); FFN: fused gate/up/activation epilogue.
+// XM / YM: kPlain or kCoherent activation loads / output stores.  If
+// wait_ctr is set, thread 0 waits for *wait_ctr >= wait_target after the
+// first weight loads are issued and before x is staged.
+// Wait hook of a tile that consumes data produced in the same launch: wait
+// until *ready >= target; then count this workgroup in *arrived, and the
+// last of `readers` workgroups resets both counters for the next launch.
+struct WaitSpec {
+    unsigned *ready = nullptr;
+    unsigned target = 0;
+    unsigned *arrived = nullptr;
+    unsigned readers = 0;
+};
+
+template <int FMT, int B, int NR, bool FFN, int XM, int YM>
+QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out, float *smem,
+                    const WaitSpec ws = WaitSpec()) {
     const int tid = threadIdx.x;
     const int c = tid & 3;
     const int grp = tid >> 2;
@@ -230,7 +269,6 @@ __global__ __launch_bounds__(kThreads) void mv_kernel(MvArgs a) {
     const int rs = grp / p_in;            // row slot in this workgroup
     const int pi = grp - rs * p_in;       // K-interleave index
     const int RS = kGroups / p_in;        // row slots per workgroup
-    const int ks = blockIdx.y;            // K-slice of this workgroup
     const int t_beg = ks * a.nk;
     const int t_end = min(a.nb, t_beg + a.nk);
     const int xstride = a.nk * kSuperPhys;
@@ -240,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void mv_kernel(MvArgs a) {
     float *red = xsum + (FMT == kQ4K ? B * sstride : 0);  // [4 waves][B], then [B]
 
     // ---- rows of this lane group
-    const int64_t slot = (int64_t)blockIdx.x * RS + rs;
+    const int64_t slot = (int64_t)bx * RS + rs;
     int64_t row[NR];
     bool rvalid[NR];
     const uint8_t *rowp[NR];
@@ -252,7 +290,33 @@ __global__ __launch_bounds__(kThreads) void mv_kernel(MvArgs a) {
         rowp[i] = ((FFN && i == 1) ? a.W1 : a.W0) + rr * a.row_bytes;
     }
 
-    // ---- the first D superunits' loads go out before the staging work
+    const int64_t K = a.K;
+    const int F = a.nk * (kSuper / 4);   // float4 per batch row in this slice
+    const int64_t k0 = (int64_t)t_beg * kSuper;
+    const bool norm = a.norm_w != nullptr;
+
+    // ---- small activation slices are loaded into registers (with the norm
+    // weight) before any weight load is issued, so they return ahead of the
+    // weight stream instead of queueing behind it
+    constexpr int kXr = 6;  // float4 per thread held this way
+    const bool early = (XM == kPlain) && (B * F <= kXr * kThreads);
+    float4 xr[kXr], wr[kXr];
+#pragma unroll
+    for (int i = 0; i < kXr; i++) {
+        xr[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        wr[i] = make_float4(1.f, 1.f, 1.f, 1.f);
+        const int f = tid + kThreads * i;
+        if (early && f < B * F) {
+            const int b = f / F;
+            const int64_t k = k0 + 4 * (f - b * F);
+            if (k < K) {
+                xr[i] = *reinterpret_cast<const float4 *>(a.x + (int64_t)b * K + k);
+                if (norm) wr[i] = *reinterpret_cast<const float4 *>(a.norm_w + k);
+            }
+        }
+    }
+
+    // ---- the first D superunits' loads
     using Raw = typename RawOf<FMT>::T;
     constexpr int D = lookahead<FMT, B, NR>();
     Raw buf[D + 1][NR];
@@ -266,67 +330,139 @@ __global__ __launch_bounds__(kThreads) void mv_kernel(MvArgs a) {
             load_unit<FMT>(buf[d][i], live ? rowp[i] : g_zero_block, live ? td : 0, c, a.nblk);
     }
 
+    if (ws.ready != nullptr) {
+        if (tid == 0) {
+            wait_counter(ws.ready, ws.target);
+            const unsigned n = __hip_atomic_fetch_add(ws.arrived, 1u, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+            if (n == ws.readers - 1) {  // every reader has seen the count
+                __hip_atomic_store(ws.ready, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(ws.arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        __syncthreads();
+    }
+
     // ---- inverse RMS of each batch row (RMS-norm fused into staging)
-    const int64_t K = a.K;
     float inv_rms[B];
 #pragma unroll
     for (int b = 0; b < B; b++) inv_rms[b] = 1.0f;
-    if (a.norm_w != nullptr) {
+    if (norm) {
         const int wave = tid >> 6;
+        float ss[B];
+#pragma unroll
+        for (int b = 0; b < B; b++) ss[b] = 0.f;
+        if (early && t_beg == 0 && t_end == a.nb) {
+            // the registers hold all of x
+#pragma unroll
+            for (int i = 0; i < kXr; i++) {
+                const int f = tid + kThreads * i;
+                const int bi = f / F;
+                float q = fmaf(xr[i].x, xr[i].x, 0.f);
+                q = fmaf(xr[i].y, xr[i].y, q);
+                q = fmaf(xr[i].z, xr[i].z, q);
+                q = fmaf(xr[i].w, xr[i].w, q);
+#pragma unroll
+                for (int b = 0; b < B; b++)
+                    if (b == bi) ss[b] += q;
+            }
+        } else {
+#pragma unroll
+            for (int b = 0; b < B; b++) {
+                const float *xb = a.x + (int64_t)b * K;
+                for (int64_t k = 4 * tid; k < K; k += 4 * kThreads) {
+                    float4 v = *reinterpret_cast<const float4 *>(xb + k);
+                    ss[b] = fmaf(v.x, v.x, ss[b]);
+                    ss[b] = fmaf(v.y, v.y, ss[b]);
+                    ss[b] = fmaf(v.z, v.z, ss[b]);
+                    ss[b] = fmaf(v.w, v.w, ss[b]);
+                }
+            }
+        }
 #pragma unroll
         for (int b = 0; b < B; b++) {
-            const float *xb = a.x + (int64_t)b * K;
-            float ss = 0.f;
-            for (int64_t k = 4 * tid; k < K; k += 4 * kThreads) {
-                float4 v = *reinterpret_cast<const float4 *>(xb + k);
-                ss = fmaf(v.x, v.x, ss);
-                ss = fmaf(v.y, v.y, ss);
-                ss = fmaf(v.z, v.z, ss);
-                ss = fmaf(v.w, v.w, ss);
-            }
-            ss = wave_sum(ss);
-            if ((tid & 63) == 0) red[wave * B + b] = ss;
+            const float w = wave_sum(ss[b]);
+            if ((tid & 63) == 0) red[wave * B + b] = w;
         }
         __syncthreads();
 #pragma unroll
         for (int b = 0; b < B; b++) {
-            float ss = (red[b] + red[B + b]) + (red[2 * B + b] + red[3 * B + b]);
-            inv_rms[b] = 1.0f / sqrtf(ss / (float)K + a.eps);
+            float sq = (red[b] + red[B + b]) + (red[2 * B + b] + red[3 * B + b]);
+            inv_rms[b] = 1.0f / sqrtf(sq / (float)K + a.eps);
         }
     }
 
     // ---- stage x[b][t_beg*256 ...) into LDS (zero past K)
-    {
-        const int F = a.nk * (kSuper / 4);   // float4 per batch row in this slice
-        const int64_t k0 = (int64_t)t_beg * kSuper;
-        for (int f = tid; f < B * F; f += kThreads) {
-            int b = f / F;
-            int f4 = f - b * F;
-            int64_t k = k0 + 4 * f4;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (k < K) {
-                v = *reinterpret_cast<const float4 *>(a.x + (int64_t)b * K + k);
-                if (a.norm_w != nullptr) {
-                    float4 w = *reinterpret_cast<const float4 *>(a.norm_w + k);
-                    float ir = inv_rms[0];
+    if constexpr (XM == kCoherent) {
+        // x was written by other workgroups of this launch: device-scope
+        // dword loads, consecutive lanes on consecutive dwords (coalesced)
+        for (int e = tid; e < B * 4 * F; e += kThreads) {
+            const int b = e / (4 * F);
+            const int kk = e - b * 4 * F;
+            const int64_t k = k0 + kk;
+            float v = 0.f;
+            if (k < K) v = __hip_atomic_load(a.x + (int64_t)b * K + k, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+            xl[b * xstride + xphys(kk)] = v;
+        }
+        if constexpr (FMT == kQ4K) {
+            __syncthreads();
+            for (int e = tid; e < B * 8 * a.nk; e += kThreads) {
+                const int b = e / (8 * a.nk);
+                const int j = e - b * 8 * a.nk;  // 32-run index
+                const float *q = xl + b * xstride + xphys(32 * j);
+                float sacc = 0.f;
 #pragma unroll
-                    for (int bb = 1; bb < B; bb++)
-                        if (bb == b) ir = inv_rms[bb];
-                    v.x = v.x * ir * w.x;
-                    v.y = v.y * ir * w.y;
-                    v.z = v.z * ir * w.z;
-                    v.w = v.w * ir * w.w;
+                for (int m = 0; m < 8; m++) {
+                    const float4 w4 = *reinterpret_cast<const float4 *>(q + 4 * m);
+                    sacc += (w4.x + w4.y) + (w4.z + w4.w);
                 }
+                xsum[b * sstride + j] = sacc;
+            }
+        }
+    } else {
+        // normalise (if asked) and store one float4 of x; for Q4_K also the
+        // sum of each 32-run (8 consecutive float4 sit in 8 consecutive
+        // lanes of one wave, and every lane of a wave takes part)
+        auto stage_one = [&](int f, float4 v, float4 w) {
+            const int b = f / F;
+            const int f4 = f - b * F;
+            if (norm) {
+                float ir = inv_rms[0];
+#pragma unroll
+                for (int bb = 1; bb < B; bb++)
+                    if (bb == b) ir = inv_rms[bb];
+                v.x = v.x * ir * w.x;
+                v.y = v.y * ir * w.y;
+                v.z = v.z * ir * w.z;
+                v.w = v.w * ir * w.w;
             }
             *reinterpret_cast<float4 *>(xl + b * xstride + xphys(4 * f4)) = v;
             if constexpr (FMT == kQ4K) {
-                // sum of each 32-run of x: 8 consecutive float4 live in 8
-                // consecutive lanes of one wave
-                float s = (v.x + v.y) + (v.z + v.w);
-                s += __shfl_xor(s, 1);
-                s += __shfl_xor(s, 2);
-                s += __shfl_xor(s, 4);
-                if ((tid & 7) == 0) xsum[b * sstride + (f4 >> 3)] = s;
+                float sm = (v.x + v.y) + (v.z + v.w);
+                sm += __shfl_xor(sm, 1);
+                sm += __shfl_xor(sm, 2);
+                sm += __shfl_xor(sm, 4);
+                if ((tid & 7) == 0) xsum[b * sstride + (f4 >> 3)] = sm;
+            }
+        };
+        if (early) {
+#pragma unroll
+            for (int i = 0; i < kXr; i++) {
+                const int f = tid + kThreads * i;
+                if (f < B * F) stage_one(f, xr[i], wr[i]);  // uniform per wave
+            }
+        } else {
+            for (int f = tid; f < B * F; f += kThreads) {
+                const int b = f / F;
+                const int64_t k = k0 + 4 * (f - b * F);
+                float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+                float4 w = make_float4(1.f, 1.f, 1.f, 1.f);
+                if (k < K) {
+                    v = *reinterpret_cast<const float4 *>(a.x + (int64_t)b * K + k);
+                    if (norm) w = *reinterpret_cast<const float4 *>(a.norm_w + k);
+                }
+                stage_one(f, v, w);
             }
         }
     }
@@ -399,14 +535,14 @@ __global__ __launch_bounds__(kThreads) void mv_kernel(MvArgs a) {
     const bool leader = (pi == 0) && (c == 0);
     const int64_t N = a.N;
 
-    if (gridDim.y == 1) {
+    if (p_out == 1) {
         if (leader) {
             if constexpr (FFN) {
                 if (rvalid[0]) {
 #pragma unroll
                     for (int b = 0; b < B; b++) {
                         float gv = v[0][b], uv = v[1][b];
-                        a.y[(int64_t)b * N + row[0]] = act_apply(a.act, gv) * uv;
+                        store_out<YM>(a.y + (int64_t)b * N + row[0], act_apply(a.act, gv) * uv);
                         if (a.g_out) a.g_out[(int64_t)b * N + row[0]] = gv;
                         if (a.u_out) a.u_out[(int64_t)b * N + row[0]] = uv;
                     }
@@ -416,7 +552,7 @@ __global__ __launch_bounds__(kThreads) void mv_kernel(MvArgs a) {
                 for (int i = 0; i < NR; i++)
                     if (rvalid[i])
 #pragma unroll
-                        for (int b = 0; b < B; b++) a.y[(int64_t)b * N + row[i]] = v[i][b];
+                        for (int b = 0; b < B; b++) store_out<YM>(a.y + (int64_t)b * N + row[i], v[i][b]);
             }
         }
         return;
@@ -439,38 +575,88 @@ __global__ __launch_bounds__(kThreads) void mv_kernel(MvArgs a) {
                         a.partials + (((int64_t)ks * B + b) * NP + (FFN ? i : 0)) * N + row[i],
                         v[i][b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's stores are complete
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);  // keep the stores above the wait
+    __builtin_amdgcn_s_waitcnt(0);            // this wave's stores are complete
     __syncthreads();
     __shared__ int s_last;
     if (tid == 0) {
-        unsigned prev = __hip_atomic_fetch_add(a.counters + blockIdx.x, 1u, __ATOMIC_RELAXED,
+        unsigned prev = __hip_atomic_fetch_add(a.counters + bx, 1u, __ATOMIC_RELAXED,
                                                __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (prev == gridDim.y - 1) ? 1 : 0;
+        s_last = (prev == (unsigned)p_out - 1) ? 1 : 0;
     }
     __syncthreads();
     if (!s_last) return;
     const int rows_here = FFN ? RS : RS * NR;
-    const int64_t row0 = (int64_t)blockIdx.x * rows_here;
+    const int64_t row0 = (int64_t)bx * rows_here;
     for (int e = tid; e < rows_here * B; e += kThreads) {
         const int b = e / rows_here;
         const int64_t r = row0 + (e - b * rows_here);
         if (r >= N) continue;
         float s0 = 0.f, s1 = 0.f;
-        for (int k = 0; k < (int)gridDim.y; k++) {
+        for (int k = 0; k < p_out; k++) {
             const float *p = a.partials + (((int64_t)k * B + b) * NP) * N + r;
             s0 += __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if constexpr (FFN) s1 += __hip_atomic_load(p + N, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         if constexpr (FFN) {
-            a.y[(int64_t)b * N + r] = act_apply(a.act, s0) * s1;
+            store_out<YM>(a.y + (int64_t)b * N + r, act_apply(a.act, s0) * s1);
             if (a.g_out) a.g_out[(int64_t)b * N + r] = s0;
             if (a.u_out) a.u_out[(int64_t)b * N + r] = s1;
         } else {
-            a.y[(int64_t)b * N + r] = s0;
+            store_out<YM>(a.y + (int64_t)b * N + r, s0);
         }
     }
     if (tid == 0)  // ready for the next call
-        __hip_atomic_store(a.counters + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.counters + bx, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int FMT, int B, int NR, bool FFN>
+__global__ __launch_bounds__(kThreads) void mv_kernel(MvArgs a) {
+    extern __shared__ __attribute__((aligned(16))) float smem[];
+    mv_tile<FMT, B, NR, FFN, kPlain, kPlain>(a, blockIdx.x, blockIdx.y, gridDim.y, smem);
+}
+
+// ------------------------------------------------------ fused decode FFN ---
+// One launch for y = Wd (act(Wg xn) * (Wu xn)).  Workgroups [0, nA) are
+// gate/up row tiles (phase A): they publish their slice of h with
+// device-scope stores and count themselves done in the h-slice they belong
+// to.  The remaining workgroups are down-projection tiles (phase B), ordered
+// slice by slice: each issues its first weight loads, waits until every
+// phase-A tile of its h-slice is done, stages that slice of h with
+// device-scope loads and runs as a split-K GEMV tile.  Workgroups are
+// dispatched in index order on each XCD, so every phase-A workgroup is
+// resident or finished before a phase-B workgroup can hold a slot on the
+// same XCD: a waiting workgroup only waits on work that is already running
+// (and the wait is bounded).  Counters live on separate 128-byte lines; the
+// last phase-B reader of a slice resets them for the next launch.
+constexpr int kCtlStride = 32;  // unsigned per counter (one 128-byte line)
+
+template <int FA, int FB, int B>
+__global__ __launch_bounds__(kThreads) void ffn_kernel(FfnArgs f) {
+    extern __shared__ __attribute__((aligned(16))) float smem[];
+    const int t = (int)blockIdx.x;
+    if (t < f.nA) {
+        mv_tile<FA, B, 2, true, kPlain, kCoherent>(f.a, t, 0, 1, smem);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);  // keep the h stores above the wait
+        __builtin_amdgcn_s_waitcnt(0);            // this wave's h stores are complete
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const int slice = (t * f.rowsA) / f.sliceRows;
+            __hip_atomic_fetch_add(f.ctl + (2 * slice) * kCtlStride, 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+    } else {
+        const int j = t - f.nA;
+        const int ks = j / f.nBx;
+        const int bx = j - ks * f.nBx;
+        const int per = f.sliceRows / f.rowsA;  // phase-A tiles per h-slice
+        WaitSpec ws;
+        ws.ready = f.ctl + (2 * ks) * kCtlStride;
+        ws.target = (unsigned)(min(f.nA, (ks + 1) * per) - ks * per);
+        ws.arrived = f.ctl + (2 * ks + 1) * kCtlStride;
+        ws.readers = (unsigned)f.nBx;
+        mv_tile<FB, B, 1, false, kCoherent, kPlain>(f.b, bx, ks, f.pB, smem, ws);
+    }
 }
 
 // ------------------------------------------------------------ launchers ---
@@ -508,6 +694,36 @@ static hipError_t launch_f(const MvArgs &a, int batch, bool ffn, int nr, dim3 gr
     case 8: return launch_fb<FMT, 8>(a, ffn, nr, grid, st);
     default: return hipErrorInvalidValue;
     }
+}
+
+template <int FA, int FB>
+static hipError_t launch_ffn_f(const FfnArgs &f, int batch, size_t lds, unsigned grid,
+                               hipStream_t st) {
+#define QD_FFN(Bv)                                                                       \
+    case Bv:                                                                             \
+        hipLaunchKernelGGL((ffn_kernel<FA, FB, Bv>), dim3(grid), dim3(kThreads), lds, st, f); \
+        break;
+    switch (batch) {
+        QD_FFN(1) QD_FFN(2) QD_FFN(3) QD_FFN(4) QD_FFN(5) QD_FFN(6) QD_FFN(7) QD_FFN(8)
+    default: return hipErrorInvalidValue;
+    }
+#undef QD_FFN
+    return hipGetLastError();
+}
+
+bool ffn_fused_supported(int fmt_a, int fmt_b) {
+    return (fmt_a == kQ4K && (fmt_b == kQ6K || fmt_b == kQ4K)) || (fmt_a == kQ80 && fmt_b == kQ80);
+}
+
+hipError_t launch_ffn(int fmt_a, int fmt_b, int batch, FfnArgs f, hipStream_t st) {
+    f.a.p_out = 1;
+    const size_t lds = std::max(mv_lds_bytes(fmt_a, batch, f.a.nk), mv_lds_bytes(fmt_b, batch, f.b.nk));
+    const unsigned grid = (unsigned)(f.nA + f.nBx * f.pB);
+    if ((size_t)f.pB * 2 * kCtlStride > (size_t)kFfnCtlWords) return hipErrorInvalidValue;
+    if (fmt_a == kQ4K && fmt_b == kQ6K) return launch_ffn_f<kQ4K, kQ6K>(f, batch, lds, grid, st);
+    if (fmt_a == kQ4K && fmt_b == kQ4K) return launch_ffn_f<kQ4K, kQ4K>(f, batch, lds, grid, st);
+    if (fmt_a == kQ80 && fmt_b == kQ80) return launch_ffn_f<kQ80, kQ80>(f, batch, lds, grid, st);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemv(int fmt, int batch, bool ffn, MvArgs a, Shape s, hipStream_t st) {

@@ -50,6 +50,22 @@ struct Shape {
 size_t mv_lds_bytes(int fmt, int batch, int nk);
 hipError_t launch_gemv(int fmt, int batch, bool ffn, MvArgs a, Shape s, hipStream_t st);
 
+// Fused decode FFN (qd_gemv.hip): phase A = gate/up/act tiles writing h,
+// phase B = down-projection split-K tiles reading h.
+struct FfnArgs {
+    MvArgs a;           // phase A: W0 = gate, W1 = up, x, norm_w, y = h
+    MvArgs b;           // phase B: W0 = down, x = h, y = out, partials, counters
+    unsigned *ctl;      // per h-slice s: phase-A tiles done, phase-B readers (one line each)
+    int nA;             // phase-A tiles
+    int nBx;            // phase-B row tiles
+    int pB;             // phase-B K-slices
+    int rowsA;          // h rows per phase-A tile
+    int sliceRows;      // h rows per phase-B K-slice (multiple of 256)
+};
+constexpr int kFfnCtlWords = 4096;  // control words the fused FFN may use
+bool ffn_fused_supported(int fmt_a, int fmt_b);
+hipError_t launch_ffn(int fmt_a, int fmt_b, int batch, FfnArgs f, hipStream_t st);
+
 // Dequantisers (qd_dequant.hip).
 hipError_t launch_dequant(int fmt, const uint8_t *W, float *out, uint16_t *out_bf16,
                           int64_t N, int64_t K, hipStream_t st);

@@ -336,3 +336,64 @@ def test_config_gemma4_31b_ffn(qd, batch):
     rows = np.unique(np.concatenate([np.arange(0, 256), np.arange(21504 - 256, 21504),
                                      np.arange(0, 21504, 41)]))
     check_ffn(qd, "q4_k", 5376, 21504, batch, "gelu_tanh", f"gemma4-31b b{batch}", rows=rows)
+
+
+# ------------------------------------------------- whole decode FFN (one call) ---
+
+def check_ffn_decode(qd, fg, fd, hidden, ff, batch, act, tag, with_h=True, reps=2):
+    Wg = synth.quant_weights(fg, ff, hidden, SEED, tensor_id=51)
+    Wu = synth.quant_weights(fg, ff, hidden, SEED, tensor_id=52)
+    Wd = synth.quant_weights(fd, hidden, ff, SEED, tensor_id=53)
+    x = synth.normal((batch, hidden), SEED, tensor_id=54)
+    nw = synth.normal((hidden,), SEED, tensor_id=55, mean=1.0, std=0.1)
+    xn32 = oracle.rmsnorm(x, nw, 1e-6).astype(np.float32)
+    g64, Sg = oracle.gemv(fg, Wg, xn32, ff, hidden)
+    u64, Su = oracle.gemv(fg, Wu, xn32, ff, hidden)
+    aid = oracle.ACT_GELU_TANH if act == "gelu_tanh" else oracle.ACT_SILU
+    href = oracle.act_vec(aid, g64) * u64
+    tol = h_tolerance(g64, u64, Sg, Su, aid)
+    args = [dev(a) for a in (Wg, Wu, Wd, x, nw)]
+    first = None
+    for rep in range(reps):   # the control block must be reset for the next call
+        say(f"ffn_decode {tag} {fg}->{fd} hidden={hidden} ff={ff} batch={batch} rep={rep}")
+        h = torch.empty((batch, ff), device="cuda") if with_h else None
+        y = qd.qffn_decode(fg, args[0], args[1], fd, args[2], args[3], args[4], 1e-6, act, h_out=h)
+        y = y.cpu().numpy()
+        if with_h:
+            hh = h.cpu().numpy()
+            err = np.abs(hh - href)
+            assert (err <= tol).all(), f"{tag} h: worst {np.max(err / tol):.3f} of tolerance"
+            yref, Sy = oracle.gemv(fd, Wd, hh, hidden, ff)
+            assert_bound(f"{tag} y", y, yref, Sy)
+        else:
+            # y against the all-oracle chain: the bound of the down GEMV on the
+            # exact h, widened by the h tolerance carried through |Wd|
+            yref, Sy = oracle.gemv(fd, Wd, href.astype(np.float32), hidden, ff)
+            wabs = np.abs(oracle.dequant(fd, Wd, ff)).astype(np.float64)
+            slack = tol @ wabs.T
+            err = np.abs(y - yref)
+            assert (err <= 1e-4 * Sy + 1e-6 + slack).all(), f"{tag} y vs chain"
+        if first is None:
+            first = y.copy()
+        else:
+            assert np.array_equal(first.view(np.uint32), y.view(np.uint32)), "not deterministic"
+
+
+@pytest.mark.parametrize("fg,fd,act,batch", [
+    ("q4_k", "q6_k", "gelu_tanh", 1), ("q4_k", "q6_k", "silu", 3), ("q4_k", "q4_k", "silu", 1),
+    ("q8_0", "q8_0", "gelu_tanh", 2), ("q6_k", "q6_k", "gelu_tanh", 1)])
+def test_ffn_decode_small(qd, fg, fd, act, batch):
+    check_ffn_decode(qd, fg, fd, 512, 1536, batch, act, "small")
+
+
+def test_ffn_decode_without_h_out(qd):
+    check_ffn_decode(qd, "q4_k", "q6_k", 512, 1024, 1, "gelu_tanh", "no-h", with_h=False)
+
+
+def test_ffn_decode_gemma3(qd):
+    check_ffn_decode(qd, "q4_k", "q6_k", 2560, 10240, 1, "gelu_tanh", "gemma3-4b", reps=3)
+
+
+def test_ffn_decode_gemma4_31b_batch8_falls_back(qd):
+    """batch 8 x K = 5376 does not fit one workgroup's LDS: two launches."""
+    check_ffn_decode(qd, "q4_k", "q6_k", 5376, 21504, 8, "gelu_tanh", "gemma4-31b b8", reps=1)
