@@ -175,28 +175,41 @@ qd_status qffn_decode(qd_format fmt_gu, const void *Wg, const void *Wu, qd_forma
                       float *y, float *h_out, int64_t N_ff, int64_t K, int batch, void *stream);
 
 /*
- * Y = X W^T for a multi-token prefill (dequantise to bf16, MFMA, fp32
- * accumulate).  dotLLM PR #320's tiled Q8_0 GEMM for prefill is the pages'
- * instance; here any of the three formats.
+ * Y = X W^T for a multi-token prefill: the weights are dequantised to bf16
+ * and contracted on the bf16 matrix cores with fp32 accumulation.  dotLLM
+ * PR #320 (Vulkan backend section) adds a tiled Q8_0 GEMM for multi-token
+ * prefill, which is the pages' instance; here any of the three formats.
  *
- *   W   N x K quantized matrix
- *   X   bf16 bits [M][K], row-major
- *   Y   fp32 [M][N], row-major; Y[m][n] = sum_k bf16(w[n][k]) * X[m][k]
- *       where bf16(w) is the round-to-nearest-even bfloat16 of the fp32
- *       dequantised weight.
+ *   W   N x K quantized matrix (rows of qd_row_bytes(fmt, K) bytes), device,
+ *       16-byte aligned
+ *   X   bf16 bits [M][K], row-major, device, 16-byte aligned
+ *   Y   fp32 [M][N], row-major, device, 4-byte aligned; written, never read
+ *       Y[m][n] = sum_k bf16(w[n][k]) * X[m][k], where bf16(w) is the
+ *       round-to-nearest-even bfloat16 of the exact fp32 dequantised weight
+ *   M   tokens, 1 <= M and M * K < 2^31
  * Accuracy: |Y - Y_exact| <= 1e-4 * sum_k |bf16(w) X| + 1e-6.
+ * Errors: QD_ESHAPE (M, N or K out of range, K not a multiple of the block),
+ * QD_EINVAL (null pointer, Y overlapping W or X), QD_EALIGN, QD_ENOMEM
+ * (split-K workspace), QD_ELAUNCH.  Shapes with few output tiles split K
+ * across workgroups through the per-stream workspace; partial sums are
+ * added in a fixed order, so results are deterministic.
  */
 qd_status qgemm_prefill(qd_format fmt, const void *W, const uint16_t *X,
                         float *Y, int64_t M, int64_t N, int64_t K,
                         void *stream);
 
 /*
- * H = bf16( act(X Wg^T) * (X Wu^T) ) for a prefill FFN: two prefill GEMMs
- * sharing X, with the activation product in the epilogue; H is rounded to
- * bf16 (nearest-even) so it can feed qgemm_prefill for the down projection.
+ * H = bf16( act(X Wg^T) * (X Wu^T) ) for a prefill FFN: the two prefill
+ * GEMMs share X and the activation product is taken in fp32 in the
+ * epilogue (GELU-tanh geglu of the larql Gemma 3 table, or SiLU), then
+ * rounded to bf16 (nearest even) so that H feeds qgemm_prefill for the down
+ * projection.
  *
- *   X   bf16 [M][K];  H  bf16 bits [M][N_ff]
+ *   Wg, Wu  N_ff x K quantized matrices, device, 16-byte aligned
+ *   X       bf16 bits [M][K], device, 16-byte aligned
+ *   H       bf16 bits [M][N_ff], device, 2-byte aligned
  *   g_out, u_out  optional fp32 [M][N_ff] gate and up products (NULL = no)
+ * Errors as qgemm_prefill, plus QD_EINVAL for an unknown act.
  */
 qd_status qgemm_prefill_gate_up_act(qd_format fmt, const void *Wg,
                                     const void *Wu, const uint16_t *X,
@@ -228,6 +241,13 @@ qd_status qd_set_launch_override(int p_in, int p_out, int nr);
  * p_in of the gate/up tiles, p_in and K-slices of the down tiles.
  */
 qd_status qd_set_ffn_override(int p_in_a, int p_in_b, int p_out_b);
+
+/*
+ * Tile override of the prefill GEMMs (0 = automatic): tm = 2 or 4 (tokens
+ * per workgroup / 32), splits = K-splits across workgroups (1..1024; more
+ * than the K-tiles of 128 weights is clamped).
+ */
+qd_status qd_set_gemm_override(int tm, int splits);
 
 #ifdef __cplusplus
 }

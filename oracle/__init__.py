@@ -247,3 +247,20 @@ def gemm_bf16(fmt, W: np.ndarray, X: np.ndarray, N: int, K: int,
     if rc != 0:
         raise ValueError("orc_gemm_bf16 failed")
     return Y, S
+
+
+def gemm_bf16_cols(fmt, W: np.ndarray, X: np.ndarray, N: int, K: int, cols):
+    """(Y64, S) of Y = X bf16(W)^T for the listed weight rows only: [M, len(cols)]."""
+    fmt_id = _fmt(fmt)
+    rb = row_bytes(fmt_id, K)
+    W = np.ascontiguousarray(W, dtype=np.uint8).reshape(N, rb)
+    X = np.ascontiguousarray(X, dtype=np.uint16)
+    M = X.shape[0]
+    cols = [int(c) for c in cols]
+    Y = np.empty((M, len(cols)), dtype=np.float64)
+    S = np.empty((M, len(cols)), dtype=np.float64)
+    for j, n in enumerate(cols):
+        y1, s1 = gemm_bf16(fmt_id, W[n:n + 1], X, 1, K)
+        Y[:, j] = y1[:, 0]
+        S[:, j] = s1[:, 0]
+    return Y, S

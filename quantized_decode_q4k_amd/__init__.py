@@ -55,6 +55,7 @@ SIGNATURES = {
     "qdequant_bf16": (_I, [_I, _P, _P, _I64, _I64, _P]),
     "qd_set_launch_override": (_I, [_I, _I, _I]),
     "qd_set_ffn_override": (_I, [_I, _I, _I]),
+    "qd_set_gemm_override": (_I, [_I, _I]),
 }
 
 _lock = threading.Lock()
@@ -272,6 +273,11 @@ def qdequant_bf16(fmt, W: torch.Tensor, K: int, out: torch.Tensor | None = None)
 def set_ffn_override(p_in_a: int = 0, p_in_b: int = 0, p_out_b: int = 0):
     """Force qffn_decode's launch shape for tuning sweeps (0 = automatic)."""
     _check("qd_set_ffn_override", lib().qd_set_ffn_override(p_in_a, p_in_b, p_out_b))
+
+
+def set_gemm_override(tm: int = 0, splits: int = 0):
+    """Prefill tile override (0 = automatic)."""
+    _check("qd_set_gemm_override", lib().qd_set_gemm_override(tm, splits))
 
 
 def set_launch_override(p_in: int = 0, p_out: int = 0, nr: int = 0):

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <atomic>
 #include <map>
 #include <mutex>
@@ -352,6 +353,96 @@ qd_status run_ffn_decode(int fmt_gu, const void *Wg, const void *Wu, int fmt_d, 
     return e == hipSuccess ? QD_OK : QD_ELAUNCH;
 }
 
+// ------------------------------------------------------------ prefill ---
+std::atomic<int> g_gemm_tm{0}, g_gemm_splits{0};
+constexpr int kGemmTargetWorkgroups = 256;  // one resident workgroup per CU (LDS and registers)
+constexpr int kGemmMinKTiles = 8;          // K-tiles per split, at least
+
+struct GemmPlan {
+    int tm, m_tiles, n_tiles, kt_total, kt_per_split, splits;
+};
+
+GemmPlan gemm_plan(bool ffn, int64_t M, int64_t N, int64_t K) {
+    GemmPlan p;
+    p.tm = g_gemm_tm.load() ? g_gemm_tm.load() : (M > 64 ? 4 : 2);
+    const int64_t bm = 32 * p.tm, bn = ffn ? qd::kGemmCols / 2 : qd::kGemmCols;
+    p.m_tiles = (int)((M + bm - 1) / bm);
+    p.n_tiles = (int)((N + bn - 1) / bn);
+    p.kt_total = (int)((K + qd::kGemmKT - 1) / qd::kGemmKT);
+    const int64_t tiles = (int64_t)p.m_tiles * p.n_tiles;
+    int s = 1;
+    if (tiles <= kMaxTiles) {
+        // split K only while the splits still fit in one round of resident
+        // workgroups: a partial tile costs a write and a read of 32*tm*256
+        // floats, and splits beyond one round only add that traffic
+        // (measured: Gemma-4-31B down, 84 tiles: 3 splits 300 us, 4: 412, 7: 502)
+        while (tiles * (s + 1) <= kGemmTargetWorkgroups && p.kt_total / (s + 1) >= kGemmMinKTiles)
+            s++;
+        if (g_gemm_splits.load()) s = std::min(g_gemm_splits.load(), p.kt_total);
+    }
+    p.kt_per_split = (p.kt_total + s - 1) / s;
+    p.splits = (p.kt_total + p.kt_per_split - 1) / p.kt_per_split;  // every split non-empty
+    return p;
+}
+
+qd_status run_gemm(int fmt, bool ffn, const void *Wg, const void *Wu, const uint16_t *X, int act,
+                   float *Y, uint16_t *H, float *g_out, float *u_out, int64_t M, int64_t N,
+                   int64_t K, void *stream) {
+    qd_status st = check_shape(fmt, N, K, 1);
+    if (st != QD_OK) return st;
+    if (M < 1 || M * K > INT32_MAX) return QD_ESHAPE;
+    if (!Wg || !X || (ffn ? (!Wu || !H) : !Y)) return QD_EINVAL;
+    if (ffn && act != QD_ACT_GELU_TANH && act != QD_ACT_SILU) return QD_EINVAL;
+    if (!aligned(Wg, 16) || (Wu && !aligned(Wu, 16)) || !aligned(X, 16)) return QD_EALIGN;
+    if ((Y && !aligned(Y, 4)) || (H && !aligned(H, 2)) || (g_out && !aligned(g_out, 4)) ||
+        (u_out && !aligned(u_out, 4)))
+        return QD_EALIGN;
+    const size_t wbytes = (size_t)N * row_bytes(fmt, K), xbytes = (size_t)M * K * 2;
+    const size_t f32bytes = (size_t)M * N * 4, hbytes = (size_t)M * N * 2;
+    const void *outs[4] = {ffn ? nullptr : Y, H, g_out, u_out};
+    const size_t osz[4] = {f32bytes, hbytes, f32bytes, f32bytes};
+    for (int i = 0; i < 4; i++) {
+        if (!outs[i]) continue;
+        if (overlap(outs[i], osz[i], X, xbytes) || overlap(outs[i], osz[i], Wg, wbytes) ||
+            (Wu && overlap(outs[i], osz[i], Wu, wbytes)))
+            return QD_EINVAL;
+        for (int j = i + 1; j < 4; j++)
+            if (outs[j] && overlap(outs[i], osz[i], outs[j], osz[j])) return QD_EINVAL;
+    }
+
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    const GemmPlan p = gemm_plan(ffn, M, N, K);
+    qd::GemmArgs a{};
+    a.Wg = static_cast<const uint8_t *>(Wg);
+    a.Wu = static_cast<const uint8_t *>(Wu);
+    a.X = X;
+    a.Y = ffn ? nullptr : Y;
+    a.H = H;
+    a.g_out = g_out;
+    a.u_out = u_out;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.row_bytes = row_bytes(fmt, K);
+    a.nblk = (int)(K / block_elems(fmt));
+    a.kt_total = p.kt_total;
+    a.kt_per_split = p.kt_per_split;
+    a.splits = p.splits;
+    a.m_tiles = p.m_tiles;
+    a.n_tiles = p.n_tiles;
+    a.act = act;
+    if (p.splits > 1) {
+        Workspace w;
+        const size_t need = (size_t)p.m_tiles * p.n_tiles * p.splits * (32 * p.tm) * qd::kGemmCols;
+        st = get_workspace(hs, need, &w);
+        if (st != QD_OK) return st;
+        a.partials = w.partials;
+        a.counters = w.counters + kCtlSlots;
+    }
+    hipError_t e = qd::launch_gemm(fmt, ffn, p.tm, a, hs);
+    return e == hipSuccess ? QD_OK : QD_ELAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -435,17 +526,22 @@ qd_status qdequant_bf16(qd_format fmt, const void *W, uint16_t *out, int64_t N, 
 
 qd_status qgemm_prefill(qd_format fmt, const void *W, const uint16_t *X, float *Y, int64_t M,
                         int64_t N, int64_t K, void *stream) {
-    (void)fmt; (void)W; (void)X; (void)Y; (void)M; (void)N; (void)K; (void)stream;
-    return QD_EUNSUPPORTED;
+    return run_gemm(fmt, false, W, nullptr, X, 0, Y, nullptr, nullptr, nullptr, M, N, K, stream);
 }
 
 qd_status qgemm_prefill_gate_up_act(qd_format fmt, const void *Wg, const void *Wu,
                                     const uint16_t *X, qd_act act, uint16_t *H, float *g_out,
                                     float *u_out, int64_t M, int64_t N_ff, int64_t K,
                                     void *stream) {
-    (void)fmt; (void)Wg; (void)Wu; (void)X; (void)act; (void)H; (void)g_out; (void)u_out;
-    (void)M; (void)N_ff; (void)K; (void)stream;
-    return QD_EUNSUPPORTED;
+    return run_gemm(fmt, true, Wg, Wu, X, act, nullptr, H, g_out, u_out, M, N_ff, K, stream);
+}
+
+qd_status qd_set_gemm_override(int tm, int splits) {
+    if (tm != 0 && tm != 2 && tm != 4) return QD_EINVAL;
+    if (splits < 0 || splits > 1024) return QD_EINVAL;
+    g_gemm_tm.store(tm);
+    g_gemm_splits.store(splits);
+    return QD_OK;
 }
 
 qd_status qd_set_ffn_override(int p_in_a, int p_in_b, int p_out_b) {

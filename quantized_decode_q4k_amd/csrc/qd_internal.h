@@ -70,19 +70,30 @@ hipError_t launch_ffn(int fmt_a, int fmt_b, int batch, FfnArgs f, hipStream_t st
 hipError_t launch_dequant(int fmt, const uint8_t *W, float *out, uint16_t *out_bf16,
                           int64_t N, int64_t K, hipStream_t st);
 
-// Prefill GEMM (qd_prefill.hip).
+// Prefill GEMM (qd_prefill.hip).  A workgroup owns 32*tm tokens by 256
+// output columns (plain: 256 weight rows; FFN: 128 rows of gate and of up)
+// over K-tiles [kt_per_split*ks, ...) of 128 weights.
+constexpr int kGemmKT = 128;          // weights per K-tile
+constexpr int kGemmCols = 256;        // accumulator columns per workgroup
 struct GemmArgs {
-    const uint8_t *Wg;      // weights (or gate for the fused FFN)
-    const uint8_t *Wu;      // up (fused FFN) or nullptr
+    const uint8_t *Wg;      // weights (or gate for the FFN variant)
+    const uint8_t *Wu;      // up (FFN variant) or nullptr
     const uint16_t *X;      // bf16 [M][K]
     float *Y;               // fp32 [M][N] (plain GEMM)
-    uint16_t *H;            // bf16 [M][N] (fused FFN)
-    float *g_out;
+    uint16_t *H;            // bf16 [M][N] (FFN variant)
+    float *g_out;           // optional fp32 [M][N] (FFN variant)
     float *u_out;
+    float *partials;        // split-K: tiles * splits * 32*tm * kGemmCols floats
+    unsigned *counters;     // split-K: one per output tile, zero between calls
     int64_t M, N, K;
     int64_t row_bytes;
+    int nblk;               // quant blocks per row
+    int kt_total;           // ceil(K / kGemmKT)
+    int kt_per_split;
+    int splits;
+    int m_tiles, n_tiles;
     int act;
 };
-hipError_t launch_gemm(int fmt, bool ffn, const GemmArgs &a, hipStream_t st);
+hipError_t launch_gemm(int fmt, bool ffn, int tm, const GemmArgs &a, hipStream_t st);
 
 }  // namespace qd

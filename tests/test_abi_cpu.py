@@ -106,6 +106,51 @@ def test_dequant_validation():
     assert L.qdequant_bf16(1, A16, A16b, 4, 300, None) == 2
 
 
+@pytest.mark.parametrize("args,status", [
+    ((0, 0, A16b, A16c, 8, 4, 256, None), 1),           # null W
+    ((0, A16, 0, A16c, 8, 4, 256, None), 1),            # null X
+    ((0, A16, A16b, 0, 8, 4, 256, None), 1),            # null Y
+    ((0, A16, A16b, A16c, 0, 4, 256, None), 2),         # M = 0
+    ((0, A16, A16b, A16c, 8, 0, 256, None), 2),         # N = 0
+    ((0, A16, A16b, A16c, 8, 4, 320, None), 2),         # K not a multiple of 256
+    ((2, A16, A16b, A16c, 8, 4, 48, None), 2),          # Q8_0 K not a multiple of 32
+    ((0, A16, A16b, A16c, 1 << 24, 4, 256, None), 2),   # M * K >= 2^31
+    ((0, A16 + 4, A16b, A16c, 8, 4, 256, None), 3),     # W misaligned
+    ((0, A16, A16b + 8, A16c, 8, 4, 256, None), 3),     # X misaligned (needs 16)
+    ((0, A16, A16b, A16c + 2, 8, 4, 256, None), 3),     # Y misaligned
+    ((0, A16, A16b, A16b + 256, 8, 4, 256, None), 1),   # Y overlaps X
+    ((0, A16, A16b, A16 + 64, 8, 4, 256, None), 1),     # Y overlaps W
+    ((7, A16, A16b, A16c, 8, 4, 256, None), 1),         # unknown format
+])
+def test_prefill_validation(args, status):
+    _, L = _lib()
+    assert L.qgemm_prefill(*args) == status
+
+
+def test_prefill_gate_up_validation():
+    _, L = _lib()
+    f = L.qgemm_prefill_gate_up_act
+    U = A16 + 0x8000
+    # null up, null H
+    assert f(0, A16, 0, A16b, 0, A16c, None, None, 8, 4, 256, None) == 1
+    assert f(0, A16, U, A16b, 0, 0, None, None, 8, 4, 256, None) == 1
+    # unknown activation
+    assert f(0, A16, U, A16b, 3, A16c, None, None, 8, 4, 256, None) == 1
+    # H misaligned (2 bytes), g_out misaligned (4 bytes)
+    assert f(0, A16, U, A16b, 0, A16c + 1, None, None, 8, 4, 256, None) == 3
+    assert f(0, A16, U, A16b, 0, A16c, A16c + 0x1002, None, 8, 4, 256, None) == 3
+    # H overlapping g_out, u_out overlapping X
+    assert f(0, A16, U, A16b, 0, A16c, A16c + 16, None, 8, 4, 256, None) == 1
+    assert f(0, A16, U, A16b, 0, A16c, None, A16b + 64, 8, 4, 256, None) == 1
+
+
+def test_gemm_override_validation():
+    _, L = _lib()
+    assert L.qd_set_gemm_override(3, 0) == 1
+    assert L.qd_set_gemm_override(0, -1) == 1
+    assert L.qd_set_gemm_override(0, 0) == 0
+
+
 def test_launch_override_validation():
     _, L = _lib()
     assert L.qd_set_launch_override(3, 0, 0) == 1
