@@ -249,6 +249,13 @@ qd_status qd_set_ffn_override(int p_in_a, int p_in_b, int p_out_b);
  */
 qd_status qd_set_gemm_override(int tm, int splits);
 
+/*
+ * Shape override of the streaming GEMV path (0 = automatic): workgroups per
+ * CU (1..8; LDS is divided between them) and ring depth pd (2..8 steps of 16
+ * superunits in flight per wave).
+ */
+qd_status qd_set_stream_override(int wg_per_cu, int pd);
+
 #ifdef __cplusplus
 }
 #endif

@@ -179,6 +179,67 @@ qd_status check_shape(int fmt, int64_t N, int64_t K, int batch) {
     return QD_OK;
 }
 
+// ------------------------------------------------- streaming GEMV plan ---
+constexpr int kCUs = 256;                  // MI355X compute units
+constexpr size_t kLdsPerCU = 160 * 1024;    // gfx950 LDS per CU
+constexpr int kStreamMaxWait = 63;          // vmcnt limit: copies in flight per wave
+std::atomic<int> g_stream_wpc{0}, g_stream_pd{0};  // tuning overrides (0 = automatic)
+constexpr int64_t kStreamMinK = 8192;       // automatic use of the streaming kernel
+
+// Streaming-kernel launch with wpc workgroups per CU, or false if the LDS
+// layout does not fit.
+bool stream_plan_wpc(int fmt, bool ffn, int64_t N, int64_t K, int batch, const float *norm_w,
+                     int wpc, qd::StreamArgs *a, unsigned *grid, size_t *lds) {
+    const int64_t rb = row_bytes(fmt, K);
+    const int G = (int)std::min<int64_t>(N, (int64_t)kCUs * wpc);
+    const size_t budget = kLdsPerCU / wpc;
+    a->N = N;
+    a->K = K;
+    a->row_bytes = rb;
+    a->mat_bytes = N * rb;
+    a->nb = (int)(K / qd::kSuper);
+    a->rows_base = (int)(N / G);
+    a->rows_extra = (int)(N % G);
+    a->units_max = (a->rows_base + (a->rows_extra > 0 ? 1 : 0)) * a->nb;
+    a->norm_w = norm_w;
+    const int copies = qd::stream_copies_per_step(fmt, ffn);
+    if (copies <= 0) return false;
+    // a shallow ring: copies queued beyond a few steps block the issuing
+    // wave without adding bandwidth (measured: depth 2 best)
+    const int pd_max = std::min(g_stream_pd.load() ? g_stream_pd.load() : 2, kStreamMaxWait / copies);
+    for (int pd = pd_max; pd >= 2; pd--) {
+        const size_t bytes = qd::stream_layout(fmt, batch, ffn, a->nb, a->units_max, pd, a);
+        if (bytes <= budget) {
+            a->pd = pd;
+            *grid = (unsigned)G;
+            *lds = bytes;
+            return true;
+        }
+    }
+    return false;
+}
+
+// Launch of the streaming kernel for this shape, or false where the
+// register-streaming kernel is used instead: batch > 2, Q8_0 rows of partial
+// superunits, a matrix whose size is not a multiple of 16 bytes, an LDS
+// layout that does not fit, and (unless overridden) shapes where it is the
+// slower of the two.  Measured on MI355X (graph replay): on Gemma-3 down
+// (K = 10240) the LDS ring at two workgroups per CU is level with or
+// slightly ahead of the register path (11.1-11.5 us vs 11.7); it loses when
+// only one workgroup per CU fits (Gemma-4 down, K = 21504: 37.4 vs 29.1)
+// and on K = 2560 (gate/up 13.5 vs 12.9, lm_head 91 vs 74), where its LDS
+// reads of x per superunit cost more than the prologue they save.
+bool stream_plan(int fmt, bool ffn, int64_t N, int64_t K, int batch, const float *norm_w,
+                 qd::StreamArgs *a, unsigned *grid, size_t *lds) {
+    if (batch > 2) return false;
+    if (K % qd::kSuper != 0) return false;
+    if ((N * row_bytes(fmt, K)) % 16 != 0) return false;
+    if (g_stream_wpc.load())
+        return stream_plan_wpc(fmt, ffn, N, K, batch, norm_w, g_stream_wpc.load(), a, grid, lds);
+    if (ffn || K < kStreamMinK) return false;
+    return stream_plan_wpc(fmt, ffn, N, K, batch, norm_w, 2, a, grid, lds);
+}
+
 qd_status run_mv(int fmt, bool ffn, const void *W0, const void *W1, const float *x,
                  const float *norm_w, float eps, int act, float *y, float *g_out, float *u_out,
                  int64_t N, int64_t K, int batch, void *stream, size_t ws_offset = 0) {
@@ -204,6 +265,24 @@ qd_status run_mv(int fmt, bool ffn, const void *W0, const void *W1, const float 
         return QD_EINVAL;
 
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    const bool forced = g_over_pin.load() || g_over_pout.load() || g_over_nr.load();
+    if (!forced) {
+        qd::StreamArgs sa{};
+        unsigned grid = 0;
+        size_t lds = 0;
+        if (stream_plan(fmt, ffn, N, K, batch, norm_w, &sa, &grid, &lds)) {
+            sa.W0 = static_cast<const uint8_t *>(W0);
+            sa.W1 = static_cast<const uint8_t *>(W1);
+            sa.x = x;
+            sa.y = y;
+            sa.g_out = g_out;
+            sa.u_out = u_out;
+            sa.act = act;
+            sa.eps = eps;
+            hipError_t e = qd::launch_stream(fmt, batch, ffn, sa, grid, lds, hs);
+            return e == hipSuccess ? QD_OK : QD_ELAUNCH;
+        }
+    }
     Plan p = choose_plan(fmt, N, K, batch, ffn);
     qd::MvArgs a{};
     a.W0 = static_cast<const uint8_t *>(W0);
@@ -550,6 +629,13 @@ qd_status qd_set_ffn_override(int p_in_a, int p_in_b, int p_out_b) {
     g_ffn_pin_a.store(p_in_a);
     g_ffn_pin_b.store(p_in_b);
     g_ffn_pout_b.store(p_out_b);
+    return QD_OK;
+}
+
+qd_status qd_set_stream_override(int wg_per_cu, int pd) {
+    if (wg_per_cu < 0 || wg_per_cu > 8 || pd < 0 || pd == 1 || pd > 8) return QD_EINVAL;
+    g_stream_wpc.store(wg_per_cu);
+    g_stream_pd.store(pd);
     return QD_OK;
 }
 

@@ -1,0 +1,558 @@
+// qd_gemv_stream.hip -- decode GEMV and fused gate/up with the weights
+// streamed through LDS (the default path for batch 1 and 2).
+//
+// Same products as qd_gemv.hip (y[b][n] = sum_k w[n][k] x[b][k], or the
+// fused act(Wg x) * (Wu x) of the larql Gemma 3 table), organised for the
+// small matrices of a decode step, whose time is set by how fast the whole
+// weight stream can be put in flight:
+//
+//  * One workgroup per CU, each owning a contiguous range of rows (row
+//    counts differ by at most one).  A row range is one contiguous byte
+//    range of the matrix, so the workgroup's weights are a single stream.
+//  * The stream is cut into steps of 16 superunits (256 weights each: one
+//    Q4_K or Q6_K block, eight Q8_0 blocks).  Wave w takes steps w, w+4, ...
+//    and copies each into a ring of its own in LDS with
+//    global_load_lds_dwordx4: 1 KB of consecutive bytes per instruction, no
+//    registers, several steps in flight while it decodes an earlier one.
+//  * Decoding reads a lane group's block (4 lanes per superunit, the lane
+//    split of the GEMV kernels) and its activations from LDS, and writes the
+//    superunit's partial sum to LDS.  After the stream, each row's partials
+//    are added in superunit order, so a result does not depend on the launch
+//    shape.
+//  * x is copied into LDS the same way (16-byte skew every 64 floats), then
+//    RMS-normalised in place; Q4_K also keeps the sum of every 32-run of x.
+// The copies are ordered by explicit waits (qd_lds.h).
+#include "qd_decode.h"
+#include "qd_lds.h"
+
+namespace qd {
+namespace {
+
+constexpr int kStepUnits = 16;  // superunits per step (one per lane group of a wave)
+constexpr int kWaves = kThreads / 64;
+
+template <int FMT>
+struct StreamFmt;
+template <>
+struct StreamFmt<kQ4K> {
+    static constexpr int UB = 144;   // bytes per superunit
+    static constexpr int NCH = 144;  // 16-byte chunks per step (steps start 16-byte aligned)
+};
+template <>
+struct StreamFmt<kQ6K> {
+    static constexpr int UB = 210;
+    static constexpr int NCH = 211;  // a step may start up to 14 bytes past a 16-byte boundary
+};
+template <>
+struct StreamFmt<kQ80> {
+    static constexpr int UB = 272;
+    static constexpr int NCH = 272;
+};
+
+template <int FMT>
+constexpr int copies_per_step() {
+    return (StreamFmt<FMT>::NCH + 63) / 64;
+}
+
+// Wait until at most n copies / loads of this wave are outstanding (n is
+// uniform; the immediate is chosen by a scalar branch).
+QD_DEV void vm_wait_n(int n) {
+    switch (n) {
+#define QD_VMW(i) case i: vm_wait<i>(); break;
+        QD_VMW(0) QD_VMW(1) QD_VMW(2) QD_VMW(3) QD_VMW(4) QD_VMW(5) QD_VMW(6) QD_VMW(7)
+        QD_VMW(8) QD_VMW(9) QD_VMW(10) QD_VMW(11) QD_VMW(12) QD_VMW(13) QD_VMW(14) QD_VMW(15)
+        QD_VMW(16) QD_VMW(17) QD_VMW(18) QD_VMW(19) QD_VMW(20) QD_VMW(21) QD_VMW(22) QD_VMW(23)
+        QD_VMW(24) QD_VMW(25) QD_VMW(26) QD_VMW(27) QD_VMW(28) QD_VMW(29) QD_VMW(30) QD_VMW(31)
+        QD_VMW(32) QD_VMW(33) QD_VMW(34) QD_VMW(35) QD_VMW(36) QD_VMW(37) QD_VMW(38) QD_VMW(39)
+        QD_VMW(40) QD_VMW(41) QD_VMW(42) QD_VMW(43) QD_VMW(44) QD_VMW(45) QD_VMW(46) QD_VMW(47)
+        QD_VMW(48) QD_VMW(49) QD_VMW(50) QD_VMW(51) QD_VMW(52) QD_VMW(53) QD_VMW(54) QD_VMW(55)
+        QD_VMW(56) QD_VMW(57) QD_VMW(58) QD_VMW(59) QD_VMW(60) QD_VMW(61) QD_VMW(62) QD_VMW(63)
+#undef QD_VMW
+    default: vm_wait<0>(); break;
+    }
+}
+
+// Logical activation index k -> LDS float index (16-byte skew every 64).
+QD_DEV int xphys(int k) { return k + ((k >> 6) << 2); }
+constexpr int kSuperPhys = kSuper + kSuper / 16;  // 272 floats per superunit
+
+// --------------------------------------------------------- block loads ---
+// One lane's share of a superunit from LDS (blk: the superunit's first byte
+// in the ring), into the register layouts of qd_decode.h.
+QD_DEV uint32_t lds32(const uint8_t *p) { return *reinterpret_cast<const uint32_t *>(p); }
+
+QD_DEV void lds_q4k(RawQ4K &r, const uint8_t *blk, int c) {
+    const uint4 h = *reinterpret_cast<const uint4 *>(blk);
+    const uint4 a = *reinterpret_cast<const uint4 *>(blk + 16 + 32 * c);
+    const uint4 b = *reinterpret_cast<const uint4 *>(blk + 32 + 32 * c);
+    r.h[0] = h.x; r.h[1] = h.y; r.h[2] = h.z; r.h[3] = h.w;
+    r.q[0] = a.x; r.q[1] = a.y; r.q[2] = a.z; r.q[3] = a.w;
+    r.q[4] = b.x; r.q[5] = b.y; r.q[6] = b.z; r.q[7] = b.w;
+}
+
+// Q6_K blocks start on 2-byte boundaries: whole dwords from the 4-byte
+// aligned address at or below each field, re-aligned by sh in decoding.
+QD_DEV void lds_q6k(RawQ6K &r, const uint8_t *blk, int h, int j) {
+    r.sh = (uint32_t)(lds_addr(blk) & 3u);
+    const uint8_t *bp = blk - r.sh;
+    const uint8_t *pa = bp + 64 * h + 16 * j;
+    const uint8_t *ph = bp + 128 + 32 * h + 16 * j;
+    const uint8_t *ps = bp + 192 + 8 * h;
+#pragma unroll
+    for (int k = 0; k < 5; k++) {
+        r.a[k] = lds32(pa + 4 * k);
+        r.b[k] = lds32(pa + 32 + 4 * k);
+        r.h[k] = lds32(ph + 4 * k);
+    }
+#pragma unroll
+    for (int k = 0; k < 3; k++) r.s[k] = lds32(ps + 4 * k);
+    r.d = lds32(bp + 208);
+}
+
+// Q8_0 superunits are 16-byte aligned in the ring (272-byte units, rows of
+// whole superunits), so lane c's two blocks start on a dword: block A (d,
+// then quants 2 bytes in) is the "Q" case of load_q80 and block B (quants on
+// a dword, d in the high half of the dword before) the "P" case.
+QD_DEV void lds_q80(RawQ80 &r, const uint8_t *blk, int c) {
+    const uint8_t *g = blk + 68 * c;
+#pragma unroll
+    for (int k = 0; k < 9; k++) r.q[k] = lds32(g + 4 * k);
+    r.pd = r.q[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) r.p[k] = lds32(g + 36 + 4 * k);
+    r.a_is_p = 0u;
+}
+
+// ------------------------------------------------- per-superunit dots ---
+// xv: this lane's 64 activations (in the lane's own order, see each format)
+// for each batch row; result: this lane's share of w . x per row stream.
+
+// Q4_K: xv[0..7] low run (64c + 0..31), xv[8..15] high run; X: sums of x
+// over sub-blocks 2c and 2c+1.
+template <int NR, int B>
+QD_DEV void dot_q4k(const RawQ4K (&r)[NR], const float4 (&xv)[B][16], const float2 (&X)[B],
+                    const Q4Lane &L, float (&out)[NR][B]) {
+    const float inv_unit = 1.0f / fp8_unit();  // exact power of two
+#pragma unroll
+    for (int i = 0; i < NR; i++) {
+        float alo[B], ahi[B];
+#pragma unroll
+        for (int b = 0; b < B; b++) { alo[b] = 0.f; ahi[b] = 0.f; }
+#pragma unroll
+        for (int dw = 0; dw < 8; dw++) {
+            const Q4Nibbles n = q4k_nibbles(r[i].q[dw]);
+#pragma unroll
+            for (int b = 0; b < B; b++) {
+                const float4 xl = xv[b][dw], xh = xv[b][8 + dw];
+                float s = alo[b];
+                s = fmaf(n.lo01.x, xl.x, s);
+                s = fmaf(n.lo01.y, xl.y, s);
+                s = fmaf(n.lo23.x, xl.z, s);
+                s = fmaf(n.lo23.y, xl.w, s);
+                alo[b] = s;
+                float u = ahi[b];
+                u = fmaf(n.hi01.x, xh.x, u);
+                u = fmaf(n.hi01.y, xh.y, u);
+                u = fmaf(n.hi23.x, xh.z, u);
+                u = fmaf(n.hi23.y, xh.w, u);
+                ahi[b] = u;
+            }
+        }
+        const Q4Scales s = q4k_scales(r[i], L);
+#pragma unroll
+        for (int b = 0; b < B; b++) {
+            const float q = s.d * fmaf(s.sc1, ahi[b], s.sc0 * alo[b]);
+            const float m = s.dmin * fmaf(s.m1, X[b].y, s.m0 * X[b].x);
+            out[i][b] = fmaf(q, inv_unit, -m);
+        }
+    }
+}
+
+// Q6_K: xv[4g + i] = activations of group g (16 per group).
+template <int NR, int B>
+QD_DEV void dot_q6k(const RawQ6K (&r)[NR], const float4 (&xv)[B][16], int j, float (&out)[NR][B]) {
+#pragma unroll
+    for (int i = 0; i < NR; i++) {
+        float acc[B][4];
+#pragma unroll
+        for (int b = 0; b < B; b++)
+#pragma unroll
+            for (int g = 0; g < 4; g++) acc[b][g] = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            uint32_t q[4];
+            q6k_qbytes(r[i], k, q);
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                const float w0 = sbyte(q[g], 0), w1 = sbyte(q[g], 1);
+                const float w2 = sbyte(q[g], 2), w3 = sbyte(q[g], 3);
+#pragma unroll
+                for (int b = 0; b < B; b++) {
+                    const float4 xx = xv[b][4 * g + k];
+                    float s = acc[b][g];
+                    s = fmaf(w0, xx.x, s);
+                    s = fmaf(w1, xx.y, s);
+                    s = fmaf(w2, xx.z, s);
+                    s = fmaf(w3, xx.w, s);
+                    acc[b][g] = s;
+                }
+            }
+        }
+        const Q6Scales s = q6k_scales(r[i], j);
+#pragma unroll
+        for (int b = 0; b < B; b++) {
+            float u = s.sc[0] * acc[b][0];
+            u = fmaf(s.sc[1], acc[b][1], u);
+            u = fmaf(s.sc[2], acc[b][2], u);
+            u = fmaf(s.sc[3], acc[b][3], u);
+            out[i][b] = s.d * u;
+        }
+    }
+}
+
+// Q8_0: xv[0..7] block A (64c + 0..31), xv[8..15] block B.
+template <int NR, int B>
+QD_DEV void dot_q80(const RawQ80 (&r)[NR], const float4 (&xv)[B][16], float (&out)[NR][B]) {
+#pragma unroll
+    for (int i = 0; i < NR; i++) {
+        const float2 d = q80_d(r[i]);
+        float accA[B], accB[B];
+#pragma unroll
+        for (int b = 0; b < B; b++) { accA[b] = 0.f; accB[b] = 0.f; }
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            const uint2 v = q80_qdwords(r[i], k);
+#pragma unroll
+            for (int b = 0; b < B; b++) {
+                const float4 xa = xv[b][k], xb = xv[b][8 + k];
+                float s = accA[b];
+                s = fmaf(sbyte(v.x, 0), xa.x, s);
+                s = fmaf(sbyte(v.x, 1), xa.y, s);
+                s = fmaf(sbyte(v.x, 2), xa.z, s);
+                s = fmaf(sbyte(v.x, 3), xa.w, s);
+                accA[b] = s;
+                float u = accB[b];
+                u = fmaf(sbyte(v.y, 0), xb.x, u);
+                u = fmaf(sbyte(v.y, 1), xb.y, u);
+                u = fmaf(sbyte(v.y, 2), xb.z, u);
+                u = fmaf(sbyte(v.y, 3), xb.w, u);
+                accB[b] = u;
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < B; b++) out[i][b] = fmaf(d.y, accB[b], d.x * accA[b]);
+    }
+}
+
+// ------------------------------------------------------------ kernel ---
+template <int FMT, int B, int NR, bool FFN>
+__global__ __launch_bounds__(kThreads) void stream_kernel(StreamArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    using Raw = typename RawOf<FMT>::T;
+    constexpr int UB = StreamFmt<FMT>::UB;
+    constexpr int NCH = StreamFmt<FMT>::NCH;
+    constexpr int NI = copies_per_step<FMT>();
+    constexpr int SLOTM = NCH * 16;  // bytes of one matrix's step in a slot
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c = lane & 3, g = lane >> 2;
+    const int64_t N = a.N, K = a.K;
+    const int nb = a.nb;
+    const int PD = a.pd;
+
+    // rows of this workgroup
+    const int wg = blockIdx.x;
+    const int64_t r0 = (int64_t)wg * a.rows_base + min(wg, a.rows_extra);
+    const int cnt = a.rows_base + (wg < a.rows_extra ? 1 : 0);
+    const int U = cnt * nb;                                   // superunits per matrix
+    const int S = (U + kStepUnits - 1) / kStepUnits;          // steps
+    const int nw = S > w ? (S - w + kWaves - 1) / kWaves : 0; // steps of this wave
+
+    // LDS layout
+    uint8_t *ring = smem + w * PD * NR * SLOTM;
+    float *xl = reinterpret_cast<float *>(smem + a.off_x);
+    float *xs = reinterpret_cast<float *>(smem + a.off_xsum);
+    const float *nwl = reinterpret_cast<const float *>(smem + a.off_nw);
+    float *part = reinterpret_cast<float *>(smem + a.off_part);
+    float *red = reinterpret_cast<float *>(smem + a.off_red);
+    const int xstride = nb * kSuperPhys;  // floats per staged batch row
+
+    // byte stream of this workgroup's rows, per matrix; a step is copied
+    // from the 16-byte boundary at or below its first byte
+    const int64_t wbeg = r0 * a.row_bytes;
+    const int off0 = (int)(wbeg & 15);
+    const uint8_t *mats[NR];
+    mats[0] = a.W0;
+    if constexpr (NR == 2) mats[1] = a.W1;
+    const int64_t last16 = a.mat_bytes - 16;  // last 16-byte chunk of a matrix
+
+    auto issue = [&](int i, int slot) {
+        // copies of this wave's i-th step (step w + 4 i) into ring slot `slot`
+        const int step = w + kWaves * i;
+        const int64_t a0 = ((wbeg + (int64_t)step * kStepUnits * UB) & ~(int64_t)15);
+#pragma unroll
+        for (int m = 0; m < NR; m++) {
+            const uint32_t dst = lds_addr(ring + (slot * NR + m) * SLOTM);
+#pragma unroll
+            for (int j = 0; j < NI; j++) {
+                const int64_t off = min(a0 + 16 * (int64_t)(64 * j + lane), last16);
+                if (j < NI - 1 || lane < NCH - 64 * (NI - 1))
+                    lds_copy16(mats[m] + off, dst + 1024 * j);
+            }
+        }
+    };
+
+    // ---- x into LDS: physical float p of batch row b holds logical
+    // k = unskew(p); pad floats receive a harmless copy of x[0]
+    const int xf4 = B * nb * (kSuperPhys / 4);  // float4 slots
+    for (int f0 = w * 64; f0 < xf4; f0 += kThreads) {
+        const int f = f0 + lane;
+        const int b = f / (nb * (kSuperPhys / 4));
+        const int p = 4 * (f - b * (nb * (kSuperPhys / 4)));  // physical float in the row
+        const int t = p / kSuperPhys, q = p - t * kSuperPhys;
+        const int run = q / 68, e = q - run * 68;
+        const int64_t k = (int64_t)t * kSuper + run * 64 + e;
+        const int64_t so = (e < 64 && k < K && f < xf4) ? (int64_t)b * K + k : 0;
+        if (f0 + 64 <= xf4 || lane < xf4 - f0) lds_copy16(a.x + so, lds_addr(xl + 4 * f0));
+    }
+    // ---- the norm weight (K floats, unskewed) the same way
+    const bool norm = a.norm_w != nullptr;
+    if (norm) {
+        const int nf4 = (int)(K / 4);
+        for (int f0 = w * 64; f0 < nf4; f0 += kThreads)
+            if (f0 + 64 <= nf4 || lane < nf4 - f0)
+                lds_copy16(a.norm_w + 4 * (int64_t)(f0 + lane), lds_addr(nwl + 4 * f0));
+    }
+
+    // ---- the first steps of the weight stream (at most PD in flight)
+    const int pro = min(PD, nw);
+    for (int i = 0; i < pro; i++) issue(i, i);
+
+    // ---- x (and the norm weight) landed: this wave's copies, then every wave's
+    vm_wait_n(pro * NR * NI);
+    block_sync();
+
+    // ---- RMS-normalise in place; Q4_K: sums of every 32-run
+    const int F = nb * (kSuper / 4);  // logical float4 per batch row
+    if (norm) {
+        float ss[B];
+#pragma unroll
+        for (int b = 0; b < B; b++) ss[b] = 0.f;
+        for (int f = tid; f < B * F; f += kThreads) {
+            const int b = f / F;
+            const int k = 4 * (f - b * F);
+            const float4 v = *reinterpret_cast<const float4 *>(xl + b * xstride + xphys(k));
+            float sq = fmaf(v.x, v.x, 0.f);
+            sq = fmaf(v.y, v.y, sq);
+            sq = fmaf(v.z, v.z, sq);
+            sq = fmaf(v.w, v.w, sq);
+#pragma unroll
+            for (int bb = 0; bb < B; bb++)
+                if (bb == b) ss[bb] += sq;
+        }
+#pragma unroll
+        for (int b = 0; b < B; b++) {
+            const float t = wave_total(ss[b]);
+            if (lane == 0) red[w * B + b] = t;
+        }
+        block_sync();
+        float inv_rms[B];
+#pragma unroll
+        for (int b = 0; b < B; b++) {
+            const float sq = (red[b] + red[B + b]) + (red[2 * B + b] + red[3 * B + b]);
+            inv_rms[b] = 1.0f / sqrtf(sq / (float)K + a.eps);
+        }
+        for (int f = tid; f < B * F; f += kThreads) {
+            const int b = f / F;
+            const int k = 4 * (f - b * F);
+            float4 *ad = reinterpret_cast<float4 *>(xl + b * xstride + xphys(k));
+            float4 v = *ad;
+            const float4 nw4 = *reinterpret_cast<const float4 *>(nwl + k);
+            float ir = inv_rms[0];
+#pragma unroll
+            for (int bb = 1; bb < B; bb++)
+                if (bb == b) ir = inv_rms[bb];
+            v.x = v.x * ir * nw4.x;
+            v.y = v.y * ir * nw4.y;
+            v.z = v.z * ir * nw4.z;
+            v.w = v.w * ir * nw4.w;
+            *ad = v;
+        }
+        block_sync();
+    }
+    if constexpr (FMT == kQ4K) {
+        // lanes 8m..8m+7 hold the 8 float4 of one 32-run: F is a multiple of 64
+        for (int f = tid; f < B * F; f += kThreads) {
+            const int b = f / F;
+            const int k = 4 * (f - b * F);
+            const float4 v = *reinterpret_cast<const float4 *>(xl + b * xstride + xphys(k));
+            const float sm = oct_sum((v.x + v.y) + (v.z + v.w));
+            if ((lane & 7) == 0) xs[b * nb * 8 + (k >> 5)] = sm;
+        }
+        block_sync();
+    }
+
+    // ---- the stream
+    const int Umax = a.units_max;
+    Q4Lane L4;
+    if constexpr (FMT == kQ4K) L4 = q4k_lane(c);
+    for (int i = 0; i < nw; i++) {
+        const int slot = i % PD;
+        // step i's copies are in LDS: the steps issued after it (at most
+        // PD - 1, fewer at the end of the stream) may still be in flight
+        vm_wait_n(min(PD - 1, nw - 1 - i) * NR * NI);
+        const int step = w + kWaves * i;
+        const int u = step * kStepUnits + g;  // this group's superunit
+        const bool live = u < U;
+        const int uu = live ? u : U - 1;
+        const int lr = uu / nb;
+        const int su = uu - lr * nb;
+        const uint8_t *blk0 = ring + slot * NR * SLOTM + off0 + g * UB;
+
+        Raw raw[NR];
+#pragma unroll
+        for (int m = 0; m < NR; m++) {
+            const uint8_t *blk = blk0 + m * SLOTM;
+            if constexpr (FMT == kQ4K) lds_q4k(raw[m], blk, c);
+            else if constexpr (FMT == kQ6K) lds_q6k(raw[m], blk, c >> 1, c & 1);
+            else lds_q80(raw[m], blk, c);
+        }
+        float4 xv[B][16];
+        float2 X[B];
+#pragma unroll
+        for (int b = 0; b < B; b++) {
+            const float *xb = xl + b * xstride;
+            if constexpr (FMT == kQ6K) {
+                const int base = su * kSuper + 128 * (c >> 1) + 16 * (c & 1);
+#pragma unroll
+                for (int gg = 0; gg < 4; gg++) {
+                    const float4 *xg = reinterpret_cast<const float4 *>(xb + xphys(base + 32 * gg));
+#pragma unroll
+                    for (int n = 0; n < 4; n++) xv[b][4 * gg + n] = xg[n];
+                }
+            } else {
+                const float4 *xp = reinterpret_cast<const float4 *>(xb + xphys(su * kSuper + 64 * c));
+#pragma unroll
+                for (int n = 0; n < 16; n++) xv[b][n] = xp[n];
+            }
+            if constexpr (FMT == kQ4K)
+                X[b] = *reinterpret_cast<const float2 *>(xs + b * nb * 8 + 8 * su + 2 * c);
+        }
+        // every read of this slot is complete before the slot is refilled
+        // with step i + PD, which streams in while this one is decoded
+        lgkm_wait();
+        if (i + PD < nw) issue(i + PD, slot);
+
+        float v[NR][B];
+        if constexpr (FMT == kQ4K) dot_q4k<NR, B>(raw, xv, X, L4, v);
+        else if constexpr (FMT == kQ6K) dot_q6k<NR, B>(raw, xv, c & 1, v);
+        else dot_q80<NR, B>(raw, xv, v);
+#pragma unroll
+        for (int m = 0; m < NR; m++)
+#pragma unroll
+            for (int b = 0; b < B; b++) {
+                const float t = quad_sum(v[m][b]);
+                if (c == 0 && live) part[(m * B + b) * Umax + u] = t;
+            }
+    }
+    vm_wait<0>();
+    block_sync();
+
+    // ---- rows: partials in superunit order
+    for (int e = tid; e < cnt * B; e += kThreads) {
+        const int b = e / cnt;
+        const int lr = e - b * cnt;
+        const int64_t row = r0 + lr;
+        float sr[NR];
+#pragma unroll
+        for (int m = 0; m < NR; m++) {
+            const float *pp = part + (m * B + b) * Umax + lr * nb;
+            float acc = 0.f;
+            for (int t = 0; t < nb; t++) acc += pp[t];
+            sr[m] = acc;
+        }
+        if constexpr (FFN) {
+            a.y[(int64_t)b * N + row] = act_apply(a.act, sr[0]) * sr[1];
+            if (a.g_out) a.g_out[(int64_t)b * N + row] = sr[0];
+            if (a.u_out) a.u_out[(int64_t)b * N + row] = sr[1];
+        } else {
+            a.y[(int64_t)b * N + row] = sr[0];
+        }
+    }
+}
+
+}  // namespace
+
+// LDS bytes and layout of one workgroup; 0 if it does not fit.
+size_t stream_layout(int fmt, int batch, bool ffn, int nb, int units_max, int pd, StreamArgs *a) {
+    const int NR = ffn ? 2 : 1;
+    int nch = fmt == kQ4K ? StreamFmt<kQ4K>::NCH : fmt == kQ6K ? StreamFmt<kQ6K>::NCH
+                                                                : StreamFmt<kQ80>::NCH;
+    size_t off = (size_t)kWaves * pd * NR * nch * 16;
+    a->off_x = (int)off;
+    off += (size_t)batch * nb * kSuperPhys * 4;
+    a->off_xsum = (int)off;
+    if (fmt == kQ4K) off += (size_t)batch * nb * 8 * 4;
+    a->off_nw = (int)off;
+    if (a->norm_w) off += (size_t)nb * kSuper * 4;
+    a->off_part = (int)off;
+    off += (size_t)NR * batch * units_max * 4;
+    a->off_red = (int)off;
+    off += 16 * 4;
+    return off;
+}
+
+int stream_copies_per_step(int fmt, bool ffn) {
+    const int NR = ffn ? 2 : 1;
+    switch (fmt) {
+    case kQ4K: return NR * copies_per_step<kQ4K>();
+    case kQ6K: return NR * copies_per_step<kQ6K>();
+    case kQ80: return NR * copies_per_step<kQ80>();
+    default: return 0;
+    }
+}
+
+// Allow each kernel the whole LDS of a CU (once per kernel).
+template <auto Kern>
+static hipError_t allow_lds() {
+    static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(Kern),
+                                                    hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                    160 * 1024);
+    return e;
+}
+
+template <int FMT, int B>
+static hipError_t launch_sb(const StreamArgs &a, bool ffn, unsigned grid, size_t lds, hipStream_t st) {
+    if (ffn) {
+        if (allow_lds<stream_kernel<FMT, B, 2, true>>() != hipSuccess) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((stream_kernel<FMT, B, 2, true>), dim3(grid), dim3(kThreads), lds, st, a);
+    } else {
+        if (allow_lds<stream_kernel<FMT, B, 1, false>>() != hipSuccess) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((stream_kernel<FMT, B, 1, false>), dim3(grid), dim3(kThreads), lds, st, a);
+    }
+    return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t launch_sf(const StreamArgs &a, int batch, bool ffn, unsigned grid, size_t lds,
+                            hipStream_t st) {
+    switch (batch) {
+    case 1: return launch_sb<FMT, 1>(a, ffn, grid, lds, st);
+    case 2: return launch_sb<FMT, 2>(a, ffn, grid, lds, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_stream(int fmt, int batch, bool ffn, const StreamArgs &a, unsigned grid,
+                         size_t lds, hipStream_t st) {
+    switch (fmt) {
+    case kQ4K: return launch_sf<kQ4K>(a, batch, ffn, grid, lds, st);
+    case kQ6K: return launch_sf<kQ6K>(a, batch, ffn, grid, lds, st);
+    case kQ80: return launch_sf<kQ80>(a, batch, ffn, grid, lds, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace qd

@@ -70,6 +70,30 @@ hipError_t launch_ffn(int fmt_a, int fmt_b, int batch, FfnArgs f, hipStream_t st
 hipError_t launch_dequant(int fmt, const uint8_t *W, float *out, uint16_t *out_bf16,
                           int64_t N, int64_t K, hipStream_t st);
 
+// Streaming GEMV (qd_gemv_stream.hip): one workgroup per row range, weights
+// copied through an LDS ring.
+struct StreamArgs {
+    const uint8_t *W0;      // weights (gate for the fused FFN)
+    const uint8_t *W1;      // up (fused FFN) or nullptr
+    const float *x;         // [batch][K], 16-byte aligned
+    const float *norm_w;    // optional RMS-norm weight [K]
+    float *y, *g_out, *u_out;
+    int64_t N, K;
+    int64_t row_bytes;
+    int64_t mat_bytes;      // N * row_bytes, a multiple of 16
+    int nb;                 // superunits per row (K / 256)
+    int rows_base, rows_extra;  // workgroup i owns rows_base + (i < rows_extra) rows
+    int units_max;          // (rows_base + (rows_extra > 0)) * nb
+    int pd;                 // ring depth (steps in flight per wave)
+    int off_x, off_xsum, off_nw, off_part, off_red;  // LDS layout (bytes)
+    int act;
+    float eps;
+};
+size_t stream_layout(int fmt, int batch, bool ffn, int nb, int units_max, int pd, StreamArgs *a);
+int stream_copies_per_step(int fmt, bool ffn);
+hipError_t launch_stream(int fmt, int batch, bool ffn, const StreamArgs &a, unsigned grid,
+                         size_t lds, hipStream_t st);
+
 // Prefill GEMM (qd_prefill.hip).  A workgroup owns 32*tm tokens by 256
 // output columns (plain: 256 weight rows; FFN: 128 rows of gate and of up)
 // over K-tiles [kt_per_split*ks, ...) of 128 weights.

@@ -1,0 +1,102 @@
+"""GPU parity of the streaming GEMV path (weights copied through an LDS ring,
+one workgroup per row range) against the oracle.
+
+The path applies to batch 1 and 2 when the matrix is a whole number of
+16-byte chunks; it is taken automatically for long rows (K >= 8192) and
+forced here with the stream override (one and two workgroups per CU) on
+shapes chosen to split rows unevenly over workgroups, leave partial last
+steps and run fewer rows than workgroups.  A launch override forces the
+register-streaming kernel, run on the same inputs as a second check.
+Bar: |y - y_ref| <= 1e-4 * sum|w x| + 1e-6 per output, h within the bound
+propagated through the activation.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import assert_bound, dev, h_tolerance, say
+
+pytestmark = pytest.mark.gpu
+
+SEED = 0x5EED
+
+
+@pytest.fixture(scope="module")
+def qd(gpu):
+    import quantized_decode_q4k_amd as qd
+    qd.lib()
+    yield qd
+    qd.set_launch_override(0, 0, 0)
+    qd.set_stream_override(0, 0)
+
+
+def forced(qd, wpc, fn):
+    qd.set_stream_override(wpc, 0)
+    try:
+        return fn()
+    finally:
+        qd.set_stream_override(0, 0)
+
+
+def streams(fmt, N, K):
+    return (N * synth.row_bytes(fmt, K)) % 16 == 0 and K % 256 == 0
+
+
+# N = 1 (one workgroup), 37 (fewer rows than workgroups), 256, 257 and 600
+# (rows split unevenly); K = 2048 keeps every Q6_K matrix a multiple of 16 bytes
+CASES = [(fmt, N, K) for fmt in ("q4_k", "q6_k", "q8_0") for N, K in
+         ((1, 2048), (37, 2048), (256, 2048), (257, 2048), (600, 2048), (64, 10240))]
+
+
+@pytest.mark.parametrize("fmt,N,K", CASES)
+@pytest.mark.parametrize("batch", [1, 2])
+def test_stream_gemv(qd, fmt, N, K, batch):
+    assert streams(fmt, N, K)
+    say(f"stream gemv {fmt} N={N} K={K} batch={batch}")
+    W = synth.quant_weights(fmt, N, K, SEED, tensor_id=81)
+    x = synth.normal((batch, K), SEED, tensor_id=82)
+    Wd, xd = dev(W), dev(x)
+    y64, S = oracle.gemv(fmt, W, x, N, K)
+    for wpc in (1, 2):
+        y = forced(qd, wpc, lambda: qd.qgemv(fmt, Wd, xd).cpu().numpy())
+        assert_bound(f"stream {fmt} wpc={wpc}", y, y64, S)
+        again = forced(qd, wpc, lambda: qd.qgemv(fmt, Wd, xd).cpu().numpy())
+        assert np.array_equal(y.view(np.uint32), again.view(np.uint32))
+    auto = qd.qgemv(fmt, Wd, xd).cpu().numpy()
+    assert_bound(f"automatic {fmt}", auto, y64, S)
+    qd.set_launch_override(2, 1, 1)
+    try:
+        legacy = qd.qgemv(fmt, Wd, xd).cpu().numpy()
+    finally:
+        qd.set_launch_override(0, 0, 0)
+    assert_bound(f"legacy {fmt}", legacy, y64, S)
+
+
+@pytest.mark.parametrize("fmt,N,K", [("q4_k", 300, 2048), ("q8_0", 40, 2560), ("q6_k", 48, 1024)])
+@pytest.mark.parametrize("batch,act,norm", [(1, "gelu_tanh", True), (2, "silu", True),
+                                            (1, "silu", False)])
+def test_stream_gate_up(qd, fmt, N, K, batch, act, norm):
+    assert streams(fmt, N, K)
+    say(f"stream gate/up {fmt} N={N} K={K} batch={batch} act={act} norm={norm}")
+    Wg = synth.quant_weights(fmt, N, K, SEED, tensor_id=83)
+    Wu = synth.quant_weights(fmt, N, K, SEED, tensor_id=84)
+    x = synth.normal((batch, K), SEED, tensor_id=85)
+    nw = synth.normal((K,), SEED, tensor_id=86, mean=1.0, std=0.1)
+    g = torch.empty((batch, N), device="cuda")
+    u = torch.empty((batch, N), device="cuda")
+    h = forced(qd, 1, lambda: qd.qffn_gate_up_act(fmt, dev(Wg), dev(Wu), dev(x),
+                                                   dev(nw) if norm else None, 1e-6, act,
+                                                   g_out=g, u_out=u).cpu().numpy())
+    g, u = g.cpu().numpy(), u.cpu().numpy()
+    xn = (oracle.rmsnorm(x, nw, 1e-6) if norm else x.astype(np.float64)).astype(np.float32)
+    g64, Sg = oracle.gemv(fmt, Wg, xn, N, K)
+    u64, Su = oracle.gemv(fmt, Wu, xn, N, K)
+    assert_bound("gate", g, g64, Sg)
+    assert_bound("up", u, u64, Su)
+    aid = oracle.ACT_GELU_TANH if act == "gelu_tanh" else oracle.ACT_SILU
+    href = oracle.act_vec(aid, g64) * u64
+    tol = h_tolerance(g64, u64, Sg, Su, aid)
+    err = np.abs(h - href)
+    assert (err <= tol).all(), f"h: worst {np.max(err / tol):.3f} of tolerance"
