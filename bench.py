@@ -1,7 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark: batch-1 k-quant decode FFN at Gemma-3-4B shape on one MI355X.
 
-One step = one pass of the decode hot path over one token:
+One step = one pass of the decode hot path over one token, one qffn_decode
+call, which launches:
   qffn_gate_up_act   RMS-norm(x) -> gate/up GEMV (Q4_K, 10240 x 2560 each)
                      -> GELU-tanh(gate) * up = h
   qgemv_q6k          down GEMV (Q6_K, 2560 x 10240) on h
@@ -10,10 +11,13 @@ Weights are seeded synthetic tensors with the workload's field distributions
 (>= 1 GiB) that neither the L2 nor the 256 MB Infinity Cache serves them.
 Inputs are resident in HBM before the timed region.
 
-Prints ONE JSON line on stdout.  `value` is weight GB/s of the whole step;
-`roofline` is for the dominant kernel (fused gate/up), timed with HIP events
-on the stream it runs on; `cpu_baseline` is the C oracle on the host cores.
-Other workloads (--workload) are for profiling and sweeps.
+Prints ONE JSON line on stdout.  `value` is weight GB/s of the whole step
+(the step's launches replayed as a HIP graph); `roofline` is for the dominant
+kernel (the gate/up GEMV), timed with HIP events on the stream it runs on, in
+an eager pass that makes the same two launches through their own entry
+points; `cpu_baseline` is the C oracle on the host cores.  Other workloads
+(--workload) are for profiling and sweeps; gemma4_prefill reports TFLOP/s of
+the 512-token prefill GEMMs against the bf16 MFMA peak.
 """
 from __future__ import annotations
 
@@ -29,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 METRIC = "batch-1 k-quant GEMV µs and weight GB/s (% of HBM peak), Gemma-3-4B FFN"
 ROTATE_BYTES = 1 << 30
 FFN_WORKLOADS = ("gemma3_ffn", "gemma3_ffn_2k", "gemma4_ffn", "gemma4_ffn_2k", "gemma4_ffn_b8")
@@ -41,7 +46,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="gemma3_ffn",
                    choices=["gemma3_ffn", "gemma3_ffn_2k", "gemma4_ffn", "gemma4_ffn_2k",
-                            "gemma4_ffn_b8", "lm_head_q4k",
+                            "gemma4_ffn_b8", "gemma4_prefill", "lm_head_q4k",
                             "lm_head_q8_0", "down_q6k", "gate_up_q4k", "copy"])
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="approximate CPU time budget of the oracle baseline (0 = skip)")
@@ -110,6 +115,19 @@ class Workload:
             self.y = torch.empty((self.batch, hidden), device=dev)
             base = {k: t(v) for k, v in mats.items()}
             self.hidden = hidden
+        elif name == "gemma4_prefill":
+            M, hidden, ff = 512, synth.GEMMA4_HIDDEN, synth.GEMMA4_FF
+            self.M, self.hidden, self.ff = M, hidden, ff
+            mats = {"gate": synth.quant_weights("q4_k", ff, hidden, seed, tensor_id=71),
+                    "up": synth.quant_weights("q4_k", ff, hidden, seed, tensor_id=72),
+                    "down": synth.quant_weights("q6_k", hidden, ff, seed, tensor_id=74)}
+            self.weight_bytes = sum(m.size for m in mats.values())
+            self.X = t(synth.normal_bf16((M, hidden), seed, tensor_id=73).view("int16"))
+            self.H = torch.empty((M, ff), dtype=torch.bfloat16, device=dev)
+            self.Y = torch.empty((M, hidden), device=dev)
+            self.flops_gate_up = 2 * 2 * M * ff * hidden
+            self.flops = self.flops_gate_up + 2 * M * hidden * ff
+            base = {k: t(v) for k, v in mats.items()}
         elif name in ("lm_head_q4k", "lm_head_q8_0"):
             fmt = "q4_k" if name == "lm_head_q4k" else "q8_0"
             self.fmt = fmt
@@ -130,10 +148,10 @@ class Workload:
     def alg_bytes(self):
         """(dominant kernel name, algorithmic bytes per launch of it)."""
         b, n = self.batch, self.name
-        if n in ("gemma3_ffn", "gemma4_ffn"):
-            # the whole FFN is one kernel: all weights, x, norm weight, y
-            return "qffn_decode", self.weight_bytes + 4 * (2 * b * self.hidden + self.hidden)
-        if n in ("gemma3_ffn_2k", "gemma4_ffn_2k", "gemma4_ffn_b8", "gate_up_q4k"):
+        if n == "gemma4_prefill":
+            return "qgemm_prefill_gate_up_act", self.flops_gate_up
+        if n in ("gemma3_ffn", "gemma4_ffn", "gemma3_ffn_2k", "gemma4_ffn_2k", "gemma4_ffn_b8",
+                 "gate_up_q4k"):
             w = 2 * self.ff * (self.hidden // 256) * 144
             return "qffn_gate_up_act", w + 4 * (b * self.hidden + self.hidden + b * self.ff)
         if n == "down_q6k":
@@ -142,43 +160,48 @@ class Workload:
             return "qgemv", self.weight_bytes + 4 * (2560 + 262144)
         return "copy", 2 * self.weight_bytes
 
-    def step(self, ev=None):
+    def step(self):
+        """One step: every launch of the workload, weights rotating."""
         c = self.copies[self.i]
         self.i = (self.i + 1) % self.ncopy
         qd, n = self.qd, self.name
         if n in ("gemma3_ffn", "gemma4_ffn"):
-            if ev:
-                ev[0].record()
             qd.qffn_decode("q4_k", c["gate"], c["up"], "q6_k", c["down"], self.x, self.nw, 1e-6,
                            "gelu_tanh", y=self.y)
-            if ev:
-                ev[1].record()
+        elif n == "gemma4_prefill":
+            qd.qgemm_prefill_gate_up_act("q4_k", c["gate"], c["up"], self.X, "gelu_tanh", H=self.H)
+            qd.qgemm_prefill("q6_k", c["down"], self.H, Y=self.Y)
         elif n in ("gemma3_ffn_2k", "gemma4_ffn_2k", "gemma4_ffn_b8", "gate_up_q4k"):
-            if ev:
-                ev[0].record()
             qd.qffn_gate_up_act("q4_k", c["gate"], c["up"], self.x, self.nw, 1e-6, "gelu_tanh", h=self.h)
-            if ev:
-                ev[1].record()
             if n != "gate_up_q4k":
                 qd.qgemv_q6k(c["down"], self.h, self.y)
         elif n == "down_q6k":
-            if ev:
-                ev[0].record()
             qd.qgemv_q6k(c["down"], self.hin, self.y)
-            if ev:
-                ev[1].record()
         elif n.startswith("lm_head"):
-            if ev:
-                ev[0].record()
             qd.qgemv(self.fmt, c["W"], self.x, self.y)
-            if ev:
-                ev[1].record()
         else:
-            if ev:
-                ev[0].record()
             self.dst.copy_(c["src"])
-            if ev:
-                ev[1].record()
+
+
+def _dominant(self):
+    """One launch of the workload's dominant kernel (the roofline's kernel)."""
+    c = self.copies[self.i]
+    self.i = (self.i + 1) % self.ncopy
+    qd, n = self.qd, self.name
+    if n == "gemma4_prefill":
+        qd.qgemm_prefill_gate_up_act("q4_k", c["gate"], c["up"], self.X, "gelu_tanh", H=self.H)
+    elif n in ("gemma3_ffn", "gemma4_ffn", "gemma3_ffn_2k", "gemma4_ffn_2k", "gemma4_ffn_b8",
+               "gate_up_q4k"):
+        qd.qffn_gate_up_act("q4_k", c["gate"], c["up"], self.x, self.nw, 1e-6, "gelu_tanh", h=self.h)
+    elif n == "down_q6k":
+        qd.qgemv_q6k(c["down"], self.hin, self.y)
+    elif n.startswith("lm_head"):
+        qd.qgemv(self.fmt, c["W"], self.x, self.y)
+    else:
+        self.dst.copy_(c["src"])
+
+
+Workload.dominant = _dominant
 
 
 def cpu_baseline(seed, budget_s):
@@ -265,29 +288,46 @@ def main():
         stream.synchronize()
         total_ms = start.elapsed_time(end)
         ms_per_step = total_ms / K
-        # Timed region 2 (roofline): the same K steps launched eagerly with a
-        # pair of events around the dominant kernel on its stream.  A GPU spin
-        # first lets the host queue every launch before the GPU reaches them,
-        # so no host gap falls between an event pair.
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(K)]
+        # Timed region 2 (roofline): the dominant kernel alone, launched K
+        # times back to back (weights rotating as in the step) between one
+        # pair of HIP events on its stream; a GPU spin first lets the host
+        # queue every launch before the GPU reaches them, so the average is
+        # kernel time, as a kernel trace reports it.
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        wl.i = 0
         if hasattr(torch.cuda, "_sleep"):
             torch.cuda._sleep(int(2e6 + 4e4 * K))
-        for k in range(K):
-            wl.step(evs[k])
+        ev0.record(stream)
+        for _ in range(K):
+            wl.dominant()
+        ev1.record(stream)
         stream.synchronize()
-    kern_ms = sorted(a.elapsed_time(b) for a, b in evs)
-    kern_avg = sum(kern_ms) / K
+    kern_avg = ev0.elapsed_time(ev1) / K
     kname, alg = wl.alg_bytes()
-    achieved = alg / (kern_avg * 1e-3) / 1e9
+    prefill = args.workload == "gemma4_prefill"
+    scale = 1e12 if prefill else 1e9                  # TFLOP/s or GB/s
+    achieved = alg / (kern_avg * 1e-3) / scale
     log(f"[bench] step {ms_per_step * 1e3:.2f} us (graph replay); {kname} avg {kern_avg * 1e3:.2f} us "
-        f"(median {kern_ms[K // 2] * 1e3:.2f}, min {kern_ms[0] * 1e3:.2f}) -> {achieved:.0f} GB/s")
+        f"over {K} back-to-back launches -> {achieved:.0f} {'TFLOP/s' if prefill else 'GB/s'}")
 
-    value = wl.weight_bytes / (ms_per_step * 1e-3) / 1e9
+    if prefill:
+        value = wl.flops / (ms_per_step * 1e-3) / 1e12
+        metric, unit, peak, bound = ("prefill TFLOP/s, Gemma-4-31B FFN, 512 tokens", "TFLOP/s",
+                                     MFMA_BF16_PEAK_TFLOPS, "mfma")
+    else:
+        value = wl.weight_bytes / (ms_per_step * 1e-3) / 1e9
+        metric = METRIC if args.workload == "gemma3_ffn" else f"weight GB/s, {args.workload}"
+        unit, peak, bound = "GB/s", HBM_PEAK_GBS, "hbm"
+    workloads = {
+        "gemma3_ffn": "Gemma-3-4B FFN decode step, batch 1: RMS-norm + gate/up Q4_K 10240x2560 + "
+                      "GELU-tanh + down Q6_K 2560x10240 (one qffn_decode call)",
+        "gemma4_prefill": "Gemma-4-31B FFN prefill, 512 tokens: gate/up Q4_K 21504x5376 + "
+                          "GELU-tanh -> bf16 h, down Q6_K 5376x21504 (bf16 MFMA, fp32 accumulate)",
+    }
     out = {
-        "metric": METRIC if args.workload == "gemma3_ffn" else f"weight GB/s, {args.workload}",
+        "metric": metric,
         "value": round(value, 2),
-        "unit": "GB/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
@@ -295,35 +335,33 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16-mfma/f32" if prefill else "f32",
         "data": "synthetic",
         "config": {
-            "workload": {
-                "gemma3_ffn": "Gemma-3-4B FFN decode step, batch 1: RMS-norm + gate/up Q4_K "
-                              "10240x2560 + GELU-tanh + down Q6_K 2560x10240, one qffn_decode launch",
-            }.get(args.workload, args.workload),
-            "batch": wl.batch,
+            "workload": workloads.get(args.workload, args.workload),
+            "batch": wl.M if prefill else wl.batch,
             "weight_bytes_per_step": wl.weight_bytes,
             "us_per_step": round(ms_per_step * 1e3, 3),
-            "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
             "rotating_weight_copies": wl.ncopy,
-            "timing": "value/ms_per_step: K steps in one HIP graph replay; roofline: eager launches, "
-                      "HIP event pair around each dominant-kernel launch",
+            "timing": "value/ms_per_step: K steps in one HIP graph replay; roofline: K eager "
+                      "back-to-back launches of the dominant kernel between one HIP event pair",
             "seed": args.seed,
         },
         "roofline": {
             "kernel": kname,
-            "bound": "hbm",
+            "bound": bound,
             "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic_from_profiles(f"{args.workload}:{kname}", alg),
-            "alg_bytes_per_launch": alg,
+            "peak": peak,
+            "unit": unit,
+            "frac": round(achieved / peak, 4),
+            "traffic": None if prefill else traffic_from_profiles(f"{args.workload}:{kname}", alg),
+            ("alg_flops_per_launch" if prefill else "alg_bytes_per_launch"): alg,
             "avg_launch_us": round(kern_avg * 1e3, 3),
         },
         "context": "pages' figure: ~1670 ms/token CPU-fallback decode of Gemma-4-E2B (larql); not a target",
     }
+    if not prefill:
+        out["config"]["pct_hbm_peak"] = round(100 * value / HBM_PEAK_GBS, 2)
     if args.cpu_seconds > 0 and args.workload == "gemma3_ffn":
         log("[bench] cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(args.seed, args.cpu_seconds)

@@ -155,10 +155,10 @@ qd_status qffn_gate_up_act(qd_format fmt, const void *Wg, const void *Wu,
  * y = Wd h,  h = act(Wg xn) * (Wu xn),  xn = RMSNorm(x) if norm_w else x
  *
  * The whole decode FFN of one layer (larql Gemma 3 table: input norm ->
- * q4k_ffn_gate_up_8sg -> geglu -> q6k_matvec), as one launch where the
- * formats and sizes allow, else as qffn_gate_up_act followed by qgemv on the
- * same stream.  Inside the one launch, down-projection workgroups start on
- * their weights while gate/up workgroups are still producing h.
+ * q4k_ffn_gate_up_8sg -> geglu -> q6k_matvec), as qffn_gate_up_act followed
+ * by qgemv on the same stream, with h kept in the library's workspace.  A
+ * single-launch variant (down-projection workgroups wait for their slice of
+ * h inside the same launch) is selected with qd_set_ffn_override.
  *
  *   fmt_gu, Wg, Wu   gate and up, N_ff x K
  *   fmt_down, Wd     down, K x N_ff
@@ -167,8 +167,8 @@ qd_status qffn_gate_up_act(qd_format fmt, const void *Wg, const void *Wu,
  *   h_out            optional fp32 [batch][N_ff] copy of h (NULL = kept in
  *                    the library's workspace), 16-byte aligned
  * Accuracy: h as in qffn_gate_up_act; y meets the GEMV bound for the h it
- * was computed from.  Fused in one launch for Q4_K gate/up with Q6_K or Q4_K
- * down and for Q8_0 throughout, when batch * K fits one workgroup's LDS.
+ * was computed from.  The single launch exists for Q4_K gate/up with Q6_K or
+ * Q4_K down and for Q8_0 throughout, when batch * K fits one workgroup's LDS.
  */
 qd_status qffn_decode(qd_format fmt_gu, const void *Wg, const void *Wu, qd_format fmt_down,
                       const void *Wd, const float *x, const float *norm_w, float eps, qd_act act,
@@ -237,7 +237,8 @@ qd_status qdequant_bf16(qd_format fmt, const void *W, uint16_t *out,
 qd_status qd_set_launch_override(int p_in, int p_out, int nr);
 
 /*
- * Launch-shape override of qffn_decode's single launch (0 = automatic):
+ * Selects qffn_decode's single launch (any non-zero value; all zero = the
+ * two launches) and its launch shape (0 = automatic):
  * p_in of the gate/up tiles, p_in and K-slices of the down tiles.
  */
 qd_status qd_set_ffn_override(int p_in_a, int p_in_b, int p_out_b);

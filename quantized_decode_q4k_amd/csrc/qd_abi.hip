@@ -357,7 +357,12 @@ qd_status run_ffn_decode(int fmt_gu, const void *Wg, const void *Wu, int fmt_d, 
                                                         lds_units_max(fmt_d, batch));
         pb = make_plan(fmt_d, K, N_ff, batch, false, t);
     }
-    const bool fused = fits && qd::ffn_fused_supported(fmt_gu, fmt_d) &&
+    // The single launch is used only when asked for (qd_set_ffn_override):
+    // measured on MI355X it is slower than the two launches (Gemma-3 FFN,
+    // graph replay: 31.9 us vs 24.6), because its down-projection
+    // workgroups only become resident as gate/up workgroups retire.
+    const bool asked = g_ffn_pin_a.load() || g_ffn_pin_b.load() || g_ffn_pout_b.load();
+    const bool fused = asked && fits && qd::ffn_fused_supported(fmt_gu, fmt_d) &&
                        pb.s.p_out * 64 <= kCtlSlots && pb.tiles <= kMaxTiles;
     if (!fused) {
         // size the workspace once for h and both calls' split-K partials, so

@@ -308,7 +308,18 @@ def test_config_gemma4_31b_ffn(qd, batch):
 
 # ------------------------------------------------- whole decode FFN (one call) ---
 
-def check_ffn_decode(qd, fg, fd, hidden, ff, batch, act, tag, with_h=True, reps=2):
+def check_ffn_decode(qd, fg, fd, hidden, ff, batch, act, tag, with_h=True, reps=2, single=False):
+    """qffn_decode against the oracle chain; single=True selects the one-launch
+    variant (down tiles wait for their h slice inside the launch)."""
+    if single:
+        qd.set_ffn_override(2, 2, 0)
+    try:
+        _check_ffn_decode(qd, fg, fd, hidden, ff, batch, act, tag, with_h, reps)
+    finally:
+        qd.set_ffn_override(0, 0, 0)
+
+
+def _check_ffn_decode(qd, fg, fd, hidden, ff, batch, act, tag, with_h, reps):
     Wg = synth.quant_weights(fg, ff, hidden, SEED, tensor_id=51)
     Wu = synth.quant_weights(fg, ff, hidden, SEED, tensor_id=52)
     Wd = synth.quant_weights(fd, hidden, ff, SEED, tensor_id=53)
@@ -350,18 +361,25 @@ def check_ffn_decode(qd, fg, fd, hidden, ff, batch, act, tag, with_h=True, reps=
 @pytest.mark.parametrize("fg,fd,act,batch", [
     ("q4_k", "q6_k", "gelu_tanh", 1), ("q4_k", "q6_k", "silu", 3), ("q4_k", "q4_k", "silu", 1),
     ("q8_0", "q8_0", "gelu_tanh", 2), ("q6_k", "q6_k", "gelu_tanh", 1)])
-def test_ffn_decode_small(qd, fg, fd, act, batch):
-    check_ffn_decode(qd, fg, fd, 512, 1536, batch, act, "small")
+@pytest.mark.parametrize("single", [False, True])
+def test_ffn_decode_small(qd, fg, fd, act, batch, single):
+    check_ffn_decode(qd, fg, fd, 512, 1536, batch, act, "small", single=single)
 
 
-def test_ffn_decode_without_h_out(qd):
-    check_ffn_decode(qd, "q4_k", "q6_k", 512, 1024, 1, "gelu_tanh", "no-h", with_h=False)
+@pytest.mark.parametrize("single", [False, True])
+def test_ffn_decode_without_h_out(qd, single):
+    check_ffn_decode(qd, "q4_k", "q6_k", 512, 1024, 1, "gelu_tanh", "no-h", with_h=False,
+                     single=single)
 
 
-def test_ffn_decode_gemma3(qd):
-    check_ffn_decode(qd, "q4_k", "q6_k", 2560, 10240, 1, "gelu_tanh", "gemma3-4b", reps=3)
+@pytest.mark.parametrize("single", [False, True])
+def test_ffn_decode_gemma3(qd, single):
+    check_ffn_decode(qd, "q4_k", "q6_k", 2560, 10240, 1, "gelu_tanh", "gemma3-4b", reps=3,
+                     single=single)
 
 
 def test_ffn_decode_gemma4_31b_batch8_falls_back(qd):
-    """batch 8 x K = 5376 does not fit one workgroup's LDS: two launches."""
-    check_ffn_decode(qd, "q4_k", "q6_k", 5376, 21504, 8, "gelu_tanh", "gemma4-31b b8", reps=1)
+    """batch 8 x K = 5376 does not fit one workgroup's LDS: two launches even
+    when the single launch is asked for."""
+    check_ffn_decode(qd, "q4_k", "q6_k", 5376, 21504, 8, "gelu_tanh", "gemma4-31b b8", reps=1,
+                     single=True)
