@@ -252,10 +252,11 @@ qd_status qd_set_gemm_override(int tm, int splits);
 
 /*
  * Shape override of the streaming GEMV path (0 = automatic): workgroups per
- * CU (1..8; LDS is divided between them) and ring depth pd (2..8 steps of 16
- * superunits in flight per wave).
+ * CU (1..8; LDS is divided between them), ring depth pd (2..8 steps of 16
+ * superunits per decoding wave) and split (1 = separate copying and
+ * decoding waves, 512 threads; 2 = every wave does both).
  */
-qd_status qd_set_stream_override(int wg_per_cu, int pd);
+qd_status qd_set_stream_override(int wg_per_cu, int pd, int split);
 
 #ifdef __cplusplus
 }

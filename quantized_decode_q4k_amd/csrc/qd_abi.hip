@@ -183,7 +183,7 @@ qd_status check_shape(int fmt, int64_t N, int64_t K, int batch) {
 constexpr int kCUs = 256;                  // MI355X compute units
 constexpr size_t kLdsPerCU = 160 * 1024;    // gfx950 LDS per CU
 constexpr int kStreamMaxWait = 63;          // vmcnt limit: copies in flight per wave
-std::atomic<int> g_stream_wpc{0}, g_stream_pd{0};  // tuning overrides (0 = automatic)
+std::atomic<int> g_stream_wpc{0}, g_stream_pd{0}, g_stream_split{0};  // tuning overrides (0 = automatic)
 constexpr int64_t kStreamMinK = 8192;       // automatic use of the streaming kernel
 
 // Streaming-kernel launch with wpc workgroups per CU, or false if the LDS
@@ -211,6 +211,7 @@ bool stream_plan_wpc(int fmt, bool ffn, int64_t N, int64_t K, int batch, const f
         const size_t bytes = qd::stream_layout(fmt, batch, ffn, a->nb, a->units_max, pd, a);
         if (bytes <= budget) {
             a->pd = pd;
+            a->split = g_stream_split.load() == 1 ? 1 : 0;
             *grid = (unsigned)G;
             *lds = bytes;
             return true;
@@ -637,10 +638,12 @@ qd_status qd_set_ffn_override(int p_in_a, int p_in_b, int p_out_b) {
     return QD_OK;
 }
 
-qd_status qd_set_stream_override(int wg_per_cu, int pd) {
+qd_status qd_set_stream_override(int wg_per_cu, int pd, int split) {
     if (wg_per_cu < 0 || wg_per_cu > 8 || pd < 0 || pd == 1 || pd > 8) return QD_EINVAL;
+    if (split < 0 || split > 2) return QD_EINVAL;
     g_stream_wpc.store(wg_per_cu);
     g_stream_pd.store(pd);
+    g_stream_split.store(split);
     return QD_OK;
 }
 

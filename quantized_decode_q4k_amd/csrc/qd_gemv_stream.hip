@@ -483,6 +483,256 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamArgs a) {
     }
 }
 
+// ------------------------------------------------ producer / consumer ---
+// The same stream with the two jobs split between waves (512 threads):
+// waves 0-3 only decode (consumers), wave 4 + w only copies consumer w's
+// steps (producer).  A wave that issues copies stalls at issue whenever the
+// memory pipeline backs up; here that stall costs no decode time.  One
+// workgroup barrier per step: before it, each producer waits for the step its
+// consumer takes next; after it, each consumer decodes that step while its
+// producer refills the slot freed by the previous step (PD - 1 steps ahead).
+constexpr int kSplitThreads = 512;
+
+template <int FMT, int B, int NR, bool FFN>
+__global__ __launch_bounds__(kSplitThreads) void stream_split_kernel(StreamArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    using Raw = typename RawOf<FMT>::T;
+    constexpr int UB = StreamFmt<FMT>::UB;
+    constexpr int NCH = StreamFmt<FMT>::NCH;
+    constexpr int NI = copies_per_step<FMT>();
+    constexpr int SLOTM = NCH * 16;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
+    const bool prod = wv >= kWaves;
+    const int w = wv & (kWaves - 1);  // consumer served (producer) or consumer index
+    const int ct = tid & (kThreads - 1);  // thread index among the consumer waves
+    const int c = lane & 3, g = lane >> 2;
+    const int64_t N = a.N, K = a.K;
+    const int nb = a.nb;
+    const int PD = a.pd;
+
+    const int wg = blockIdx.x;
+    const int64_t r0 = (int64_t)wg * a.rows_base + min(wg, a.rows_extra);
+    const int cnt = a.rows_base + (wg < a.rows_extra ? 1 : 0);
+    const int U = cnt * nb;
+    const int S = (U + kStepUnits - 1) / kStepUnits;
+    const int nw = S > w ? (S - w + kWaves - 1) / kWaves : 0;  // steps of consumer w
+    const int iters = (S + kWaves - 1) / kWaves;               // same for every wave
+
+    uint8_t *ring = smem + w * PD * NR * SLOTM;
+    float *xl = reinterpret_cast<float *>(smem + a.off_x);
+    float *xs = reinterpret_cast<float *>(smem + a.off_xsum);
+    const float *nwl = reinterpret_cast<const float *>(smem + a.off_nw);
+    float *part = reinterpret_cast<float *>(smem + a.off_part);
+    float *red = reinterpret_cast<float *>(smem + a.off_red);
+    const int xstride = nb * kSuperPhys;
+
+    const int64_t wbeg = r0 * a.row_bytes;
+    const int off0 = (int)(wbeg & 15);
+    const uint8_t *mats[NR];
+    mats[0] = a.W0;
+    if constexpr (NR == 2) mats[1] = a.W1;
+    const int64_t last16 = a.mat_bytes - 16;
+
+    auto issue = [&](int i, int slot) {  // step w + 4 i of consumer w into its slot
+        const int step = w + kWaves * i;
+        const int64_t a0 = ((wbeg + (int64_t)step * kStepUnits * UB) & ~(int64_t)15);
+#pragma unroll
+        for (int m = 0; m < NR; m++) {
+            const uint32_t dst = lds_addr(ring + (slot * NR + m) * SLOTM);
+#pragma unroll
+            for (int j = 0; j < NI; j++) {
+                const int64_t off = min(a0 + 16 * (int64_t)(64 * j + lane), last16);
+                if (j < NI - 1 || lane < NCH - 64 * (NI - 1))
+                    lds_copy16(mats[m] + off, dst + 1024 * j);
+            }
+        }
+    };
+
+    // ---- x and the norm weight (consumers copy them, ahead of any weight copy)
+    const bool norm = a.norm_w != nullptr;
+    if (!prod) {
+        const int xf4 = B * nb * (kSuperPhys / 4);
+        for (int f0 = w * 64; f0 < xf4; f0 += kThreads) {
+            const int f = f0 + lane;
+            const int b = f / (nb * (kSuperPhys / 4));
+            const int p = 4 * (f - b * (nb * (kSuperPhys / 4)));
+            const int t = p / kSuperPhys, q = p - t * kSuperPhys;
+            const int run = q / 68, e = q - run * 68;
+            const int64_t k = (int64_t)t * kSuper + run * 64 + e;
+            const int64_t so = (e < 64 && k < K && f < xf4) ? (int64_t)b * K + k : 0;
+            if (f0 + 64 <= xf4 || lane < xf4 - f0) lds_copy16(a.x + so, lds_addr(xl + 4 * f0));
+        }
+        if (norm) {
+            const int nf4 = (int)(K / 4);
+            for (int f0 = w * 64; f0 < nf4; f0 += kThreads)
+                if (f0 + 64 <= nf4 || lane < nf4 - f0)
+                    lds_copy16(a.norm_w + 4 * (int64_t)(f0 + lane), lds_addr(nwl + 4 * f0));
+        }
+    }
+    block_sync();
+    if (prod) {
+        const int pro = min(PD - 1, nw);
+        for (int i = 0; i < pro; i++) issue(i, i);
+    } else {
+        vm_wait<0>();  // this consumer's x copies
+    }
+    block_sync();
+
+    // ---- RMS-normalise in place; Q4_K: sums of every 32-run (consumers)
+    const int F = nb * (kSuper / 4);
+    if (norm) {
+        float inv_rms[B];
+        if (!prod) {
+            float ss[B];
+#pragma unroll
+            for (int b = 0; b < B; b++) ss[b] = 0.f;
+            for (int f = ct; f < B * F; f += kThreads) {
+                const int b = f / F;
+                const int k = 4 * (f - b * F);
+                const float4 v = *reinterpret_cast<const float4 *>(xl + b * xstride + xphys(k));
+                float sq = fmaf(v.x, v.x, 0.f);
+                sq = fmaf(v.y, v.y, sq);
+                sq = fmaf(v.z, v.z, sq);
+                sq = fmaf(v.w, v.w, sq);
+#pragma unroll
+                for (int bb = 0; bb < B; bb++)
+                    if (bb == b) ss[bb] += sq;
+            }
+#pragma unroll
+            for (int b = 0; b < B; b++) {
+                const float t = wave_total(ss[b]);
+                if (lane == 0) red[w * B + b] = t;
+            }
+        }
+        block_sync();
+        if (!prod) {
+#pragma unroll
+            for (int b = 0; b < B; b++) {
+                const float sq = (red[b] + red[B + b]) + (red[2 * B + b] + red[3 * B + b]);
+                inv_rms[b] = 1.0f / sqrtf(sq / (float)K + a.eps);
+            }
+            for (int f = ct; f < B * F; f += kThreads) {
+                const int b = f / F;
+                const int k = 4 * (f - b * F);
+                float4 *ad = reinterpret_cast<float4 *>(xl + b * xstride + xphys(k));
+                float4 v = *ad;
+                const float4 nw4 = *reinterpret_cast<const float4 *>(nwl + k);
+                float ir = inv_rms[0];
+#pragma unroll
+                for (int bb = 1; bb < B; bb++)
+                    if (bb == b) ir = inv_rms[bb];
+                v.x = v.x * ir * nw4.x;
+                v.y = v.y * ir * nw4.y;
+                v.z = v.z * ir * nw4.z;
+                v.w = v.w * ir * nw4.w;
+                *ad = v;
+            }
+        }
+        block_sync();
+    }
+    if constexpr (FMT == kQ4K) {
+        if (!prod) {
+            for (int f = ct; f < B * F; f += kThreads) {
+                const int b = f / F;
+                const int k = 4 * (f - b * F);
+                const float4 v = *reinterpret_cast<const float4 *>(xl + b * xstride + xphys(k));
+                const float sm = oct_sum((v.x + v.y) + (v.z + v.w));
+                if ((lane & 7) == 0) xs[b * nb * 8 + (k >> 5)] = sm;
+            }
+        }
+        block_sync();
+    }
+
+    // ---- the stream
+    const int Umax = a.units_max;
+    Q4Lane L4;
+    if constexpr (FMT == kQ4K) L4 = q4k_lane(c);
+    for (int i = 0; i < iters; i++) {
+        if (prod && i < nw)  // step i has landed; the steps issued after it may be in flight
+            vm_wait_n(min(PD - 2, nw - 1 - i) * NR * NI);
+        block_sync();  // step i is ready for every consumer; step i-1 is consumed
+        if (prod) {
+            if (i + PD - 1 < nw) issue(i + PD - 1, (i + PD - 1) % PD);
+            continue;
+        }
+        if (i >= nw) continue;
+        const int slot = i % PD;
+        const int step = w + kWaves * i;
+        const int u = step * kStepUnits + g;
+        const bool live = u < U;
+        const int uu = live ? u : U - 1;
+        const int lr = uu / nb;
+        const int su = uu - lr * nb;
+        const uint8_t *blk0 = ring + slot * NR * SLOTM + off0 + g * UB;
+        Raw raw[NR];
+#pragma unroll
+        for (int m = 0; m < NR; m++) {
+            const uint8_t *blk = blk0 + m * SLOTM;
+            if constexpr (FMT == kQ4K) lds_q4k(raw[m], blk, c);
+            else if constexpr (FMT == kQ6K) lds_q6k(raw[m], blk, c >> 1, c & 1);
+            else lds_q80(raw[m], blk, c);
+        }
+        float4 xv[B][16];
+        float2 X[B];
+#pragma unroll
+        for (int b = 0; b < B; b++) {
+            const float *xb = xl + b * xstride;
+            if constexpr (FMT == kQ6K) {
+                const int base = su * kSuper + 128 * (c >> 1) + 16 * (c & 1);
+#pragma unroll
+                for (int gg = 0; gg < 4; gg++) {
+                    const float4 *xg = reinterpret_cast<const float4 *>(xb + xphys(base + 32 * gg));
+#pragma unroll
+                    for (int n = 0; n < 4; n++) xv[b][4 * gg + n] = xg[n];
+                }
+            } else {
+                const float4 *xp = reinterpret_cast<const float4 *>(xb + xphys(su * kSuper + 64 * c));
+#pragma unroll
+                for (int n = 0; n < 16; n++) xv[b][n] = xp[n];
+            }
+            if constexpr (FMT == kQ4K)
+                X[b] = *reinterpret_cast<const float2 *>(xs + b * nb * 8 + 8 * su + 2 * c);
+        }
+        float v[NR][B];
+        if constexpr (FMT == kQ4K) dot_q4k<NR, B>(raw, xv, X, L4, v);
+        else if constexpr (FMT == kQ6K) dot_q6k<NR, B>(raw, xv, c & 1, v);
+        else dot_q80<NR, B>(raw, xv, v);
+#pragma unroll
+        for (int m = 0; m < NR; m++)
+#pragma unroll
+            for (int b = 0; b < B; b++) {
+                const float t = quad_sum(v[m][b]);
+                if (c == 0 && live) part[(m * B + b) * Umax + u] = t;
+            }
+    }
+    vm_wait<0>();
+    block_sync();
+
+    for (int e = tid; e < cnt * B; e += kSplitThreads) {
+        const int b = e / cnt;
+        const int lr = e - b * cnt;
+        const int64_t row = r0 + lr;
+        float sr[NR];
+#pragma unroll
+        for (int m = 0; m < NR; m++) {
+            const float *pp = part + (m * B + b) * Umax + lr * nb;
+            float acc = 0.f;
+            for (int t = 0; t < nb; t++) acc += pp[t];
+            sr[m] = acc;
+        }
+        if constexpr (FFN) {
+            a.y[(int64_t)b * N + row] = act_apply(a.act, sr[0]) * sr[1];
+            if (a.g_out) a.g_out[(int64_t)b * N + row] = sr[0];
+            if (a.u_out) a.u_out[(int64_t)b * N + row] = sr[1];
+        } else {
+            a.y[(int64_t)b * N + row] = sr[0];
+        }
+    }
+}
+
 }  // namespace
 
 // LDS bytes and layout of one workgroup; 0 if it does not fit.
@@ -525,6 +775,18 @@ static hipError_t allow_lds() {
 
 template <int FMT, int B>
 static hipError_t launch_sb(const StreamArgs &a, bool ffn, unsigned grid, size_t lds, hipStream_t st) {
+    if (a.split) {
+        if (ffn) {
+            if (allow_lds<stream_split_kernel<FMT, B, 2, true>>() != hipSuccess) return hipErrorInvalidValue;
+            hipLaunchKernelGGL((stream_split_kernel<FMT, B, 2, true>), dim3(grid), dim3(kSplitThreads),
+                               lds, st, a);
+        } else {
+            if (allow_lds<stream_split_kernel<FMT, B, 1, false>>() != hipSuccess) return hipErrorInvalidValue;
+            hipLaunchKernelGGL((stream_split_kernel<FMT, B, 1, false>), dim3(grid), dim3(kSplitThreads),
+                               lds, st, a);
+        }
+        return hipGetLastError();
+    }
     if (ffn) {
         if (allow_lds<stream_kernel<FMT, B, 2, true>>() != hipSuccess) return hipErrorInvalidValue;
         hipLaunchKernelGGL((stream_kernel<FMT, B, 2, true>), dim3(grid), dim3(kThreads), lds, st, a);

@@ -85,6 +85,7 @@ struct StreamArgs {
     int rows_base, rows_extra;  // workgroup i owns rows_base + (i < rows_extra) rows
     int units_max;          // (rows_base + (rows_extra > 0)) * nb
     int pd;                 // ring depth (steps in flight per wave)
+    int split;              // 1: producer / consumer waves (512 threads)
     int off_x, off_xsum, off_nw, off_part, off_red;  // LDS layout (bytes)
     int act;
     float eps;

@@ -29,15 +29,15 @@ def qd(gpu):
     qd.lib()
     yield qd
     qd.set_launch_override(0, 0, 0)
-    qd.set_stream_override(0, 0)
+    qd.set_stream_override(0, 0, 0)
 
 
-def forced(qd, wpc, fn):
-    qd.set_stream_override(wpc, 0)
+def forced(qd, wpc, fn, split=2):
+    qd.set_stream_override(wpc, 0 if split == 2 else 4, split)
     try:
         return fn()
     finally:
-        qd.set_stream_override(0, 0)
+        qd.set_stream_override(0, 0, 0)
 
 
 def streams(fmt, N, K):
@@ -60,10 +60,11 @@ def test_stream_gemv(qd, fmt, N, K, batch):
     Wd, xd = dev(W), dev(x)
     y64, S = oracle.gemv(fmt, W, x, N, K)
     for wpc in (1, 2):
-        y = forced(qd, wpc, lambda: qd.qgemv(fmt, Wd, xd).cpu().numpy())
-        assert_bound(f"stream {fmt} wpc={wpc}", y, y64, S)
-        again = forced(qd, wpc, lambda: qd.qgemv(fmt, Wd, xd).cpu().numpy())
-        assert np.array_equal(y.view(np.uint32), again.view(np.uint32))
+        for split in (2, 1):
+            y = forced(qd, wpc, lambda: qd.qgemv(fmt, Wd, xd).cpu().numpy(), split)
+            assert_bound(f"stream {fmt} wpc={wpc} split={split}", y, y64, S)
+            again = forced(qd, wpc, lambda: qd.qgemv(fmt, Wd, xd).cpu().numpy(), split)
+            assert np.array_equal(y.view(np.uint32), again.view(np.uint32))
     auto = qd.qgemv(fmt, Wd, xd).cpu().numpy()
     assert_bound(f"automatic {fmt}", auto, y64, S)
     qd.set_launch_override(2, 1, 1)
@@ -77,9 +78,10 @@ def test_stream_gemv(qd, fmt, N, K, batch):
 @pytest.mark.parametrize("fmt,N,K", [("q4_k", 300, 2048), ("q8_0", 40, 2560), ("q6_k", 48, 1024)])
 @pytest.mark.parametrize("batch,act,norm", [(1, "gelu_tanh", True), (2, "silu", True),
                                             (1, "silu", False)])
-def test_stream_gate_up(qd, fmt, N, K, batch, act, norm):
+@pytest.mark.parametrize("split", [2, 1])
+def test_stream_gate_up(qd, fmt, N, K, batch, act, norm, split):
     assert streams(fmt, N, K)
-    say(f"stream gate/up {fmt} N={N} K={K} batch={batch} act={act} norm={norm}")
+    say(f"stream gate/up {fmt} N={N} K={K} batch={batch} act={act} norm={norm} split={split}")
     Wg = synth.quant_weights(fmt, N, K, SEED, tensor_id=83)
     Wu = synth.quant_weights(fmt, N, K, SEED, tensor_id=84)
     x = synth.normal((batch, K), SEED, tensor_id=85)
@@ -88,7 +90,7 @@ def test_stream_gate_up(qd, fmt, N, K, batch, act, norm):
     u = torch.empty((batch, N), device="cuda")
     h = forced(qd, 1, lambda: qd.qffn_gate_up_act(fmt, dev(Wg), dev(Wu), dev(x),
                                                    dev(nw) if norm else None, 1e-6, act,
-                                                   g_out=g, u_out=u).cpu().numpy())
+                                                   g_out=g, u_out=u).cpu().numpy(), split)
     g, u = g.cpu().numpy(), u.cpu().numpy()
     xn = (oracle.rmsnorm(x, nw, 1e-6) if norm else x.astype(np.float64)).astype(np.float32)
     g64, Sg = oracle.gemv(fmt, Wg, xn, N, K)
