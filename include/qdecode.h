@@ -251,12 +251,20 @@ qd_status qd_set_ffn_override(int p_in_a, int p_in_b, int p_out_b);
 qd_status qd_set_gemm_override(int tm, int splits);
 
 /*
- * Shape override of the streaming GEMV path (0 = automatic): workgroups per
- * CU (1..8; LDS is divided between them), ring depth pd (2..8 steps of 16
- * superunits per decoding wave) and split (1 = separate copying and
- * decoding waves, 512 threads; 2 = every wave does both).
+ * Shape override of the streaming GEMV path (process-wide; 0 = automatic).
+ *   wg_per_cu  workgroups per CU (1..8; LDS is divided between them)
+ *   depth      steps of 16 superunits in flight: per wave for the kernel in
+ *              which every wave copies and decodes (2..8), per copying wave
+ *              for the producer / consumer kernel (1..32, capped by what its
+ *              ring and wait counter allow)
+ *   consumers  1 = every wave copies and decodes; 4 or 8 = that many
+ *              decoding waves beside the copying waves and one staging x
+ *   producers  copying waves of the producer / consumer kernel (1 or 2;
+ *              0 = 2); must be 0 unless consumers is 4 or 8
+ * A non-zero wg_per_cu forces the streaming path where the shape allows it.
+ * Returns QD_EINVAL for values outside these sets.
  */
-qd_status qd_set_stream_override(int wg_per_cu, int pd, int split);
+qd_status qd_set_stream_override(int wg_per_cu, int depth, int consumers, int producers);
 
 #ifdef __cplusplus
 }

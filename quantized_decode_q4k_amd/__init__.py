@@ -56,7 +56,7 @@ SIGNATURES = {
     "qd_set_launch_override": (_I, [_I, _I, _I]),
     "qd_set_ffn_override": (_I, [_I, _I, _I]),
     "qd_set_gemm_override": (_I, [_I, _I]),
-    "qd_set_stream_override": (_I, [_I, _I, _I]),
+    "qd_set_stream_override": (_I, [_I, _I, _I, _I]),
 }
 
 _lock = threading.Lock()
@@ -281,9 +281,12 @@ def set_gemm_override(tm: int = 0, splits: int = 0):
     _check("qd_set_gemm_override", lib().qd_set_gemm_override(tm, splits))
 
 
-def set_stream_override(wg_per_cu: int = 0, pd: int = 0, split: int = 0):
-    """Streaming GEMV shape override (0 = automatic)."""
-    _check("qd_set_stream_override", lib().qd_set_stream_override(wg_per_cu, pd, split))
+def set_stream_override(wg_per_cu: int = 0, depth: int = 0, consumers: int = 0, producers: int = 0):
+    """Streaming GEMV shape override (0 = automatic): workgroups per CU, steps
+    in flight, decoding waves (1 = every wave copies and decodes; 4 or 8 = the
+    producer / consumer kernel) and its copying waves (1 or 2)."""
+    _check("qd_set_stream_override",
+           lib().qd_set_stream_override(wg_per_cu, depth, consumers, producers))
 
 
 def set_launch_override(p_in: int = 0, p_out: int = 0, nr: int = 0):

@@ -183,16 +183,14 @@ qd_status check_shape(int fmt, int64_t N, int64_t K, int batch) {
 constexpr int kCUs = 256;                  // MI355X compute units
 constexpr size_t kLdsPerCU = 160 * 1024;    // gfx950 LDS per CU
 constexpr int kStreamMaxWait = 63;          // vmcnt limit: copies in flight per wave
-std::atomic<int> g_stream_wpc{0}, g_stream_pd{0}, g_stream_split{0};  // tuning overrides (0 = automatic)
+// tuning overrides (0 = automatic)
+std::atomic<int> g_stream_wpc{0}, g_stream_depth{0}, g_stream_consumers{0}, g_stream_producers{0};
 constexpr int64_t kStreamMinK = 8192;       // automatic use of the streaming kernel
 
-// Streaming-kernel launch with wpc workgroups per CU, or false if the LDS
-// layout does not fit.
-bool stream_plan_wpc(int fmt, bool ffn, int64_t N, int64_t K, int batch, const float *norm_w,
-                     int wpc, qd::StreamArgs *a, unsigned *grid, size_t *lds) {
+void stream_rows(int64_t N, int64_t K, int fmt, int wpc, const float *norm_w, qd::StreamArgs *a,
+                 unsigned *grid) {
     const int64_t rb = row_bytes(fmt, K);
     const int G = (int)std::min<int64_t>(N, (int64_t)kCUs * wpc);
-    const size_t budget = kLdsPerCU / wpc;
     a->N = N;
     a->K = K;
     a->row_bytes = rb;
@@ -202,17 +200,25 @@ bool stream_plan_wpc(int fmt, bool ffn, int64_t N, int64_t K, int batch, const f
     a->rows_extra = (int)(N % G);
     a->units_max = (a->rows_base + (a->rows_extra > 0 ? 1 : 0)) * a->nb;
     a->norm_w = norm_w;
+    *grid = (unsigned)G;
+}
+
+// Kernel in which every wave copies and decodes, wpc workgroups per CU; false
+// if its LDS layout does not fit.
+bool stream_plan_wpc(int fmt, bool ffn, int64_t N, int64_t K, int batch, const float *norm_w,
+                     int wpc, qd::StreamArgs *a, unsigned *grid, size_t *lds) {
+    stream_rows(N, K, fmt, wpc, norm_w, a, grid);
+    const size_t budget = kLdsPerCU / wpc;
     const int copies = qd::stream_copies_per_step(fmt, ffn);
     if (copies <= 0) return false;
     // a shallow ring: copies queued beyond a few steps block the issuing
-    // wave without adding bandwidth (measured: depth 2 best)
-    const int pd_max = std::min(g_stream_pd.load() ? g_stream_pd.load() : 2, kStreamMaxWait / copies);
+    // wave without adding bandwidth (measured: depth 3 best, 2 close)
+    const int pd_max = std::min(g_stream_depth.load() ? g_stream_depth.load() : 3, kStreamMaxWait / copies);
     for (int pd = pd_max; pd >= 2; pd--) {
         const size_t bytes = qd::stream_layout(fmt, batch, ffn, a->nb, a->units_max, pd, a);
         if (bytes <= budget) {
             a->pd = pd;
-            a->split = g_stream_split.load() == 1 ? 1 : 0;
-            *grid = (unsigned)G;
+            a->consumers = 0;
             *lds = bytes;
             return true;
         }
@@ -220,24 +226,81 @@ bool stream_plan_wpc(int fmt, bool ffn, int64_t N, int64_t K, int batch, const f
     return false;
 }
 
-// Launch of the streaming kernel for this shape, or false where the
+// Producer / consumer kernel: as many ring slots as the LDS share holds (a
+// multiple of the copying waves, no more than the workgroup's steps need), and
+// as many steps in flight per copying wave as its vmcnt can track.  When slots
+// are reused, slots >= consumers + producers * (lag - 1) keeps every wait of a
+// copying wave for a free slot finite.  False if it does not fit.
+bool stream_plan_pc(int fmt, bool ffn, int64_t N, int64_t K, int batch, const float *norm_w,
+                    int wpc, int consumers, int producers, int lag_default, qd::StreamArgs *a,
+                    unsigned *grid, size_t *lds) {
+    stream_rows(N, K, fmt, wpc, norm_w, a, grid);
+    a->consumers = consumers;
+    a->producers = producers;
+    const size_t budget = kLdsPerCU / wpc;
+    const int copies = qd::stream_copies_per_step(fmt, ffn);
+    if (copies <= 0) return false;
+    const size_t fixed = qd::stream_pc_layout(fmt, batch, ffn, a->nb, a->units_max, 0, a);
+    const size_t per_slot = qd::stream_pc_layout(fmt, batch, ffn, a->nb, a->units_max, 1, a) - fixed + 16;
+    if (fixed >= budget) return false;
+    const int steps = (a->units_max + 15) / 16;
+    const int need = (steps + producers - 1) / producers * producers;
+    int slots = (int)std::min<size_t>((size_t)need, (budget - fixed) / per_slot);
+    slots -= slots % producers;
+    while (slots >= producers && qd::stream_pc_layout(fmt, batch, ffn, a->nb, a->units_max, slots, a) > budget)
+        slots -= producers;
+    if (slots < producers) return false;
+    *lds = qd::stream_pc_layout(fmt, batch, ffn, a->nb, a->units_max, slots, a);
+    if (*lds > budget) return false;
+    const int lag_max = 1 + kStreamMaxWait / copies;
+    int lag = g_stream_depth.load() ? g_stream_depth.load() : lag_default;
+    lag = std::min(lag, lag_max);
+    if (steps > slots) lag = std::min(lag, (slots - consumers) / producers + 1);
+    if (lag < 1) return false;
+    a->pd = 0;
+    a->slots = slots;
+    a->lag = lag;
+    return true;
+}
+
+// Launch of a streaming kernel for this shape, or false where the
 // register-streaming kernel is used instead: batch > 2, Q8_0 rows of partial
 // superunits, a matrix whose size is not a multiple of 16 bytes, an LDS
-// layout that does not fit, and (unless overridden) shapes where it is the
-// slower of the two.  Measured on MI355X (graph replay): on Gemma-3 down
-// (K = 10240) the LDS ring at two workgroups per CU is level with or
-// slightly ahead of the register path (11.1-11.5 us vs 11.7); it loses when
-// only one workgroup per CU fits (Gemma-4 down, K = 21504: 37.4 vs 29.1)
-// and on K = 2560 (gate/up 13.5 vs 12.9, lm_head 91 vs 74), where its LDS
-// reads of x per superunit cost more than the prologue they save.
+// layout that does not fit, and (unless overridden) plain GEMVs with K <
+// 8192.  Measured on MI355X (graph replay, 1 GiB of rotating weights):
+//   * fused gate/up: the producer / consumer kernel, at one workgroup per CU
+//     with 8 decoding waves when a workgroup's whole row range fits in its
+//     ring (Gemma-3 10240 x 2560: 11.8 us, against 13.2 for the register
+//     kernel and 14.0 for the kernel in which every wave copies), else two
+//     per CU with 4 (Gemma-4 21504 x 5376: 32.1 us against 33.4);
+//   * plain GEMV with K >= 8192: every wave copies and decodes, two
+//     workgroups per CU, depth 3 (Gemma-3 down: 11.2 us against 11.7;
+//     Gemma-4 down 30.4 against 30.0 -- level);
+//   * K = 2560 plain GEMVs stay on the register kernel (lm_head 262144 rows:
+//     73 us against 91 or more on either streaming kernel).
 bool stream_plan(int fmt, bool ffn, int64_t N, int64_t K, int batch, const float *norm_w,
                  qd::StreamArgs *a, unsigned *grid, size_t *lds) {
     if (batch > 2) return false;
     if (K % qd::kSuper != 0) return false;
     if ((N * row_bytes(fmt, K)) % 16 != 0) return false;
-    if (g_stream_wpc.load())
-        return stream_plan_wpc(fmt, ffn, N, K, batch, norm_w, g_stream_wpc.load(), a, grid, lds);
-    if (ffn || K < kStreamMinK) return false;
+    const int wpc = g_stream_wpc.load();
+    const int cons = g_stream_consumers.load();
+    constexpr int kPcLag = 3;  // steps in flight per copying wave
+    if (wpc) {
+        if (cons == 4 || cons == 8) {
+            const int prod = g_stream_producers.load() ? g_stream_producers.load() : 2;
+            return stream_plan_pc(fmt, ffn, N, K, batch, norm_w, wpc, cons, prod, kPcLag, a, grid, lds);
+        }
+        return stream_plan_wpc(fmt, ffn, N, K, batch, norm_w, wpc, a, grid, lds);
+    }
+    if (ffn) {
+        // 8 decoding waves spill registers at batch 2
+        if (stream_plan_pc(fmt, ffn, N, K, batch, norm_w, 1, batch == 1 ? 8 : 4, 2, kPcLag, a, grid, lds) &&
+            a->slots * 16 >= a->units_max)
+            return true;
+        return stream_plan_pc(fmt, ffn, N, K, batch, norm_w, 2, 4, 2, kPcLag, a, grid, lds);
+    }
+    if (K < kStreamMinK) return false;
     return stream_plan_wpc(fmt, ffn, N, K, batch, norm_w, 2, a, grid, lds);
 }
 
@@ -638,12 +701,15 @@ qd_status qd_set_ffn_override(int p_in_a, int p_in_b, int p_out_b) {
     return QD_OK;
 }
 
-qd_status qd_set_stream_override(int wg_per_cu, int pd, int split) {
-    if (wg_per_cu < 0 || wg_per_cu > 8 || pd < 0 || pd == 1 || pd > 8) return QD_EINVAL;
-    if (split < 0 || split > 2) return QD_EINVAL;
+qd_status qd_set_stream_override(int wg_per_cu, int depth, int consumers, int producers) {
+    if (wg_per_cu < 0 || wg_per_cu > 8 || depth < 0 || depth > 32) return QD_EINVAL;
+    if (consumers != 0 && consumers != 1 && consumers != 4 && consumers != 8) return QD_EINVAL;
+    if (consumers <= 1 && (depth == 1 || depth > 8)) return QD_EINVAL;
+    if (producers < 0 || producers > 2 || (producers && consumers <= 1)) return QD_EINVAL;
     g_stream_wpc.store(wg_per_cu);
-    g_stream_pd.store(pd);
-    g_stream_split.store(split);
+    g_stream_depth.store(depth);
+    g_stream_consumers.store(consumers);
+    g_stream_producers.store(producers);
     return QD_OK;
 }
 

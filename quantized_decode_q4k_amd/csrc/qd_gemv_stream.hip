@@ -244,11 +244,62 @@ QD_DEV void dot_q80(const RawQ80 (&r)[NR], const float4 (&xv)[B][16], float (&ou
     }
 }
 
+// ------------------------------------------------------ one step ---
+// A lane's operands for one superunit: its share of the block (per row
+// stream) and its 64 activations (per batch row) from LDS.
+template <int FMT, int B, int NR>
+struct StepRegs {
+    typename RawOf<FMT>::T raw[NR];
+    float4 xv[B][16];
+    float2 X[B];  // Q4_K: sums of x over the lane's two sub-blocks
+};
+
+// blk0: the lane group's superunit in row stream 0 (stream m is m * mstride
+// bytes further); su: its superunit index within the row.
+template <int FMT, int B, int NR>
+QD_DEV void read_step(StepRegs<FMT, B, NR> &st, const uint8_t *blk0, int mstride, const float *xl,
+                      const float *xs, int xstride, int nb, int su, int c) {
+#pragma unroll
+    for (int m = 0; m < NR; m++) {
+        const uint8_t *blk = blk0 + m * mstride;
+        if constexpr (FMT == kQ4K) lds_q4k(st.raw[m], blk, c);
+        else if constexpr (FMT == kQ6K) lds_q6k(st.raw[m], blk, c >> 1, c & 1);
+        else lds_q80(st.raw[m], blk, c);
+    }
+#pragma unroll
+    for (int b = 0; b < B; b++) {
+        const float *xb = xl + b * xstride;
+        if constexpr (FMT == kQ6K) {
+            const int base = su * kSuper + 128 * (c >> 1) + 16 * (c & 1);
+#pragma unroll
+            for (int gg = 0; gg < 4; gg++) {
+                const float4 *xg = reinterpret_cast<const float4 *>(xb + xphys(base + 32 * gg));
+#pragma unroll
+                for (int n = 0; n < 4; n++) st.xv[b][4 * gg + n] = xg[n];
+            }
+        } else {
+            const float4 *xp = reinterpret_cast<const float4 *>(xb + xphys(su * kSuper + 64 * c));
+#pragma unroll
+            for (int n = 0; n < 16; n++) st.xv[b][n] = xp[n];
+        }
+        if constexpr (FMT == kQ4K)
+            st.X[b] = *reinterpret_cast<const float2 *>(xs + b * nb * 8 + 8 * su + 2 * c);
+        else
+            st.X[b] = make_float2(0.f, 0.f);
+    }
+}
+
+template <int FMT, int B, int NR>
+QD_DEV void dot_step(const StepRegs<FMT, B, NR> &st, const Q4Lane &L4, int c, float (&v)[NR][B]) {
+    if constexpr (FMT == kQ4K) dot_q4k<NR, B>(st.raw, st.xv, st.X, L4, v);
+    else if constexpr (FMT == kQ6K) dot_q6k<NR, B>(st.raw, st.xv, c & 1, v);
+    else dot_q80<NR, B>(st.raw, st.xv, v);
+}
+
 // ------------------------------------------------------------ kernel ---
 template <int FMT, int B, int NR, bool FFN>
 __global__ __launch_bounds__(kThreads) void stream_kernel(StreamArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    using Raw = typename RawOf<FMT>::T;
     constexpr int UB = StreamFmt<FMT>::UB;
     constexpr int NCH = StreamFmt<FMT>::NCH;
     constexpr int NI = copies_per_step<FMT>();
@@ -411,44 +462,15 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamArgs a) {
         const int su = uu - lr * nb;
         const uint8_t *blk0 = ring + slot * NR * SLOTM + off0 + g * UB;
 
-        Raw raw[NR];
-#pragma unroll
-        for (int m = 0; m < NR; m++) {
-            const uint8_t *blk = blk0 + m * SLOTM;
-            if constexpr (FMT == kQ4K) lds_q4k(raw[m], blk, c);
-            else if constexpr (FMT == kQ6K) lds_q6k(raw[m], blk, c >> 1, c & 1);
-            else lds_q80(raw[m], blk, c);
-        }
-        float4 xv[B][16];
-        float2 X[B];
-#pragma unroll
-        for (int b = 0; b < B; b++) {
-            const float *xb = xl + b * xstride;
-            if constexpr (FMT == kQ6K) {
-                const int base = su * kSuper + 128 * (c >> 1) + 16 * (c & 1);
-#pragma unroll
-                for (int gg = 0; gg < 4; gg++) {
-                    const float4 *xg = reinterpret_cast<const float4 *>(xb + xphys(base + 32 * gg));
-#pragma unroll
-                    for (int n = 0; n < 4; n++) xv[b][4 * gg + n] = xg[n];
-                }
-            } else {
-                const float4 *xp = reinterpret_cast<const float4 *>(xb + xphys(su * kSuper + 64 * c));
-#pragma unroll
-                for (int n = 0; n < 16; n++) xv[b][n] = xp[n];
-            }
-            if constexpr (FMT == kQ4K)
-                X[b] = *reinterpret_cast<const float2 *>(xs + b * nb * 8 + 8 * su + 2 * c);
-        }
+        StepRegs<FMT, B, NR> st;
+        read_step<FMT, B, NR>(st, blk0, SLOTM, xl, xs, xstride, nb, su, c);
         // every read of this slot is complete before the slot is refilled
         // with step i + PD, which streams in while this one is decoded
         lgkm_wait();
         if (i + PD < nw) issue(i + PD, slot);
 
         float v[NR][B];
-        if constexpr (FMT == kQ4K) dot_q4k<NR, B>(raw, xv, X, L4, v);
-        else if constexpr (FMT == kQ6K) dot_q6k<NR, B>(raw, xv, c & 1, v);
-        else dot_q80<NR, B>(raw, xv, v);
+        dot_step<FMT, B, NR>(st, L4, c, v);
 #pragma unroll
         for (int m = 0; m < NR; m++)
 #pragma unroll
@@ -484,115 +506,190 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamArgs a) {
 }
 
 // ------------------------------------------------ producer / consumer ---
-// The same stream with the two jobs split between waves (512 threads):
-// waves 0-3 only decode (consumers), wave 4 + w only copies consumer w's
-// steps (producer).  A wave that issues copies stalls at issue whenever the
-// memory pipeline backs up; here that stall costs no decode time.  One
-// workgroup barrier per step: before it, each producer waits for the step its
-// consumer takes next; after it, each consumer decodes that step while its
-// producer refills the slot freed by the previous step (PD - 1 steps ahead).
-constexpr int kSplitThreads = 512;
-
-template <int FMT, int B, int NR, bool FFN>
-__global__ __launch_bounds__(kSplitThreads) void stream_split_kernel(StreamArgs a) {
+// The same products with the two jobs given to different waves, which never
+// wait on a workgroup barrier inside the stream.  A wave that issues copies
+// stalls at issue whenever the memory pipeline backs up, so the copying waves
+// do little else, and their copies are issued from scalar registers:
+//   * waves NC and NC + 1 copy (producers; the second only when the launch
+//     asks for two).  Producer 0 first copies x (and the norm weight) and
+//     raises xland once they have landed; no weight copy is issued before
+//     then, so x does not queue behind the weight stream.  Producer p then
+//     takes the steps j = p (mod producers), each into ring slot j % slots,
+//     keeping up to `lag` of its steps in flight; once one of its steps has
+//     landed (its own vmcnt) it stores the step number in ready[slot];
+//   * waves 0 .. NC-1 decode (consumers).  First they stage x together, a
+//     64-float4 slice at a time: x * w_norm in place, each wave's sum of
+//     squares of x (added in wave order, so the inverse RMS does not depend
+//     on timing), and for Q4_K the sum of every 32-run; they meet on a
+//     counter in LDS.  Then consumer c takes steps c, c + NC, ... and, after
+//     reading a step out of its slot, stores the number of its steps read
+//     so far in done[c].
+// Slot reuse: producer p may refill the slot of step j once step j - slots
+// has been read, which it knows from the smallest done[] of its own
+// consumers (consumers c = p mod producers take only producer p's steps).
+// The host keeps slots a multiple of the producer count and, when slots are
+// reused, slots >= NC + producers * (lag - 1): then every step such a wait
+// depends on has been published, so the wait ends.  The RMS factor is
+// applied to each row's sum at the end (every product is linear in the
+// staged activations).
+template <int FMT, int B, int NR, bool FFN, int NC>
+__global__ __launch_bounds__(64 * (NC + 2)) void stream_pc_kernel(StreamArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    using Raw = typename RawOf<FMT>::T;
     constexpr int UB = StreamFmt<FMT>::UB;
     constexpr int NCH = StreamFmt<FMT>::NCH;
     constexpr int NI = copies_per_step<FMT>();
     constexpr int SLOTM = NCH * 16;
+    constexpr int CPS = NR * NI;  // copies per step
+    constexpr int NT = 64 * (NC + 2);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7
-    const bool prod = wv >= kWaves;
-    const int w = wv & (kWaves - 1);  // consumer served (producer) or consumer index
-    const int ct = tid & (kThreads - 1);  // thread index among the consumer waves
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 3, g = lane >> 2;
     const int64_t N = a.N, K = a.K;
     const int nb = a.nb;
-    const int PD = a.pd;
+    const int R = a.slots;
+    const int NP = a.producers;
 
     const int wg = blockIdx.x;
     const int64_t r0 = (int64_t)wg * a.rows_base + min(wg, a.rows_extra);
     const int cnt = a.rows_base + (wg < a.rows_extra ? 1 : 0);
     const int U = cnt * nb;
     const int S = (U + kStepUnits - 1) / kStepUnits;
-    const int nw = S > w ? (S - w + kWaves - 1) / kWaves : 0;  // steps of consumer w
-    const int iters = (S + kWaves - 1) / kWaves;               // same for every wave
 
-    uint8_t *ring = smem + w * PD * NR * SLOTM;
+    uint8_t *ring = smem;
     float *xl = reinterpret_cast<float *>(smem + a.off_x);
     float *xs = reinterpret_cast<float *>(smem + a.off_xsum);
-    const float *nwl = reinterpret_cast<const float *>(smem + a.off_nw);
+    float *nwl = reinterpret_cast<float *>(smem + a.off_nw);
     float *part = reinterpret_cast<float *>(smem + a.off_part);
-    float *red = reinterpret_cast<float *>(smem + a.off_red);
+    int *ready = reinterpret_cast<int *>(smem + a.off_red);
+    int *done = ready + R;     // [NC]
+    int *xland = done + NC;
+    int *staged = xland + 1;
+    float *rinv = reinterpret_cast<float *>(staged + 1);  // [B]
+    float *ssq = rinv + B;                                // [NC][B]
     const int xstride = nb * kSuperPhys;
-
     const int64_t wbeg = r0 * a.row_bytes;
     const int off0 = (int)(wbeg & 15);
-    const uint8_t *mats[NR];
-    mats[0] = a.W0;
-    if constexpr (NR == 2) mats[1] = a.W1;
-    const int64_t last16 = a.mat_bytes - 16;
+    const bool norm = a.norm_w != nullptr;
 
-    auto issue = [&](int i, int slot) {  // step w + 4 i of consumer w into its slot
-        const int step = w + kWaves * i;
-        const int64_t a0 = ((wbeg + (int64_t)step * kStepUnits * UB) & ~(int64_t)15);
+    for (int i = tid; i < R + NC + 2; i += NT) ready[i] = i < R ? -1 : 0;
+    block_sync();
+
+    if (wv == NC || wv == NC + 1) {
+        // ---------------------------------------------------- producer ---
+        const int p = wv - NC;
+        if (p < NP) {
+            __builtin_amdgcn_s_setprio(3);
+            if (p == 0) {
+                // x: batch row b, physical float4 q of the row (17 per 64-float
+                // run, the last a pad that receives a copy of x[0]) holds
+                // logical float4 16 * (q / 17) + q % 17
+                const int nq = nb * (kSuperPhys / 4);
+                int n = 0;
 #pragma unroll
-        for (int m = 0; m < NR; m++) {
-            const uint32_t dst = lds_addr(ring + (slot * NR + m) * SLOTM);
+                for (int b = 0; b < B; b++) {
+                    const float *xb = a.x + (int64_t)b * K;
+                    float *dstrow = xl + b * xstride;
+                    for (int q0 = 0; q0 < nq; q0 += 64) {
+                        const int q = q0 + lane;
+                        const int run = q / 17, e = q - 17 * run;
+                        const float *srcp = (e < 16 && q < nq) ? xb + 4 * (16 * run + e) : xb;
+                        if (q0 + 64 <= nq || lane < nq - q0) lds_copy16(srcp, lds_addr(dstrow + 4 * q0));
+                        if (++n == 48) { vm_wait<16>(); n = 16; }
+                    }
+                }
+                if (norm) {
+                    const int nf4 = (int)(K / 4);
+                    for (int f0 = 0; f0 < nf4; f0 += 64) {
+                        if (f0 + 64 <= nf4 || lane < nf4 - f0)
+                            lds_copy16(a.norm_w + 4 * (int64_t)(f0 + lane), lds_addr(nwl + 4 * f0));
+                        if (++n == 48) { vm_wait<16>(); n = 16; }
+                    }
+                }
+                vm_wait<0>();
+                if (lane == 0) lds_flag(xland, 1);
+            } else {
+                lds_wait_eq(xland, 1);
+            }
+            // weight steps j = p + NP * k
+            constexpr int SB = kStepUnits * UB;  // bytes per step and matrix
+            const int64_t base = wbeg & ~(int64_t)15;
+            uint32_t voff[NI];  // lane offset of each of a step's copies
 #pragma unroll
-            for (int j = 0; j < NI; j++) {
-                const int64_t off = min(a0 + 16 * (int64_t)(64 * j + lane), last16);
-                if (j < NI - 1 || lane < NCH - 64 * (NI - 1))
-                    lds_copy16(mats[m] + off, dst + 1024 * j);
+            for (int q = 0; q < NI; q++) voff[q] = 16u * (uint32_t)lane + 1024u * (uint32_t)q;
+            const bool tail_lane = lane < NCH - 64 * (NI - 1);  // lanes of the last copy
+            const int64_t safe = a.mat_bytes - (int64_t)NCH * 16;  // steps starting at or below copy whole
+            const int lag = a.lag;
+            const int nk = S > p ? (S - p + NP - 1) / NP : 0;
+            int k = 0, kp = 0;            // next step to issue / to publish (own numbering)
+            int slot = p, pslot = p;      // their slots
+            int freed = 0;                // own steps below NC * freed have been read
+            while (kp < nk) {
+                while (k < nk && k - kp < lag) {
+                    const int j = p + NP * k;
+                    if (j >= R && j - R >= NC * freed) {
+                        // smallest done[] of this producer's consumers
+                        for (;;) {
+                            int m = 0x7fffffff;
+                            for (int cc = p; cc < NC; cc += NP) m = min(m, lds_poll(&done[cc]));
+                            freed = m;
+                            if (j - R < NC * freed) break;
+                            __builtin_amdgcn_s_sleep(1);
+                        }
+                        asm volatile("" ::: "memory");
+                    }
+                    const uint32_t dst = lds_addr(ring + slot * NR * SLOTM);
+                    const int64_t a0 = base + (int64_t)j * SB;
+                    if (a0 <= safe) {
+#pragma unroll
+                        for (int m = 0; m < NR; m++) {
+                            const uint8_t *sp = (m == 0 ? a.W0 : a.W1) + a0;
+#pragma unroll
+                            for (int q = 0; q < NI; q++)
+                                if (q < NI - 1 || tail_lane)
+                                    lds_copy16_s(sp, voff[q], dst + m * SLOTM + 1024 * q);
+                        }
+                    } else {
+                        // only a step reaching past the end of the matrix: clamp
+                        // its sources (per lane) to the matrix's last 16 bytes
+                        const int64_t last16 = a.mat_bytes - 16;
+#pragma unroll
+                        for (int m = 0; m < NR; m++)
+#pragma unroll
+                            for (int q = 0; q < NI; q++) {
+                                const int64_t off = min(a0 + 16 * (int64_t)(64 * q + lane), last16);
+                                if (q < NI - 1 || tail_lane)
+                                    lds_copy16((m == 0 ? a.W0 : a.W1) + off, dst + m * SLOTM + 1024 * q);
+                            }
+                    }
+                    k++;
+                    slot += NP;
+                    if (slot >= R) slot -= R;
+                }
+                // own step kp has landed once at most (k - kp - 1) are in flight
+                vm_wait_n((k - kp - 1) * CPS);
+                if (lane == 0) lds_flag(&ready[pslot], p + NP * kp);
+                kp++;
+                pslot += NP;
+                if (pslot >= R) pslot -= R;
             }
         }
-    };
-
-    // ---- x and the norm weight (consumers copy them, ahead of any weight copy)
-    const bool norm = a.norm_w != nullptr;
-    if (!prod) {
-        const int xf4 = B * nb * (kSuperPhys / 4);
-        for (int f0 = w * 64; f0 < xf4; f0 += kThreads) {
-            const int f = f0 + lane;
-            const int b = f / (nb * (kSuperPhys / 4));
-            const int p = 4 * (f - b * (nb * (kSuperPhys / 4)));
-            const int t = p / kSuperPhys, q = p - t * kSuperPhys;
-            const int run = q / 68, e = q - run * 68;
-            const int64_t k = (int64_t)t * kSuper + run * 64 + e;
-            const int64_t so = (e < 64 && k < K && f < xf4) ? (int64_t)b * K + k : 0;
-            if (f0 + 64 <= xf4 || lane < xf4 - f0) lds_copy16(a.x + so, lds_addr(xl + 4 * f0));
-        }
-        if (norm) {
-            const int nf4 = (int)(K / 4);
-            for (int f0 = w * 64; f0 < nf4; f0 += kThreads)
-                if (f0 + 64 <= nf4 || lane < nf4 - f0)
-                    lds_copy16(a.norm_w + 4 * (int64_t)(f0 + lane), lds_addr(nwl + 4 * f0));
-        }
-    }
-    block_sync();
-    if (prod) {
-        const int pro = min(PD - 1, nw);
-        for (int i = 0; i < pro; i++) issue(i, i);
     } else {
-        vm_wait<0>();  // this consumer's x copies
-    }
-    block_sync();
-
-    // ---- RMS-normalise in place; Q4_K: sums of every 32-run (consumers)
-    const int F = nb * (kSuper / 4);
-    if (norm) {
-        float inv_rms[B];
-        if (!prod) {
-            float ss[B];
+        // -------------------------------------------------- consumers ---
+        // stage x: slice it (64 float4 of one batch row) goes to wave it % NC
+        lds_wait_eq(xland, 1);
+        const int F = nb * (kSuper / 4);  // logical float4 per batch row (a multiple of 64)
+        const int nit = F / 64;
+        float ss[B];
 #pragma unroll
-            for (int b = 0; b < B; b++) ss[b] = 0.f;
-            for (int f = ct; f < B * F; f += kThreads) {
-                const int b = f / F;
-                const int k = 4 * (f - b * F);
-                const float4 v = *reinterpret_cast<const float4 *>(xl + b * xstride + xphys(k));
+        for (int b = 0; b < B; b++) ss[b] = 0.f;
+        for (int it = wv; it < B * nit; it += NC) {
+            const int b = it / nit;
+            const int k = 4 * (64 * (it - b * nit) + lane);
+            float4 *ad = reinterpret_cast<float4 *>(xl + b * xstride + xphys(k));
+            float4 v = *ad;
+            if (norm) {
                 float sq = fmaf(v.x, v.x, 0.f);
                 sq = fmaf(v.y, v.y, sq);
                 sq = fmaf(v.z, v.z, sq);
@@ -600,118 +697,72 @@ __global__ __launch_bounds__(kSplitThreads) void stream_split_kernel(StreamArgs 
 #pragma unroll
                 for (int bb = 0; bb < B; bb++)
                     if (bb == b) ss[bb] += sq;
-            }
-#pragma unroll
-            for (int b = 0; b < B; b++) {
-                const float t = wave_total(ss[b]);
-                if (lane == 0) red[w * B + b] = t;
-            }
-        }
-        block_sync();
-        if (!prod) {
-#pragma unroll
-            for (int b = 0; b < B; b++) {
-                const float sq = (red[b] + red[B + b]) + (red[2 * B + b] + red[3 * B + b]);
-                inv_rms[b] = 1.0f / sqrtf(sq / (float)K + a.eps);
-            }
-            for (int f = ct; f < B * F; f += kThreads) {
-                const int b = f / F;
-                const int k = 4 * (f - b * F);
-                float4 *ad = reinterpret_cast<float4 *>(xl + b * xstride + xphys(k));
-                float4 v = *ad;
                 const float4 nw4 = *reinterpret_cast<const float4 *>(nwl + k);
-                float ir = inv_rms[0];
-#pragma unroll
-                for (int bb = 1; bb < B; bb++)
-                    if (bb == b) ir = inv_rms[bb];
-                v.x = v.x * ir * nw4.x;
-                v.y = v.y * ir * nw4.y;
-                v.z = v.z * ir * nw4.z;
-                v.w = v.w * ir * nw4.w;
+                v.x *= nw4.x;
+                v.y *= nw4.y;
+                v.z *= nw4.z;
+                v.w *= nw4.w;
                 *ad = v;
             }
-        }
-        block_sync();
-    }
-    if constexpr (FMT == kQ4K) {
-        if (!prod) {
-            for (int f = ct; f < B * F; f += kThreads) {
-                const int b = f / F;
-                const int k = 4 * (f - b * F);
-                const float4 v = *reinterpret_cast<const float4 *>(xl + b * xstride + xphys(k));
+            if constexpr (FMT == kQ4K) {
+                // lanes 8m .. 8m+7 hold the 8 float4 of one 32-run
                 const float sm = oct_sum((v.x + v.y) + (v.z + v.w));
                 if ((lane & 7) == 0) xs[b * nb * 8 + (k >> 5)] = sm;
             }
         }
-        block_sync();
-    }
-
-    // ---- the stream
-    const int Umax = a.units_max;
-    Q4Lane L4;
-    if constexpr (FMT == kQ4K) L4 = q4k_lane(c);
-    for (int i = 0; i < iters; i++) {
-        if (prod && i < nw)  // step i has landed; the steps issued after it may be in flight
-            vm_wait_n(min(PD - 2, nw - 1 - i) * NR * NI);
-        block_sync();  // step i is ready for every consumer; step i-1 is consumed
-        if (prod) {
-            if (i + PD - 1 < nw) issue(i + PD - 1, (i + PD - 1) % PD);
-            continue;
-        }
-        if (i >= nw) continue;
-        const int slot = i % PD;
-        const int step = w + kWaves * i;
-        const int u = step * kStepUnits + g;
-        const bool live = u < U;
-        const int uu = live ? u : U - 1;
-        const int lr = uu / nb;
-        const int su = uu - lr * nb;
-        const uint8_t *blk0 = ring + slot * NR * SLOTM + off0 + g * UB;
-        Raw raw[NR];
-#pragma unroll
-        for (int m = 0; m < NR; m++) {
-            const uint8_t *blk = blk0 + m * SLOTM;
-            if constexpr (FMT == kQ4K) lds_q4k(raw[m], blk, c);
-            else if constexpr (FMT == kQ6K) lds_q6k(raw[m], blk, c >> 1, c & 1);
-            else lds_q80(raw[m], blk, c);
-        }
-        float4 xv[B][16];
-        float2 X[B];
-#pragma unroll
-        for (int b = 0; b < B; b++) {
-            const float *xb = xl + b * xstride;
-            if constexpr (FMT == kQ6K) {
-                const int base = su * kSuper + 128 * (c >> 1) + 16 * (c & 1);
-#pragma unroll
-                for (int gg = 0; gg < 4; gg++) {
-                    const float4 *xg = reinterpret_cast<const float4 *>(xb + xphys(base + 32 * gg));
-#pragma unroll
-                    for (int n = 0; n < 4; n++) xv[b][4 * gg + n] = xg[n];
-                }
-            } else {
-                const float4 *xp = reinterpret_cast<const float4 *>(xb + xphys(su * kSuper + 64 * c));
-#pragma unroll
-                for (int n = 0; n < 16; n++) xv[b][n] = xp[n];
-            }
-            if constexpr (FMT == kQ4K)
-                X[b] = *reinterpret_cast<const float2 *>(xs + b * nb * 8 + 8 * su + 2 * c);
-        }
-        float v[NR][B];
-        if constexpr (FMT == kQ4K) dot_q4k<NR, B>(raw, xv, X, L4, v);
-        else if constexpr (FMT == kQ6K) dot_q6k<NR, B>(raw, xv, c & 1, v);
-        else dot_q80<NR, B>(raw, xv, v);
-#pragma unroll
-        for (int m = 0; m < NR; m++)
+        if (norm) {
 #pragma unroll
             for (int b = 0; b < B; b++) {
-                const float t = quad_sum(v[m][b]);
-                if (c == 0 && live) part[(m * B + b) * Umax + u] = t;
+                const float t = wave_total(ss[b]);
+                if (lane == 0) ssq[wv * B + b] = t;
             }
+        }
+        lgkm_wait();
+        if (lane == 0) lds_add(staged, 1);
+        lds_wait_eq(staged, NC);
+        if (wv == 0 && lane == 0) {
+#pragma unroll
+            for (int b = 0; b < B; b++) {
+                float t = 0.f;
+                for (int w = 0; w < NC; w++) t += norm ? ssq[w * B + b] : 0.f;
+                rinv[b] = norm ? 1.0f / sqrtf(t / (float)K + a.eps) : 1.0f;
+            }
+        }
+        const int Umax = a.units_max;
+        Q4Lane L4;
+        if constexpr (FMT == kQ4K) L4 = q4k_lane(c);
+        int slot = wv % R, nread = 0;
+        const int sstep = NC % R;
+        for (int j = wv; j < S; j += NC) {
+            const int u = j * kStepUnits + g;
+            const bool live = u < U;
+            const int uu = live ? u : U - 1;
+            const int lr = uu / nb;
+            const int su = uu - lr * nb;
+            lds_wait_eq(&ready[slot], j);
+            StepRegs<FMT, B, NR> st;
+            read_step<FMT, B, NR>(st, ring + slot * NR * SLOTM + off0 + g * UB, SLOTM, xl, xs, xstride,
+                                  nb, su, c);
+            lgkm_wait();  // the slot may be refilled from here on
+            if (lane == 0) lds_flag(&done[wv], ++nread);
+            float v[NR][B];
+            dot_step<FMT, B, NR>(st, L4, c, v);
+#pragma unroll
+            for (int m = 0; m < NR; m++)
+#pragma unroll
+                for (int b = 0; b < B; b++) {
+                    const float t = quad_sum(v[m][b]);
+                    if (c == 0 && live) part[(m * B + b) * Umax + u] = t;
+                }
+            slot += sstep;
+            if (slot >= R) slot -= R;
+        }
     }
-    vm_wait<0>();
     block_sync();
 
-    for (int e = tid; e < cnt * B; e += kSplitThreads) {
+    // ---- rows: partials in superunit order, times the inverse RMS
+    const int Umax = a.units_max;
+    for (int e = tid; e < cnt * B; e += NT) {
         const int b = e / cnt;
         const int lr = e - b * cnt;
         const int64_t row = r0 + lr;
@@ -721,7 +772,7 @@ __global__ __launch_bounds__(kSplitThreads) void stream_split_kernel(StreamArgs 
             const float *pp = part + (m * B + b) * Umax + lr * nb;
             float acc = 0.f;
             for (int t = 0; t < nb; t++) acc += pp[t];
-            sr[m] = acc;
+            sr[m] = acc * rinv[b];
         }
         if constexpr (FFN) {
             a.y[(int64_t)b * N + row] = act_apply(a.act, sr[0]) * sr[1];
@@ -754,6 +805,27 @@ size_t stream_layout(int fmt, int batch, bool ffn, int nb, int units_max, int pd
     return off;
 }
 
+// LDS layout of the producer / consumer kernel with `slots` ring slots; returns
+// the bytes used.
+size_t stream_pc_layout(int fmt, int batch, bool ffn, int nb, int units_max, int slots,
+                        StreamArgs *a) {
+    const int NR = ffn ? 2 : 1;
+    int nch = fmt == kQ4K ? StreamFmt<kQ4K>::NCH : fmt == kQ6K ? StreamFmt<kQ6K>::NCH
+                                                                : StreamFmt<kQ80>::NCH;
+    size_t off = (size_t)slots * NR * nch * 16;
+    a->off_x = (int)off;
+    off += (size_t)batch * nb * kSuperPhys * 4;
+    a->off_xsum = (int)off;
+    if (fmt == kQ4K) off += (size_t)batch * nb * 8 * 4;
+    a->off_nw = (int)off;
+    if (a->norm_w) off += (size_t)nb * kSuper * 4;
+    a->off_part = (int)off;
+    off += (size_t)NR * batch * units_max * 4;
+    a->off_red = (int)off;  // ready[slots], done[consumers], xland, staged, rinv[batch], ssq[consumers][batch]
+    off += (size_t)(slots + a->consumers + 2 + batch + a->consumers * batch) * 4;
+    return (off + 15) & ~(size_t)15;
+}
+
 int stream_copies_per_step(int fmt, bool ffn) {
     const int NR = ffn ? 2 : 1;
     switch (fmt) {
@@ -773,20 +845,22 @@ static hipError_t allow_lds() {
     return e;
 }
 
+template <int FMT, int B, bool FFN, int NC>
+static hipError_t launch_pc(const StreamArgs &a, unsigned grid, size_t lds, hipStream_t st) {
+    constexpr int NR = FFN ? 2 : 1;
+    if (allow_lds<stream_pc_kernel<FMT, B, NR, FFN, NC>>() != hipSuccess) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((stream_pc_kernel<FMT, B, NR, FFN, NC>), dim3(grid), dim3(64 * (NC + 2)), lds,
+                       st, a);
+    return hipGetLastError();
+}
+
 template <int FMT, int B>
 static hipError_t launch_sb(const StreamArgs &a, bool ffn, unsigned grid, size_t lds, hipStream_t st) {
-    if (a.split) {
-        if (ffn) {
-            if (allow_lds<stream_split_kernel<FMT, B, 2, true>>() != hipSuccess) return hipErrorInvalidValue;
-            hipLaunchKernelGGL((stream_split_kernel<FMT, B, 2, true>), dim3(grid), dim3(kSplitThreads),
-                               lds, st, a);
-        } else {
-            if (allow_lds<stream_split_kernel<FMT, B, 1, false>>() != hipSuccess) return hipErrorInvalidValue;
-            hipLaunchKernelGGL((stream_split_kernel<FMT, B, 1, false>), dim3(grid), dim3(kSplitThreads),
-                               lds, st, a);
-        }
-        return hipGetLastError();
-    }
+    if (a.consumers == 4)
+        return ffn ? launch_pc<FMT, B, true, 4>(a, grid, lds, st) : launch_pc<FMT, B, false, 4>(a, grid, lds, st);
+    if (a.consumers == 8)
+        return ffn ? launch_pc<FMT, B, true, 8>(a, grid, lds, st) : launch_pc<FMT, B, false, 8>(a, grid, lds, st);
+    if (a.consumers != 0) return hipErrorInvalidValue;
     if (ffn) {
         if (allow_lds<stream_kernel<FMT, B, 2, true>>() != hipSuccess) return hipErrorInvalidValue;
         hipLaunchKernelGGL((stream_kernel<FMT, B, 2, true>), dim3(grid), dim3(kThreads), lds, st, a);

@@ -85,12 +85,18 @@ struct StreamArgs {
     int rows_base, rows_extra;  // workgroup i owns rows_base + (i < rows_extra) rows
     int units_max;          // (rows_base + (rows_extra > 0)) * nb
     int pd;                 // ring depth (steps in flight per wave)
-    int split;              // 1: producer / consumer waves (512 threads)
+    int consumers;          // 0: every wave copies and decodes; 4 or 8: decoding
+                            // waves of the producer / consumer kernel
+    int producers;          // producer / consumer: copying waves (1 or 2)
+    int slots;              // producer / consumer: ring slots (steps)
+    int lag;                // producer / consumer: steps in flight per copying wave
     int off_x, off_xsum, off_nw, off_part, off_red;  // LDS layout (bytes)
     int act;
     float eps;
 };
 size_t stream_layout(int fmt, int batch, bool ffn, int nb, int units_max, int pd, StreamArgs *a);
+size_t stream_pc_layout(int fmt, int batch, bool ffn, int nb, int units_max, int slots,
+                        StreamArgs *a);
 int stream_copies_per_step(int fmt, bool ffn);
 hipError_t launch_stream(int fmt, int batch, bool ffn, const StreamArgs &a, unsigned grid,
                          size_t lds, hipStream_t st);

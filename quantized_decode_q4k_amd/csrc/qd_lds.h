@@ -41,6 +41,22 @@ QD_DEV void lds_copy16(const void *src, uint32_t base) {
         : "memory");
 }
 
+// The same copy from a wave-uniform 64-bit base (scalar registers) plus a
+// per-lane 32-bit byte offset voff: issuing it takes no vector ALU
+// instruction.  No immediate offset is used: on an LDS-DMA load the
+// instruction offset moves the LDS destination as well as the source.
+QD_DEV void lds_copy16_s(const void *sbase, uint32_t voff, uint32_t base) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(sbase), "s"(base)
+        : "memory");
+}
+
 template <int N>
 QD_DEV void vm_wait() {
     static_assert(N >= 0 && N < 64, "vmcnt field");
@@ -50,6 +66,31 @@ QD_DEV void vm_wait() {
 QD_DEV void lgkm_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 QD_DEV void block_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Flags in LDS shared between the waves of a workgroup: a load that is
+// executed every time (ds_read_b32) and a plain store (ds_write_b32).  The
+// caller orders them against its other accesses with lgkm_wait / vm_wait and
+// the compiler barrier after a poll.
+QD_DEV int lds_poll(const int *p) {
+    return __atomic_load_n((const __attribute__((address_space(3))) int *)p, __ATOMIC_RELAXED);
+}
+QD_DEV void lds_flag(int *p, int v) {
+    __atomic_store_n((__attribute__((address_space(3))) int *)p, v, __ATOMIC_RELAXED);
+}
+// *p += v in LDS (ds_add_u32).
+QD_DEV void lds_add(int *p, int v) {
+    __atomic_fetch_add((__attribute__((address_space(3))) int *)p, v, __ATOMIC_RELAXED);
+}
+// Spin (with a short sleep between polls) until *p == v.
+QD_DEV void lds_wait_eq(const int *p, int v) {
+    while (lds_poll(p) != v) __builtin_amdgcn_s_sleep(1);
+    asm volatile("" ::: "memory");
+}
+// Spin until *p >= v.
+QD_DEV void lds_wait_ge(const int *p, int v) {
+    while (lds_poll(p) < v) __builtin_amdgcn_s_sleep(1);
+    asm volatile("" ::: "memory");
+}
 
 // Cross-lane sums with DPP (no LDS traffic).
 // v + v of lane ^ 1, then ^ 2 (every lane of a quad gets the quad's sum).

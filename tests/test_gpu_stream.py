@@ -3,12 +3,18 @@ one workgroup per row range) against the oracle.
 
 The path applies to batch 1 and 2 when the matrix is a whole number of
 16-byte chunks; it is taken automatically for long rows (K >= 8192) and
-forced here with the stream override (one and two workgroups per CU) on
-shapes chosen to split rows unevenly over workgroups, leave partial last
-steps and run fewer rows than workgroups.  A launch override forces the
+forced here with the stream override on shapes chosen to split rows
+unevenly over workgroups, leave partial last steps and run fewer rows than
+workgroups.  Both kernels are run: the one in which every wave copies and
+decodes (one and two workgroups per CU), and the producer / consumer kernel
+with 4 and 8 decoding waves and one or two copying waves.  The Gemma-3 down
+and gate/up shapes at two workgroups per CU hold more steps than the ring
+has slots, so the copying waves reuse slots; a depth override of 1 keeps a
+single step in flight per copying wave.  A launch override forces the
 register-streaming kernel, run on the same inputs as a second check.
 Bar: |y - y_ref| <= 1e-4 * sum|w x| + 1e-6 per output, h within the bound
-propagated through the activation.
+propagated through the activation; two runs of one launch shape agree bit
+for bit.
 """
 import numpy as np
 import pytest
@@ -29,15 +35,20 @@ def qd(gpu):
     qd.lib()
     yield qd
     qd.set_launch_override(0, 0, 0)
-    qd.set_stream_override(0, 0, 0)
+    qd.set_stream_override(0, 0, 0, 0)
 
 
-def forced(qd, wpc, fn, split=2):
-    qd.set_stream_override(wpc, 0 if split == 2 else 4, split)
+def forced(qd, wpc, fn, consumers=1, depth=0, producers=0):
+    qd.set_stream_override(wpc, depth, consumers, producers)
     try:
         return fn()
     finally:
-        qd.set_stream_override(0, 0, 0)
+        qd.set_stream_override(0, 0, 0, 0)
+
+
+# (workgroups per CU, decoding waves, copying waves): decoding waves 1 =
+# every wave copies and decodes
+VARIANTS = [(1, 1, 0), (2, 1, 0), (1, 4, 1), (1, 4, 2), (2, 4, 2), (1, 8, 1), (1, 8, 2), (2, 8, 2)]
 
 
 def streams(fmt, N, K):
@@ -59,12 +70,11 @@ def test_stream_gemv(qd, fmt, N, K, batch):
     x = synth.normal((batch, K), SEED, tensor_id=82)
     Wd, xd = dev(W), dev(x)
     y64, S = oracle.gemv(fmt, W, x, N, K)
-    for wpc in (1, 2):
-        for split in (2, 1):
-            y = forced(qd, wpc, lambda: qd.qgemv(fmt, Wd, xd).cpu().numpy(), split)
-            assert_bound(f"stream {fmt} wpc={wpc} split={split}", y, y64, S)
-            again = forced(qd, wpc, lambda: qd.qgemv(fmt, Wd, xd).cpu().numpy(), split)
-            assert np.array_equal(y.view(np.uint32), again.view(np.uint32))
+    for wpc, cons, prod in VARIANTS:
+        y = forced(qd, wpc, lambda: qd.qgemv(fmt, Wd, xd).cpu().numpy(), cons, 0, prod)
+        assert_bound(f"stream {fmt} wpc={wpc} consumers={cons} producers={prod}", y, y64, S)
+        again = forced(qd, wpc, lambda: qd.qgemv(fmt, Wd, xd).cpu().numpy(), cons, 0, prod)
+        assert np.array_equal(y.view(np.uint32), again.view(np.uint32))
     auto = qd.qgemv(fmt, Wd, xd).cpu().numpy()
     assert_bound(f"automatic {fmt}", auto, y64, S)
     qd.set_launch_override(2, 1, 1)
@@ -78,10 +88,10 @@ def test_stream_gemv(qd, fmt, N, K, batch):
 @pytest.mark.parametrize("fmt,N,K", [("q4_k", 300, 2048), ("q8_0", 40, 2560), ("q6_k", 48, 1024)])
 @pytest.mark.parametrize("batch,act,norm", [(1, "gelu_tanh", True), (2, "silu", True),
                                             (1, "silu", False)])
-@pytest.mark.parametrize("split", [2, 1])
-def test_stream_gate_up(qd, fmt, N, K, batch, act, norm, split):
+@pytest.mark.parametrize("consumers,producers", [(1, 0), (4, 1), (8, 2)])
+def test_stream_gate_up(qd, fmt, N, K, batch, act, norm, consumers, producers):
     assert streams(fmt, N, K)
-    say(f"stream gate/up {fmt} N={N} K={K} batch={batch} act={act} norm={norm} split={split}")
+    say(f"stream gate/up {fmt} N={N} K={K} batch={batch} act={act} norm={norm} consumers={consumers}")
     Wg = synth.quant_weights(fmt, N, K, SEED, tensor_id=83)
     Wu = synth.quant_weights(fmt, N, K, SEED, tensor_id=84)
     x = synth.normal((batch, K), SEED, tensor_id=85)
@@ -90,7 +100,8 @@ def test_stream_gate_up(qd, fmt, N, K, batch, act, norm, split):
     u = torch.empty((batch, N), device="cuda")
     h = forced(qd, 1, lambda: qd.qffn_gate_up_act(fmt, dev(Wg), dev(Wu), dev(x),
                                                    dev(nw) if norm else None, 1e-6, act,
-                                                   g_out=g, u_out=u).cpu().numpy(), split)
+                                                   g_out=g, u_out=u).cpu().numpy(), consumers, 0,
+               producers)
     g, u = g.cpu().numpy(), u.cpu().numpy()
     xn = (oracle.rmsnorm(x, nw, 1e-6) if norm else x.astype(np.float64)).astype(np.float32)
     g64, Sg = oracle.gemv(fmt, Wg, xn, N, K)
@@ -102,3 +113,48 @@ def test_stream_gate_up(qd, fmt, N, K, batch, act, norm, split):
     tol = h_tolerance(g64, u64, Sg, Su, aid)
     err = np.abs(h - href)
     assert (err <= tol).all(), f"h: worst {np.max(err / tol):.3f} of tolerance"
+
+
+# Gemma-3 down (Q6_K 2560 x 10240) and gate/up (Q4_K 10240 x 2560): at two
+# workgroups per CU a workgroup's steps outnumber the ring slots.
+@pytest.mark.parametrize("consumers", [4, 8])
+@pytest.mark.parametrize("depth", [0, 1])
+@pytest.mark.parametrize("producers", [1, 2])
+def test_stream_ring_reuse_down(qd, consumers, depth, producers):
+    fmt, N, K = "q6_k", 2560, 10240
+    say(f"stream ring reuse {fmt} N={N} K={K} consumers={consumers} depth={depth}")
+    W = synth.quant_weights(fmt, N, K, SEED, tensor_id=87)
+    x = synth.normal((1, K), SEED, tensor_id=88)
+    y64, S = oracle.gemv(fmt, W, x, N, K)
+    Wd, xd = dev(W), dev(x)
+    for wpc in (1, 2):
+        y = forced(qd, wpc, lambda: qd.qgemv(fmt, Wd, xd).cpu().numpy(), consumers, depth, producers)
+        assert_bound(f"down wpc={wpc}", y, y64, S)
+
+
+@pytest.mark.parametrize("consumers", [4, 8])
+@pytest.mark.parametrize("depth", [0, 1])
+@pytest.mark.parametrize("producers", [1, 2])
+def test_stream_ring_reuse_gate_up(qd, consumers, depth, producers):
+    fmt, N, K = "q4_k", 10240, 2560
+    say(f"stream ring reuse gate/up {fmt} N={N} K={K} consumers={consumers} depth={depth}")
+    Wg = synth.quant_weights(fmt, N, K, SEED, tensor_id=89)
+    Wu = synth.quant_weights(fmt, N, K, SEED, tensor_id=90)
+    x = synth.normal((1, K), SEED, tensor_id=91)
+    nw = synth.normal((K,), SEED, tensor_id=92, mean=1.0, std=0.1)
+    xn = oracle.rmsnorm(x, nw, 1e-6).astype(np.float32)
+    g64, Sg = oracle.gemv(fmt, Wg, xn, N, K)
+    u64, Su = oracle.gemv(fmt, Wu, xn, N, K)
+    aid = oracle.ACT_GELU_TANH
+    href = oracle.act_vec(aid, g64) * u64
+    tol = h_tolerance(g64, u64, Sg, Su, aid)
+    for wpc in (1, 2):
+        g = torch.empty((1, N), device="cuda")
+        u = torch.empty((1, N), device="cuda")
+        h = forced(qd, wpc, lambda: qd.qffn_gate_up_act(fmt, dev(Wg), dev(Wu), dev(x), dev(nw), 1e-6,
+                                                       "gelu_tanh", g_out=g, u_out=u).cpu().numpy(),
+                   consumers, depth, producers)
+        assert_bound(f"gate wpc={wpc}", g.cpu().numpy(), g64, Sg)
+        assert_bound(f"up wpc={wpc}", u.cpu().numpy(), u64, Su)
+        err = np.abs(h - href)
+        assert (err <= tol).all(), f"h wpc={wpc}: worst {np.max(err / tol):.3f} of tolerance"
