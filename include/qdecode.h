@@ -259,8 +259,8 @@ qd_status qd_set_gemm_override(int tm, int splits);
  *              ring and wait counter allow)
  *   consumers  1 = every wave copies and decodes; 4 or 8 = that many
  *              decoding waves beside the copying waves and one staging x
- *   producers  copying waves of the producer / consumer kernel (1 or 2;
- *              0 = 2); must be 0 unless consumers is 4 or 8
+ *   producers  copying waves of the producer / consumer kernel (1, 2 or 4;
+ *              0 = automatic); must be 0 unless consumers is 4 or 8
  * A non-zero wg_per_cu forces the streaming path where the shape allows it.
  * Returns QD_EINVAL for values outside these sets.
  */

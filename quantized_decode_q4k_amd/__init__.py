@@ -284,7 +284,7 @@ def set_gemm_override(tm: int = 0, splits: int = 0):
 def set_stream_override(wg_per_cu: int = 0, depth: int = 0, consumers: int = 0, producers: int = 0):
     """Streaming GEMV shape override (0 = automatic): workgroups per CU, steps
     in flight, decoding waves (1 = every wave copies and decodes; 4 or 8 = the
-    producer / consumer kernel) and its copying waves (1 or 2)."""
+    producer / consumer kernel) and its copying waves (1, 2 or 4)."""
     _check("qd_set_stream_override",
            lib().qd_set_stream_override(wg_per_cu, depth, consumers, producers))
 

@@ -267,17 +267,17 @@ bool stream_plan_pc(int fmt, bool ffn, int64_t N, int64_t K, int batch, const fl
 // register-streaming kernel is used instead: batch > 2, Q8_0 rows of partial
 // superunits, a matrix whose size is not a multiple of 16 bytes, an LDS
 // layout that does not fit, and (unless overridden) plain GEMVs with K <
-// 8192.  Measured on MI355X (graph replay, 1 GiB of rotating weights):
-//   * fused gate/up: the producer / consumer kernel, at one workgroup per CU
-//     with 8 decoding waves when a workgroup's whole row range fits in its
-//     ring (Gemma-3 10240 x 2560: 11.8 us, against 13.2 for the register
-//     kernel and 14.0 for the kernel in which every wave copies), else two
-//     per CU with 4 (Gemma-4 21504 x 5376: 32.1 us against 33.4);
-//   * plain GEMV with K >= 8192: every wave copies and decodes, two
-//     workgroups per CU, depth 3 (Gemma-3 down: 11.2 us against 11.7;
-//     Gemma-4 down 30.4 against 30.0 -- level);
-//   * K = 2560 plain GEMVs stay on the register kernel (lm_head 262144 rows:
-//     73 us against 91 or more on either streaming kernel).
+// 8192.  The fused gate/up and the long-row GEMVs take the producer /
+// consumer kernel with two copying waves and 3 steps in flight each: one
+// workgroup per CU with 8 decoding waves when a workgroup's whole row range
+// fits in its ring, else two per CU with 4.  Measured on MI355X (graph
+// replay, 1 GiB of rotating weights), against the register kernel:
+//   Gemma-3 gate/up 10240 x 2560:   10.9 us (13.3)
+//   Gemma-3 down Q6_K 2560 x 10240:  9.8 us (11.8)
+//   Gemma-4 gate/up 21504 x 5376:   32.1 us (33.4)
+//   Gemma-4 down Q6_K 5376 x 21504: 29.8 us (30.0)
+// K = 2560 plain GEMVs stay on the register kernel (lm_head 262144 rows:
+// 76-79 us against 87 or more on either streaming kernel).
 bool stream_plan(int fmt, bool ffn, int64_t N, int64_t K, int batch, const float *norm_w,
                  qd::StreamArgs *a, unsigned *grid, size_t *lds) {
     if (batch > 2) return false;
@@ -293,15 +293,12 @@ bool stream_plan(int fmt, bool ffn, int64_t N, int64_t K, int batch, const float
         }
         return stream_plan_wpc(fmt, ffn, N, K, batch, norm_w, wpc, a, grid, lds);
     }
-    if (ffn) {
-        // 8 decoding waves spill registers at batch 2
-        if (stream_plan_pc(fmt, ffn, N, K, batch, norm_w, 1, batch == 1 ? 8 : 4, 2, kPcLag, a, grid, lds) &&
-            a->slots * 16 >= a->units_max)
-            return true;
-        return stream_plan_pc(fmt, ffn, N, K, batch, norm_w, 2, 4, 2, kPcLag, a, grid, lds);
-    }
-    if (K < kStreamMinK) return false;
-    return stream_plan_wpc(fmt, ffn, N, K, batch, norm_w, 2, a, grid, lds);
+    if (!ffn && K < kStreamMinK) return false;
+    // 8 decoding waves spill registers at batch 2
+    if (stream_plan_pc(fmt, ffn, N, K, batch, norm_w, 1, batch == 1 ? 8 : 4, 2, kPcLag, a, grid, lds) &&
+        a->slots * 16 >= a->units_max)
+        return true;
+    return stream_plan_pc(fmt, ffn, N, K, batch, norm_w, 2, 4, 2, kPcLag, a, grid, lds);
 }
 
 qd_status run_mv(int fmt, bool ffn, const void *W0, const void *W1, const float *x,
@@ -705,7 +702,7 @@ qd_status qd_set_stream_override(int wg_per_cu, int depth, int consumers, int pr
     if (wg_per_cu < 0 || wg_per_cu > 8 || depth < 0 || depth > 32) return QD_EINVAL;
     if (consumers != 0 && consumers != 1 && consumers != 4 && consumers != 8) return QD_EINVAL;
     if (consumers <= 1 && (depth == 1 || depth > 8)) return QD_EINVAL;
-    if (producers < 0 || producers > 2 || (producers && consumers <= 1)) return QD_EINVAL;
+    if (producers < 0 || producers == 3 || producers > 4 || (producers && consumers <= 1)) return QD_EINVAL;
     g_stream_wpc.store(wg_per_cu);
     g_stream_depth.store(depth);
     g_stream_consumers.store(consumers);

@@ -510,20 +510,21 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamArgs a) {
 // wait on a workgroup barrier inside the stream.  A wave that issues copies
 // stalls at issue whenever the memory pipeline backs up, so the copying waves
 // do little else, and their copies are issued from scalar registers:
-//   * waves NC and NC + 1 copy (producers; the second only when the launch
-//     asks for two).  Producer 0 first copies x (and the norm weight) and
-//     raises xland once they have landed; no weight copy is issued before
-//     then, so x does not queue behind the weight stream.  Producer p then
-//     takes the steps j = p (mod producers), each into ring slot j % slots,
-//     keeping up to `lag` of its steps in flight; once one of its steps has
-//     landed (its own vmcnt) it stores the step number in ready[slot];
-//   * waves 0 .. NC-1 decode (consumers).  First they stage x together, a
-//     64-float4 slice at a time: x * w_norm in place, each wave's sum of
-//     squares of x (added in wave order, so the inverse RMS does not depend
-//     on timing), and for Q4_K the sum of every 32-run; they meet on a
-//     counter in LDS.  Then consumer c takes steps c, c + NC, ... and, after
-//     reading a step out of its slot, stores the number of its steps read
-//     so far in done[c].
+//   * waves 0 .. NC-1 decode (consumers).  First they copy x (and the norm
+//     weight) into LDS, each a share of the 1 KB copies, and count
+//     themselves on `landed` once theirs have landed.  Then they stage x
+//     together, a 64-float4 slice at a time: x * w_norm in place, each
+//     wave's sum of squares of x (added in wave order, so the inverse RMS
+//     does not depend on timing), and for Q4_K the sum of every 32-run;
+//     they meet on `staged`.  Then consumer c takes steps c, c + NC, ...
+//     and, after reading a step out of its slot, stores the number of its
+//     steps read so far in done[c];
+//   * waves NC .. NC + 3 copy the weights (producers; as many as the launch
+//     asks for, 1, 2 or 4, and the others idle).  They issue nothing before x has landed, so
+//     x does not queue behind the weight stream.  Producer p takes the
+//     steps j = p (mod producers), each into ring slot j % slots, keeping up
+//     to `lag` of its steps in flight; once one of its steps has landed (its
+//     own vmcnt) it stores the step number in ready[slot].
 // Slot reuse: producer p may refill the slot of step j once step j - slots
 // has been read, which it knows from the smallest done[] of its own
 // consumers (consumers c = p mod producers take only producer p's steps).
@@ -532,15 +533,17 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamArgs a) {
 // depends on has been published, so the wait ends.  The RMS factor is
 // applied to each row's sum at the end (every product is linear in the
 // staged activations).
+constexpr int kPcMaxProducers = 4;
+
 template <int FMT, int B, int NR, bool FFN, int NC>
-__global__ __launch_bounds__(64 * (NC + 2)) void stream_pc_kernel(StreamArgs a) {
+__global__ __launch_bounds__(64 * (NC + kPcMaxProducers)) void stream_pc_kernel(StreamArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr int UB = StreamFmt<FMT>::UB;
     constexpr int NCH = StreamFmt<FMT>::NCH;
     constexpr int NI = copies_per_step<FMT>();
     constexpr int SLOTM = NCH * 16;
     constexpr int CPS = NR * NI;  // copies per step
-    constexpr int NT = 64 * (NC + 2);
+    constexpr int NT = 64 * (NC + kPcMaxProducers);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -564,8 +567,8 @@ __global__ __launch_bounds__(64 * (NC + 2)) void stream_pc_kernel(StreamArgs a) 
     float *part = reinterpret_cast<float *>(smem + a.off_part);
     int *ready = reinterpret_cast<int *>(smem + a.off_red);
     int *done = ready + R;     // [NC]
-    int *xland = done + NC;
-    int *staged = xland + 1;
+    int *landed = done + NC;
+    int *staged = landed + 1;
     float *rinv = reinterpret_cast<float *>(staged + 1);  // [B]
     float *ssq = rinv + B;                                // [NC][B]
     const int xstride = nb * kSuperPhys;
@@ -576,42 +579,12 @@ __global__ __launch_bounds__(64 * (NC + 2)) void stream_pc_kernel(StreamArgs a) 
     for (int i = tid; i < R + NC + 2; i += NT) ready[i] = i < R ? -1 : 0;
     block_sync();
 
-    if (wv == NC || wv == NC + 1) {
+    if (wv >= NC) {
         // ---------------------------------------------------- producer ---
         const int p = wv - NC;
         if (p < NP) {
             __builtin_amdgcn_s_setprio(3);
-            if (p == 0) {
-                // x: batch row b, physical float4 q of the row (17 per 64-float
-                // run, the last a pad that receives a copy of x[0]) holds
-                // logical float4 16 * (q / 17) + q % 17
-                const int nq = nb * (kSuperPhys / 4);
-                int n = 0;
-#pragma unroll
-                for (int b = 0; b < B; b++) {
-                    const float *xb = a.x + (int64_t)b * K;
-                    float *dstrow = xl + b * xstride;
-                    for (int q0 = 0; q0 < nq; q0 += 64) {
-                        const int q = q0 + lane;
-                        const int run = q / 17, e = q - 17 * run;
-                        const float *srcp = (e < 16 && q < nq) ? xb + 4 * (16 * run + e) : xb;
-                        if (q0 + 64 <= nq || lane < nq - q0) lds_copy16(srcp, lds_addr(dstrow + 4 * q0));
-                        if (++n == 48) { vm_wait<16>(); n = 16; }
-                    }
-                }
-                if (norm) {
-                    const int nf4 = (int)(K / 4);
-                    for (int f0 = 0; f0 < nf4; f0 += 64) {
-                        if (f0 + 64 <= nf4 || lane < nf4 - f0)
-                            lds_copy16(a.norm_w + 4 * (int64_t)(f0 + lane), lds_addr(nwl + 4 * f0));
-                        if (++n == 48) { vm_wait<16>(); n = 16; }
-                    }
-                }
-                vm_wait<0>();
-                if (lane == 0) lds_flag(xland, 1);
-            } else {
-                lds_wait_eq(xland, 1);
-            }
+            lds_wait_eq(landed, NC);
             // weight steps j = p + NP * k
             constexpr int SB = kStepUnits * UB;  // bytes per step and matrix
             const int64_t base = wbeg & ~(int64_t)15;
@@ -677,8 +650,38 @@ __global__ __launch_bounds__(64 * (NC + 2)) void stream_pc_kernel(StreamArgs a) 
         }
     } else {
         // -------------------------------------------------- consumers ---
+        // copy x: batch row b, physical float4 q of the row (17 per 64-float
+        // run, the last a pad that receives a copy of x[0]) holds logical
+        // float4 16 * (q / 17) + q % 17; then the norm weight.  Copy i of
+        // the workgroup (64 float4 each) is issued by wave i % NC.
+        {
+            const int nq = nb * (kSuperPhys / 4);
+            const int xc = (nq + 63) / 64;               // copies per batch row of x
+            const int nf4 = norm ? (int)(K / 4) : 0;
+            const int total = B * xc + (nf4 + 63) / 64;
+            int n = 0;
+            for (int i = wv; i < total; i += NC) {
+                if (i < B * xc) {
+                    const int b = i / xc;
+                    const int q0 = 64 * (i - b * xc);
+                    const int q = q0 + lane;
+                    const int run = q / 17, e = q - 17 * run;
+                    const float *xb = a.x + (int64_t)b * K;
+                    const float *srcp = (e < 16 && q < nq) ? xb + 4 * (16 * run + e) : xb;
+                    if (q0 + 64 <= nq || lane < nq - q0)
+                        lds_copy16(srcp, lds_addr(xl + b * xstride + 4 * q0));
+                } else {
+                    const int f0 = 64 * (i - B * xc);
+                    if (f0 + 64 <= nf4 || lane < nf4 - f0)
+                        lds_copy16(a.norm_w + 4 * (int64_t)(f0 + lane), lds_addr(nwl + 4 * f0));
+                }
+                if (++n == 48) { vm_wait<16>(); n = 16; }
+            }
+            vm_wait<0>();
+            if (lane == 0) lds_add(landed, 1);
+        }
         // stage x: slice it (64 float4 of one batch row) goes to wave it % NC
-        lds_wait_eq(xland, 1);
+        lds_wait_eq(landed, NC);
         const int F = nb * (kSuper / 4);  // logical float4 per batch row (a multiple of 64)
         const int nit = F / 64;
         float ss[B];
@@ -821,7 +824,7 @@ size_t stream_pc_layout(int fmt, int batch, bool ffn, int nb, int units_max, int
     if (a->norm_w) off += (size_t)nb * kSuper * 4;
     a->off_part = (int)off;
     off += (size_t)NR * batch * units_max * 4;
-    a->off_red = (int)off;  // ready[slots], done[consumers], xland, staged, rinv[batch], ssq[consumers][batch]
+    a->off_red = (int)off;  // ready[slots], done[consumers], landed, staged, rinv[batch], ssq[consumers][batch]
     off += (size_t)(slots + a->consumers + 2 + batch + a->consumers * batch) * 4;
     return (off + 15) & ~(size_t)15;
 }
@@ -849,7 +852,7 @@ template <int FMT, int B, bool FFN, int NC>
 static hipError_t launch_pc(const StreamArgs &a, unsigned grid, size_t lds, hipStream_t st) {
     constexpr int NR = FFN ? 2 : 1;
     if (allow_lds<stream_pc_kernel<FMT, B, NR, FFN, NC>>() != hipSuccess) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((stream_pc_kernel<FMT, B, NR, FFN, NC>), dim3(grid), dim3(64 * (NC + 2)), lds,
+    hipLaunchKernelGGL((stream_pc_kernel<FMT, B, NR, FFN, NC>), dim3(grid), dim3(64 * (NC + kPcMaxProducers)), lds,
                        st, a);
     return hipGetLastError();
 }

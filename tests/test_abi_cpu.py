@@ -158,7 +158,9 @@ def test_stream_override_validation():
     assert L.qd_set_stream_override(1, 0, 3, 0) == 1      # decoding waves 1, 4 or 8
     assert L.qd_set_stream_override(1, 9, 1, 0) == 1      # depth <= 8 per copying-and-decoding wave
     assert L.qd_set_stream_override(1, 33, 4, 0) == 1     # depth <= 32 per copying wave
-    assert L.qd_set_stream_override(1, 0, 4, 3) == 1      # one or two copying waves
+    assert L.qd_set_stream_override(1, 0, 4, 3) == 1      # one, two or four copying waves
+    assert L.qd_set_stream_override(1, 0, 8, 8) == 1
+    assert L.qd_set_stream_override(1, 0, 8, 4) == 0
     assert L.qd_set_stream_override(1, 0, 1, 2) == 1      # copying waves only with decoding waves
     assert L.qd_set_stream_override(1, 1, 8, 1) == 0
     assert L.qd_set_stream_override(1, 16, 8, 2) == 0

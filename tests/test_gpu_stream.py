@@ -7,7 +7,7 @@ forced here with the stream override on shapes chosen to split rows
 unevenly over workgroups, leave partial last steps and run fewer rows than
 workgroups.  Both kernels are run: the one in which every wave copies and
 decodes (one and two workgroups per CU), and the producer / consumer kernel
-with 4 and 8 decoding waves and one or two copying waves.  The Gemma-3 down
+with 4 and 8 decoding waves and one, two or four copying waves.  The Gemma-3 down
 and gate/up shapes at two workgroups per CU hold more steps than the ring
 has slots, so the copying waves reuse slots; a depth override of 1 keeps a
 single step in flight per copying wave.  A launch override forces the
@@ -48,7 +48,8 @@ def forced(qd, wpc, fn, consumers=1, depth=0, producers=0):
 
 # (workgroups per CU, decoding waves, copying waves): decoding waves 1 =
 # every wave copies and decodes
-VARIANTS = [(1, 1, 0), (2, 1, 0), (1, 4, 1), (1, 4, 2), (2, 4, 2), (1, 8, 1), (1, 8, 2), (2, 8, 2)]
+VARIANTS = [(1, 1, 0), (2, 1, 0), (1, 4, 1), (1, 4, 2), (1, 4, 4), (2, 4, 2), (1, 8, 1), (1, 8, 2),
+            (1, 8, 4), (2, 8, 2)]
 
 
 def streams(fmt, N, K):
@@ -88,7 +89,7 @@ def test_stream_gemv(qd, fmt, N, K, batch):
 @pytest.mark.parametrize("fmt,N,K", [("q4_k", 300, 2048), ("q8_0", 40, 2560), ("q6_k", 48, 1024)])
 @pytest.mark.parametrize("batch,act,norm", [(1, "gelu_tanh", True), (2, "silu", True),
                                             (1, "silu", False)])
-@pytest.mark.parametrize("consumers,producers", [(1, 0), (4, 1), (8, 2)])
+@pytest.mark.parametrize("consumers,producers", [(1, 0), (4, 1), (8, 2), (8, 4)])
 def test_stream_gate_up(qd, fmt, N, K, batch, act, norm, consumers, producers):
     assert streams(fmt, N, K)
     say(f"stream gate/up {fmt} N={N} K={K} batch={batch} act={act} norm={norm} consumers={consumers}")
@@ -119,7 +120,7 @@ def test_stream_gate_up(qd, fmt, N, K, batch, act, norm, consumers, producers):
 # workgroups per CU a workgroup's steps outnumber the ring slots.
 @pytest.mark.parametrize("consumers", [4, 8])
 @pytest.mark.parametrize("depth", [0, 1])
-@pytest.mark.parametrize("producers", [1, 2])
+@pytest.mark.parametrize("producers", [1, 2, 4])
 def test_stream_ring_reuse_down(qd, consumers, depth, producers):
     fmt, N, K = "q6_k", 2560, 10240
     say(f"stream ring reuse {fmt} N={N} K={K} consumers={consumers} depth={depth}")
@@ -134,7 +135,7 @@ def test_stream_ring_reuse_down(qd, consumers, depth, producers):
 
 @pytest.mark.parametrize("consumers", [4, 8])
 @pytest.mark.parametrize("depth", [0, 1])
-@pytest.mark.parametrize("producers", [1, 2])
+@pytest.mark.parametrize("producers", [1, 2, 4])
 def test_stream_ring_reuse_gate_up(qd, consumers, depth, producers):
     fmt, N, K = "q4_k", 10240, 2560
     say(f"stream ring reuse gate/up {fmt} N={N} K={K} consumers={consumers} depth={depth}")
