@@ -156,9 +156,13 @@ qd_status qffn_gate_up_act(qd_format fmt, const void *Wg, const void *Wu,
  *
  * The whole decode FFN of one layer (larql Gemma 3 table: input norm ->
  * q4k_ffn_gate_up_8sg -> geglu -> q6k_matvec), as qffn_gate_up_act followed
- * by qgemv on the same stream, with h kept in the library's workspace.  A
- * single-launch variant (down-projection workgroups wait for their slice of
- * h inside the same launch) is selected with qd_set_ffn_override.
+ * by qgemv on the same stream, with h kept in the library's workspace.  Two
+ * single-launch forms exist: with qd_set_ffn_mode(2), at batch 1 when K and
+ * N_ff are multiples of 256 and both matrices whole numbers of 16-byte
+ * chunks, one workgroup per CU runs the gate/up phase, writes h, meets the
+ * others at a grid barrier and runs the down phase (its weights stream in
+ * during the gate/up phase); with qd_set_ffn_override, down-projection
+ * workgroups wait for their slice of h.
  *
  *   fmt_gu, Wg, Wu   gate and up, N_ff x K
  *   fmt_down, Wd     down, K x N_ff
@@ -167,8 +171,13 @@ qd_status qffn_gate_up_act(qd_format fmt, const void *Wg, const void *Wu,
  *   h_out            optional fp32 [batch][N_ff] copy of h (NULL = kept in
  *                    the library's workspace), 16-byte aligned
  * Accuracy: h as in qffn_gate_up_act; y meets the GEMV bound for the h it
- * was computed from.  The single launch exists for Q4_K gate/up with Q6_K or
- * Q4_K down and for Q8_0 throughout, when batch * K fits one workgroup's LDS.
+ * was computed from.  The older single launch exists for Q4_K gate/up with
+ * Q6_K or Q4_K down and for Q8_0 throughout, when batch * K fits one
+ * workgroup's LDS.  The grid-barrier form needs every workgroup of its grid
+ * resident at once (one per CU); its barrier wait is bounded, so on a device
+ * shared with other work it returns wrong values rather than hanging -- use
+ * it only on an otherwise idle device.
+ * Calls that overlap on one stream's workspace race (h and the barrier).
  */
 qd_status qffn_decode(qd_format fmt_gu, const void *Wg, const void *Wu, qd_format fmt_down,
                       const void *Wd, const float *x, const float *norm_w, float eps, qd_act act,
@@ -242,6 +251,13 @@ qd_status qd_set_launch_override(int p_in, int p_out, int nr);
  * p_in of the gate/up tiles, p_in and K-slices of the down tiles.
  */
 qd_status qd_set_ffn_override(int p_in_a, int p_in_b, int p_out_b);
+
+/*
+ * qffn_decode's form (process-wide): 0 = automatic (the two launches),
+ * 1 = the two launches, 2 = the one launch with a grid barrier where the
+ * shape allows it (else the two launches).  QD_EINVAL otherwise.
+ */
+qd_status qd_set_ffn_mode(int mode);
 
 /*
  * Tile override of the prefill GEMMs (0 = automatic): tm = 2 or 4 (tokens

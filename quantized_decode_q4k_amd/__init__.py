@@ -57,6 +57,7 @@ SIGNATURES = {
     "qd_set_ffn_override": (_I, [_I, _I, _I]),
     "qd_set_gemm_override": (_I, [_I, _I]),
     "qd_set_stream_override": (_I, [_I, _I, _I, _I]),
+    "qd_set_ffn_mode": (_I, [_I]),
 }
 
 _lock = threading.Lock()
@@ -287,6 +288,12 @@ def set_stream_override(wg_per_cu: int = 0, depth: int = 0, consumers: int = 0, 
     producer / consumer kernel) and its copying waves (1, 2 or 4)."""
     _check("qd_set_stream_override",
            lib().qd_set_stream_override(wg_per_cu, depth, consumers, producers))
+
+
+def set_ffn_mode(mode: int = 0):
+    """qffn_decode's form: 0 = automatic (two launches), 1 = two launches,
+    2 = one launch with a grid barrier where the shape allows it."""
+    _check("qd_set_ffn_mode", lib().qd_set_ffn_mode(mode))
 
 
 def set_launch_override(p_in: int = 0, p_out: int = 0, nr: int = 0):

@@ -59,6 +59,7 @@ std::atomic<int> g_ffn_pin_a{0}, g_ffn_pin_b{0}, g_ffn_pout_b{0};
 constexpr int kTargetWorkgroups = 400;   // enough to keep every CU streaming
 constexpr int kMaxTiles = 1 << 16;       // split-K counters per workspace
 constexpr int kCtlSlots = qd::kFfnCtlWords;  // leading counters: the fused FFN's control block
+constexpr int kBarWords = 64;                  // trailing counters: the one-launch FFN's grid barrier
 
 int lds_units_max(int fmt, int batch) {
     // largest nk whose staging fits the per-workgroup LDS budget
@@ -147,11 +148,11 @@ qd_status get_workspace(hipStream_t st, size_t need_floats, Workspace *out) {
         float *p = nullptr;
         unsigned *c = nullptr;
         if (hipMalloc(&p, n * sizeof(float)) != hipSuccess) return QD_ENOMEM;
-        if (hipMalloc(&c, (kMaxTiles + kCtlSlots) * sizeof(unsigned)) != hipSuccess) {
+        if (hipMalloc(&c, (kMaxTiles + kCtlSlots + kBarWords) * sizeof(unsigned)) != hipSuccess) {
             (void)hipFree(p);
             return QD_ENOMEM;
         }
-        if (hipMemsetAsync(c, 0, (kMaxTiles + kCtlSlots) * sizeof(unsigned), st) != hipSuccess) {
+        if (hipMemsetAsync(c, 0, (kMaxTiles + kCtlSlots + kBarWords) * sizeof(unsigned), st) != hipSuccess) {
             (void)hipFree(p);
             (void)hipFree(c);
             return QD_ELAUNCH;
@@ -375,6 +376,51 @@ qd_status run_mv(int fmt, bool ffn, const void *W0, const void *W1, const float 
 
 // y = Wd (act(Wg xn) * (Wu xn)) in one launch when the shapes allow it,
 // else as the two calls qffn_gate_up_act + qgemv on the same stream.
+std::atomic<int> g_ffn_mode{0};  // 0 = automatic (two launches), 1 = two launches, 2 = one streaming launch
+
+// One-launch FFN plan (batch 1): one workgroup per CU; phase A's ring holds
+// up to 12 steps (reused), phase B's as many as fit, at least 8 each unless
+// a workgroup has fewer steps.  False where the shape does not qualify.
+bool ffn_stream_plan(int fmt_a, int fmt_b, int64_t N_ff, int64_t K, const float *norm_w,
+                     qd::FfnStreamArgs *a, unsigned *grid, size_t *lds) {
+    if (K % qd::kSuper != 0 || N_ff % qd::kSuper != 0) return false;
+    const int64_t rbA = row_bytes(fmt_a, K), rbB = row_bytes(fmt_b, N_ff);
+    if ((N_ff * rbA) % 16 != 0 || (K * rbB) % 16 != 0) return false;
+    const int G = (int)std::min<int64_t>(std::min<int64_t>(N_ff, K), kCUs);
+    a->KA = K;
+    a->KB = N_ff;
+    a->row_bytesA = rbA;
+    a->row_bytesB = rbB;
+    a->mat_bytesA = N_ff * rbA;
+    a->mat_bytesB = K * rbB;
+    a->nbA = (int)(K / qd::kSuper);
+    a->nbB = (int)(N_ff / qd::kSuper);
+    a->rowsA_base = (int)(N_ff / G);
+    a->rowsA_extra = (int)(N_ff % G);
+    a->rowsB_base = (int)(K / G);
+    a->rowsB_extra = (int)(K % G);
+    a->unitsA_max = (a->rowsA_base + (a->rowsA_extra > 0 ? 1 : 0)) * a->nbA;
+    a->unitsB_max = (a->rowsB_base + (a->rowsB_extra > 0 ? 1 : 0)) * a->nbB;
+    const int SA = (a->unitsA_max + 15) / 16, SB = (a->unitsB_max + 15) / 16;
+    const bool norm = norm_w != nullptr;
+    const int minA = std::min(SA, 8), minB = std::min(SB, 8);
+    for (int slotsA = std::min(SA, 12); slotsA >= minA; slotsA--) {
+        int slotsB = SB;
+        while (slotsB >= minB && qd::ffn_stream_layout(fmt_a, fmt_b, norm, slotsA, slotsB, a) > kLdsPerCU)
+            slotsB--;
+        if (slotsB < minB) continue;
+        *lds = qd::ffn_stream_layout(fmt_a, fmt_b, norm, slotsA, slotsB, a);
+        a->slotsA = slotsA;
+        a->slotsB = slotsB;
+        const int lag_max = 1 + kStreamMaxWait / qd::ffn_stream_copies(fmt_a, fmt_b);
+        const int d = g_stream_depth.load();
+        a->lag = std::max(1, std::min(d ? d : 3, lag_max));
+        *grid = (unsigned)G;
+        return true;
+    }
+    return false;
+}
+
 qd_status run_ffn_decode(int fmt_gu, const void *Wg, const void *Wu, int fmt_d, const void *Wd,
                          const float *x, const float *norm_w, float eps, int act, float *y,
                          float *h_out, int64_t N_ff, int64_t K, int batch, void *stream) {
@@ -423,6 +469,34 @@ qd_status run_ffn_decode(int fmt_gu, const void *Wg, const void *Wu, int fmt_d, 
     // graph replay: 31.9 us vs 24.6), because its down-projection
     // workgroups only become resident as gate/up workgroups retire.
     const bool asked = g_ffn_pin_a.load() || g_ffn_pin_b.load() || g_ffn_pout_b.load();
+    // The one streaming launch is correct but slower on the Gemma shapes
+    // (MI355X, graph replay: Gemma-3 24.9 us against 21.5 for two launches,
+    // Gemma-4 80.3 against 66.5): the two rings do not fit in LDS together,
+    // so phase A runs on a 12-step ring, and h's device-scope stores and the
+    // grid barrier add 3-5 us under the down weights' stream.  Used only
+    // when asked for.
+    if (!asked && g_ffn_mode.load() == 2 && batch == 1) {
+        qd::FfnStreamArgs fa{};
+        unsigned grid = 0;
+        size_t lds = 0;
+        if (ffn_stream_plan(fmt_gu, fmt_d, N_ff, K, norm_w, &fa, &grid, &lds)) {
+            Workspace w;
+            st = get_workspace(hs, std::max<size_t>(h_floats, 64), &w);
+            if (st != QD_OK) return st;
+            fa.Wg = static_cast<const uint8_t *>(Wg);
+            fa.Wu = static_cast<const uint8_t *>(Wu);
+            fa.Wd = static_cast<const uint8_t *>(Wd);
+            fa.x = x;
+            fa.norm_w = norm_w;
+            fa.h = h_out ? h_out : w.partials;
+            fa.y = y;
+            fa.bar = w.counters + kCtlSlots + kMaxTiles;
+            fa.act = act;
+            fa.eps = eps;
+            hipError_t e = qd::launch_ffn_stream(fmt_gu, fmt_d, fa, grid, lds, hs);
+            return e == hipSuccess ? QD_OK : QD_ELAUNCH;
+        }
+    }
     const bool fused = asked && fits && qd::ffn_fused_supported(fmt_gu, fmt_d) &&
                        pb.s.p_out * 64 <= kCtlSlots && pb.tiles <= kMaxTiles;
     if (!fused) {
@@ -695,6 +769,12 @@ qd_status qd_set_ffn_override(int p_in_a, int p_in_b, int p_out_b) {
     g_ffn_pin_a.store(p_in_a);
     g_ffn_pin_b.store(p_in_b);
     g_ffn_pout_b.store(p_out_b);
+    return QD_OK;
+}
+
+qd_status qd_set_ffn_mode(int mode) {
+    if (mode < 0 || mode > 2) return QD_EINVAL;
+    g_ffn_mode.store(mode);
     return QD_OK;
 }
 

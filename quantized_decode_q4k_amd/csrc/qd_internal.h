@@ -101,6 +101,31 @@ int stream_copies_per_step(int fmt, bool ffn);
 hipError_t launch_stream(int fmt, int batch, bool ffn, const StreamArgs &a, unsigned grid,
                          size_t lds, hipStream_t st);
 
+// One-launch decode FFN on the producer / consumer stream (qd_gemv_stream.hip),
+// batch 1: phase A = gate/up (NA = N_ff rows of KA = hidden), phase B = down
+// (NB = hidden rows of KB = N_ff), one workgroup per CU.
+struct FfnStreamArgs {
+    const uint8_t *Wg, *Wu, *Wd;
+    const float *x;         // [KA]
+    const float *norm_w;    // [KA] or nullptr
+    float *h;               // [NA]: device-scope stores in phase A, loads in phase B
+    float *y;               // [NB]
+    unsigned *bar;          // grid barrier: [0] arrivals, [32] generation (zero-initialised)
+    int64_t KA, KB;
+    int64_t row_bytesA, row_bytesB, mat_bytesA, mat_bytesB;
+    int nbA, nbB;
+    int rowsA_base, rowsA_extra, rowsB_base, rowsB_extra;
+    int unitsA_max, unitsB_max;
+    int slotsA, slotsB, lag;
+    int off_ringA, off_ringB, off_xA, off_xsA, off_nwA, off_xB, off_xsB, off_partA, off_partB, off_flags;
+    int act;
+    float eps;
+};
+size_t ffn_stream_layout(int fmt_a, int fmt_b, bool norm, int slotsA, int slotsB, FfnStreamArgs *a);
+int ffn_stream_copies(int fmt_a, int fmt_b);
+hipError_t launch_ffn_stream(int fmt_a, int fmt_b, const FfnStreamArgs &a, unsigned grid, size_t lds,
+                             hipStream_t st);
+
 // Prefill GEMM (qd_prefill.hip).  A workgroup owns 32*tm tokens by 256
 // output columns (plain: 256 weight rows; FFN: 128 rows of gate and of up)
 // over K-tiles [kt_per_split*ks, ...) of 128 weights.

@@ -41,6 +41,20 @@ QD_DEV void lds_copy16(const void *src, uint32_t base) {
         : "memory");
 }
 
+// The same copy with device-scope coherence (sc1): data another workgroup
+// stored with device-scope stores earlier in the same launch.
+QD_DEV void lds_copy16_coh(const void *src, uint32_t base) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %1, off sc1\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(__builtin_amdgcn_readfirstlane(base))
+        : "memory");
+}
+
 // The same copy from a wave-uniform 64-bit base (scalar registers) plus a
 // per-lane 32-bit byte offset voff: issuing it takes no vector ALU
 // instruction.  No immediate offset is used: on an LDS-DMA load the

@@ -168,6 +168,14 @@ def test_stream_override_validation():
     assert L.qd_set_stream_override(0, 0, 0, 0) == 0
 
 
+def test_ffn_mode_validation():
+    _, L = _lib()
+    assert L.qd_set_ffn_mode(3) == 1
+    assert L.qd_set_ffn_mode(-1) == 1
+    assert L.qd_set_ffn_mode(2) == 0
+    assert L.qd_set_ffn_mode(0) == 0
+
+
 def test_launch_override_validation():
     _, L = _lib()
     assert L.qd_set_launch_override(3, 0, 0) == 1

@@ -307,79 +307,101 @@ def test_config_gemma4_31b_ffn(qd, batch):
 
 
 # ------------------------------------------------- whole decode FFN (one call) ---
+# Modes: "auto" (the two launches), "grid" the one launch with a grid
+# barrier at batch 1 where the shape allows it, "single" the older one-launch
+# form.  Repetitions alternate two inputs, so an h left over from the
+# previous call cannot pass.
 
-def check_ffn_decode(qd, fg, fd, hidden, ff, batch, act, tag, with_h=True, reps=2, single=False):
-    """qffn_decode against the oracle chain; single=True selects the one-launch
-    variant (down tiles wait for their h slice inside the launch)."""
-    if single:
+def check_ffn_decode(qd, fg, fd, hidden, ff, batch, act, tag, with_h=True, reps=3, mode="auto", rows=None):
+    """qffn_decode against the oracle chain (rows: output rows of y checked)."""
+    if mode == "single":
         qd.set_ffn_override(2, 2, 0)
+    elif mode == "grid":
+        qd.set_ffn_mode(2)
     try:
-        _check_ffn_decode(qd, fg, fd, hidden, ff, batch, act, tag, with_h, reps)
+        _check_ffn_decode(qd, fg, fd, hidden, ff, batch, act, f"{tag} [{mode}]", with_h, reps, rows)
     finally:
         qd.set_ffn_override(0, 0, 0)
+        qd.set_ffn_mode(0)
 
 
-def _check_ffn_decode(qd, fg, fd, hidden, ff, batch, act, tag, with_h, reps):
+def _check_ffn_decode(qd, fg, fd, hidden, ff, batch, act, tag, with_h, reps, rows):
     Wg = synth.quant_weights(fg, ff, hidden, SEED, tensor_id=51)
     Wu = synth.quant_weights(fg, ff, hidden, SEED, tensor_id=52)
     Wd = synth.quant_weights(fd, hidden, ff, SEED, tensor_id=53)
-    x = synth.normal((batch, hidden), SEED, tensor_id=54)
     nw = synth.normal((hidden,), SEED, tensor_id=55, mean=1.0, std=0.1)
-    xn32 = oracle.rmsnorm(x, nw, 1e-6).astype(np.float32)
-    g64, Sg = oracle.gemv(fg, Wg, xn32, ff, hidden)
-    u64, Su = oracle.gemv(fg, Wu, xn32, ff, hidden)
+    xs = [synth.normal((batch, hidden), SEED, tensor_id=54), synth.normal((batch, hidden), SEED, tensor_id=56)]
     aid = oracle.ACT_GELU_TANH if act == "gelu_tanh" else oracle.ACT_SILU
-    href = oracle.act_vec(aid, g64) * u64
-    tol = h_tolerance(g64, u64, Sg, Su, aid)
-    args = [dev(a) for a in (Wg, Wu, Wd, x, nw)]
-    first = None
-    for rep in range(reps):   # the control block must be reset for the next call
+    refs = []
+    for x in xs:
+        xn32 = oracle.rmsnorm(x, nw, 1e-6).astype(np.float32)
+        g64, Sg = oracle.gemv(fg, Wg, xn32, ff, hidden)
+        u64, Su = oracle.gemv(fg, Wu, xn32, ff, hidden)
+        refs.append((oracle.act_vec(aid, g64) * u64, h_tolerance(g64, u64, Sg, Su, aid)))
+    dW = [dev(a) for a in (Wg, Wu, Wd, nw)]
+    dx = [dev(x) for x in xs]
+    firsts = [None, None]
+    wabs = None
+    for rep in range(reps):
+        i = rep % 2
         say(f"ffn_decode {tag} {fg}->{fd} hidden={hidden} ff={ff} batch={batch} rep={rep}")
+        href, tol = refs[i]
         h = torch.empty((batch, ff), device="cuda") if with_h else None
-        y = qd.qffn_decode(fg, args[0], args[1], fd, args[2], args[3], args[4], 1e-6, act, h_out=h)
+        y = qd.qffn_decode(fg, dW[0], dW[1], fd, dW[2], dx[i], dW[3], 1e-6, act, h_out=h)
         y = y.cpu().numpy()
         if with_h:
             hh = h.cpu().numpy()
             err = np.abs(hh - href)
             assert (err <= tol).all(), f"{tag} h: worst {np.max(err / tol):.3f} of tolerance"
-            yref, Sy = oracle.gemv(fd, Wd, hh, hidden, ff)
-            assert_bound(f"{tag} y", y, yref, Sy)
+            if rows is None:
+                yref, Sy = oracle.gemv(fd, Wd, hh, hidden, ff)
+                assert_bound(f"{tag} y", y, yref, Sy)
+            else:
+                yref, Sy = _gemv_rows(fd, Wd, hh, hidden, ff, rows)
+                assert_bound(f"{tag} y", y, yref, Sy, rows)
         else:
             # y against the all-oracle chain: the bound of the down GEMV on the
             # exact h, widened by the h tolerance carried through |Wd|
             yref, Sy = oracle.gemv(fd, Wd, href.astype(np.float32), hidden, ff)
-            wabs = np.abs(oracle.dequant(fd, Wd, ff)).astype(np.float64)
+            if wabs is None:
+                wabs = np.abs(oracle.dequant(fd, Wd, ff)).astype(np.float64)
             slack = tol @ wabs.T
             err = np.abs(y - yref)
             assert (err <= 1e-4 * Sy + 1e-6 + slack).all(), f"{tag} y vs chain"
-        if first is None:
-            first = y.copy()
+        if firsts[i] is None:
+            firsts[i] = y.copy()
         else:
-            assert np.array_equal(first.view(np.uint32), y.view(np.uint32)), "not deterministic"
+            assert np.array_equal(firsts[i].view(np.uint32), y.view(np.uint32)), "not deterministic"
 
 
 @pytest.mark.parametrize("fg,fd,act,batch", [
     ("q4_k", "q6_k", "gelu_tanh", 1), ("q4_k", "q6_k", "silu", 3), ("q4_k", "q4_k", "silu", 1),
-    ("q8_0", "q8_0", "gelu_tanh", 2), ("q6_k", "q6_k", "gelu_tanh", 1)])
-@pytest.mark.parametrize("single", [False, True])
-def test_ffn_decode_small(qd, fg, fd, act, batch, single):
-    check_ffn_decode(qd, fg, fd, 512, 1536, batch, act, "small", single=single)
+    ("q8_0", "q8_0", "gelu_tanh", 2), ("q8_0", "q8_0", "silu", 1), ("q6_k", "q6_k", "gelu_tanh", 1),
+    ("q6_k", "q4_k", "silu", 1)])
+@pytest.mark.parametrize("mode", ["auto", "grid", "single"])
+def test_ffn_decode_small(qd, fg, fd, act, batch, mode):
+    check_ffn_decode(qd, fg, fd, 512, 1536, batch, act, "small", mode=mode)
 
 
-@pytest.mark.parametrize("single", [False, True])
-def test_ffn_decode_without_h_out(qd, single):
-    check_ffn_decode(qd, "q4_k", "q6_k", 512, 1024, 1, "gelu_tanh", "no-h", with_h=False,
-                     single=single)
+@pytest.mark.parametrize("mode", ["auto", "grid", "single"])
+def test_ffn_decode_without_h_out(qd, mode):
+    check_ffn_decode(qd, "q4_k", "q6_k", 512, 1024, 1, "gelu_tanh", "no-h", with_h=False, mode=mode)
 
 
-@pytest.mark.parametrize("single", [False, True])
-def test_ffn_decode_gemma3(qd, single):
-    check_ffn_decode(qd, "q4_k", "q6_k", 2560, 10240, 1, "gelu_tanh", "gemma3-4b", reps=3,
-                     single=single)
+@pytest.mark.parametrize("mode", ["auto", "grid", "single"])
+def test_ffn_decode_gemma3(qd, mode):
+    check_ffn_decode(qd, "q4_k", "q6_k", 2560, 10240, 1, "gelu_tanh", "gemma3-4b", reps=4, mode=mode)
+
+
+def test_ffn_decode_gemma4_31b_batch1(qd):
+    """Gemma-4-31B FFN at batch 1 in the grid-barrier launch: both rings are reused."""
+    rows = np.unique(np.concatenate([np.arange(0, 256), np.arange(5376 - 256, 5376), np.arange(0, 5376, 7)]))
+    check_ffn_decode(qd, "q4_k", "q6_k", 5376, 21504, 1, "gelu_tanh", "gemma4-31b b1", reps=2, rows=rows,
+                     mode="grid")
 
 
 def test_ffn_decode_gemma4_31b_batch8_falls_back(qd):
     """batch 8 x K = 5376 does not fit one workgroup's LDS: two launches even
     when the single launch is asked for."""
     check_ffn_decode(qd, "q4_k", "q6_k", 5376, 21504, 8, "gelu_tanh", "gemma4-31b b8", reps=1,
-                     single=True)
+                     mode="single")
