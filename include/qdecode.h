@@ -246,6 +246,14 @@ qd_status qdequant_bf16(qd_format fmt, const void *W, uint16_t *out,
 qd_status qd_set_launch_override(int p_in, int p_out, int nr);
 
 /*
+ * Row slots each lane group of the register-streaming GEMV walks one after
+ * another (process-wide; 0 = automatic, else 1..64).  Larger values give
+ * each workgroup more rows for the one staging of its activation slice.
+ * Returns QD_EINVAL outside 0..64.
+ */
+qd_status qd_set_walk_override(int rows_per_group);
+
+/*
  * Selects qffn_decode's single launch (any non-zero value; all zero = the
  * two launches) and its launch shape (0 = automatic):
  * p_in of the gate/up tiles, p_in and K-slices of the down tiles.

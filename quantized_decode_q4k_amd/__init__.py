@@ -54,6 +54,7 @@ SIGNATURES = {
     "qdequant": (_I, [_I, _P, _P, _I64, _I64, _P]),
     "qdequant_bf16": (_I, [_I, _P, _P, _I64, _I64, _P]),
     "qd_set_launch_override": (_I, [_I, _I, _I]),
+    "qd_set_walk_override": (_I, [_I]),
     "qd_set_ffn_override": (_I, [_I, _I, _I]),
     "qd_set_gemm_override": (_I, [_I, _I]),
     "qd_set_stream_override": (_I, [_I, _I, _I, _I]),
@@ -294,6 +295,12 @@ def set_ffn_mode(mode: int = 0):
     """qffn_decode's form: 0 = automatic (two launches), 1 = two launches,
     2 = one launch with a grid barrier where the shape allows it."""
     _check("qd_set_ffn_mode", lib().qd_set_ffn_mode(mode))
+
+
+def set_walk_override(rows_per_group: int = 0):
+    """Row slots each lane group of the register-streaming GEMV walks
+    (0 = automatic)."""
+    _check("qd_set_walk_override", lib().qd_set_walk_override(rows_per_group))
 
 
 def set_launch_override(p_in: int = 0, p_out: int = 0, nr: int = 0):

@@ -53,10 +53,11 @@ bool overlap(const void *p, size_t n, const void *q, size_t m) {
 }
 
 // ------------------------------------------------------- launch shapes ---
-std::atomic<int> g_over_pin{0}, g_over_pout{0}, g_over_nr{0};
+std::atomic<int> g_over_pin{0}, g_over_pout{0}, g_over_nr{0}, g_over_rpg{0};
 std::atomic<int> g_ffn_pin_a{0}, g_ffn_pin_b{0}, g_ffn_pout_b{0};
 
 constexpr int kTargetWorkgroups = 400;   // enough to keep every CU streaming
+constexpr int kWalkMinWorkgroups = 1000; // batch 1-2 row walk only with rows to spare
 constexpr int kMaxTiles = 1 << 16;       // split-K counters per workspace
 constexpr int kCtlSlots = qd::kFfnCtlWords;  // leading counters: the fused FFN's control block
 constexpr int kBarWords = 64;                  // trailing counters: the one-launch FFN's grid barrier
@@ -80,7 +81,7 @@ Plan make_plan(int fmt, int64_t N, int64_t K, int batch, bool ffn, Shape s) {
     p.s = s;
     p.nk = (nb + s.p_out - 1) / s.p_out;
     p.s.p_out = (nb + p.nk - 1) / p.nk;  // every slice non-empty
-    const int rows_wg = (qd::kGroups / s.p_in) * (ffn ? 1 : s.nr);
+    const int rows_wg = (qd::kGroups / s.p_in) * (ffn ? 1 : s.nr) * std::max(1, s.rpg);
     p.tiles = (N + rows_wg - 1) / rows_wg;
     return p;
 }
@@ -106,10 +107,34 @@ Plan choose_plan(int fmt, int64_t N, int64_t K, int batch, bool ffn) {
         if (q.s.p_out == p.s.p_out && q.s.p_in == p.s.p_in) break;
         p = q;
     }
+    // Row walk (measured on MI355X): where the matrix has rows to spare, lane
+    // groups walk several row slots, so a workgroup stages its activation
+    // slice once for more rows and its load ring runs on across rows.
+    //  * batch 3..8: one lane group per row (p_in 1), two row slots each
+    //    (Gemma-4-31B FFN at batch 8: gate/up 194-282 -> 114-137 us, down
+    //    113 -> 85 us);
+    //  * batch 1..2 plain GEMV over many rows: two rows per lane group, two
+    //    row slots (four for Q8_0's longer rows) (lm_head 262144 x 2560:
+    //    Q4_K 82 -> 71-75 us, Q8_0 155 -> 144 us).
+    if (batch >= 3) {
+        Shape t = p.s;
+        t.p_in = 1;
+        t.rpg = 2;
+        Plan q = make_plan(fmt, N, K, batch, ffn, t);
+        if (q.tiles * q.s.p_out >= kTargetWorkgroups) p = q;
+    } else if (!ffn && p.s.p_in == 2) {
+        Shape t = p.s;
+        t.nr = 2;
+        t.rpg = fmt == qd::kQ80 ? 4 : 2;
+        Plan q = make_plan(fmt, N, K, batch, ffn, t);
+        if (q.tiles * q.s.p_out >= kWalkMinWorkgroups) p = q;
+    }
     // explicit overrides (tuning sweeps)
     const int op = g_over_pin.load(), oq = g_over_pout.load(), onr = g_over_nr.load();
     if (op || oq || onr) {
         Shape t = p.s;
+        t.nr = 1;   // a forced shape walks one row slot of one row unless asked
+        t.rpg = 1;
         if (op) t.p_in = op;
         if (oq) t.p_out = std::max(oq, p_lds);
         if (onr && !ffn) t.nr = onr;
@@ -118,6 +143,12 @@ Plan choose_plan(int fmt, int64_t N, int64_t K, int batch, bool ffn) {
     if (p.s.p_out > 1 && p.tiles > kMaxTiles) {  // fall back: no split across workgroups
         Shape t = p.s;
         t.p_out = p_lds;
+        p = make_plan(fmt, N, K, batch, ffn, t);
+    }
+    // row slots per lane group (explicit override, tuning sweeps)
+    if (const int orpg = g_over_rpg.load()) {
+        Shape t = p.s;
+        t.rpg = orpg;
         p = make_plan(fmt, N, K, batch, ffn, t);
     }
     return p;
@@ -787,6 +818,12 @@ qd_status qd_set_stream_override(int wg_per_cu, int depth, int consumers, int pr
     g_stream_depth.store(depth);
     g_stream_consumers.store(consumers);
     g_stream_producers.store(producers);
+    return QD_OK;
+}
+
+qd_status qd_set_walk_override(int rows_per_group) {
+    if (rows_per_group < 0 || rows_per_group > 64) return QD_EINVAL;
+    g_over_rpg.store(rows_per_group);
     return QD_OK;
 }
 

@@ -277,17 +277,18 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
     const int sstride = a.nk * 8;
     float *red = xsum + (FMT == kQ4K ? B * sstride : 0);  // [4 waves][B], then [B]
 
-    // ---- rows of this lane group
-    const int64_t slot = (int64_t)bx * RS + rs;
-    int64_t row[NR];
-    bool rvalid[NR];
-    const uint8_t *rowp[NR];
+    // ---- rows of this lane group: row slots bx * RS * rpg + r * RS + rs for
+    // r < rpg (a row slot is one row of each matrix for the fused FFN, NR
+    // consecutive rows otherwise); the group walks them one after another
+    const int rpg = a.rpg > 1 ? a.rpg : 1;
+    const int64_t slot0 = (int64_t)bx * RS * rpg + rs;
+    const int64_t rstep = (int64_t)RS * (FFN ? 1 : NR);  // rows between a group's row slots
+    int64_t row0[NR];
+    const uint8_t *mat[NR];
 #pragma unroll
     for (int i = 0; i < NR; i++) {
-        row[i] = FFN ? slot : slot * NR + i;
-        rvalid[i] = row[i] < a.N;
-        int64_t rr = rvalid[i] ? row[i] : a.N - 1;
-        rowp[i] = ((FFN && i == 1) ? a.W1 : a.W0) + rr * a.row_bytes;
+        row0[i] = FFN ? slot0 : slot0 * NR + i;
+        mat[i] = (FFN && i == 1) ? a.W1 : a.W0;
     }
 
     const int64_t K = a.K;
@@ -316,18 +317,30 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
         }
     }
 
-    // ---- the first D superunits' loads
+    // ---- the first D superunits' loads.  The group's work is Q = rpg * nsu
+    // units: unit q is superunit t0 + (q % nsu) * p_in of its row slot q / nsu.
+    // Units past the end of the K-slice or of the matrix read a small zero
+    // block (which stays in cache) and add nothing.
     using Raw = typename RawOf<FMT>::T;
     constexpr int D = lookahead<FMT, B, NR>();
     Raw buf[D + 1][NR];
     const int t0 = t_beg + pi;
+    const int nsu = (a.nk + p_in - 1) / p_in;
+    const int Q = rpg * nsu;
+    auto load_at = [&](Raw (&dst)[NR], int r, int u, bool inq) {
+        const int t = t0 + u * p_in;
+#pragma unroll
+        for (int i = 0; i < NR; i++) {
+            const int64_t rw = row0[i] + r * rstep;
+            const bool live = inq && t < t_end && rw < a.N;
+            load_unit<FMT>(dst[i], live ? mat[i] + rw * a.row_bytes : g_zero_block, live ? t : 0, c, a.nblk);
+        }
+    };
+    int rl = 0, ul = 0;  // row slot and unit of the next unit to load
 #pragma unroll
     for (int d = 0; d < D; d++) {
-        const int td = t0 + d * p_in;
-        const bool live = td < t_end;
-#pragma unroll
-        for (int i = 0; i < NR; i++)
-            load_unit<FMT>(buf[d][i], live ? rowp[i] : g_zero_block, live ? td : 0, c, a.nblk);
+        load_at(buf[d], rl, ul, d < Q);
+        if (++ul == nsu) { ul = 0; rl++; }
     }
 
     if (ws.ready != nullptr) {
@@ -468,7 +481,7 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
     }
     __syncthreads();
 
-    // ---- main loop over this group's superunits
+    // ---- main loop over this group's units
     float acc[NR][B], acc2[NR][B];
 #pragma unroll
     for (int i = 0; i < NR; i++)
@@ -477,26 +490,80 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
 
     Q4Lane L4;
     if constexpr (FMT == kQ4K) L4 = q4k_lane(c);
+    const bool leader = (pi == 0) && (c == 0);
+    const int64_t N = a.N;
+    constexpr int NP = FFN ? 2 : 1;  // split-K partial planes per batch row
 
-    // Ring of D + 1 load buffers: while superunit t is being multiplied, the
-    // loads of t + p_in .. t + D*p_in are in flight.  The inner loop is fully
-    // unrolled so every buffer index is a compile-time constant (no register
-    // copies, no wait for loads issued in the same iteration).
-    for (int t = t0; t < t_end; t += (D + 1) * p_in) {
+    // A row slot is complete: combine per lane, reduce over the 4 * p_in
+    // lanes of the row, and store the result (or this K-slice's partial).
+    auto finish_row = [&](int r) {
+        float v[NR][B];
 #pragma unroll
-        for (int s = 0; s <= D; s++) {
-            const int ts = t + s * p_in;
-            if (ts >= t_end) break;
-            // issued on every path so the wait counts are the same on every
-            // path; past the end of the slice it reads a small zero block that
-            // stays in cache instead of weight bytes
-            const int tl = ts + D * p_in;
-            const bool live = tl < t_end;
+        for (int i = 0; i < NR; i++)
+#pragma unroll
+            for (int b = 0; b < B; b++) {
+                if constexpr (FMT == kQ4K) v[i][b] = fmaf(acc[i][b], 1.0f / fp8_unit(), -acc2[i][b]);
+                else v[i][b] = acc[i][b];
+                acc[i][b] = 0.f;
+                acc2[i][b] = 0.f;
+            }
+        for (int off = 1; off < 4 * p_in; off <<= 1) {
 #pragma unroll
             for (int i = 0; i < NR; i++)
-                load_unit<FMT>(buf[(s + D) % (D + 1)][i], live ? rowp[i] : g_zero_block,
-                               live ? tl : 0, c, a.nblk);
-            const int tlo = ts - t_beg;
+#pragma unroll
+                for (int b = 0; b < B; b++) v[i][b] += __shfl_xor(v[i][b], off);
+        }
+        if (!leader) return;
+        int64_t row[NR];
+#pragma unroll
+        for (int i = 0; i < NR; i++) row[i] = row0[i] + r * rstep;
+        if (p_out == 1) {
+            if constexpr (FFN) {
+                if (row[0] < N) {
+#pragma unroll
+                    for (int b = 0; b < B; b++) {
+                        const float gv = v[0][b], uv = v[1][b];
+                        store_out<YM>(a.y + (int64_t)b * N + row[0], act_apply(a.act, gv) * uv);
+                        if (a.g_out) a.g_out[(int64_t)b * N + row[0]] = gv;
+                        if (a.u_out) a.u_out[(int64_t)b * N + row[0]] = uv;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < NR; i++)
+                    if (row[i] < N)
+#pragma unroll
+                        for (int b = 0; b < B; b++) store_out<YM>(a.y + (int64_t)b * N + row[i], v[i][b]);
+            }
+        } else {
+            // partials are written with device-scope stores (write-through,
+            // no cache-wide writeback needed before the counter below)
+#pragma unroll
+            for (int i = 0; i < NR; i++)
+                if (row[i] < N)
+#pragma unroll
+                    for (int b = 0; b < B; b++)
+                        __hip_atomic_store(
+                            a.partials + (((int64_t)ks * B + b) * NP + (FFN ? i : 0)) * N + row[i],
+                            v[i][b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    };
+
+    // Ring of D + 1 load buffers: while unit q is being multiplied, the loads
+    // of units q + 1 .. q + D are in flight, across row-slot boundaries.  The
+    // inner loop is fully unrolled so every buffer index is a compile-time
+    // constant (no register copies, no wait for loads issued in the same
+    // iteration).
+    int rc = 0, uc = 0;  // row slot and unit being multiplied
+    for (int q0 = 0; q0 < Q; q0 += D + 1) {
+#pragma unroll
+        for (int s = 0; s <= D; s++) {
+            const int q = q0 + s;
+            if (q >= Q) break;
+            // issued on every path so the wait counts are the same on every path
+            load_at(buf[(s + D) % (D + 1)], rl, ul, q + D < Q);
+            if (++ul == nsu) { ul = 0; rl++; }
+            const int tlo = min(t0 + uc * p_in, t_end - 1) - t_beg;  // dead units: zero weights
             if constexpr (FMT == kQ4K) {
                 const float *xp = xl + xphys(kSuper * tlo + 64 * c);
                 const float *sp = xsum + 8 * tlo + 2 * c;
@@ -509,72 +576,19 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
             } else {
                 q80_step<NR, B>(buf[s], xl + xphys(kSuper * tlo + 64 * c), xstride, acc);
             }
-        }
-    }
-
-    // ---- combine per lane, then reduce over the 4 * p_in lanes of a row
-    float v[NR][B];
-    if constexpr (FMT == kQ4K) {
-        const float inv_unit = 1.0f / fp8_unit();  // exact power of two
-#pragma unroll
-        for (int i = 0; i < NR; i++)
-#pragma unroll
-            for (int b = 0; b < B; b++) v[i][b] = fmaf(acc[i][b], inv_unit, -acc2[i][b]);
-    } else {
-#pragma unroll
-        for (int i = 0; i < NR; i++)
-#pragma unroll
-            for (int b = 0; b < B; b++) v[i][b] = acc[i][b];
-    }
-    for (int off = 1; off < 4 * p_in; off <<= 1) {
-#pragma unroll
-        for (int i = 0; i < NR; i++)
-#pragma unroll
-            for (int b = 0; b < B; b++) v[i][b] += __shfl_xor(v[i][b], off);
-    }
-    const bool leader = (pi == 0) && (c == 0);
-    const int64_t N = a.N;
-
-    if (p_out == 1) {
-        if (leader) {
-            if constexpr (FFN) {
-                if (rvalid[0]) {
-#pragma unroll
-                    for (int b = 0; b < B; b++) {
-                        float gv = v[0][b], uv = v[1][b];
-                        store_out<YM>(a.y + (int64_t)b * N + row[0], act_apply(a.act, gv) * uv);
-                        if (a.g_out) a.g_out[(int64_t)b * N + row[0]] = gv;
-                        if (a.u_out) a.u_out[(int64_t)b * N + row[0]] = uv;
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < NR; i++)
-                    if (rvalid[i])
-#pragma unroll
-                        for (int b = 0; b < B; b++) store_out<YM>(a.y + (int64_t)b * N + row[i], v[i][b]);
+            if (++uc == nsu) {
+                finish_row(rc);
+                uc = 0;
+                rc++;
             }
         }
-        return;
     }
+    if (p_out == 1) return;
 
-    // ---- split-K: publish partials; the last workgroup of this row tile sums
-    // them in slice order.  Partials are written and read with device-scope
-    // atomic stores and loads (write-through / L2-bypassing accesses), so no
-    // cache-wide writeback is needed: each wave waits until its stores have
-    // completed, the workgroup synchronises, and only then bumps the tile's
-    // counter with a device-scope atomic.
-    constexpr int NP = FFN ? 2 : 1;  // partial planes per batch row
-    if (leader) {
-#pragma unroll
-        for (int i = 0; i < NR; i++)
-            if (rvalid[i])
-#pragma unroll
-                for (int b = 0; b < B; b++)
-                    __hip_atomic_store(
-                        a.partials + (((int64_t)ks * B + b) * NP + (FFN ? i : 0)) * N + row[i],
-                        v[i][b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    // ---- split-K: the last workgroup of this row tile sums the partials in
+    // slice order.  Each wave waits until its partial stores have completed,
+    // the workgroup synchronises, and only then bumps the tile's counter with
+    // a device-scope atomic.
     __atomic_signal_fence(__ATOMIC_SEQ_CST);  // keep the stores above the wait
     __builtin_amdgcn_s_waitcnt(0);            // this wave's stores are complete
     __syncthreads();
@@ -586,11 +600,11 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
     }
     __syncthreads();
     if (!s_last) return;
-    const int rows_here = FFN ? RS : RS * NR;
-    const int64_t row0 = (int64_t)bx * rows_here;
+    const int rows_here = (FFN ? RS : RS * NR) * rpg;
+    const int64_t tile0 = (int64_t)bx * rows_here;
     for (int e = tid; e < rows_here * B; e += kThreads) {
         const int b = e / rows_here;
-        const int64_t r = row0 + (e - b * rows_here);
+        const int64_t r = tile0 + (e - b * rows_here);
         if (r >= N) continue;
         float s0 = 0.f, s1 = 0.f;
         for (int k = 0; k < p_out; k++) {
@@ -729,8 +743,9 @@ hipError_t launch_ffn(int fmt_a, int fmt_b, int batch, FfnArgs f, hipStream_t st
 hipError_t launch_gemv(int fmt, int batch, bool ffn, MvArgs a, Shape s, hipStream_t st) {
     a.p_in = s.p_in;
     a.p_out = s.p_out;
+    a.rpg = s.rpg;
     const int nr = ffn ? 2 : s.nr;
-    const int rows_per_wg = (kGroups / s.p_in) * (ffn ? 1 : nr);
+    const int rows_per_wg = (kGroups / s.p_in) * (ffn ? 1 : nr) * std::max(1, s.rpg);
     const int64_t tiles = (a.N + rows_per_wg - 1) / rows_per_wg;
     dim3 grid((unsigned)tiles, (unsigned)s.p_out);
     switch (fmt) {

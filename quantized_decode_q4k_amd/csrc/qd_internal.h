@@ -35,6 +35,7 @@ struct MvArgs {
     int nk;                 // superunits per K-slice (split across workgroups)
     int p_in;               // K-interleave inside a workgroup
     int p_out;              // K-slices across workgroups (gridDim.y)
+    int rpg;                // row slots each lane group walks (0 or 1: one)
     int act;                // qd_act
     float eps;
 };
@@ -43,6 +44,7 @@ struct Shape {
     int p_in;
     int p_out;
     int nr;   // row streams per lane group: 2 for FFN (gate, up); 1 or 2 for GEMV
+    int rpg = 1;  // row slots walked by each lane group
 };
 
 // Launchers (qd_gemv.hip).

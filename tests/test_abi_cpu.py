@@ -183,6 +183,14 @@ def test_launch_override_validation():
     assert L.qd_set_launch_override(0, 0, 0) == 0
 
 
+def test_walk_override_validation():
+    _, L = _lib()
+    assert L.qd_set_walk_override(-1) == 1
+    assert L.qd_set_walk_override(65) == 1
+    assert L.qd_set_walk_override(8) == 0
+    assert L.qd_set_walk_override(0) == 0
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     qd, _ = _lib()

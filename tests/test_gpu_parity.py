@@ -32,6 +32,7 @@ def qd(gpu):
     qd.lib()
     yield qd
     qd.set_launch_override(0, 0, 0)
+    qd.set_walk_override(0)
 
 
 from helpers import GELU_LIP, SILU_LIP, assert_bound, dev, h_tolerance, say  # noqa: E402
@@ -133,6 +134,70 @@ def test_gemv_forced_launch_shapes(qd, fmt):
                 assert_bound(f"{fmt} {p_in}/{p_out}/{nr} rep{rep}", y, y64, S)
     finally:
         qd.set_launch_override(0, 0, 0)
+
+
+# (p_in, p_out, nr, rows per lane group): groups walking several row slots,
+# with K = 2560 (10 superunits) leaving dead units when p_in does not divide
+# a slice, split-K across workgroups, and row counts that end mid-walk
+WALKS = [(2, 1, 1, 2), (2, 1, 1, 8), (1, 1, 2, 3), (4, 1, 1, 5), (2, 3, 1, 4), (1, 4, 2, 2),
+         (8, 2, 1, 3), (16, 1, 1, 2)]
+
+
+@pytest.mark.parametrize("fmt", ["q4_k", "q6_k", "q8_0"])
+@pytest.mark.parametrize("N,batch", [(300, 1), (1, 2), (1000, 8), (37, 1)])
+def test_gemv_row_walk(qd, fmt, N, batch):
+    """Lane groups that walk several rows (the register-streaming kernel's
+    row walk) stay within the bound for every launch shape; a call repeated
+    with the same shape is bitwise identical (split-K counters reset)."""
+    K = 2560
+    W = synth.quant_weights(fmt, N, K, SEED, tensor_id=57)
+    x = synth.normal((batch, K), SEED, tensor_id=58)
+    y64, S = oracle.gemv(fmt, W, x, N, K)
+    Wd, xd = dev(W), dev(x)
+    try:
+        for p_in, p_out, nr, rpg in WALKS:
+            say(f"gemv walk {fmt} N={N} batch={batch} p_in={p_in} p_out={p_out} nr={nr} rpg={rpg}")
+            qd.set_launch_override(p_in, p_out, nr)
+            qd.set_walk_override(rpg)
+            y = qd.qgemv(fmt, Wd, xd).cpu().numpy()
+            assert_bound(f"{fmt} walk {p_in}/{p_out}/{nr}/{rpg}", y, y64, S)
+            again = qd.qgemv(fmt, Wd, xd).cpu().numpy()
+            assert np.array_equal(y.view(np.uint32), again.view(np.uint32))
+    finally:
+        qd.set_launch_override(0, 0, 0)
+        qd.set_walk_override(0)
+
+
+@pytest.mark.parametrize("fmt,N,K", [("q4_k", 300, 2560), ("q8_0", 77, 1024), ("q6_k", 130, 2048)])
+@pytest.mark.parametrize("batch", [1, 8])
+def test_gate_up_row_walk(qd, fmt, N, K, batch):
+    """The fused gate/up on the register-streaming kernel with walking lane
+    groups: g, u each within the bound, h within the propagated bound."""
+    Wg = synth.quant_weights(fmt, N, K, SEED, tensor_id=59)
+    Wu = synth.quant_weights(fmt, N, K, SEED, tensor_id=60)
+    x = synth.normal((batch, K), SEED, tensor_id=61)
+    nw = synth.normal((K,), SEED, tensor_id=62, mean=1.0, std=0.1)
+    xn = oracle.rmsnorm(x, nw, 1e-6).astype(np.float32)
+    g64, Sg = oracle.gemv(fmt, Wg, xn, N, K)
+    u64, Su = oracle.gemv(fmt, Wu, xn, N, K)
+    href = oracle.act_vec(oracle.ACT_GELU_TANH, g64) * u64
+    tol = h_tolerance(g64, u64, Sg, Su, oracle.ACT_GELU_TANH)
+    try:
+        for p_in, p_out, rpg in ((2, 1, 4), (1, 2, 3), (4, 1, 7)):
+            say(f"gate/up walk {fmt} N={N} K={K} batch={batch} p_in={p_in} p_out={p_out} rpg={rpg}")
+            qd.set_launch_override(p_in, p_out, 0)
+            qd.set_walk_override(rpg)
+            g = torch.empty((batch, N), device="cuda")
+            u = torch.empty((batch, N), device="cuda")
+            h = qd.qffn_gate_up_act(fmt, dev(Wg), dev(Wu), dev(x), dev(nw), 1e-6, "gelu_tanh",
+                                    g_out=g, u_out=u).cpu().numpy()
+            assert_bound("gate", g.cpu().numpy(), g64, Sg)
+            assert_bound("up", u.cpu().numpy(), u64, Su)
+            err = np.abs(h - href)
+            assert (err <= tol).all(), f"h: worst {np.max(err / tol):.3f} of tolerance"
+    finally:
+        qd.set_launch_override(0, 0, 0)
+        qd.set_walk_override(0)
 
 
 @pytest.mark.parametrize("fmt,K", [("q4_k", 2560), ("q6_k", 2560), ("q8_0", 2560)])
