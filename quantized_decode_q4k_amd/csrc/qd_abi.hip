@@ -300,16 +300,20 @@ bool stream_plan_pc(int fmt, bool ffn, int64_t N, int64_t K, int batch, const fl
 // superunits, a matrix whose size is not a multiple of 16 bytes, an LDS
 // layout that does not fit, and (unless overridden) plain GEMVs with K <
 // 8192.  The fused gate/up and the long-row GEMVs take the producer /
-// consumer kernel with two copying waves and 3 steps in flight each: one
-// workgroup per CU with 8 decoding waves when a workgroup's whole row range
-// fits in its ring, else two per CU with 4.  Measured on MI355X (graph
-// replay, 1 GiB of rotating weights), against the register kernel:
-//   Gemma-3 gate/up 10240 x 2560:   10.9 us (13.3)
-//   Gemma-3 down Q6_K 2560 x 10240:  9.8 us (11.8)
-//   Gemma-4 gate/up 21504 x 5376:   32.1 us (33.4)
-//   Gemma-4 down Q6_K 5376 x 21504: 29.8 us (30.0)
+// consumer kernel.  At batch 1: one workgroup per CU with 8 decoding waves,
+// 5 steps in flight per copying wave (fewer where the ring's slot-reuse
+// bound asks), and 4 copying waves when a workgroup's rows hold 256 KB or
+// more (2 below).  At batch 2 (8 decoding waves spill registers): 4
+// decoding waves, 2 copying waves, 3 steps in flight, one workgroup per CU
+// when its whole row range fits in the ring, else two.  Measured on MI355X
+// (graph replay, 1 GiB of rotating weights; two runs each), against the
+// register kernel:
+//   Gemma-3 gate/up 10240 x 2560:   10.9-11.1 us (13.4)
+//   Gemma-3 down Q6_K 2560 x 10240: 10.0 us (12.2)
+//   Gemma-4 gate/up 21504 x 5376:   29.8-30.5 us (33.9; 33.3 with 2 copying waves)
+//   Gemma-4 down Q6_K 5376 x 21504: 27.6-28.4 us (30.4; 29.5 with 2 copying waves)
 // K = 2560 plain GEMVs stay on the register kernel (lm_head 262144 rows:
-// 76-79 us against 87 or more on either streaming kernel).
+// 72-79 us against 87 or more on either streaming kernel).
 bool stream_plan(int fmt, bool ffn, int64_t N, int64_t K, int batch, const float *norm_w,
                  qd::StreamArgs *a, unsigned *grid, size_t *lds) {
     if (batch > 2) return false;
@@ -326,8 +330,14 @@ bool stream_plan(int fmt, bool ffn, int64_t N, int64_t K, int batch, const float
         return stream_plan_wpc(fmt, ffn, N, K, batch, norm_w, wpc, a, grid, lds);
     }
     if (!ffn && K < kStreamMinK) return false;
+    if (batch == 1) {
+        constexpr int kPcLag1 = 5;
+        const int64_t wg_bytes = (N + kCUs - 1) / kCUs * row_bytes(fmt, K) * (ffn ? 2 : 1);
+        const int prod = wg_bytes >= (int64_t(256) << 10) ? 4 : 2;
+        return stream_plan_pc(fmt, ffn, N, K, batch, norm_w, 1, 8, prod, kPcLag1, a, grid, lds);
+    }
     // 8 decoding waves spill registers at batch 2
-    if (stream_plan_pc(fmt, ffn, N, K, batch, norm_w, 1, batch == 1 ? 8 : 4, 2, kPcLag, a, grid, lds) &&
+    if (stream_plan_pc(fmt, ffn, N, K, batch, norm_w, 1, 4, 2, kPcLag, a, grid, lds) &&
         a->slots * 16 >= a->units_max)
         return true;
     return stream_plan_pc(fmt, ffn, N, K, batch, norm_w, 2, 4, 2, kPcLag, a, grid, lds);

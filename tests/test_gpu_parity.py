@@ -458,11 +458,14 @@ def test_ffn_decode_gemma3(qd, mode):
     check_ffn_decode(qd, "q4_k", "q6_k", 2560, 10240, 1, "gelu_tanh", "gemma3-4b", reps=4, mode=mode)
 
 
-def test_ffn_decode_gemma4_31b_batch1(qd):
-    """Gemma-4-31B FFN at batch 1 in the grid-barrier launch: both rings are reused."""
+@pytest.mark.parametrize("mode", ["auto", "grid"])
+def test_ffn_decode_gemma4_31b_batch1(qd, mode):
+    """Gemma-4-31B FFN at batch 1, in the automatic two launches (one
+    workgroup per CU, four copying waves, ring slots reused) and in the
+    grid-barrier launch (both rings reused)."""
     rows = np.unique(np.concatenate([np.arange(0, 256), np.arange(5376 - 256, 5376), np.arange(0, 5376, 7)]))
     check_ffn_decode(qd, "q4_k", "q6_k", 5376, 21504, 1, "gelu_tanh", "gemma4-31b b1", reps=2, rows=rows,
-                     mode="grid")
+                     mode=mode)
 
 
 def test_ffn_decode_gemma4_31b_batch8_falls_back(qd):
