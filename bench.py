@@ -46,7 +46,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="gemma3_ffn",
                    choices=["gemma3_ffn", "gemma3_ffn_2k", "gemma4_ffn", "gemma4_ffn_2k",
-                            "gemma4_ffn_b8", "gemma4_prefill", "lm_head_q4k",
+                            "gemma4_ffn_b8", "gemma4_prefill", "gemma3_qkv", "gemma3_qkv_q8_0",
+                            "lm_head_q4k",
                             "lm_head_q8_0", "down_q6k", "gate_up_q4k", "copy"])
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="approximate CPU time budget of the oracle baseline (0 = skip)")
@@ -128,6 +129,17 @@ class Workload:
             self.flops_gate_up = 2 * 2 * M * ff * hidden
             self.flops = self.flops_gate_up + 2 * M * hidden * ff
             base = {k: t(v) for k, v in mats.items()}
+        elif name in ("gemma3_qkv", "gemma3_qkv_q8_0"):
+            self.qkv_fmts = ("q4_k", "q4_k", "q6_k") if name == "gemma3_qkv" else ("q8_0",) * 3
+            hidden = 2560
+            mats = {"q": synth.quant_weights(self.qkv_fmts[0], 2048, hidden, seed, tensor_id=61),
+                    "k": synth.quant_weights(self.qkv_fmts[1], 1024, hidden, seed, tensor_id=62),
+                    "v": synth.quant_weights(self.qkv_fmts[2], 1024, hidden, seed, tensor_id=63)}
+            self.weight_bytes = sum(m.size for m in mats.values())
+            self.x = t(synth.normal((1, hidden), seed, tensor_id=64))
+            self.nw = t(synth.normal((hidden,), seed, tensor_id=65, mean=1.0, std=0.1))
+            self.qkv_out = [torch.empty((1, n), device=dev) for n in (2048, 1024, 1024)]
+            base = {k: t(v) for k, v in mats.items()}
         elif name in ("lm_head_q4k", "lm_head_q8_0"):
             fmt = "q4_k" if name == "lm_head_q4k" else "q8_0"
             self.fmt = fmt
@@ -156,6 +168,8 @@ class Workload:
             return "qffn_gate_up_act", w + 4 * (b * self.hidden + self.hidden + b * self.ff)
         if n == "down_q6k":
             return "qgemv_q6k", self.hidden * (self.ff // 256) * 210 + 4 * b * (self.ff + self.hidden)
+        if n.startswith("gemma3_qkv"):
+            return "qqkv_proj", self.weight_bytes + 4 * (2 * 2560 + 4096)
         if n.startswith("lm_head"):
             return "qgemv", self.weight_bytes + 4 * (2560 + 262144)
         return "copy", 2 * self.weight_bytes
@@ -179,8 +193,15 @@ class Workload:
             qd.qgemv_q6k(c["down"], self.hin, self.y)
         elif n.startswith("lm_head"):
             qd.qgemv(self.fmt, c["W"], self.x, self.y)
+        elif n.startswith("gemma3_qkv"):
+            self.qkv(c)
         else:
             self.dst.copy_(c["src"])
+
+    def qkv(self, c):
+        o = self.qkv_out
+        self.qd.qqkv_proj(self.qkv_fmts, c["q"], c["k"], c["v"], self.x, self.nw, 1e-6,
+                          q=o[0], k=o[1], v=o[2])
 
 
 def _dominant(self):
@@ -197,6 +218,8 @@ def _dominant(self):
         qd.qgemv_q6k(c["down"], self.hin, self.y)
     elif n.startswith("lm_head"):
         qd.qgemv(self.fmt, c["W"], self.x, self.y)
+    elif n.startswith("gemma3_qkv"):
+        self.qkv(c)
     else:
         self.dst.copy_(c["src"])
 
@@ -321,6 +344,10 @@ def main():
     workloads = {
         "gemma3_ffn": "Gemma-3-4B FFN decode step, batch 1: RMS-norm + gate/up Q4_K 10240x2560 + "
                       "GELU-tanh + down Q6_K 2560x10240 (one qffn_decode call)",
+        "gemma3_qkv": "Gemma-3-4B attention input projections, batch 1: RMS-norm + Q Q4_K 2048x2560, "
+                      "K Q4_K 1024x2560, V Q6_K 1024x2560 (one qqkv_proj call)",
+        "gemma3_qkv_q8_0": "Gemma-3-4B attention input projections in Q8_0, batch 1: RMS-norm + Q "
+                           "2048x2560, K 1024x2560, V 1024x2560 (one qqkv_proj call)",
         "gemma4_prefill": "Gemma-4-31B FFN prefill, 512 tokens: gate/up Q4_K 21504x5376 + "
                           "GELU-tanh -> bf16 h, down Q6_K 5376x21504 (bf16 MFMA, fp32 accumulate)",
     }

@@ -125,6 +125,34 @@ qd_status qgemv(qd_format fmt, const void *W, const float *x, float *y,
                 int64_t N, int64_t K, int batch, void *stream);
 
 /*
+ * q = Wq xn,  k = Wk xn,  v = Wv xn,  xn = RMSNorm(x) if norm_w != NULL else x
+ *
+ * The attention input projections of one decoder layer in one launch: the
+ * larql Gemma 3 table fuses the input RMS-norm with the Q, K and V
+ * projections (Q and K in Q4_K, V in Q6_K, "Q4_K_M" mix) into one dispatch;
+ * here each matrix may have its own format.
+ *
+ *   fmt_q, Wq, Nq   Q projection, Nq x K
+ *   fmt_k, Wk, Nk   K projection, Nk x K
+ *   fmt_v, Wv, Nv   V projection, Nv x K
+ *   x               fp32 [batch][K]
+ *   norm_w, eps     RMS-norm as in qffn_gate_up_act (NULL = no norm)
+ *   q, k, v         fp32 [batch][Nq], [batch][Nk], [batch][Nv]; they must not
+ *                   overlap each other or any input
+ *   K               a multiple of 256 when any matrix is Q4_K or Q6_K (of 32
+ *                   when all are Q8_0)
+ * Accuracy: each output meets the GEMV bound for xn.  One launch when every
+ * matrix's activation slice fits one workgroup's LDS (K up to 14592 at
+ * batch 1 in Q4_K) and K is a multiple of 256; otherwise the same results
+ * from three GEMV launches.  Needs no workspace.
+ * Errors: as qgemv for each matrix (QD_ESHAPE, QD_EALIGN, QD_EINVAL).
+ */
+qd_status qqkv_proj(qd_format fmt_q, const void *Wq, int64_t Nq, qd_format fmt_k,
+                    const void *Wk, int64_t Nk, qd_format fmt_v, const void *Wv, int64_t Nv,
+                    const float *x, const float *norm_w, float eps, float *q, float *k,
+                    float *v, int64_t K, int batch, void *stream);
+
+/*
  * h = act(Wg xn) * (Wu xn),  xn = RMSNorm(x) if norm_w != NULL else x
  *
  * The fused FFN gate+up of larql's q4k_ffn_gate_up_8sg with the geglu

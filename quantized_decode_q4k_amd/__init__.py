@@ -8,6 +8,7 @@ library is not built, or a tensor is not on the GPU, the call raises.
 
 Entry points (same names as the C ABI):
     qgemv_q4k, qgemv_q6k, qgemv_q8_0, qgemv        y = W x, batch 1..8
+    qqkv_proj                                      q, k, v = Wq xn, Wk xn, Wv xn (one launch)
     qffn_gate_up_act                               h = act(Wg xn) * (Wu xn)
     qffn_decode                                    y = Wd h (whole FFN, one launch)
     qgemm_prefill, qgemm_prefill_gate_up_act       bf16 MFMA prefill GEMMs
@@ -47,6 +48,8 @@ SIGNATURES = {
     "qgemv_q6k": (_I, [_P, _P, _P, _I64, _I64, _I, _P]),
     "qgemv_q8_0": (_I, [_P, _P, _P, _I64, _I64, _I, _P]),
     "qgemv": (_I, [_I, _P, _P, _P, _I64, _I64, _I, _P]),
+    "qqkv_proj": (_I, [_I, _P, _I64, _I, _P, _I64, _I, _P, _I64, _P, _P, _F, _P, _P, _P, _I64, _I,
+                       _P]),
     "qffn_gate_up_act": (_I, [_I, _P, _P, _P, _P, _F, _I, _P, _P, _P, _I64, _I64, _I, _P]),
     "qffn_decode": (_I, [_I, _P, _P, _I, _P, _P, _P, _F, _I, _P, _P, _I64, _I64, _I, _P]),
     "qgemm_prefill": (_I, [_I, _P, _P, _P, _I64, _I64, _I64, _P]),
@@ -169,6 +172,32 @@ def qgemv_q6k(W, x, y=None):
 
 def qgemv_q8_0(W, x, y=None):
     return qgemv(Q8_0, W, x, y)
+
+
+def qqkv_proj(fmts, Wq: torch.Tensor, Wk: torch.Tensor, Wv: torch.Tensor, x: torch.Tensor,
+              norm_w: torch.Tensor | None = None, eps: float = 1e-6,
+              q: torch.Tensor | None = None, k: torch.Tensor | None = None,
+              v: torch.Tensor | None = None):
+    """(q, k, v) = (Wq xn, Wk xn, Wv xn), xn = RMSNorm(x) (if norm_w) or x, in
+    one launch.  fmts: the three weight formats, e.g. ("q4_k", "q4_k", "q6_k")."""
+    f = [_fmt(t) for t in fmts]
+    if len(f) != 3:
+        raise ValueError("fmts must name three formats (q, k, v)")
+    K = x.shape[-1]
+    batch = 1 if x.dim() == 1 else x.shape[0]
+    Ns = [_rows(fi, W, K) for fi, W in zip(f, (Wq, Wk, Wv))]
+    outs = []
+    for o, n in zip((q, k, v), Ns):
+        shape = (n,) if x.dim() == 1 else (batch, n)
+        outs.append(torch.empty(shape, dtype=torch.float32, device=x.device) if o is None else o)
+    nw = _dev(norm_w, "norm_w", torch.float32) if norm_w is not None else None
+    st = lib().qqkv_proj(f[0], _dev(Wq, "Wq", torch.uint8), Ns[0], f[1], _dev(Wk, "Wk", torch.uint8),
+                         Ns[1], f[2], _dev(Wv, "Wv", torch.uint8), Ns[2], _dev(x, "x", torch.float32),
+                         nw, float(eps), _dev(outs[0], "q", torch.float32),
+                         _dev(outs[1], "k", torch.float32), _dev(outs[2], "v", torch.float32), K,
+                         batch, _stream())
+    _check("qqkv_proj", st)
+    return tuple(outs)
 
 
 def qffn_gate_up_act(fmt, Wg: torch.Tensor, Wu: torch.Tensor, x: torch.Tensor,

@@ -703,6 +703,82 @@ qd_status run_gemm(int fmt, bool ffn, const void *Wg, const void *Wu, const uint
     return e == hipSuccess ? QD_OK : QD_ELAUNCH;
 }
 
+// Q, K and V projections of one attention input in one launch (larql Gemma 3
+// table: the input norm and the QKV projection fused into one dispatch, Q/K
+// in Q4_K and V in Q6_K).  Each matrix keeps the launch shape the planner
+// gives it as a plain GEMV, without a split across workgroups; where its
+// activation slice does not fit one workgroup's LDS the three projections
+// run as three GEMV calls instead.
+qd_status run_qkv(const int fmt[3], const void *const W[3], const int64_t N[3], const float *x,
+                  const float *norm_w, float eps, float *const y[3], int64_t K, int batch,
+                  void *stream) {
+    for (int i = 0; i < 3; i++) {
+        qd_status st = check_shape(fmt[i], N[i], K, batch);
+        if (st != QD_OK) return st;
+        if (!W[i] || !y[i]) return QD_EINVAL;
+    }
+    if (!x) return QD_EINVAL;
+    if (!aligned(x, 16) || (norm_w && !aligned(norm_w, 16))) return QD_EALIGN;
+    for (int i = 0; i < 3; i++)
+        if (!aligned(W[i], 16) || !aligned(y[i], 4)) return QD_EALIGN;
+    const size_t xbytes = (size_t)batch * K * 4;
+    for (int i = 0; i < 3; i++) {
+        const size_t yb = (size_t)batch * N[i] * 4;
+        if (overlap(y[i], yb, x, xbytes) || (norm_w && overlap(y[i], yb, norm_w, (size_t)K * 4)))
+            return QD_EINVAL;
+        for (int j = 0; j < 3; j++) {
+            if (overlap(y[i], yb, W[j], (size_t)N[j] * row_bytes(fmt[j], K))) return QD_EINVAL;
+            if (j != i && overlap(y[i], yb, y[j], (size_t)batch * N[j] * 4)) return QD_EINVAL;
+        }
+    }
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    const int nb = (int)(K / qd::kSuper);
+    bool fused = K % qd::kSuper == 0;
+    for (int i = 0; i < 3 && fused; i++) fused = nb <= lds_units_max(fmt[i], batch);
+    if (!fused) {
+        for (int i = 0; i < 3; i++) {
+            qd_status st = run_mv(fmt[i], false, W[i], nullptr, x, norm_w, eps, 0, y[i], nullptr,
+                                  nullptr, N[i], K, batch, stream);
+            if (st != QD_OK) return st;
+        }
+        return QD_OK;
+    }
+    // Lane groups per row: the fewest (from 2) that give the launch a
+    // workgroup per CU.  Measured on MI355X, Gemma-3-4B Q/K/V (4096 rows over
+    // K = 2560, graph replay, rotating weights): 4 per row (256 workgroups)
+    // 7.4 us, 8 per row 7.4 us, 16 per row (1024 workgroups, each staging x)
+    // 10.1-10.3 us; three separate GEMV launches 18.3 us.
+    int p_in = 2;
+    const int64_t rows = N[0] + N[1] + N[2];
+    while (p_in < 16 && rows * p_in / qd::kGroups < kCUs) p_in *= 2;
+    if (const int op = g_over_pin.load()) p_in = op;
+    qd::QkvArgs q{};
+    size_t lds = 0;
+    for (int i = 0; i < 3; i++) {
+        const Plan p = make_plan(fmt[i], N[i], K, batch, false, Shape{p_in, 1, 1, 1});
+        qd::MvArgs &a = q.a[i];
+        a.W0 = static_cast<const uint8_t *>(W[i]);
+        a.x = x;
+        a.norm_w = norm_w;
+        a.y = y[i];
+        a.N = N[i];
+        a.K = K;
+        a.row_bytes = row_bytes(fmt[i], K);
+        a.nb = nb;
+        a.nblk = (int)(K / block_elems(fmt[i]));
+        a.nk = p.nk;
+        a.p_in = p.s.p_in;
+        a.p_out = 1;
+        a.rpg = 1;
+        a.eps = eps;
+        q.fmt[i] = fmt[i];
+        q.tiles[i] = (int)p.tiles;
+        lds = std::max(lds, qd::mv_lds_bytes(fmt[i], batch, p.nk));
+    }
+    hipError_t e = qd::launch_qkv(q, batch, lds, hs);
+    return e == hipSuccess ? QD_OK : QD_ELAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -744,6 +820,17 @@ qd_status qgemv_q6k(const void *W, const float *x, float *y, int64_t N, int64_t 
 qd_status qgemv_q8_0(const void *W, const float *x, float *y, int64_t N, int64_t K, int batch,
                      void *stream) {
     return qgemv(QD_Q8_0, W, x, y, N, K, batch, stream);
+}
+
+qd_status qqkv_proj(qd_format fmt_q, const void *Wq, int64_t Nq, qd_format fmt_k, const void *Wk,
+                    int64_t Nk, qd_format fmt_v, const void *Wv, int64_t Nv, const float *x,
+                    const float *norm_w, float eps, float *q, float *k, float *v, int64_t K, int batch,
+                    void *stream) {
+    const int fmt[3] = {fmt_q, fmt_k, fmt_v};
+    const void *const W[3] = {Wq, Wk, Wv};
+    const int64_t N[3] = {Nq, Nk, Nv};
+    float *const y[3] = {q, k, v};
+    return run_qkv(fmt, W, N, x, norm_w, eps, y, K, batch, stream);
 }
 
 qd_status qffn_gate_up_act(qd_format fmt, const void *Wg, const void *Wu, const float *x,

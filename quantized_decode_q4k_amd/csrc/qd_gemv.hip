@@ -673,6 +673,49 @@ __global__ __launch_bounds__(kThreads) void ffn_kernel(FfnArgs f) {
     }
 }
 
+// ------------------------------------------------ fused Q/K/V projection ---
+// The larql Gemma 3 table runs the input RMS-norm and the Q, K and V
+// projections of attention as one fused dispatch (Q and K in Q4_K, V in
+// Q6_K).  Here the three projections share one launch: workgroup t belongs
+// to matrix 0, 1 or 2 by its index, and runs that matrix's row tile in that
+// matrix's format.  Every tile stages (and RMS-normalises) the activation
+// rows itself, so the tiles are independent and the launch needs no
+// workspace.
+template <int B>
+__global__ __launch_bounds__(kThreads) void qkv_kernel(QkvArgs q) {
+    extern __shared__ __attribute__((aligned(16))) float smem[];
+    int t = (int)blockIdx.x;
+    int s = 0;
+    if (t >= q.tiles[0]) {
+        t -= q.tiles[0];
+        s = 1;
+        if (t >= q.tiles[1]) {
+            t -= q.tiles[1];
+            s = 2;
+        }
+    }
+    const MvArgs &a = q.a[s];
+    switch (q.fmt[s]) {
+    case kQ4K: mv_tile<kQ4K, B, 1, false, kPlain, kPlain>(a, t, 0, 1, smem); break;
+    case kQ6K: mv_tile<kQ6K, B, 1, false, kPlain, kPlain>(a, t, 0, 1, smem); break;
+    default: mv_tile<kQ80, B, 1, false, kPlain, kPlain>(a, t, 0, 1, smem); break;
+    }
+}
+
+hipError_t launch_qkv(const QkvArgs &q, int batch, size_t lds, hipStream_t st) {
+    const unsigned grid = (unsigned)(q.tiles[0] + q.tiles[1] + q.tiles[2]);
+#define QD_QKV(Bv)                                                                       \
+    case Bv:                                                                             \
+        hipLaunchKernelGGL((qkv_kernel<Bv>), dim3(grid), dim3(kThreads), lds, st, q);    \
+        break;
+    switch (batch) {
+        QD_QKV(1) QD_QKV(2) QD_QKV(3) QD_QKV(4) QD_QKV(5) QD_QKV(6) QD_QKV(7) QD_QKV(8)
+    default: return hipErrorInvalidValue;
+    }
+#undef QD_QKV
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------ launchers ---
 size_t mv_lds_bytes(int fmt, int batch, int nk) {
     size_t floats = (size_t)batch * nk * kSuperPhys;

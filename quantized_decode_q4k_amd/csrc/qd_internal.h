@@ -52,6 +52,18 @@ struct Shape {
 size_t mv_lds_bytes(int fmt, int batch, int nk);
 hipError_t launch_gemv(int fmt, int batch, bool ffn, MvArgs a, Shape s, hipStream_t st);
 
+// Fused Q/K/V projection (qd_gemv.hip): three GEMVs over the same activation
+// rows in one launch.  Workgroups [0, tiles[0]) are row tiles of matrix 0,
+// the next tiles[1] of matrix 1, then tiles[2] of matrix 2; each runs the
+// GEMV tile of its own format with no split across workgroups (a[i].p_out
+// must be 1 and a[i].nk == a[i].nb).
+struct QkvArgs {
+    MvArgs a[3];
+    int fmt[3];
+    int tiles[3];
+};
+hipError_t launch_qkv(const QkvArgs &q, int batch, size_t lds, hipStream_t st);
+
 // Fused decode FFN (qd_gemv.hip): phase A = gate/up/act tiles writing h,
 // phase B = down-projection split-K tiles reading h.
 struct FfnArgs {

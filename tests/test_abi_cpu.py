@@ -99,6 +99,38 @@ def test_ffn_validation():
     assert f(0, A16, A16 + 0x8000, A16b, None, 1e-6, 0, A16c, A16c + 4, None, 4, 256, 1, None) == 1
 
 
+QK, QV = A16 + 0x4000, A16 + 0x8000   # three weight matrices
+YQ, YK, YV = A16c, A16c + 0x1000, A16c + 0x2000  # three outputs
+
+
+def _qkv(L, fq=0, wq=A16, nq=4, fk=0, wk=QK, nk=4, fv=1, wv=QV, nv=4, x=A16b, nw=None,
+         q=YQ, k=YK, v=YV, K=256, batch=1):
+    return L.qqkv_proj(fq, wq, nq, fk, wk, nk, fv, wv, nv, x, nw, 1e-6, q, k, v, K, batch, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(wk=0), 1),                      # null K weights
+    (dict(x=0), 1),                       # null x
+    (dict(v=0), 1),                       # null v output
+    (dict(fv=7), 1),                      # unknown format
+    (dict(nk=0), 2),                      # K projection with no rows
+    (dict(K=320), 2),                     # K not a multiple of 256 (k-quants)
+    (dict(fq=2, fk=2, fv=2, K=48), 2),    # Q8_0 K not a multiple of 32
+    (dict(batch=9), 2),                   # batch above 8
+    (dict(wv=QV + 8), 3),                 # V weights misaligned
+    (dict(x=A16b + 4), 3),                # x misaligned
+    (dict(nw=A16b + 0x1004), 3),          # norm weight misaligned
+    (dict(k=YK + 2), 3),                  # k output misaligned
+    (dict(k=YQ + 8), 1),                  # k overlaps q
+    (dict(v=A16b + 64), 1),               # v overlaps x
+    (dict(q=QK + 16), 1),                 # q overlaps the K weights
+    (dict(nw=A16b + 0x1000, v=A16b + 0x1010), 1),  # v overlaps the norm weight
+])
+def test_qkv_validation(kw, status):
+    _, L = _lib()
+    assert _qkv(L, **kw) == status
+
+
 def test_dequant_validation():
     _, L = _lib()
     assert L.qdequant(0, 0, A16b, 4, 256, None) == 1
