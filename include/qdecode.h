@@ -125,6 +125,26 @@ qd_status qgemv(qd_format fmt, const void *W, const float *x, float *y,
                 int64_t N, int64_t K, int batch, void *stream);
 
 /*
+ * y = W x + r  (GEMV with the residual add fused into its epilogue)
+ *
+ * The decoder's residual stream: larql's Gemma 3 table follows the O
+ * projection with post_attn_residual_norm_store and the down projection
+ * with post_ffn_norm_residual_add; the residual add of both is folded into
+ * the GEMV's store here (the norms, which need the whole output row, are not).
+ *
+ *   fmt, W, x, N, K, batch   as qgemv
+ *   r      fp32 [batch][N] residual, 4-byte aligned; it may be y itself
+ *          (y += W x in place) but must not otherwise overlap y
+ *   y      fp32 [batch][N]; y[b][n] = sum_k w[n][k] x[b][k] + r[b][n]
+ * Accuracy: |y - y_exact| <= 1e-4 * sum_k |w x| + 1e-6 + one fp32 rounding
+ * of the sum.
+ * Errors: as qgemv; QD_EINVAL for a NULL r or an r that overlaps y without
+ * being y.
+ */
+qd_status qgemv_residual(qd_format fmt, const void *W, const float *x, const float *r, float *y,
+                         int64_t N, int64_t K, int batch, void *stream);
+
+/*
  * q = Wq xn,  k = Wk xn,  v = Wv xn,  xn = RMSNorm(x) if norm_w != NULL else x
  *
  * The attention input projections of one decoder layer in one launch: the
@@ -210,6 +230,21 @@ qd_status qffn_gate_up_act(qd_format fmt, const void *Wg, const void *Wu,
 qd_status qffn_decode(qd_format fmt_gu, const void *Wg, const void *Wu, qd_format fmt_down,
                       const void *Wd, const float *x, const float *norm_w, float eps, qd_act act,
                       float *y, float *h_out, int64_t N_ff, int64_t K, int batch, void *stream);
+
+/*
+ * y = Wd h + r,  h = act(Wg xn) * (Wu xn)   (qffn_decode with the residual
+ * add of larql's post_ffn_norm_residual_add folded into the down store)
+ *
+ * Arguments as qffn_decode, plus r: fp32 [batch][K] residual, 4-byte
+ * aligned, which may be y itself (y += FFN(x) in place) but must not
+ * otherwise overlap y or h_out.
+ * Errors: as qffn_decode; QD_EINVAL for a NULL or overlapping r.
+ */
+qd_status qffn_decode_residual(qd_format fmt_gu, const void *Wg, const void *Wu,
+                               qd_format fmt_down, const void *Wd, const float *x,
+                               const float *norm_w, float eps, qd_act act, const float *r,
+                               float *y, float *h_out, int64_t N_ff, int64_t K, int batch,
+                               void *stream);
 
 /*
  * Y = X W^T for a multi-token prefill: the weights are dequantised to bf16

@@ -8,9 +8,11 @@ library is not built, or a tensor is not on the GPU, the call raises.
 
 Entry points (same names as the C ABI):
     qgemv_q4k, qgemv_q6k, qgemv_q8_0, qgemv        y = W x, batch 1..8
+    qgemv_residual                                 y = W x + r (r may be y)
     qqkv_proj                                      q, k, v = Wq xn, Wk xn, Wv xn (one launch)
     qffn_gate_up_act                               h = act(Wg xn) * (Wu xn)
     qffn_decode                                    y = Wd h (whole FFN, one launch)
+    qffn_decode_residual                           y = Wd h + r
     qgemm_prefill, qgemm_prefill_gate_up_act       bf16 MFMA prefill GEMMs
     qdequant, qdequant_bf16                        decoded weights (tests)
 """
@@ -48,6 +50,9 @@ SIGNATURES = {
     "qgemv_q6k": (_I, [_P, _P, _P, _I64, _I64, _I, _P]),
     "qgemv_q8_0": (_I, [_P, _P, _P, _I64, _I64, _I, _P]),
     "qgemv": (_I, [_I, _P, _P, _P, _I64, _I64, _I, _P]),
+    "qgemv_residual": (_I, [_I, _P, _P, _P, _P, _I64, _I64, _I, _P]),
+    "qffn_decode_residual": (_I, [_I, _P, _P, _I, _P, _P, _P, _F, _I, _P, _P, _P, _I64, _I64, _I,
+                                  _P]),
     "qqkv_proj": (_I, [_I, _P, _I64, _I, _P, _I64, _I, _P, _I64, _P, _P, _F, _P, _P, _P, _I64, _I,
                        _P]),
     "qffn_gate_up_act": (_I, [_I, _P, _P, _P, _P, _F, _I, _P, _P, _P, _I64, _I64, _I, _P]),
@@ -162,6 +167,24 @@ def qgemv(fmt, W: torch.Tensor, x: torch.Tensor, y: torch.Tensor | None = None) 
     return y
 
 
+def qgemv_residual(fmt, W: torch.Tensor, x: torch.Tensor, r: torch.Tensor,
+                   y: torch.Tensor | None = None) -> torch.Tensor:
+    """y = W x + r (pass y=r to add in place)."""
+    f = _fmt(fmt)
+    K = x.shape[-1]
+    batch = 1 if x.dim() == 1 else x.shape[0]
+    N = _rows(f, W, K)
+    if tuple(r.shape) != ((N,) if x.dim() == 1 else (batch, N)):
+        raise ValueError("r must have the output's shape")
+    if y is None:
+        y = torch.empty_like(r)
+    st = lib().qgemv_residual(f, _dev(W, "W", torch.uint8), _dev(x, "x", torch.float32),
+                              _dev(r, "r", torch.float32), _dev(y, "y", torch.float32), N, K, batch,
+                              _stream())
+    _check("qgemv_residual", st)
+    return y
+
+
 def qgemv_q4k(W, x, y=None):
     return qgemv(Q4_K, W, x, y)
 
@@ -243,6 +266,31 @@ def qffn_decode(fmt_gu, Wg: torch.Tensor, Wu: torch.Tensor, fmt_down, Wd: torch.
                            _dev(Wd, "Wd", torch.uint8), _dev(x, "x", torch.float32), nw, float(eps),
                            _act(act), _dev(y, "y", torch.float32), hp, N, K, batch, _stream())
     _check("qffn_decode", st)
+    return y
+
+
+def qffn_decode_residual(fmt_gu, Wg: torch.Tensor, Wu: torch.Tensor, fmt_down, Wd: torch.Tensor,
+                         x: torch.Tensor, r: torch.Tensor, norm_w: torch.Tensor | None = None,
+                         eps: float = 1e-6, act="gelu_tanh", y: torch.Tensor | None = None,
+                         h_out: torch.Tensor | None = None) -> torch.Tensor:
+    """y = Wd (act(Wg xn) * (Wu xn)) + r (pass y=r to add in place)."""
+    fg, fd = _fmt(fmt_gu), _fmt(fmt_down)
+    K = x.shape[-1]
+    batch = 1 if x.dim() == 1 else x.shape[0]
+    N = _rows(fg, Wg, K)
+    if _rows(fg, Wu, K) != N or _rows(fd, Wd, N) != K:
+        raise ValueError("gate/up must be N_ff x K and down K x N_ff")
+    if tuple(r.shape) != tuple(x.shape):
+        raise ValueError("r must have x's shape")
+    if y is None:
+        y = torch.empty_like(x)
+    nw = _dev(norm_w, "norm_w", torch.float32) if norm_w is not None else None
+    hp = _dev(h_out, "h_out", torch.float32) if h_out is not None else None
+    st = lib().qffn_decode_residual(fg, _dev(Wg, "Wg", torch.uint8), _dev(Wu, "Wu", torch.uint8), fd,
+                                    _dev(Wd, "Wd", torch.uint8), _dev(x, "x", torch.float32), nw,
+                                    float(eps), _act(act), _dev(r, "r", torch.float32),
+                                    _dev(y, "y", torch.float32), hp, N, K, batch, _stream())
+    _check("qffn_decode_residual", st)
     return y
 
 

@@ -345,7 +345,8 @@ bool stream_plan(int fmt, bool ffn, int64_t N, int64_t K, int batch, const float
 
 qd_status run_mv(int fmt, bool ffn, const void *W0, const void *W1, const float *x,
                  const float *norm_w, float eps, int act, float *y, float *g_out, float *u_out,
-                 int64_t N, int64_t K, int batch, void *stream, size_t ws_offset = 0) {
+                 int64_t N, int64_t K, int batch, void *stream, size_t ws_offset = 0,
+                 const float *res = nullptr) {
     qd_status st = check_shape(fmt, N, K, batch);
     if (st != QD_OK) return st;
     if (!W0 || !x || !y || (ffn && !W1)) return QD_EINVAL;
@@ -366,6 +367,10 @@ qd_status run_mv(int fmt, bool ffn, const void *W0, const void *W1, const float 
     if (overlap(y, ybytes, g_out, ybytes) || overlap(y, ybytes, u_out, ybytes) ||
         overlap(g_out, ybytes, u_out, ybytes))
         return QD_EINVAL;
+    // the residual is read at each output's own index just before that
+    // output is written, so it may be y itself, but no other part of it
+    if (res && (ffn || (res != y && overlap(res, ybytes, y, ybytes)))) return QD_EINVAL;
+    if (res && !aligned(res, 4)) return QD_EALIGN;
 
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     const bool forced = g_over_pin.load() || g_over_pout.load() || g_over_nr.load();
@@ -380,6 +385,7 @@ qd_status run_mv(int fmt, bool ffn, const void *W0, const void *W1, const float 
             sa.y = y;
             sa.g_out = g_out;
             sa.u_out = u_out;
+            sa.res = res;
             sa.act = act;
             sa.eps = eps;
             hipError_t e = qd::launch_stream(fmt, batch, ffn, sa, grid, lds, hs);
@@ -395,6 +401,7 @@ qd_status run_mv(int fmt, bool ffn, const void *W0, const void *W1, const float 
     a.y = y;
     a.g_out = g_out;
     a.u_out = u_out;
+    a.res = res;
     a.N = N;
     a.K = K;
     a.row_bytes = row_bytes(fmt, K);
@@ -464,7 +471,8 @@ bool ffn_stream_plan(int fmt_a, int fmt_b, int64_t N_ff, int64_t K, const float 
 
 qd_status run_ffn_decode(int fmt_gu, const void *Wg, const void *Wu, int fmt_d, const void *Wd,
                          const float *x, const float *norm_w, float eps, int act, float *y,
-                         float *h_out, int64_t N_ff, int64_t K, int batch, void *stream) {
+                         float *h_out, int64_t N_ff, int64_t K, int batch, void *stream,
+                         const float *res = nullptr) {
     qd_status st = check_shape(fmt_gu, N_ff, K, batch);
     if (st != QD_OK) return st;
     st = check_shape(fmt_d, K, N_ff, batch);
@@ -483,6 +491,9 @@ qd_status run_ffn_decode(int fmt_gu, const void *Wg, const void *Wu, int fmt_d, 
             return QD_EINVAL;
     }
     if (h_out && overlap(y, xbytes, h_out, hbytes)) return QD_EINVAL;
+    if (res && ((res != y && overlap(res, xbytes, y, xbytes)) || (h_out && overlap(res, xbytes, h_out, hbytes))))
+        return QD_EINVAL;
+    if (res && !aligned(res, 4)) return QD_EALIGN;
 
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     const size_t h_floats = h_out ? 0 : (((size_t)batch * N_ff + 63) / 64) * 64;
@@ -531,6 +542,7 @@ qd_status run_ffn_decode(int fmt_gu, const void *Wg, const void *Wu, int fmt_d, 
             fa.norm_w = norm_w;
             fa.h = h_out ? h_out : w.partials;
             fa.y = y;
+            fa.res = res;
             fa.bar = w.counters + kCtlSlots + kMaxTiles;
             fa.act = act;
             fa.eps = eps;
@@ -558,7 +570,7 @@ qd_status run_ffn_decode(int fmt_gu, const void *Wg, const void *Wu, int fmt_d, 
                     stream, h_floats);
         if (st != QD_OK) return st;
         return run_mv(fmt_d, false, Wd, nullptr, h, nullptr, 0.f, 0, y, nullptr, nullptr, K, N_ff,
-                      batch, stream, h_floats);
+                      batch, stream, h_floats, res);
     }
     {
         Shape t = pa.s;
@@ -593,6 +605,7 @@ qd_status run_ffn_decode(int fmt_gu, const void *Wg, const void *Wu, int fmt_d, 
     b.W0 = static_cast<const uint8_t *>(Wd);
     b.x = h;
     b.y = y;
+    b.res = res;
     b.partials = w.partials + h_floats;
     b.counters = w.counters + kCtlSlots;
     b.N = K;
@@ -807,6 +820,13 @@ qd_status qgemv(qd_format fmt, const void *W, const float *x, float *y, int64_t 
                   stream);
 }
 
+qd_status qgemv_residual(qd_format fmt, const void *W, const float *x, const float *r, float *y,
+                         int64_t N, int64_t K, int batch, void *stream) {
+    if (!r) return QD_EINVAL;
+    return run_mv(fmt, false, W, nullptr, x, nullptr, 0.f, 0, y, nullptr, nullptr, N, K, batch,
+                  stream, 0, r);
+}
+
 qd_status qgemv_q4k(const void *W, const float *x, float *y, int64_t N, int64_t K, int batch,
                     void *stream) {
     return qgemv(QD_Q4_K, W, x, y, N, K, batch, stream);
@@ -837,6 +857,15 @@ qd_status qffn_gate_up_act(qd_format fmt, const void *Wg, const void *Wu, const 
                            const float *norm_w, float eps, qd_act act, float *h, float *g_out,
                            float *u_out, int64_t N_ff, int64_t K, int batch, void *stream) {
     return run_mv(fmt, true, Wg, Wu, x, norm_w, eps, act, h, g_out, u_out, N_ff, K, batch, stream);
+}
+
+qd_status qffn_decode_residual(qd_format fmt_gu, const void *Wg, const void *Wu, qd_format fmt_down,
+                               const void *Wd, const float *x, const float *norm_w, float eps,
+                               qd_act act, const float *r, float *y, float *h_out, int64_t N_ff,
+                               int64_t K, int batch, void *stream) {
+    if (!r) return QD_EINVAL;
+    return run_ffn_decode(fmt_gu, Wg, Wu, fmt_down, Wd, x, norm_w, eps, act, y, h_out, N_ff, K,
+                          batch, stream, r);
 }
 
 qd_status qffn_decode(qd_format fmt_gu, const void *Wg, const void *Wu, qd_format fmt_down,

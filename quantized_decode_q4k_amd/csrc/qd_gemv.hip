@@ -533,7 +533,10 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
                 for (int i = 0; i < NR; i++)
                     if (row[i] < N)
 #pragma unroll
-                        for (int b = 0; b < B; b++) store_out<YM>(a.y + (int64_t)b * N + row[i], v[i][b]);
+                        for (int b = 0; b < B; b++) {
+                            const int64_t o = (int64_t)b * N + row[i];
+                            store_out<YM>(a.y + o, a.res ? v[i][b] + a.res[o] : v[i][b]);
+                        }
             }
         } else {
             // partials are written with device-scope stores (write-through,
@@ -617,7 +620,8 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
             if (a.g_out) a.g_out[(int64_t)b * N + r] = s0;
             if (a.u_out) a.u_out[(int64_t)b * N + r] = s1;
         } else {
-            store_out<YM>(a.y + (int64_t)b * N + r, s0);
+            const int64_t o = (int64_t)b * N + r;
+            store_out<YM>(a.y + o, a.res ? s0 + a.res[o] : s0);
         }
     }
     if (tid == 0)  // ready for the next call

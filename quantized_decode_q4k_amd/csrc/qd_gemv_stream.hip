@@ -500,7 +500,8 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamArgs a) {
             if (a.g_out) a.g_out[(int64_t)b * N + row] = sr[0];
             if (a.u_out) a.u_out[(int64_t)b * N + row] = sr[1];
         } else {
-            a.y[(int64_t)b * N + row] = sr[0];
+            const int64_t o = (int64_t)b * N + row;
+            a.y[o] = a.res ? sr[0] + a.res[o] : sr[0];
         }
     }
 }
@@ -782,7 +783,8 @@ __global__ __launch_bounds__(64 * (NC + kPcMaxProducers)) void stream_pc_kernel(
             if (a.g_out) a.g_out[(int64_t)b * N + row] = sr[0];
             if (a.u_out) a.u_out[(int64_t)b * N + row] = sr[1];
         } else {
-            a.y[(int64_t)b * N + row] = sr[0];
+            const int64_t o = (int64_t)b * N + row;
+            a.y[o] = a.res ? sr[0] + a.res[o] : sr[0];
         }
     }
 }
@@ -1164,7 +1166,7 @@ __global__ __launch_bounds__(64 * (NC + 2)) void ffn_pc_kernel(FfnStreamArgs a) 
         const float *pp = partB + lr * a.nbB;
         float acc = 0.f;
         for (int t = 0; t < a.nbB; t++) acc += pp[t];
-        a.y[rB0 + lr] = acc;
+        a.y[rB0 + lr] = a.res ? acc + a.res[rB0 + lr] : acc;
     }
 }
 

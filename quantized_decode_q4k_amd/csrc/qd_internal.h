@@ -23,6 +23,7 @@ struct MvArgs {
     const float *x;         // [batch][K]
     const float *norm_w;    // [K] or nullptr
     float *y;               // GEMV: [batch][N]; FFN: h [batch][N]
+    const float *res;       // GEMV: optional [batch][N] added to y (may equal y)
     float *g_out;           // FFN optional [batch][N]
     float *u_out;           // FFN optional [batch][N]
     float *partials;        // split-K: [p_out][batch][nr][N]
@@ -92,6 +93,7 @@ struct StreamArgs {
     const float *x;         // [batch][K], 16-byte aligned
     const float *norm_w;    // optional RMS-norm weight [K]
     float *y, *g_out, *u_out;
+    const float *res;       // GEMV: optional [batch][N] added to y (may equal y)
     int64_t N, K;
     int64_t row_bytes;
     int64_t mat_bytes;      // N * row_bytes, a multiple of 16
@@ -124,6 +126,7 @@ struct FfnStreamArgs {
     const float *norm_w;    // [KA] or nullptr
     float *h;               // [NA]: device-scope stores in phase A, loads in phase B
     float *y;               // [NB]
+    const float *res;       // optional [NB] added to y (may equal y)
     unsigned *bar;          // grid barrier: [0] arrivals, [32] generation (zero-initialised)
     int64_t KA, KB;
     int64_t row_bytesA, row_bytesB, mat_bytesA, mat_bytesB;

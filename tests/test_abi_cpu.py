@@ -131,6 +131,23 @@ def test_qkv_validation(kw, status):
     assert _qkv(L, **kw) == status
 
 
+def test_residual_validation():
+    _, L = _lib()
+    g = L.qgemv_residual
+    R = A16c + 0x4000
+    assert g(0, A16, A16b, 0, A16c, 4, 256, 1, None) == 1            # null r
+    assert g(0, A16, A16b, R + 2, A16c, 4, 256, 1, None) == 3        # r misaligned
+    assert g(0, A16, A16b, A16c + 4, A16c, 4, 256, 1, None) == 1     # r overlaps y, not equal
+    assert g(0, A16, A16b, R, A16c, 4, 100, 1, None) == 2            # K not a multiple of 256
+    f = L.qffn_decode_residual
+    H = A16c + 0x8000
+    args = (0, A16, A16 + 0x8000, 1, A16 + 0x10000, A16b, None, 1e-6, 0)
+    assert f(*args, 0, A16c, None, 256, 256, 1, None) == 1           # null r
+    assert f(*args, A16c + 8, A16c, None, 256, 256, 1, None) == 1    # r overlaps y, not equal
+    assert f(*args, H + 4, A16c, H, 256, 256, 1, None) == 1          # r overlaps h_out
+    assert f(*args, R + 1, A16c, None, 256, 256, 1, None) == 3       # r misaligned
+
+
 def test_dequant_validation():
     _, L = _lib()
     assert L.qdequant(0, 0, A16b, 4, 256, None) == 1
