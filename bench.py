@@ -47,6 +47,7 @@ def parse():
     p.add_argument("--workload", default="gemma3_ffn",
                    choices=["gemma3_ffn", "gemma3_ffn_2k", "gemma4_ffn", "gemma4_ffn_2k",
                             "gemma4_ffn_b8", "gemma4_prefill", "gemma3_qkv", "gemma3_qkv_q8_0",
+                            "moe_decode",
                             "lm_head_q4k",
                             "lm_head_q8_0", "down_q6k", "gate_up_q4k", "copy"])
     p.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -129,6 +130,28 @@ class Workload:
             self.flops_gate_up = 2 * 2 * M * ff * hidden
             self.flops = self.flops_gate_up + 2 * M * hidden * ff
             base = {k: t(v) for k, v in mats.items()}
+        elif name == "moe_decode":
+            # 8 of 128 experts per token, hidden 2560, expert FF 1024 (Q4_K
+            # gate/up, Q6_K down); the routed ids differ from step to step,
+            # so the experts a step reads rotate through all 128 (653 MB)
+            self.n_exp, self.n_sel, hidden, ff = 128, 8, 2560, 1024
+            self.hidden, self.ff = hidden, ff
+            Wg = synth.quant_weights("q4_k", self.n_exp * ff, hidden, seed, tensor_id=101)
+            Wu = synth.quant_weights("q4_k", self.n_exp * ff, hidden, seed, tensor_id=102)
+            Wd = synth.quant_weights("q6_k", self.n_exp * hidden, ff, seed, tensor_id=103)
+            self.moe_w = (t(Wg), t(Wu), t(Wd))
+            self.weight_bytes = self.n_sel * (Wg.size + Wu.size + Wd.size) // self.n_exp
+            self.x = t(synth.normal((hidden,), seed, tensor_id=104))
+            self.nw = t(synth.normal((hidden,), seed, tensor_id=105, mean=1.0, std=0.1))
+            self.y = torch.empty((hidden,), device=dev)
+            import numpy as np
+            rng = np.random.default_rng(seed)
+            nsteps = 4096
+            ids = np.stack([rng.choice(self.n_exp, self.n_sel, replace=False) for _ in range(nsteps)])
+            coef = rng.dirichlet(np.ones(self.n_sel), size=nsteps)
+            self.moe_ids = t(ids.astype(np.int32))
+            self.moe_coef = t(coef.astype(np.float32))
+            base = {}
         elif name in ("gemma3_qkv", "gemma3_qkv_q8_0"):
             self.qkv_fmts = ("q4_k", "q4_k", "q6_k") if name == "gemma3_qkv" else ("q8_0",) * 3
             hidden = 2560
@@ -152,7 +175,13 @@ class Workload:
             self.weight_bytes = 512 << 20
             base = {"src": torch.empty(self.weight_bytes // 4, device=dev).fill_(1.0)}
             self.dst = torch.empty_like(base["src"])
-        ncopy = max(2, math.ceil(ROTATE_BYTES / max(1, self.weight_bytes))) if name != "copy" else 1
+        ncopy = max(2, math.ceil(ROTATE_BYTES / max(1, self.weight_bytes))) if name not in ("copy", "moe_decode") else 1
+        if name == "moe_decode":
+            ncopy = self.moe_ids.shape[0]   # one routed id set per step
+            self.copies = [base] * ncopy
+            self.ncopy = ncopy
+            self.i = 0
+            return
         self.copies = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(ncopy - 1)]
         self.ncopy = ncopy
         self.i = 0
@@ -170,6 +199,8 @@ class Workload:
             return "qgemv_q6k", self.hidden * (self.ff // 256) * 210 + 4 * b * (self.ff + self.hidden)
         if n.startswith("gemma3_qkv"):
             return "qqkv_proj", self.weight_bytes + 4 * (2 * 2560 + 4096)
+        if n == "moe_decode":
+            return "qmoe_ffn_decode", self.weight_bytes + 4 * (3 * self.hidden + 2 * self.n_sel * self.ff)
         if n.startswith("lm_head"):
             return "qgemv", self.weight_bytes + 4 * (2560 + 262144)
         return "copy", 2 * self.weight_bytes
@@ -195,8 +226,16 @@ class Workload:
             qd.qgemv(self.fmt, c["W"], self.x, self.y)
         elif n.startswith("gemma3_qkv"):
             self.qkv(c)
+        elif n == "moe_decode":
+            self.moe()
         else:
             self.dst.copy_(c["src"])
+
+    def moe(self):
+        j = self.i  # already advanced: the step's own routed set
+        Wg, Wu, Wd = self.moe_w
+        self.qd.qmoe_ffn_decode("q4_k", Wg, Wu, "q6_k", Wd, self.n_exp, self.moe_ids[j], self.moe_coef[j],
+                                self.x, self.nw, 1e-6, "gelu_tanh", y=self.y)
 
     def qkv(self, c):
         o = self.qkv_out
@@ -220,6 +259,8 @@ def _dominant(self):
         qd.qgemv(self.fmt, c["W"], self.x, self.y)
     elif n.startswith("gemma3_qkv"):
         self.qkv(c)
+    elif n == "moe_decode":
+        self.moe()
     else:
         self.dst.copy_(c["src"])
 
@@ -348,6 +389,9 @@ def main():
                       "K Q4_K 1024x2560, V Q6_K 1024x2560 (one qqkv_proj call)",
         "gemma3_qkv_q8_0": "Gemma-3-4B attention input projections in Q8_0, batch 1: RMS-norm + Q "
                            "2048x2560, K 1024x2560, V 1024x2560 (one qqkv_proj call)",
+        "moe_decode": "MoE decode FFN, batch 1: 8 of 128 experts (hidden 2560, expert FF 1024; Q4_K "
+                      "gate/up + GELU-tanh, Q6_K down), routed ids and weights on the device, new ids "
+                      "every step (one qmoe_ffn_decode call)",
         "gemma4_prefill": "Gemma-4-31B FFN prefill, 512 tokens: gate/up Q4_K 21504x5376 + "
                           "GELU-tanh -> bf16 h, down Q6_K 5376x21504 (bf16 MFMA, fp32 accumulate)",
     }

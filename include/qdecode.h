@@ -247,6 +247,43 @@ qd_status qffn_decode_residual(qd_format fmt_gu, const void *Wg, const void *Wu,
                                void *stream);
 
 /*
+ * y = sum_z coef[z] * Wd[e_z] h_z,  h_z = act(Wg[e_z] xn) * (Wu[e_z] xn),
+ * e_z = ids[z], z < n_sel, xn = RMSNorm(x) if norm_w else x   (batch 1)
+ *
+ * The mixture-of-experts FFN of one decode token (larql's MoE table: each
+ * routed expert's gate+up with the activation, then its down projection,
+ * the expert outputs combined with the router's weights).  The expert ids
+ * and weights are device arrays, read by the kernels (no host round trip),
+ * so a router running on the GPU can feed this call inside a graph.
+ *
+ *   fmt_gu, Wg, Wu  n_experts stacked N_ff x K matrices each (expert e at
+ *                   byte offset e * N_ff * qd_row_bytes(fmt_gu, K))
+ *   fmt_down, Wd    n_experts stacked K x N_ff matrices (expert e at byte
+ *                   offset e * K * qd_row_bytes(fmt_down, N_ff))
+ *   ids             int32 [n_sel] expert per slot (repeats allowed; an id
+ *                   outside [0, n_experts) makes its slot contribute zero)
+ *   coef            fp32 [n_sel] routing weight per slot
+ *   n_sel           1..64 selected slots
+ *   x, norm_w, eps, act   as qffn_gate_up_act (one token: x is fp32 [K])
+ *   y               fp32 [K], overwritten
+ *   h_out           optional fp32 [n_sel][N_ff] (16-byte aligned) copy of
+ *                   every slot's h (NULL = kept in the workspace)
+ * Accuracy: each h_z as in qffn_gate_up_act; y within
+ * sum_z |coef[z]| (1e-4 sum|w h_z| + 1e-6) plus the fp32 rounding of the
+ * weighted sum, for the h it was computed from.  The slots are summed in
+ * slot order (deterministic).
+ * Errors: QD_ESHAPE (shapes, n_experts < 1, n_sel outside 1..64),
+ * QD_EINVAL (NULL pointers, bad act, outputs overlapping inputs),
+ * QD_EALIGN, QD_EUNSUPPORTED when K or N_ff does not fit one workgroup's
+ * LDS (K or N_ff up to 14592 in Q4_K).  Calls that overlap on one stream's
+ * workspace race.
+ */
+qd_status qmoe_ffn_decode(qd_format fmt_gu, const void *Wg, const void *Wu, qd_format fmt_down,
+                          const void *Wd, int n_experts, const int32_t *ids, const float *coef,
+                          int n_sel, const float *x, const float *norm_w, float eps, qd_act act,
+                          float *y, float *h_out, int64_t N_ff, int64_t K, void *stream);
+
+/*
  * Y = X W^T for a multi-token prefill: the weights are dequantised to bf16
  * and contracted on the bf16 matrix cores with fp32 accumulation.  dotLLM
  * PR #320 (Vulkan backend section) adds a tiled Q8_0 GEMM for multi-token

@@ -13,6 +13,7 @@ Entry points (same names as the C ABI):
     qffn_gate_up_act                               h = act(Wg xn) * (Wu xn)
     qffn_decode                                    y = Wd h (whole FFN, one launch)
     qffn_decode_residual                           y = Wd h + r
+    qmoe_ffn_decode                                mixture-of-experts FFN (routed ids on device)
     qgemm_prefill, qgemm_prefill_gate_up_act       bf16 MFMA prefill GEMMs
     qdequant, qdequant_bf16                        decoded weights (tests)
 """
@@ -51,6 +52,8 @@ SIGNATURES = {
     "qgemv_q8_0": (_I, [_P, _P, _P, _I64, _I64, _I, _P]),
     "qgemv": (_I, [_I, _P, _P, _P, _I64, _I64, _I, _P]),
     "qgemv_residual": (_I, [_I, _P, _P, _P, _P, _I64, _I64, _I, _P]),
+    "qmoe_ffn_decode": (_I, [_I, _P, _P, _I, _P, _I, _P, _P, _I, _P, _P, _F, _I, _P, _P, _I64, _I64,
+                             _P]),
     "qffn_decode_residual": (_I, [_I, _P, _P, _I, _P, _P, _P, _F, _I, _P, _P, _P, _I64, _I64, _I,
                                   _P]),
     "qqkv_proj": (_I, [_I, _P, _I64, _I, _P, _I64, _I, _P, _I64, _P, _P, _F, _P, _P, _P, _I64, _I,
@@ -291,6 +294,37 @@ def qffn_decode_residual(fmt_gu, Wg: torch.Tensor, Wu: torch.Tensor, fmt_down, W
                                     float(eps), _act(act), _dev(r, "r", torch.float32),
                                     _dev(y, "y", torch.float32), hp, N, K, batch, _stream())
     _check("qffn_decode_residual", st)
+    return y
+
+
+def qmoe_ffn_decode(fmt_gu, Wg: torch.Tensor, Wu: torch.Tensor, fmt_down, Wd: torch.Tensor,
+                    n_experts: int, ids: torch.Tensor, coef: torch.Tensor, x: torch.Tensor,
+                    norm_w: torch.Tensor | None = None, eps: float = 1e-6, act="gelu_tanh",
+                    y: torch.Tensor | None = None, h_out: torch.Tensor | None = None) -> torch.Tensor:
+    """y = sum_z coef[z] Wd[ids[z]] (act(Wg[ids[z]] xn) * (Wu[ids[z]] xn)) for one token.
+    Wg, Wu, Wd hold n_experts stacked matrices; ids (int32) and coef (fp32)
+    are device tensors of n_sel slots."""
+    fg, fd = _fmt(fmt_gu), _fmt(fmt_down)
+    K = x.shape[-1]
+    if x.dim() != 1:
+        raise ValueError("x must be one token, shape [K]")
+    if Wg.numel() % n_experts or Wd.numel() % n_experts:
+        raise ValueError("weights must hold n_experts equal matrices")
+    N = _rows(fg, Wg[: Wg.numel() // n_experts], K)
+    if Wu.numel() != Wg.numel() or _rows(fd, Wd[: Wd.numel() // n_experts], N) != K:
+        raise ValueError("gate/up must be n_experts x N_ff x K and down n_experts x K x N_ff")
+    n_sel = ids.numel()
+    if coef.numel() != n_sel:
+        raise ValueError("ids and coef must have one entry per slot")
+    if y is None:
+        y = torch.empty_like(x)
+    nw = _dev(norm_w, "norm_w", torch.float32) if norm_w is not None else None
+    hp = _dev(h_out, "h_out", torch.float32) if h_out is not None else None
+    st = lib().qmoe_ffn_decode(fg, _dev(Wg, "Wg", torch.uint8), _dev(Wu, "Wu", torch.uint8), fd,
+                               _dev(Wd, "Wd", torch.uint8), n_experts, _dev(ids, "ids", torch.int32),
+                               _dev(coef, "coef", torch.float32), n_sel, _dev(x, "x", torch.float32), nw,
+                               float(eps), _act(act), _dev(y, "y", torch.float32), hp, N, K, _stream())
+    _check("qmoe_ffn_decode", st)
     return y
 
 

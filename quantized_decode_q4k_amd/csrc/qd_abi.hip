@@ -792,6 +792,104 @@ qd_status run_qkv(const int fmt[3], const void *const W[3], const int64_t N[3], 
     return e == hipSuccess ? QD_OK : QD_ELAUNCH;
 }
 
+// Mixture-of-experts decode FFN, batch 1: y = sum_z coef[z] * Wd[e_z] h_z,
+// h_z = act(Wg[e_z] xn) * (Wu[e_z] xn), e_z = ids[z] (device arrays).
+constexpr int kMoeMaxSlots = 64;
+
+// Lane groups per row: the fewest (from 2) that give a workgroup per CU over
+// all slots.
+int moe_p_in(int64_t rows, int n_sel) {
+    int p_in = 2;
+    while (p_in < 16 && (rows * p_in / qd::kGroups) * n_sel < kCUs) p_in *= 2;
+    return p_in;
+}
+
+qd_status run_moe(int fmt_gu, const void *Wg, const void *Wu, int fmt_d, const void *Wd, int n_experts,
+                  const int32_t *ids, const float *coef, int n_sel, const float *x, const float *norm_w,
+                  float eps, int act, float *y, float *h_out, int64_t N_ff, int64_t K, void *stream) {
+    qd_status st = check_shape(fmt_gu, N_ff, K, 1);
+    if (st != QD_OK) return st;
+    st = check_shape(fmt_d, K, N_ff, 1);
+    if (st != QD_OK) return st;
+    if (n_experts < 1 || n_sel < 1 || n_sel > kMoeMaxSlots) return QD_ESHAPE;
+    if (!Wg || !Wu || !Wd || !ids || !coef || !x || !y) return QD_EINVAL;
+    if (act != QD_ACT_GELU_TANH && act != QD_ACT_SILU) return QD_EINVAL;
+    if (!aligned(Wg, 16) || !aligned(Wu, 16) || !aligned(Wd, 16) || !aligned(x, 16)) return QD_EALIGN;
+    if ((norm_w && !aligned(norm_w, 16)) || (h_out && !aligned(h_out, 16))) return QD_EALIGN;
+    if (!aligned(y, 4) || !aligned(ids, 4) || !aligned(coef, 4)) return QD_EALIGN;
+    const int64_t rb_a = row_bytes(fmt_gu, K), rb_b = row_bytes(fmt_d, N_ff);
+    const size_t ybytes = (size_t)K * 4, hbytes = (size_t)n_sel * N_ff * 4;
+    const void *ins[7] = {Wg, Wu, Wd, x, norm_w, ids, coef};
+    const size_t insz[7] = {(size_t)n_experts * N_ff * rb_a, (size_t)n_experts * N_ff * rb_a,
+                            (size_t)n_experts * K * rb_b, (size_t)K * 4, (size_t)K * 4,
+                            (size_t)n_sel * 4, (size_t)n_sel * 4};
+    for (int i = 0; i < 7; i++)
+        if (overlap(y, ybytes, ins[i], insz[i]) || (h_out && overlap(h_out, hbytes, ins[i], insz[i])))
+            return QD_EINVAL;
+    if (h_out && overlap(y, ybytes, h_out, hbytes)) return QD_EINVAL;
+    // every slot stages its whole activation row in one workgroup
+    const int nb_a = (int)((K + qd::kSuper - 1) / qd::kSuper);
+    const int nb_b = (int)((N_ff + qd::kSuper - 1) / qd::kSuper);
+    if (nb_a > lds_units_max(fmt_gu, 1) || nb_b > lds_units_max(fmt_d, 1)) return QD_EUNSUPPORTED;
+
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    const Plan pa = make_plan(fmt_gu, N_ff, K, 1, true, Shape{moe_p_in(N_ff, n_sel), 1, 1, 1});
+    const Plan pb = make_plan(fmt_d, K, N_ff, 1, false, Shape{moe_p_in(K, n_sel), 1, 1, 1});
+    if (pb.tiles > kMaxTiles) return QD_EUNSUPPORTED;
+    const size_t h_floats = h_out ? 0 : (((size_t)n_sel * N_ff + 63) / 64) * 64;
+    Workspace w;
+    st = get_workspace(hs, h_floats + (size_t)n_sel * K, &w);
+    if (st != QD_OK) return st;
+    float *h = h_out ? h_out : w.partials;
+
+    qd::MvArgs a{};
+    a.W0 = static_cast<const uint8_t *>(Wg);
+    a.W1 = static_cast<const uint8_t *>(Wu);
+    a.x = x;
+    a.norm_w = norm_w;
+    a.y = h;
+    a.N = N_ff;
+    a.K = K;
+    a.row_bytes = rb_a;
+    a.nb = nb_a;
+    a.nblk = (int)(K / block_elems(fmt_gu));
+    a.nk = nb_a;
+    a.p_in = pa.s.p_in;
+    a.p_out = 1;
+    a.rpg = 1;
+    a.act = act;
+    a.eps = eps;
+    a.ids = ids;
+    a.w_estride = N_ff * rb_a;
+    a.y_sstride = N_ff;
+    a.n_experts = n_experts;
+    hipError_t e = qd::launch_moe(fmt_gu, true, a, pa.tiles, n_sel, hs);
+    if (e != hipSuccess) return QD_ELAUNCH;
+
+    qd::MvArgs b{};
+    b.W0 = static_cast<const uint8_t *>(Wd);
+    b.x = h;
+    b.y = y;
+    b.partials = w.partials + h_floats;
+    b.counters = w.counters + kCtlSlots;
+    b.N = K;
+    b.K = N_ff;
+    b.row_bytes = rb_b;
+    b.nb = nb_b;
+    b.nblk = (int)(N_ff / block_elems(fmt_d));
+    b.nk = nb_b;
+    b.p_in = pb.s.p_in;
+    b.p_out = n_sel;
+    b.rpg = 1;
+    b.ids = ids;
+    b.coef = coef;
+    b.w_estride = K * rb_b;
+    b.x_sstride = N_ff;
+    b.n_experts = n_experts;
+    e = qd::launch_moe(fmt_d, false, b, pb.tiles, n_sel, hs);
+    return e == hipSuccess ? QD_OK : QD_ELAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -866,6 +964,14 @@ qd_status qffn_decode_residual(qd_format fmt_gu, const void *Wg, const void *Wu,
     if (!r) return QD_EINVAL;
     return run_ffn_decode(fmt_gu, Wg, Wu, fmt_down, Wd, x, norm_w, eps, act, y, h_out, N_ff, K,
                           batch, stream, r);
+}
+
+qd_status qmoe_ffn_decode(qd_format fmt_gu, const void *Wg, const void *Wu, qd_format fmt_down,
+                          const void *Wd, int n_experts, const int32_t *ids, const float *coef, int n_sel,
+                          const float *x, const float *norm_w, float eps, qd_act act, float *y,
+                          float *h_out, int64_t N_ff, int64_t K, void *stream) {
+    return run_moe(fmt_gu, Wg, Wu, fmt_down, Wd, n_experts, ids, coef, n_sel, x, norm_w, eps, act, y,
+                   h_out, N_ff, K, stream);
 }
 
 qd_status qffn_decode(qd_format fmt_gu, const void *Wg, const void *Wu, qd_format fmt_down,

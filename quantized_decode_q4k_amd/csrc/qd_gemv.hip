@@ -269,7 +269,7 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
     const int rs = grp / p_in;            // row slot in this workgroup
     const int pi = grp - rs * p_in;       // K-interleave index
     const int RS = kGroups / p_in;        // row slots per workgroup
-    const int t_beg = ks * a.nk;
+    const int t_beg = a.coef ? 0 : ks * a.nk;  // expert slots each take the whole row
     const int t_end = min(a.nb, t_beg + a.nk);
     const int xstride = a.nk * kSuperPhys;
     float *xl = smem;                                 // [B][nk * 272]
@@ -535,7 +535,8 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
 #pragma unroll
                         for (int b = 0; b < B; b++) {
                             const int64_t o = (int64_t)b * N + row[i];
-                            store_out<YM>(a.y + o, a.res ? v[i][b] + a.res[o] : v[i][b]);
+                            const float vv = a.coef ? a.coef[ks] * v[i][b] : v[i][b];
+                            store_out<YM>(a.y + o, a.res ? vv + a.res[o] : vv);
                         }
             }
         } else {
@@ -612,7 +613,8 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
         float s0 = 0.f, s1 = 0.f;
         for (int k = 0; k < p_out; k++) {
             const float *p = a.partials + (((int64_t)k * B + b) * NP) * N + r;
-            s0 += __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const float pv = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s0 = a.coef ? fmaf(a.coef[k], pv, s0) : s0 + pv;
             if constexpr (FFN) s1 += __hip_atomic_load(p + N, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         if constexpr (FFN) {
@@ -674,6 +676,66 @@ __global__ __launch_bounds__(kThreads) void ffn_kernel(FfnArgs f) {
         ws.arrived = f.ctl + (2 * ks + 1) * kCtlStride;
         ws.readers = (unsigned)f.nBx;
         mv_tile<FB, B, 1, false, kCoherent, kPlain>(f.b, bx, ks, f.pB, smem, ws);
+    }
+}
+
+// ------------------------------------------- mixture-of-experts decode ---
+// The larql MoE rows (Gemma 4 26B-A4B and the other expert models) run the
+// FFN of each routed expert: gate/up with the activation, then down, with
+// the experts' outputs summed with their routing weights.  The expert ids
+// and weights stay on the device (no host round trip): slot z of the launch
+// reads ids[z] and offsets the weight pointers by that expert's matrix.
+//  * gate/up (FFN = true, grid (tiles, 1, n_sel)): slot z = blockIdx.z
+//    writes its h rows at y + z * y_sstride; an id outside [0, n_experts)
+//    writes zeros (the slot contributes nothing);
+//  * down (FFN = false, grid (tiles, n_sel)): slot z = blockIdx.y reads
+//    h_z over the whole row as split-K slice z, and the last workgroup of a
+//    row tile sums coef[z] * partial_z in slot order (deterministic).  An
+//    invalid id reads expert 0's weights against its zero h.
+template <int FMT, bool FFN>
+__global__ __launch_bounds__(kThreads) void moe_kernel(MvArgs a) {
+    extern __shared__ __attribute__((aligned(16))) float smem[];
+    const int slot = FFN ? (int)blockIdx.z : (int)blockIdx.y;
+    int e = a.ids[slot];
+    const bool valid = e >= 0 && e < a.n_experts;
+    e = valid ? e : 0;
+    MvArgs b = a;
+    b.W0 = a.W0 + (int64_t)e * a.w_estride;
+    if constexpr (FFN) {
+        b.W1 = a.W1 + (int64_t)e * a.w_estride;
+        b.y = a.y + (int64_t)slot * a.y_sstride;
+        if (!valid) {
+            const int rows = kGroups / a.p_in;
+            const int64_t r0 = (int64_t)blockIdx.x * rows;
+            for (int r = threadIdx.x; r < rows; r += kThreads)
+                if (r0 + r < a.N) b.y[r0 + r] = 0.f;
+            return;
+        }
+        mv_tile<FMT, 1, 2, true, kPlain, kPlain>(b, blockIdx.x, 0, 1, smem);
+    } else {
+        b.x = a.x + (int64_t)slot * a.x_sstride;
+        mv_tile<FMT, 1, 1, false, kPlain, kPlain>(b, blockIdx.x, slot, gridDim.y, smem);
+    }
+}
+
+template <int FMT>
+static hipError_t launch_moe_f(bool ffn, const MvArgs &a, int64_t tiles, int n_sel, hipStream_t st) {
+    const size_t lds = mv_lds_bytes(FMT, 1, a.nk);
+    if (ffn)
+        hipLaunchKernelGGL((moe_kernel<FMT, true>), dim3((unsigned)tiles, 1, (unsigned)n_sel), dim3(kThreads), lds,
+                           st, a);
+    else
+        hipLaunchKernelGGL((moe_kernel<FMT, false>), dim3((unsigned)tiles, (unsigned)n_sel), dim3(kThreads), lds,
+                           st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_moe(int fmt, bool ffn, const MvArgs &a, int64_t tiles, int n_sel, hipStream_t st) {
+    switch (fmt) {
+    case kQ4K: return launch_moe_f<kQ4K>(ffn, a, tiles, n_sel, st);
+    case kQ6K: return launch_moe_f<kQ6K>(ffn, a, tiles, n_sel, st);
+    case kQ80: return launch_moe_f<kQ80>(ffn, a, tiles, n_sel, st);
+    default: return hipErrorInvalidValue;
     }
 }
 

@@ -39,6 +39,15 @@ struct MvArgs {
     int rpg;                // row slots each lane group walks (0 or 1: one)
     int act;                // qd_act
     float eps;
+    // Mixture-of-experts decode (moe_kernel): slot z of the launch uses
+    // expert ids[z] of n_experts stacked matrices (w_estride bytes apart).
+    // Gate/up: slot z writes y + z * y_sstride.  Down: slot z reads
+    // x + z * x_sstride over the whole row and is split-K slice z, and the
+    // slices are summed with weights coef[z].
+    const int32_t *ids;
+    const float *coef;
+    int64_t w_estride, x_sstride, y_sstride;
+    int n_experts;
 };
 
 struct Shape {
@@ -52,6 +61,9 @@ struct Shape {
 // LDS bytes the GEMV kernel needs for `nk` staged superunits of `batch` rows.
 size_t mv_lds_bytes(int fmt, int batch, int nk);
 hipError_t launch_gemv(int fmt, int batch, bool ffn, MvArgs a, Shape s, hipStream_t st);
+// Mixture-of-experts decode GEMVs (qd_gemv.hip), batch 1, n_sel slots:
+// gate/up (ffn) on a (tiles, 1, n_sel) grid, down on (tiles, n_sel).
+hipError_t launch_moe(int fmt, bool ffn, const MvArgs &a, int64_t tiles, int n_sel, hipStream_t st);
 
 // Fused Q/K/V projection (qd_gemv.hip): three GEMVs over the same activation
 // rows in one launch.  Workgroups [0, tiles[0]) are row tiles of matrix 0,

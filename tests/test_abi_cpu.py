@@ -148,6 +148,34 @@ def test_residual_validation():
     assert f(*args, R + 1, A16c, None, 256, 256, 1, None) == 3       # r misaligned
 
 
+def test_moe_validation():
+    _, L = _lib()
+    f = L.qmoe_ffn_decode
+    Wg, Wu, Wd = A16, A16 + 0x10000, A16 + 0x20000
+    I, C, X, Y = 0x100000, 0x100100, 0x100200, 0x110000
+    ok = dict(fg=0, wg=Wg, wu=Wu, fd=1, wd=Wd, ne=2, ids=I, coef=C, ns=2, x=X, nw=None, act=0,
+              y=Y, h=None, nff=256, k=256)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["fg"], a["wg"], a["wu"], a["fd"], a["wd"], a["ne"], a["ids"], a["coef"], a["ns"],
+                 a["x"], a["nw"], 1e-6, a["act"], a["y"], a["h"], a["nff"], a["k"], None)
+    assert call(ids=0) == 1          # null ids
+    assert call(coef=0) == 1         # null coef
+    assert call(act=4) == 1          # bad activation
+    assert call(ne=0) == 2           # no experts
+    assert call(ns=0) == 2           # no slots
+    assert call(ns=65) == 2          # too many slots
+    assert call(nff=100) == 2        # N_ff not a multiple of 256
+    assert call(ids=I + 2) == 3      # ids misaligned
+    assert call(h=Y + 0x1008) == 3   # h_out misaligned
+    assert call(y=Wd + 64) == 1      # y overlaps the down weights
+    assert call(h=X) == 1            # h_out overlaps x
+    assert call(y=I) == 1            # y overlaps ids
+    far = dict(wg=1 << 40, wu=2 << 40, wd=3 << 40, x=4 << 40, y=5 << 40, ids=6 << 40, coef=7 << 40)
+    assert call(nff=16384, k=16384, **far) == 5   # rows beyond one workgroup's LDS
+
+
 def test_dequant_validation():
     _, L = _lib()
     assert L.qdequant(0, 0, A16b, 4, 256, None) == 1
