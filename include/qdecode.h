@@ -42,7 +42,11 @@
  *     argument returns an error code and enqueues nothing.  Launch failures
  *     return QD_ELAUNCH.  A device fault surfaces at the caller's next
  *     synchronisation of the stream.
- *   - Shapes: N, M >= 1; batch in 1..QD_MAX_BATCH; K a positive multiple of
+ *   - Shapes: N, M >= 1; batch in 1..QD_MAX_BATCH (1 for qmoe_ffn_decode);
+ *     batches above QD_BATCH_CHUNK run as successive launches of up to
+ *     QD_BATCH_CHUNK columns on the same stream (the weights are streamed
+ *     once per chunk; dotLLM's batched decode reads them once per batch);
+ *     K a positive multiple of
  *     256 for Q4_K and Q6_K, of 32 for Q8_0 (dotLLM's CPU Q8_0 kernels reject
  *     lengths that are not a multiple of the 32-element block).
  *   - Alignment: weight pointers 16-byte aligned; fp32 and bf16 activation
@@ -80,7 +84,10 @@ typedef enum qd_format { QD_Q4_K = 0, QD_Q6_K = 1, QD_Q8_0 = 2 } qd_format;
  * the gerbil architecture guide's SwiGLU MLP: SiLU(gate) times up. */
 typedef enum qd_act { QD_ACT_GELU_TANH = 0, QD_ACT_SILU = 1 } qd_act;
 
-#define QD_MAX_BATCH 8
+#define QD_MAX_BATCH 64
+/* Columns of x one launch streams the weights for; larger batches run as
+ * successive launches of up to this many columns each. */
+#define QD_BATCH_CHUNK 8
 
 /* Weights per block (256, 256, 32) and bytes per block (144, 210, 34);
  * 0 for an unknown format. */

@@ -32,7 +32,8 @@ Q4_K, Q6_K, Q8_0 = 0, 1, 2
 FORMATS = {"q4_k": Q4_K, "q6_k": Q6_K, "q8_0": Q8_0}
 ACT_GELU_TANH, ACT_SILU = 0, 1
 ACTS = {"gelu_tanh": ACT_GELU_TANH, "silu": ACT_SILU}
-MAX_BATCH = 8
+MAX_BATCH = 64
+BATCH_CHUNK = 8
 
 QD_OK, QD_EINVAL, QD_ESHAPE, QD_EALIGN, QD_ELAUNCH, QD_EUNSUPPORTED, QD_ENOMEM = range(7)
 

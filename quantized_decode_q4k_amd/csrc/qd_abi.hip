@@ -371,6 +371,17 @@ qd_status run_mv(int fmt, bool ffn, const void *W0, const void *W1, const float 
     // output is written, so it may be y itself, but no other part of it
     if (res && (ffn || (res != y && overlap(res, ybytes, y, ybytes)))) return QD_EINVAL;
     if (res && !aligned(res, 4)) return QD_EALIGN;
+    if (batch > QD_BATCH_CHUNK) {
+        // successive launches of up to QD_BATCH_CHUNK columns
+        for (int c0 = 0; c0 < batch; c0 += QD_BATCH_CHUNK) {
+            const int nb = std::min(QD_BATCH_CHUNK, batch - c0);
+            const int64_t xo = (int64_t)c0 * K, yo = (int64_t)c0 * N;
+            qd_status cs = run_mv(fmt, ffn, W0, W1, x + xo, norm_w, eps, act, y + yo, g_out ? g_out + yo : nullptr,
+                                  u_out ? u_out + yo : nullptr, N, K, nb, stream, ws_offset, res ? res + yo : nullptr);
+            if (cs != QD_OK) return cs;
+        }
+        return QD_OK;
+    }
 
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     const bool forced = g_over_pin.load() || g_over_pout.load() || g_over_nr.load();
@@ -494,6 +505,17 @@ qd_status run_ffn_decode(int fmt_gu, const void *Wg, const void *Wu, int fmt_d, 
     if (res && ((res != y && overlap(res, xbytes, y, xbytes)) || (h_out && overlap(res, xbytes, h_out, hbytes))))
         return QD_EINVAL;
     if (res && !aligned(res, 4)) return QD_EALIGN;
+    if (batch > QD_BATCH_CHUNK) {
+        for (int c0 = 0; c0 < batch; c0 += QD_BATCH_CHUNK) {
+            const int nb = std::min(QD_BATCH_CHUNK, batch - c0);
+            const int64_t xo = (int64_t)c0 * K;
+            qd_status cs = run_ffn_decode(fmt_gu, Wg, Wu, fmt_d, Wd, x + xo, norm_w, eps, act, y + xo,
+                                          h_out ? h_out + (int64_t)c0 * N_ff : nullptr, N_ff, K, nb, stream,
+                                          res ? res + xo : nullptr);
+            if (cs != QD_OK) return cs;
+        }
+        return QD_OK;
+    }
 
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     const size_t h_floats = h_out ? 0 : (((size_t)batch * N_ff + 63) / 64) * 64;
@@ -743,6 +765,15 @@ qd_status run_qkv(const int fmt[3], const void *const W[3], const int64_t N[3], 
             if (overlap(y[i], yb, W[j], (size_t)N[j] * row_bytes(fmt[j], K))) return QD_EINVAL;
             if (j != i && overlap(y[i], yb, y[j], (size_t)batch * N[j] * 4)) return QD_EINVAL;
         }
+    }
+    if (batch > QD_BATCH_CHUNK) {
+        for (int c0 = 0; c0 < batch; c0 += QD_BATCH_CHUNK) {
+            const int nbc = std::min(QD_BATCH_CHUNK, batch - c0);
+            float *const yc[3] = {y[0] + (int64_t)c0 * N[0], y[1] + (int64_t)c0 * N[1], y[2] + (int64_t)c0 * N[2]};
+            qd_status cs = run_qkv(fmt, W, N, x + (int64_t)c0 * K, norm_w, eps, yc, K, nbc, stream);
+            if (cs != QD_OK) return cs;
+        }
+        return QD_OK;
     }
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     const int nb = (int)(K / qd::kSuper);

@@ -69,7 +69,7 @@ A16c = 0x30000
     ((A16, A16b, A16c, 0, 256, 1, None), 2),        # N = 0
     ((A16, A16b, A16c, 4, 100, 1, None), 2),        # K not a multiple of 256
     ((A16, A16b, A16c, 4, 256, 0, None), 2),        # batch 0
-    ((A16, A16b, A16c, 4, 256, 9, None), 2),        # batch 9
+    ((A16, A16b, A16c, 4, 256, 65, None), 2),       # batch 65
     ((A16 + 4, A16b, A16c, 4, 256, 1, None), 3),    # W misaligned
     ((A16, A16b + 4, A16c, 4, 256, 1, None), 3),    # x misaligned
     ((A16, A16b, A16c + 2, 4, 256, 1, None), 3),    # y misaligned
@@ -116,7 +116,7 @@ def _qkv(L, fq=0, wq=A16, nq=4, fk=0, wk=QK, nk=4, fv=1, wv=QV, nv=4, x=A16b, nw
     (dict(nk=0), 2),                      # K projection with no rows
     (dict(K=320), 2),                     # K not a multiple of 256 (k-quants)
     (dict(fq=2, fk=2, fv=2, K=48), 2),    # Q8_0 K not a multiple of 32
-    (dict(batch=9), 2),                   # batch above 8
+    (dict(batch=65), 2),                  # batch above 64
     (dict(wv=QV + 8), 3),                 # V weights misaligned
     (dict(x=A16b + 4), 3),                # x misaligned
     (dict(nw=A16b + 0x1004), 3),          # norm weight misaligned
