@@ -31,7 +31,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t *W, flo
     load_unit<FMT>(r, rowp, t, c, nblk);
     if constexpr (FMT == kQ4K) {
         const Q4Scales s = q4k_scales(r, q4k_lane(c));
-        const float inv_unit = 1.0f / fp8_unit();
+        const float inv_unit = fp8_inv_unit();
         const float a0 = s.d * s.sc0 * inv_unit, a1 = s.d * s.sc1 * inv_unit;
         const float b0 = -(s.dmin * s.m0), b1 = -(s.dmin * s.m1);
         for (int dw = 0; dw < 8; dw++) {

@@ -45,6 +45,10 @@ QD_DEV float2 nib2_hi(uint32_t v) {  // bytes 2, 3
     return make_float2(r[0], r[1]);
 }
 QD_DEV float fp8_unit() { return __builtin_amdgcn_cvt_f32_fp8(1, 0); }
+// 1 / fp8_unit() as a constant: gfx950's converter reads OCP e4m3, whose
+// smallest subnormal is 2^-9 (a division by the converted value would not
+// fold and costs a full-precision divide wherever it is used).
+QD_DEV constexpr float fp8_inv_unit() { return 512.0f; }
 
 // Activations in fp32 (the larql Gemma 3 table's GELU-tanh geglu; the Llama
 // table's SiLU).

@@ -327,13 +327,28 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
     const int t0 = t_beg + pi;
     const int nsu = (a.nk + p_in - 1) / p_in;
     const int Q = rpg * nsu;
+    // Q4_K / Q6_K: each lane's block of unit (0, 0) per row stream, once; unit
+    // (r, u) lies r * rstep rows and u * p_in blocks further (uniform byte
+    // offsets, so no per-lane 64-bit multiply per load).  Q8_0 keeps the
+    // block index for its partial-superunit check.
+    constexpr int64_t kUB = FMT == kQ4K ? 144 : 210;
+    const uint8_t *ub0[NR];
+#pragma unroll
+    for (int i = 0; i < NR; i++) ub0[i] = mat[i] + row0[i] * a.row_bytes + (int64_t)t0 * kUB;
+    const int64_t rstride_b = rstep * a.row_bytes;
+    const int64_t ustride_b = (int64_t)p_in * kUB;
     auto load_at = [&](Raw (&dst)[NR], int r, int u, bool inq) {
         const int t = t0 + u * p_in;
 #pragma unroll
         for (int i = 0; i < NR; i++) {
             const int64_t rw = row0[i] + r * rstep;
             const bool live = inq && t < t_end && rw < a.N;
-            load_unit<FMT>(dst[i], live ? mat[i] + rw * a.row_bytes : g_zero_block, live ? t : 0, c, a.nblk);
+            if constexpr (FMT == kQ80) {
+                load_unit<FMT>(dst[i], live ? mat[i] + rw * a.row_bytes : g_zero_block, live ? t : 0, c, a.nblk);
+            } else {
+                const uint8_t *blk = ub0[i] + (r * rstride_b + u * ustride_b);
+                load_unit<FMT>(dst[i], live ? blk : g_zero_block, 0, c, a.nblk);
+            }
         }
     };
     int rl = 0, ul = 0;  // row slot and unit of the next unit to load
@@ -502,7 +517,7 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
         for (int i = 0; i < NR; i++)
 #pragma unroll
             for (int b = 0; b < B; b++) {
-                if constexpr (FMT == kQ4K) v[i][b] = fmaf(acc[i][b], 1.0f / fp8_unit(), -acc2[i][b]);
+                if constexpr (FMT == kQ4K) v[i][b] = fmaf(acc[i][b], fp8_inv_unit(), -acc2[i][b]);
                 else v[i][b] = acc[i][b];
                 acc[i][b] = 0.f;
                 acc2[i][b] = 0.f;

@@ -132,7 +132,7 @@ QD_DEV void lds_q80(RawQ80 &r, const uint8_t *blk, int c) {
 template <int NR, int B>
 QD_DEV void dot_q4k(const RawQ4K (&r)[NR], const float4 (&xv)[B][16], const float2 (&X)[B],
                     const Q4Lane &L, float (&out)[NR][B]) {
-    const float inv_unit = 1.0f / fp8_unit();  // exact power of two
+    const float inv_unit = fp8_inv_unit();  // exact power of two
 #pragma unroll
     for (int i = 0; i < NR; i++) {
         float alo[B], ahi[B];

@@ -78,7 +78,7 @@ struct Dec<kQ4K> {
 
     QD_DEV void prep(const RawQ4K &r, int c) {
         const Q4Scales s = q4k_scales(r, q4k_lane(c));
-        const float inv_unit = 1.0f / fp8_unit();
+        const float inv_unit = fp8_inv_unit();
         a0 = s.d * s.sc0 * inv_unit;
         a1 = s.d * s.sc1 * inv_unit;
         b0 = -(s.dmin * s.m0);
