@@ -168,8 +168,11 @@ struct Dec<kQ80> {
     }
 };
 
+// One workgroup per CU and so one wave per SIMD: the whole register file is
+// this wave's, which lets the next step's activation operands load while the
+// current step's MFMAs run.
 template <int FMT, bool FFN, int TM>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(GemmArgs a) {
     constexpr int BM = 32 * TM;
     constexpr int XBUF = BM * kXRowBytes;     // bytes per activation buffer
     constexpr int XLOADS = BM / 16;           // global_load_lds per wave per K-tile
@@ -259,13 +262,21 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
         dec[1].prep(cur[1], c);
         if (kt + 1 < kt1) issue(kt + 1, buf ^ 1, nxt);
         const uint8_t *xb = xa + buf * XBUF;
-        auto mstep = [&](auto sc) {
+        // A operands of step S (TM token rows) from LDS
+        auto load_a = [&](auto sc, bf16x8 (&A)[TM]) {
             constexpr int S = decltype(sc)::value;
             const int off = 16 * (xchunk<FMT>(S, h) ^ sw);
-            bf16x8 A[TM];
 #pragma unroll
             for (int i = 0; i < TM; i++)
                 A[i] = *reinterpret_cast<const bf16x8 *>(xb + i * 32 * kXRowBytes + off);
+            // keep these reads ahead of the MFMAs that follow (the scheduler
+            // would otherwise sink them next to their own, later MFMAs)
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        // step S's MFMAs on A; the operands of step S + 1 are read into the
+        // other buffer first, so their LDS latency overlaps these MFMAs
+        auto mstep = [&](auto sc, const bf16x8 (&A)[TM]) {
+            constexpr int S = decltype(sc)::value;
             const bf16x8 B0 = dec[0].template step<S>();
             const bf16x8 B1 = dec[1].template step<S>();
 #pragma unroll
@@ -274,14 +285,23 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
                 acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[i], B1, acc[i][1], 0, 0, 0);
             }
         };
-        mstep(std::integral_constant<int, 0>{});
-        mstep(std::integral_constant<int, 1>{});
-        mstep(std::integral_constant<int, 2>{});
-        mstep(std::integral_constant<int, 3>{});
-        mstep(std::integral_constant<int, 4>{});
-        mstep(std::integral_constant<int, 5>{});
-        mstep(std::integral_constant<int, 6>{});
-        mstep(std::integral_constant<int, 7>{});
+        bf16x8 Ae[TM], Ao[TM];
+        load_a(std::integral_constant<int, 0>{}, Ae);
+        load_a(std::integral_constant<int, 1>{}, Ao);
+        mstep(std::integral_constant<int, 0>{}, Ae);
+        load_a(std::integral_constant<int, 2>{}, Ae);
+        mstep(std::integral_constant<int, 1>{}, Ao);
+        load_a(std::integral_constant<int, 3>{}, Ao);
+        mstep(std::integral_constant<int, 2>{}, Ae);
+        load_a(std::integral_constant<int, 4>{}, Ae);
+        mstep(std::integral_constant<int, 3>{}, Ao);
+        load_a(std::integral_constant<int, 5>{}, Ao);
+        mstep(std::integral_constant<int, 4>{}, Ae);
+        load_a(std::integral_constant<int, 6>{}, Ae);
+        mstep(std::integral_constant<int, 5>{}, Ao);
+        load_a(std::integral_constant<int, 7>{}, Ao);
+        mstep(std::integral_constant<int, 6>{}, Ae);
+        mstep(std::integral_constant<int, 7>{}, Ao);
     };
 
     if (kt0 < kt1) issue(kt0, 0, raw[0]);
