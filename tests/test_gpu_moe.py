@@ -97,3 +97,13 @@ def test_moe_q6k_experts_many_slots(qd):
     ids = list(range(0, 24, 2)) + [1, 3, 5, 7]
     coef = list(np.linspace(0.02, 0.2, len(ids)))
     check_moe(qd, "q6_k", "q6_k", 768, 512, 24, ids, coef, "silu", tag="16 slots")
+
+
+def test_moe_bench_configuration(qd):
+    """The moe_decode bench workload's shape and launch configuration: 8 of 128
+    experts, hidden 2560, expert FF 1024, Q4_K gate/up with GELU-tanh, Q6_K
+    down, routing weights summing to one."""
+    rng = np.random.default_rng(7)
+    ids = [int(v) for v in rng.choice(128, 8, replace=False)]
+    coef = [float(v) for v in rng.dirichlet(np.ones(8))]
+    check_moe(qd, "q4_k", "q6_k", 2560, 1024, 128, ids, coef, "gelu_tanh", tag="bench config")
