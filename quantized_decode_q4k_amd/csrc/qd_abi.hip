@@ -301,7 +301,7 @@ bool stream_plan_pc(int fmt, bool ffn, int64_t N, int64_t K, int batch, const fl
 // layout that does not fit, and (unless overridden) plain GEMVs with K <
 // 8192.  The fused gate/up and the long-row GEMVs take the producer /
 // consumer kernel.  At batch 1: one workgroup per CU with 8 decoding waves,
-// 5 steps in flight per copying wave (fewer where the ring's slot-reuse
+// 4 steps in flight per copying wave (fewer where the ring's slot-reuse
 // bound asks), and 4 copying waves when a workgroup's rows hold 256 KB or
 // more (2 below).  At batch 2 (8 decoding waves spill registers): 4
 // decoding waves, 2 copying waves, 3 steps in flight, one workgroup per CU
@@ -331,7 +331,10 @@ bool stream_plan(int fmt, bool ffn, int64_t N, int64_t K, int batch, const float
     }
     if (!ffn && K < kStreamMinK) return false;
     if (batch == 1) {
-        constexpr int kPcLag1 = 5;
+        // steps in flight per copying wave (MI355X, decode FFN in graph
+        // replay, medians of 6 interleaved runs; lag 3 / 4 / 5): Gemma-3
+        // 20.32 / 20.26 / 20.49 us, Gemma-4-31B 56.64 / 56.86 / 56.77 us
+        constexpr int kPcLag1 = 4;
         const int64_t wg_bytes = (N + kCUs - 1) / kCUs * row_bytes(fmt, K) * (ffn ? 2 : 1);
         const int prod = wg_bytes >= (int64_t(256) << 10) ? 4 : 2;
         return stream_plan_pc(fmt, ffn, N, K, batch, norm_w, 1, 8, prod, kPcLag1, a, grid, lds);
