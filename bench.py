@@ -47,12 +47,15 @@ def parse():
     p.add_argument("--workload", default="gemma3_ffn",
                    choices=["gemma3_ffn", "gemma3_ffn_2k", "gemma4_ffn", "gemma4_ffn_2k",
                             "gemma4_ffn_b8", "gemma4_prefill", "gemma3_qkv", "gemma3_qkv_q8_0",
-                            "moe_decode",
+                            "moe_decode", "q4k_512x512",
                             "lm_head_q4k",
                             "lm_head_q8_0", "down_q6k", "gate_up_q4k", "copy"])
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="approximate CPU time budget of the oracle baseline (0 = skip)")
     p.add_argument("--seed", type=int, default=0x5EED)
+    p.add_argument("--rotate-mib", type=int, default=1024,
+                   help="distinct weight copies totalling at least this many MiB rotate through "
+                        "the steps (0 = one copy: warm caches)")
     p.add_argument("--override", default="",
                    help="p_in,p_out,nr launch-shape override (tuning only)")
     return p.parse_args()
@@ -89,7 +92,7 @@ def traffic_from_profiles(kernel_key: str, alg_bytes: float):
 class Workload:
     """Weights (rotating copies), activations and the per-step launches."""
 
-    def __init__(self, name, seed, dev):
+    def __init__(self, name, seed, dev, rotate_bytes=ROTATE_BYTES):
         import torch
         import synth
         import quantized_decode_q4k_amd as qd
@@ -130,6 +133,13 @@ class Workload:
             self.flops_gate_up = 2 * 2 * M * ff * hidden
             self.flops = self.flops_gate_up + 2 * M * hidden * ff
             base = {k: t(v) for k, v in mats.items()}
+        elif name == "q4k_512x512":
+            # the small parity configuration: one Q4_K GEMV, 512 rows x K = 512
+            W = synth.quant_weights("q4_k", 512, 512, seed, tensor_id=1)
+            self.weight_bytes = W.size
+            self.x = t(synth.normal((1, 512), seed, tensor_id=2))
+            self.y = torch.empty((1, 512), device=dev)
+            base = {"W": t(W)}
         elif name == "moe_decode":
             # 8 of 128 experts per token, hidden 2560, expert FF 1024 (Q4_K
             # gate/up, Q6_K down); the routed ids differ from step to step,
@@ -175,7 +185,9 @@ class Workload:
             self.weight_bytes = 512 << 20
             base = {"src": torch.empty(self.weight_bytes // 4, device=dev).fill_(1.0)}
             self.dst = torch.empty_like(base["src"])
-        ncopy = max(2, math.ceil(ROTATE_BYTES / max(1, self.weight_bytes))) if name not in ("copy", "moe_decode") else 1
+        ncopy = max(2, math.ceil(rotate_bytes / max(1, self.weight_bytes))) if name not in ("copy", "moe_decode") else 1
+        if rotate_bytes == 0:
+            ncopy = 1
         if name == "moe_decode":
             ncopy = self.moe_ids.shape[0]   # one routed id set per step
             self.copies = [base] * ncopy
@@ -199,6 +211,8 @@ class Workload:
             return "qgemv_q6k", self.hidden * (self.ff // 256) * 210 + 4 * b * (self.ff + self.hidden)
         if n.startswith("gemma3_qkv"):
             return "qqkv_proj", self.weight_bytes + 4 * (2 * 2560 + 4096)
+        if n == "q4k_512x512":
+            return "qgemv_q4k", self.weight_bytes + 4 * (512 + 512)
         if n == "moe_decode":
             return "qmoe_ffn_decode", self.weight_bytes + 4 * (3 * self.hidden + 2 * self.n_sel * self.ff)
         if n.startswith("lm_head"):
@@ -228,6 +242,8 @@ class Workload:
             self.qkv(c)
         elif n == "moe_decode":
             self.moe()
+        elif n == "q4k_512x512":
+            qd.qgemv_q4k(c["W"], self.x, self.y)
         else:
             self.dst.copy_(c["src"])
 
@@ -261,6 +277,8 @@ def _dominant(self):
         self.qkv(c)
     elif n == "moe_decode":
         self.moe()
+    elif n == "q4k_512x512":
+        qd.qgemv_q4k(c["W"], self.x, self.y)
     else:
         self.dst.copy_(c["src"])
 
@@ -324,7 +342,7 @@ def main():
         qd.set_launch_override(p_in, p_out, nr)
 
     log(f"[bench] workload={args.workload} steps={args.steps} warmup={args.warmup}")
-    wl = Workload(args.workload, args.seed, dev)
+    wl = Workload(args.workload, args.seed, dev, rotate_bytes=args.rotate_mib << 20)
     log(f"[bench] weight bytes/step={wl.weight_bytes} rotating copies={wl.ncopy}")
     for _ in range(args.warmup):
         wl.step()
@@ -414,6 +432,7 @@ def main():
             "weight_bytes_per_step": wl.weight_bytes,
             "us_per_step": round(ms_per_step * 1e3, 3),
             "rotating_weight_copies": wl.ncopy,
+            "rotate_mib": args.rotate_mib,
             "timing": "value/ms_per_step: K steps in one HIP graph replay; roofline: K eager "
                       "back-to-back launches of the dominant kernel between one HIP event pair",
             "seed": args.seed,
