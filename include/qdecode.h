@@ -73,7 +73,7 @@ typedef enum qd_status {
     QD_ESHAPE = 2,       /* N, M, K or batch out of range */
     QD_EALIGN = 3,       /* pointer not aligned as required */
     QD_ELAUNCH = 4,      /* the HIP runtime refused the launch */
-    QD_EUNSUPPORTED = 5, /* valid arguments this build does not handle */
+    QD_EUNSUPPORTED = 5, /* valid arguments the library has no kernel for */
     QD_ENOMEM = 6        /* workspace allocation failed */
 } qd_status;
 

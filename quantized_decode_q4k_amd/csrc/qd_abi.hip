@@ -940,7 +940,7 @@ const char *qd_status_str(qd_status s) {
     case QD_ESHAPE: return "shape out of range (N, M, K or batch)";
     case QD_EALIGN: return "pointer not aligned as required";
     case QD_ELAUNCH: return "kernel launch failed";
-    case QD_EUNSUPPORTED: return "not supported by this build";
+    case QD_EUNSUPPORTED: return "not supported by the library";
     case QD_ENOMEM: return "workspace allocation failed";
     default: return "unknown status";
     }

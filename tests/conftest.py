@@ -22,7 +22,7 @@ def gpu_available() -> bool:
 
 @pytest.fixture(scope="session")
 def gpu():
-    """Skip GPU tests where no GPU is present (this marker's tests are run on the GPU machine)."""
+    """Skip GPU tests where no GPU is present."""
     if not gpu_available():
         pytest.skip("no GPU")
     import torch
