@@ -52,5 +52,22 @@ def build(jobs: int = 4) -> str:
     return LIB
 
 
+def build_c_example() -> str:
+    """tests/c_abi_example.bin: a plain-C program calling the C ABI (host code
+    only, gcc) against the HIP runtime and the C oracle."""
+    src = os.path.join(ROOT, "tests", "c_abi_example.c")
+    out = os.path.join(ROOT, "tests", "c_abi_example.bin")
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(HIPCC)))
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-I", os.path.join(rocm, "include"), src,
+           os.path.join(ROOT, "oracle", "oracle.c"), "-o", out + ".tmp",
+           "-L", HERE, "-lqdecode", "-Wl,-rpath,$ORIGIN/../quantized_decode_q4k_amd",
+           "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-Wl,-rpath," + os.path.join(rocm, "lib"), "-lm"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"gcc failed for c_abi_example.c:\n{r.stderr}")
+    os.replace(out + ".tmp", out)
+    return out
+
+
 if __name__ == "__main__":
     print(build())
