@@ -56,6 +56,14 @@
  *     a small per-(device, stream) workspace allocated on first use; calls on
  *     the same stream are ordered by the stream, so they never share it
  *     concurrently.
+ *   - HIP graphs: a call captured into a graph keeps the address of the
+ *     workspace it used, and a later call on the same stream that needs a
+ *     larger workspace replaces it (after synchronising the stream) and frees
+ *     the old one.  Make one uncaptured call of each shape before capturing
+ *     (the workspace then has its final size), and do not make larger calls
+ *     on that stream while the graph is in use.  Counters in the workspace
+ *     return to zero at the end of every kernel that uses them, so replays
+ *     need no reset.
  */
 #ifndef QDECODE_H
 #define QDECODE_H
