@@ -70,6 +70,8 @@ def _load():
             "orc_silu": (D, [D]),
             "orc_act": (D, [I, D]),
             "orc_gemm_bf16": (I, [I, P, P, I64, I64, I64, I64, I64, I64, I64, P, P]),
+            "orc_quantize_q8_act": (I, [P, I64, I, P, P]),
+            "orc_gemv_q8_0_q8act": (I, [P, P, P, I64, I64, I, I64, I64, P, P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(lib, name)
@@ -162,6 +164,34 @@ def gemv(fmt, W: np.ndarray, x: np.ndarray, N: int, K: int,
     rc = _load().orc_gemv(fmt, _ptr(W), _ptr(x2), N, K, batch, n0, n1, _ptr(y), _ptr(S))
     if rc != 0:
         raise ValueError("orc_gemv failed")
+    return y, S
+
+
+def quantize_q8_act(x: np.ndarray):
+    """(q, d): x [batch, K] (or [K]) quantized per run of 32 to int8 q and
+    fp32 d = max|x| / 127, q = round(x / d) halves away from zero."""
+    x2 = np.ascontiguousarray(np.atleast_2d(x), dtype=np.float32)
+    batch, K = x2.shape
+    q = np.empty((batch, K), dtype=np.int8)
+    d = np.empty((batch, K // 32), dtype=np.float32)
+    if _load().orc_quantize_q8_act(_ptr(x2), K, batch, _ptr(q), _ptr(d)) != 0:
+        raise ValueError("orc_quantize_q8_act failed")
+    return q, d
+
+
+def gemv_q8_0_q8act(W: np.ndarray, q: np.ndarray, d: np.ndarray, N: int, K: int,
+                    n0: int = 0, n1: int | None = None):
+    """(y64, S) of Q8_0 weights against quantized activations (q, d) for rows
+    [n0, n1): y = sum_j dw dx sum qw qx, S over |products|, fp64."""
+    W = np.ascontiguousarray(W, dtype=np.uint8)
+    q = np.ascontiguousarray(np.atleast_2d(q), dtype=np.int8)
+    d = np.ascontiguousarray(np.atleast_2d(d), dtype=np.float32)
+    batch = q.shape[0]
+    n1 = N if n1 is None else n1
+    y = np.full((batch, N), np.nan, dtype=np.float64)
+    S = np.full((batch, N), np.nan, dtype=np.float64)
+    if _load().orc_gemv_q8_0_q8act(_ptr(W), _ptr(q), _ptr(d), N, K, batch, n0, n1, _ptr(y), _ptr(S)) != 0:
+        raise ValueError("orc_gemv_q8_0_q8act failed")
     return y, S
 
 

@@ -233,6 +233,63 @@ int orc_gemv(int fmt, const uint8_t *W, const float *x, int64_t N, int64_t K,
     return 0;
 }
 
+/* ----------------------------------------- int8-quantized activations ---
+ * dotLLM PR #320, the CPU Q8_0 kernel work (GemmQ8_0 with pre-quantized
+ * input): the activation row is itself quantized to Q8_0 form before the
+ * integer dot product.  Per run of 32 activations: d = max|x| / 127 (fp32);
+ * q = x / d (fp32 division) rounded to the nearest integer, halves away from
+ * zero; a run of zeros has d = 0 and q = 0.  K must be a multiple of 32. */
+int orc_quantize_q8_act(const float *x, int64_t K, int batch, int8_t *q, float *d) {
+    if (K <= 0 || K % 32 != 0 || batch < 1) return -1;
+    for (int64_t r = 0; r < (int64_t)batch * (K / 32); r++) {
+        const float *xr = x + 32 * r;
+        float amax = 0.0f;
+        for (int i = 0; i < 32; i++) {
+            float a = fabsf(xr[i]);
+            if (a > amax) amax = a;
+        }
+        float dr = amax / 127.0f;
+        d[r] = dr;
+        for (int i = 0; i < 32; i++) {
+            float v = dr > 0.0f ? roundf(xr[i] / dr) : 0.0f;
+            q[32 * r + i] = (int8_t)v;
+        }
+    }
+    return 0;
+}
+
+/* Q8_0 weights against int8-quantized activations (from orc_quantize_q8_act):
+ * y64[b*N + n] = sum over 32-runs j of dw[n][j] * dx[b][j] * sum_i qw * qx,
+ * S[b*N + n] the same with every product's absolute value, both in fp64, for
+ * rows [n0, n1).  Returns 0, or -1 on a bad shape. */
+int orc_gemv_q8_0_q8act(const uint8_t *W, const int8_t *qx, const float *dx, int64_t N, int64_t K,
+                        int batch, int64_t n0, int64_t n1, double *y64, double *S) {
+    const int64_t rb = orc_row_bytes(ORC_Q8_0, K);
+    if (rb == 0 || batch < 1 || n0 < 0 || n1 < n0 || n1 > N) return -1;
+    const int64_t nb = K / 32;
+    for (int64_t n = n0; n < n1; n++) {
+        const uint8_t *row = W + n * rb;
+        for (int b = 0; b < batch; b++) {
+            double acc = 0.0, acc_abs = 0.0;
+            for (int64_t j = 0; j < nb; j++) {
+                const uint8_t *blk = row + 34 * j;
+                const double dw = (double)orc_f16_to_f32(rd_u16(blk));
+                const double dxj = (double)dx[(int64_t)b * nb + j];
+                const int8_t *qw = (const int8_t *)(blk + 2);
+                const int8_t *qa = qx + ((int64_t)b * nb + j) * 32;
+                for (int i = 0; i < 32; i++) {
+                    const double p = dw * dxj * (double)qw[i] * (double)qa[i];
+                    acc += p;
+                    acc_abs += fabs(p);
+                }
+            }
+            if (y64) y64[(int64_t)b * N + n] = acc;
+            if (S) S[(int64_t)b * N + n] = acc_abs;
+        }
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------- RMS-norm ---
  * larql Gemma 3 table, "Input RMS-norm": standard RMS-norm with the weight
  * offset baked into the stored weight, so the weight multiplies directly.

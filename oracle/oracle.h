@@ -61,6 +61,17 @@ int orc_dequant_rows(int fmt, const uint8_t *W, int64_t K, int64_t n0,
 int orc_gemv(int fmt, const uint8_t *W, const float *x, int64_t N, int64_t K,
              int batch, int64_t n0, int64_t n1, double *y64, double *S);
 
+/* Activations quantized to Q8_0 form per run of 32 (dotLLM's pre-quantized
+ * input for its Q8_0 GEMM): d = max|x| / 127 in fp32, q = round(x / d) with
+ * halves away from zero (fp32 division), zeros for an all-zero run.
+ * q: int8 [batch][K], d: fp32 [batch][K/32].  Returns 0 or -1 (K % 32). */
+int orc_quantize_q8_act(const float *x, int64_t K, int batch, int8_t *q, float *d);
+
+/* Q8_0 weights against quantized activations: y64 = sum_j dw * dx * sum q*q,
+ * S = the same over |products|, fp64, rows [n0, n1).  Returns 0 or -1. */
+int orc_gemv_q8_0_q8act(const uint8_t *W, const int8_t *qx, const float *dx, int64_t N, int64_t K,
+                        int batch, int64_t n0, int64_t n1, double *y64, double *S);
+
 /* RMS-norm in fp64: out[b*K + k] = x[b*K+k] * w[k] / sqrt(mean_k(x^2) + eps).
  * The weight multiplies directly (any "1 + w" offset is already in w). */
 void orc_rmsnorm(const float *x, const float *w, int64_t K, int batch,

@@ -411,3 +411,58 @@ def test_gemm_bf16_m1_reduces_to_gemv_on_bf16_weights():
     xb = (X.astype(np.uint32) << 16).view(np.float32)
     exact = [sum(float(a) * float(b) for a, b in zip(wb[n], xb[0])) for n in range(N)]
     np.testing.assert_allclose(Y[0], exact, rtol=1e-12)
+
+
+# ------------------------------------------- int8-quantized activations ---
+# dotLLM PR #320 (CPU Q8_0 kernels: GemmQ8_0 on pre-quantized input).  Pins of
+# the quantizer: worked values, exact power-of-two scaling, sign symmetry and
+# range; of the Q8_0 x int8 GEMV: an independent numpy float64 evaluation from
+# the raw bytes, and closeness to the unquantized GEMV.
+
+def test_q8_act_quantizer_worked_values():
+    x = np.zeros((1, 64), np.float32)
+    x[0, :6] = [127.0, -63.5, 2.5, -2.5, 0.4, -0.5]
+    q, d = oracle.quantize_q8_act(x)
+    assert d[0, 0] == np.float32(1.0) and d[0, 1] == 0.0          # amax 127 -> d 1; zero run -> d 0
+    assert list(q[0, :6]) == [127, -64, 3, -3, 0, -1]              # halves away from zero
+    assert not q[0, 32:].any()
+
+
+def test_q8_act_quantizer_scaling_sign_and_range():
+    x = synth.normal((3, 256), 0x5EED, tensor_id=201)
+    q, d = oracle.quantize_q8_act(x)
+    for k in (-7, 3):                                              # x * 2^k: same q, d * 2^k exactly
+        q2, d2 = oracle.quantize_q8_act((x * np.float32(2.0 ** k)).astype(np.float32))
+        assert np.array_equal(q2, q) and np.array_equal(d2, d * np.float32(2.0 ** k))
+    qn, dn = oracle.quantize_q8_act(-x)
+    assert np.array_equal(qn, -q) and np.array_equal(dn, d)
+    assert np.abs(q).max() <= 127
+    assert (np.abs(q).reshape(3, 8, 32).max(axis=2) == 127).all()  # every run reaches the full range
+    # each value is within half a step of its quantized value
+    err = np.abs(x.reshape(3, 8, 32) - q.reshape(3, 8, 32) * d[:, :, None])
+    assert (err <= 0.5 * d[:, :, None] * (1 + 1e-6)).all()
+
+
+def test_q8_act_gemv_against_numpy_from_bytes():
+    N, K = 5, 96
+    W = synth.quant_weights("q8_0", N, K, 0x5EED, tensor_id=202)
+    x = synth.normal((2, K), 0x5EED, tensor_id=203)
+    q, d = oracle.quantize_q8_act(x)
+    y, S = oracle.gemv_q8_0_q8act(W, q, d, N, K)
+    blocks = W.reshape(N, K // 32, 34)
+    dw = blocks[:, :, :2].copy().view(np.float16)[:, :, 0].astype(np.float64)   # numpy's f16 decode
+    qw = blocks[:, :, 2:].view(np.int8).astype(np.float64)
+    qx = q.reshape(2, K // 32, 32).astype(np.float64)
+    prod = dw[None, :, :, None] * d.astype(np.float64)[:, None, :, None] * qw[None] * qx[:, None]
+    assert np.allclose(y, prod.sum(axis=(2, 3)), rtol=1e-13, atol=0)
+    assert np.allclose(S, np.abs(prod).sum(axis=(2, 3)), rtol=1e-13, atol=0)
+
+
+def test_q8_act_gemv_close_to_exact_gemv():
+    N, K = 64, 2560
+    W = synth.quant_weights("q8_0", N, K, 0x5EED, tensor_id=204)
+    x = synth.normal((1, K), 0x5EED, tensor_id=205)
+    q, d = oracle.quantize_q8_act(x)
+    yq, _ = oracle.gemv_q8_0_q8act(W, q, d, N, K)
+    y, S = oracle.gemv("q8_0", W, x, N, K)
+    assert (np.abs(yq - y) <= 5e-2 * S + 1e-6).all()
