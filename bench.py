@@ -49,7 +49,7 @@ def parse():
                             "gemma4_ffn_b8", "gemma4_prefill", "gemma3_qkv", "gemma3_qkv_q8_0",
                             "moe_decode", "q4k_512x512",
                             "lm_head_q4k",
-                            "lm_head_q8_0", "down_q6k", "gate_up_q4k", "copy"])
+                            "lm_head_q8_0", "lm_head_q8_0_q8act", "down_q6k", "gate_up_q4k", "copy"])
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="approximate CPU time budget of the oracle baseline (0 = skip)")
     p.add_argument("--seed", type=int, default=0x5EED)
@@ -173,7 +173,7 @@ class Workload:
             self.nw = t(synth.normal((hidden,), seed, tensor_id=65, mean=1.0, std=0.1))
             self.qkv_out = [torch.empty((1, n), device=dev) for n in (2048, 1024, 1024)]
             base = {k: t(v) for k, v in mats.items()}
-        elif name in ("lm_head_q4k", "lm_head_q8_0"):
+        elif name in ("lm_head_q4k", "lm_head_q8_0", "lm_head_q8_0_q8act"):
             fmt = "q4_k" if name == "lm_head_q4k" else "q8_0"
             self.fmt = fmt
             W = synth.quant_weights(fmt, 262144, 2560, seed, tensor_id=10)
@@ -215,6 +215,8 @@ class Workload:
             return "qgemv_q4k", self.weight_bytes + 4 * (512 + 512)
         if n == "moe_decode":
             return "qmoe_ffn_decode", self.weight_bytes + 4 * (3 * self.hidden + 2 * self.n_sel * self.ff)
+        if n == "lm_head_q8_0_q8act":
+            return "qgemv_q8_0_q8act", self.weight_bytes + 4 * (2560 + 262144)
         if n.startswith("lm_head"):
             return "qgemv", self.weight_bytes + 4 * (2560 + 262144)
         return "copy", 2 * self.weight_bytes
@@ -236,6 +238,8 @@ class Workload:
                 qd.qgemv_q6k(c["down"], self.h, self.y)
         elif n == "down_q6k":
             qd.qgemv_q6k(c["down"], self.hin, self.y)
+        elif n == "lm_head_q8_0_q8act":
+            qd.qgemv_q8_0_q8act(c["W"], self.x, self.y)
         elif n.startswith("lm_head"):
             qd.qgemv(self.fmt, c["W"], self.x, self.y)
         elif n.startswith("gemma3_qkv"):
@@ -271,6 +275,8 @@ def _dominant(self):
         qd.qffn_gate_up_act("q4_k", c["gate"], c["up"], self.x, self.nw, 1e-6, "gelu_tanh", h=self.h)
     elif n == "down_q6k":
         qd.qgemv_q6k(c["down"], self.hin, self.y)
+    elif n == "lm_head_q8_0_q8act":
+        qd.qgemv_q8_0_q8act(c["W"], self.x, self.y)
     elif n.startswith("lm_head"):
         qd.qgemv(self.fmt, c["W"], self.x, self.y)
     elif n.startswith("gemma3_qkv"):

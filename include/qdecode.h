@@ -140,6 +140,30 @@ qd_status qgemv(qd_format fmt, const void *W, const float *x, float *y,
                 int64_t N, int64_t K, int batch, void *stream);
 
 /*
+ * y = Q8_0 W times x quantized to int8  (opt-in; a different result from
+ * qgemv_q8_0)
+ *
+ * dotLLM PR #320's CPU Q8_0 GEMM runs on pre-quantized input: the activation
+ * row is quantized to Q8_0 form and multiplied with integer dot products.
+ * Here each run of 32 activations gets d = max|x| / 127 and
+ * q = round(x / d) (fp32 division, halves away from zero; zeros for an
+ * all-zero run), and
+ *   y[b][n] = sum_j dw[n][j] * d[b][j] * sum_i qw[n][32j+i] * q[b][32j+i].
+ *
+ *   W, N, K, batch   as qgemv_q8_0 (K a multiple of 32; x finite)
+ *   x                fp32 [batch][K], 16-byte aligned
+ *   y                fp32 [batch][N]
+ * Accuracy: within 1e-4 * sum |dw d qw q| + 1e-6 of that quantized sum
+ * computed exactly; against the fp32 qgemv_q8_0 it differs by the
+ * activation rounding, within 5e-2 * sum|w x| for N(0,1)-like activations.
+ * Errors: as qgemv; QD_EUNSUPPORTED when one quantized activation row (K
+ * bytes plus K/8 bytes of scales) does not fit one workgroup's 63 KB of LDS,
+ * i.e. K > 57344.
+ */
+qd_status qgemv_q8_0_q8act(const void *W, const float *x, float *y, int64_t N, int64_t K,
+                          int batch, void *stream);
+
+/*
  * y = W x + r  (GEMV with the residual add fused into its epilogue)
  *
  * The decoder's residual stream: larql's Gemma 3 table follows the O

@@ -9,6 +9,7 @@ library is not built, or a tensor is not on the GPU, the call raises.
 Entry points (same names as the C ABI):
     qgemv_q4k, qgemv_q6k, qgemv_q8_0, qgemv        y = W x, batch 1..8
     qgemv_residual                                 y = W x + r (r may be y)
+    qgemv_q8_0_q8act                               Q8_0 GEMV on int8-quantized x (opt-in)
     qqkv_proj                                      q, k, v = Wq xn, Wk xn, Wv xn (one launch)
     qffn_gate_up_act                               h = act(Wg xn) * (Wu xn)
     qffn_decode                                    y = Wd h (whole FFN, one launch)
@@ -53,6 +54,7 @@ SIGNATURES = {
     "qgemv_q8_0": (_I, [_P, _P, _P, _I64, _I64, _I, _P]),
     "qgemv": (_I, [_I, _P, _P, _P, _I64, _I64, _I, _P]),
     "qgemv_residual": (_I, [_I, _P, _P, _P, _P, _I64, _I64, _I, _P]),
+    "qgemv_q8_0_q8act": (_I, [_P, _P, _P, _I64, _I64, _I, _P]),
     "qmoe_ffn_decode": (_I, [_I, _P, _P, _I, _P, _I, _P, _P, _I, _P, _P, _F, _I, _P, _P, _I64, _I64,
                              _P]),
     "qffn_decode_residual": (_I, [_I, _P, _P, _I, _P, _P, _P, _F, _I, _P, _P, _P, _I64, _I64, _I,
@@ -186,6 +188,20 @@ def qgemv_residual(fmt, W: torch.Tensor, x: torch.Tensor, r: torch.Tensor,
                               _dev(r, "r", torch.float32), _dev(y, "y", torch.float32), N, K, batch,
                               _stream())
     _check("qgemv_residual", st)
+    return y
+
+
+def qgemv_q8_0_q8act(W: torch.Tensor, x: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
+    """y = W q(x): Q8_0 weights against x quantized per 32 to int8 (opt-in;
+    differs from qgemv_q8_0 by the activation rounding)."""
+    K = x.shape[-1]
+    batch = 1 if x.dim() == 1 else x.shape[0]
+    N = _rows(Q8_0, W, K)
+    if y is None:
+        y = torch.empty((N,) if x.dim() == 1 else (batch, N), dtype=torch.float32, device=x.device)
+    st = lib().qgemv_q8_0_q8act(_dev(W, "W", torch.uint8), _dev(x, "x", torch.float32),
+                                _dev(y, "y", torch.float32), N, K, batch, _stream())
+    _check("qgemv_q8_0_q8act", st)
     return y
 
 

@@ -16,7 +16,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libqdecode.so")
 
-SOURCES = ["qd_abi.hip", "qd_gemv.hip", "qd_gemv_stream.hip", "qd_dequant.hip", "qd_prefill.hip"]
+SOURCES = ["qd_abi.hip", "qd_gemv.hip", "qd_gemv_stream.hip", "qd_gemv_i8.hip", "qd_dequant.hip",
+           "qd_prefill.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

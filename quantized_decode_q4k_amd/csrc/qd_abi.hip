@@ -924,6 +924,51 @@ qd_status run_moe(int fmt_gu, const void *Wg, const void *Wu, int fmt_d, const v
     return e == hipSuccess ? QD_OK : QD_ELAUNCH;
 }
 
+// Q8_0 weights against int8-quantized activations (opt-in; dotLLM's CPU
+// Q8_0 GEMM on pre-quantized input).
+// workgroups per CU of the int8-activation GEMV: each quantizes x once and
+// then takes ceil(tiles / grid) row tiles (1 to 16 time the same on the
+// 262144 x 2560 lm_head)
+constexpr int kQ8aWgPerCu = 4;
+
+qd_status run_q8act(const void *W, const float *x, float *y, int64_t N, int64_t K, int batch, void *stream) {
+    qd_status st = check_shape(QD_Q8_0, N, K, batch);
+    if (st != QD_OK) return st;
+    if (!W || !x || !y) return QD_EINVAL;
+    if (!aligned(W, 16) || !aligned(x, 16)) return QD_EALIGN;
+    if (!aligned(y, 4)) return QD_EALIGN;
+    const size_t ybytes = (size_t)batch * N * 4;
+    if (overlap(y, ybytes, x, (size_t)batch * K * 4) || overlap(y, ybytes, W, (size_t)N * row_bytes(QD_Q8_0, K)))
+        return QD_EINVAL;
+    // columns per launch: at most QD_BATCH_CHUNK, and as many as one
+    // workgroup's LDS holds quantized
+    int chunk = std::min(batch, QD_BATCH_CHUNK);
+    while (chunk > 1 && qd::q8act_lds_bytes(chunk, K) > (size_t)qd::kLdsBudgetBytes) chunk--;
+    if (qd::q8act_lds_bytes(chunk, K) > (size_t)qd::kLdsBudgetBytes) return QD_EUNSUPPORTED;
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    const int nsu = (int)((K / 32 + 7) / 8);
+    int p = 1;
+    while (p < 16 && 2 * p <= nsu && (N * p + qd::kGroups - 1) / qd::kGroups < 2 * kCUs) p *= 2;
+    for (int c0 = 0; c0 < batch; c0 += chunk) {
+        const int nb = std::min(chunk, batch - c0);
+        qd::Q8ActArgs a{};
+        a.W = static_cast<const uint8_t *>(W);
+        a.x = x + (int64_t)c0 * K;
+        a.y = y + (int64_t)c0 * N;
+        a.N = N;
+        a.K = K;
+        a.row_bytes = row_bytes(QD_Q8_0, K);
+        a.p = p;
+        a.off_scales = (int)(((size_t)nb * K + 15) & ~(size_t)15);
+        const int64_t rows_wg = qd::kGroups / p;
+        const int64_t tiles = (N + rows_wg - 1) / rows_wg;
+        const unsigned grid = (unsigned)std::min<int64_t>(tiles, (int64_t)kQ8aWgPerCu * kCUs);
+        hipError_t e = qd::launch_q8act(a, nb, grid, hs);
+        if (e != hipSuccess) return QD_ELAUNCH;
+    }
+    return QD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -957,6 +1002,11 @@ qd_status qgemv_residual(qd_format fmt, const void *W, const float *x, const flo
     if (!r) return QD_EINVAL;
     return run_mv(fmt, false, W, nullptr, x, nullptr, 0.f, 0, y, nullptr, nullptr, N, K, batch,
                   stream, 0, r);
+}
+
+qd_status qgemv_q8_0_q8act(const void *W, const float *x, float *y, int64_t N, int64_t K, int batch,
+                          void *stream) {
+    return run_q8act(W, x, y, N, K, batch, stream);
 }
 
 qd_status qgemv_q4k(const void *W, const float *x, float *y, int64_t N, int64_t K, int batch,

@@ -1,0 +1,138 @@
+// qd_gemv_i8.hip -- Q8_0 GEMV on int8-quantized activations (opt-in).
+//
+// What is computed: dotLLM PR #320's CPU Q8_0 path quantizes the activation
+// row to Q8_0 form before an integer dot product (GemmQ8_0 on pre-quantized
+// input).  Here, per run of 32 activations, d = max|x| / 127 and
+// q = round(x / d) (fp32 division, halves away from zero; zeros for an
+// all-zero run), and
+//   y[b][n] = sum over runs j of dw[n][j] * dx[b][j] * sum_i qw[n][32j+i] * qx[b][32j+i],
+// the inner sum an exact int32 from v_dot4_i32_i8 (four int8 products per
+// instruction, so the weights are never converted to float).  This is a
+// different result from the fp32 GEMV (the activations are rounded): it is
+// held to the usual bound against the same quantized computation, and its
+// distance from the fp32 GEMV is a separate, wider tolerance class.
+//
+// Mapping: a workgroup quantizes its activation rows into LDS (int8 values,
+// fp32 scales) once, then takes row tiles strided over the grid; in a tile,
+// lane groups of 4 lanes walk a row's superunits of 8
+// blocks (lane c takes blocks 2c and 2c+1, as the fp32 kernels do, with the
+// same alignment-safe block loads); P lane groups share a row and split its
+// superunits, loading the next superunit before decoding the current one;
+// the 4 * P lanes of a row are summed with cross-lane shuffles.
+#include "qd_decode.h"
+
+namespace qd {
+namespace {
+
+QD_DEV float row_sum(float v, int width) {
+    for (int off = 1; off < width; off <<= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+template <int B>
+__global__ __launch_bounds__(kThreads) void q8act_kernel(Q8ActArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int tid = threadIdx.x;
+    const int64_t K = a.K;
+    const int nblk = (int)(K / 32);
+    int8_t *xq = reinterpret_cast<int8_t *>(smem);                 // [B][K]
+    float *xd = reinterpret_cast<float *>(smem + a.off_scales);    // [B][nblk]
+
+    // ---- quantize the activation rows, one 32-run per thread
+    for (int r = tid; r < B * nblk; r += kThreads) {
+        const float4 *src = reinterpret_cast<const float4 *>(a.x + (int64_t)r * 32);
+        float4 v[8];
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            v[i] = src[i];
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+        }
+        const float d = __fdiv_rn(amax, 127.0f);
+        int4 *dst = reinterpret_cast<int4 *>(xq + (int64_t)r * 32);
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            int w[4];
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const float4 f = v[4 * h + j];
+                const int q0 = d > 0.f ? (int)roundf(__fdiv_rn(f.x, d)) : 0;
+                const int q1 = d > 0.f ? (int)roundf(__fdiv_rn(f.y, d)) : 0;
+                const int q2 = d > 0.f ? (int)roundf(__fdiv_rn(f.z, d)) : 0;
+                const int q3 = d > 0.f ? (int)roundf(__fdiv_rn(f.w, d)) : 0;
+                w[j] = (q0 & 0xFF) | ((q1 & 0xFF) << 8) | ((q2 & 0xFF) << 16) | ((q3 & 0xFF) << 24);
+            }
+            dst[h] = make_int4(w[0], w[1], w[2], w[3]);
+        }
+        xd[r] = d;
+    }
+    __syncthreads();
+
+    // ---- row tiles of kGroups / P rows, strided over the grid (the grid is
+    // sized so that each workgroup's quantization is spent on several tiles);
+    // lane group grp, lane c; P groups per row
+    const int c = tid & 3, grp = tid >> 2;
+    const int P = a.p;
+    const int rows_wg = kGroups / P;
+    const int pi = grp - (grp / P) * P;
+    const int nsu = (nblk + 7) / 8;
+    for (int64_t base = (int64_t)blockIdx.x * rows_wg; base < a.N; base += (int64_t)gridDim.x * rows_wg) {
+        const int64_t row = base + grp / P;
+        float acc[B];
+#pragma unroll
+        for (int b = 0; b < B; b++) acc[b] = 0.f;
+        if (row < a.N) {
+            const uint8_t *rowp = a.W + row * a.row_bytes;
+            RawQ80 cur, nxt;
+            if (pi < nsu) load_q80(cur, rowp, pi, c, nblk);  // blocks past the row decode to zeros, d = 0
+            for (int t = pi; t < nsu; t += P) {
+                if (t + P < nsu) load_q80(nxt, rowp, t + P, c, nblk);  // next superunit in flight
+                const float2 dw = q80_d(cur);
+                const int ja = min(8 * t + 2 * c, nblk - 1), jb = min(8 * t + 2 * c + 1, nblk - 1);
+#pragma unroll
+                for (int b = 0; b < B; b++) {
+                    const int *xa = reinterpret_cast<const int *>(xq + (int64_t)b * K + 32 * ja);
+                    const int *xb = reinterpret_cast<const int *>(xq + (int64_t)b * K + 32 * jb);
+                    int sa = 0, sb = 0;
+#pragma unroll
+                    for (int k = 0; k < 8; k++) {
+                        const uint2 v = q80_qdwords(cur, k);
+                        sa = __builtin_amdgcn_sdot4((int)v.x, xa[k], sa, false);
+                        sb = __builtin_amdgcn_sdot4((int)v.y, xb[k], sb, false);
+                    }
+                    acc[b] = fmaf(dw.x * xd[b * nblk + ja], (float)sa, acc[b]);
+                    acc[b] = fmaf(dw.y * xd[b * nblk + jb], (float)sb, acc[b]);
+                }
+                cur = nxt;
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < B; b++) {
+            const float v = row_sum(acc[b], 4 * P);
+            if (row < a.N && pi == 0 && c == 0) a.y[(int64_t)b * a.N + row] = v;
+        }
+    }
+}
+
+}  // namespace
+
+size_t q8act_lds_bytes(int batch, int64_t K) {
+    const size_t q = ((size_t)batch * (size_t)K + 15) & ~(size_t)15;  // int8 values, then the scales
+    return q + (size_t)batch * (size_t)(K / 32) * 4;
+}
+
+hipError_t launch_q8act(const Q8ActArgs &a, int batch, unsigned grid, hipStream_t st) {
+    const size_t lds = q8act_lds_bytes(batch, a.K);
+#define QD_Q8A(Bv)                                                                        \
+    case Bv:                                                                              \
+        hipLaunchKernelGGL((q8act_kernel<Bv>), dim3(grid), dim3(kThreads), lds, st, a);  \
+        break;
+    switch (batch) {
+        QD_Q8A(1) QD_Q8A(2) QD_Q8A(3) QD_Q8A(4) QD_Q8A(5) QD_Q8A(6) QD_Q8A(7) QD_Q8A(8)
+    default: return hipErrorInvalidValue;
+    }
+#undef QD_Q8A
+    return hipGetLastError();
+}
+
+}  // namespace qd

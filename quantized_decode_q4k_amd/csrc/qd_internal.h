@@ -65,6 +65,18 @@ hipError_t launch_gemv(int fmt, int batch, bool ffn, MvArgs a, Shape s, hipStrea
 // gate/up (ffn) on a (tiles, 1, n_sel) grid, down on (tiles, n_sel).
 hipError_t launch_moe(int fmt, bool ffn, const MvArgs &a, int64_t tiles, int n_sel, hipStream_t st);
 
+// Q8_0 GEMV on int8-quantized activations (qd_gemv_i8.hip).
+struct Q8ActArgs {
+    const uint8_t *W;       // N x K Q8_0
+    const float *x;         // [batch][K], 16-byte aligned
+    float *y;               // [batch][N]
+    int64_t N, K, row_bytes;
+    int p;                  // lane groups per row (1, 2, 4, 8, 16)
+    int off_scales;         // LDS byte offset of the activation scales
+};
+size_t q8act_lds_bytes(int batch, int64_t K);
+hipError_t launch_q8act(const Q8ActArgs &a, int batch, unsigned grid, hipStream_t st);
+
 // Fused Q/K/V projection (qd_gemv.hip): three GEMVs over the same activation
 // rows in one launch.  Workgroups [0, tiles[0]) are row tiles of matrix 0,
 // the next tiles[1] of matrix 1, then tiles[2] of matrix 2; each runs the

@@ -86,6 +86,19 @@ def test_q8_0_accepts_k_multiple_of_32_only_in_validation():
     assert L.qgemv(7, A16, A16b, A16c, 4, 256, 1, None) == 1
 
 
+def test_q8act_validation():
+    _, L = _lib()
+    f = L.qgemv_q8_0_q8act
+    assert f(0, A16b, A16c, 4, 256, 1, None) == 1                    # null W
+    assert f(A16, A16b, A16c, 4, 48, 1, None) == 2                   # K not a multiple of 32
+    assert f(A16, A16b, A16c, 4, 256, 65, None) == 2                 # batch 65
+    assert f(A16, A16b + 4, A16c, 4, 256, 1, None) == 3              # x not 16-byte aligned
+    assert f(A16, A16b, A16c + 2, 4, 256, 1, None) == 3              # y misaligned
+    assert f(A16, A16b, A16b + 512, 4, 256, 1, None) == 1            # y overlaps x
+    big = 0x10000000
+    assert f(A16, big, 2 * big, 4, 57344 + 32, 1, None) == 5         # one quantized row exceeds LDS
+
+
 def test_ffn_validation():
     _, L = _lib()
     f = L.qffn_gate_up_act
