@@ -156,12 +156,45 @@ qd_status qgemv(qd_format fmt, const void *W, const float *x, float *y,
  * Accuracy: within 1e-4 * sum |dw d qw q| + 1e-6 of that quantized sum
  * computed exactly; against the fp32 qgemv_q8_0 it differs by the
  * activation rounding, within 5e-2 * sum|w x| for N(0,1)-like activations.
- * Errors: as qgemv; QD_EUNSUPPORTED when one quantized activation row (K
+ * The activations are quantized into the stream's workspace (as
+ * qquantize_q8_act does), then multiplied as qgemv_q8_0_preq does: two
+ * launches.
+ * Errors: as qgemv, QD_ENOMEM; QD_EUNSUPPORTED when one quantized activation row (K
  * bytes plus K/8 bytes of scales) does not fit one workgroup's 63 KB of LDS,
  * i.e. K > 57344.
  */
 qd_status qgemv_q8_0_q8act(const void *W, const float *x, float *y, int64_t N, int64_t K,
                           int batch, void *stream);
+
+/*
+ * Activations quantized to int8 per run of 32, as qgemv_q8_0_q8act does
+ * before its integer dots (dotLLM PR #320: the CPU Q8_0 GEMM runs on input
+ * quantized once, then reused).  For run j of column b:
+ *   d[b][j] = max|x[b][32j .. 32j+31]| / 127          (fp32, correctly rounded)
+ *   q[b][32j+i] = round(x[b][32j+i] / d[b][j])        (fp32 quotient, halves away
+ *                                                      from zero; 0 when d = 0)
+ *
+ *   x   fp32 [batch][K], 16-byte aligned, finite
+ *   q   int8 [batch][K], 16-byte aligned (out)
+ *   d   fp32 [batch][K / 32], 4-byte aligned (out)
+ *   K   a multiple of 32; batch 1..QD_MAX_BATCH
+ * Errors: QD_EINVAL (null or overlapping buffers), QD_ESHAPE, QD_EALIGN.
+ */
+qd_status qquantize_q8_act(const float *x, int8_t *q, float *d, int64_t K, int batch, void *stream);
+
+/*
+ * y = Q8_0 W times activations already quantized by qquantize_q8_act:
+ *   y[b][n] = sum_j dw[n][j] * d[b][j] * sum_i qw[n][32j+i] * q[b][32j+i]
+ * (dotLLM PR #320: Q8_0 GEMM on pre-quantized input).  One quantization can
+ * serve every projection of the same activations.
+ *
+ *   W, N, K, batch, y  as qgemv_q8_0
+ *   q, d               as qquantize_q8_act writes them (q 16-byte aligned)
+ * Accuracy: within 1e-4 * sum |dw d qw q| + 1e-6 of the exact sum.
+ * Errors: as qgemv_q8_0_q8act.
+ */
+qd_status qgemv_q8_0_preq(const void *W, const int8_t *q, const float *d, float *y, int64_t N,
+                         int64_t K, int batch, void *stream);
 
 /*
  * y = W x + r  (GEMV with the residual add fused into its epilogue)

@@ -10,6 +10,7 @@ Entry points (same names as the C ABI):
     qgemv_q4k, qgemv_q6k, qgemv_q8_0, qgemv        y = W x, batch 1..8
     qgemv_residual                                 y = W x + r (r may be y)
     qgemv_q8_0_q8act                               Q8_0 GEMV on int8-quantized x (opt-in)
+    qquantize_q8_act, qgemv_q8_0_preq              its two halves: quantize once, GEMV on the codes
     qqkv_proj                                      q, k, v = Wq xn, Wk xn, Wv xn (one launch)
     qffn_gate_up_act                               h = act(Wg xn) * (Wu xn)
     qffn_decode                                    y = Wd h (whole FFN, one launch)
@@ -55,6 +56,8 @@ SIGNATURES = {
     "qgemv": (_I, [_I, _P, _P, _P, _I64, _I64, _I, _P]),
     "qgemv_residual": (_I, [_I, _P, _P, _P, _P, _I64, _I64, _I, _P]),
     "qgemv_q8_0_q8act": (_I, [_P, _P, _P, _I64, _I64, _I, _P]),
+    "qquantize_q8_act": (_I, [_P, _P, _P, _I64, _I, _P]),
+    "qgemv_q8_0_preq": (_I, [_P, _P, _P, _P, _I64, _I64, _I, _P]),
     "qmoe_ffn_decode": (_I, [_I, _P, _P, _I, _P, _I, _P, _P, _I, _P, _P, _F, _I, _P, _P, _I64, _I64,
                              _P]),
     "qffn_decode_residual": (_I, [_I, _P, _P, _I, _P, _P, _P, _F, _I, _P, _P, _P, _I64, _I64, _I,
@@ -202,6 +205,34 @@ def qgemv_q8_0_q8act(W: torch.Tensor, x: torch.Tensor, y: torch.Tensor | None = 
     st = lib().qgemv_q8_0_q8act(_dev(W, "W", torch.uint8), _dev(x, "x", torch.float32),
                                 _dev(y, "y", torch.float32), N, K, batch, _stream())
     _check("qgemv_q8_0_q8act", st)
+    return y
+
+
+def qquantize_q8_act(x: torch.Tensor, q: torch.Tensor | None = None, d: torch.Tensor | None = None):
+    """(q int8 [.., K], d fp32 [.., K/32]): x quantized per run of 32."""
+    K = x.shape[-1]
+    batch = 1 if x.dim() == 1 else x.shape[0]
+    lead = () if x.dim() == 1 else (batch,)
+    if q is None:
+        q = torch.empty(lead + (K,), dtype=torch.int8, device=x.device)
+    if d is None:
+        d = torch.empty(lead + (K // 32,), dtype=torch.float32, device=x.device)
+    st = lib().qquantize_q8_act(_dev(x, "x", torch.float32), _dev(q, "q", torch.int8), _dev(d, "d", torch.float32),
+                                K, batch, _stream())
+    _check("qquantize_q8_act", st)
+    return q, d
+
+
+def qgemv_q8_0_preq(W: torch.Tensor, q: torch.Tensor, d: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
+    """y = W (d, q): Q8_0 weights against activations from qquantize_q8_act."""
+    K = q.shape[-1]
+    batch = 1 if q.dim() == 1 else q.shape[0]
+    N = _rows(Q8_0, W, K)
+    if y is None:
+        y = torch.empty((N,) if q.dim() == 1 else (batch, N), dtype=torch.float32, device=q.device)
+    st = lib().qgemv_q8_0_preq(_dev(W, "W", torch.uint8), _dev(q, "q", torch.int8), _dev(d, "d", torch.float32),
+                               _dev(y, "y", torch.float32), N, K, batch, _stream())
+    _check("qgemv_q8_0_preq", st)
     return y
 
 

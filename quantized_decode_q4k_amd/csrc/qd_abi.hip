@@ -931,29 +931,27 @@ qd_status run_moe(int fmt_gu, const void *Wg, const void *Wu, int fmt_d, const v
 // 262144 x 2560 lm_head)
 constexpr int kQ8aWgPerCu = 4;
 
-qd_status run_q8act(const void *W, const float *x, float *y, int64_t N, int64_t K, int batch, void *stream) {
-    qd_status st = check_shape(QD_Q8_0, N, K, batch);
-    if (st != QD_OK) return st;
-    if (!W || !x || !y) return QD_EINVAL;
-    if (!aligned(W, 16) || !aligned(x, 16)) return QD_EALIGN;
-    if (!aligned(y, 4)) return QD_EALIGN;
-    const size_t ybytes = (size_t)batch * N * 4;
-    if (overlap(y, ybytes, x, (size_t)batch * K * 4) || overlap(y, ybytes, W, (size_t)N * row_bytes(QD_Q8_0, K)))
-        return QD_EINVAL;
-    // columns per launch: at most QD_BATCH_CHUNK, and as many as one
-    // workgroup's LDS holds quantized
+// Columns per launch of the int8-activation GEMV: at most QD_BATCH_CHUNK, and
+// as many as one workgroup's LDS holds quantized; 0 if not even one fits.
+int q8act_chunk(int batch, int64_t K) {
     int chunk = std::min(batch, QD_BATCH_CHUNK);
     while (chunk > 1 && qd::q8act_lds_bytes(chunk, K) > (size_t)qd::kLdsBudgetBytes) chunk--;
-    if (qd::q8act_lds_bytes(chunk, K) > (size_t)qd::kLdsBudgetBytes) return QD_EUNSUPPORTED;
-    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    const int nsu = (int)((K / 32 + 7) / 8);
+    return qd::q8act_lds_bytes(chunk, K) > (size_t)qd::kLdsBudgetBytes ? 0 : chunk;
+}
+
+// The GEMV launches on validated codes q [batch][K] and scales d [batch][K/32].
+qd_status launch_q8act_chunks(const void *W, const int8_t *q, const float *d, float *y, int64_t N, int64_t K,
+                              int batch, int chunk, hipStream_t hs) {
+    const int64_t nblk = K / 32;
+    const int nsu = (int)((nblk + 7) / 8);
     int p = 1;
     while (p < 16 && 2 * p <= nsu && (N * p + qd::kGroups - 1) / qd::kGroups < 2 * kCUs) p *= 2;
     for (int c0 = 0; c0 < batch; c0 += chunk) {
         const int nb = std::min(chunk, batch - c0);
         qd::Q8ActArgs a{};
         a.W = static_cast<const uint8_t *>(W);
-        a.x = x + (int64_t)c0 * K;
+        a.q = q + (int64_t)c0 * K;
+        a.d = d + (int64_t)c0 * nblk;
         a.y = y + (int64_t)c0 * N;
         a.N = N;
         a.K = K;
@@ -963,10 +961,59 @@ qd_status run_q8act(const void *W, const float *x, float *y, int64_t N, int64_t 
         const int64_t rows_wg = qd::kGroups / p;
         const int64_t tiles = (N + rows_wg - 1) / rows_wg;
         const unsigned grid = (unsigned)std::min<int64_t>(tiles, (int64_t)kQ8aWgPerCu * kCUs);
-        hipError_t e = qd::launch_q8act(a, nb, grid, hs);
-        if (e != hipSuccess) return QD_ELAUNCH;
+        if (qd::launch_q8act(a, nb, grid, hs) != hipSuccess) return QD_ELAUNCH;
     }
     return QD_OK;
+}
+
+qd_status run_q8quant(const float *x, int8_t *q, float *d, int64_t K, int batch, void *stream) {
+    qd_status st = check_shape(QD_Q8_0, 1, K, batch);
+    if (st != QD_OK) return st;
+    if (!x || !q || !d) return QD_EINVAL;
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(d, 4)) return QD_EALIGN;
+    const size_t xb = (size_t)batch * K * 4, qb = (size_t)batch * K, db = (size_t)batch * (K / 32) * 4;
+    if (overlap(q, qb, x, xb) || overlap(d, db, x, xb) || overlap(q, qb, d, db)) return QD_EINVAL;
+    const hipError_t e = qd::launch_q8quant(x, q, d, (int64_t)batch * (K / 32), reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? QD_OK : QD_ELAUNCH;
+}
+
+qd_status run_q8preq(const void *W, const int8_t *q, const float *d, float *y, int64_t N, int64_t K, int batch,
+                     void *stream) {
+    qd_status st = check_shape(QD_Q8_0, N, K, batch);
+    if (st != QD_OK) return st;
+    if (!W || !q || !d || !y) return QD_EINVAL;
+    if (!aligned(W, 16) || !aligned(q, 16) || !aligned(d, 4) || !aligned(y, 4)) return QD_EALIGN;
+    const size_t yb = (size_t)batch * N * 4;
+    if (overlap(y, yb, q, (size_t)batch * K) || overlap(y, yb, d, (size_t)batch * (K / 32) * 4) ||
+        overlap(y, yb, W, (size_t)N * row_bytes(QD_Q8_0, K)))
+        return QD_EINVAL;
+    const int chunk = q8act_chunk(batch, K);
+    if (chunk == 0) return QD_EUNSUPPORTED;
+    return launch_q8act_chunks(W, q, d, y, N, K, batch, chunk, reinterpret_cast<hipStream_t>(stream));
+}
+
+// Quantize into the stream's workspace, then the GEMV on the codes.
+qd_status run_q8act(const void *W, const float *x, float *y, int64_t N, int64_t K, int batch, void *stream) {
+    qd_status st = check_shape(QD_Q8_0, N, K, batch);
+    if (st != QD_OK) return st;
+    if (!W || !x || !y) return QD_EINVAL;
+    if (!aligned(W, 16) || !aligned(x, 16)) return QD_EALIGN;
+    if (!aligned(y, 4)) return QD_EALIGN;
+    const size_t ybytes = (size_t)batch * N * 4;
+    if (overlap(y, ybytes, x, (size_t)batch * K * 4) || overlap(y, ybytes, W, (size_t)N * row_bytes(QD_Q8_0, K)))
+        return QD_EINVAL;
+    const int chunk = q8act_chunk(batch, K);
+    if (chunk == 0) return QD_EUNSUPPORTED;
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    // codes first (batch * K bytes, rounded up to 256), then the scales
+    const size_t code_floats = (((size_t)batch * K + 255) / 256) * 64;
+    Workspace w;
+    st = get_workspace(hs, code_floats + (size_t)batch * (K / 32), &w);
+    if (st != QD_OK) return st;
+    int8_t *q = reinterpret_cast<int8_t *>(w.partials);
+    float *d = w.partials + code_floats;
+    if (qd::launch_q8quant(x, q, d, (int64_t)batch * (K / 32), hs) != hipSuccess) return QD_ELAUNCH;
+    return launch_q8act_chunks(W, q, d, y, N, K, batch, chunk, hs);
 }
 
 }  // namespace
@@ -1007,6 +1054,15 @@ qd_status qgemv_residual(qd_format fmt, const void *W, const float *x, const flo
 qd_status qgemv_q8_0_q8act(const void *W, const float *x, float *y, int64_t N, int64_t K, int batch,
                           void *stream) {
     return run_q8act(W, x, y, N, K, batch, stream);
+}
+
+qd_status qquantize_q8_act(const float *x, int8_t *q, float *d, int64_t K, int batch, void *stream) {
+    return run_q8quant(x, q, d, K, batch, stream);
+}
+
+qd_status qgemv_q8_0_preq(const void *W, const int8_t *q, const float *d, float *y, int64_t N, int64_t K,
+                          int batch, void *stream) {
+    return run_q8preq(W, q, d, y, N, K, batch, stream);
 }
 
 qd_status qgemv_q4k(const void *W, const float *x, float *y, int64_t N, int64_t K, int batch,

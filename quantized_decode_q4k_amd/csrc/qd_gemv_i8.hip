@@ -12,11 +12,12 @@
 // held to the usual bound against the same quantized computation, and its
 // distance from the fp32 GEMV is a separate, wider tolerance class.
 //
-// Mapping: a workgroup quantizes its activation rows into LDS (int8 values,
-// fp32 scales) once, then takes row tiles strided over the grid; in a tile,
-// lane groups of 4 lanes walk a row's superunits of 8
-// blocks (lane c takes blocks 2c and 2c+1, as the fp32 kernels do, with the
-// same alignment-safe block loads); P lane groups share a row and split its
+// Mapping: q8quant_kernel quantizes x once (8 lanes per run of 32); each
+// GEMV workgroup copies the codes and scales into LDS once, then takes row
+// tiles strided over the grid; in a tile, lane groups of 4 lanes walk a
+// row's superunits of 8 blocks (lane c takes blocks 2c and 2c+1, as the fp32
+// kernels do, with the same alignment-safe block loads); P lane groups share
+// a row and split its
 // superunits, loading the next superunit before decoding the current one;
 // the 4 * P lanes of a row are summed with cross-lane shuffles.
 #include "qd_decode.h"
@@ -29,6 +30,29 @@ QD_DEV float row_sum(float v, int width) {
     return v;
 }
 
+// Quantize x [runs][32] per run: 8 lanes per run, 4 values per lane; the
+// run's max |x| from 3 cross-lane steps, then one correctly rounded fp32
+// division per value and round half away from zero.
+__global__ __launch_bounds__(kThreads) void q8quant_kernel(const float *__restrict__ x, int8_t *__restrict__ q,
+                                                         float *__restrict__ d, int64_t runs) {
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;  // lane i: values 4i .. 4i+3
+    const bool live = i < runs * 8;
+    const float4 v = live ? reinterpret_cast<const float4 *>(x)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    amax = fmaxf(amax, __shfl_xor(amax, 4));  // the 8 lanes of a run are aligned in the wave
+    const float dr = __fdiv_rn(amax, 127.0f);
+    const int q0 = dr > 0.f ? (int)roundf(__fdiv_rn(v.x, dr)) : 0;
+    const int q1 = dr > 0.f ? (int)roundf(__fdiv_rn(v.y, dr)) : 0;
+    const int q2 = dr > 0.f ? (int)roundf(__fdiv_rn(v.z, dr)) : 0;
+    const int q3 = dr > 0.f ? (int)roundf(__fdiv_rn(v.w, dr)) : 0;
+    if (live) {
+        reinterpret_cast<int *>(q)[i] = (q0 & 0xFF) | ((q1 & 0xFF) << 8) | ((q2 & 0xFF) << 16) | ((q3 & 0xFF) << 24);
+        if ((i & 7) == 0) d[i >> 3] = dr;
+    }
+}
+
 template <int B>
 __global__ __launch_bounds__(kThreads) void q8act_kernel(Q8ActArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -38,34 +62,11 @@ __global__ __launch_bounds__(kThreads) void q8act_kernel(Q8ActArgs a) {
     int8_t *xq = reinterpret_cast<int8_t *>(smem);                 // [B][K]
     float *xd = reinterpret_cast<float *>(smem + a.off_scales);    // [B][nblk]
 
-    // ---- quantize the activation rows, one 32-run per thread
-    for (int r = tid; r < B * nblk; r += kThreads) {
-        const float4 *src = reinterpret_cast<const float4 *>(a.x + (int64_t)r * 32);
-        float4 v[8];
-        float amax = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-            v[i] = src[i];
-            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
-        }
-        const float d = __fdiv_rn(amax, 127.0f);
-        int4 *dst = reinterpret_cast<int4 *>(xq + (int64_t)r * 32);
-#pragma unroll
-        for (int h = 0; h < 2; h++) {
-            int w[4];
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const float4 f = v[4 * h + j];
-                const int q0 = d > 0.f ? (int)roundf(__fdiv_rn(f.x, d)) : 0;
-                const int q1 = d > 0.f ? (int)roundf(__fdiv_rn(f.y, d)) : 0;
-                const int q2 = d > 0.f ? (int)roundf(__fdiv_rn(f.z, d)) : 0;
-                const int q3 = d > 0.f ? (int)roundf(__fdiv_rn(f.w, d)) : 0;
-                w[j] = (q0 & 0xFF) | ((q1 & 0xFF) << 8) | ((q2 & 0xFF) << 16) | ((q3 & 0xFF) << 24);
-            }
-            dst[h] = make_int4(w[0], w[1], w[2], w[3]);
-        }
-        xd[r] = d;
-    }
+    // ---- stage the quantized activation columns: int8 codes, then scales
+    const int64_t n16 = (int64_t)B * K / 16;
+    for (int64_t i = tid; i < n16; i += kThreads)
+        reinterpret_cast<int4 *>(xq)[i] = reinterpret_cast<const int4 *>(a.q)[i];
+    for (int i = tid; i < B * nblk; i += kThreads) xd[i] = a.d[i];
     __syncthreads();
 
     // ---- row tiles of kGroups / P rows, strided over the grid (the grid is
@@ -119,6 +120,13 @@ __global__ __launch_bounds__(kThreads) void q8act_kernel(Q8ActArgs a) {
 size_t q8act_lds_bytes(int batch, int64_t K) {
     const size_t q = ((size_t)batch * (size_t)K + 15) & ~(size_t)15;  // int8 values, then the scales
     return q + (size_t)batch * (size_t)(K / 32) * 4;
+}
+
+hipError_t launch_q8quant(const float *x, int8_t *q, float *d, int64_t runs, hipStream_t st) {
+    const int64_t lanes = runs * 8;
+    const unsigned grid = (unsigned)((lanes + kThreads - 1) / kThreads);
+    hipLaunchKernelGGL(q8quant_kernel, dim3(grid), dim3(kThreads), 0, st, x, q, d, runs);
+    return hipGetLastError();
 }
 
 hipError_t launch_q8act(const Q8ActArgs &a, int batch, unsigned grid, hipStream_t st) {

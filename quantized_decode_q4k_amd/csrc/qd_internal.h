@@ -65,10 +65,12 @@ hipError_t launch_gemv(int fmt, int batch, bool ffn, MvArgs a, Shape s, hipStrea
 // gate/up (ffn) on a (tiles, 1, n_sel) grid, down on (tiles, n_sel).
 hipError_t launch_moe(int fmt, bool ffn, const MvArgs &a, int64_t tiles, int n_sel, hipStream_t st);
 
-// Q8_0 GEMV on int8-quantized activations (qd_gemv_i8.hip).
+// Q8_0 GEMV on int8-quantized activations (qd_gemv_i8.hip), and the
+// quantizer (x [runs][32] -> q int8 codes, d fp32 scale per run).
 struct Q8ActArgs {
     const uint8_t *W;       // N x K Q8_0
-    const float *x;         // [batch][K], 16-byte aligned
+    const int8_t *q;        // [batch][K] codes, 16-byte aligned
+    const float *d;         // [batch][K / 32] scales
     float *y;               // [batch][N]
     int64_t N, K, row_bytes;
     int p;                  // lane groups per row (1, 2, 4, 8, 16)
@@ -76,6 +78,7 @@ struct Q8ActArgs {
 };
 size_t q8act_lds_bytes(int batch, int64_t K);
 hipError_t launch_q8act(const Q8ActArgs &a, int batch, unsigned grid, hipStream_t st);
+hipError_t launch_q8quant(const float *x, int8_t *q, float *d, int64_t runs, hipStream_t st);
 
 // Fused Q/K/V projection (qd_gemv.hip): three GEMVs over the same activation
 // rows in one launch.  Workgroups [0, tiles[0]) are row tiles of matrix 0,

@@ -99,6 +99,28 @@ def test_q8act_validation():
     assert f(A16, big, 2 * big, 4, 57344 + 32, 1, None) == 5         # one quantized row exceeds LDS
 
 
+def test_quantize_and_preq_validation():
+    _, L = _lib()
+    f = L.qquantize_q8_act
+    X, Q, D = A16, A16b, A16c
+    assert f(0, Q, D, 256, 1, None) == 1                             # null x
+    assert f(X, Q, 0, 256, 1, None) == 1                             # null d
+    assert f(X, Q, D, 48, 1, None) == 2                              # K not a multiple of 32
+    assert f(X, Q, D, 256, 65, None) == 2                            # batch 65
+    assert f(X, Q + 4, D, 256, 1, None) == 3                         # q not 16-byte aligned
+    assert f(X, Q, D + 2, 256, 1, None) == 3                         # d misaligned
+    assert f(X, X + 512, D, 256, 1, None) == 1                       # q overlaps x
+    assert f(X, Q, Q + 128, 256, 1, None) == 1                       # d overlaps q
+    g = L.qgemv_q8_0_preq
+    Y = 0x40000
+    assert g(A16, Q, D, Y, 4, 256, 0, None) == 2                     # batch 0
+    assert g(A16, Q + 8, D, Y, 4, 256, 1, None) == 3                 # q not 16-byte aligned
+    assert g(A16, Q, D, Q + 64, 4, 256, 1, None) == 1                # y overlaps q
+    assert g(A16, Q, D, D, 4, 256, 1, None) == 1                     # y overlaps d
+    big = 0x10000000
+    assert g(A16, big, 2 * big, 3 * big, 4, 57344 + 32, 1, None) == 5  # one column exceeds LDS
+
+
 def test_ffn_validation():
     _, L = _lib()
     f = L.qffn_gate_up_act

@@ -11,6 +11,9 @@ Two bars, both against the oracle:
   so |y - W x| <= sum_j d_j/2 sum_i |w_ji| + 1e-4 * S_exact + 1e-6 (checked
   with the oracle's dequantized weights), and for N(0,1) activations that
   distance stays below 5e-2 * sum|w x|.
+The two halves are also checked apart: qquantize_q8_act's codes and scales
+must equal the oracle's bit for bit, and qgemv_q8_0_preq, fed the oracle's
+own codes, must meet the bound.
 Shapes: ragged rows, K not a multiple of 256 (ragged superunits), batch 1, 3,
 8 and 11 (two launches), K = 16384 where LDS holds three quantized columns,
 all-zero and half-way activation runs, and the lm_head shape
@@ -119,3 +122,30 @@ def test_q8act_codes_match_fp32_path_on_exact_inputs(qd):
     got = qd.qgemv_q8_0_q8act(dev(W), dev(x)).cpu().numpy().reshape(1, N)
     ye, Se = oracle.gemv("q8_0", W, x, N, K)
     assert_bound("q8act exact inputs vs fp32 GEMV", got, ye, Se)
+
+
+@pytest.mark.parametrize("batch,K", [(1, 2560), (3, 96), (64, 512), (8, 10240), (2, 32)])
+def test_quantize_codes_bit_exact(qd, batch, K):
+    say(f"qquantize_q8_act batch={batch} K={K}")
+    x = synth.normal((batch, K), SEED, tensor_id=200) * np.float32(3.0)
+    x[0, :32] = 0.0                                            # an all-zero run
+    if K >= 96:
+        d = np.float32(2.0 ** -3)
+        x[-1, 64:96] = (np.arange(32, dtype=np.float32) - 15.5) * d   # exact halves
+        x[-1, 95] = 127 * d
+    q_ref, d_ref = oracle.quantize_q8_act(x)
+    q, dd = qd.qquantize_q8_act(dev(x))
+    q, dd = q.cpu().numpy(), dd.cpu().numpy()
+    assert np.array_equal(q, q_ref), f"{np.count_nonzero(q != q_ref)} codes differ"
+    assert np.array_equal(dd.view(np.uint32), d_ref.view(np.uint32)), "scales differ"
+
+
+@pytest.mark.parametrize("N,K,batch", [(300, 2560, 1), (2560, 10240, 8), (77, 96, 3), (100, 16384, 7)])
+def test_preq_gemv_on_oracle_codes(qd, N, K, batch):
+    say(f"qgemv_q8_0_preq {N}x{K} batch={batch}")
+    W = synth.quant_weights("q8_0", N, K, SEED, tensor_id=201)
+    x = synth.normal((batch, K), SEED, tensor_id=202)
+    q, d = oracle.quantize_q8_act(x)
+    y = qd.qgemv_q8_0_preq(dev(W), dev(q), dev(d)).cpu().numpy().reshape(batch, N)
+    y64, S = oracle.gemv_q8_0_q8act(W, q, d, N, K)
+    assert_bound(f"qgemv_q8_0_preq {N}x{K} b{batch}", y, y64, S)
