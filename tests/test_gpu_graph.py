@@ -6,8 +6,8 @@ counters are rewritten in between; a replay that depended on stale workspace
 state, or on a counter left non-zero, would differ.  Each case makes one
 uncaptured call first, so the workspace has its final size before capture.
 Cases: the decode FFN (LDS-streaming kernels, h in the workspace), a split-K
-GEMV, the fused Q/K/V projection, the MoE FFN (split-K over slots) and a
-split-K prefill GEMM.
+GEMV, the fused Q/K/V projection, the MoE FFN (split-K over slots), a
+split-K prefill GEMM, and the int8-activation GEMV (codes in the workspace).
 """
 import numpy as np
 import pytest
@@ -114,3 +114,13 @@ def test_graph_moe_and_prefill(qd):
                       lambda: qd.qgemm_prefill("q6_k", W, X2, Y=Y2))
     finally:
         qd.set_gemm_override(0, 0)
+
+
+def test_graph_int8_activations(qd):
+    say("graph int8-activation gemv")
+    N, K = 513, 2560
+    W = dev(synth.quant_weights("q8_0", N, K, SEED, tensor_id=183))
+    x, x2 = dev(synth.normal((8, K), SEED, tensor_id=184)), dev(synth.normal((8, K), SEED, tensor_id=185))
+    y, y2 = torch.empty((8, N), device="cuda"), torch.empty((8, N), device="cuda")
+    check_replays("qgemv_q8_0_q8act", lambda: qd.qgemv_q8_0_q8act(W, x, y), [y],
+                  lambda: qd.qgemv_q8_0_q8act(W, x2, y2))

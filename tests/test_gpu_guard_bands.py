@@ -5,7 +5,8 @@ sentinel bit for bit (no kernel wrote past its output) and the window must
 hold none (every output element was written).  Each entry point runs through
 the kernels its shapes select: register GEMV with and without split-K,
 LDS-streaming GEMV and fused gate/up, the decode FFN's three forms, fused
-Q/K/V, MoE, prefill GEMMs and the dequantisers.
+Q/K/V, MoE, prefill GEMMs, the dequantisers, and the int8-activation
+quantizer and GEMV.
 """
 import numpy as np
 import pytest
@@ -162,3 +163,22 @@ def test_prefill_and_dequant_guard_bands(qd, fmt, M, N, K):
     qd.qdequant_bf16(fmt, W, K, out=Db.view)
     D.check(f"qdequant {fmt}")
     Db.check(f"qdequant_bf16 {fmt}")
+
+
+@pytest.mark.parametrize("N,K,batch", [(300, 2560, 1), (77, 96, 3), (40, 16384, 5), (64, 512, 11)])
+def test_int8_activation_guard_bands(qd, N, K, batch):
+    say(f"guard int8 activations {N}x{K} batch={batch}")
+    W = dev(synth.quant_weights("q8_0", N, K, SEED, tensor_id=154))
+    x = dev(synth.normal((batch, K), SEED, tensor_id=155))
+    y = Guarded((batch, N))
+    qd.qgemv_q8_0_q8act(W, x, y.view)
+    y.check("qgemv_q8_0_q8act")
+    # codes: an int8 buffer seen as bytes inside a guarded fp32 buffer
+    qb, d = Guarded(((batch * K) // 4,)), Guarded((batch, K // 32))
+    qd.qquantize_q8_act(x, q=qb.view.view(torch.int8).view(batch, K), d=d.view)
+    d.check("qquantize_q8_act d")
+    raw = qb.buf.cpu().numpy().view(np.uint32)
+    assert (raw[:GUARD] == SENT32).all() and (raw[GUARD + qb.n:] == SENT32).all(), "codes written outside q"
+    y2 = Guarded((batch, N))
+    qd.qgemv_q8_0_preq(W, qb.view.view(torch.int8).view(batch, K), d.view, y2.view)
+    y2.check("qgemv_q8_0_preq")
