@@ -410,7 +410,8 @@ qd_status qdequant_bf16(qd_format fmt, const void *W, uint16_t *out,
 
 /*
  * Launch-shape override for tuning sweeps (process-wide; 0 = automatic).
- *   p_in   K-slices interleaved inside one workgroup (1, 2, 4, 8, 16)
+ *   p_in   K-slices interleaved inside one workgroup (1, 2, 4, 8, 16; also
+ *          the lane groups per row of qgemv_q8_0_preq / qgemv_q8_0_q8act)
  *   p_out  K-slices across workgroups (>= 1; > 1 uses the split-K workspace)
  *   nr     rows per lane group for plain GEMV (1 or 2)
  * Returns QD_EINVAL for values outside these sets.

@@ -944,10 +944,20 @@ qd_status launch_q8act_chunks(const void *W, const int8_t *q, const float *d, fl
                               int batch, int chunk, hipStream_t hs) {
     const int64_t nblk = K / 32;
     const int nsu = (int)((nblk + 7) / 8);
-    int p = 1;
-    while (p < 16 && 2 * p <= nsu && (N * p + qd::kGroups - 1) / qd::kGroups < 2 * kCUs) p *= 2;
     for (int c0 = 0; c0 < batch; c0 += chunk) {
         const int nb = std::min(chunk, batch - c0);
+        // lane groups per row.  One column: as many as leave each at least
+        // two superunits (parallelism within the row).  More columns: at
+        // most 4, and at least 8 superunits each, because lane groups of
+        // different rows read the same LDS codes (a broadcast) only when
+        // they walk the same superunit, and each column multiplies those
+        // reads (sweep over the Gemma-3/4 and lm_head shapes, batch 1-8).
+        int p = 1;
+        if (nb == 1)
+            while (p < 16 && 4 * p <= nsu) p *= 2;
+        else
+            while (p < 4 && 16 * p <= nsu) p *= 2;
+        if (g_over_pin.load() != 0) p = g_over_pin.load();  // tuning override
         qd::Q8ActArgs a{};
         a.W = static_cast<const uint8_t *>(W);
         a.q = q + (int64_t)c0 * K;
