@@ -6,8 +6,10 @@
  *
  * Cases: a Q4_K GEMV (512 x 512, batch 1), a Q6_K GEMV through the
  * LDS-streaming kernel (256 x 8192, batch 2), the whole decode FFN with the
- * residual added in place (hidden 512, FF 1024), and a rejected call that
- * must return QD_ESHAPE without enqueuing anything.  Built by
+ * residual added in place (hidden 512, FF 1024), activations quantized to
+ * int8 (codes and scales equal to the oracle's bit for bit) and the Q8_0
+ * GEMV on them (300 x 2560, batch 3), and a rejected call that must return
+ * QD_ESHAPE without enqueuing anything.  Built by
  * __graft_entry__.build() into tests/c_abi_example.bin (gcc, host code
  * only); run by tests/test_gpu_c_abi.py.  Prints one "ok" line and exits 0.
  */
@@ -58,6 +60,15 @@ static void fill_q6k(uint8_t *W, int64_t nblk) {
         for (int k = 192; k < 208; k++) b[k] = (uint8_t)(int8_t)((int)(next_u32() % 128) - 64);
         const uint16_t d = f16_bits(1e-4f + 9e-4f * unit());
         memcpy(b + 208, &d, 2);
+    }
+}
+
+static void fill_q80(uint8_t *W, int64_t nblk) {
+    for (int64_t i = 0; i < nblk; i++) {
+        uint8_t *b = W + 34 * i;
+        const uint16_t d = f16_bits(1e-3f + 9e-3f * unit());
+        memcpy(b, &d, 2);
+        for (int k = 2; k < 34; k++) b[k] = (uint8_t)(int8_t)((int)(next_u32() % 255) - 127);
     }
 }
 
@@ -158,12 +169,49 @@ static void ffn_case(hipStream_t s) {
     free(Wg); free(Wu); free(Wd);
 }
 
+static void int8_case(hipStream_t s) {
+    const int64_t N = 300, K = 2560;
+    const int batch = 3;
+    const int64_t rb = qd_row_bytes(QD_Q8_0, K), nq = batch * K, nd = batch * (K / 32);
+    uint8_t *W = malloc((size_t)(N * rb));
+    float *x = malloc(sizeof(float) * (size_t)nq), *y = malloc(sizeof(float) * (size_t)(batch * N));
+    float *d = malloc(sizeof(float) * (size_t)nd), *d_ref = malloc(sizeof(float) * (size_t)nd);
+    int8_t *q = malloc((size_t)nq), *q_ref = malloc((size_t)nq);
+    double *y64 = malloc(sizeof(double) * (size_t)(batch * N)), *S = malloc(sizeof(double) * (size_t)(batch * N));
+    fill_q80(W, N * K / 32);
+    for (int64_t i = 0; i < nq; i++) x[i] = normalish();
+    for (int i = 0; i < 32; i++) x[K + i] = 0.0f; /* an all-zero run */
+    void *dW = to_device(W, (size_t)(N * rb));
+    float *dx = to_device(x, sizeof(float) * (size_t)nq), *dd = NULL, *dy = NULL;
+    int8_t *dq = NULL;
+    CHECK_HIP(hipMalloc((void **)&dq, (size_t)nq));
+    CHECK_HIP(hipMalloc((void **)&dd, sizeof(float) * (size_t)nd));
+    CHECK_HIP(hipMalloc((void **)&dy, sizeof(float) * (size_t)(batch * N)));
+    CHECK_QD(qquantize_q8_act(dx, dq, dd, K, batch, s));
+    CHECK_QD(qgemv_q8_0_preq(dW, dq, dd, dy, N, K, batch, s));
+    CHECK_HIP(hipStreamSynchronize(s));
+    CHECK_HIP(hipMemcpy(q, dq, (size_t)nq, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(d, dd, sizeof(float) * (size_t)nd, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(y, dy, sizeof(float) * (size_t)(batch * N), hipMemcpyDeviceToHost));
+    if (orc_quantize_q8_act(x, K, batch, q_ref, d_ref) != 0) failures++;
+    if (memcmp(q, q_ref, (size_t)nq) != 0 || memcmp(d, d_ref, sizeof(float) * (size_t)nd) != 0) {
+        fprintf(stderr, "qquantize_q8_act: codes or scales differ from the oracle\n");
+        failures++;
+    }
+    if (orc_gemv_q8_0_q8act(W, q_ref, d_ref, N, K, batch, 0, N, y64, S) != 0) failures++;
+    within("qgemv_q8_0_preq", y, y64, S, batch * N);
+    CHECK_HIP(hipFree(dW)); CHECK_HIP(hipFree(dx)); CHECK_HIP(hipFree(dq));
+    CHECK_HIP(hipFree(dd)); CHECK_HIP(hipFree(dy));
+    free(W); free(x); free(y); free(d); free(d_ref); free(q); free(q_ref); free(y64); free(S);
+}
+
 int main(void) {
     hipStream_t s;
     CHECK_HIP(hipStreamCreate(&s));
     gemv_case(QD_Q4_K, 512, 512, 1, s);
     gemv_case(QD_Q6_K, 256, 8192, 2, s);
     ffn_case(s);
+    int8_case(s);
     /* a rejected call: K not a multiple of 256 */
     if (qgemv_q4k((void *)0x10000, (const float *)0x20000, (float *)0x30000, 4, 100, 1, s) != QD_ESHAPE)
         failures++;
