@@ -931,33 +931,75 @@ qd_status run_moe(int fmt_gu, const void *Wg, const void *Wu, int fmt_d, const v
 // 262144 x 2560 lm_head)
 constexpr int kQ8aWgPerCu = 4;
 
-// Columns per launch of the int8-activation GEMV: at most QD_BATCH_CHUNK, and
-// as many as one workgroup's LDS holds quantized; 0 if not even one fits.
-int q8act_chunk(int batch, int64_t K) {
+// Launch plan of the int8-activation GEMV.
+struct Q8Plan {
+    int p = 1;        // lane groups per row
+    int ks = 1;       // K-slices across workgroups
+    int su_per = 0;   // superunits per slice
+    int chunk = 0;    // columns per launch (0: one column's slice does not fit LDS)
+    int64_t tiles = 0;
+};
+
+Q8Plan q8act_plan(int64_t N, int64_t K, int batch) {
+    const int nsu = (int)((K / 32 + 7) / 8);
+    Q8Plan pl;
+    // lane groups per row.  One column: as many as leave each at least two
+    // superunits (parallelism within the row).  More columns: at most 4, and
+    // at least 8 superunits each, because lane groups of different rows read
+    // the same LDS codes (a broadcast) only when they walk the same
+    // superunit, and each column multiplies those reads (sweep over the
+    // Gemma-3/4 and lm_head shapes, batch 1-8).
+    if (batch == 1)
+        while (pl.p < 16 && 4 * pl.p <= nsu) pl.p *= 2;
+    else
+        while (pl.p < 4 && 16 * pl.p <= nsu) pl.p *= 2;
+    // Several columns on a matrix with few row tiles: split K across
+    // workgroups instead (one lane group per row, up to 8 slices of at least
+    // two superunits, aiming at 1024 workgroups), so each stages only its
+    // slice of the codes.  Gemma-3 down at batch 8: 53 -> 23 us; Gemma-4
+    // down 141 -> 47 us; Gemma-3 gate 24 -> 19 us.  One column gains nothing.
+    if (batch > 1) {
+        const int64_t tiles1 = (N + qd::kGroups - 1) / qd::kGroups;
+        const int64_t want = (1024 + tiles1 - 1) / tiles1;
+        const int ks = (int)std::min<int64_t>(std::min<int64_t>(8, nsu / 2), want);
+        if (ks > 1) {
+            pl.p = 1;
+            pl.ks = ks;
+        }
+    }
+    if (g_over_pin.load() != 0) pl.p = g_over_pin.load();  // tuning overrides
+    if (g_over_pout.load() != 0) pl.ks = g_over_pout.load();
+    const int64_t rows_wg = qd::kGroups / pl.p;
+    pl.tiles = (N + rows_wg - 1) / rows_wg;
+    pl.ks = std::min(pl.ks, nsu);
+    pl.su_per = (nsu + pl.ks - 1) / pl.ks;
+    pl.ks = (nsu + pl.su_per - 1) / pl.su_per;  // every slice non-empty
+    if (pl.ks > 1 && pl.tiles > kMaxTiles) {
+        pl.ks = 1;
+        pl.su_per = nsu;
+    }
+    // columns per launch: at most QD_BATCH_CHUNK, and as many as one
+    // workgroup's LDS holds quantized (its K-slice of each)
+    const int64_t kslice = std::min<int64_t>(K, (int64_t)pl.su_per * qd::kSuper);
     int chunk = std::min(batch, QD_BATCH_CHUNK);
-    while (chunk > 1 && qd::q8act_lds_bytes(chunk, K) > (size_t)qd::kLdsBudgetBytes) chunk--;
-    return qd::q8act_lds_bytes(chunk, K) > (size_t)qd::kLdsBudgetBytes ? 0 : chunk;
+    while (chunk > 1 && qd::q8act_lds_bytes(chunk, kslice) > (size_t)qd::kLdsBudgetBytes) chunk--;
+    pl.chunk = qd::q8act_lds_bytes(chunk, kslice) > (size_t)qd::kLdsBudgetBytes ? 0 : chunk;
+    return pl;
+}
+
+// Partial-sum floats the plan needs in the workspace.
+size_t q8act_partial_floats(const Q8Plan &pl, int64_t N) {
+    return pl.ks > 1 ? (size_t)pl.ks * (size_t)pl.chunk * (size_t)N : 0;
 }
 
 // The GEMV launches on validated codes q [batch][K] and scales d [batch][K/32].
-qd_status launch_q8act_chunks(const void *W, const int8_t *q, const float *d, float *y, int64_t N, int64_t K,
-                              int batch, int chunk, hipStream_t hs) {
+qd_status launch_q8act_chunks(const Q8Plan &pl, const void *W, const int8_t *q, const float *d, float *y,
+                              int64_t N, int64_t K, int batch, float *partials, unsigned *counters,
+                              hipStream_t hs) {
     const int64_t nblk = K / 32;
-    const int nsu = (int)((nblk + 7) / 8);
-    for (int c0 = 0; c0 < batch; c0 += chunk) {
-        const int nb = std::min(chunk, batch - c0);
-        // lane groups per row.  One column: as many as leave each at least
-        // two superunits (parallelism within the row).  More columns: at
-        // most 4, and at least 8 superunits each, because lane groups of
-        // different rows read the same LDS codes (a broadcast) only when
-        // they walk the same superunit, and each column multiplies those
-        // reads (sweep over the Gemma-3/4 and lm_head shapes, batch 1-8).
-        int p = 1;
-        if (nb == 1)
-            while (p < 16 && 4 * p <= nsu) p *= 2;
-        else
-            while (p < 4 && 16 * p <= nsu) p *= 2;
-        if (g_over_pin.load() != 0) p = g_over_pin.load();  // tuning override
+    const int64_t kslice = std::min<int64_t>(K, (int64_t)pl.su_per * qd::kSuper);
+    for (int c0 = 0; c0 < batch; c0 += pl.chunk) {
+        const int nb = std::min(pl.chunk, batch - c0);
         qd::Q8ActArgs a{};
         a.W = static_cast<const uint8_t *>(W);
         a.q = q + (int64_t)c0 * K;
@@ -966,11 +1008,16 @@ qd_status launch_q8act_chunks(const void *W, const int8_t *q, const float *d, fl
         a.N = N;
         a.K = K;
         a.row_bytes = row_bytes(QD_Q8_0, K);
-        a.p = p;
-        a.off_scales = (int)(((size_t)nb * K + 15) & ~(size_t)15);
-        const int64_t rows_wg = qd::kGroups / p;
-        const int64_t tiles = (N + rows_wg - 1) / rows_wg;
-        const unsigned grid = (unsigned)std::min<int64_t>(tiles, (int64_t)kQ8aWgPerCu * kCUs);
+        a.p = pl.p;
+        a.off_scales = (int)(((size_t)nb * kslice + 15) & ~(size_t)15);
+        a.ks = pl.ks;
+        a.su_per = pl.su_per;
+        a.partials = partials;
+        a.counters = counters;
+        // split K: one row tile per workgroup; else a grid that strides over
+        // the tiles, each workgroup staging the codes once
+        const unsigned grid = (unsigned)(pl.ks > 1 ? pl.tiles
+                                                   : std::min<int64_t>(pl.tiles, (int64_t)kQ8aWgPerCu * kCUs));
         if (qd::launch_q8act(a, nb, grid, hs) != hipSuccess) return QD_ELAUNCH;
     }
     return QD_OK;
@@ -997,9 +1044,19 @@ qd_status run_q8preq(const void *W, const int8_t *q, const float *d, float *y, i
     if (overlap(y, yb, q, (size_t)batch * K) || overlap(y, yb, d, (size_t)batch * (K / 32) * 4) ||
         overlap(y, yb, W, (size_t)N * row_bytes(QD_Q8_0, K)))
         return QD_EINVAL;
-    const int chunk = q8act_chunk(batch, K);
-    if (chunk == 0) return QD_EUNSUPPORTED;
-    return launch_q8act_chunks(W, q, d, y, N, K, batch, chunk, reinterpret_cast<hipStream_t>(stream));
+    const Q8Plan pl = q8act_plan(N, K, batch);
+    if (pl.chunk == 0) return QD_EUNSUPPORTED;
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    float *partials = nullptr;
+    unsigned *counters = nullptr;
+    if (pl.ks > 1) {
+        Workspace w;
+        st = get_workspace(hs, q8act_partial_floats(pl, N), &w);
+        if (st != QD_OK) return st;
+        partials = w.partials;
+        counters = w.counters + kCtlSlots;
+    }
+    return launch_q8act_chunks(pl, W, q, d, y, N, K, batch, partials, counters, hs);
 }
 
 // Quantize into the stream's workspace, then the GEMV on the codes.
@@ -1012,18 +1069,21 @@ qd_status run_q8act(const void *W, const float *x, float *y, int64_t N, int64_t 
     const size_t ybytes = (size_t)batch * N * 4;
     if (overlap(y, ybytes, x, (size_t)batch * K * 4) || overlap(y, ybytes, W, (size_t)N * row_bytes(QD_Q8_0, K)))
         return QD_EINVAL;
-    const int chunk = q8act_chunk(batch, K);
-    if (chunk == 0) return QD_EUNSUPPORTED;
+    const Q8Plan pl = q8act_plan(N, K, batch);
+    if (pl.chunk == 0) return QD_EUNSUPPORTED;
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    // codes first (batch * K bytes, rounded up to 256), then the scales
+    // codes first (batch * K bytes, rounded up to 256), then the scales,
+    // then the split-K partial sums
     const size_t code_floats = (((size_t)batch * K + 255) / 256) * 64;
+    const size_t scale_floats = (((size_t)batch * (K / 32) + 63) / 64) * 64;
     Workspace w;
-    st = get_workspace(hs, code_floats + (size_t)batch * (K / 32), &w);
+    st = get_workspace(hs, code_floats + scale_floats + q8act_partial_floats(pl, N), &w);
     if (st != QD_OK) return st;
     int8_t *q = reinterpret_cast<int8_t *>(w.partials);
     float *d = w.partials + code_floats;
     if (qd::launch_q8quant(x, q, d, (int64_t)batch * (K / 32), hs) != hipSuccess) return QD_ELAUNCH;
-    return launch_q8act_chunks(W, q, d, y, N, K, batch, chunk, hs);
+    return launch_q8act_chunks(pl, W, q, d, y, N, K, batch, w.partials + code_floats + scale_floats,
+                               w.counters + kCtlSlots, hs);
 }
 
 }  // namespace

@@ -59,14 +59,27 @@ __global__ __launch_bounds__(kThreads) void q8act_kernel(Q8ActArgs a) {
     const int tid = threadIdx.x;
     const int64_t K = a.K;
     const int nblk = (int)(K / 32);
-    int8_t *xq = reinterpret_cast<int8_t *>(smem);                 // [B][K]
-    float *xd = reinterpret_cast<float *>(smem + a.off_scales);    // [B][nblk]
+    const int nsu = (nblk + 7) / 8;
+    // K-slice kz of the row: superunits [su0, su1), activations [kb0, kb0 + klen)
+    const int kz = blockIdx.y;
+    const int su0 = kz * a.su_per, su1 = min(nsu, su0 + a.su_per);
+    const int64_t kb0 = (int64_t)su0 * kSuper;
+    const int64_t klen = min(K, (int64_t)su1 * kSuper) - kb0;  // a multiple of 32
+    const int nbl = (int)(klen / 32);
+    int8_t *xq = reinterpret_cast<int8_t *>(smem);                 // [B][klen]
+    float *xd = reinterpret_cast<float *>(smem + a.off_scales);    // [B][nbl]
 
-    // ---- stage the quantized activation columns: int8 codes, then scales
-    const int64_t n16 = (int64_t)B * K / 16;
-    for (int64_t i = tid; i < n16; i += kThreads)
-        reinterpret_cast<int4 *>(xq)[i] = reinterpret_cast<const int4 *>(a.q)[i];
-    for (int i = tid; i < B * nblk; i += kThreads) xd[i] = a.d[i];
+    // ---- stage this slice of the quantized activation columns
+    const int n16 = (int)(klen / 16);
+    for (int i = tid; i < B * n16; i += kThreads) {
+        const int b = i / n16, j = i - b * n16;
+        reinterpret_cast<int4 *>(xq + (int64_t)b * klen)[j] =
+            reinterpret_cast<const int4 *>(a.q + (int64_t)b * K + kb0)[j];
+    }
+    for (int i = tid; i < B * nbl; i += kThreads) {
+        const int b = i / nbl;
+        xd[i] = a.d[(int64_t)b * nblk + 8 * su0 + (i - b * nbl)];
+    }
     __syncthreads();
 
     // ---- row tiles of kGroups / P rows, strided over the grid (the grid is
@@ -76,7 +89,6 @@ __global__ __launch_bounds__(kThreads) void q8act_kernel(Q8ActArgs a) {
     const int P = a.p;
     const int rows_wg = kGroups / P;
     const int pi = grp - (grp / P) * P;
-    const int nsu = (nblk + 7) / 8;
     for (int64_t base = (int64_t)blockIdx.x * rows_wg; base < a.N; base += (int64_t)gridDim.x * rows_wg) {
         const int64_t row = base + grp / P;
         float acc[B];
@@ -85,15 +97,17 @@ __global__ __launch_bounds__(kThreads) void q8act_kernel(Q8ActArgs a) {
         if (row < a.N) {
             const uint8_t *rowp = a.W + row * a.row_bytes;
             RawQ80 cur, nxt;
-            if (pi < nsu) load_q80(cur, rowp, pi, c, nblk);  // blocks past the row decode to zeros, d = 0
-            for (int t = pi; t < nsu; t += P) {
-                if (t + P < nsu) load_q80(nxt, rowp, t + P, c, nblk);  // next superunit in flight
+            if (su0 + pi < su1) load_q80(cur, rowp, su0 + pi, c, nblk);  // blocks past the row: zeros, d = 0
+            for (int t = su0 + pi; t < su1; t += P) {
+                if (t + P < su1) load_q80(nxt, rowp, t + P, c, nblk);  // next superunit in flight
                 const float2 dw = q80_d(cur);
-                const int ja = min(8 * t + 2 * c, nblk - 1), jb = min(8 * t + 2 * c + 1, nblk - 1);
+                // slice-local block indexes (clamped blocks carry d = 0)
+                const int ja = min(8 * t + 2 * c, nblk - 1) - 8 * su0;
+                const int jb = min(8 * t + 2 * c + 1, nblk - 1) - 8 * su0;
 #pragma unroll
                 for (int b = 0; b < B; b++) {
-                    const int *xa = reinterpret_cast<const int *>(xq + (int64_t)b * K + 32 * ja);
-                    const int *xb = reinterpret_cast<const int *>(xq + (int64_t)b * K + 32 * jb);
+                    const int *xa = reinterpret_cast<const int *>(xq + (int64_t)b * klen + 32 * ja);
+                    const int *xb = reinterpret_cast<const int *>(xq + (int64_t)b * klen + 32 * jb);
                     int sa = 0, sb = 0;
 #pragma unroll
                     for (int k = 0; k < 8; k++) {
@@ -101,8 +115,8 @@ __global__ __launch_bounds__(kThreads) void q8act_kernel(Q8ActArgs a) {
                         sa = __builtin_amdgcn_sdot4((int)v.x, xa[k], sa, false);
                         sb = __builtin_amdgcn_sdot4((int)v.y, xb[k], sb, false);
                     }
-                    acc[b] = fmaf(dw.x * xd[b * nblk + ja], (float)sa, acc[b]);
-                    acc[b] = fmaf(dw.y * xd[b * nblk + jb], (float)sb, acc[b]);
+                    acc[b] = fmaf(dw.x * xd[b * nbl + ja], (float)sa, acc[b]);
+                    acc[b] = fmaf(dw.y * xd[b * nbl + jb], (float)sb, acc[b]);
                 }
                 cur = nxt;
             }
@@ -110,9 +124,44 @@ __global__ __launch_bounds__(kThreads) void q8act_kernel(Q8ActArgs a) {
 #pragma unroll
         for (int b = 0; b < B; b++) {
             const float v = row_sum(acc[b], 4 * P);
-            if (row < a.N && pi == 0 && c == 0) a.y[(int64_t)b * a.N + row] = v;
+            if (row < a.N && pi == 0 && c == 0) {
+                if (a.ks == 1)
+                    a.y[(int64_t)b * a.N + row] = v;
+                else  // device-scope store: visible to the last workgroup of the tile
+                    __hip_atomic_store(a.partials + ((int64_t)kz * B + b) * a.N + row, v, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
     }
+    if (a.ks == 1) return;
+
+    // ---- K split across workgroups (one row tile per workgroup): the last
+    // of the tile's ks workgroups sums the partials in slice order.  Every
+    // wave's partial stores complete before the workgroup bumps the counter.
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    __shared__ int s_last;
+    if (tid == 0) {
+        const unsigned prev = __hip_atomic_fetch_add(a.counters + blockIdx.x, 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        s_last = prev == (unsigned)a.ks - 1 ? 1 : 0;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    const int64_t tile0 = (int64_t)blockIdx.x * rows_wg;
+    for (int e = tid; e < rows_wg * B; e += kThreads) {
+        const int b = e / rows_wg;
+        const int64_t r = tile0 + (e - b * rows_wg);
+        if (r >= a.N) continue;
+        float s0 = 0.f;
+        for (int k = 0; k < a.ks; k++)
+            s0 += __hip_atomic_load(a.partials + ((int64_t)k * B + b) * a.N + r, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+        a.y[(int64_t)b * a.N + r] = s0;
+    }
+    if (tid == 0)  // ready for the next launch
+        __hip_atomic_store(a.counters + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
@@ -130,10 +179,10 @@ hipError_t launch_q8quant(const float *x, int8_t *q, float *d, int64_t runs, hip
 }
 
 hipError_t launch_q8act(const Q8ActArgs &a, int batch, unsigned grid, hipStream_t st) {
-    const size_t lds = q8act_lds_bytes(batch, a.K);
+    const size_t lds = q8act_lds_bytes(batch, std::min<int64_t>(a.K, (int64_t)a.su_per * kSuper));
 #define QD_Q8A(Bv)                                                                        \
     case Bv:                                                                              \
-        hipLaunchKernelGGL((q8act_kernel<Bv>), dim3(grid), dim3(kThreads), lds, st, a);  \
+        hipLaunchKernelGGL((q8act_kernel<Bv>), dim3(grid, a.ks), dim3(kThreads), lds, st, a);  \
         break;
     switch (batch) {
         QD_Q8A(1) QD_Q8A(2) QD_Q8A(3) QD_Q8A(4) QD_Q8A(5) QD_Q8A(6) QD_Q8A(7) QD_Q8A(8)

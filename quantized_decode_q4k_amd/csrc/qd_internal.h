@@ -75,6 +75,9 @@ struct Q8ActArgs {
     int64_t N, K, row_bytes;
     int p;                  // lane groups per row (1, 2, 4, 8, 16)
     int off_scales;         // LDS byte offset of the activation scales
+    int ks, su_per;         // K-slices across workgroups (grid.y) and superunits per slice
+    float *partials;        // ks > 1: [ks][batch][N] partial sums
+    unsigned *counters;     // ks > 1: one per row tile, zero between launches
 };
 size_t q8act_lds_bytes(int batch, int64_t K);
 hipError_t launch_q8act(const Q8ActArgs &a, int batch, unsigned grid, hipStream_t st);

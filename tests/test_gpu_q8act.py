@@ -13,7 +13,9 @@ Two bars, both against the oracle:
   distance stays below 5e-2 * sum|w x|.
 The two halves are also checked apart: qquantize_q8_act's codes and scales
 must equal the oracle's bit for bit, and qgemv_q8_0_preq, fed the oracle's
-own codes, must meet the bound.
+own codes, must meet the bound, with K unsplit and split across workgroups
+(forced slice counts, ragged last slices, the per-tile counters reused by
+consecutive calls).
 Shapes: ragged rows, K not a multiple of 256 (ragged superunits), batch 1, 3,
 8 and 11 (two launches), K = 16384 where LDS holds three quantized columns,
 all-zero and half-way activation runs, and the lm_head shape
@@ -35,7 +37,8 @@ SEED = 0x5EED
 def qd(gpu):
     import quantized_decode_q4k_amd as qd
     qd.lib()
-    return qd
+    yield qd
+    qd.set_launch_override(0, 0, 0)
 
 
 from helpers import assert_bound, dev, say  # noqa: E402
@@ -149,3 +152,26 @@ def test_preq_gemv_on_oracle_codes(qd, N, K, batch):
     y = qd.qgemv_q8_0_preq(dev(W), dev(q), dev(d)).cpu().numpy().reshape(batch, N)
     y64, S = oracle.gemv_q8_0_q8act(W, q, d, N, K)
     assert_bound(f"qgemv_q8_0_preq {N}x{K} b{batch}", y, y64, S)
+
+
+@pytest.mark.parametrize("N,K,batch,p,ks", [
+    (513, 1056, 8, 2, 3),     # 5 superunits in slices of 2, 2, 1 (the last ragged)
+    (300, 10240, 4, 1, 8),    # 40 superunits, 8 slices of 5
+    (77, 2560, 1, 4, 2),      # one column, split
+    (2560, 10240, 8, 1, 7),   # 7 slices of 6, 6, ..., 4
+    (130, 5376, 3, 1, 21),    # 21 superunits, one per slice
+])
+def test_preq_split_k(qd, N, K, batch, p, ks):
+    say(f"qgemv_q8_0_preq split {N}x{K} batch={batch} p={p} ks={ks}")
+    W = synth.quant_weights("q8_0", N, K, SEED, tensor_id=203)
+    x = synth.normal((batch, K), SEED, tensor_id=204)
+    q, d = oracle.quantize_q8_act(x)
+    y64, S = oracle.gemv_q8_0_q8act(W, q, d, N, K)
+    Wd, qd_, dd = dev(W), dev(q), dev(d)
+    qd.set_launch_override(p, ks, 0)
+    try:
+        for rep in range(2):  # the tile counters must be back at zero for the second call
+            y = qd.qgemv_q8_0_preq(Wd, qd_, dd).cpu().numpy().reshape(batch, N)
+            assert_bound(f"preq split {N}x{K} b{batch} p{p} ks{ks} call {rep}", y, y64, S)
+    finally:
+        qd.set_launch_override(0, 0, 0)
