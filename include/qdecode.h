@@ -186,7 +186,10 @@ qd_status qquantize_q8_act(const float *x, int8_t *q, float *d, int64_t K, int b
  * y = Q8_0 W times activations already quantized by qquantize_q8_act:
  *   y[b][n] = sum_j dw[n][j] * d[b][j] * sum_i qw[n][32j+i] * q[b][32j+i]
  * (dotLLM PR #320: Q8_0 GEMM on pre-quantized input).  One quantization can
- * serve every projection of the same activations.
+ * serve every projection of the same activations.  At batch > 1 on a
+ * matrix with few row tiles the sum over K is split across workgroups, with
+ * partial sums in the stream's workspace (allocated on first need, as the
+ * other split-K calls do); the result is deterministic either way.
  *
  *   W, N, K, batch, y  as qgemv_q8_0
  *   q, d               as qquantize_q8_act writes them (q 16-byte aligned)

@@ -17,9 +17,12 @@
 // tiles strided over the grid; in a tile, lane groups of 4 lanes walk a
 // row's superunits of 8 blocks (lane c takes blocks 2c and 2c+1, as the fp32
 // kernels do, with the same alignment-safe block loads); P lane groups share
-// a row and split its
-// superunits, loading the next superunit before decoding the current one;
-// the 4 * P lanes of a row are summed with cross-lane shuffles.
+// a row and split its superunits, loading the next superunit before decoding
+// the current one;
+// the 4 * P lanes of a row are summed with cross-lane shuffles.  With K split
+// across workgroups (grid.y slices), a workgroup stages only its slice of the
+// codes and takes one row tile; the last of a tile's workgroups to finish sums
+// the partials in slice order.
 #include "qd_decode.h"
 
 namespace qd {
@@ -82,8 +85,8 @@ __global__ __launch_bounds__(kThreads) void q8act_kernel(Q8ActArgs a) {
     }
     __syncthreads();
 
-    // ---- row tiles of kGroups / P rows, strided over the grid (the grid is
-    // sized so that each workgroup's quantization is spent on several tiles);
+    // ---- row tiles of kGroups / P rows, strided over the grid (unsplit, the
+    // grid is sized so that each workgroup's staging serves several tiles);
     // lane group grp, lane c; P groups per row
     const int c = tid & 3, grp = tid >> 2;
     const int P = a.p;
