@@ -159,9 +159,10 @@ qd_status qgemv(qd_format fmt, const void *W, const float *x, float *y,
  * The activations are quantized into the stream's workspace (as
  * qquantize_q8_act does), then multiplied as qgemv_q8_0_preq does: two
  * launches.
- * Errors: as qgemv, QD_ENOMEM; QD_EUNSUPPORTED when one quantized activation row (K
- * bytes plus K/8 bytes of scales) does not fit one workgroup's 63 KB of LDS,
- * i.e. K > 57344.
+ * Errors: as qgemv, QD_ENOMEM; QD_EUNSUPPORTED when the codes one
+ * workgroup stages for one column (its K-slice: K bytes plus K/8 bytes of
+ * scales when K is not split, as at batch 1) do not fit its 63 KB of LDS,
+ * i.e. K > 57344 unsplit.
  */
 qd_status qgemv_q8_0_q8act(const void *W, const float *x, float *y, int64_t N, int64_t K,
                           int batch, void *stream);
