@@ -160,9 +160,9 @@ qd_status qgemv(qd_format fmt, const void *W, const float *x, float *y,
  * qquantize_q8_act does), then multiplied as qgemv_q8_0_preq does: two
  * launches.
  * Errors: as qgemv, QD_ENOMEM; QD_EUNSUPPORTED when the codes one
- * workgroup stages for one column (its K-slice: K bytes plus K/8 bytes of
- * scales when K is not split, as at batch 1) do not fit its 63 KB of LDS,
- * i.e. K > 57344 unsplit.
+ * workgroup stages for one column (its K-slice, K/ks bytes plus scales) do
+ * not fit its 63 KB of LDS and K cannot be split (more than 65536 row tiles:
+ * K > 57344 with N above about 262144).
  */
 qd_status qgemv_q8_0_q8act(const void *W, const float *x, float *y, int64_t N, int64_t K,
                           int batch, void *stream);

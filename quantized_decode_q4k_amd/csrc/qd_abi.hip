@@ -978,6 +978,15 @@ Q8Plan q8act_plan(int64_t N, int64_t K, int batch) {
         pl.ks = 1;
         pl.su_per = nsu;
     }
+    // a column whose codes do not fit one workgroup's LDS: split K until one
+    // slice does (when the row tiles can carry counters)
+    while (qd::q8act_lds_bytes(1, std::min<int64_t>(K, (int64_t)pl.su_per * qd::kSuper)) >
+               (size_t)qd::kLdsBudgetBytes &&
+           pl.su_per > 1 && pl.tiles <= kMaxTiles) {
+        pl.ks++;
+        pl.su_per = (nsu + pl.ks - 1) / pl.ks;
+        pl.ks = (nsu + pl.su_per - 1) / pl.su_per;
+    }
     // columns per launch: at most QD_BATCH_CHUNK, and as many as one
     // workgroup's LDS holds quantized (its K-slice of each)
     const int64_t kslice = std::min<int64_t>(K, (int64_t)pl.su_per * qd::kSuper);

@@ -95,8 +95,9 @@ def test_q8act_validation():
     assert f(A16, A16b + 4, A16c, 4, 256, 1, None) == 3              # x not 16-byte aligned
     assert f(A16, A16b, A16c + 2, 4, 256, 1, None) == 3              # y misaligned
     assert f(A16, A16b, A16b + 512, 4, 256, 1, None) == 1            # y overlaps x
-    big = 0x10000000
-    assert f(A16, big, 2 * big, 4, 57344 + 32, 1, None) == 5         # one quantized row exceeds LDS
+    big = 0x800000000  # past the 18 GB weight matrix of this shape
+    # a quantized row beyond LDS that cannot be split (more than 65536 row tiles)
+    assert f(A16, big, big + 0x100000000, 300000, 57344 + 32, 1, None) == 5
 
 
 def test_quantize_and_preq_validation():
@@ -117,8 +118,8 @@ def test_quantize_and_preq_validation():
     assert g(A16, Q + 8, D, Y, 4, 256, 1, None) == 3                 # q not 16-byte aligned
     assert g(A16, Q, D, Q + 64, 4, 256, 1, None) == 1                # y overlaps q
     assert g(A16, Q, D, D, 4, 256, 1, None) == 1                     # y overlaps d
-    big = 0x10000000
-    assert g(A16, big, 2 * big, 3 * big, 4, 57344 + 32, 1, None) == 5  # one column exceeds LDS
+    big = 0x800000000  # past the 18 GB weight matrix of this shape
+    assert g(A16, big, big + 0x100000000, big + 0x200000000, 300000, 57344 + 32, 1, None) == 5  # cannot split
 
 
 def test_ffn_validation():

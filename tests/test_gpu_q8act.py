@@ -66,6 +66,7 @@ def check(name, W, x, got, N, K, n0=0, n1=None):
     (513, 1056, 8),      # 33 blocks: ragged last superunit, batch 8
     (64, 512, 11),       # two launches of 8 + 3 columns
     (40, 16384, 5),      # LDS holds 3 columns: launches of 3 + 2
+    (70, 65536, 1),      # one column beyond LDS: K split until a slice fits
 ])
 def test_q8act_parity(qd, N, K, batch):
     say(f"q8act {N}x{K} batch={batch}")
