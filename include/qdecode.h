@@ -52,18 +52,21 @@
  *   - Alignment: weight pointers 16-byte aligned; fp32 and bf16 activation
  *     pointers 16-byte aligned; output pointers 4-byte aligned.
  *   - Outputs must not overlap inputs.
- *   - Threads: calls may be made from any host thread.  Split-K launches use
- *     a small per-(device, stream) workspace allocated on first use; calls on
- *     the same stream are ordered by the stream, so they never share it
- *     concurrently.
- *   - HIP graphs: a call captured into a graph keeps the address of the
- *     workspace it used, and a later call on the same stream that needs a
- *     larger workspace replaces it (after synchronising the stream) and frees
- *     the old one.  Make one uncaptured call of each shape before capturing
- *     (the workspace then has its final size), and do not make larger calls
- *     on that stream while the graph is in use.  Counters in the workspace
- *     return to zero at the end of every kernel that uses them, so replays
- *     need no reset.
+ *   - Threads: calls may be made from any host thread.  Calls that keep
+ *     partial sums or counters between kernels (split-K launches, h of the
+ *     decode FFN, the int8 activation codes, row epilogues) use a
+ *     per-(device, stream) workspace that the library allocates on first
+ *     need and grows when a larger call needs more; calls on the same stream
+ *     are ordered by the stream, so they never share it concurrently.
+ *   - HIP graphs: a call made while its stream is being captured never
+ *     allocates and never enqueues a memory set: if its workspace would
+ *     have to be created or grown, it returns QD_ECAPTURE, enqueues
+ *     nothing, and the capture stays valid.  Make one uncaptured call of
+ *     each shape on the stream first (the workspace then has its size).  A
+ *     workspace that is outgrown later stays allocated until the process
+ *     ends, so graphs captured with it stay valid.  Counters in the
+ *     workspace return to zero at the end of every kernel that uses them, so
+ *     replays need no reset.
  */
 #ifndef QDECODE_H
 #define QDECODE_H
@@ -82,7 +85,9 @@ typedef enum qd_status {
     QD_EALIGN = 3,       /* pointer not aligned as required */
     QD_ELAUNCH = 4,      /* the HIP runtime refused the launch */
     QD_EUNSUPPORTED = 5, /* valid arguments the library has no kernel for */
-    QD_ENOMEM = 6        /* workspace allocation failed */
+    QD_ENOMEM = 6,       /* workspace allocation failed */
+    QD_ECAPTURE = 7      /* the stream is capturing and the call would have to
+                            create or grow its workspace (nothing enqueued) */
 } qd_status;
 
 typedef enum qd_format { QD_Q4_K = 0, QD_Q6_K = 1, QD_Q8_0 = 2 } qd_format;
@@ -123,10 +128,11 @@ int qd_version(void);
  *   y      fp32 [batch][N], row-major; y[b][n] = sum_k w[n][k] * x[b][k]
  *
  * Accuracy: |y - y_exact| <= 1e-4 * sum_k |w[n][k] x[b][k]| + 1e-6, where w
- * is the exactly dequantised weight.  For Q4_K the kernel applies the scale
- * and the min per 32-weight sub-block (sum of q*x and sum of x); the bound
- * holds whenever the two terms do not cancel to a row whose every weight is
- * zero while scale and min are not.
+ * is the exactly dequantised weight.  Every weight is formed in fp32 with
+ * one rounding (Q4_K: d*scale*q - dmin*min as one fused multiply-add;
+ * Q6_K and Q8_0 products are exact) before it meets its activation, so the
+ * bound holds on every block, including blocks whose scale and min terms
+ * cancel.
  */
 qd_status qgemv_q4k(const void *W, const float *x, float *y, int64_t N,
                     int64_t K, int batch, void *stream);
@@ -221,6 +227,42 @@ qd_status qgemv_residual(qd_format fmt, const void *W, const float *x, const flo
                          int64_t N, int64_t K, int batch, void *stream);
 
 /*
+ * y = r + RMSNorm(W x; post_w),  y2 = RMSNorm(y; next_w)   (GEMV with the
+ * post-norm, residual and next-norm epilogue)
+ *
+ * The post-norm pipeline of the larql Gemma 3 table ("has_post_norms", four
+ * norms per layer): after the O projection, post_attn_residual_norm_store
+ * applies the post-attention RMS-norm to the projection, adds the residual,
+ * applies the FFN input norm to the sum and stores both; after the down
+ * projection, post_ffn_norm_residual_add applies the post-FFN RMS-norm and
+ * adds the residual (the next layer's input).  Per batch column b:
+ *   p      = W x[b]                                 (the GEMV)
+ *   y[b]   = r[b] + p * post_w / sqrt(mean(p^2) + eps)
+ *   y2[b]  = y[b] * next_w / sqrt(mean(y[b]^2) + eps)   (only with next_w)
+ * The norm of p needs the whole output row: every workgroup stores its
+ * rows of p in the stream's workspace, and the last workgroup to finish
+ * (a release / acquire counter) forms y and y2 with sums in a fixed order.
+ *
+ *   fmt, W, x, N, K, batch   as qgemv
+ *   post_w  fp32 [N] post-norm weight, multiplied directly (the page's
+ *           "weight offset baked into stored weight")
+ *   eps     added to the mean square inside each square root
+ *   r       fp32 [batch][N] residual; may be y itself (in place), must not
+ *           otherwise overlap y or y2
+ *   y       fp32 [batch][N]
+ *   next_w  fp32 [N] or NULL; y2 fp32 [batch][N] or NULL (both or neither)
+ * Accuracy: p meets the GEMV bound; y and y2 carry that error through the
+ * norm (relative error of 1/rms at most
+ * sum_n (2|p_n| e_n + e_n^2) / (2 sum_n p_n^2 + 2 N eps) for per-element GEMV
+ * errors e_n) plus a few fp32 roundings.
+ * Errors: as qgemv; QD_EINVAL for a NULL post_w or r, next_w without y2 (or
+ * the reverse), overlapping buffers; QD_ENOMEM, QD_ECAPTURE (workspace).
+ */
+qd_status qgemv_post_norm_residual(qd_format fmt, const void *W, const float *x, const float *post_w,
+                                   float eps, const float *r, float *y, const float *next_w, float *y2,
+                                   int64_t N, int64_t K, int batch, void *stream);
+
+/*
  * q = Wq xn,  k = Wk xn,  v = Wv xn,  xn = RMSNorm(x) if norm_w != NULL else x
  *
  * The attention input projections of one decoder layer in one launch: the
@@ -280,13 +322,7 @@ qd_status qffn_gate_up_act(qd_format fmt, const void *Wg, const void *Wu,
  *
  * The whole decode FFN of one layer (larql Gemma 3 table: input norm ->
  * q4k_ffn_gate_up_8sg -> geglu -> q6k_matvec), as qffn_gate_up_act followed
- * by qgemv on the same stream, with h kept in the library's workspace.  Two
- * single-launch forms exist: with qd_set_ffn_mode(2), at batch 1 when K and
- * N_ff are multiples of 256 and both matrices whole numbers of 16-byte
- * chunks, one workgroup per CU runs the gate/up phase, writes h, meets the
- * others at a grid barrier and runs the down phase (its weights stream in
- * during the gate/up phase); with qd_set_ffn_override, down-projection
- * workgroups wait for their slice of h.
+ * by qgemv on the same stream, with h kept in the library's workspace.
  *
  *   fmt_gu, Wg, Wu   gate and up, N_ff x K
  *   fmt_down, Wd     down, K x N_ff
@@ -295,13 +331,8 @@ qd_status qffn_gate_up_act(qd_format fmt, const void *Wg, const void *Wu,
  *   h_out            optional fp32 [batch][N_ff] copy of h (NULL = kept in
  *                    the library's workspace), 16-byte aligned
  * Accuracy: h as in qffn_gate_up_act; y meets the GEMV bound for the h it
- * was computed from.  The older single launch exists for Q4_K gate/up with
- * Q6_K or Q4_K down and for Q8_0 throughout, when batch * K fits one
- * workgroup's LDS.  The grid-barrier form needs every workgroup of its grid
- * resident at once (one per CU); its barrier wait is bounded, so on a device
- * shared with other work it returns wrong values rather than hanging -- use
- * it only on an otherwise idle device.
- * Calls that overlap on one stream's workspace race (h and the barrier).
+ * was computed from.
+ * Errors: as qffn_gate_up_act and qgemv, QD_ENOMEM, QD_ECAPTURE.
  */
 qd_status qffn_decode(qd_format fmt_gu, const void *Wg, const void *Wu, qd_format fmt_down,
                       const void *Wd, const float *x, const float *norm_w, float eps, qd_act act,
@@ -321,6 +352,23 @@ qd_status qffn_decode_residual(qd_format fmt_gu, const void *Wg, const void *Wu,
                                const float *norm_w, float eps, qd_act act, const float *r,
                                float *y, float *h_out, int64_t N_ff, int64_t K, int batch,
                                void *stream);
+
+/*
+ * y = r + RMSNorm(Wd h; post_w),  y2 = RMSNorm(y; next_w),
+ * h = act(Wg xn) * (Wu xn)   (qffn_decode with the post_ffn_norm_residual_add
+ * epilogue of the larql Gemma 3 table on the down projection)
+ *
+ * Arguments as qffn_decode, plus post_w, r, next_w and y2 as in
+ * qgemv_post_norm_residual (r, y, y2 are [batch][K]); eps serves the input
+ * norm and both post norms.  In the Gemma 3 pipeline x is already
+ * normalised by the previous call's next_w, so norm_w is NULL there.
+ * Errors: as qffn_decode and qgemv_post_norm_residual.
+ */
+qd_status qffn_decode_post_norm_residual(qd_format fmt_gu, const void *Wg, const void *Wu,
+                                         qd_format fmt_down, const void *Wd, const float *x,
+                                         const float *norm_w, float eps, qd_act act, const float *post_w,
+                                         const float *r, float *y, const float *next_w, float *y2,
+                                         float *h_out, int64_t N_ff, int64_t K, int batch, void *stream);
 
 /*
  * y = sum_z coef[z] * Wd[e_z] h_z,  h_z = act(Wg[e_z] xn) * (Wu[e_z] xn),
@@ -404,8 +452,15 @@ qd_status qgemm_prefill_gate_up_act(qd_format fmt, const void *Wg,
 
 /*
  * out = dequantised W, fp32 [N][K] (exact: the single rounding of the real
- * value of each weight), or its round-to-nearest-even bf16 bits.  Used by
- * tests to check the in-kernel decoders bit for bit.
+ * value of each weight), or its round-to-nearest-even bf16 bits.  dotLLM PR
+ * #320's CPU kernels have the same operation for one row
+ * (DequantizeRowToF32); here it serves the tests, which check the
+ * in-kernel decoders bit for bit against the oracle.
+ *   W    N x K quantized matrix, device, 16-byte aligned
+ *   out  fp32 [N][K] (4-byte aligned) or bf16 bits [N][K] (2-byte aligned),
+ *        device, must not overlap W
+ * Errors: QD_ESHAPE, QD_EINVAL (null pointer, unknown format, overlap),
+ * QD_EALIGN, QD_ELAUNCH.
  */
 qd_status qdequant(qd_format fmt, const void *W, float *out, int64_t N,
                    int64_t K, void *stream);
@@ -431,20 +486,6 @@ qd_status qd_set_launch_override(int p_in, int p_out, int nr);
 qd_status qd_set_walk_override(int rows_per_group);
 
 /*
- * Selects qffn_decode's single launch (any non-zero value; all zero = the
- * two launches) and its launch shape (0 = automatic):
- * p_in of the gate/up tiles, p_in and K-slices of the down tiles.
- */
-qd_status qd_set_ffn_override(int p_in_a, int p_in_b, int p_out_b);
-
-/*
- * qffn_decode's form (process-wide): 0 = automatic (the two launches),
- * 1 = the two launches, 2 = the one launch with a grid barrier where the
- * shape allows it (else the two launches).  QD_EINVAL otherwise.
- */
-qd_status qd_set_ffn_mode(int mode);
-
-/*
  * Tile override of the prefill GEMMs (0 = automatic): tm = 2 or 4 (tokens
  * per workgroup / 32), splits = K-splits across workgroups (1..1024; more
  * than the K-tiles of 128 weights is clamped).
@@ -454,18 +495,24 @@ qd_status qd_set_gemm_override(int tm, int splits);
 /*
  * Shape override of the streaming GEMV path (process-wide; 0 = automatic).
  *   wg_per_cu  workgroups per CU (1..8; LDS is divided between them)
- *   depth      steps of 16 superunits in flight: per wave for the kernel in
- *              which every wave copies and decodes (2..8), per copying wave
- *              for the producer / consumer kernel (1..32, capped by what its
- *              ring and wait counter allow)
- *   consumers  1 = every wave copies and decodes; 4 or 8 = that many
- *              decoding waves beside the copying waves and one staging x
- *   producers  copying waves of the producer / consumer kernel (1, 2 or 4;
- *              0 = automatic); must be 0 unless consumers is 4 or 8
+ *   depth      steps of 16 superunits in flight per copying wave (1..32,
+ *              capped by what the ring and the wait counter allow)
+ *   consumers  decoding waves beside the copying waves (4 or 8; 0 = 8)
+ *   producers  copying waves (1, 2 or 4; 0 = automatic)
  * A non-zero wg_per_cu forces the streaming path where the shape allows it.
  * Returns QD_EINVAL for values outside these sets.
  */
 qd_status qd_set_stream_override(int wg_per_cu, int depth, int consumers, int producers);
+
+/*
+ * Launch plan qgemv_q8_0_preq / qgemv_q8_0_q8act would use for this shape,
+ * computed on the host without any HIP call (tests and tuning):
+ *   out[0] lane groups per row, out[1] K-slices across workgroups,
+ *   out[2] superunits (256 weights) per slice, out[3] columns per launch
+ *   (0 = the shape is not supported: QD_EUNSUPPORTED from those calls).
+ * Errors: QD_ESHAPE / QD_EINVAL as qgemv_q8_0 (out must not be NULL).
+ */
+qd_status qd_plan_q8act(int64_t N, int64_t K, int batch, int32_t *out);
 
 #ifdef __cplusplus
 }

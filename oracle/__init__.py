@@ -66,6 +66,7 @@ def _load():
             "orc_dequant_rows": (I, [I, P, I64, I64, I64, P]),
             "orc_gemv": (I, [I, P, P, I64, I64, I, I64, I64, P, P]),
             "orc_rmsnorm": (None, [P, P, I64, I, D, P]),
+            "orc_post_norm_residual": (None, [P, P, P, P, I64, I, D, P, P]),
             "orc_gelu_tanh": (D, [D]),
             "orc_silu": (D, [D]),
             "orc_act": (D, [I, D]),
@@ -249,6 +250,22 @@ def rmsnorm(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
     return out
 
 
+def post_norm_residual(p: np.ndarray, r: np.ndarray, w1: np.ndarray, eps: float, w2=None):
+    """(y, y2) of orc_post_norm_residual: y = r + RMSNorm(p; w1), y2 =
+    RMSNorm(y; w2) (None without w2); p fp64 [batch, N] or [N]."""
+    p2 = np.ascontiguousarray(np.atleast_2d(p), dtype=np.float64)
+    r2 = np.ascontiguousarray(np.atleast_2d(r), dtype=np.float32)
+    batch, N = p2.shape
+    assert r2.shape == (batch, N)
+    w1 = np.ascontiguousarray(w1, dtype=np.float32)
+    y = np.empty((batch, N), dtype=np.float64)
+    y2 = np.empty((batch, N), dtype=np.float64) if w2 is not None else None
+    w2c = np.ascontiguousarray(w2, dtype=np.float32) if w2 is not None else None
+    _load().orc_post_norm_residual(_ptr(p2), _ptr(r2), _ptr(w1), _ptr(w2c) if w2c is not None else None,
+                                   N, batch, eps, _ptr(y), _ptr(y2) if y2 is not None else None)
+    return y, y2
+
+
 def act(kind: int, g: float) -> float:
     return _load().orc_act(kind, g)
 
@@ -277,6 +294,44 @@ def gemm_bf16(fmt, W: np.ndarray, X: np.ndarray, N: int, K: int,
     if rc != 0:
         raise ValueError("orc_gemm_bf16 failed")
     return Y, S
+
+
+def gemm_bf16_threaded(fmt, W: np.ndarray, X: np.ndarray, N: int, K: int, threads: int):
+    """Same as gemm_bf16 over the whole output, weight rows split over
+    `threads` host threads (ctypes releases the GIL during the C call)."""
+    fmt = _fmt(fmt)
+    W = np.ascontiguousarray(W, dtype=np.uint8)
+    X = np.ascontiguousarray(X, dtype=np.uint16)
+    M = X.shape[0]
+    assert X.shape[1] == K
+    Y = np.empty((M, N), dtype=np.float64)
+    S = np.empty((M, N), dtype=np.float64)
+    lib = _load()
+    bounds = np.linspace(0, N, threads + 1).astype(np.int64)
+    rcs = [0] * threads
+
+    def work(t):
+        rcs[t] = lib.orc_gemm_bf16(fmt, _ptr(W), _ptr(X), M, N, K, 0, M, int(bounds[t]), int(bounds[t + 1]),
+                                   _ptr(Y), _ptr(S))
+
+    ts = [threading.Thread(target=work, args=(t,)) for t in range(threads)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    if any(rcs):
+        raise ValueError("orc_gemm_bf16 failed")
+    return Y, S
+
+
+def host_threads(cap: int = 16) -> int:
+    """Threads for the threaded oracle calls: the cores this process may run
+    on, at most `cap`."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(cap, n))
 
 
 def gemm_bf16_cols(fmt, W: np.ndarray, X: np.ndarray, N: int, K: int, cols):

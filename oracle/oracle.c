@@ -306,6 +306,37 @@ void orc_rmsnorm(const float *x, const float *w, int64_t K, int batch,
     }
 }
 
+/* ----------------------------------------------- Post-norm residual ---
+ * larql "Architecture -> Metal shader map", Gemma 3 table ("has_post_norms":
+ * four norms per layer): after the O projection, post_attn_residual_norm_store
+ * (the post-attention RMS-norm of the projection, the residual add, the FFN
+ * input norm of the sum, both stored); after the down projection,
+ * post_ffn_norm_residual_add (the post-FFN RMS-norm of the projection added
+ * to the residual, the next layer's input).  Reading: the post-norm order
+ * of that pipeline -- the norm applies to the projection before the
+ * residual add -- with each weight multiplied directly, as in orc_rmsnorm:
+ *   y[n]  = r[n] + p[n] * w1[n] / sqrt(mean(p^2) + eps)
+ *   y2[n] = y[n] * w2[n] / sqrt(mean(y^2) + eps)        (when w2 and y2)
+ * per batch column; p in fp64 (the exact projection), everything in fp64. */
+void orc_post_norm_residual(const double *p, const float *r, const float *w1, const float *w2,
+                            int64_t N, int batch, double eps, double *y, double *y2) {
+    for (int b = 0; b < batch; b++) {
+        const double *pb = p + (int64_t)b * N;
+        const float *rb = r + (int64_t)b * N;
+        double *yb = y + (int64_t)b * N;
+        double ss = 0.0;
+        for (int64_t n = 0; n < N; n++) ss += pb[n] * pb[n];
+        const double inv = 1.0 / sqrt(ss / (double)N + eps);
+        for (int64_t n = 0; n < N; n++) yb[n] = (double)rb[n] + pb[n] * inv * (double)w1[n];
+        if (w2 && y2) {
+            double ss2 = 0.0;
+            for (int64_t n = 0; n < N; n++) ss2 += yb[n] * yb[n];
+            const double inv2 = 1.0 / sqrt(ss2 / (double)N + eps);
+            for (int64_t n = 0; n < N; n++) y2[(int64_t)b * N + n] = yb[n] * inv2 * (double)w2[n];
+        }
+    }
+}
+
 /* ---------------------------------------------------------- Activations ---
  * larql Gemma 3 table, "GEGLU activation": the GELU-tanh variant applied to
  * gate, times up.  GELU with the tanh approximation (Hendrycks & Gimpel):

@@ -77,6 +77,14 @@ int orc_gemv_q8_0_q8act(const uint8_t *W, const int8_t *qx, const float *dx, int
 void orc_rmsnorm(const float *x, const float *w, int64_t K, int batch,
                  double eps, double *out);
 
+/* Post-norm and residual (larql Gemma 3 table, post_attn_residual_norm_store
+ * and post_ffn_norm_residual_add), fp64, per batch column of N:
+ *   y  = r + p * w1 / sqrt(mean(p^2) + eps)
+ *   y2 = y * w2 / sqrt(mean(y^2) + eps)     (skipped when w2 or y2 is NULL)
+ * p [batch][N] fp64; r [batch][N], w1 [N], w2 [N] fp32. */
+void orc_post_norm_residual(const double *p, const float *r, const float *w1, const float *w2,
+                            int64_t N, int batch, double eps, double *y, double *y2);
+
 /* Activations in fp64. */
 double orc_gelu_tanh(double g);
 double orc_silu(double g);

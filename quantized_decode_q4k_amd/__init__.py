@@ -9,6 +9,8 @@ library is not built, or a tensor is not on the GPU, the call raises.
 Entry points (same names as the C ABI):
     qgemv_q4k, qgemv_q6k, qgemv_q8_0, qgemv        y = W x, batch 1..8
     qgemv_residual                                 y = W x + r (r may be y)
+    qgemv_post_norm_residual                       y = r + RMSNorm(W x), y2 = RMSNorm(y)
+    qffn_decode_post_norm_residual                 the same epilogue on the FFN's down projection
     qgemv_q8_0_q8act                               Q8_0 GEMV on int8-quantized x (opt-in)
     qquantize_q8_act, qgemv_q8_0_preq              its two halves: quantize once, GEMV on the codes
     qqkv_proj                                      q, k, v = Wq xn, Wk xn, Wv xn (one launch)
@@ -37,7 +39,7 @@ ACTS = {"gelu_tanh": ACT_GELU_TANH, "silu": ACT_SILU}
 MAX_BATCH = 64
 BATCH_CHUNK = 8
 
-QD_OK, QD_EINVAL, QD_ESHAPE, QD_EALIGN, QD_ELAUNCH, QD_EUNSUPPORTED, QD_ENOMEM = range(7)
+QD_OK, QD_EINVAL, QD_ESHAPE, QD_EALIGN, QD_ELAUNCH, QD_EUNSUPPORTED, QD_ENOMEM, QD_ECAPTURE = range(8)
 
 # Every function the header declares, with its ctypes signature.
 _P = ctypes.c_void_p
@@ -55,6 +57,9 @@ SIGNATURES = {
     "qgemv_q8_0": (_I, [_P, _P, _P, _I64, _I64, _I, _P]),
     "qgemv": (_I, [_I, _P, _P, _P, _I64, _I64, _I, _P]),
     "qgemv_residual": (_I, [_I, _P, _P, _P, _P, _I64, _I64, _I, _P]),
+    "qgemv_post_norm_residual": (_I, [_I, _P, _P, _P, _F, _P, _P, _P, _P, _I64, _I64, _I, _P]),
+    "qffn_decode_post_norm_residual": (_I, [_I, _P, _P, _I, _P, _P, _P, _F, _I, _P, _P, _P, _P, _P, _P, _I64,
+                                            _I64, _I, _P]),
     "qgemv_q8_0_q8act": (_I, [_P, _P, _P, _I64, _I64, _I, _P]),
     "qquantize_q8_act": (_I, [_P, _P, _P, _I64, _I, _P]),
     "qgemv_q8_0_preq": (_I, [_P, _P, _P, _P, _I64, _I64, _I, _P]),
@@ -72,10 +77,9 @@ SIGNATURES = {
     "qdequant_bf16": (_I, [_I, _P, _P, _I64, _I64, _P]),
     "qd_set_launch_override": (_I, [_I, _I, _I]),
     "qd_set_walk_override": (_I, [_I]),
-    "qd_set_ffn_override": (_I, [_I, _I, _I]),
     "qd_set_gemm_override": (_I, [_I, _I]),
     "qd_set_stream_override": (_I, [_I, _I, _I, _I]),
-    "qd_set_ffn_mode": (_I, [_I]),
+    "qd_plan_q8act": (_I, [_I64, _I64, _I, _P]),
 }
 
 _lock = threading.Lock()
@@ -192,6 +196,61 @@ def qgemv_residual(fmt, W: torch.Tensor, x: torch.Tensor, r: torch.Tensor,
                               _stream())
     _check("qgemv_residual", st)
     return y
+
+
+def qgemv_post_norm_residual(fmt, W: torch.Tensor, x: torch.Tensor, post_w: torch.Tensor, r: torch.Tensor,
+                             eps: float = 1e-6, y: torch.Tensor | None = None,
+                             next_w: torch.Tensor | None = None, y2: torch.Tensor | None = None):
+    """y = r + RMSNorm(W x; post_w) and, with next_w, y2 = RMSNorm(y; next_w).
+    Pass y=r to update the residual in place.  Returns y, or (y, y2)."""
+    f = _fmt(fmt)
+    K = x.shape[-1]
+    batch = 1 if x.dim() == 1 else x.shape[0]
+    N = _rows(f, W, K)
+    if tuple(r.shape) != ((N,) if x.dim() == 1 else (batch, N)):
+        raise ValueError("r must have the output's shape")
+    if y is None:
+        y = torch.empty_like(r)
+    if next_w is not None and y2 is None:
+        y2 = torch.empty_like(r)
+    st = lib().qgemv_post_norm_residual(
+        f, _dev(W, "W", torch.uint8), _dev(x, "x", torch.float32), _dev(post_w, "post_w", torch.float32),
+        float(eps), _dev(r, "r", torch.float32), _dev(y, "y", torch.float32),
+        _dev(next_w, "next_w", torch.float32) if next_w is not None else None,
+        _dev(y2, "y2", torch.float32) if next_w is not None else None, N, K, batch, _stream())
+    _check("qgemv_post_norm_residual", st)
+    return (y, y2) if next_w is not None else y
+
+
+def qffn_decode_post_norm_residual(fmt_gu, Wg: torch.Tensor, Wu: torch.Tensor, fmt_down, Wd: torch.Tensor,
+                                   x: torch.Tensor, post_w: torch.Tensor, r: torch.Tensor,
+                                   norm_w: torch.Tensor | None = None, eps: float = 1e-6, act="gelu_tanh",
+                                   y: torch.Tensor | None = None, next_w: torch.Tensor | None = None,
+                                   y2: torch.Tensor | None = None, h_out: torch.Tensor | None = None):
+    """y = r + RMSNorm(Wd h; post_w), h = act(Wg xn) * (Wu xn); with next_w
+    also y2 = RMSNorm(y; next_w).  Returns y, or (y, y2)."""
+    fg, fd = _fmt(fmt_gu), _fmt(fmt_down)
+    K = x.shape[-1]
+    batch = 1 if x.dim() == 1 else x.shape[0]
+    N = _rows(fg, Wg, K)
+    if _rows(fg, Wu, K) != N or _rows(fd, Wd, N) != K:
+        raise ValueError("gate/up must be N_ff x K and down K x N_ff")
+    if tuple(r.shape) != tuple(x.shape):
+        raise ValueError("r must have x's shape")
+    if y is None:
+        y = torch.empty_like(x)
+    if next_w is not None and y2 is None:
+        y2 = torch.empty_like(x)
+    nw = _dev(norm_w, "norm_w", torch.float32) if norm_w is not None else None
+    hp = _dev(h_out, "h_out", torch.float32) if h_out is not None else None
+    st = lib().qffn_decode_post_norm_residual(
+        fg, _dev(Wg, "Wg", torch.uint8), _dev(Wu, "Wu", torch.uint8), fd, _dev(Wd, "Wd", torch.uint8),
+        _dev(x, "x", torch.float32), nw, float(eps), _act(act), _dev(post_w, "post_w", torch.float32),
+        _dev(r, "r", torch.float32), _dev(y, "y", torch.float32),
+        _dev(next_w, "next_w", torch.float32) if next_w is not None else None,
+        _dev(y2, "y2", torch.float32) if next_w is not None else None, hp, N, K, batch, _stream())
+    _check("qffn_decode_post_norm_residual", st)
+    return (y, y2) if next_w is not None else y
 
 
 def qgemv_q8_0_q8act(W: torch.Tensor, x: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
@@ -432,11 +491,6 @@ def qdequant_bf16(fmt, W: torch.Tensor, K: int, out: torch.Tensor | None = None)
     return out
 
 
-def set_ffn_override(p_in_a: int = 0, p_in_b: int = 0, p_out_b: int = 0):
-    """Force qffn_decode's launch shape for tuning sweeps (0 = automatic)."""
-    _check("qd_set_ffn_override", lib().qd_set_ffn_override(p_in_a, p_in_b, p_out_b))
-
-
 def set_gemm_override(tm: int = 0, splits: int = 0):
     """Prefill tile override (0 = automatic)."""
     _check("qd_set_gemm_override", lib().qd_set_gemm_override(tm, splits))
@@ -444,16 +498,10 @@ def set_gemm_override(tm: int = 0, splits: int = 0):
 
 def set_stream_override(wg_per_cu: int = 0, depth: int = 0, consumers: int = 0, producers: int = 0):
     """Streaming GEMV shape override (0 = automatic): workgroups per CU, steps
-    in flight, decoding waves (1 = every wave copies and decodes; 4 or 8 = the
-    producer / consumer kernel) and its copying waves (1, 2 or 4)."""
+    in flight per copying wave, decoding waves (4 or 8) and copying waves
+    (1, 2 or 4)."""
     _check("qd_set_stream_override",
            lib().qd_set_stream_override(wg_per_cu, depth, consumers, producers))
-
-
-def set_ffn_mode(mode: int = 0):
-    """qffn_decode's form: 0 = automatic (two launches), 1 = two launches,
-    2 = one launch with a grid barrier where the shape allows it."""
-    _check("qd_set_ffn_mode", lib().qd_set_ffn_mode(mode))
 
 
 def set_walk_override(rows_per_group: int = 0):
@@ -465,3 +513,11 @@ def set_walk_override(rows_per_group: int = 0):
 def set_launch_override(p_in: int = 0, p_out: int = 0, nr: int = 0):
     """Force the GEMV launch shape for tuning sweeps (0 = automatic)."""
     _check("qd_set_launch_override", lib().qd_set_launch_override(p_in, p_out, nr))
+
+
+def plan_q8act(N: int, K: int, batch: int = 1):
+    """(lane groups per row, K-slices, superunits per slice, columns per
+    launch) of the int8-activation GEMV for this shape; host only."""
+    out = (ctypes.c_int32 * 4)()
+    _check("qd_plan_q8act", lib().qd_plan_q8act(N, K, batch, out))
+    return tuple(out)

@@ -9,6 +9,7 @@
 #include <map>
 #include <mutex>
 #include <utility>
+#include <vector>
 
 #include "qd_internal.h"
 #include "qdecode.h"
@@ -54,13 +55,11 @@ bool overlap(const void *p, size_t n, const void *q, size_t m) {
 
 // ------------------------------------------------------- launch shapes ---
 std::atomic<int> g_over_pin{0}, g_over_pout{0}, g_over_nr{0}, g_over_rpg{0};
-std::atomic<int> g_ffn_pin_a{0}, g_ffn_pin_b{0}, g_ffn_pout_b{0};
 
 constexpr int kTargetWorkgroups = 400;   // enough to keep every CU streaming
 constexpr int kWalkMinWorkgroups = 1000; // batch 1-2 row walk only with rows to spare
 constexpr int kMaxTiles = 1 << 16;       // split-K counters per workspace
-constexpr int kCtlSlots = qd::kFfnCtlWords;  // leading counters: the fused FFN's control block
-constexpr int kBarWords = 64;                  // trailing counters: the one-launch FFN's grid barrier
+constexpr int kAuxWords = 4096;          // counters after the tile counters: row epilogues, FFN flags
 
 int lds_units_max(int fmt, int batch) {
     // largest nk whose staging fits the per-workgroup LDS budget
@@ -155,19 +154,34 @@ Plan choose_plan(int fmt, int64_t N, int64_t K, int batch, bool ffn) {
 }
 
 // ---------------------------------------------------------- workspace ---
-// Split-K partial sums and per-tile counters, one block per (device, stream)
-// so that calls on different streams never share it.  Counters start at
-// zero and every kernel that uses one resets it before it ends.
+// Split-K partial sums and counters, one block per (device, stream) so that
+// calls on different streams never share it.  Counters start at zero and
+// every kernel that uses one resets it before it ends, so a block needs no
+// reset between calls.  A block is allocated (and its counters cleared on
+// the caller's stream) only by a call made while the stream is not being
+// captured; a capturing call that would need a new or larger block returns
+// QD_ECAPTURE with nothing enqueued.  A block that has been outgrown stays
+// allocated until the process ends, so a graph captured with it stays
+// valid.
 struct Workspace {
     float *partials = nullptr;
-    unsigned *counters = nullptr;
+    unsigned *counters = nullptr;   // [kMaxTiles] tile counters, then [kAuxWords]
     size_t partial_floats = 0;
 };
 
 std::mutex g_ws_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+std::vector<std::pair<float *, unsigned *>> g_ws_retired;
 
 constexpr size_t kInitialPartials = size_t(8) << 20;  // 32 MiB of floats
+constexpr size_t kCounterWords = (size_t)kMaxTiles + kAuxWords;
+
+// True when `st` is being captured into a graph (or its state cannot be read).
+bool capturing(hipStream_t st) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess) return true;
+    return cs != hipStreamCaptureStatusNone;
+}
 
 qd_status get_workspace(hipStream_t st, size_t need_floats, Workspace *out) {
     int dev = 0;
@@ -175,25 +189,22 @@ qd_status get_workspace(hipStream_t st, size_t need_floats, Workspace *out) {
     std::lock_guard<std::mutex> lk(g_ws_mu);
     Workspace &w = g_ws[{dev, st}];
     if (w.partials == nullptr || w.partial_floats < need_floats) {
+        if (capturing(st)) return QD_ECAPTURE;
         size_t n = std::max(kInitialPartials, need_floats);
+        if (w.partials != nullptr) n = std::max(n, 2 * w.partial_floats);
         float *p = nullptr;
         unsigned *c = nullptr;
         if (hipMalloc(&p, n * sizeof(float)) != hipSuccess) return QD_ENOMEM;
-        if (hipMalloc(&c, (kMaxTiles + kCtlSlots + kBarWords) * sizeof(unsigned)) != hipSuccess) {
+        if (hipMalloc(&c, kCounterWords * sizeof(unsigned)) != hipSuccess) {
             (void)hipFree(p);
             return QD_ENOMEM;
         }
-        if (hipMemsetAsync(c, 0, (kMaxTiles + kCtlSlots + kBarWords) * sizeof(unsigned), st) != hipSuccess) {
+        if (hipMemsetAsync(c, 0, kCounterWords * sizeof(unsigned), st) != hipSuccess) {
             (void)hipFree(p);
             (void)hipFree(c);
             return QD_ELAUNCH;
         }
-        if (w.partials != nullptr) {
-            // an older, smaller block: wait for its users on this stream
-            (void)hipStreamSynchronize(st);
-            (void)hipFree(w.partials);
-            (void)hipFree(w.counters);
-        }
+        if (w.partials != nullptr) g_ws_retired.emplace_back(w.partials, w.counters);
         w.partials = p;
         w.counters = c;
         w.partial_floats = n;
@@ -235,29 +246,6 @@ void stream_rows(int64_t N, int64_t K, int fmt, int wpc, const float *norm_w, qd
     *grid = (unsigned)G;
 }
 
-// Kernel in which every wave copies and decodes, wpc workgroups per CU; false
-// if its LDS layout does not fit.
-bool stream_plan_wpc(int fmt, bool ffn, int64_t N, int64_t K, int batch, const float *norm_w,
-                     int wpc, qd::StreamArgs *a, unsigned *grid, size_t *lds) {
-    stream_rows(N, K, fmt, wpc, norm_w, a, grid);
-    const size_t budget = kLdsPerCU / wpc;
-    const int copies = qd::stream_copies_per_step(fmt, ffn);
-    if (copies <= 0) return false;
-    // a shallow ring: copies queued beyond a few steps block the issuing
-    // wave without adding bandwidth (measured: depth 3 best, 2 close)
-    const int pd_max = std::min(g_stream_depth.load() ? g_stream_depth.load() : 3, kStreamMaxWait / copies);
-    for (int pd = pd_max; pd >= 2; pd--) {
-        const size_t bytes = qd::stream_layout(fmt, batch, ffn, a->nb, a->units_max, pd, a);
-        if (bytes <= budget) {
-            a->pd = pd;
-            a->consumers = 0;
-            *lds = bytes;
-            return true;
-        }
-    }
-    return false;
-}
-
 // Producer / consumer kernel: as many ring slots as the LDS share holds (a
 // multiple of the copying waves, no more than the workgroup's steps need), and
 // as many steps in flight per copying wave as its vmcnt can track.  When slots
@@ -289,7 +277,7 @@ bool stream_plan_pc(int fmt, bool ffn, int64_t N, int64_t K, int batch, const fl
     lag = std::min(lag, lag_max);
     if (steps > slots) lag = std::min(lag, (slots - consumers) / producers + 1);
     if (lag < 1) return false;
-    a->pd = 0;
+
     a->slots = slots;
     a->lag = lag;
     return true;
@@ -323,11 +311,8 @@ bool stream_plan(int fmt, bool ffn, int64_t N, int64_t K, int batch, const float
     const int cons = g_stream_consumers.load();
     constexpr int kPcLag = 3;  // steps in flight per copying wave
     if (wpc) {
-        if (cons == 4 || cons == 8) {
-            const int prod = g_stream_producers.load() ? g_stream_producers.load() : 2;
-            return stream_plan_pc(fmt, ffn, N, K, batch, norm_w, wpc, cons, prod, kPcLag, a, grid, lds);
-        }
-        return stream_plan_wpc(fmt, ffn, N, K, batch, norm_w, wpc, a, grid, lds);
+        const int prod = g_stream_producers.load() ? g_stream_producers.load() : 2;
+        return stream_plan_pc(fmt, ffn, N, K, batch, norm_w, wpc, cons ? cons : 8, prod, kPcLag, a, grid, lds);
     }
     if (!ffn && K < kStreamMinK) return false;
     if (batch == 1) {
@@ -346,10 +331,18 @@ bool stream_plan(int fmt, bool ffn, int64_t N, int64_t K, int batch, const float
     return stream_plan_pc(fmt, ffn, N, K, batch, norm_w, 2, 4, 2, kPcLag, a, grid, lds);
 }
 
+// Row epilogue arguments of a plain GEMV (post-norm, residual, next norm).
+struct PostArgs {
+    const float *w1 = nullptr;  // post-norm weight [N]; nullptr = none
+    const float *w2 = nullptr;  // next-norm weight [N] or nullptr
+    float *y2 = nullptr;        // [batch][N] with w2
+    float eps = 0.f;
+};
+
 qd_status run_mv(int fmt, bool ffn, const void *W0, const void *W1, const float *x,
                  const float *norm_w, float eps, int act, float *y, float *g_out, float *u_out,
                  int64_t N, int64_t K, int batch, void *stream, size_t ws_offset = 0,
-                 const float *res = nullptr) {
+                 const float *res = nullptr, const PostArgs &post = PostArgs()) {
     qd_status st = check_shape(fmt, N, K, batch);
     if (st != QD_OK) return st;
     if (!W0 || !x || !y || (ffn && !W1)) return QD_EINVAL;
@@ -358,48 +351,78 @@ qd_status run_mv(int fmt, bool ffn, const void *W0, const void *W1, const float 
     if (norm_w && !aligned(norm_w, 16)) return QD_EALIGN;
     if (!aligned(y, 4) || (g_out && !aligned(g_out, 4)) || (u_out && !aligned(u_out, 4)))
         return QD_EALIGN;
+    const bool pnorm = post.w1 != nullptr;
+    if (pnorm && (ffn || !res || (post.w2 == nullptr) != (post.y2 == nullptr))) return QD_EINVAL;
+    if (pnorm && (!aligned(post.w1, 4) || (post.w2 && !aligned(post.w2, 4)) || !aligned(post.y2, 4)))
+        return QD_EALIGN;
     const size_t xbytes = (size_t)batch * K * 4, ybytes = (size_t)batch * N * 4;
     const size_t wbytes = (size_t)N * row_bytes(fmt, K);
-    const void *outs[3] = {y, g_out, u_out};
+    const void *outs[4] = {y, g_out, u_out, post.y2};
     for (const void *o : outs) {
         if (!o) continue;
         if (overlap(o, ybytes, x, xbytes) || overlap(o, ybytes, W0, wbytes) ||
-            (W1 && overlap(o, ybytes, W1, wbytes)) || (norm_w && overlap(o, ybytes, norm_w, K * 4)))
+            (W1 && overlap(o, ybytes, W1, wbytes)) || (norm_w && overlap(o, ybytes, norm_w, K * 4)) ||
+            (post.w1 && overlap(o, ybytes, post.w1, N * 4)) || (post.w2 && overlap(o, ybytes, post.w2, N * 4)))
             return QD_EINVAL;
     }
     if (overlap(y, ybytes, g_out, ybytes) || overlap(y, ybytes, u_out, ybytes) ||
-        overlap(g_out, ybytes, u_out, ybytes))
+        overlap(g_out, ybytes, u_out, ybytes) || overlap(y, ybytes, post.y2, ybytes))
         return QD_EINVAL;
     // the residual is read at each output's own index just before that
     // output is written, so it may be y itself, but no other part of it
     if (res && (ffn || (res != y && overlap(res, ybytes, y, ybytes)))) return QD_EINVAL;
+    if (res && overlap(res, ybytes, post.y2, ybytes)) return QD_EINVAL;
     if (res && !aligned(res, 4)) return QD_EALIGN;
     if (batch > QD_BATCH_CHUNK) {
         // successive launches of up to QD_BATCH_CHUNK columns
         for (int c0 = 0; c0 < batch; c0 += QD_BATCH_CHUNK) {
             const int nb = std::min(QD_BATCH_CHUNK, batch - c0);
             const int64_t xo = (int64_t)c0 * K, yo = (int64_t)c0 * N;
+            PostArgs pc = post;
+            if (pc.y2) pc.y2 += yo;
             qd_status cs = run_mv(fmt, ffn, W0, W1, x + xo, norm_w, eps, act, y + yo, g_out ? g_out + yo : nullptr,
-                                  u_out ? u_out + yo : nullptr, N, K, nb, stream, ws_offset, res ? res + yo : nullptr);
+                                  u_out ? u_out + yo : nullptr, N, K, nb, stream, ws_offset, res ? res + yo : nullptr,
+                                  pc);
             if (cs != QD_OK) return cs;
         }
         return QD_OK;
     }
 
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    // the row epilogue keeps the projection in the workspace, after the
+    // split-K partials (if any)
+    qd::PostNorm pn{};
+    auto bind_post = [&](size_t p_offset, unsigned tiles, const Workspace &w) {
+        pn.w1 = post.w1;
+        pn.w2 = post.w2;
+        pn.r = res;
+        pn.y2 = post.y2;
+        pn.p = w.partials + p_offset;
+        pn.ctr = w.counters + kMaxTiles;  // auxiliary counter 0
+        pn.tiles = tiles;
+        pn.eps = post.eps;
+    };
+    const size_t p_floats = pnorm ? (size_t)batch * N : 0;
     const bool forced = g_over_pin.load() || g_over_pout.load() || g_over_nr.load();
     if (!forced) {
         qd::StreamArgs sa{};
         unsigned grid = 0;
         size_t lds = 0;
         if (stream_plan(fmt, ffn, N, K, batch, norm_w, &sa, &grid, &lds)) {
+            if (pnorm) {
+                Workspace w;
+                st = get_workspace(hs, ws_offset + p_floats, &w);
+                if (st != QD_OK) return st;
+                bind_post(ws_offset, grid, w);
+                sa.pn = pn;
+            }
             sa.W0 = static_cast<const uint8_t *>(W0);
             sa.W1 = static_cast<const uint8_t *>(W1);
             sa.x = x;
             sa.y = y;
             sa.g_out = g_out;
             sa.u_out = u_out;
-            sa.res = res;
+            sa.res = pnorm ? nullptr : res;
             sa.act = act;
             sa.eps = eps;
             hipError_t e = qd::launch_stream(fmt, batch, ffn, sa, grid, lds, hs);
@@ -415,7 +438,7 @@ qd_status run_mv(int fmt, bool ffn, const void *W0, const void *W1, const float 
     a.y = y;
     a.g_out = g_out;
     a.u_out = u_out;
-    a.res = res;
+    a.res = pnorm ? nullptr : res;
     a.N = N;
     a.K = K;
     a.row_bytes = row_bytes(fmt, K);
@@ -424,69 +447,28 @@ qd_status run_mv(int fmt, bool ffn, const void *W0, const void *W1, const float 
     a.nk = p.nk;
     a.act = act;
     a.eps = eps;
-    if (p.s.p_out > 1) {
+    const size_t part_floats = p.s.p_out > 1 ? (size_t)p.s.p_out * batch * (ffn ? 2 : 1) * N : 0;
+    if (part_floats + p_floats > 0) {
         Workspace w;
-        const size_t need = ws_offset + (size_t)p.s.p_out * batch * (ffn ? 2 : 1) * N;
-        qd_status ws = get_workspace(hs, need, &w);
+        qd_status ws = get_workspace(hs, ws_offset + part_floats + p_floats, &w);
         if (ws != QD_OK) return ws;
         a.partials = w.partials + ws_offset;
-        a.counters = w.counters + kCtlSlots;
+        a.counters = w.counters;
+        if (pnorm) {
+            bind_post(ws_offset + part_floats, (unsigned)p.tiles, w);
+            a.pn = pn;
+        }
     }
     hipError_t e = qd::launch_gemv(fmt, batch, ffn, a, p.s, hs);
     return e == hipSuccess ? QD_OK : QD_ELAUNCH;
 }
 
-// y = Wd (act(Wg xn) * (Wu xn)) in one launch when the shapes allow it,
-// else as the two calls qffn_gate_up_act + qgemv on the same stream.
-std::atomic<int> g_ffn_mode{0};  // 0 = automatic (two launches), 1 = two launches, 2 = one streaming launch
-
-// One-launch FFN plan (batch 1): one workgroup per CU; phase A's ring holds
-// up to 12 steps (reused), phase B's as many as fit, at least 8 each unless
-// a workgroup has fewer steps.  False where the shape does not qualify.
-bool ffn_stream_plan(int fmt_a, int fmt_b, int64_t N_ff, int64_t K, const float *norm_w,
-                     qd::FfnStreamArgs *a, unsigned *grid, size_t *lds) {
-    if (K % qd::kSuper != 0 || N_ff % qd::kSuper != 0) return false;
-    const int64_t rbA = row_bytes(fmt_a, K), rbB = row_bytes(fmt_b, N_ff);
-    if ((N_ff * rbA) % 16 != 0 || (K * rbB) % 16 != 0) return false;
-    const int G = (int)std::min<int64_t>(std::min<int64_t>(N_ff, K), kCUs);
-    a->KA = K;
-    a->KB = N_ff;
-    a->row_bytesA = rbA;
-    a->row_bytesB = rbB;
-    a->mat_bytesA = N_ff * rbA;
-    a->mat_bytesB = K * rbB;
-    a->nbA = (int)(K / qd::kSuper);
-    a->nbB = (int)(N_ff / qd::kSuper);
-    a->rowsA_base = (int)(N_ff / G);
-    a->rowsA_extra = (int)(N_ff % G);
-    a->rowsB_base = (int)(K / G);
-    a->rowsB_extra = (int)(K % G);
-    a->unitsA_max = (a->rowsA_base + (a->rowsA_extra > 0 ? 1 : 0)) * a->nbA;
-    a->unitsB_max = (a->rowsB_base + (a->rowsB_extra > 0 ? 1 : 0)) * a->nbB;
-    const int SA = (a->unitsA_max + 15) / 16, SB = (a->unitsB_max + 15) / 16;
-    const bool norm = norm_w != nullptr;
-    const int minA = std::min(SA, 8), minB = std::min(SB, 8);
-    for (int slotsA = std::min(SA, 12); slotsA >= minA; slotsA--) {
-        int slotsB = SB;
-        while (slotsB >= minB && qd::ffn_stream_layout(fmt_a, fmt_b, norm, slotsA, slotsB, a) > kLdsPerCU)
-            slotsB--;
-        if (slotsB < minB) continue;
-        *lds = qd::ffn_stream_layout(fmt_a, fmt_b, norm, slotsA, slotsB, a);
-        a->slotsA = slotsA;
-        a->slotsB = slotsB;
-        const int lag_max = 1 + kStreamMaxWait / qd::ffn_stream_copies(fmt_a, fmt_b);
-        const int d = g_stream_depth.load();
-        a->lag = std::max(1, std::min(d ? d : 3, lag_max));
-        *grid = (unsigned)G;
-        return true;
-    }
-    return false;
-}
-
+// y = Wd (act(Wg xn) * (Wu xn)) as the two calls qffn_gate_up_act + qgemv on
+// the same stream, h in the stream's workspace unless the caller keeps it.
 qd_status run_ffn_decode(int fmt_gu, const void *Wg, const void *Wu, int fmt_d, const void *Wd,
                          const float *x, const float *norm_w, float eps, int act, float *y,
                          float *h_out, int64_t N_ff, int64_t K, int batch, void *stream,
-                         const float *res = nullptr) {
+                         const float *res = nullptr, const PostArgs &post = PostArgs()) {
     qd_status st = check_shape(fmt_gu, N_ff, K, batch);
     if (st != QD_OK) return st;
     st = check_shape(fmt_d, K, N_ff, batch);
@@ -507,14 +489,21 @@ qd_status run_ffn_decode(int fmt_gu, const void *Wg, const void *Wu, int fmt_d, 
     if (h_out && overlap(y, xbytes, h_out, hbytes)) return QD_EINVAL;
     if (res && ((res != y && overlap(res, xbytes, y, xbytes)) || (h_out && overlap(res, xbytes, h_out, hbytes))))
         return QD_EINVAL;
+    if (post.y2) {
+        for (int i = 0; i < 5; i++)
+            if (overlap(post.y2, xbytes, ins[i], insz[i])) return QD_EINVAL;
+        if (h_out && overlap(post.y2, xbytes, h_out, hbytes)) return QD_EINVAL;
+    }
     if (res && !aligned(res, 4)) return QD_EALIGN;
     if (batch > QD_BATCH_CHUNK) {
         for (int c0 = 0; c0 < batch; c0 += QD_BATCH_CHUNK) {
             const int nb = std::min(QD_BATCH_CHUNK, batch - c0);
             const int64_t xo = (int64_t)c0 * K;
+            PostArgs pc = post;
+            if (pc.y2) pc.y2 += xo;
             qd_status cs = run_ffn_decode(fmt_gu, Wg, Wu, fmt_d, Wd, x + xo, norm_w, eps, act, y + xo,
                                           h_out ? h_out + (int64_t)c0 * N_ff : nullptr, N_ff, K, nb, stream,
-                                          res ? res + xo : nullptr);
+                                          res ? res + xo : nullptr, pc);
             if (cs != QD_OK) return cs;
         }
         return QD_OK;
@@ -522,133 +511,25 @@ qd_status run_ffn_decode(int fmt_gu, const void *Wg, const void *Wu, int fmt_d, 
 
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     const size_t h_floats = h_out ? 0 : (((size_t)batch * N_ff + 63) / 64) * 64;
-
-    // phase A: gate/up with the whole of K in one workgroup
-    Plan pa = choose_plan(fmt_gu, N_ff, K, batch, true);
-    const int nb_a = (int)((K + qd::kSuper - 1) / qd::kSuper);
-    const bool fits = lds_units_max(fmt_gu, batch) >= nb_a;
-    // phase B: down tiles wait for their slice of h and stage it from
-    // memory, so h is split into slices of about five superunits and each
-    // workgroup takes many rows of one slice (h read once per row tile)
-    Plan pb;
-    {
-        const int nb_b = (int)((N_ff + qd::kSuper - 1) / qd::kSuper);
-        const int nk_b = std::min(lds_units_max(fmt_d, batch), 5);
-        Shape t{2, (nb_b + nk_b - 1) / nk_b, 1};
-        if (g_ffn_pin_b.load()) t.p_in = g_ffn_pin_b.load();
-        if (g_ffn_pout_b.load())
-            t.p_out = std::max(g_ffn_pout_b.load(), (nb_b + lds_units_max(fmt_d, batch) - 1) /
-                                                        lds_units_max(fmt_d, batch));
-        pb = make_plan(fmt_d, K, N_ff, batch, false, t);
-    }
-    // The single launch is used only when asked for (qd_set_ffn_override):
-    // measured on MI355X it is slower than the two launches (Gemma-3 FFN,
-    // graph replay: 31.9 us vs 24.6), because its down-projection
-    // workgroups only become resident as gate/up workgroups retire.
-    const bool asked = g_ffn_pin_a.load() || g_ffn_pin_b.load() || g_ffn_pout_b.load();
-    // The one streaming launch is correct but slower on the Gemma shapes
-    // (MI355X, graph replay: Gemma-3 24.9 us against 21.5 for two launches,
-    // Gemma-4 80.3 against 66.5): the two rings do not fit in LDS together,
-    // so phase A runs on a 12-step ring, and h's device-scope stores and the
-    // grid barrier add 3-5 us under the down weights' stream.  Used only
-    // when asked for.
-    if (!asked && g_ffn_mode.load() == 2 && batch == 1) {
-        qd::FfnStreamArgs fa{};
-        unsigned grid = 0;
-        size_t lds = 0;
-        if (ffn_stream_plan(fmt_gu, fmt_d, N_ff, K, norm_w, &fa, &grid, &lds)) {
-            Workspace w;
-            st = get_workspace(hs, std::max<size_t>(h_floats, 64), &w);
-            if (st != QD_OK) return st;
-            fa.Wg = static_cast<const uint8_t *>(Wg);
-            fa.Wu = static_cast<const uint8_t *>(Wu);
-            fa.Wd = static_cast<const uint8_t *>(Wd);
-            fa.x = x;
-            fa.norm_w = norm_w;
-            fa.h = h_out ? h_out : w.partials;
-            fa.y = y;
-            fa.res = res;
-            fa.bar = w.counters + kCtlSlots + kMaxTiles;
-            fa.act = act;
-            fa.eps = eps;
-            hipError_t e = qd::launch_ffn_stream(fmt_gu, fmt_d, fa, grid, lds, hs);
-            return e == hipSuccess ? QD_OK : QD_ELAUNCH;
-        }
-    }
-    const bool fused = asked && fits && qd::ffn_fused_supported(fmt_gu, fmt_d) &&
-                       pb.s.p_out * 64 <= kCtlSlots && pb.tiles <= kMaxTiles;
-    if (!fused) {
-        // size the workspace once for h and both calls' split-K partials, so
-        // that neither call reallocates it under h
-        const Plan qa = choose_plan(fmt_gu, N_ff, K, batch, true);
-        const Plan qb = choose_plan(fmt_d, K, N_ff, batch, false);
-        const size_t need_a = qa.s.p_out > 1 ? (size_t)qa.s.p_out * batch * 2 * N_ff : 0;
-        const size_t need_b = qb.s.p_out > 1 ? (size_t)qb.s.p_out * batch * K : 0;
-        float *h = h_out;
-        if (h_floats + std::max(need_a, need_b) > 0) {
-            Workspace w;
-            st = get_workspace(hs, h_floats + std::max(need_a, need_b), &w);
-            if (st != QD_OK) return st;
-            if (!h) h = w.partials;
-        }
-        st = run_mv(fmt_gu, true, Wg, Wu, x, norm_w, eps, act, h, nullptr, nullptr, N_ff, K, batch,
-                    stream, h_floats);
+    // size the workspace once for h and both calls' split-K partials, so
+    // that neither call reallocates it under h
+    const Plan qa = choose_plan(fmt_gu, N_ff, K, batch, true);
+    const Plan qb = choose_plan(fmt_d, K, N_ff, batch, false);
+    const size_t need_a = qa.s.p_out > 1 ? (size_t)qa.s.p_out * batch * 2 * N_ff : 0;
+    const size_t need_b = (qb.s.p_out > 1 ? (size_t)qb.s.p_out * batch * K : 0) +
+                          (post.w1 ? (size_t)batch * K : 0);
+    float *h = h_out;
+    if (h_floats + std::max(need_a, need_b) > 0) {
+        Workspace w;
+        st = get_workspace(hs, h_floats + std::max(need_a, need_b), &w);
         if (st != QD_OK) return st;
-        return run_mv(fmt_d, false, Wd, nullptr, h, nullptr, 0.f, 0, y, nullptr, nullptr, K, N_ff,
-                      batch, stream, h_floats, res);
+        if (!h) h = w.partials;
     }
-    {
-        Shape t = pa.s;
-        t.p_out = 1;
-        if (g_ffn_pin_a.load()) t.p_in = g_ffn_pin_a.load();
-        pa = make_plan(fmt_gu, N_ff, K, batch, true, t);
-    }
-    Workspace w;
-    const size_t need = h_floats + (size_t)pb.s.p_out * batch * K;
-    st = get_workspace(hs, need, &w);
+    st = run_mv(fmt_gu, true, Wg, Wu, x, norm_w, eps, act, h, nullptr, nullptr, N_ff, K, batch, stream,
+                h_floats);
     if (st != QD_OK) return st;
-    float *h = h_out ? h_out : w.partials;
-
-    qd::FfnArgs f{};
-    qd::MvArgs &a = f.a;
-    a.W0 = static_cast<const uint8_t *>(Wg);
-    a.W1 = static_cast<const uint8_t *>(Wu);
-    a.x = x;
-    a.norm_w = norm_w;
-    a.y = h;
-    a.N = N_ff;
-    a.K = K;
-    a.row_bytes = row_bytes(fmt_gu, K);
-    a.nb = nb_a;
-    a.nblk = (int)(K / block_elems(fmt_gu));
-    a.nk = pa.nk;
-    a.p_in = pa.s.p_in;
-    a.p_out = 1;
-    a.act = act;
-    a.eps = eps;
-    qd::MvArgs &b = f.b;
-    b.W0 = static_cast<const uint8_t *>(Wd);
-    b.x = h;
-    b.y = y;
-    b.res = res;
-    b.partials = w.partials + h_floats;
-    b.counters = w.counters + kCtlSlots;
-    b.N = K;
-    b.K = N_ff;
-    b.row_bytes = row_bytes(fmt_d, N_ff);
-    b.nb = (int)((N_ff + qd::kSuper - 1) / qd::kSuper);
-    b.nblk = (int)(N_ff / block_elems(fmt_d));
-    b.nk = pb.nk;
-    b.p_in = pb.s.p_in;
-    b.p_out = pb.s.p_out;
-    f.ctl = w.counters;
-    f.nA = (int)pa.tiles;
-    f.nBx = (int)pb.tiles;
-    f.pB = pb.s.p_out;
-    f.rowsA = qd::kGroups / pa.s.p_in;
-    f.sliceRows = pb.nk * qd::kSuper;
-    hipError_t e = qd::launch_ffn(fmt_gu, fmt_d, batch, f, hs);
-    return e == hipSuccess ? QD_OK : QD_ELAUNCH;
+    return run_mv(fmt_d, false, Wd, nullptr, h, nullptr, 0.f, 0, y, nullptr, nullptr, K, N_ff, batch, stream,
+                  h_floats, res, post);
 }
 
 // ------------------------------------------------------------ prefill ---
@@ -735,7 +616,7 @@ qd_status run_gemm(int fmt, bool ffn, const void *Wg, const void *Wu, const uint
         st = get_workspace(hs, need, &w);
         if (st != QD_OK) return st;
         a.partials = w.partials;
-        a.counters = w.counters + kCtlSlots;
+        a.counters = w.counters;
     }
     hipError_t e = qd::launch_gemm(fmt, ffn, p.tm, a, hs);
     return e == hipSuccess ? QD_OK : QD_ELAUNCH;
@@ -905,7 +786,7 @@ qd_status run_moe(int fmt_gu, const void *Wg, const void *Wu, int fmt_d, const v
     b.x = h;
     b.y = y;
     b.partials = w.partials + h_floats;
-    b.counters = w.counters + kCtlSlots;
+    b.counters = w.counters;
     b.N = K;
     b.K = N_ff;
     b.row_bytes = rb_b;
@@ -978,14 +859,20 @@ Q8Plan q8act_plan(int64_t N, int64_t K, int batch) {
         pl.ks = 1;
         pl.su_per = nsu;
     }
-    // a column whose codes do not fit one workgroup's LDS: split K until one
-    // slice does (when the row tiles can carry counters)
-    while (qd::q8act_lds_bytes(1, std::min<int64_t>(K, (int64_t)pl.su_per * qd::kSuper)) >
-               (size_t)qd::kLdsBudgetBytes &&
-           pl.su_per > 1 && pl.tiles <= kMaxTiles) {
-        pl.ks++;
-        pl.su_per = (nsu + pl.ks - 1) / pl.ks;
-        pl.ks = (nsu + pl.su_per - 1) / pl.su_per;
+    // a column whose codes do not fit one workgroup's LDS: slices of the
+    // largest superunit count that fits (when the row tiles can carry
+    // counters).  su_fit only decreases, so the search ends; the slices are
+    // then balanced, which never makes one larger than su_fit.
+    if (pl.tiles <= kMaxTiles) {
+        int su_fit = pl.su_per;
+        while (su_fit > 1 && qd::q8act_lds_bytes(1, std::min<int64_t>(K, (int64_t)su_fit * qd::kSuper)) >
+                                 (size_t)qd::kLdsBudgetBytes)
+            su_fit--;
+        if (su_fit < pl.su_per) {
+            pl.ks = (nsu + su_fit - 1) / su_fit;
+            pl.su_per = (nsu + pl.ks - 1) / pl.ks;
+            pl.ks = (nsu + pl.su_per - 1) / pl.su_per;
+        }
     }
     // columns per launch: at most QD_BATCH_CHUNK, and as many as one
     // workgroup's LDS holds quantized (its K-slice of each)
@@ -1063,7 +950,7 @@ qd_status run_q8preq(const void *W, const int8_t *q, const float *d, float *y, i
         st = get_workspace(hs, q8act_partial_floats(pl, N), &w);
         if (st != QD_OK) return st;
         partials = w.partials;
-        counters = w.counters + kCtlSlots;
+        counters = w.counters;
     }
     return launch_q8act_chunks(pl, W, q, d, y, N, K, batch, partials, counters, hs);
 }
@@ -1092,7 +979,7 @@ qd_status run_q8act(const void *W, const float *x, float *y, int64_t N, int64_t 
     float *d = w.partials + code_floats;
     if (qd::launch_q8quant(x, q, d, (int64_t)batch * (K / 32), hs) != hipSuccess) return QD_ELAUNCH;
     return launch_q8act_chunks(pl, W, q, d, y, N, K, batch, w.partials + code_floats + scale_floats,
-                               w.counters + kCtlSlots, hs);
+                               w.counters, hs);
 }
 
 }  // namespace
@@ -1113,6 +1000,7 @@ const char *qd_status_str(qd_status s) {
     case QD_ELAUNCH: return "kernel launch failed";
     case QD_EUNSUPPORTED: return "not supported by the library";
     case QD_ENOMEM: return "workspace allocation failed";
+    case QD_ECAPTURE: return "the stream is capturing a graph and the call needs a new or larger workspace";
     default: return "unknown status";
     }
 }
@@ -1128,6 +1016,33 @@ qd_status qgemv_residual(qd_format fmt, const void *W, const float *x, const flo
     if (!r) return QD_EINVAL;
     return run_mv(fmt, false, W, nullptr, x, nullptr, 0.f, 0, y, nullptr, nullptr, N, K, batch,
                   stream, 0, r);
+}
+
+qd_status qgemv_post_norm_residual(qd_format fmt, const void *W, const float *x, const float *post_w, float eps,
+                                   const float *r, float *y, const float *next_w, float *y2, int64_t N, int64_t K,
+                                   int batch, void *stream) {
+    if (!post_w || !r || (next_w == nullptr) != (y2 == nullptr)) return QD_EINVAL;
+    PostArgs pa;
+    pa.w1 = post_w;
+    pa.w2 = next_w;
+    pa.y2 = y2;
+    pa.eps = eps;
+    return run_mv(fmt, false, W, nullptr, x, nullptr, 0.f, 0, y, nullptr, nullptr, N, K, batch, stream, 0, r, pa);
+}
+
+qd_status qffn_decode_post_norm_residual(qd_format fmt_gu, const void *Wg, const void *Wu, qd_format fmt_down,
+                                         const void *Wd, const float *x, const float *norm_w, float eps, qd_act act,
+                                         const float *post_w, const float *r, float *y, const float *next_w,
+                                         float *y2, float *h_out, int64_t N_ff, int64_t K, int batch,
+                                         void *stream) {
+    if (!post_w || !r || (next_w == nullptr) != (y2 == nullptr)) return QD_EINVAL;
+    PostArgs pa;
+    pa.w1 = post_w;
+    pa.w2 = next_w;
+    pa.y2 = y2;
+    pa.eps = eps;
+    return run_ffn_decode(fmt_gu, Wg, Wu, fmt_down, Wd, x, norm_w, eps, act, y, h_out, N_ff, K, batch, stream, r,
+                          pa);
 }
 
 qd_status qgemv_q8_0_q8act(const void *W, const float *x, float *y, int64_t N, int64_t K, int batch,
@@ -1245,30 +1160,26 @@ qd_status qd_set_gemm_override(int tm, int splits) {
     return QD_OK;
 }
 
-qd_status qd_set_ffn_override(int p_in_a, int p_in_b, int p_out_b) {
-    auto ok = [](int v) { return v == 0 || v == 1 || v == 2 || v == 4 || v == 8 || v == 16; };
-    if (!ok(p_in_a) || !ok(p_in_b) || p_out_b < 0 || p_out_b > kCtlSlots / 64) return QD_EINVAL;
-    g_ffn_pin_a.store(p_in_a);
-    g_ffn_pin_b.store(p_in_b);
-    g_ffn_pout_b.store(p_out_b);
-    return QD_OK;
-}
-
-qd_status qd_set_ffn_mode(int mode) {
-    if (mode < 0 || mode > 2) return QD_EINVAL;
-    g_ffn_mode.store(mode);
-    return QD_OK;
-}
-
 qd_status qd_set_stream_override(int wg_per_cu, int depth, int consumers, int producers) {
     if (wg_per_cu < 0 || wg_per_cu > 8 || depth < 0 || depth > 32) return QD_EINVAL;
-    if (consumers != 0 && consumers != 1 && consumers != 4 && consumers != 8) return QD_EINVAL;
-    if (consumers <= 1 && (depth == 1 || depth > 8)) return QD_EINVAL;
-    if (producers < 0 || producers == 3 || producers > 4 || (producers && consumers <= 1)) return QD_EINVAL;
+    if (consumers != 0 && consumers != 4 && consumers != 8) return QD_EINVAL;
+    if (producers < 0 || producers == 3 || producers > 4) return QD_EINVAL;
     g_stream_wpc.store(wg_per_cu);
     g_stream_depth.store(depth);
     g_stream_consumers.store(consumers);
     g_stream_producers.store(producers);
+    return QD_OK;
+}
+
+qd_status qd_plan_q8act(int64_t N, int64_t K, int batch, int32_t *out) {
+    qd_status st = check_shape(QD_Q8_0, N, K, batch);
+    if (st != QD_OK) return st;
+    if (!out) return QD_EINVAL;
+    const Q8Plan pl = q8act_plan(N, K, batch);
+    out[0] = pl.p;
+    out[1] = pl.ks;
+    out[2] = pl.su_per;
+    out[3] = pl.chunk;
     return QD_OK;
 }
 

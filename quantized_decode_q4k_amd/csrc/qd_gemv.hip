@@ -24,16 +24,18 @@
 //  * x (optionally RMS-normalised on the way in) is staged once per
 //    workgroup in LDS with a 16-byte skew every 64 floats, so the four lanes
 //    of a group, which read the same offsets 64 floats apart, hit different
-//    banks.  Q4_K also stages per-32 sums of x for its min term.
+//    banks.
 //  * Decoding: Q4_K nibbles become floats through the fp8 converter (two
-//    per instruction, exact); Q6_K quants become signed (q - 32) bytes with a
-//    byte-permute lookup of the high bits, then one sign-extending convert;
-//    Q8_0 bytes take one sign-extending convert.  Scales are applied once per
-//    16 or 32 weights.
+//    per instruction, exact) and each weight is formed with one fused
+//    multiply-add of its sub-block's scale and min; Q6_K quants become
+//    signed (q - 32) bytes with a byte-permute lookup of the high bits, then
+//    one sign-extending convert, and Q8_0 bytes take one sign-extending
+//    convert, their (exact) scales applied once per 16 or 32 weights.
 //  * Per-lane partials are reduced across the 4*p_in lanes of a row with
 //    cross-lane shuffles; one lane writes each output (and, for the fused
 //    FFN, applies the GELU-tanh or SiLU product).
 #include "qd_decode.h"
+#include "qd_epilogue.h"
 
 #include <algorithm>
 
@@ -52,21 +54,27 @@ constexpr int kSuperPhys = kSuper + kSuper / 16;  // 272
 // One superunit of NR row streams against B staged activation rows.
 
 // Q4_K.  xp: this lane's 64 activations (logical 256*tl + 64c, contiguous in
-// LDS); sp: the staged sums of x over sub-blocks 2c and 2c+1.  Accumulates,
-// per row stream and batch row,
-//   yq += d * (sc0 * sum(q x) over the low nibbles + sc1 * sum(q x) high)
-//         (in units of fp8_unit())
-//   ym += dmin * (m0 * X0 + m1 * X1)
-// so that the row result is yq / fp8_unit() - ym.
+// LDS).  Each weight is formed on its own, w = d*sc*q - dmin*m with one fused
+// multiply-add (the nibble arrives as q * fp8_unit(), so d*sc is scaled by
+// 1/fp8_unit(); both factors are exact), then multiplied by its activation:
+// the rounding error is that of a plain dot product of the exact weights,
+// whatever the scale and min terms cancel to.  The superunit's sum (two
+// chains of 32 terms) is added to y.
 template <int NR, int B>
-QD_DEV void q4k_step(const RawQ4K (&r)[NR], const float *__restrict__ xp, int xstride,
-                     const float *__restrict__ sp, int sstride, const Q4Lane &L,
-                     float (&yq)[NR][B], float (&ym)[NR][B]) {
+QD_DEV void q4k_step(const RawQ4K (&r)[NR], const float *__restrict__ xp, int xstride, const Q4Lane &L,
+                     float (&y)[NR][B]) {
     float alo[NR][B], ahi[NR][B];
+    float a0[NR], a1[NR], b0[NR], b1[NR];
 #pragma unroll
-    for (int i = 0; i < NR; i++)
+    for (int i = 0; i < NR; i++) {
+        const Q4Scales s = q4k_scales(r[i], L);
+        a0[i] = (s.d * s.sc0) * fp8_inv_unit();
+        a1[i] = (s.d * s.sc1) * fp8_inv_unit();
+        b0[i] = -(s.dmin * s.m0);
+        b1[i] = -(s.dmin * s.m1);
 #pragma unroll
         for (int b = 0; b < B; b++) { alo[i][b] = 0.f; ahi[i][b] = 0.f; }
+    }
 
 #pragma unroll
     for (int dw = 0; dw < 8; dw++) {
@@ -79,34 +87,32 @@ QD_DEV void q4k_step(const RawQ4K (&r)[NR], const float *__restrict__ xp, int xs
 #pragma unroll
         for (int i = 0; i < NR; i++) {
             const Q4Nibbles n = q4k_nibbles(r[i].q[dw]);
+            const float l0 = fmaf(n.lo01.x, a0[i], b0[i]), l1 = fmaf(n.lo01.y, a0[i], b0[i]);
+            const float l2 = fmaf(n.lo23.x, a0[i], b0[i]), l3 = fmaf(n.lo23.y, a0[i], b0[i]);
+            const float h0 = fmaf(n.hi01.x, a1[i], b1[i]), h1 = fmaf(n.hi01.y, a1[i], b1[i]);
+            const float h2 = fmaf(n.hi23.x, a1[i], b1[i]), h3 = fmaf(n.hi23.y, a1[i], b1[i]);
 #pragma unroll
             for (int b = 0; b < B; b++) {
                 float s = alo[i][b];
-                s = fmaf(n.lo01.x, xl[b].x, s);
-                s = fmaf(n.lo01.y, xl[b].y, s);
-                s = fmaf(n.lo23.x, xl[b].z, s);
-                s = fmaf(n.lo23.y, xl[b].w, s);
+                s = fmaf(l0, xl[b].x, s);
+                s = fmaf(l1, xl[b].y, s);
+                s = fmaf(l2, xl[b].z, s);
+                s = fmaf(l3, xl[b].w, s);
                 alo[i][b] = s;
                 float u = ahi[i][b];
-                u = fmaf(n.hi01.x, xh[b].x, u);
-                u = fmaf(n.hi01.y, xh[b].y, u);
-                u = fmaf(n.hi23.x, xh[b].z, u);
-                u = fmaf(n.hi23.y, xh[b].w, u);
+                u = fmaf(h0, xh[b].x, u);
+                u = fmaf(h1, xh[b].y, u);
+                u = fmaf(h2, xh[b].z, u);
+                u = fmaf(h3, xh[b].w, u);
                 ahi[i][b] = u;
             }
         }
     }
 
 #pragma unroll
-    for (int i = 0; i < NR; i++) {
-        const Q4Scales s = q4k_scales(r[i], L);
+    for (int i = 0; i < NR; i++)
 #pragma unroll
-        for (int b = 0; b < B; b++) {
-            const float2 X = *reinterpret_cast<const float2 *>(sp + b * sstride);
-            yq[i][b] = fmaf(s.d, fmaf(s.sc1, ahi[i][b], s.sc0 * alo[i][b]), yq[i][b]);
-            ym[i][b] = fmaf(s.dmin, fmaf(s.m1, X.y, s.m0 * X.x), ym[i][b]);
-        }
-    }
+        for (int b = 0; b < B; b++) y[i][b] += alo[i][b] + ahi[i][b];
 }
 
 // Q6_K.  xg0..xg3: this lane's four runs of 16 activations (groups g).
@@ -220,48 +226,13 @@ constexpr int lookahead() {
 #endif
 }
 
-// Where a tile's activations come from and where its outputs go.
-enum : int {
-    kPlain = 0,     // ordinary loads / stores
-    kCoherent = 1,  // device-scope loads / stores: data produced or consumed by
-                    // other workgroups of the same launch (fused FFN)
-};
-
-template <int YM>
-QD_DEV void store_out(float *p, float v) {
-    if constexpr (YM == kCoherent) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else *p = v;
-}
-
-// Bounded wait of thread 0 until *ctr >= target (device-scope loads).  The
-// bound is a safety net: the producers of every counter waited on here are
-// already running when the wait starts, so it ends long before the bound.
-QD_DEV void wait_counter(const unsigned *ctr, unsigned target) {
-    for (int it = 0; it < (1 << 20); it++) {
-        if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) return;
-        __builtin_amdgcn_s_sleep(4);
-    }
-}
+QD_DEV void store_out(float *p, float v) { *p = v; }
 
 // One workgroup tile: rows [bx * rows_per_wg, ...) over K-slice ks of
 // p_out.  FMT: block format; B: batch rows (1..8); NR: row streams per lane
 // group (FFN: 2 = gate, up); FFN: fused gate/up/activation epilogue.
-// XM / YM: kPlain or kCoherent activation loads / output stores.  If
-// wait_ctr is set, thread 0 waits for *wait_ctr >= wait_target after the
-// first weight loads are issued and before x is staged.
-// Wait hook of a tile that consumes data produced in the same launch: wait
-// until *ready >= target; then count this workgroup in *arrived, and the
-// last of `readers` workgroups resets both counters for the next launch.
-struct WaitSpec {
-    unsigned *ready = nullptr;
-    unsigned target = 0;
-    unsigned *arrived = nullptr;
-    unsigned readers = 0;
-};
-
-template <int FMT, int B, int NR, bool FFN, int XM, int YM>
-QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out, float *smem,
-                    const WaitSpec ws = WaitSpec()) {
+template <int FMT, int B, int NR, bool FFN>
+QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out, float *smem) {
     const int tid = threadIdx.x;
     const int c = tid & 3;
     const int grp = tid >> 2;
@@ -273,9 +244,7 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
     const int t_end = min(a.nb, t_beg + a.nk);
     const int xstride = a.nk * kSuperPhys;
     float *xl = smem;                                 // [B][nk * 272]
-    float *xsum = smem + B * xstride;                 // Q4_K: [B][nk * 8]
-    const int sstride = a.nk * 8;
-    float *red = xsum + (FMT == kQ4K ? B * sstride : 0);  // [4 waves][B], then [B]
+    float *red = smem + B * xstride;                  // [4 waves][B]
 
     // ---- rows of this lane group: row slots bx * RS * rpg + r * RS + rs for
     // r < rpg (a row slot is one row of each matrix for the fused FFN, NR
@@ -300,7 +269,7 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
     // weight) before any weight load is issued, so they return ahead of the
     // weight stream instead of queueing behind it
     constexpr int kXr = 6;  // float4 per thread held this way
-    const bool early = (XM == kPlain) && (B * F <= kXr * kThreads);
+    const bool early = B * F <= kXr * kThreads;
     float4 xr[kXr], wr[kXr];
 #pragma unroll
     for (int i = 0; i < kXr; i++) {
@@ -358,19 +327,6 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
         if (++ul == nsu) { ul = 0; rl++; }
     }
 
-    if (ws.ready != nullptr) {
-        if (tid == 0) {
-            wait_counter(ws.ready, ws.target);
-            const unsigned n = __hip_atomic_fetch_add(ws.arrived, 1u, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT);
-            if (n == ws.readers - 1) {  // every reader has seen the count
-                __hip_atomic_store(ws.ready, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(ws.arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
-        __syncthreads();
-    }
-
     // ---- inverse RMS of each batch row (RMS-norm fused into staging)
     float inv_rms[B];
 #pragma unroll
@@ -421,37 +377,8 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
     }
 
     // ---- stage x[b][t_beg*256 ...) into LDS (zero past K)
-    if constexpr (XM == kCoherent) {
-        // x was written by other workgroups of this launch: device-scope
-        // dword loads, consecutive lanes on consecutive dwords (coalesced)
-        for (int e = tid; e < B * 4 * F; e += kThreads) {
-            const int b = e / (4 * F);
-            const int kk = e - b * 4 * F;
-            const int64_t k = k0 + kk;
-            float v = 0.f;
-            if (k < K) v = __hip_atomic_load(a.x + (int64_t)b * K + k, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-            xl[b * xstride + xphys(kk)] = v;
-        }
-        if constexpr (FMT == kQ4K) {
-            __syncthreads();
-            for (int e = tid; e < B * 8 * a.nk; e += kThreads) {
-                const int b = e / (8 * a.nk);
-                const int j = e - b * 8 * a.nk;  // 32-run index
-                const float *q = xl + b * xstride + xphys(32 * j);
-                float sacc = 0.f;
-#pragma unroll
-                for (int m = 0; m < 8; m++) {
-                    const float4 w4 = *reinterpret_cast<const float4 *>(q + 4 * m);
-                    sacc += (w4.x + w4.y) + (w4.z + w4.w);
-                }
-                xsum[b * sstride + j] = sacc;
-            }
-        }
-    } else {
-        // normalise (if asked) and store one float4 of x; for Q4_K also the
-        // sum of each 32-run (8 consecutive float4 sit in 8 consecutive
-        // lanes of one wave, and every lane of a wave takes part)
+    {
+        // normalise (if asked) and store one float4 of x
         auto stage_one = [&](int f, float4 v, float4 w) {
             const int b = f / F;
             const int f4 = f - b * F;
@@ -466,13 +393,6 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
                 v.w = v.w * ir * w.w;
             }
             *reinterpret_cast<float4 *>(xl + b * xstride + xphys(4 * f4)) = v;
-            if constexpr (FMT == kQ4K) {
-                float sm = (v.x + v.y) + (v.z + v.w);
-                sm += __shfl_xor(sm, 1);
-                sm += __shfl_xor(sm, 2);
-                sm += __shfl_xor(sm, 4);
-                if ((tid & 7) == 0) xsum[b * sstride + (f4 >> 3)] = sm;
-            }
         };
         if (early) {
 #pragma unroll
@@ -497,11 +417,11 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
     __syncthreads();
 
     // ---- main loop over this group's units
-    float acc[NR][B], acc2[NR][B];
+    float acc[NR][B];
 #pragma unroll
     for (int i = 0; i < NR; i++)
 #pragma unroll
-        for (int b = 0; b < B; b++) { acc[i][b] = 0.f; acc2[i][b] = 0.f; }
+        for (int b = 0; b < B; b++) acc[i][b] = 0.f;
 
     Q4Lane L4;
     if constexpr (FMT == kQ4K) L4 = q4k_lane(c);
@@ -517,10 +437,8 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
         for (int i = 0; i < NR; i++)
 #pragma unroll
             for (int b = 0; b < B; b++) {
-                if constexpr (FMT == kQ4K) v[i][b] = fmaf(acc[i][b], fp8_inv_unit(), -acc2[i][b]);
-                else v[i][b] = acc[i][b];
+                v[i][b] = acc[i][b];
                 acc[i][b] = 0.f;
-                acc2[i][b] = 0.f;
             }
         for (int off = 1; off < 4 * p_in; off <<= 1) {
 #pragma unroll
@@ -538,7 +456,7 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
 #pragma unroll
                     for (int b = 0; b < B; b++) {
                         const float gv = v[0][b], uv = v[1][b];
-                        store_out<YM>(a.y + (int64_t)b * N + row[0], act_apply(a.act, gv) * uv);
+                        store_out(a.y + (int64_t)b * N + row[0], act_apply(a.act, gv) * uv);
                         if (a.g_out) a.g_out[(int64_t)b * N + row[0]] = gv;
                         if (a.u_out) a.u_out[(int64_t)b * N + row[0]] = uv;
                     }
@@ -551,20 +469,17 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
                         for (int b = 0; b < B; b++) {
                             const int64_t o = (int64_t)b * N + row[i];
                             const float vv = a.coef ? a.coef[ks] * v[i][b] : v[i][b];
-                            store_out<YM>(a.y + o, a.res ? vv + a.res[o] : vv);
+                            if (a.pn.w1) a.pn.p[o] = vv;  // the row epilogue forms y
+                            else store_out(a.y + o, a.res ? vv + a.res[o] : vv);
                         }
             }
         } else {
-            // partials are written with device-scope stores (write-through,
-            // no cache-wide writeback needed before the counter below)
 #pragma unroll
             for (int i = 0; i < NR; i++)
                 if (row[i] < N)
 #pragma unroll
                     for (int b = 0; b < B; b++)
-                        __hip_atomic_store(
-                            a.partials + (((int64_t)ks * B + b) * NP + (FFN ? i : 0)) * N + row[i],
-                            v[i][b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        a.partials[(((int64_t)ks * B + b) * NP + (FFN ? i : 0)) * N + row[i]] = v[i][b];
         }
     };
 
@@ -585,8 +500,7 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
             const int tlo = min(t0 + uc * p_in, t_end - 1) - t_beg;  // dead units: zero weights
             if constexpr (FMT == kQ4K) {
                 const float *xp = xl + xphys(kSuper * tlo + 64 * c);
-                const float *sp = xsum + 8 * tlo + 2 * c;
-                q4k_step<NR, B>(buf[s], xp, xstride, sp, sstride, L4, acc, acc2);
+                q4k_step<NR, B>(buf[s], xp, xstride, L4, acc);
             } else if constexpr (FMT == kQ6K) {
                 const int h = c >> 1, j = c & 1;
                 const int base = kSuper * tlo + 128 * h + 16 * j;
@@ -602,23 +516,15 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
             }
         }
     }
-    if (p_out == 1) return;
+    __shared__ int s_last;
+    if (p_out == 1) {
+        if (!FFN && a.pn.w1) post_norm_tail<kThreads>(a.pn, a.y, B, N, red, &s_last);
+        return;
+    }
 
     // ---- split-K: the last workgroup of this row tile sums the partials in
-    // slice order.  Each wave waits until its partial stores have completed,
-    // the workgroup synchronises, and only then bumps the tile's counter with
-    // a device-scope atomic.
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);  // keep the stores above the wait
-    __builtin_amdgcn_s_waitcnt(0);            // this wave's stores are complete
-    __syncthreads();
-    __shared__ int s_last;
-    if (tid == 0) {
-        unsigned prev = __hip_atomic_fetch_add(a.counters + bx, 1u, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (prev == (unsigned)p_out - 1) ? 1 : 0;
-    }
-    __syncthreads();
-    if (!s_last) return;
+    // slice order (release / acquire on the tile's counter, qd_epilogue.h)
+    if (!arrive_last<kThreads>(a.counters + bx, (unsigned)p_out, &s_last)) return;
     const int rows_here = (FFN ? RS : RS * NR) * rpg;
     const int64_t tile0 = (int64_t)bx * rows_here;
     for (int e = tid; e < rows_here * B; e += kThreads) {
@@ -628,70 +534,28 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
         float s0 = 0.f, s1 = 0.f;
         for (int k = 0; k < p_out; k++) {
             const float *p = a.partials + (((int64_t)k * B + b) * NP) * N + r;
-            const float pv = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            s0 = a.coef ? fmaf(a.coef[k], pv, s0) : s0 + pv;
-            if constexpr (FFN) s1 += __hip_atomic_load(p + N, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s0 = a.coef ? fmaf(a.coef[k], p[0], s0) : s0 + p[0];
+            if constexpr (FFN) s1 += p[N];
         }
         if constexpr (FFN) {
-            store_out<YM>(a.y + (int64_t)b * N + r, act_apply(a.act, s0) * s1);
+            store_out(a.y + (int64_t)b * N + r, act_apply(a.act, s0) * s1);
             if (a.g_out) a.g_out[(int64_t)b * N + r] = s0;
             if (a.u_out) a.u_out[(int64_t)b * N + r] = s1;
         } else {
             const int64_t o = (int64_t)b * N + r;
-            store_out<YM>(a.y + o, a.res ? s0 + a.res[o] : s0);
+            if (a.pn.w1) a.pn.p[o] = s0;
+            else store_out(a.y + o, a.res ? s0 + a.res[o] : s0);
         }
     }
     if (tid == 0)  // ready for the next call
         __hip_atomic_store(a.counters + bx, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!FFN && a.pn.w1) post_norm_tail<kThreads>(a.pn, a.y, B, N, red, &s_last);
 }
 
 template <int FMT, int B, int NR, bool FFN>
 __global__ __launch_bounds__(kThreads) void mv_kernel(MvArgs a) {
     extern __shared__ __attribute__((aligned(16))) float smem[];
-    mv_tile<FMT, B, NR, FFN, kPlain, kPlain>(a, blockIdx.x, blockIdx.y, gridDim.y, smem);
-}
-
-// ------------------------------------------------------ fused decode FFN ---
-// One launch for y = Wd (act(Wg xn) * (Wu xn)).  Workgroups [0, nA) are
-// gate/up row tiles (phase A): they publish their slice of h with
-// device-scope stores and count themselves done in the h-slice they belong
-// to.  The remaining workgroups are down-projection tiles (phase B), ordered
-// slice by slice: each issues its first weight loads, waits until every
-// phase-A tile of its h-slice is done, stages that slice of h with
-// device-scope loads and runs as a split-K GEMV tile.  Workgroups are
-// dispatched in index order on each XCD, so every phase-A workgroup is
-// resident or finished before a phase-B workgroup can hold a slot on the
-// same XCD: a waiting workgroup only waits on work that is already running
-// (and the wait is bounded).  Counters live on separate 128-byte lines; the
-// last phase-B reader of a slice resets them for the next launch.
-constexpr int kCtlStride = 32;  // unsigned per counter (one 128-byte line)
-
-template <int FA, int FB, int B>
-__global__ __launch_bounds__(kThreads) void ffn_kernel(FfnArgs f) {
-    extern __shared__ __attribute__((aligned(16))) float smem[];
-    const int t = (int)blockIdx.x;
-    if (t < f.nA) {
-        mv_tile<FA, B, 2, true, kPlain, kCoherent>(f.a, t, 0, 1, smem);
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);  // keep the h stores above the wait
-        __builtin_amdgcn_s_waitcnt(0);            // this wave's h stores are complete
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            const int slice = (t * f.rowsA) / f.sliceRows;
-            __hip_atomic_fetch_add(f.ctl + (2 * slice) * kCtlStride, 1u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        }
-    } else {
-        const int j = t - f.nA;
-        const int ks = j / f.nBx;
-        const int bx = j - ks * f.nBx;
-        const int per = f.sliceRows / f.rowsA;  // phase-A tiles per h-slice
-        WaitSpec ws;
-        ws.ready = f.ctl + (2 * ks) * kCtlStride;
-        ws.target = (unsigned)(min(f.nA, (ks + 1) * per) - ks * per);
-        ws.arrived = f.ctl + (2 * ks + 1) * kCtlStride;
-        ws.readers = (unsigned)f.nBx;
-        mv_tile<FB, B, 1, false, kCoherent, kPlain>(f.b, bx, ks, f.pB, smem, ws);
-    }
+    mv_tile<FMT, B, NR, FFN>(a, blockIdx.x, blockIdx.y, gridDim.y, smem);
 }
 
 // ------------------------------------------- mixture-of-experts decode ---
@@ -726,10 +590,10 @@ __global__ __launch_bounds__(kThreads) void moe_kernel(MvArgs a) {
                 if (r0 + r < a.N) b.y[r0 + r] = 0.f;
             return;
         }
-        mv_tile<FMT, 1, 2, true, kPlain, kPlain>(b, blockIdx.x, 0, 1, smem);
+        mv_tile<FMT, 1, 2, true>(b, blockIdx.x, 0, 1, smem);
     } else {
         b.x = a.x + (int64_t)slot * a.x_sstride;
-        mv_tile<FMT, 1, 1, false, kPlain, kPlain>(b, blockIdx.x, slot, gridDim.y, smem);
+        mv_tile<FMT, 1, 1, false>(b, blockIdx.x, slot, gridDim.y, smem);
     }
 }
 
@@ -777,9 +641,9 @@ __global__ __launch_bounds__(kThreads) void qkv_kernel(QkvArgs q) {
     }
     const MvArgs &a = q.a[s];
     switch (q.fmt[s]) {
-    case kQ4K: mv_tile<kQ4K, B, 1, false, kPlain, kPlain>(a, t, 0, 1, smem); break;
-    case kQ6K: mv_tile<kQ6K, B, 1, false, kPlain, kPlain>(a, t, 0, 1, smem); break;
-    default: mv_tile<kQ80, B, 1, false, kPlain, kPlain>(a, t, 0, 1, smem); break;
+    case kQ4K: mv_tile<kQ4K, B, 1, false>(a, t, 0, 1, smem); break;
+    case kQ6K: mv_tile<kQ6K, B, 1, false>(a, t, 0, 1, smem); break;
+    default: mv_tile<kQ80, B, 1, false>(a, t, 0, 1, smem); break;
     }
 }
 
@@ -800,7 +664,6 @@ hipError_t launch_qkv(const QkvArgs &q, int batch, size_t lds, hipStream_t st) {
 // ------------------------------------------------------------ launchers ---
 size_t mv_lds_bytes(int fmt, int batch, int nk) {
     size_t floats = (size_t)batch * nk * kSuperPhys;
-    if (fmt == kQ4K) floats += (size_t)batch * nk * 8;
     floats += 4 * 8;  // cross-wave scratch: [4 waves][batch]
     return floats * sizeof(float);
 }
@@ -832,36 +695,6 @@ static hipError_t launch_f(const MvArgs &a, int batch, bool ffn, int nr, dim3 gr
     case 8: return launch_fb<FMT, 8>(a, ffn, nr, grid, st);
     default: return hipErrorInvalidValue;
     }
-}
-
-template <int FA, int FB>
-static hipError_t launch_ffn_f(const FfnArgs &f, int batch, size_t lds, unsigned grid,
-                               hipStream_t st) {
-#define QD_FFN(Bv)                                                                       \
-    case Bv:                                                                             \
-        hipLaunchKernelGGL((ffn_kernel<FA, FB, Bv>), dim3(grid), dim3(kThreads), lds, st, f); \
-        break;
-    switch (batch) {
-        QD_FFN(1) QD_FFN(2) QD_FFN(3) QD_FFN(4) QD_FFN(5) QD_FFN(6) QD_FFN(7) QD_FFN(8)
-    default: return hipErrorInvalidValue;
-    }
-#undef QD_FFN
-    return hipGetLastError();
-}
-
-bool ffn_fused_supported(int fmt_a, int fmt_b) {
-    return (fmt_a == kQ4K && (fmt_b == kQ6K || fmt_b == kQ4K)) || (fmt_a == kQ80 && fmt_b == kQ80);
-}
-
-hipError_t launch_ffn(int fmt_a, int fmt_b, int batch, FfnArgs f, hipStream_t st) {
-    f.a.p_out = 1;
-    const size_t lds = std::max(mv_lds_bytes(fmt_a, batch, f.a.nk), mv_lds_bytes(fmt_b, batch, f.b.nk));
-    const unsigned grid = (unsigned)(f.nA + f.nBx * f.pB);
-    if ((size_t)f.pB * 2 * kCtlStride > (size_t)kFfnCtlWords) return hipErrorInvalidValue;
-    if (fmt_a == kQ4K && fmt_b == kQ6K) return launch_ffn_f<kQ4K, kQ6K>(f, batch, lds, grid, st);
-    if (fmt_a == kQ4K && fmt_b == kQ4K) return launch_ffn_f<kQ4K, kQ4K>(f, batch, lds, grid, st);
-    if (fmt_a == kQ80 && fmt_b == kQ80) return launch_ffn_f<kQ80, kQ80>(f, batch, lds, grid, st);
-    return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemv(int fmt, int batch, bool ffn, MvArgs a, Shape s, hipStream_t st) {

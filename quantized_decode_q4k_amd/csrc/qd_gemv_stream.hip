@@ -10,19 +10,21 @@
 //    counts differ by at most one).  A row range is one contiguous byte
 //    range of the matrix, so the workgroup's weights are a single stream.
 //  * The stream is cut into steps of 16 superunits (256 weights each: one
-//    Q4_K or Q6_K block, eight Q8_0 blocks).  Wave w takes steps w, w+4, ...
-//    and copies each into a ring of its own in LDS with
-//    global_load_lds_dwordx4: 1 KB of consecutive bytes per instruction, no
-//    registers, several steps in flight while it decodes an earlier one.
+//    Q4_K or Q6_K block, eight Q8_0 blocks).  Copying waves put the steps
+//    into a ring in LDS with global_load_lds_dwordx4 (1 KB of consecutive
+//    bytes per instruction, no registers), several steps in flight;
+//    decoding waves take them out of the ring as they land.
 //  * Decoding reads a lane group's block (4 lanes per superunit, the lane
 //    split of the GEMV kernels) and its activations from LDS, and writes the
 //    superunit's partial sum to LDS.  After the stream, each row's partials
 //    are added in superunit order, so a result does not depend on the launch
 //    shape.
 //  * x is copied into LDS the same way (16-byte skew every 64 floats), then
-//    RMS-normalised in place; Q4_K also keeps the sum of every 32-run of x.
+//    multiplied by the RMS-norm weight in place; the inverse RMS is applied
+//    to each row's sum at the end.
 // The copies are ordered by explicit waits (qd_lds.h).
 #include "qd_decode.h"
+#include "qd_epilogue.h"
 #include "qd_lds.h"
 
 namespace qd {
@@ -127,44 +129,45 @@ QD_DEV void lds_q80(RawQ80 &r, const uint8_t *blk, int c) {
 // xv: this lane's 64 activations (in the lane's own order, see each format)
 // for each batch row; result: this lane's share of w . x per row stream.
 
-// Q4_K: xv[0..7] low run (64c + 0..31), xv[8..15] high run; X: sums of x
-// over sub-blocks 2c and 2c+1.
+// Q4_K: xv[0..7] low run (64c + 0..31), xv[8..15] high run.  Each weight is
+// formed on its own with one fused multiply-add of its sub-block's scale
+// and min (exact factors, one rounding), then multiplied by its activation.
 template <int NR, int B>
-QD_DEV void dot_q4k(const RawQ4K (&r)[NR], const float4 (&xv)[B][16], const float2 (&X)[B],
-                    const Q4Lane &L, float (&out)[NR][B]) {
-    const float inv_unit = fp8_inv_unit();  // exact power of two
+QD_DEV void dot_q4k(const RawQ4K (&r)[NR], const float4 (&xv)[B][16], const Q4Lane &L, float (&out)[NR][B]) {
 #pragma unroll
     for (int i = 0; i < NR; i++) {
+        const Q4Scales s = q4k_scales(r[i], L);
+        const float a0 = (s.d * s.sc0) * fp8_inv_unit(), a1 = (s.d * s.sc1) * fp8_inv_unit();
+        const float b0 = -(s.dmin * s.m0), b1 = -(s.dmin * s.m1);
         float alo[B], ahi[B];
 #pragma unroll
         for (int b = 0; b < B; b++) { alo[b] = 0.f; ahi[b] = 0.f; }
 #pragma unroll
         for (int dw = 0; dw < 8; dw++) {
             const Q4Nibbles n = q4k_nibbles(r[i].q[dw]);
+            const float l0 = fmaf(n.lo01.x, a0, b0), l1 = fmaf(n.lo01.y, a0, b0);
+            const float l2 = fmaf(n.lo23.x, a0, b0), l3 = fmaf(n.lo23.y, a0, b0);
+            const float h0 = fmaf(n.hi01.x, a1, b1), h1 = fmaf(n.hi01.y, a1, b1);
+            const float h2 = fmaf(n.hi23.x, a1, b1), h3 = fmaf(n.hi23.y, a1, b1);
 #pragma unroll
             for (int b = 0; b < B; b++) {
                 const float4 xl = xv[b][dw], xh = xv[b][8 + dw];
-                float s = alo[b];
-                s = fmaf(n.lo01.x, xl.x, s);
-                s = fmaf(n.lo01.y, xl.y, s);
-                s = fmaf(n.lo23.x, xl.z, s);
-                s = fmaf(n.lo23.y, xl.w, s);
-                alo[b] = s;
+                float t = alo[b];
+                t = fmaf(l0, xl.x, t);
+                t = fmaf(l1, xl.y, t);
+                t = fmaf(l2, xl.z, t);
+                t = fmaf(l3, xl.w, t);
+                alo[b] = t;
                 float u = ahi[b];
-                u = fmaf(n.hi01.x, xh.x, u);
-                u = fmaf(n.hi01.y, xh.y, u);
-                u = fmaf(n.hi23.x, xh.z, u);
-                u = fmaf(n.hi23.y, xh.w, u);
+                u = fmaf(h0, xh.x, u);
+                u = fmaf(h1, xh.y, u);
+                u = fmaf(h2, xh.z, u);
+                u = fmaf(h3, xh.w, u);
                 ahi[b] = u;
             }
         }
-        const Q4Scales s = q4k_scales(r[i], L);
 #pragma unroll
-        for (int b = 0; b < B; b++) {
-            const float q = s.d * fmaf(s.sc1, ahi[b], s.sc0 * alo[b]);
-            const float m = s.dmin * fmaf(s.m1, X[b].y, s.m0 * X[b].x);
-            out[i][b] = fmaf(q, inv_unit, -m);
-        }
+        for (int b = 0; b < B; b++) out[i][b] = alo[b] + ahi[b];
     }
 }
 
@@ -251,14 +254,13 @@ template <int FMT, int B, int NR>
 struct StepRegs {
     typename RawOf<FMT>::T raw[NR];
     float4 xv[B][16];
-    float2 X[B];  // Q4_K: sums of x over the lane's two sub-blocks
 };
 
 // blk0: the lane group's superunit in row stream 0 (stream m is m * mstride
 // bytes further); su: its superunit index within the row.
 template <int FMT, int B, int NR>
 QD_DEV void read_step(StepRegs<FMT, B, NR> &st, const uint8_t *blk0, int mstride, const float *xl,
-                      const float *xs, int xstride, int nb, int su, int c) {
+                      int xstride, int su, int c) {
 #pragma unroll
     for (int m = 0; m < NR; m++) {
         const uint8_t *blk = blk0 + m * mstride;
@@ -282,228 +284,14 @@ QD_DEV void read_step(StepRegs<FMT, B, NR> &st, const uint8_t *blk0, int mstride
 #pragma unroll
             for (int n = 0; n < 16; n++) st.xv[b][n] = xp[n];
         }
-        if constexpr (FMT == kQ4K)
-            st.X[b] = *reinterpret_cast<const float2 *>(xs + b * nb * 8 + 8 * su + 2 * c);
-        else
-            st.X[b] = make_float2(0.f, 0.f);
     }
 }
 
 template <int FMT, int B, int NR>
 QD_DEV void dot_step(const StepRegs<FMT, B, NR> &st, const Q4Lane &L4, int c, float (&v)[NR][B]) {
-    if constexpr (FMT == kQ4K) dot_q4k<NR, B>(st.raw, st.xv, st.X, L4, v);
+    if constexpr (FMT == kQ4K) dot_q4k<NR, B>(st.raw, st.xv, L4, v);
     else if constexpr (FMT == kQ6K) dot_q6k<NR, B>(st.raw, st.xv, c & 1, v);
     else dot_q80<NR, B>(st.raw, st.xv, v);
-}
-
-// ------------------------------------------------------------ kernel ---
-template <int FMT, int B, int NR, bool FFN>
-__global__ __launch_bounds__(kThreads) void stream_kernel(StreamArgs a) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    constexpr int UB = StreamFmt<FMT>::UB;
-    constexpr int NCH = StreamFmt<FMT>::NCH;
-    constexpr int NI = copies_per_step<FMT>();
-    constexpr int SLOTM = NCH * 16;  // bytes of one matrix's step in a slot
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int c = lane & 3, g = lane >> 2;
-    const int64_t N = a.N, K = a.K;
-    const int nb = a.nb;
-    const int PD = a.pd;
-
-    // rows of this workgroup
-    const int wg = blockIdx.x;
-    const int64_t r0 = (int64_t)wg * a.rows_base + min(wg, a.rows_extra);
-    const int cnt = a.rows_base + (wg < a.rows_extra ? 1 : 0);
-    const int U = cnt * nb;                                   // superunits per matrix
-    const int S = (U + kStepUnits - 1) / kStepUnits;          // steps
-    const int nw = S > w ? (S - w + kWaves - 1) / kWaves : 0; // steps of this wave
-
-    // LDS layout
-    uint8_t *ring = smem + w * PD * NR * SLOTM;
-    float *xl = reinterpret_cast<float *>(smem + a.off_x);
-    float *xs = reinterpret_cast<float *>(smem + a.off_xsum);
-    const float *nwl = reinterpret_cast<const float *>(smem + a.off_nw);
-    float *part = reinterpret_cast<float *>(smem + a.off_part);
-    float *red = reinterpret_cast<float *>(smem + a.off_red);
-    const int xstride = nb * kSuperPhys;  // floats per staged batch row
-
-    // byte stream of this workgroup's rows, per matrix; a step is copied
-    // from the 16-byte boundary at or below its first byte
-    const int64_t wbeg = r0 * a.row_bytes;
-    const int off0 = (int)(wbeg & 15);
-    const uint8_t *mats[NR];
-    mats[0] = a.W0;
-    if constexpr (NR == 2) mats[1] = a.W1;
-    const int64_t last16 = a.mat_bytes - 16;  // last 16-byte chunk of a matrix
-
-    auto issue = [&](int i, int slot) {
-        // copies of this wave's i-th step (step w + 4 i) into ring slot `slot`
-        const int step = w + kWaves * i;
-        const int64_t a0 = ((wbeg + (int64_t)step * kStepUnits * UB) & ~(int64_t)15);
-#pragma unroll
-        for (int m = 0; m < NR; m++) {
-            const uint32_t dst = lds_addr(ring + (slot * NR + m) * SLOTM);
-#pragma unroll
-            for (int j = 0; j < NI; j++) {
-                const int64_t off = min(a0 + 16 * (int64_t)(64 * j + lane), last16);
-                if (j < NI - 1 || lane < NCH - 64 * (NI - 1))
-                    lds_copy16(mats[m] + off, dst + 1024 * j);
-            }
-        }
-    };
-
-    // ---- x into LDS: physical float p of batch row b holds logical
-    // k = unskew(p); pad floats receive a harmless copy of x[0]
-    const int xf4 = B * nb * (kSuperPhys / 4);  // float4 slots
-    for (int f0 = w * 64; f0 < xf4; f0 += kThreads) {
-        const int f = f0 + lane;
-        const int b = f / (nb * (kSuperPhys / 4));
-        const int p = 4 * (f - b * (nb * (kSuperPhys / 4)));  // physical float in the row
-        const int t = p / kSuperPhys, q = p - t * kSuperPhys;
-        const int run = q / 68, e = q - run * 68;
-        const int64_t k = (int64_t)t * kSuper + run * 64 + e;
-        const int64_t so = (e < 64 && k < K && f < xf4) ? (int64_t)b * K + k : 0;
-        if (f0 + 64 <= xf4 || lane < xf4 - f0) lds_copy16(a.x + so, lds_addr(xl + 4 * f0));
-    }
-    // ---- the norm weight (K floats, unskewed) the same way
-    const bool norm = a.norm_w != nullptr;
-    if (norm) {
-        const int nf4 = (int)(K / 4);
-        for (int f0 = w * 64; f0 < nf4; f0 += kThreads)
-            if (f0 + 64 <= nf4 || lane < nf4 - f0)
-                lds_copy16(a.norm_w + 4 * (int64_t)(f0 + lane), lds_addr(nwl + 4 * f0));
-    }
-
-    // ---- the first steps of the weight stream (at most PD in flight)
-    const int pro = min(PD, nw);
-    for (int i = 0; i < pro; i++) issue(i, i);
-
-    // ---- x (and the norm weight) landed: this wave's copies, then every wave's
-    vm_wait_n(pro * NR * NI);
-    block_sync();
-
-    // ---- RMS-normalise in place; Q4_K: sums of every 32-run
-    const int F = nb * (kSuper / 4);  // logical float4 per batch row
-    if (norm) {
-        float ss[B];
-#pragma unroll
-        for (int b = 0; b < B; b++) ss[b] = 0.f;
-        for (int f = tid; f < B * F; f += kThreads) {
-            const int b = f / F;
-            const int k = 4 * (f - b * F);
-            const float4 v = *reinterpret_cast<const float4 *>(xl + b * xstride + xphys(k));
-            float sq = fmaf(v.x, v.x, 0.f);
-            sq = fmaf(v.y, v.y, sq);
-            sq = fmaf(v.z, v.z, sq);
-            sq = fmaf(v.w, v.w, sq);
-#pragma unroll
-            for (int bb = 0; bb < B; bb++)
-                if (bb == b) ss[bb] += sq;
-        }
-#pragma unroll
-        for (int b = 0; b < B; b++) {
-            const float t = wave_total(ss[b]);
-            if (lane == 0) red[w * B + b] = t;
-        }
-        block_sync();
-        float inv_rms[B];
-#pragma unroll
-        for (int b = 0; b < B; b++) {
-            const float sq = (red[b] + red[B + b]) + (red[2 * B + b] + red[3 * B + b]);
-            inv_rms[b] = 1.0f / sqrtf(sq / (float)K + a.eps);
-        }
-        for (int f = tid; f < B * F; f += kThreads) {
-            const int b = f / F;
-            const int k = 4 * (f - b * F);
-            float4 *ad = reinterpret_cast<float4 *>(xl + b * xstride + xphys(k));
-            float4 v = *ad;
-            const float4 nw4 = *reinterpret_cast<const float4 *>(nwl + k);
-            float ir = inv_rms[0];
-#pragma unroll
-            for (int bb = 1; bb < B; bb++)
-                if (bb == b) ir = inv_rms[bb];
-            v.x = v.x * ir * nw4.x;
-            v.y = v.y * ir * nw4.y;
-            v.z = v.z * ir * nw4.z;
-            v.w = v.w * ir * nw4.w;
-            *ad = v;
-        }
-        block_sync();
-    }
-    if constexpr (FMT == kQ4K) {
-        // lanes 8m..8m+7 hold the 8 float4 of one 32-run: F is a multiple of 64
-        for (int f = tid; f < B * F; f += kThreads) {
-            const int b = f / F;
-            const int k = 4 * (f - b * F);
-            const float4 v = *reinterpret_cast<const float4 *>(xl + b * xstride + xphys(k));
-            const float sm = oct_sum((v.x + v.y) + (v.z + v.w));
-            if ((lane & 7) == 0) xs[b * nb * 8 + (k >> 5)] = sm;
-        }
-        block_sync();
-    }
-
-    // ---- the stream
-    const int Umax = a.units_max;
-    Q4Lane L4;
-    if constexpr (FMT == kQ4K) L4 = q4k_lane(c);
-    for (int i = 0; i < nw; i++) {
-        const int slot = i % PD;
-        // step i's copies are in LDS: the steps issued after it (at most
-        // PD - 1, fewer at the end of the stream) may still be in flight
-        vm_wait_n(min(PD - 1, nw - 1 - i) * NR * NI);
-        const int step = w + kWaves * i;
-        const int u = step * kStepUnits + g;  // this group's superunit
-        const bool live = u < U;
-        const int uu = live ? u : U - 1;
-        const int lr = uu / nb;
-        const int su = uu - lr * nb;
-        const uint8_t *blk0 = ring + slot * NR * SLOTM + off0 + g * UB;
-
-        StepRegs<FMT, B, NR> st;
-        read_step<FMT, B, NR>(st, blk0, SLOTM, xl, xs, xstride, nb, su, c);
-        // every read of this slot is complete before the slot is refilled
-        // with step i + PD, which streams in while this one is decoded
-        lgkm_wait();
-        if (i + PD < nw) issue(i + PD, slot);
-
-        float v[NR][B];
-        dot_step<FMT, B, NR>(st, L4, c, v);
-#pragma unroll
-        for (int m = 0; m < NR; m++)
-#pragma unroll
-            for (int b = 0; b < B; b++) {
-                const float t = quad_sum(v[m][b]);
-                if (c == 0 && live) part[(m * B + b) * Umax + u] = t;
-            }
-    }
-    vm_wait<0>();
-    block_sync();
-
-    // ---- rows: partials in superunit order
-    for (int e = tid; e < cnt * B; e += kThreads) {
-        const int b = e / cnt;
-        const int lr = e - b * cnt;
-        const int64_t row = r0 + lr;
-        float sr[NR];
-#pragma unroll
-        for (int m = 0; m < NR; m++) {
-            const float *pp = part + (m * B + b) * Umax + lr * nb;
-            float acc = 0.f;
-            for (int t = 0; t < nb; t++) acc += pp[t];
-            sr[m] = acc;
-        }
-        if constexpr (FFN) {
-            a.y[(int64_t)b * N + row] = act_apply(a.act, sr[0]) * sr[1];
-            if (a.g_out) a.g_out[(int64_t)b * N + row] = sr[0];
-            if (a.u_out) a.u_out[(int64_t)b * N + row] = sr[1];
-        } else {
-            const int64_t o = (int64_t)b * N + row;
-            a.y[o] = a.res ? sr[0] + a.res[o] : sr[0];
-        }
-    }
 }
 
 // ------------------------------------------------ producer / consumer ---
@@ -563,7 +351,6 @@ __global__ __launch_bounds__(64 * (NC + kPcMaxProducers)) void stream_pc_kernel(
 
     uint8_t *ring = smem;
     float *xl = reinterpret_cast<float *>(smem + a.off_x);
-    float *xs = reinterpret_cast<float *>(smem + a.off_xsum);
     float *nwl = reinterpret_cast<float *>(smem + a.off_nw);
     float *part = reinterpret_cast<float *>(smem + a.off_part);
     int *ready = reinterpret_cast<int *>(smem + a.off_red);
@@ -708,11 +495,6 @@ __global__ __launch_bounds__(64 * (NC + kPcMaxProducers)) void stream_pc_kernel(
                 v.w *= nw4.w;
                 *ad = v;
             }
-            if constexpr (FMT == kQ4K) {
-                // lanes 8m .. 8m+7 hold the 8 float4 of one 32-run
-                const float sm = oct_sum((v.x + v.y) + (v.z + v.w));
-                if ((lane & 7) == 0) xs[b * nb * 8 + (k >> 5)] = sm;
-            }
         }
         if (norm) {
 #pragma unroll
@@ -745,8 +527,7 @@ __global__ __launch_bounds__(64 * (NC + kPcMaxProducers)) void stream_pc_kernel(
             const int su = uu - lr * nb;
             lds_wait_eq(&ready[slot], j);
             StepRegs<FMT, B, NR> st;
-            read_step<FMT, B, NR>(st, ring + slot * NR * SLOTM + off0 + g * UB, SLOTM, xl, xs, xstride,
-                                  nb, su, c);
+            read_step<FMT, B, NR>(st, ring + slot * NR * SLOTM + off0 + g * UB, SLOTM, xl, xstride, su, c);
             lgkm_wait();  // the slot may be refilled from here on
             if (lane == 0) lds_flag(&done[wv], ++nread);
             float v[NR][B];
@@ -784,412 +565,18 @@ __global__ __launch_bounds__(64 * (NC + kPcMaxProducers)) void stream_pc_kernel(
             if (a.u_out) a.u_out[(int64_t)b * N + row] = sr[1];
         } else {
             const int64_t o = (int64_t)b * N + row;
-            a.y[o] = a.res ? sr[0] + a.res[o] : sr[0];
+            if (a.pn.w1) a.pn.p[o] = sr[0];  // the row epilogue forms y
+            else a.y[o] = a.res ? sr[0] + a.res[o] : sr[0];
         }
     }
-}
-
-// ------------------------------------------------ shared stream pieces ---
-// Copies of one step (16 superunits of each of NR row streams) into LDS at
-// dst (stream m at dst + m * SLOTM), from the 16-byte boundary a0 of the
-// workgroup's byte stream.  `whole`: the step lies inside the matrix, so the
-// copies are issued from a scalar base and a per-lane offset; otherwise each
-// lane's source is clamped to the matrix's last 16 bytes.
-template <int NI, int NCH, int SLOTM, int NR>
-QD_DEV void issue_step(const uint8_t *W0, const uint8_t *W1, int64_t a0, bool whole, int64_t mat_bytes,
-                       uint32_t dst, int lane, bool tail_lane) {
-    if (whole) {
-#pragma unroll
-        for (int m = 0; m < NR; m++) {
-            const uint8_t *sp = (m == 0 ? W0 : W1) + a0;
-#pragma unroll
-            for (int q = 0; q < NI; q++)
-                if (q < NI - 1 || tail_lane)
-                    lds_copy16_s(sp, 16u * (uint32_t)lane + 1024u * (uint32_t)q, dst + m * SLOTM + 1024 * q);
-        }
-    } else {
-        const int64_t last16 = mat_bytes - 16;
-#pragma unroll
-        for (int m = 0; m < NR; m++)
-#pragma unroll
-            for (int q = 0; q < NI; q++) {
-                const int64_t off = min(a0 + 16 * (int64_t)(64 * q + lane), last16);
-                if (q < NI - 1 || tail_lane) lds_copy16((m == 0 ? W0 : W1) + off, dst + m * SLOTM + 1024 * q);
-            }
-    }
-}
-
-// This wave's share (copies wv, wv + NC, ...) of copying one activation row
-// of K floats into the skewed LDS layout (physical float4 q of the row holds
-// logical float4 16 * (q / 17) + q % 17; pad float4 receive a copy of x[0]),
-// and of the norm weight (K floats, unskewed) when nwsrc is not null.  COH:
-// device-scope loads.  Returns when this wave's copies have landed.
-template <int NC, bool COH>
-QD_DEV void copy_x_share(const float *x, int64_t K, int nb, float *xl, const float *nwsrc, float *nwl, int wv,
-                         int lane) {
-    const int nq = nb * (kSuperPhys / 4);
-    const int xc = (nq + 63) / 64;
-    const int nf4 = nwsrc ? (int)(K / 4) : 0;
-    const int total = xc + (nf4 + 63) / 64;
-    int n = 0;
-    for (int i = wv; i < total; i += NC) {
-        if (i < xc) {
-            const int q0 = 64 * i;
-            const int q = q0 + lane;
-            const int run = q / 17, e = q - 17 * run;
-            const float *srcp = (e < 16 && q < nq) ? x + 4 * (16 * run + e) : x;
-            if (q0 + 64 <= nq || lane < nq - q0) {
-                if constexpr (COH) lds_copy16_coh(srcp, lds_addr(xl + 4 * q0));
-                else lds_copy16(srcp, lds_addr(xl + 4 * q0));
-            }
-        } else {
-            const int f0 = 64 * (i - xc);
-            if (f0 + 64 <= nf4 || lane < nf4 - f0) lds_copy16(nwsrc + 4 * (int64_t)(f0 + lane), lds_addr(nwl + 4 * f0));
-        }
-        if (++n == 48) {
-            vm_wait<16>();
-            n = 16;
-        }
-    }
-    vm_wait<0>();
-}
-
-// This wave's share (64-float4 slices wv, wv + NC, ...) of staging one
-// activation row in place: x * w_norm when nwl is not null, and for Q4_K
-// the sum of every 32-run into xs.  Returns the wave's sum of squares of x
-// (0 without a norm weight); every lane takes part.
-template <int FMT, int NC>
-QD_DEV float stage_x_share(float *xl, float *xs, const float *nwl, int nb, int wv, int lane) {
-    float ss = 0.f;
-    for (int it = wv; it < nb; it += NC) {  // nb slices of 64 float4 per row
-        const int k = 4 * (64 * it + lane);
-        float4 *ad = reinterpret_cast<float4 *>(xl + xphys(k));
-        float4 v = *ad;
-        if (nwl) {
-            float sq = fmaf(v.x, v.x, 0.f);
-            sq = fmaf(v.y, v.y, sq);
-            sq = fmaf(v.z, v.z, sq);
-            sq = fmaf(v.w, v.w, sq);
-            ss += sq;
-            const float4 nw4 = *reinterpret_cast<const float4 *>(nwl + k);
-            v.x *= nw4.x;
-            v.y *= nw4.y;
-            v.z *= nw4.z;
-            v.w *= nw4.w;
-            *ad = v;
-        }
-        if constexpr (FMT == kQ4K) {
-            const float sm = oct_sum((v.x + v.y) + (v.z + v.w));
-            if ((lane & 7) == 0) xs[k >> 5] = sm;
-        }
-    }
-    return nwl ? wave_total(ss) : 0.f;
-}
-
-// ------------------------------------------------- one-launch decode FFN ---
-// h = act(Wg x') * (Wu x') with x' = RMS-norm(x), then y = Wd h, batch 1, in
-// one launch of one workgroup per CU, built from the producer / consumer
-// kernel above.  Phase A (gate/up) and phase B (down) each own a ring; the
-// copying waves stream phase A's steps and then phase B's without a break,
-// so the down weights stream in while gate/up is still being decoded.
-// Between the phases:
-//   * the decoding waves of a workgroup sum their gate/up rows, apply the
-//     activation and store their h rows with device-scope stores;
-//   * the workgroup then arrives at a grid barrier (a device-scope counter
-//     that the last arriver resets, and a generation word it advances); the
-//     wait is bounded (about 50 ms), so a grid that is not all resident at
-//     once ends with wrong numbers instead of hanging;
-//   * the decoding waves copy h (device-scope loads) into the LDS that
-//     phase A's ring and x used, and decode phase B's steps.
-// A copying wave never waits for a free slot while one of its issued steps
-// is still unpublished (it publishes instead), so it cannot hold up the
-// steps the decoding waves need; phase A's steps come first in its order,
-// so every workgroup finishes phase A whatever phase B's ring holds.
-constexpr int kFfnSpinLimit = 1 << 20;
-
-template <int FA, int FB, int NC>
-__global__ __launch_bounds__(64 * (NC + 2)) void ffn_pc_kernel(FfnStreamArgs a) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    constexpr int UBA = StreamFmt<FA>::UB, NCHA = StreamFmt<FA>::NCH;
-    constexpr int NIA = copies_per_step<FA>(), SLOTA = NCHA * 16, CPSA = 2 * NIA;
-    constexpr int UBB = StreamFmt<FB>::UB, NCHB = StreamFmt<FB>::NCH;
-    constexpr int NIB = copies_per_step<FB>(), SLOTB = NCHB * 16, CPSB = NIB;
-    constexpr int NP = 2;  // copying waves
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int c = lane & 3, g = lane >> 2;
-    const int wg = blockIdx.x;
-    const int G = gridDim.x;
-
-    // rows of this workgroup in each phase
-    const int64_t rA0 = (int64_t)wg * a.rowsA_base + min(wg, a.rowsA_extra);
-    const int cntA = a.rowsA_base + (wg < a.rowsA_extra ? 1 : 0);
-    const int UA = cntA * a.nbA;
-    const int SA = (UA + kStepUnits - 1) / kStepUnits;
-    const int64_t rB0 = (int64_t)wg * a.rowsB_base + min(wg, a.rowsB_extra);
-    const int cntB = a.rowsB_base + (wg < a.rowsB_extra ? 1 : 0);
-    const int UB_ = cntB * a.nbB;
-    const int SB = (UB_ + kStepUnits - 1) / kStepUnits;
-    const int RA = a.slotsA, RB = a.slotsB;
-
-    uint8_t *ringA = smem + a.off_ringA;
-    uint8_t *ringB = smem + a.off_ringB;
-    float *xA = reinterpret_cast<float *>(smem + a.off_xA);
-    float *xsA = reinterpret_cast<float *>(smem + a.off_xsA);
-    float *nwA = reinterpret_cast<float *>(smem + a.off_nwA);
-    float *xB = reinterpret_cast<float *>(smem + a.off_xB);
-    float *xsB = reinterpret_cast<float *>(smem + a.off_xsB);
-    float *partA = reinterpret_cast<float *>(smem + a.off_partA);
-    float *partB = reinterpret_cast<float *>(smem + a.off_partB);
-    int *readyA = reinterpret_cast<int *>(smem + a.off_flags);
-    int *readyB = readyA + RA;
-    int *doneA = readyB + RB;     // [NC]
-    int *doneB = doneA + NC;      // [NC]
-    int *cnt = doneB + NC;        // counters below
-    int *landed = cnt + 0, *staged = cnt + 1, *adone = cnt + 2, *hdone = cnt + 3;
-    int *hready = cnt + 4, *bland = cnt + 5, *bstaged = cnt + 6, *bdone = cnt + 7;
-    float *ssq = reinterpret_cast<float *>(cnt + 8);  // [NC]
-    const int nflags = RA + RB + 2 * NC + 8;
-    const int xstrideA = a.nbA * kSuperPhys, xstrideB = a.nbB * kSuperPhys;
-    const int64_t wbegA = rA0 * a.row_bytesA, wbegB = rB0 * a.row_bytesB;
-    const bool norm = a.norm_w != nullptr;
-
-    for (int i = tid; i < nflags; i += 64 * (NC + 2)) readyA[i] = i < RA + RB ? -1 : 0;
-    block_sync();
-
-    if (wv >= NC) {
-        // ---------------------------------------------------- producers ---
-        const int p = wv - NC;
-        __builtin_amdgcn_s_setprio(3);
-        lds_wait_eq(landed, NC);
-        const int nkA = SA > p ? (SA - p + NP - 1) / NP : 0;
-        const int nkB = SB > p ? (SB - p + NP - 1) / NP : 0;
-        const int nk = nkA + nkB;
-        const int64_t baseA = wbegA & ~(int64_t)15, baseB = wbegB & ~(int64_t)15;
-        const int64_t safeA = a.mat_bytesA - (int64_t)NCHA * 16, safeB = a.mat_bytesB - (int64_t)NCHB * 16;
-        const bool tailA = lane < NCHA - 64 * (NIA - 1), tailB = lane < NCHB - 64 * (NIB - 1);
-        int k = 0, kp = 0;
-        int slotA = p, pslotA = p, slotB = p, pslotB = p;
-        int freedA = 0, freedB = 0;
-        auto smallest = [&](const int *done) {
-            int m = 0x7fffffff;
-            for (int cc = p; cc < NC; cc += NP) m = min(m, lds_poll(&done[cc]));
-            return m;
-        };
-        while (kp < nk) {
-            bool issued = false;
-            if (k < nk && k - kp < a.lag) {
-                const bool isA = k < nkA;
-                const int j = isA ? p + NP * k : p + NP * (k - nkA);
-                const int R = isA ? RA : RB;
-                int &freed = isA ? freedA : freedB;
-                bool wait = j >= R && j - R >= NC * freed;
-                if (wait) {
-                    freed = smallest(isA ? doneA : doneB);
-                    wait = j - R >= NC * freed;
-                }
-                if (wait && k == kp) {
-                    // nothing unpublished: wait for the slot
-                    while (wait) {
-                        __builtin_amdgcn_s_sleep(1);
-                        freed = smallest(isA ? doneA : doneB);
-                        wait = j - R >= NC * freed;
-                    }
-                }
-                if (!wait) {
-                    asm volatile("" ::: "memory");
-                    if (isA) {
-                        const uint32_t dst = lds_addr(ringA + slotA * 2 * SLOTA);
-                        const int64_t a0 = baseA + (int64_t)j * kStepUnits * UBA;
-                        issue_step<NIA, NCHA, SLOTA, 2>(a.Wg, a.Wu, a0, a0 <= safeA, a.mat_bytesA, dst, lane, tailA);
-                        slotA += NP;
-                        if (slotA >= RA) slotA -= RA;
-                    } else {
-                        const uint32_t dst = lds_addr(ringB + slotB * SLOTB);
-                        const int64_t a0 = baseB + (int64_t)j * kStepUnits * UBB;
-                        issue_step<NIB, NCHB, SLOTB, 1>(a.Wd, nullptr, a0, a0 <= safeB, a.mat_bytesB, dst, lane, tailB);
-                        slotB += NP;
-                        if (slotB >= RB) slotB -= RB;
-                    }
-                    k++;
-                    issued = true;
-                }
-            }
-            if (!issued) {
-                // publish own step kp: it has landed once the copies of the
-                // steps issued after it are all that is outstanding
-                const int nA = max(0, min(k, nkA) - (kp + 1));
-                const int nB = max(0, k - max(kp + 1, nkA));
-                vm_wait_n(nA * CPSA + nB * CPSB);
-                if (kp < nkA) {
-                    if (lane == 0) lds_flag(&readyA[pslotA], p + NP * kp);
-                    pslotA += NP;
-                    if (pslotA >= RA) pslotA -= RA;
-                } else {
-                    if (lane == 0) lds_flag(&readyB[pslotB], p + NP * (kp - nkA));
-                    pslotB += NP;
-                    if (pslotB >= RB) pslotB -= RB;
-                }
-                kp++;
-            }
-        }
-        return;
-    }
-
-    // -------------------------------------------------------- consumers ---
-    Q4Lane L4;
-    L4 = q4k_lane(c);
-    // phase A: x and the norm weight
-    copy_x_share<NC, false>(a.x, a.KA, a.nbA, xA, norm ? a.norm_w : nullptr, nwA, wv, lane);
-    if (lane == 0) lds_add(landed, 1);
-    lds_wait_eq(landed, NC);
-    {
-        const float ss = stage_x_share<FA, NC>(xA, xsA, norm ? nwA : nullptr, a.nbA, wv, lane);
-        if (lane == 0) ssq[wv] = ss;
-        lgkm_wait();
-        if (lane == 0) lds_add(staged, 1);
-        lds_wait_eq(staged, NC);
-    }
-    float rinv = 1.0f;
-    if (norm) {
-        float t = 0.f;
-        for (int w = 0; w < NC; w++) t += ssq[w];
-        rinv = 1.0f / sqrtf(t / (float)a.KA + a.eps);
-    }
-    {
-        const int off0 = (int)(wbegA & 15);
-        int slot = wv % RA, nread = 0;
-        const int sstep = NC % RA;
-        for (int j = wv; j < SA; j += NC) {
-            const int u = j * kStepUnits + g;
-            const bool live = u < UA;
-            const int uu = live ? u : UA - 1;
-            const int su = uu - (uu / a.nbA) * a.nbA;
-            lds_wait_eq(&readyA[slot], j);
-            StepRegs<FA, 1, 2> st;
-            read_step<FA, 1, 2>(st, ringA + slot * 2 * SLOTA + off0 + g * UBA, SLOTA, xA, xsA, xstrideA, a.nbA,
-                                su, c);
-            lgkm_wait();
-            if (lane == 0) lds_flag(&doneA[wv], ++nread);
-            float v[2][1];
-            dot_step<FA, 1, 2>(st, L4, c, v);
-#pragma unroll
-            for (int m = 0; m < 2; m++) {
-                const float t = quad_sum(v[m][0]);
-                if (c == 0 && live) partA[m * a.unitsA_max + u] = t;
-            }
-            slot += sstep;
-            if (slot >= RA) slot -= RA;
-        }
-    }
-    lgkm_wait();
-    if (lane == 0) lds_add(adone, 1);
-    lds_wait_eq(adone, NC);
-    // h rows of this workgroup (device-scope stores, then counted)
-    for (int lr = wv * 64 + lane; lr < cntA; lr += NC * 64) {
-        const float *pg = partA + lr * a.nbA, *pu = partA + a.unitsA_max + lr * a.nbA;
-        float sg = 0.f, su_ = 0.f;
-        for (int t = 0; t < a.nbA; t++) {
-            sg += pg[t];
-            su_ += pu[t];
-        }
-        sg *= rinv;
-        su_ *= rinv;
-        __hip_atomic_store(a.h + rA0 + lr, act_apply(a.act, sg) * su_, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    }
-    vm_wait<0>();
-    if (lane == 0) lds_add(hdone, 1);
-    if (wv == 0) {
-        lds_wait_eq(hdone, NC);
-        if (lane == 0) {
-            // h is already at device scope (device-scope stores, waited for),
-            // so the barrier's own accesses are relaxed device-scope atomics:
-            // a fence per poll would write back and invalidate caches on
-            // every one of them
-            unsigned *arrived = a.bar, *gen = a.bar + 32;
-            const unsigned g0 = __hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // g0 read before arriving
-            const unsigned n = __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (n == (unsigned)G - 1) {
-                __hip_atomic_store(arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // reset before the generation moves
-                __hip_atomic_fetch_add(gen, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            } else {
-                for (int it = 0; it < kFfnSpinLimit; it++) {
-                    if (__hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != g0) break;
-                    __builtin_amdgcn_s_sleep(2);
-                }
-            }
-            lds_flag(hready, 1);
-        }
-    }
-    lds_wait_eq(hready, 1);
-    // phase B: h into the LDS that phase A's ring and x used
-    copy_x_share<NC, true>(a.h, a.KB, a.nbB, xB, nullptr, nullptr, wv, lane);
-    if (lane == 0) lds_add(bland, 1);
-    lds_wait_eq(bland, NC);
-    if constexpr (FB == kQ4K) {
-        (void)stage_x_share<FB, NC>(xB, xsB, nullptr, a.nbB, wv, lane);
-        lgkm_wait();
-        if (lane == 0) lds_add(bstaged, 1);
-        lds_wait_eq(bstaged, NC);
-    }
-    {
-        const int off0 = (int)(wbegB & 15);
-        int slot = wv % RB, nread = 0;
-        const int sstep = NC % RB;
-        for (int j = wv; j < SB; j += NC) {
-            const int u = j * kStepUnits + g;
-            const bool live = u < UB_;
-            const int uu = live ? u : UB_ - 1;
-            const int su = uu - (uu / a.nbB) * a.nbB;
-            lds_wait_eq(&readyB[slot], j);
-            StepRegs<FB, 1, 1> st;
-            read_step<FB, 1, 1>(st, ringB + slot * SLOTB + off0 + g * UBB, SLOTB, xB, xsB, xstrideB, a.nbB, su, c);
-            lgkm_wait();
-            if (lane == 0) lds_flag(&doneB[wv], ++nread);
-            float v[1][1];
-            dot_step<FB, 1, 1>(st, L4, c, v);
-            const float t = quad_sum(v[0][0]);
-            if (c == 0 && live) partB[u] = t;
-            slot += sstep;
-            if (slot >= RB) slot -= RB;
-        }
-    }
-    lgkm_wait();
-    if (lane == 0) lds_add(bdone, 1);
-    lds_wait_eq(bdone, NC);
-    for (int lr = wv * 64 + lane; lr < cntB; lr += NC * 64) {
-        const float *pp = partB + lr * a.nbB;
-        float acc = 0.f;
-        for (int t = 0; t < a.nbB; t++) acc += pp[t];
-        a.y[rB0 + lr] = a.res ? acc + a.res[rB0 + lr] : acc;
+    if constexpr (!FFN) {
+        // the ring (offset 0) is free once every step has been decoded
+        if (a.pn.w1)
+            post_norm_tail<NT>(a.pn, a.y, B, N, reinterpret_cast<float *>(smem), reinterpret_cast<int *>(smem + 64));
     }
 }
 
 }  // namespace
-
-// LDS bytes and layout of one workgroup; 0 if it does not fit.
-size_t stream_layout(int fmt, int batch, bool ffn, int nb, int units_max, int pd, StreamArgs *a) {
-    const int NR = ffn ? 2 : 1;
-    int nch = fmt == kQ4K ? StreamFmt<kQ4K>::NCH : fmt == kQ6K ? StreamFmt<kQ6K>::NCH
-                                                                : StreamFmt<kQ80>::NCH;
-    size_t off = (size_t)kWaves * pd * NR * nch * 16;
-    a->off_x = (int)off;
-    off += (size_t)batch * nb * kSuperPhys * 4;
-    a->off_xsum = (int)off;
-    if (fmt == kQ4K) off += (size_t)batch * nb * 8 * 4;
-    a->off_nw = (int)off;
-    if (a->norm_w) off += (size_t)nb * kSuper * 4;
-    a->off_part = (int)off;
-    off += (size_t)NR * batch * units_max * 4;
-    a->off_red = (int)off;
-    off += 16 * 4;
-    return off;
-}
 
 // LDS layout of the producer / consumer kernel with `slots` ring slots; returns
 // the bytes used.
@@ -1201,8 +588,6 @@ size_t stream_pc_layout(int fmt, int batch, bool ffn, int nb, int units_max, int
     size_t off = (size_t)slots * NR * nch * 16;
     a->off_x = (int)off;
     off += (size_t)batch * nb * kSuperPhys * 4;
-    a->off_xsum = (int)off;
-    if (fmt == kQ4K) off += (size_t)batch * nb * 8 * 4;
     a->off_nw = (int)off;
     if (a->norm_w) off += (size_t)nb * kSuper * 4;
     a->off_part = (int)off;
@@ -1246,15 +631,7 @@ static hipError_t launch_sb(const StreamArgs &a, bool ffn, unsigned grid, size_t
         return ffn ? launch_pc<FMT, B, true, 4>(a, grid, lds, st) : launch_pc<FMT, B, false, 4>(a, grid, lds, st);
     if (a.consumers == 8)
         return ffn ? launch_pc<FMT, B, true, 8>(a, grid, lds, st) : launch_pc<FMT, B, false, 8>(a, grid, lds, st);
-    if (a.consumers != 0) return hipErrorInvalidValue;
-    if (ffn) {
-        if (allow_lds<stream_kernel<FMT, B, 2, true>>() != hipSuccess) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((stream_kernel<FMT, B, 2, true>), dim3(grid), dim3(kThreads), lds, st, a);
-    } else {
-        if (allow_lds<stream_kernel<FMT, B, 1, false>>() != hipSuccess) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((stream_kernel<FMT, B, 1, false>), dim3(grid), dim3(kThreads), lds, st, a);
-    }
-    return hipGetLastError();
+    return hipErrorInvalidValue;
 }
 
 template <int FMT>
@@ -1277,76 +654,5 @@ hipError_t launch_stream(int fmt, int batch, bool ffn, const StreamArgs &a, unsi
     }
 }
 
-
-// ------------------------------------------------ one-launch decode FFN ---
-template <int FA, int FB>
-static hipError_t launch_ffn_pc_fb(const FfnStreamArgs &a, unsigned grid, size_t lds, hipStream_t st) {
-    if (allow_lds<ffn_pc_kernel<FA, FB, 8>>() != hipSuccess) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((ffn_pc_kernel<FA, FB, 8>), dim3(grid), dim3(64 * (8 + 2)), lds, st, a);
-    return hipGetLastError();
-}
-
-template <int FA>
-static hipError_t launch_ffn_pc_fa(int fmt_b, const FfnStreamArgs &a, unsigned grid, size_t lds, hipStream_t st) {
-    switch (fmt_b) {
-    case kQ4K: return launch_ffn_pc_fb<FA, kQ4K>(a, grid, lds, st);
-    case kQ6K: return launch_ffn_pc_fb<FA, kQ6K>(a, grid, lds, st);
-    case kQ80: return launch_ffn_pc_fb<FA, kQ80>(a, grid, lds, st);
-    default: return hipErrorInvalidValue;
-    }
-}
-
-hipError_t launch_ffn_stream(int fmt_a, int fmt_b, const FfnStreamArgs &a, unsigned grid, size_t lds,
-                             hipStream_t st) {
-    switch (fmt_a) {
-    case kQ4K: return launch_ffn_pc_fa<kQ4K>(fmt_b, a, grid, lds, st);
-    case kQ6K: return launch_ffn_pc_fa<kQ6K>(fmt_b, a, grid, lds, st);
-    case kQ80: return launch_ffn_pc_fa<kQ80>(fmt_b, a, grid, lds, st);
-    default: return hipErrorInvalidValue;
-    }
-}
-
-static int nch_of(int fmt) {
-    return fmt == kQ4K ? StreamFmt<kQ4K>::NCH : fmt == kQ6K ? StreamFmt<kQ6K>::NCH : StreamFmt<kQ80>::NCH;
-}
-
-// LDS layout of the one-launch FFN (8 decoding waves): phase B's ring, then
-// the region phase A's ring, x, run sums and norm weight share with phase
-// B's h and run sums, then the partials and the flags.  Returns the bytes
-// used.
-size_t ffn_stream_layout(int fmt_a, int fmt_b, bool norm, int slotsA, int slotsB, FfnStreamArgs *a) {
-    constexpr int NC = 8;
-    size_t off = 0;
-    a->off_ringB = 0;
-    off += (size_t)slotsB * nch_of(fmt_b) * 16;
-    const size_t region = off;
-    a->off_ringA = (int)off;
-    size_t ra = (size_t)slotsA * 2 * nch_of(fmt_a) * 16;
-    a->off_xA = (int)(region + ra);
-    ra += (size_t)a->nbA * kSuperPhys * 4;
-    a->off_xsA = (int)(region + ra);
-    ra += (size_t)a->nbA * 8 * 4;
-    a->off_nwA = (int)(region + ra);
-    if (norm) ra += (size_t)a->nbA * kSuper * 4;
-    size_t rb = 0;
-    a->off_xB = (int)region;
-    rb += (size_t)a->nbB * kSuperPhys * 4;
-    a->off_xsB = (int)(region + rb);
-    rb += (size_t)a->nbB * 8 * 4;
-    off = region + std::max(ra, rb);
-    a->off_partA = (int)off;
-    off += (size_t)2 * a->unitsA_max * 4;
-    a->off_partB = (int)off;
-    off += (size_t)a->unitsB_max * 4;
-    off = (off + 15) & ~(size_t)15;
-    a->off_flags = (int)off;
-    off += (size_t)(slotsA + slotsB + 2 * NC + 8 + NC) * 4;
-    return (off + 15) & ~(size_t)15;
-}
-
-int ffn_stream_copies(int fmt_a, int fmt_b) {
-    const int cpa = 2 * ((nch_of(fmt_a) + 63) / 64), cpb = (nch_of(fmt_b) + 63) / 64;
-    return cpa > cpb ? cpa : cpb;
-}
 
 }  // namespace qd

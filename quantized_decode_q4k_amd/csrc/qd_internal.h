@@ -16,6 +16,19 @@ constexpr int kThreads = 256;            // threads per workgroup (4 waves)
 constexpr int kGroups = kThreads / 4;    // lane groups per workgroup
 constexpr int kLdsBudgetBytes = 65536 - 1024;  // dynamic LDS per workgroup (two fit on a CU)
 
+// Row epilogue of a GEMV (qd_epilogue.h): y = r + RMSNorm(p; w1) and
+// optionally y2 = RMSNorm(y; w2), formed by the last workgroup to finish.
+struct PostNorm {
+    const float *w1 = nullptr;  // post-norm weight [N]; nullptr = no epilogue
+    const float *w2 = nullptr;  // next-norm weight [N] or nullptr
+    const float *r = nullptr;   // residual [batch][N] (may be the output)
+    float *y2 = nullptr;        // [batch][N] when w2 is given
+    float *p = nullptr;         // workspace [batch][N]: the projection
+    unsigned *ctr = nullptr;    // completed row tiles (zero between launches)
+    unsigned tiles = 0;         // row tiles of the launch
+    float eps = 0.f;
+};
+
 // Arguments of the GEMV / fused gate-up kernels.
 struct MvArgs {
     const uint8_t *W0;      // row stream 0: the matrix (GEMV) or gate (FFN)
@@ -48,6 +61,7 @@ struct MvArgs {
     const float *coef;
     int64_t w_estride, x_sstride, y_sstride;
     int n_experts;
+    PostNorm pn;            // GEMV row epilogue (pn.w1 = nullptr: none)
 };
 
 struct Shape {
@@ -95,22 +109,6 @@ struct QkvArgs {
 };
 hipError_t launch_qkv(const QkvArgs &q, int batch, size_t lds, hipStream_t st);
 
-// Fused decode FFN (qd_gemv.hip): phase A = gate/up/act tiles writing h,
-// phase B = down-projection split-K tiles reading h.
-struct FfnArgs {
-    MvArgs a;           // phase A: W0 = gate, W1 = up, x, norm_w, y = h
-    MvArgs b;           // phase B: W0 = down, x = h, y = out, partials, counters
-    unsigned *ctl;      // per h-slice s: phase-A tiles done, phase-B readers (one line each)
-    int nA;             // phase-A tiles
-    int nBx;            // phase-B row tiles
-    int pB;             // phase-B K-slices
-    int rowsA;          // h rows per phase-A tile
-    int sliceRows;      // h rows per phase-B K-slice (multiple of 256)
-};
-constexpr int kFfnCtlWords = 4096;  // control words the fused FFN may use
-bool ffn_fused_supported(int fmt_a, int fmt_b);
-hipError_t launch_ffn(int fmt_a, int fmt_b, int batch, FfnArgs f, hipStream_t st);
-
 // Dequantisers (qd_dequant.hip).
 hipError_t launch_dequant(int fmt, const uint8_t *W, float *out, uint16_t *out_bf16,
                           int64_t N, int64_t K, hipStream_t st);
@@ -130,48 +128,20 @@ struct StreamArgs {
     int nb;                 // superunits per row (K / 256)
     int rows_base, rows_extra;  // workgroup i owns rows_base + (i < rows_extra) rows
     int units_max;          // (rows_base + (rows_extra > 0)) * nb
-    int pd;                 // ring depth (steps in flight per wave)
-    int consumers;          // 0: every wave copies and decodes; 4 or 8: decoding
-                            // waves of the producer / consumer kernel
-    int producers;          // producer / consumer: copying waves (1 or 2)
-    int slots;              // producer / consumer: ring slots (steps)
-    int lag;                // producer / consumer: steps in flight per copying wave
-    int off_x, off_xsum, off_nw, off_part, off_red;  // LDS layout (bytes)
+    int consumers;          // decoding waves (4 or 8)
+    int producers;          // copying waves (1, 2 or 4)
+    int slots;              // ring slots (steps)
+    int lag;                // steps in flight per copying wave
+    int off_x, off_nw, off_part, off_red;  // LDS layout (bytes)
     int act;
     float eps;
+    PostNorm pn;            // GEMV row epilogue (pn.w1 = nullptr: none)
 };
-size_t stream_layout(int fmt, int batch, bool ffn, int nb, int units_max, int pd, StreamArgs *a);
 size_t stream_pc_layout(int fmt, int batch, bool ffn, int nb, int units_max, int slots,
                         StreamArgs *a);
 int stream_copies_per_step(int fmt, bool ffn);
 hipError_t launch_stream(int fmt, int batch, bool ffn, const StreamArgs &a, unsigned grid,
                          size_t lds, hipStream_t st);
-
-// One-launch decode FFN on the producer / consumer stream (qd_gemv_stream.hip),
-// batch 1: phase A = gate/up (NA = N_ff rows of KA = hidden), phase B = down
-// (NB = hidden rows of KB = N_ff), one workgroup per CU.
-struct FfnStreamArgs {
-    const uint8_t *Wg, *Wu, *Wd;
-    const float *x;         // [KA]
-    const float *norm_w;    // [KA] or nullptr
-    float *h;               // [NA]: device-scope stores in phase A, loads in phase B
-    float *y;               // [NB]
-    const float *res;       // optional [NB] added to y (may equal y)
-    unsigned *bar;          // grid barrier: [0] arrivals, [32] generation (zero-initialised)
-    int64_t KA, KB;
-    int64_t row_bytesA, row_bytesB, mat_bytesA, mat_bytesB;
-    int nbA, nbB;
-    int rowsA_base, rowsA_extra, rowsB_base, rowsB_extra;
-    int unitsA_max, unitsB_max;
-    int slotsA, slotsB, lag;
-    int off_ringA, off_ringB, off_xA, off_xsA, off_nwA, off_xB, off_xsB, off_partA, off_partB, off_flags;
-    int act;
-    float eps;
-};
-size_t ffn_stream_layout(int fmt_a, int fmt_b, bool norm, int slotsA, int slotsB, FfnStreamArgs *a);
-int ffn_stream_copies(int fmt_a, int fmt_b);
-hipError_t launch_ffn_stream(int fmt_a, int fmt_b, const FfnStreamArgs &a, unsigned grid, size_t lds,
-                             hipStream_t st);
 
 // Prefill GEMM (qd_prefill.hip).  A workgroup owns 32*tm tokens by 256
 // output columns (plain: 256 weight rows; FFN: 128 rows of gate and of up)

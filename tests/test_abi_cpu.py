@@ -267,26 +267,51 @@ def test_gemm_override_validation():
 def test_stream_override_validation():
     _, L = _lib()
     assert L.qd_set_stream_override(9, 0, 0, 0) == 1      # workgroups per CU 1..8
-    assert L.qd_set_stream_override(1, 1, 1, 0) == 1      # depth 0 or >= 2 per copying-and-decoding wave
-    assert L.qd_set_stream_override(1, 0, 3, 0) == 1      # decoding waves 1, 4 or 8
-    assert L.qd_set_stream_override(1, 9, 1, 0) == 1      # depth <= 8 per copying-and-decoding wave
+    assert L.qd_set_stream_override(1, 0, 3, 0) == 1      # decoding waves 4 or 8
+    assert L.qd_set_stream_override(1, 0, 1, 0) == 1
     assert L.qd_set_stream_override(1, 33, 4, 0) == 1     # depth <= 32 per copying wave
     assert L.qd_set_stream_override(1, 0, 4, 3) == 1      # one, two or four copying waves
     assert L.qd_set_stream_override(1, 0, 8, 8) == 1
     assert L.qd_set_stream_override(1, 0, 8, 4) == 0
-    assert L.qd_set_stream_override(1, 0, 1, 2) == 1      # copying waves only with decoding waves
     assert L.qd_set_stream_override(1, 1, 8, 1) == 0
     assert L.qd_set_stream_override(1, 16, 8, 2) == 0
-    assert L.qd_set_stream_override(2, 3, 1, 0) == 0
+    assert L.qd_set_stream_override(2, 3, 0, 0) == 0
     assert L.qd_set_stream_override(0, 0, 0, 0) == 0
 
 
-def test_ffn_mode_validation():
+def _q8plan(L, N, K, batch):
+    import ctypes
+    out = (ctypes.c_int32 * 4)()
+    st = L.qd_plan_q8act(N, K, batch, out)
+    return st, tuple(out)
+
+
+def test_q8act_plan_terminates_and_fits_lds():
+    """The int8-activation GEMV's launch plan, on the host only: large legal K
+    (up to the 2^24 the shape check accepts, and around the K at which one
+    column's codes stop fitting a workgroup's LDS) gives a plan whose staged
+    K-slice fits 63 KB of LDS, whose slices cover K, and every slice is
+    non-empty.  An earlier plan loop never ended for some of these K."""
     _, L = _lib()
-    assert L.qd_set_ffn_mode(3) == 1
-    assert L.qd_set_ffn_mode(-1) == 1
-    assert L.qd_set_ffn_mode(2) == 0
-    assert L.qd_set_ffn_mode(0) == 0
+    budget = 65536 - 1024
+    cases = [(4, 1 << 24, 1), (4, 12959776, 1), (4, 12000000, 1), (64, 57344, 1), (64, 57344 + 32, 1),
+             (64, 57344 + 256, 1), (64, 65536, 1), (300, 57344 + 32, 8), (262144, 2560, 1),
+             (2560, 10240, 8), (5376, 21504, 3), (1, 32, 1)]
+    for N, K, batch in cases:
+        st, (p, ks, su_per, chunk) = _q8plan(L, N, K, batch)
+        assert st == 0, (N, K, batch)
+        nsu = (K // 32 + 7) // 8
+        assert ks >= 1 and su_per >= 1 and p in (1, 2, 4, 8, 16), (N, K, batch)
+        assert (ks - 1) * su_per < nsu <= ks * su_per, (N, K, batch, ks, su_per)
+        kslice = min(K, su_per * 256)
+        assert chunk >= 1, (N, K, batch)
+        lds = (chunk * kslice + 15) // 16 * 16 + chunk * (kslice // 32) * 4
+        assert lds <= budget, (N, K, batch, lds)
+    # more row tiles than the split-K counters cover: unsupported, not a hang
+    st, (_, _, _, chunk) = _q8plan(L, 300000 * 64, 57344 + 32, 1)
+    assert st == 0 and chunk == 0
+    assert _q8plan(L, 4, 48, 1)[0] == 2
+    assert L.qd_plan_q8act(4, 256, 1, None) == 1
 
 
 def test_launch_override_validation():

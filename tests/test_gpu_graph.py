@@ -124,3 +124,49 @@ def test_graph_int8_activations(qd):
     y, y2 = torch.empty((8, N), device="cuda"), torch.empty((8, N), device="cuda")
     check_replays("qgemv_q8_0_q8act", lambda: qd.qgemv_q8_0_q8act(W, x, y), [y],
                   lambda: qd.qgemv_q8_0_q8act(W, x2, y2))
+
+
+def test_capture_without_workspace_returns_status(qd):
+    """A call made while its stream is capturing, which would have to create
+    the stream's workspace, returns QD_ECAPTURE and enqueues nothing: the
+    capture stays valid, and the graph (holding only the other call, a
+    dequantisation that uses no workspace) replays with correct results.
+    After one uncaptured call on the stream the same call can be captured."""
+    say("capture without workspace")
+    hidden, ff = 512, 1024
+    Wg = dev(synth.quant_weights("q4_k", ff, hidden, SEED, tensor_id=186))
+    Wu = dev(synth.quant_weights("q4_k", ff, hidden, SEED, tensor_id=187))
+    Wd = dev(synth.quant_weights("q6_k", hidden, ff, SEED, tensor_id=188))
+    W = dev(synth.quant_weights("q4_k", 64, hidden, SEED, tensor_id=189))
+    x = dev(synth.normal((1, hidden), SEED, tensor_id=190))
+    w_out = torch.empty((64, hidden), device="cuda")
+    y_ffn = torch.empty((1, hidden), device="cuda")
+    s = torch.cuda.Stream()   # a fresh stream: no workspace yet
+    with torch.cuda.stream(s):
+        ref_w = qd.qdequant("q4_k", W, hidden).clone()
+        s.synchronize()
+        g = torch.cuda.CUDAGraph()
+        status = None
+        with torch.cuda.graph(g, stream=s):
+            try:
+                qd.qffn_decode("q4_k", Wg, Wu, "q6_k", Wd, x, None, 1e-6, "gelu_tanh", y=y_ffn)
+            except qd.QDError as e:
+                status = e.status
+            qd.qdequant("q4_k", W, hidden, out=w_out)
+        assert status == qd.QD_ECAPTURE, status
+        for rep in range(3):
+            w_out.fill_(float("nan"))
+            g.replay()
+            s.synchronize()
+            assert np.array_equal(w_out.cpu().numpy().view(np.uint32), ref_w.cpu().numpy().view(np.uint32))
+        # one uncaptured call creates the workspace; the captured call then works
+        ref_ffn = qd.qffn_decode("q4_k", Wg, Wu, "q6_k", Wd, x, None, 1e-6, "gelu_tanh").clone()
+        s.synchronize()
+        g2 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g2, stream=s):
+            qd.qffn_decode("q4_k", Wg, Wu, "q6_k", Wd, x, None, 1e-6, "gelu_tanh", y=y_ffn)
+        for rep in range(3):
+            y_ffn.fill_(float("nan"))
+            g2.replay()
+            s.synchronize()
+            assert np.array_equal(y_ffn.cpu().numpy().view(np.uint32), ref_ffn.cpu().numpy().view(np.uint32))

@@ -28,8 +28,6 @@ def qd(gpu):
     qd.lib()
     yield qd
     qd.set_launch_override(0, 0, 0)
-    qd.set_ffn_override(0, 0, 0)
-    qd.set_ffn_mode(0)
 
 
 from helpers import dev, say  # noqa: E402
@@ -99,27 +97,18 @@ def test_gate_up_guard_bands(qd, fmt, N, K, batch):
         t.check(f"qffn_gate_up_act {name}")
 
 
-@pytest.mark.parametrize("mode", ["auto", "grid", "single"])
-def test_ffn_decode_guard_bands(qd, mode):
+def test_ffn_decode_guard_bands(qd):
     hidden, ff = 2560, 10240
-    say(f"guard ffn_decode mode={mode}")
+    say("guard ffn_decode")
     Wg = dev(synth.quant_weights("q4_k", ff, hidden, SEED, tensor_id=138))
     Wu = dev(synth.quant_weights("q4_k", ff, hidden, SEED, tensor_id=139))
     Wd = dev(synth.quant_weights("q6_k", hidden, ff, SEED, tensor_id=140))
     x = dev(synth.normal((1, hidden), SEED, tensor_id=141))
     nw = dev(synth.normal((hidden,), SEED, tensor_id=142, mean=1.0, std=0.1))
     y, h = Guarded((1, hidden)), Guarded((1, ff))
-    if mode == "single":
-        qd.set_ffn_override(2, 2, 0)
-    elif mode == "grid":
-        qd.set_ffn_mode(2)
-    try:
-        qd.qffn_decode("q4_k", Wg, Wu, "q6_k", Wd, x, nw, 1e-6, "gelu_tanh", y=y.view, h_out=h.view)
-    finally:
-        qd.set_ffn_override(0, 0, 0)
-        qd.set_ffn_mode(0)
-    y.check(f"qffn_decode y [{mode}]")
-    h.check(f"qffn_decode h [{mode}]")
+    qd.qffn_decode("q4_k", Wg, Wu, "q6_k", Wd, x, nw, 1e-6, "gelu_tanh", y=y.view, h_out=h.view)
+    y.check("qffn_decode y")
+    h.check("qffn_decode h")
 
 
 def test_qkv_and_moe_guard_bands(qd):

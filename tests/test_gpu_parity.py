@@ -265,7 +265,7 @@ def test_gemv_deterministic_and_batch_columns(qd):
 
 # ---------------------------------------------------------------- FFN ---
 
-def check_ffn(qd, fmt_gu, hidden, ff, batch, act, tag, rows=None, with_norm=True, down=True):
+def check_ffn(qd, fmt_gu, hidden, ff, batch, act, tag, with_norm=True, down=True):
     Wg = synth.quant_weights(fmt_gu, ff, hidden, SEED, tensor_id=41)
     Wu = synth.quant_weights(fmt_gu, ff, hidden, SEED, tensor_id=42)
     x = synth.normal((batch, hidden), SEED, tensor_id=43)
@@ -280,29 +280,22 @@ def check_ffn(qd, fmt_gu, hidden, ff, batch, act, tag, rows=None, with_norm=True
     # the oracle takes fp32 x: the normalised x rounded to fp32 (an ulp-level
     # difference from fp64, far inside the bound)
     xn32 = xn.astype(np.float32)
-    r = rows if rows is not None else np.arange(ff)
-    gref, Sg = oracle.gemv(fmt_gu, Wg, xn32, ff, hidden, 0, ff) if rows is None else \
-        _gemv_rows(fmt_gu, Wg, xn32, ff, hidden, r)
-    uref, Su = oracle.gemv(fmt_gu, Wu, xn32, ff, hidden, 0, ff) if rows is None else \
-        _gemv_rows(fmt_gu, Wu, xn32, ff, hidden, r)
-    assert_bound(f"{tag} gate", g, gref, Sg, r)
-    assert_bound(f"{tag} up", u, uref, Su, r)
+    th = oracle.host_threads()
+    g64, Sg = oracle.gemv_threaded(fmt_gu, Wg, xn32, ff, hidden, th)
+    u64, Su = oracle.gemv_threaded(fmt_gu, Wu, xn32, ff, hidden, th)
+    assert_bound(f"{tag} gate", g, g64, Sg)
+    assert_bound(f"{tag} up", u, u64, Su)
     aid = oracle.ACT_GELU_TANH if act == "gelu_tanh" else oracle.ACT_SILU
-    g64, u64 = gref[:, r], uref[:, r]
     href = oracle.act_vec(aid, g64) * u64
-    tol = h_tolerance(g64, u64, Sg[:, r], Su[:, r], aid)
-    err = np.abs(h[:, r] - href)
+    tol = h_tolerance(g64, u64, Sg, Su, aid)
+    err = np.abs(h - href)
     assert (err <= tol).all(), f"{tag} h: worst {np.max(err / tol):.3f} of tolerance"
     if down:
         Wd = synth.quant_weights("q6_k", hidden, ff, SEED, tensor_id=45)
         say(f"ffn {tag} down q6_k {hidden}x{ff} batch={batch}")
         y = qd.qgemv_q6k(dev(Wd), dev(h)).cpu().numpy()
-        yref, Sy = oracle.gemv("q6_k", Wd, h, hidden, ff)
+        yref, Sy = oracle.gemv_threaded("q6_k", Wd, h, hidden, ff, th)
         assert_bound(f"{tag} down", y, yref, Sy)
-
-
-def _gemv_rows(fmt, W, x, N, K, rows):
-    return oracle.gemv_rows(fmt, W, x, N, K, rows)
 
 
 @pytest.mark.parametrize("act", ["gelu_tanh", "silu"])
@@ -358,39 +351,25 @@ def test_config_gemma3_qkv_lm_head(qd, variant):
     say(f"config: {variant} lm_head {fm[3]} {N}x{K}")
     W = synth.quant_weights(fm[3], N, K, SEED, tensor_id=10)
     y = qd.qgemv(fm[3], dev(W), xd).cpu().numpy()
-    rows = np.unique(np.concatenate([np.arange(0, 512), np.arange(N - 512, N),
-                                     np.arange(0, N, 97)]))
-    y64, S = _gemv_rows(fm[3], W, x[None], N, K, rows)
-    assert_bound(f"{variant} lm_head", y, y64[0], S[0], rows)
+    y64, S = oracle.gemv_threaded(fm[3], W, x[None], N, K, oracle.host_threads())
+    assert_bound(f"{variant} lm_head", y, y64[0], S[0])
 
 
 @pytest.mark.parametrize("batch", [1, 8])
 def test_config_gemma4_31b_ffn(qd, batch):
-    rows = np.unique(np.concatenate([np.arange(0, 256), np.arange(21504 - 256, 21504),
-                                     np.arange(0, 21504, 41)]))
-    check_ffn(qd, "q4_k", 5376, 21504, batch, "gelu_tanh", f"gemma4-31b b{batch}", rows=rows)
+    check_ffn(qd, "q4_k", 5376, 21504, batch, "gelu_tanh", f"gemma4-31b b{batch}")
 
 
 # ------------------------------------------------- whole decode FFN (one call) ---
-# Modes: "auto" (the two launches), "grid" the one launch with a grid
-# barrier at batch 1 where the shape allows it, "single" the older one-launch
-# form.  Repetitions alternate two inputs, so an h left over from the
-# previous call cannot pass.
+# Repetitions alternate two inputs, so an h left over from the previous call
+# cannot pass.
 
-def check_ffn_decode(qd, fg, fd, hidden, ff, batch, act, tag, with_h=True, reps=3, mode="auto", rows=None):
-    """qffn_decode against the oracle chain (rows: output rows of y checked)."""
-    if mode == "single":
-        qd.set_ffn_override(2, 2, 0)
-    elif mode == "grid":
-        qd.set_ffn_mode(2)
-    try:
-        _check_ffn_decode(qd, fg, fd, hidden, ff, batch, act, f"{tag} [{mode}]", with_h, reps, rows)
-    finally:
-        qd.set_ffn_override(0, 0, 0)
-        qd.set_ffn_mode(0)
+def check_ffn_decode(qd, fg, fd, hidden, ff, batch, act, tag, with_h=True, reps=3):
+    """qffn_decode against the oracle chain, every output checked."""
+    _check_ffn_decode(qd, fg, fd, hidden, ff, batch, act, tag, with_h, reps)
 
 
-def _check_ffn_decode(qd, fg, fd, hidden, ff, batch, act, tag, with_h, reps, rows):
+def _check_ffn_decode(qd, fg, fd, hidden, ff, batch, act, tag, with_h, reps):
     Wg = synth.quant_weights(fg, ff, hidden, SEED, tensor_id=51)
     Wu = synth.quant_weights(fg, ff, hidden, SEED, tensor_id=52)
     Wd = synth.quant_weights(fd, hidden, ff, SEED, tensor_id=53)
@@ -400,8 +379,8 @@ def _check_ffn_decode(qd, fg, fd, hidden, ff, batch, act, tag, with_h, reps, row
     refs = []
     for x in xs:
         xn32 = oracle.rmsnorm(x, nw, 1e-6).astype(np.float32)
-        g64, Sg = oracle.gemv(fg, Wg, xn32, ff, hidden)
-        u64, Su = oracle.gemv(fg, Wu, xn32, ff, hidden)
+        g64, Sg = oracle.gemv_threaded(fg, Wg, xn32, ff, hidden, oracle.host_threads())
+        u64, Su = oracle.gemv_threaded(fg, Wu, xn32, ff, hidden, oracle.host_threads())
         refs.append((oracle.act_vec(aid, g64) * u64, h_tolerance(g64, u64, Sg, Su, aid)))
     dW = [dev(a) for a in (Wg, Wu, Wd, nw)]
     dx = [dev(x) for x in xs]
@@ -418,12 +397,8 @@ def _check_ffn_decode(qd, fg, fd, hidden, ff, batch, act, tag, with_h, reps, row
             hh = h.cpu().numpy()
             err = np.abs(hh - href)
             assert (err <= tol).all(), f"{tag} h: worst {np.max(err / tol):.3f} of tolerance"
-            if rows is None:
-                yref, Sy = oracle.gemv(fd, Wd, hh, hidden, ff)
-                assert_bound(f"{tag} y", y, yref, Sy)
-            else:
-                yref, Sy = _gemv_rows(fd, Wd, hh, hidden, ff, rows)
-                assert_bound(f"{tag} y", y, yref, Sy, rows)
+            yref, Sy = oracle.gemv_threaded(fd, Wd, hh, hidden, ff, oracle.host_threads())
+            assert_bound(f"{tag} y", y, yref, Sy)
         else:
             # y against the all-oracle chain: the bound of the down GEMV on the
             # exact h, widened by the h tolerance carried through |Wd|
@@ -443,33 +418,24 @@ def _check_ffn_decode(qd, fg, fd, hidden, ff, batch, act, tag, with_h, reps, row
     ("q4_k", "q6_k", "gelu_tanh", 1), ("q4_k", "q6_k", "silu", 3), ("q4_k", "q4_k", "silu", 1),
     ("q8_0", "q8_0", "gelu_tanh", 2), ("q8_0", "q8_0", "silu", 1), ("q6_k", "q6_k", "gelu_tanh", 1),
     ("q6_k", "q4_k", "silu", 1)])
-@pytest.mark.parametrize("mode", ["auto", "grid", "single"])
-def test_ffn_decode_small(qd, fg, fd, act, batch, mode):
-    check_ffn_decode(qd, fg, fd, 512, 1536, batch, act, "small", mode=mode)
+def test_ffn_decode_small(qd, fg, fd, act, batch):
+    check_ffn_decode(qd, fg, fd, 512, 1536, batch, act, "small")
 
 
-@pytest.mark.parametrize("mode", ["auto", "grid", "single"])
-def test_ffn_decode_without_h_out(qd, mode):
-    check_ffn_decode(qd, "q4_k", "q6_k", 512, 1024, 1, "gelu_tanh", "no-h", with_h=False, mode=mode)
+def test_ffn_decode_without_h_out(qd):
+    check_ffn_decode(qd, "q4_k", "q6_k", 512, 1024, 1, "gelu_tanh", "no-h", with_h=False)
 
 
-@pytest.mark.parametrize("mode", ["auto", "grid", "single"])
-def test_ffn_decode_gemma3(qd, mode):
-    check_ffn_decode(qd, "q4_k", "q6_k", 2560, 10240, 1, "gelu_tanh", "gemma3-4b", reps=4, mode=mode)
+def test_ffn_decode_gemma3(qd):
+    check_ffn_decode(qd, "q4_k", "q6_k", 2560, 10240, 1, "gelu_tanh", "gemma3-4b", reps=4)
 
 
-@pytest.mark.parametrize("mode", ["auto", "grid"])
-def test_ffn_decode_gemma4_31b_batch1(qd, mode):
-    """Gemma-4-31B FFN at batch 1, in the automatic two launches (one
-    workgroup per CU, four copying waves, ring slots reused) and in the
-    grid-barrier launch (both rings reused)."""
-    rows = np.unique(np.concatenate([np.arange(0, 256), np.arange(5376 - 256, 5376), np.arange(0, 5376, 7)]))
-    check_ffn_decode(qd, "q4_k", "q6_k", 5376, 21504, 1, "gelu_tanh", "gemma4-31b b1", reps=2, rows=rows,
-                     mode=mode)
+def test_ffn_decode_gemma4_31b_batch1(qd):
+    """Gemma-4-31B FFN at batch 1 (one workgroup per CU, four copying waves,
+    ring slots reused), every output row checked."""
+    check_ffn_decode(qd, "q4_k", "q6_k", 5376, 21504, 1, "gelu_tanh", "gemma4-31b b1", reps=2)
 
 
-def test_ffn_decode_gemma4_31b_batch8_falls_back(qd):
-    """batch 8 x K = 5376 does not fit one workgroup's LDS: two launches even
-    when the single launch is asked for."""
-    check_ffn_decode(qd, "q4_k", "q6_k", 5376, 21504, 8, "gelu_tanh", "gemma4-31b b8", reps=1,
-                     mode="single")
+def test_ffn_decode_gemma4_31b_batch8(qd):
+    """batch 8 x K = 5376: the register-streaming kernels, every row checked."""
+    check_ffn_decode(qd, "q4_k", "q6_k", 5376, 21504, 8, "gelu_tanh", "gemma4-31b b8", reps=1)

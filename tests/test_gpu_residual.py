@@ -27,8 +27,6 @@ def qd(gpu):
     qd.lib()
     yield qd
     qd.set_launch_override(0, 0, 0)
-    qd.set_ffn_override(0, 0, 0)
-    qd.set_ffn_mode(0)
 
 
 from helpers import dev, h_tolerance, say  # noqa: E402
@@ -67,9 +65,8 @@ def test_gemv_residual(qd, fmt, N, K, batch, shape, inplace):
     assert_residual(f"{fmt} residual", got, y64, S, r)
 
 
-@pytest.mark.parametrize("mode", ["auto", "grid", "single"])
 @pytest.mark.parametrize("inplace", [False, True])
-def test_ffn_decode_residual(qd, mode, inplace):
+def test_ffn_decode_residual(qd, inplace):
     hidden, ff, batch = 2560, 10240, 1
     Wg = synth.quant_weights("q4_k", ff, hidden, SEED, tensor_id=84)
     Wu = synth.quant_weights("q4_k", ff, hidden, SEED, tensor_id=85)
@@ -77,20 +74,12 @@ def test_ffn_decode_residual(qd, mode, inplace):
     x = synth.normal((batch, hidden), SEED, tensor_id=87)
     nw = synth.normal((hidden,), SEED, tensor_id=88, mean=1.0, std=0.1)
     r = synth.normal((batch, hidden), SEED, tensor_id=89)
-    say(f"ffn_decode_residual gemma3 mode={mode} inplace={inplace}")
-    if mode == "single":
-        qd.set_ffn_override(2, 2, 0)
-    elif mode == "grid":
-        qd.set_ffn_mode(2)
-    try:
-        h = torch.empty((batch, ff), device="cuda")
-        rd = dev(r)
-        y = qd.qffn_decode_residual("q4_k", dev(Wg), dev(Wu), "q6_k", dev(Wd), dev(x), rd, dev(nw), 1e-6,
-                                    "gelu_tanh", y=rd if inplace else None, h_out=h)
-        got, hh = y.cpu().numpy(), h.cpu().numpy()
-    finally:
-        qd.set_ffn_override(0, 0, 0)
-        qd.set_ffn_mode(0)
+    say(f"ffn_decode_residual gemma3 inplace={inplace}")
+    h = torch.empty((batch, ff), device="cuda")
+    rd = dev(r)
+    y = qd.qffn_decode_residual("q4_k", dev(Wg), dev(Wu), "q6_k", dev(Wd), dev(x), rd, dev(nw), 1e-6,
+                                "gelu_tanh", y=rd if inplace else None, h_out=h)
+    got, hh = y.cpu().numpy(), h.cpu().numpy()
     xn32 = oracle.rmsnorm(x, nw, 1e-6).astype(np.float32)
     g64, Sg = oracle.gemv("q4_k", Wg, xn32, ff, hidden)
     u64, Su = oracle.gemv("q4_k", Wu, xn32, ff, hidden)

@@ -362,6 +362,54 @@ def test_rmsnorm_unit_rms_and_weight_direct():
     np.testing.assert_array_equal(out2, 2 * out)
 
 
+# ------------------------------------------------- Post-norm residual ---
+
+def test_post_norm_constant_projection_closed_form():
+    """p = c * 1: the normalised projection is w1 * c / sqrt(c^2 + eps), so
+    y = r + w1 * c / sqrt(c^2 + eps); the sign of c carries through."""
+    N, eps = 96, 1e-6
+    r = synth.normal((2, N), seed=5)
+    w1 = np.linspace(0.5, 1.5, N).astype(np.float32)
+    for c in (3.0, -0.25):
+        p = np.full((2, N), c)
+        y, _ = oracle.post_norm_residual(p, r, w1, eps)
+        exp = r.astype(np.float64) + w1.astype(np.float64) * c / math.sqrt(c * c + eps)
+        np.testing.assert_allclose(y, exp, rtol=1e-14, atol=1e-15)
+
+
+def test_post_norm_zero_projection_is_residual():
+    """p = 0 adds nothing (the norm of zero is zero for eps > 0), so y = r
+    exactly; y2 is then the RMS-norm of r, which equals orc_rmsnorm of r."""
+    N = 128
+    r = synth.normal((3, N), seed=6)
+    w1 = synth.normal((N,), seed=7, mean=1.0, std=0.1)
+    w2 = synth.normal((N,), seed=8, mean=1.0, std=0.1)
+    y, y2 = oracle.post_norm_residual(np.zeros((3, N)), r, w1, 1e-6, w2)
+    np.testing.assert_array_equal(y, r.astype(np.float64))
+    np.testing.assert_array_equal(y2, oracle.rmsnorm(r, w2, 1e-6))
+
+
+def test_post_norm_scale_invariance_and_unit_rms():
+    """With eps = 0 the normalised projection does not depend on the scale
+    of p (p -> 2^k p gives the same y exactly), and with w2 = 1 the second
+    output has mean square 1; the weights enter linearly (no 1 + w)."""
+    N = 256
+    p = synth.normal((2, N), seed=9).astype(np.float64)
+    r = synth.normal((2, N), seed=10)
+    w1 = synth.normal((N,), seed=11, mean=1.0, std=0.1)
+    ones = np.ones(N, np.float32)
+    y, y2 = oracle.post_norm_residual(p, r, w1, 0.0, ones)
+    y8, _ = oracle.post_norm_residual(8.0 * p, r, w1, 0.0)
+    np.testing.assert_array_equal(y, y8)
+    np.testing.assert_allclose((y2 ** 2).mean(axis=1), 1.0, rtol=1e-12)
+    z0, _ = oracle.post_norm_residual(p, np.zeros_like(r), w1, 0.0)
+    z1, _ = oracle.post_norm_residual(p, np.zeros_like(r), 2 * w1, 0.0)
+    np.testing.assert_array_equal(z1, 2 * z0)
+    # the normalised part has unit RMS before the weight: w1 = 1, r = 0
+    u, _ = oracle.post_norm_residual(p, np.zeros_like(r), ones, 0.0)
+    np.testing.assert_allclose((u ** 2).mean(axis=1), 1.0, rtol=1e-12)
+
+
 # -------------------------------------------------------- Activations ---
 
 def test_activations_against_torch_float64():
@@ -466,3 +514,25 @@ def test_q8_act_gemv_close_to_exact_gemv():
     yq, _ = oracle.gemv_q8_0_q8act(W, q, d, N, K)
     y, S = oracle.gemv("q8_0", W, x, N, K)
     assert (np.abs(yq - y) <= 5e-2 * S + 1e-6).all()
+
+
+def test_cancelling_q4k_blocks_decode_to_zero():
+    """The cancelling Q4_K blocks the GPU tests build (constant quant q0 per
+    sub-block, d*sc*q0 == dmin*m exactly) decode to exact zeros, and moving
+    a quant by +-1 gives +-d*sc exactly: the oracle's single rounding of
+    d*sc*q - dmin*m is exact here, whatever the size of the two terms."""
+    import sys
+    sys.path.insert(0, os.path.dirname(__file__))
+    from helpers import cancelling_q4k
+    W = cancelling_q4k(16, 1024, seed=3)
+    assert not oracle.dequant("q4_k", W, 1024).any()
+    Wf = cancelling_q4k(16, 1024, seed=4, flip_frac=0.1)
+    w = oracle.dequant("q4_k", Wf, 1024)
+    blocks = Wf.reshape(-1, 144)
+    for bi in range(0, blocks.shape[0], 7):
+        d = float(np.frombuffer(blocks[bi, 0:2].tobytes(), np.float16)[0])
+        for j in range(8):
+            sc, _ = oracle.q4k_scale_min(blocks[bi], j)
+            row, col = divmod(bi, 1024 // 256)
+            sub = w[row, 256 * col + 32 * j: 256 * col + 32 * j + 32]
+            assert set(np.unique(np.abs(sub)).tolist()) <= {0.0, float(np.float32(d * sc))}
