@@ -87,4 +87,4 @@ def test_ffn_decode_residual(qd, inplace):
     tol = h_tolerance(g64, u64, Sg, Su, oracle.ACT_GELU_TANH)
     assert (np.abs(hh - href) <= tol).all(), "h out of tolerance"
     y64, Sy = oracle.gemv("q6_k", Wd, hh, hidden, ff)
-    assert_residual(f"ffn residual [{mode}]", got, y64, Sy, r)
+    assert_residual("ffn residual", got, y64, Sy, r)
