@@ -86,8 +86,10 @@ typedef enum qd_status {
     QD_ELAUNCH = 4,      /* the HIP runtime refused the launch */
     QD_EUNSUPPORTED = 5, /* valid arguments the library has no kernel for */
     QD_ENOMEM = 6,       /* workspace allocation failed */
-    QD_ECAPTURE = 7      /* the stream is capturing and the call would have to
+    QD_ECAPTURE = 7,     /* the stream is capturing and the call would have to
                             create or grow its workspace (nothing enqueued) */
+    QD_ETOOBIG = 8       /* the allocation-free call needs more scratch than it
+                            holds (nothing enqueued) */
 } qd_status;
 
 typedef enum qd_format { QD_Q4_K = 0, QD_Q6_K = 1, QD_Q8_0 = 2 } qd_format;
@@ -352,6 +354,31 @@ qd_status qffn_decode_residual(qd_format fmt_gu, const void *Wg, const void *Wu,
                                const float *norm_w, float eps, qd_act act, const float *r,
                                float *y, float *h_out, int64_t N_ff, int64_t K, int batch,
                                void *stream);
+
+/*
+ * qffn_decode without any allocation, for callers that cannot allocate
+ * device memory: code running under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.
+ *
+ * Same arguments, results (bit for bit) and kernels as qffn_decode; h (when
+ * h_out is NULL), split-K partial sums and counters live in a fixed scratch
+ * array the library holds on each GPU it runs on (8 MiB of floats plus
+ * 272 KB of counters, kept until the process ends), not in the stream's
+ * workspace.  Nothing is allocated, ever: the scratch's address on the
+ * current device is looked up once (hipGetSymbolAddress), and each call
+ * that uses it first clears its counters with a small kernel on `stream`.
+ * Every call on one GPU shares that GPU's scratch, whatever the stream:
+ * calls that overlap on one GPU (concurrent streams, or host threads
+ * without ordering) race and give wrong results.
+ * Limit: batch <= QD_BATCH_CHUNK columns need h plus the larger launch's
+ * partial sums within the 2^21 floats (e.g. the Gemma-4-31B FFN at batch 8
+ * needs about 1.2 M); a call that needs more returns QD_ETOOBIG with
+ * nothing enqueued.
+ * Errors: as qffn_decode (never QD_ENOMEM or QD_ECAPTURE), QD_ETOOBIG.
+ */
+qd_status qffn_decode_noalloc(qd_format fmt_gu, const void *Wg, const void *Wu, qd_format fmt_down,
+                              const void *Wd, const float *x, const float *norm_w, float eps, qd_act act,
+                              float *y, float *h_out, int64_t N_ff, int64_t K, int batch, void *stream);
 
 /*
  * y = r + RMSNorm(Wd h; post_w),  y2 = RMSNorm(y; next_w),

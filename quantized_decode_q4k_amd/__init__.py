@@ -16,6 +16,7 @@ Entry points (same names as the C ABI):
     qqkv_proj                                      q, k, v = Wq xn, Wk xn, Wv xn (one launch)
     qffn_gate_up_act                               h = act(Wg xn) * (Wu xn)
     qffn_decode                                    y = Wd h (whole FFN, one launch)
+    qffn_decode_noalloc                            qffn_decode with no allocation (fixed scratch)
     qffn_decode_residual                           y = Wd h + r
     qmoe_ffn_decode                                mixture-of-experts FFN (routed ids on device)
     qgemm_prefill, qgemm_prefill_gate_up_act       bf16 MFMA prefill GEMMs
@@ -39,7 +40,7 @@ ACTS = {"gelu_tanh": ACT_GELU_TANH, "silu": ACT_SILU}
 MAX_BATCH = 64
 BATCH_CHUNK = 8
 
-QD_OK, QD_EINVAL, QD_ESHAPE, QD_EALIGN, QD_ELAUNCH, QD_EUNSUPPORTED, QD_ENOMEM, QD_ECAPTURE = range(8)
+QD_OK, QD_EINVAL, QD_ESHAPE, QD_EALIGN, QD_ELAUNCH, QD_EUNSUPPORTED, QD_ENOMEM, QD_ECAPTURE, QD_ETOOBIG = range(9)
 
 # Every function the header declares, with its ctypes signature.
 _P = ctypes.c_void_p
@@ -71,6 +72,7 @@ SIGNATURES = {
                        _P]),
     "qffn_gate_up_act": (_I, [_I, _P, _P, _P, _P, _F, _I, _P, _P, _P, _I64, _I64, _I, _P]),
     "qffn_decode": (_I, [_I, _P, _P, _I, _P, _P, _P, _F, _I, _P, _P, _I64, _I64, _I, _P]),
+    "qffn_decode_noalloc": (_I, [_I, _P, _P, _I, _P, _P, _P, _F, _I, _P, _P, _I64, _I64, _I, _P]),
     "qgemm_prefill": (_I, [_I, _P, _P, _P, _I64, _I64, _I64, _P]),
     "qgemm_prefill_gate_up_act": (_I, [_I, _P, _P, _P, _I, _P, _P, _P, _I64, _I64, _I64, _P]),
     "qdequant": (_I, [_I, _P, _P, _I64, _I64, _P]),
@@ -376,6 +378,26 @@ def qffn_decode(fmt_gu, Wg: torch.Tensor, Wu: torch.Tensor, fmt_down, Wd: torch.
                            _dev(Wd, "Wd", torch.uint8), _dev(x, "x", torch.float32), nw, float(eps),
                            _act(act), _dev(y, "y", torch.float32), hp, N, K, batch, _stream())
     _check("qffn_decode", st)
+    return y
+
+
+def qffn_decode_noalloc(fmt_gu, Wg: torch.Tensor, Wu: torch.Tensor, fmt_down, Wd: torch.Tensor,
+                        x: torch.Tensor, norm_w: torch.Tensor | None, eps: float, act, y: torch.Tensor,
+                        h_out: torch.Tensor | None = None) -> torch.Tensor:
+    """qffn_decode with h and partial sums in the library's fixed per-GPU
+    scratch (no allocation); y must be given."""
+    fg, fd = _fmt(fmt_gu), _fmt(fmt_down)
+    K = x.shape[-1]
+    batch = 1 if x.dim() == 1 else x.shape[0]
+    N = _rows(fg, Wg, K)
+    if _rows(fg, Wu, K) != N or _rows(fd, Wd, N) != K:
+        raise ValueError("gate/up must be N_ff x K and down K x N_ff")
+    nw = _dev(norm_w, "norm_w", torch.float32) if norm_w is not None else None
+    hp = _dev(h_out, "h_out", torch.float32) if h_out is not None else None
+    st = lib().qffn_decode_noalloc(fg, _dev(Wg, "Wg", torch.uint8), _dev(Wu, "Wu", torch.uint8), fd,
+                                   _dev(Wd, "Wd", torch.uint8), _dev(x, "x", torch.float32), nw, float(eps),
+                                   _act(act), _dev(y, "y", torch.float32), hp, N, K, batch, _stream())
+    _check("qffn_decode_noalloc", st)
     return y
 
 

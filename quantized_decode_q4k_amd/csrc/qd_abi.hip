@@ -15,8 +15,26 @@
 #include "qdecode.h"
 
 namespace {
+constexpr size_t kScratchFloats = size_t(2) << 20;  // partial sums and h: 8 MiB
+constexpr size_t kScratchCounterWords = (size_t(1) << 16) + 4096;
+}  // namespace
+
+// Scratch of the allocation-free entry point (qffn_decode_noalloc): one per
+// GPU, held until the process ends.  Host code never uses this name as an
+// address; it asks hipGetSymbolAddress for the device's copy (see
+// scratch_workspace below).
+static __device__ __align__(256) float scratch[kScratchFloats + kScratchCounterWords];
+
+namespace {
 
 using qd::Shape;
+
+// Zero n words (a kernel rather than a memory set, so that it may sit in a
+// captured graph).
+__global__ void zero_words_kernel(unsigned *p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
 
 constexpr int kVersion = 10000;  // 1.0.0
 
@@ -175,6 +193,7 @@ std::vector<std::pair<float *, unsigned *>> g_ws_retired;
 
 constexpr size_t kInitialPartials = size_t(8) << 20;  // 32 MiB of floats
 constexpr size_t kCounterWords = (size_t)kMaxTiles + kAuxWords;
+static_assert(kCounterWords == kScratchCounterWords, "the scratch holds the workspace's counters");
 
 // True when `st` is being captured into a graph (or its state cannot be read).
 bool capturing(hipStream_t st) {
@@ -210,6 +229,43 @@ qd_status get_workspace(hipStream_t st, size_t need_floats, Workspace *out) {
         w.partial_floats = n;
     }
     *out = w;
+    return QD_OK;
+}
+
+// The workspace of a call: the stream's own (allocated on first need), or a
+// fixed block the caller hands in (the allocation-free entry point's
+// scratch), which is never grown: a call that needs more returns
+// QD_ETOOBIG with nothing enqueued.
+qd_status acquire_ws(hipStream_t st, size_t need_floats, const Workspace *fixed, Workspace *out) {
+    if (fixed) {
+        if (need_floats > fixed->partial_floats) return QD_ETOOBIG;
+        *out = *fixed;
+        return QD_OK;
+    }
+    return get_workspace(st, need_floats, out);
+}
+
+// The device's scratch as a fixed workspace: its address from
+// hipGetSymbolAddress, asked once per device with that device current (each
+// GPU holds its own copy of the array).
+std::mutex g_scratch_mu;
+constexpr int kMaxDevices = 64;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+qd_status scratch_workspace(Workspace *out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return QD_ELAUNCH;
+    if (dev < 0 || dev >= kMaxDevices) return QD_EUNSUPPORTED;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return QD_ELAUNCH;
+        g_scratch_ptr[dev] = p;
+    }
+    float *base = static_cast<float *>(g_scratch_ptr[dev]);
+    out->partials = base;
+    out->counters = reinterpret_cast<unsigned *>(base + kScratchFloats);
+    out->partial_floats = kScratchFloats;
     return QD_OK;
 }
 
@@ -342,7 +398,8 @@ struct PostArgs {
 qd_status run_mv(int fmt, bool ffn, const void *W0, const void *W1, const float *x,
                  const float *norm_w, float eps, int act, float *y, float *g_out, float *u_out,
                  int64_t N, int64_t K, int batch, void *stream, size_t ws_offset = 0,
-                 const float *res = nullptr, const PostArgs &post = PostArgs()) {
+                 const float *res = nullptr, const PostArgs &post = PostArgs(),
+                 const Workspace *fixed = nullptr) {
     qd_status st = check_shape(fmt, N, K, batch);
     if (st != QD_OK) return st;
     if (!W0 || !x || !y || (ffn && !W1)) return QD_EINVAL;
@@ -382,7 +439,7 @@ qd_status run_mv(int fmt, bool ffn, const void *W0, const void *W1, const float 
             if (pc.y2) pc.y2 += yo;
             qd_status cs = run_mv(fmt, ffn, W0, W1, x + xo, norm_w, eps, act, y + yo, g_out ? g_out + yo : nullptr,
                                   u_out ? u_out + yo : nullptr, N, K, nb, stream, ws_offset, res ? res + yo : nullptr,
-                                  pc);
+                                  pc, fixed);
             if (cs != QD_OK) return cs;
         }
         return QD_OK;
@@ -411,7 +468,7 @@ qd_status run_mv(int fmt, bool ffn, const void *W0, const void *W1, const float 
         if (stream_plan(fmt, ffn, N, K, batch, norm_w, &sa, &grid, &lds)) {
             if (pnorm) {
                 Workspace w;
-                st = get_workspace(hs, ws_offset + p_floats, &w);
+                st = acquire_ws(hs, ws_offset + p_floats, fixed, &w);
                 if (st != QD_OK) return st;
                 bind_post(ws_offset, grid, w);
                 sa.pn = pn;
@@ -450,7 +507,7 @@ qd_status run_mv(int fmt, bool ffn, const void *W0, const void *W1, const float 
     const size_t part_floats = p.s.p_out > 1 ? (size_t)p.s.p_out * batch * (ffn ? 2 : 1) * N : 0;
     if (part_floats + p_floats > 0) {
         Workspace w;
-        qd_status ws = get_workspace(hs, ws_offset + part_floats + p_floats, &w);
+        qd_status ws = acquire_ws(hs, ws_offset + part_floats + p_floats, fixed, &w);
         if (ws != QD_OK) return ws;
         a.partials = w.partials + ws_offset;
         a.counters = w.counters;
@@ -468,7 +525,8 @@ qd_status run_mv(int fmt, bool ffn, const void *W0, const void *W1, const float 
 qd_status run_ffn_decode(int fmt_gu, const void *Wg, const void *Wu, int fmt_d, const void *Wd,
                          const float *x, const float *norm_w, float eps, int act, float *y,
                          float *h_out, int64_t N_ff, int64_t K, int batch, void *stream,
-                         const float *res = nullptr, const PostArgs &post = PostArgs()) {
+                         const float *res = nullptr, const PostArgs &post = PostArgs(),
+                         const Workspace *fixed = nullptr) {
     qd_status st = check_shape(fmt_gu, N_ff, K, batch);
     if (st != QD_OK) return st;
     st = check_shape(fmt_d, K, N_ff, batch);
@@ -503,7 +561,7 @@ qd_status run_ffn_decode(int fmt_gu, const void *Wg, const void *Wu, int fmt_d, 
             if (pc.y2) pc.y2 += xo;
             qd_status cs = run_ffn_decode(fmt_gu, Wg, Wu, fmt_d, Wd, x + xo, norm_w, eps, act, y + xo,
                                           h_out ? h_out + (int64_t)c0 * N_ff : nullptr, N_ff, K, nb, stream,
-                                          res ? res + xo : nullptr, pc);
+                                          res ? res + xo : nullptr, pc, fixed);
             if (cs != QD_OK) return cs;
         }
         return QD_OK;
@@ -521,15 +579,21 @@ qd_status run_ffn_decode(int fmt_gu, const void *Wg, const void *Wu, int fmt_d, 
     float *h = h_out;
     if (h_floats + std::max(need_a, need_b) > 0) {
         Workspace w;
-        st = get_workspace(hs, h_floats + std::max(need_a, need_b), &w);
+        st = acquire_ws(hs, h_floats + std::max(need_a, need_b), fixed, &w);
         if (st != QD_OK) return st;
         if (!h) h = w.partials;
+        if (fixed) {
+            // the scratch keeps the last call's contents: its counters start
+            // this call at zero
+            hipLaunchKernelGGL(zero_words_kernel, dim3(64), dim3(256), 0, hs, w.counters, kCounterWords);
+            if (hipGetLastError() != hipSuccess) return QD_ELAUNCH;
+        }
     }
     st = run_mv(fmt_gu, true, Wg, Wu, x, norm_w, eps, act, h, nullptr, nullptr, N_ff, K, batch, stream,
-                h_floats);
+                h_floats, nullptr, PostArgs(), fixed);
     if (st != QD_OK) return st;
     return run_mv(fmt_d, false, Wd, nullptr, h, nullptr, 0.f, 0, y, nullptr, nullptr, K, N_ff, batch, stream,
-                  h_floats, res, post);
+                  h_floats, res, post, fixed);
 }
 
 // ------------------------------------------------------------ prefill ---
@@ -1001,6 +1065,7 @@ const char *qd_status_str(qd_status s) {
     case QD_EUNSUPPORTED: return "not supported by the library";
     case QD_ENOMEM: return "workspace allocation failed";
     case QD_ECAPTURE: return "the stream is capturing a graph and the call needs a new or larger workspace";
+    case QD_ETOOBIG: return "the call needs more scratch than the allocation-free entry point holds";
     default: return "unknown status";
     }
 }
@@ -1113,6 +1178,16 @@ qd_status qffn_decode(qd_format fmt_gu, const void *Wg, const void *Wu, qd_forma
                       float *y, float *h_out, int64_t N_ff, int64_t K, int batch, void *stream) {
     return run_ffn_decode(fmt_gu, Wg, Wu, fmt_down, Wd, x, norm_w, eps, act, y, h_out, N_ff, K,
                           batch, stream);
+}
+
+qd_status qffn_decode_noalloc(qd_format fmt_gu, const void *Wg, const void *Wu, qd_format fmt_down,
+                              const void *Wd, const float *x, const float *norm_w, float eps, qd_act act,
+                              float *y, float *h_out, int64_t N_ff, int64_t K, int batch, void *stream) {
+    Workspace w;
+    qd_status st = scratch_workspace(&w);
+    if (st != QD_OK) return st;
+    return run_ffn_decode(fmt_gu, Wg, Wu, fmt_down, Wd, x, norm_w, eps, act, y, h_out, N_ff, K, batch, stream,
+                          nullptr, PostArgs(), &w);
 }
 
 qd_status qdequant(qd_format fmt, const void *W, float *out, int64_t N, int64_t K, void *stream) {
