@@ -5,15 +5,24 @@
 // the cross-workgroup hand-off it rests on.
 //
 // Every workgroup that completes a row tile of the projection p stores its
-// rows into a buffer and counts itself on a device-scope counter: each
-// thread releases its stores at agent scope, the workgroup synchronises,
-// and one thread increments the counter with an acquire-release atomic.
-// The workgroup that brings the count to the number of tiles acquires and
-// forms, per batch column (every sum in a fixed order, so results do not
-// depend on which workgroup finishes last):
+// rows into a buffer and counts itself on a device-scope counter; the
+// workgroup that brings the count to the number of tiles forms, per batch
+// column (every sum in a fixed order, so results do not depend on which
+// workgroup finishes last):
 //   y  = r + p * w1 / sqrt(mean(p^2) + eps)
 //   y2 = y * w2 / sqrt(mean(y^2) + eps)            (when w2 is given)
 // then returns the counter to zero for the next launch.
+//
+// Hand-off between workgroups.  Values that another workgroup of the same
+// launch reads are stored and loaded as agent-scope atomics (xstore /
+// xload): on gfx950 these are the device-coherent forms of the global
+// store and load (scope bits set), so they neither leave a stale line in
+// one XCD's L2 nor read one.  A workgroup counts itself only after every
+// wave has waited for its own such stores to complete (s_waitcnt vmcnt(0)),
+// so the count can reach the last workgroup only after the values have.
+// This is what the compiler's release / acquire at agent scope would order,
+// without its whole-L2 writeback and invalidate per wave, which measured
+// about 15 us per hand-off under a running weight stream.
 #pragma once
 
 #include "qd_device.h"
@@ -21,6 +30,11 @@
 #include "qd_lds.h"
 
 namespace qd {
+
+QD_DEV void xstore(float *p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+QD_DEV float xload(const float *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+// This wave's global stores (and loads) have completed.
+QD_DEV void vm_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Sum of v over the NT threads of the workgroup, the same value in every
 // thread: per wave with cross-lane adds, then the wave totals in wave order.
@@ -38,26 +52,24 @@ QD_DEV float block_total(float v, float *red) {
     return s;
 }
 
-// Release this workgroup's global stores and count it on *ctr; true (in
-// every thread) for the workgroup that completes the count of `total`,
-// which has then acquired every counted workgroup's stores.  flag: one int
+// Count this workgroup on *ctr once its xstore-d values have completed;
+// true (in every thread) for the workgroup that completes the count of
+// `total`, which then reads the others' values with xload.  flag: one int
 // of LDS.
 template <int NT>
 QD_DEV bool arrive_last(unsigned *ctr, unsigned total, int *flag) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    vm_drain();
     __syncthreads();
     if (threadIdx.x == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         *flag = prev == total - 1 ? 1 : 0;
     }
     __syncthreads();
-    const bool last = *flag != 0;
-    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    return last;
+    return *flag != 0;
 }
 
 // The row epilogue, called by every thread of a workgroup after it has
-// stored the final p rows of the tiles it completed (p at pn.p).  y: the
+// stored (xstore) the final p rows of the tiles it completed (p at pn.p).  y: the
 // call's output [batch][N].  red: NT / 64 floats of LDS; flag: one int.
 template <int NT>
 QD_DEV void post_norm_tail(const PostNorm &pn, float *y, int batch, int64_t N, float *red, int *flag) {
@@ -69,12 +81,15 @@ QD_DEV void post_norm_tail(const PostNorm &pn, float *y, int batch, int64_t N, f
         const float *rb = pn.r + (int64_t)b * N;
         float *yb = y + (int64_t)b * N;
         float ss = 0.f;
-        for (int64_t n = tid; n < N; n += NT) ss = fmaf(pb[n], pb[n], ss);
+        for (int64_t n = tid; n < N; n += NT) {
+            const float v = xload(pb + n);
+            ss = fmaf(v, v, ss);
+        }
         ss = block_total<NT>(ss, red);
         const float rinv = 1.0f / sqrtf(ss * invN + pn.eps);
         float ss2 = 0.f;
         for (int64_t n = tid; n < N; n += NT) {
-            const float v = rb[n] + pb[n] * rinv * pn.w1[n];
+            const float v = rb[n] + xload(pb + n) * rinv * pn.w1[n];
             yb[n] = v;
             ss2 = fmaf(v, v, ss2);
         }

@@ -469,7 +469,7 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
                         for (int b = 0; b < B; b++) {
                             const int64_t o = (int64_t)b * N + row[i];
                             const float vv = a.coef ? a.coef[ks] * v[i][b] : v[i][b];
-                            if (a.pn.w1) a.pn.p[o] = vv;  // the row epilogue forms y
+                            if (a.pn.w1) xstore(a.pn.p + o, vv);  // the row epilogue forms y
                             else store_out(a.y + o, a.res ? vv + a.res[o] : vv);
                         }
             }
@@ -479,7 +479,7 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
                 if (row[i] < N)
 #pragma unroll
                     for (int b = 0; b < B; b++)
-                        a.partials[(((int64_t)ks * B + b) * NP + (FFN ? i : 0)) * N + row[i]] = v[i][b];
+                        xstore(a.partials + (((int64_t)ks * B + b) * NP + (FFN ? i : 0)) * N + row[i], v[i][b]);
         }
     };
 
@@ -523,7 +523,7 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
     }
 
     // ---- split-K: the last workgroup of this row tile sums the partials in
-    // slice order (release / acquire on the tile's counter, qd_epilogue.h)
+    // slice order (the hand-off of qd_epilogue.h on the tile's counter)
     if (!arrive_last<kThreads>(a.counters + bx, (unsigned)p_out, &s_last)) return;
     const int rows_here = (FFN ? RS : RS * NR) * rpg;
     const int64_t tile0 = (int64_t)bx * rows_here;
@@ -534,8 +534,9 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
         float s0 = 0.f, s1 = 0.f;
         for (int k = 0; k < p_out; k++) {
             const float *p = a.partials + (((int64_t)k * B + b) * NP) * N + r;
-            s0 = a.coef ? fmaf(a.coef[k], p[0], s0) : s0 + p[0];
-            if constexpr (FFN) s1 += p[N];
+            const float pv = xload(p);
+            s0 = a.coef ? fmaf(a.coef[k], pv, s0) : s0 + pv;
+            if constexpr (FFN) s1 += xload(p + N);
         }
         if constexpr (FFN) {
             store_out(a.y + (int64_t)b * N + r, act_apply(a.act, s0) * s1);
@@ -543,7 +544,7 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
             if (a.u_out) a.u_out[(int64_t)b * N + r] = s1;
         } else {
             const int64_t o = (int64_t)b * N + r;
-            if (a.pn.w1) a.pn.p[o] = s0;
+            if (a.pn.w1) xstore(a.pn.p + o, s0);
             else store_out(a.y + o, a.res ? s0 + a.res[o] : s0);
         }
     }

@@ -565,7 +565,7 @@ __global__ __launch_bounds__(64 * (NC + kPcMaxProducers)) void stream_pc_kernel(
             if (a.u_out) a.u_out[(int64_t)b * N + row] = sr[1];
         } else {
             const int64_t o = (int64_t)b * N + row;
-            if (a.pn.w1) a.pn.p[o] = sr[0];  // the row epilogue forms y
+            if (a.pn.w1) xstore(a.pn.p + o, sr[0]);  // the row epilogue forms y
             else a.y[o] = a.res ? sr[0] + a.res[o] : sr[0];
         }
     }

@@ -21,7 +21,7 @@ def assert_bound(name, got, y64, S, rows=None):
         got, y64, S = got[..., rows], y64[..., rows], S[..., rows]
     err = np.abs(got - y64)
     bound = 1e-4 * S + 1e-6
-    bad = err > bound
+    bad = ~(err <= bound)   # NaN fails
     if bad.any():
         idx = np.unravel_index(np.argmax(err / bound), err.shape)
         raise AssertionError(f"{name}: {bad.sum()} outputs out of bound; worst at {idx}: "
