@@ -35,6 +35,7 @@
 //    cross-lane shuffles; one lane writes each output (and, for the fused
 //    FFN, applies the GELU-tanh or SiLU product).
 #include "qd_decode.h"
+#include "qd_digits.h"
 #include "qd_epilogue.h"
 
 #include <algorithm>
@@ -243,8 +244,13 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
     const int t_beg = a.coef ? 0 : ks * a.nk;  // expert slots each take the whole row
     const int t_end = min(a.nb, t_beg + a.nk);
     const int xstride = a.nk * kSuperPhys;
-    float *xl = smem;                                 // [B][nk * 272]
-    float *red = smem + B * xstride;                  // [4 waves][B]
+    // batch 1-2: activation digits (qd_digits.h), nk * kDigSU bytes per
+    // batch row; else fp32 activations, nk * 272 floats per batch row
+    constexpr bool DIG = B <= 2;
+    const int xsb = a.nk * kDigSU;
+    float *xl = smem;                                 // [B][nk * 272] or digits
+    float *red = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(smem) +
+                                           (DIG ? (size_t)B * xsb : (size_t)B * xstride * 4));  // [4 waves][B]
 
     // ---- rows of this lane group: row slots bx * RS * rpg + r * RS + rs for
     // r < rpg (a row slot is one row of each matrix for the fused FFN, NR
@@ -392,7 +398,12 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
                 v.z = v.z * ir * w.z;
                 v.w = v.w * ir * w.w;
             }
-            *reinterpret_cast<float4 *>(xl + b * xstride + xphys(4 * f4)) = v;
+            if constexpr (DIG) {
+                uint8_t *su = reinterpret_cast<uint8_t *>(xl) + b * xsb + (f4 >> 6) * kDigSU;
+                stage_digits<FMT == kQ4K>(v, su, 4 * (f4 & 63));
+            } else {
+                *reinterpret_cast<float4 *>(xl + b * xstride + xphys(4 * f4)) = v;
+            }
         };
         if (early) {
 #pragma unroll
@@ -498,7 +509,12 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
             load_at(buf[(s + D) % (D + 1)], rl, ul, q + D < Q);
             if (++ul == nsu) { ul = 0; rl++; }
             const int tlo = min(t0 + uc * p_in, t_end - 1) - t_beg;  // dead units: zero weights
-            if constexpr (FMT == kQ4K) {
+            if constexpr (DIG) {
+                const uint8_t *xd = reinterpret_cast<const uint8_t *>(xl) + tlo * kDigSU;
+                if constexpr (FMT == kQ4K) q4k_step_dig<NR, B>(buf[s], xd, xsb, c, L4, acc);
+                else if constexpr (FMT == kQ6K) q6k_step_dig<NR, B>(buf[s], xd, xsb, c >> 1, c & 1, acc);
+                else q80_step_dig<NR, B>(buf[s], xd, xsb, c, acc);
+            } else if constexpr (FMT == kQ4K) {
                 const float *xp = xl + xphys(kSuper * tlo + 64 * c);
                 q4k_step<NR, B>(buf[s], xp, xstride, L4, acc);
             } else if constexpr (FMT == kQ6K) {
@@ -664,9 +680,9 @@ hipError_t launch_qkv(const QkvArgs &q, int batch, size_t lds, hipStream_t st) {
 
 // ------------------------------------------------------------ launchers ---
 size_t mv_lds_bytes(int fmt, int batch, int nk) {
-    size_t floats = (size_t)batch * nk * kSuperPhys;
-    floats += 4 * 8;  // cross-wave scratch: [4 waves][batch]
-    return floats * sizeof(float);
+    // staged activations: digits at batch 1-2, fp32 beyond
+    const size_t x = batch <= 2 ? (size_t)batch * nk * kDigSU : (size_t)batch * nk * kSuperPhys * sizeof(float);
+    return x + 4 * 8 * sizeof(float);  // cross-wave scratch: [4 waves][batch]
 }
 
 template <int FMT, int B, int NR, bool FFN>

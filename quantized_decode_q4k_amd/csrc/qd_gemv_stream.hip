@@ -15,15 +15,16 @@
 //    bytes per instruction, no registers), several steps in flight;
 //    decoding waves take them out of the ring as they land.
 //  * Decoding reads a lane group's block (4 lanes per superunit, the lane
-//    split of the GEMV kernels) and its activations from LDS, and writes the
-//    superunit's partial sum to LDS.  After the stream, each row's partials
-//    are added in superunit order, so a result does not depend on the launch
-//    shape.
-//  * x is copied into LDS the same way (16-byte skew every 64 floats), then
-//    multiplied by the RMS-norm weight in place; the inverse RMS is applied
-//    to each row's sum at the end.
+//    split of the GEMV kernels) and its activation digits from LDS, and
+//    writes the superunit's partial sum to LDS.  After the stream, each
+//    row's partials are added in superunit order, so a result does not
+//    depend on the launch shape.
+//  * x is multiplied by the RMS-norm weight and staged once per workgroup
+//    as activation digits (qd_digits.h: exact integer products); the
+//    inverse RMS is applied to each row's sum at the end.
 // The copies are ordered by explicit waits (qd_lds.h).
 #include "qd_decode.h"
+#include "qd_digits.h"
 #include "qd_epilogue.h"
 #include "qd_lds.h"
 
@@ -74,9 +75,6 @@ QD_DEV void vm_wait_n(int n) {
     }
 }
 
-// Logical activation index k -> LDS float index (16-byte skew every 64).
-QD_DEV int xphys(int k) { return k + ((k >> 6) << 2); }
-constexpr int kSuperPhys = kSuper + kSuper / 16;  // 272 floats per superunit
 
 // --------------------------------------------------------- block loads ---
 // One lane's share of a superunit from LDS (blk: the superunit's first byte
@@ -125,142 +123,18 @@ QD_DEV void lds_q80(RawQ80 &r, const uint8_t *blk, int c) {
     r.a_is_p = 0u;
 }
 
-// ------------------------------------------------- per-superunit dots ---
-// xv: this lane's 64 activations (in the lane's own order, see each format)
-// for each batch row; result: this lane's share of w . x per row stream.
-
-// Q4_K: xv[0..7] low run (64c + 0..31), xv[8..15] high run.  Each weight is
-// formed on its own with one fused multiply-add of its sub-block's scale
-// and min (exact factors, one rounding), then multiplied by its activation.
-template <int NR, int B>
-QD_DEV void dot_q4k(const RawQ4K (&r)[NR], const float4 (&xv)[B][16], const Q4Lane &L, float (&out)[NR][B]) {
-#pragma unroll
-    for (int i = 0; i < NR; i++) {
-        const Q4Scales s = q4k_scales(r[i], L);
-        const float a0 = (s.d * s.sc0) * fp8_inv_unit(), a1 = (s.d * s.sc1) * fp8_inv_unit();
-        const float b0 = -(s.dmin * s.m0), b1 = -(s.dmin * s.m1);
-        float alo[B], ahi[B];
-#pragma unroll
-        for (int b = 0; b < B; b++) { alo[b] = 0.f; ahi[b] = 0.f; }
-#pragma unroll
-        for (int dw = 0; dw < 8; dw++) {
-            const Q4Nibbles n = q4k_nibbles(r[i].q[dw]);
-            const float l0 = fmaf(n.lo01.x, a0, b0), l1 = fmaf(n.lo01.y, a0, b0);
-            const float l2 = fmaf(n.lo23.x, a0, b0), l3 = fmaf(n.lo23.y, a0, b0);
-            const float h0 = fmaf(n.hi01.x, a1, b1), h1 = fmaf(n.hi01.y, a1, b1);
-            const float h2 = fmaf(n.hi23.x, a1, b1), h3 = fmaf(n.hi23.y, a1, b1);
-#pragma unroll
-            for (int b = 0; b < B; b++) {
-                const float4 xl = xv[b][dw], xh = xv[b][8 + dw];
-                float t = alo[b];
-                t = fmaf(l0, xl.x, t);
-                t = fmaf(l1, xl.y, t);
-                t = fmaf(l2, xl.z, t);
-                t = fmaf(l3, xl.w, t);
-                alo[b] = t;
-                float u = ahi[b];
-                u = fmaf(h0, xh.x, u);
-                u = fmaf(h1, xh.y, u);
-                u = fmaf(h2, xh.z, u);
-                u = fmaf(h3, xh.w, u);
-                ahi[b] = u;
-            }
-        }
-#pragma unroll
-        for (int b = 0; b < B; b++) out[i][b] = alo[b] + ahi[b];
-    }
-}
-
-// Q6_K: xv[4g + i] = activations of group g (16 per group).
-template <int NR, int B>
-QD_DEV void dot_q6k(const RawQ6K (&r)[NR], const float4 (&xv)[B][16], int j, float (&out)[NR][B]) {
-#pragma unroll
-    for (int i = 0; i < NR; i++) {
-        float acc[B][4];
-#pragma unroll
-        for (int b = 0; b < B; b++)
-#pragma unroll
-            for (int g = 0; g < 4; g++) acc[b][g] = 0.f;
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-            uint32_t q[4];
-            q6k_qbytes(r[i], k, q);
-#pragma unroll
-            for (int g = 0; g < 4; g++) {
-                const float w0 = sbyte(q[g], 0), w1 = sbyte(q[g], 1);
-                const float w2 = sbyte(q[g], 2), w3 = sbyte(q[g], 3);
-#pragma unroll
-                for (int b = 0; b < B; b++) {
-                    const float4 xx = xv[b][4 * g + k];
-                    float s = acc[b][g];
-                    s = fmaf(w0, xx.x, s);
-                    s = fmaf(w1, xx.y, s);
-                    s = fmaf(w2, xx.z, s);
-                    s = fmaf(w3, xx.w, s);
-                    acc[b][g] = s;
-                }
-            }
-        }
-        const Q6Scales s = q6k_scales(r[i], j);
-#pragma unroll
-        for (int b = 0; b < B; b++) {
-            float u = s.sc[0] * acc[b][0];
-            u = fmaf(s.sc[1], acc[b][1], u);
-            u = fmaf(s.sc[2], acc[b][2], u);
-            u = fmaf(s.sc[3], acc[b][3], u);
-            out[i][b] = s.d * u;
-        }
-    }
-}
-
-// Q8_0: xv[0..7] block A (64c + 0..31), xv[8..15] block B.
-template <int NR, int B>
-QD_DEV void dot_q80(const RawQ80 (&r)[NR], const float4 (&xv)[B][16], float (&out)[NR][B]) {
-#pragma unroll
-    for (int i = 0; i < NR; i++) {
-        const float2 d = q80_d(r[i]);
-        float accA[B], accB[B];
-#pragma unroll
-        for (int b = 0; b < B; b++) { accA[b] = 0.f; accB[b] = 0.f; }
-#pragma unroll
-        for (int k = 0; k < 8; k++) {
-            const uint2 v = q80_qdwords(r[i], k);
-#pragma unroll
-            for (int b = 0; b < B; b++) {
-                const float4 xa = xv[b][k], xb = xv[b][8 + k];
-                float s = accA[b];
-                s = fmaf(sbyte(v.x, 0), xa.x, s);
-                s = fmaf(sbyte(v.x, 1), xa.y, s);
-                s = fmaf(sbyte(v.x, 2), xa.z, s);
-                s = fmaf(sbyte(v.x, 3), xa.w, s);
-                accA[b] = s;
-                float u = accB[b];
-                u = fmaf(sbyte(v.y, 0), xb.x, u);
-                u = fmaf(sbyte(v.y, 1), xb.y, u);
-                u = fmaf(sbyte(v.y, 2), xb.z, u);
-                u = fmaf(sbyte(v.y, 3), xb.w, u);
-                accB[b] = u;
-            }
-        }
-#pragma unroll
-        for (int b = 0; b < B; b++) out[i][b] = fmaf(d.y, accB[b], d.x * accA[b]);
-    }
-}
-
 // ------------------------------------------------------ one step ---
-// A lane's operands for one superunit: its share of the block (per row
-// stream) and its 64 activations (per batch row) from LDS.
-template <int FMT, int B, int NR>
+// A lane's share of one superunit (per row stream) out of the ring; the
+// activations are read as digits (qd_digits.h) while multiplying.
+template <int FMT, int NR>
 struct StepRegs {
     typename RawOf<FMT>::T raw[NR];
-    float4 xv[B][16];
 };
 
 // blk0: the lane group's superunit in row stream 0 (stream m is m * mstride
-// bytes further); su: its superunit index within the row.
-template <int FMT, int B, int NR>
-QD_DEV void read_step(StepRegs<FMT, B, NR> &st, const uint8_t *blk0, int mstride, const float *xl,
-                      int xstride, int su, int c) {
+// bytes further).
+template <int FMT, int NR>
+QD_DEV void read_step(StepRegs<FMT, NR> &st, const uint8_t *blk0, int mstride, int c) {
 #pragma unroll
     for (int m = 0; m < NR; m++) {
         const uint8_t *blk = blk0 + m * mstride;
@@ -268,30 +142,20 @@ QD_DEV void read_step(StepRegs<FMT, B, NR> &st, const uint8_t *blk0, int mstride
         else if constexpr (FMT == kQ6K) lds_q6k(st.raw[m], blk, c >> 1, c & 1);
         else lds_q80(st.raw[m], blk, c);
     }
-#pragma unroll
-    for (int b = 0; b < B; b++) {
-        const float *xb = xl + b * xstride;
-        if constexpr (FMT == kQ6K) {
-            const int base = su * kSuper + 128 * (c >> 1) + 16 * (c & 1);
-#pragma unroll
-            for (int gg = 0; gg < 4; gg++) {
-                const float4 *xg = reinterpret_cast<const float4 *>(xb + xphys(base + 32 * gg));
-#pragma unroll
-                for (int n = 0; n < 4; n++) st.xv[b][4 * gg + n] = xg[n];
-            }
-        } else {
-            const float4 *xp = reinterpret_cast<const float4 *>(xb + xphys(su * kSuper + 64 * c));
-#pragma unroll
-            for (int n = 0; n < 16; n++) st.xv[b][n] = xp[n];
-        }
-    }
 }
 
+// xd: the staged digits of superunit su of batch row 0; xsb: bytes per
+// batch row of staged digits.
 template <int FMT, int B, int NR>
-QD_DEV void dot_step(const StepRegs<FMT, B, NR> &st, const Q4Lane &L4, int c, float (&v)[NR][B]) {
-    if constexpr (FMT == kQ4K) dot_q4k<NR, B>(st.raw, st.xv, L4, v);
-    else if constexpr (FMT == kQ6K) dot_q6k<NR, B>(st.raw, st.xv, c & 1, v);
-    else dot_q80<NR, B>(st.raw, st.xv, v);
+QD_DEV void dot_step(const StepRegs<FMT, NR> &st, const uint8_t *xd, int xsb, const Q4Lane &L4, int c,
+                     float (&v)[NR][B]) {
+#pragma unroll
+    for (int m = 0; m < NR; m++)
+#pragma unroll
+        for (int b = 0; b < B; b++) v[m][b] = 0.f;
+    if constexpr (FMT == kQ4K) q4k_step_dig<NR, B>(st.raw, xd, xsb, c, L4, v);
+    else if constexpr (FMT == kQ6K) q6k_step_dig<NR, B>(st.raw, xd, xsb, c >> 1, c & 1, v);
+    else q80_step_dig<NR, B>(st.raw, xd, xsb, c, v);
 }
 
 // ------------------------------------------------ producer / consumer ---
@@ -299,15 +163,16 @@ QD_DEV void dot_step(const StepRegs<FMT, B, NR> &st, const Q4Lane &L4, int c, fl
 // wait on a workgroup barrier inside the stream.  A wave that issues copies
 // stalls at issue whenever the memory pipeline backs up, so the copying waves
 // do little else, and their copies are issued from scalar registers:
-//   * waves 0 .. NC-1 decode (consumers).  First they copy x (and the norm
-//     weight) into LDS, each a share of the 1 KB copies, and count
-//     themselves on `landed` once theirs have landed.  Then they stage x
-//     together, a 64-float4 slice at a time: x * w_norm in place, each
-//     wave's sum of squares of x (added in wave order, so the inverse RMS
-//     does not depend on timing), and for Q4_K the sum of every 32-run;
-//     they meet on `staged`.  Then consumer c takes steps c, c + NC, ...
-//     and, after reading a step out of its slot, stores the number of its
-//     steps read so far in done[c];
+//   * waves 0 .. NC-1 decode (consumers).  First they stage x as digits
+//     (qd_digits.h), one superunit of one batch row per slice, each wave
+//     its own slices: loaded straight into registers with the norm weight
+//     (each wave counts itself on `landed` once its first slices have
+//     arrived), x * w_norm, each wave's sum of squares of x (added in wave
+//     order, so the inverse RMS does not depend on timing), digits and run
+//     records into LDS; they meet on `staged`.  Then consumer c takes steps
+//     c, c + NC, ... and, after reading a step's weights out of its slot
+//     (the digits stay), stores the number of its steps read so far in
+//     done[c];
 //   * waves NC .. NC + 3 copy the weights (producers; as many as the launch
 //     asks for, 1, 2 or 4, and the others idle).  They issue nothing before x has landed, so
 //     x does not queue behind the weight stream.  Producer p takes the
@@ -350,8 +215,7 @@ __global__ __launch_bounds__(64 * (NC + kPcMaxProducers)) void stream_pc_kernel(
     const int S = (U + kStepUnits - 1) / kStepUnits;
 
     uint8_t *ring = smem;
-    float *xl = reinterpret_cast<float *>(smem + a.off_x);
-    float *nwl = reinterpret_cast<float *>(smem + a.off_nw);
+    uint8_t *xd = smem + a.off_x;  // [B][nb] staged digit superunits
     float *part = reinterpret_cast<float *>(smem + a.off_part);
     int *ready = reinterpret_cast<int *>(smem + a.off_red);
     int *done = ready + R;     // [NC]
@@ -359,7 +223,7 @@ __global__ __launch_bounds__(64 * (NC + kPcMaxProducers)) void stream_pc_kernel(
     int *staged = landed + 1;
     float *rinv = reinterpret_cast<float *>(staged + 1);  // [B]
     float *ssq = rinv + B;                                // [NC][B]
-    const int xstride = nb * kSuperPhys;
+    const int xsb = nb * kDigSU;  // bytes per batch row of staged digits
     const int64_t wbeg = r0 * a.row_bytes;
     const int off0 = (int)(wbeg & 15);
     const bool norm = a.norm_w != nullptr;
@@ -438,63 +302,59 @@ __global__ __launch_bounds__(64 * (NC + kPcMaxProducers)) void stream_pc_kernel(
         }
     } else {
         // -------------------------------------------------- consumers ---
-        // copy x: batch row b, physical float4 q of the row (17 per 64-float
-        // run, the last a pad that receives a copy of x[0]) holds logical
-        // float4 16 * (q / 17) + q % 17; then the norm weight.  Copy i of
-        // the workgroup (64 float4 each) is issued by wave i % NC.
-        {
-            const int nq = nb * (kSuperPhys / 4);
-            const int xc = (nq + 63) / 64;               // copies per batch row of x
-            const int nf4 = norm ? (int)(K / 4) : 0;
-            const int total = B * xc + (nf4 + 63) / 64;
-            int n = 0;
-            for (int i = wv; i < total; i += NC) {
-                if (i < B * xc) {
-                    const int b = i / xc;
-                    const int q0 = 64 * (i - b * xc);
-                    const int q = q0 + lane;
-                    const int run = q / 17, e = q - 17 * run;
-                    const float *xb = a.x + (int64_t)b * K;
-                    const float *srcp = (e < 16 && q < nq) ? xb + 4 * (16 * run + e) : xb;
-                    if (q0 + 64 <= nq || lane < nq - q0)
-                        lds_copy16(srcp, lds_addr(xl + b * xstride + 4 * q0));
-                } else {
-                    const int f0 = 64 * (i - B * xc);
-                    if (f0 + 64 <= nf4 || lane < nf4 - f0)
-                        lds_copy16(a.norm_w + 4 * (int64_t)(f0 + lane), lds_addr(nwl + 4 * f0));
-                }
-                if (++n == 48) { vm_wait<16>(); n = 16; }
-            }
-            vm_wait<0>();
-            if (lane == 0) lds_add(landed, 1);
-        }
-        // stage x: slice it (64 float4 of one batch row) goes to wave it % NC
-        lds_wait_eq(landed, NC);
-        const int F = nb * (kSuper / 4);  // logical float4 per batch row (a multiple of 64)
-        const int nit = F / 64;
+        // stage x as digits (qd_digits.h): slice it (one superunit of one
+        // batch row, 64 float4) goes to wave it % NC.  The wave loads a
+        // chunk of its slices straight into registers (x and the norm
+        // weight), counts itself on `landed` once its first chunk has
+        // arrived (the copying waves start then, so x does not queue behind
+        // the weight stream), multiplies by the norm weight, adds its sums
+        // of squares, and writes the digits.
+        const int nslices = B * nb;
         float ss[B];
 #pragma unroll
         for (int b = 0; b < B; b++) ss[b] = 0.f;
-        for (int it = wv; it < B * nit; it += NC) {
-            const int b = it / nit;
-            const int k = 4 * (64 * (it - b * nit) + lane);
-            float4 *ad = reinterpret_cast<float4 *>(xl + b * xstride + xphys(k));
-            float4 v = *ad;
-            if (norm) {
-                float sq = fmaf(v.x, v.x, 0.f);
-                sq = fmaf(v.y, v.y, sq);
-                sq = fmaf(v.z, v.z, sq);
-                sq = fmaf(v.w, v.w, sq);
+        constexpr int CH = 6;  // slices per chunk
+        for (int c0 = 0;; c0 += CH) {
+            float4 xv[CH], nv[CH];
 #pragma unroll
-                for (int bb = 0; bb < B; bb++)
-                    if (bb == b) ss[bb] += sq;
-                const float4 nw4 = *reinterpret_cast<const float4 *>(nwl + k);
-                v.x *= nw4.x;
-                v.y *= nw4.y;
-                v.z *= nw4.z;
-                v.w *= nw4.w;
-                *ad = v;
+            for (int i = 0; i < CH; i++) {
+                const int it = wv + NC * (c0 + i);
+                nv[i] = make_float4(1.f, 1.f, 1.f, 1.f);
+                if (it < nslices) {  // uniform per wave
+                    const int b = it / nb;
+                    const int64_t k = (int64_t)(it - b * nb) * kSuper + 4 * lane;
+                    xv[i] = *reinterpret_cast<const float4 *>(a.x + (int64_t)b * K + k);
+                    if (norm) nv[i] = *reinterpret_cast<const float4 *>(a.norm_w + k);
+                }
             }
+            if (c0 == 0) {
+                vm_wait<0>();
+                if (lane == 0) lds_add(landed, 1);
+            }
+#pragma unroll
+            for (int i = 0; i < CH; i++) {
+                const int it = wv + NC * (c0 + i);
+                if (it >= nslices) break;  // uniform per wave
+                const int b = it / nb;
+                const int su = it - b * nb;
+                float4 v = xv[i];
+                if (norm) {
+                    float sq = fmaf(v.x, v.x, 0.f);
+                    sq = fmaf(v.y, v.y, sq);
+                    sq = fmaf(v.z, v.z, sq);
+                    sq = fmaf(v.w, v.w, sq);
+#pragma unroll
+                    for (int bb = 0; bb < B; bb++)
+                        if (bb == b) ss[bb] += sq;
+                    v.x *= nv[i].x;
+                    v.y *= nv[i].y;
+                    v.z *= nv[i].z;
+                    v.w *= nv[i].w;
+                }
+                uint8_t *sup = xd + b * xsb + su * kDigSU;
+                stage_digits<FMT == kQ4K>(v, sup, 4 * lane);
+            }
+            if (wv + NC * (c0 + CH) >= nslices) break;
         }
         if (norm) {
 #pragma unroll
@@ -526,12 +386,12 @@ __global__ __launch_bounds__(64 * (NC + kPcMaxProducers)) void stream_pc_kernel(
             const int lr = uu / nb;
             const int su = uu - lr * nb;
             lds_wait_eq(&ready[slot], j);
-            StepRegs<FMT, B, NR> st;
-            read_step<FMT, B, NR>(st, ring + slot * NR * SLOTM + off0 + g * UB, SLOTM, xl, xstride, su, c);
+            StepRegs<FMT, NR> st;
+            read_step<FMT, NR>(st, ring + slot * NR * SLOTM + off0 + g * UB, SLOTM, c);
             lgkm_wait();  // the slot may be refilled from here on
             if (lane == 0) lds_flag(&done[wv], ++nread);
             float v[NR][B];
-            dot_step<FMT, B, NR>(st, L4, c, v);
+            dot_step<FMT, B, NR>(st, xd + su * kDigSU, xsb, L4, c, v);
 #pragma unroll
             for (int m = 0; m < NR; m++)
 #pragma unroll
@@ -587,9 +447,7 @@ size_t stream_pc_layout(int fmt, int batch, bool ffn, int nb, int units_max, int
                                                                 : StreamFmt<kQ80>::NCH;
     size_t off = (size_t)slots * NR * nch * 16;
     a->off_x = (int)off;
-    off += (size_t)batch * nb * kSuperPhys * 4;
-    a->off_nw = (int)off;
-    if (a->norm_w) off += (size_t)nb * kSuper * 4;
+    off += (size_t)batch * nb * kDigSU;
     a->off_part = (int)off;
     off += (size_t)NR * batch * units_max * 4;
     a->off_red = (int)off;  // ready[slots], done[consumers], landed, staged, rinv[batch], ssq[consumers][batch]

@@ -132,7 +132,7 @@ struct StreamArgs {
     int producers;          // copying waves (1, 2 or 4)
     int slots;              // ring slots (steps)
     int lag;                // steps in flight per copying wave
-    int off_x, off_nw, off_part, off_red;  // LDS layout (bytes)
+    int off_x, off_part, off_red;  // LDS layout (bytes): staged digits, row partials, flags
     int act;
     float eps;
     PostNorm pn;            // GEMV row epilogue (pn.w1 = nullptr: none)

@@ -242,9 +242,11 @@ def test_gemv_zero_weight_blocks(qd):
 
 def test_gemv_deterministic_and_batch_columns(qd):
     """Repeated calls are bitwise identical; with the same launch shape every
-    batch column equals the batch-1 result on that column, bitwise.  (The
-    automatic shape may split K differently for batch 8, whose staged x is 8
-    times larger; the shape is therefore forced here.)"""
+    batch column is computed on its own: batch 2 equals batch 1 on each
+    column (both on activation digits), batch 8 equals batch 3 on the columns
+    they share (both fp32), bitwise.  (The automatic shape may split K
+    differently for batch 8, whose staged x is 8 times larger; the shape is
+    therefore forced here.)"""
     say("gemv determinism")
     fmt, N, K = "q4_k", 1024, 2560
     W = dev(synth.quant_weights(fmt, N, K, SEED, tensor_id=31))
@@ -256,9 +258,13 @@ def test_gemv_deterministic_and_batch_columns(qd):
     try:
         qd.set_launch_override(2, 2, 1)
         y8 = qd.qgemv(fmt, W, xd).cpu().numpy()
-        for col in range(8):
+        y2 = qd.qgemv(fmt, W, dev(x[:2])).cpu().numpy()
+        for col in range(2):
             y1 = qd.qgemv(fmt, W, dev(x[col])).cpu().numpy()
-            assert np.array_equal(y1.view(np.uint32), y8[col].view(np.uint32)), col
+            assert np.array_equal(y1.view(np.uint32), y2[col].view(np.uint32)), col
+        for lo in (0, 3, 5):
+            y3 = qd.qgemv(fmt, W, dev(x[lo:lo + 3])).cpu().numpy()
+            assert np.array_equal(y3.view(np.uint32), y8[lo:lo + 3].view(np.uint32)), lo
     finally:
         qd.set_launch_override(0, 0, 0)
 

@@ -5,11 +5,13 @@ A Q4_K weight is d*sc*q - dmin*m.  In a sub-block with a constant quant q0
 and d*sc*q0 == dmin*m exactly, every weight is zero although both terms are
 large (up to ~0.6 here); with a few quants moved by +-1, a few weights are
 +-d*sc among zeros.  A kernel that applied the scale and the min per
-sub-block (d*sc*sum(q x) - dmin*m*sum(x)) would carry the rounding error of
-those large terms into an output whose bound, 1e-4 * sum|w x| + 1e-6, is set
-by the small weights alone (1e-6 for an all-zero row).  Every path forms
-each weight first, so all-zero rows come out as exact zeros and the rest
-within the bound: the register GEMV (several launch shapes, split-K across
+sub-block in fp32 (d*sc*sum(q x) - dmin*m*sum(x)) would carry the rounding
+error of those large terms into an output whose bound, 1e-4 * sum|w x| +
+1e-6, is set by the small weights alone (1e-6 for an all-zero row).  The
+batch-1..2 paths form sum(q X) and sum(X) exactly in integers and combine
+the two terms in fp64 (one rounding of the exact value), the batch-3..8
+paths form each weight first; either way all-zero rows come out as exact
+zeros and the rest within the bound: the register GEMV (several launch shapes, split-K across
 workgroups, row walks, batch 1-8), the LDS-streaming GEMV (automatic at
 K >= 8192 and forced at K = 2560 / 5376), the fused gate/up, the fused
 Q/K/V launch, the mixture-of-experts launches and the prefill GEMM.
