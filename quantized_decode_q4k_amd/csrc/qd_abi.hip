@@ -285,6 +285,7 @@ constexpr int kStreamMaxWait = 63;          // vmcnt limit: copies in flight per
 // tuning overrides (0 = automatic)
 std::atomic<int> g_stream_wpc{0}, g_stream_depth{0}, g_stream_consumers{0}, g_stream_producers{0};
 constexpr int64_t kStreamMinK = 8192;       // automatic use of the streaming kernel
+constexpr int64_t kStreamMinRowsTall = 65536;  // ... and for tall Q6_K / Q8_0 matrices at batch 1
 
 void stream_rows(int64_t N, int64_t K, int fmt, int wpc, const float *norm_w, qd::StreamArgs *a,
                  unsigned *grid) {
@@ -343,21 +344,21 @@ bool stream_plan_pc(int fmt, bool ffn, int64_t N, int64_t K, int batch, const fl
 // register-streaming kernel is used instead: batch > 2, Q8_0 rows of partial
 // superunits, a matrix whose size is not a multiple of 16 bytes, an LDS
 // layout that does not fit, and (unless overridden) plain GEMVs with K <
-// 8192.  The fused gate/up and the long-row GEMVs take the producer /
-// consumer kernel.  At batch 1: one workgroup per CU with 8 decoding waves,
-// 4 steps in flight per copying wave (fewer where the ring's slot-reuse
-// bound asks), and 4 copying waves when a workgroup's rows hold 256 KB or
-// more (2 below).  At batch 2 (8 decoding waves spill registers): 4
-// decoding waves, 2 copying waves, 3 steps in flight, one workgroup per CU
-// when its whole row range fits in the ring, else two.  Measured on MI355X
-// (graph replay, 1 GiB of rotating weights; two runs each), against the
-// register kernel:
-//   Gemma-3 gate/up 10240 x 2560:   10.9-11.1 us (13.4)
-//   Gemma-3 down Q6_K 2560 x 10240: 10.0 us (12.2)
-//   Gemma-4 gate/up 21504 x 5376:   29.8-30.5 us (33.9; 33.3 with 2 copying waves)
-//   Gemma-4 down Q6_K 5376 x 21504: 27.6-28.4 us (30.4; 29.5 with 2 copying waves)
-// K = 2560 plain GEMVs stay on the register kernel (lm_head 262144 rows:
-// 72-79 us against 87 or more on either streaming kernel).
+// 8192 other than the tall Q6_K / Q8_0 ones at batch 1.  The fused gate/up
+// and the long-row GEMVs take the producer / consumer kernel.  At batch 1:
+// one workgroup per CU with 8 decoding waves, 4 steps in flight per copying
+// wave (fewer where the ring's slot-reuse bound asks), and 4 copying waves
+// when a workgroup's rows hold 256 KB or more (2 below).  At batch 2 (8
+// decoding waves spill registers): 4 decoding waves, 2 copying waves, 3
+// steps in flight, one workgroup per CU when its whole row range fits in
+// the ring, else two.  Measured on MI355X (graph replay, 1 GiB of rotating
+// weights, after the clocks and the weight copies have warmed up), batch 1:
+//   Gemma-3 gate/up 10240 x 2560:   9.9-10.0 us
+//   Gemma-3 down Q6_K 2560 x 10240: 9.9-10.1 us
+//   Gemma-4 gate/up 21504 x 5376:   28.9-29.3 us
+//   Gemma-4 down Q6_K 5376 x 21504: 25.8-25.9 us
+//   lm_head 262144 x 2560: Q8_0 127.4 us (register kernel 141.6), Q6_K
+//   114.1 (123.0); Q4_K stays on the register kernel, 78-79 (88).
 bool stream_plan(int fmt, bool ffn, int64_t N, int64_t K, int batch, const float *norm_w,
                  qd::StreamArgs *a, unsigned *grid, size_t *lds) {
     if (batch > 2) return false;
@@ -370,7 +371,11 @@ bool stream_plan(int fmt, bool ffn, int64_t N, int64_t K, int batch, const float
         const int prod = g_stream_producers.load() ? g_stream_producers.load() : 2;
         return stream_plan_pc(fmt, ffn, N, K, batch, norm_w, wpc, cons ? cons : 8, prod, kPcLag, a, grid, lds);
     }
-    if (!ffn && K < kStreamMinK) return false;
+    // plain GEMVs: the long rows, and the tall Q6_K / Q8_0 matrices at batch
+    // 1 (lm_head 262144 x 2560, graph replay: Q8_0 141.6 -> 127.4 us, Q6_K
+    // 123.0 -> 114.1 us; Q4_K stays on the register kernel, 79 against 88)
+    const bool tall = batch == 1 && fmt != QD_Q4_K && N >= kStreamMinRowsTall;
+    if (!ffn && K < kStreamMinK && !tall) return false;
     if (batch == 1) {
         // steps in flight per copying wave (MI355X, decode FFN in graph
         // replay, medians of 6 interleaved runs; lag 3 / 4 / 5): Gemma-3

@@ -17,8 +17,8 @@
 //  * Decoding reads a lane group's block (4 lanes per superunit, the lane
 //    split of the GEMV kernels) and its activation digits from LDS, and
 //    writes the superunit's partial sum to LDS.  After the stream, each
-//    row's partials are added in superunit order, so a result does not
-//    depend on the launch shape.
+//    row's partials are added in an order fixed by the row length alone
+//    (8 lanes per row), so a result does not depend on the launch shape.
 //  * x is multiplied by the RMS-norm weight and staged once per workgroup
 //    as activation digits (qd_digits.h: exact integer products); the
 //    inverse RMS is applied to each row's sum at the end.
@@ -405,20 +405,27 @@ __global__ __launch_bounds__(64 * (NC + kPcMaxProducers)) void stream_pc_kernel(
     }
     block_sync();
 
-    // ---- rows: partials in superunit order, times the inverse RMS
+    // ---- rows: partials summed in a fixed order (lane t of a row's 8 adds
+    // superunits t, t + 8, ... in order, then the 8 sums are added by a
+    // fixed cross-lane tree), times the inverse RMS
     const int Umax = a.units_max;
-    for (int e = tid; e < cnt * B; e += NT) {
-        const int b = e / cnt;
-        const int lr = e - b * cnt;
+    const int l8 = tid & 7;
+    for (int e0 = 0; e0 < cnt * B; e0 += NT / 8) {
+        const int e = e0 + (tid >> 3);
+        const bool on = e < cnt * B;  // the same for the 8 lanes of a row
+        const int b = on ? e / cnt : 0;
+        const int lr = on ? e - b * cnt : 0;
         const int64_t row = r0 + lr;
         float sr[NR];
 #pragma unroll
         for (int m = 0; m < NR; m++) {
             const float *pp = part + (m * B + b) * Umax + lr * nb;
             float acc = 0.f;
-            for (int t = 0; t < nb; t++) acc += pp[t];
-            sr[m] = acc * rinv[b];
+            if (on)
+                for (int t = l8; t < nb; t += 8) acc += pp[t];
+            sr[m] = oct_sum(acc) * rinv[b];
         }
+        if (!on || l8 != 0) continue;
         if constexpr (FFN) {
             a.y[(int64_t)b * N + row] = act_apply(a.act, sr[0]) * sr[1];
             if (a.g_out) a.g_out[(int64_t)b * N + row] = sr[0];
