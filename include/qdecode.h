@@ -130,11 +130,17 @@ int qd_version(void);
  *   y      fp32 [batch][N], row-major; y[b][n] = sum_k w[n][k] * x[b][k]
  *
  * Accuracy: |y - y_exact| <= 1e-4 * sum_k |w[n][k] x[b][k]| + 1e-6, where w
- * is the exactly dequantised weight.  Every weight is formed in fp32 with
- * one rounding (Q4_K: d*scale*q - dmin*min as one fused multiply-add;
- * Q6_K and Q8_0 products are exact) before it meets its activation, so the
- * bound holds on every block, including blocks whose scale and min terms
- * cancel.
+ * is the exactly dequantised weight, on every block, including Q4_K blocks
+ * whose scale and min terms cancel.  Batch 1-2: each run of 32 activations
+ * is staged as 2^-s X with X a 31-bit integer (exact for activations within
+ * 2^7 of the run's largest magnitude, else rounded at 2^-31 of it), the
+ * products of integer quants and X are summed exactly (int8 dot products),
+ * and the block scales are applied per sub-block (Q4_K: scale and min terms
+ * combined in fp64 and rounded once; Q6_K, Q8_0: one fp32 product).  Batch
+ * 3-8: every weight is formed in fp32 with one rounding (Q4_K: d*scale*q -
+ * dmin*min as one fused multiply-add; Q6_K and Q8_0 products are exact)
+ * before it meets its activation.  A NaN or infinite activation makes every
+ * output it reaches non-finite.
  */
 qd_status qgemv_q4k(const void *W, const float *x, float *y, int64_t N,
                     int64_t K, int batch, void *stream);

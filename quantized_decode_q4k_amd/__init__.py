@@ -15,7 +15,7 @@ Entry points (same names as the C ABI):
     qquantize_q8_act, qgemv_q8_0_preq              its two halves: quantize once, GEMV on the codes
     qqkv_proj                                      q, k, v = Wq xn, Wk xn, Wv xn (one launch)
     qffn_gate_up_act                               h = act(Wg xn) * (Wu xn)
-    qffn_decode                                    y = Wd h (whole FFN, one launch)
+    qffn_decode                                    y = Wd h (whole FFN: gate/up launch, then down)
     qffn_decode_noalloc                            qffn_decode with no allocation (fixed scratch)
     qffn_decode_residual                           y = Wd h + r
     qmoe_ffn_decode                                mixture-of-experts FFN (routed ids on device)

@@ -1,5 +1,7 @@
 // qd_gemv.hip -- batch-1..8 GEMV and fused FFN gate+up over Q4_K, Q6_K and
-// Q8_0 weights, dequantised in registers and fused into fp32 FMAs.
+// Q8_0 weights, decoded in registers: exact integer dot products against
+// activation digits at batch 1-2 (qd_digits.h), fp32 FMAs on weights
+// dequantised one at a time at batch 3-8.
 //
 // What is computed: y[b][n] = sum_k w[n][k] x[b][k] for the decode-path
 // projections of the larql "Architecture -> Metal shader map" page (Gemma 3
@@ -22,15 +24,18 @@
 //    go to a workspace and the last workgroup to finish a row tile sums them
 //    in slice order.
 //  * x (optionally RMS-normalised on the way in) is staged once per
-//    workgroup in LDS with a 16-byte skew every 64 floats, so the four lanes
-//    of a group, which read the same offsets 64 floats apart, hit different
+//    workgroup in LDS: at batch 1-2 as activation digits (qd_digits.h), at
+//    batch 3-8 as fp32 with a 16-byte skew every 64 floats; either way the
+//    four lanes of a group, which read positions 64 apart, hit different
 //    banks.
-//  * Decoding: Q4_K nibbles become floats through the fp8 converter (two
-//    per instruction, exact) and each weight is formed with one fused
-//    multiply-add of its sub-block's scale and min; Q6_K quants become
-//    signed (q - 32) bytes with a byte-permute lookup of the high bits, then
-//    one sign-extending convert, and Q8_0 bytes take one sign-extending
-//    convert, their (exact) scales applied once per 16 or 32 weights.
+//  * Decoding at batch 3-8: Q4_K nibbles become floats through the fp8
+//    converter (two per instruction, exact) and each weight is formed with
+//    one fused multiply-add of its sub-block's scale and min; Q6_K quants
+//    become signed (q - 32) bytes with a byte-permute lookup of the high
+//    bits, then one sign-extending convert, and Q8_0 bytes take one
+//    sign-extending convert, their (exact) scales applied once per 16 or 32
+//    weights.  At batch 1-2 the same bytes go into v_dot4_i32_i8 against
+//    the digit planes.
 //  * Per-lane partials are reduced across the 4*p_in lanes of a row with
 //    cross-lane shuffles; one lane writes each output (and, for the fused
 //    FFN, applies the GELU-tanh or SiLU product).
