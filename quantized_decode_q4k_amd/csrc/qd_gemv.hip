@@ -236,8 +236,9 @@ QD_DEV void store_out(float *p, float v) { *p = v; }
 
 // One workgroup tile: rows [bx * rows_per_wg, ...) over K-slice ks of
 // p_out.  FMT: block format; B: batch rows (1..8); NR: row streams per lane
-// group (FFN: 2 = gate, up); FFN: fused gate/up/activation epilogue.
-template <int FMT, int B, int NR, bool FFN>
+// group (FFN: 2 = gate, up); FFN: fused gate/up/activation epilogue; DIG:
+// activation digits and integer dot products (batch 1-2), else fp32.
+template <int FMT, int B, int NR, bool FFN, bool DIG>
 QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out, float *smem) {
     const int tid = threadIdx.x;
     const int c = tid & 3;
@@ -251,7 +252,7 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
     const int xstride = a.nk * kSuperPhys;
     // batch 1-2: activation digits (qd_digits.h), nk * kDigSU bytes per
     // batch row; else fp32 activations, nk * 272 floats per batch row
-    constexpr bool DIG = B <= 2;
+    static_assert(!DIG || B <= 2, "activation digits: batch 1-2");
     const int xsb = a.nk * kDigSU;
     float *xl = smem;                                 // [B][nk * 272] or digits
     float *red = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(smem) +
@@ -574,10 +575,10 @@ QD_DEV void mv_tile(const MvArgs &a, const int bx, const int ks, const int p_out
     if (!FFN && a.pn.w1) post_norm_tail<kThreads>(a.pn, a.y, B, N, red, &s_last);
 }
 
-template <int FMT, int B, int NR, bool FFN>
+template <int FMT, int B, int NR, bool FFN, bool DIG>
 __global__ __launch_bounds__(kThreads) void mv_kernel(MvArgs a) {
     extern __shared__ __attribute__((aligned(16))) float smem[];
-    mv_tile<FMT, B, NR, FFN>(a, blockIdx.x, blockIdx.y, gridDim.y, smem);
+    mv_tile<FMT, B, NR, FFN, DIG>(a, blockIdx.x, blockIdx.y, gridDim.y, smem);
 }
 
 // ------------------------------------------- mixture-of-experts decode ---
@@ -612,10 +613,10 @@ __global__ __launch_bounds__(kThreads) void moe_kernel(MvArgs a) {
                 if (r0 + r < a.N) b.y[r0 + r] = 0.f;
             return;
         }
-        mv_tile<FMT, 1, 2, true>(b, blockIdx.x, 0, 1, smem);
+        mv_tile<FMT, 1, 2, true, false>(b, blockIdx.x, 0, 1, smem);
     } else {
         b.x = a.x + (int64_t)slot * a.x_sstride;
-        mv_tile<FMT, 1, 1, false>(b, blockIdx.x, slot, gridDim.y, smem);
+        mv_tile<FMT, 1, 1, false, false>(b, blockIdx.x, slot, gridDim.y, smem);
     }
 }
 
@@ -663,9 +664,9 @@ __global__ __launch_bounds__(kThreads) void qkv_kernel(QkvArgs q) {
     }
     const MvArgs &a = q.a[s];
     switch (q.fmt[s]) {
-    case kQ4K: mv_tile<kQ4K, B, 1, false>(a, t, 0, 1, smem); break;
-    case kQ6K: mv_tile<kQ6K, B, 1, false>(a, t, 0, 1, smem); break;
-    default: mv_tile<kQ80, B, 1, false>(a, t, 0, 1, smem); break;
+    case kQ4K: mv_tile<kQ4K, B, 1, false, false>(a, t, 0, 1, smem); break;
+    case kQ6K: mv_tile<kQ6K, B, 1, false, false>(a, t, 0, 1, smem); break;
+    default: mv_tile<kQ80, B, 1, false, false>(a, t, 0, 1, smem); break;
     }
 }
 
@@ -690,10 +691,23 @@ size_t mv_lds_bytes(int fmt, int batch, int nk) {
     return x + 4 * 8 * sizeof(float);  // cross-wave scratch: [4 waves][batch]
 }
 
+// Activation digits for the batch-1..2 register GEMVs of tall matrices,
+// where the decode's VALU work matters (lm_head 262144 x 2560 Q4_K, graph
+// replay: 86 -> 78 us); the smaller, latency-bound shapes (and the Q/K/V
+// and MoE launches) stage fp32, whose staging is shorter (Gemma-3 Q/K/V in
+// one launch: 8.1 us on digits, 7.6 on fp32).
+constexpr int64_t kDigMinRows = 16384;
+
 template <int FMT, int B, int NR, bool FFN>
 static hipError_t launch_one(const MvArgs &a, dim3 grid, hipStream_t st) {
     size_t lds = mv_lds_bytes(FMT, B, a.nk);
-    hipLaunchKernelGGL((mv_kernel<FMT, B, NR, FFN>), grid, dim3(kThreads), lds, st, a);
+    if constexpr (B <= 2) {
+        if (a.N >= kDigMinRows) {
+            hipLaunchKernelGGL((mv_kernel<FMT, B, NR, FFN, true>), grid, dim3(kThreads), lds, st, a);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((mv_kernel<FMT, B, NR, FFN, false>), grid, dim3(kThreads), lds, st, a);
     return hipGetLastError();
 }
 
