@@ -248,8 +248,9 @@ qd_status qgemv_residual(qd_format fmt, const void *W, const float *x, const flo
  *   y[b]   = r[b] + p * post_w / sqrt(mean(p^2) + eps)
  *   y2[b]  = y[b] * next_w / sqrt(mean(y[b]^2) + eps)   (only with next_w)
  * The norm of p needs the whole output row: every workgroup stores its
- * rows of p in the stream's workspace, and the last workgroup to finish
- * (a release / acquire counter) forms y and y2 with sums in a fixed order.
+ * rows of p in the stream's workspace (device-coherent stores), and the
+ * last workgroup to finish (a device-scope counter, counted only after its
+ * stores have completed) forms y and y2 with sums in a fixed order.
  *
  *   fmt, W, x, N, K, batch   as qgemv
  *   post_w  fp32 [N] post-norm weight, multiplied directly (the page's
