@@ -512,6 +512,19 @@ qd_status qdequant_bf16(qd_format fmt, const void *W, uint16_t *out,
 qd_status qd_set_launch_override(int p_in, int p_out, int nr);
 
 /*
+ * Batch path of qgemv*, qffn_gate_up_act and qffn_decode* at batch 3..64
+ * (process-wide; tuning and comparisons):
+ *   0  automatic: the matrix-core kernels, which stream the weights once
+ *      per call for every batch row (integer products of the quants with
+ *      the activations' digits, the same result class as batch 1..2)
+ *   1  the fp32 register kernel, in launches of up to 8 batch rows
+ * k_slices: K-slices across workgroups of the matrix-core kernels (0 =
+ * automatic; else 1..1024, capped at the row's superunits of 256 weights).
+ * Returns QD_EINVAL for other values.
+ */
+qd_status qd_set_batch_override(int mode, int k_slices);
+
+/*
  * Row slots each lane group of the register-streaming GEMV walks one after
  * another (process-wide; 0 = automatic, else 1..64).  Larger values give
  * each workgroup more rows for the one staging of its activation slice.

@@ -81,6 +81,7 @@ SIGNATURES = {
     "qd_set_walk_override": (_I, [_I]),
     "qd_set_gemm_override": (_I, [_I, _I]),
     "qd_set_stream_override": (_I, [_I, _I, _I, _I]),
+    "qd_set_batch_override": (_I, [_I, _I]),
     "qd_plan_q8act": (_I, [_I64, _I64, _I, _P]),
 }
 
@@ -524,6 +525,13 @@ def set_stream_override(wg_per_cu: int = 0, depth: int = 0, consumers: int = 0, 
     (1, 2 or 4)."""
     _check("qd_set_stream_override",
            lib().qd_set_stream_override(wg_per_cu, depth, consumers, producers))
+
+
+def set_batch_override(mode: int = 0, k_slices: int = 0):
+    """Batch 3..64 path: 0 = the matrix-core kernels (automatic), 1 = the fp32
+    register kernel in launches of 8 batch rows; k_slices = K-slices of the
+    matrix-core kernels (0 = automatic)."""
+    _check("qd_set_batch_override", lib().qd_set_batch_override(mode, k_slices))
 
 
 def set_walk_override(rows_per_group: int = 0):

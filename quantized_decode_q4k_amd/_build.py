@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libqdecode.so")
 
-SOURCES = ["qd_abi.hip", "qd_gemv.hip", "qd_gemv_stream.hip", "qd_gemv_i8.hip", "qd_dequant.hip",
+SOURCES = ["qd_abi.hip", "qd_gemv.hip", "qd_gemv_stream.hip", "qd_gemv_mfma.hip", "qd_gemv_i8.hip", "qd_dequant.hip",
            "qd_prefill.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -30,9 +30,15 @@ FLAGS = [
 ]
 
 
+# Per-file device flags: the batch GEMV's products are read by the vector
+# ALU right away, so its MFMA results go to ordinary vector registers (no
+# accumulation-register copies).
+FILE_FLAGS = {"qd_gemv_mfma.hip": ["-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

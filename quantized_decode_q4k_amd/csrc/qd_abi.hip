@@ -269,6 +269,81 @@ qd_status scratch_workspace(Workspace *out) {
     return QD_OK;
 }
 
+// Compute units of the current device (asked once per device).
+int cu_count() {
+    static std::mutex mu;
+    static std::map<int, int> cus;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = cus.find(dev);
+    if (it != cus.end()) return it->second;
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+    return n;
+}
+
+// ------------------------------------------------ matrix-core batch path ---
+// Batch 3..64 (qd_gemv_mfma.hip): the call's activation digits, then one
+// launch that streams the weights once for every batch row.  Process-wide
+// mode (qd_set_batch_override): 0 = automatic (matrix cores from batch 3
+// on), 1 = the fp32 register kernel in launches of up to 8 batch rows.
+std::atomic<int> g_batch_mode{0}, g_mq_pout{0};
+
+size_t round64(size_t n) { return (n + 63) / 64 * 64; }
+
+struct MqPlan {
+    int ng = 1, nb = 0, nk = 1, p_out = 1;
+    int64_t tiles = 0;
+    size_t dig_floats = 0, part_floats = 0;
+    size_t floats() const { return dig_floats + part_floats; }
+};
+
+MqPlan mq_plan(int fmt, int64_t N, int64_t K, int batch, bool ffn) {
+    MqPlan p;
+    p.ng = batch <= 8 ? 1 : batch <= 16 ? 2 : batch <= 32 ? 4 : 8;
+    const int nb = (int)((K + qd::kSuper - 1) / qd::kSuper);
+    p.nb = nb;
+    p.tiles = (N + qd::mq_tile_rows(ffn) - 1) / qd::mq_tile_rows(ffn);
+    // K-slices: the fewest superunits on the busiest slot, counting the
+    // rounds of workgroups the resident slots take (the fewest slices among
+    // equals: less split-K traffic)
+    const int64_t slots = (int64_t)cu_count() * qd::mq_wg_per_cu(fmt, p.ng, ffn);
+    int64_t best = INT64_MAX;
+    for (int po = 1; po <= nb; po++) {
+        if (po > 1 && p.tiles > kMaxTiles) break;  // a counter per row tile
+        const int nk = (nb + po - 1) / po;
+        const int pp = (nb + nk - 1) / nk;
+        if (pp != po) continue;
+        // a workgroup's start (digits, first loads) costs about two
+        // superunits; the last workgroup of a tile reads its slices' partial
+        // sums about 8 at a time, each batch about one superunit
+        const int64_t cost = (p.tiles * pp + slots - 1) / slots * (nk + 2) + (pp > 1 ? (pp + 7) / 8 : 0);
+        if (cost < best) {
+            best = cost;
+            p.nk = nk;
+            p.p_out = pp;
+        }
+    }
+    if (const int fo = g_mq_pout.load()) {  // tuning override
+        const int po = std::min(fo, p.tiles > kMaxTiles ? 1 : nb);
+        p.nk = (nb + po - 1) / po;
+        p.p_out = (nb + p.nk - 1) / p.nk;
+    }
+    p.dig_floats = round64((size_t)p.ng * nb * qd::mq_su_bytes_host(fmt) / 4);
+    p.part_floats = p.p_out > 1 ? (size_t)p.p_out * batch * (ffn ? 2 : 1) * N : 0;
+    return p;
+}
+
+bool launch_forced() { return g_over_pin.load() || g_over_pout.load() || g_over_nr.load(); }
+// (a Q8_0 row whose length is not a multiple of 256 has a partial last
+// superunit, which the matrix kernel's whole-unit tile reads do not take)
+bool use_mq(int batch, int64_t K) {
+    return batch >= 3 && K % qd::kSuper == 0 && K <= qd::xdig_max_k() && g_batch_mode.load() == 0 &&
+           !launch_forced();
+}
+
 // ------------------------------------------------------------- checks ---
 qd_status check_shape(int fmt, int64_t N, int64_t K, int batch) {
     if (block_elems(fmt) == 0) return QD_EINVAL;
@@ -435,6 +510,55 @@ qd_status run_mv(int fmt, bool ffn, const void *W0, const void *W1, const float 
     if (res && (ffn || (res != y && overlap(res, ybytes, y, ybytes)))) return QD_EINVAL;
     if (res && overlap(res, ybytes, post.y2, ybytes)) return QD_EINVAL;
     if (res && !aligned(res, 4)) return QD_EALIGN;
+    if (use_mq(batch, K)) {
+        hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+        const MqPlan p = mq_plan(fmt, N, K, batch, ffn);
+        const size_t p_floats = pnorm ? (size_t)batch * N : 0;
+        Workspace w;
+        st = acquire_ws(hs, ws_offset + p.floats() + p_floats, fixed, &w);
+        if (st != QD_OK) return st;
+        float *base = w.partials + ws_offset;
+        qd::XdArgs xa{};
+        xa.x = x;
+        xa.norm_w = norm_w;
+        xa.eps = eps;
+        xa.dig = reinterpret_cast<uint8_t *>(base);
+        xa.K = K;
+        xa.R = (int)(K / 32);
+        xa.nb = p.nb;
+        xa.batch = batch;
+        if (qd::launch_xdig(xa, p.ng, fmt == QD_Q4_K, hs) != hipSuccess) return QD_ELAUNCH;
+        qd::MqArgs a{};
+        a.W0 = static_cast<const uint8_t *>(W0);
+        a.W1 = static_cast<const uint8_t *>(W1);
+        a.dig = xa.dig;
+        a.y = y;
+        a.g_out = g_out;
+        a.u_out = u_out;
+        a.res = pnorm ? nullptr : res;
+        a.partials = base + p.dig_floats;
+        a.counters = w.counters;
+        a.N = N;
+        a.K = K;
+        a.row_bytes = row_bytes(fmt, K);
+        a.nb = (int)((K + qd::kSuper - 1) / qd::kSuper);
+        a.nblk = (int)(K / block_elems(fmt));
+        a.nk = p.nk;
+        a.batch = batch;
+        a.act = act;
+        if (pnorm) {
+            a.pn.w1 = post.w1;
+            a.pn.w2 = post.w2;
+            a.pn.r = res;
+            a.pn.y2 = post.y2;
+            a.pn.p = base + p.floats();
+            a.pn.ctr = w.counters + kMaxTiles;  // auxiliary counter 0
+            a.pn.tiles = (unsigned)p.tiles;
+            a.pn.eps = post.eps;
+        }
+        const hipError_t e = qd::launch_mq(fmt, p.ng, ffn, a, (unsigned)p.tiles, (unsigned)p.p_out, hs);
+        return e == hipSuccess ? QD_OK : QD_ELAUNCH;
+    }
     if (batch > QD_BATCH_CHUNK) {
         // successive launches of up to QD_BATCH_CHUNK columns
         for (int c0 = 0; c0 < batch; c0 += QD_BATCH_CHUNK) {
@@ -465,8 +589,7 @@ qd_status run_mv(int fmt, bool ffn, const void *W0, const void *W1, const float 
         pn.eps = post.eps;
     };
     const size_t p_floats = pnorm ? (size_t)batch * N : 0;
-    const bool forced = g_over_pin.load() || g_over_pout.load() || g_over_nr.load();
-    if (!forced) {
+    if (!launch_forced()) {
         qd::StreamArgs sa{};
         unsigned grid = 0;
         size_t lds = 0;
@@ -558,7 +681,8 @@ qd_status run_ffn_decode(int fmt_gu, const void *Wg, const void *Wu, int fmt_d, 
         if (h_out && overlap(post.y2, xbytes, h_out, hbytes)) return QD_EINVAL;
     }
     if (res && !aligned(res, 4)) return QD_EALIGN;
-    if (batch > QD_BATCH_CHUNK) {
+    const bool mq = use_mq(batch, K) && use_mq(batch, N_ff);
+    if (!mq && batch > QD_BATCH_CHUNK) {
         for (int c0 = 0; c0 < batch; c0 += QD_BATCH_CHUNK) {
             const int nb = std::min(QD_BATCH_CHUNK, batch - c0);
             const int64_t xo = (int64_t)c0 * K;
@@ -576,11 +700,16 @@ qd_status run_ffn_decode(int fmt_gu, const void *Wg, const void *Wu, int fmt_d, 
     const size_t h_floats = h_out ? 0 : (((size_t)batch * N_ff + 63) / 64) * 64;
     // size the workspace once for h and both calls' split-K partials, so
     // that neither call reallocates it under h
-    const Plan qa = choose_plan(fmt_gu, N_ff, K, batch, true);
-    const Plan qb = choose_plan(fmt_d, K, N_ff, batch, false);
-    const size_t need_a = qa.s.p_out > 1 ? (size_t)qa.s.p_out * batch * 2 * N_ff : 0;
-    const size_t need_b = (qb.s.p_out > 1 ? (size_t)qb.s.p_out * batch * K : 0) +
-                          (post.w1 ? (size_t)batch * K : 0);
+    size_t need_a = 0, need_b = post.w1 ? (size_t)batch * K : 0;
+    if (mq) {
+        need_a = mq_plan(fmt_gu, N_ff, K, batch, true).floats();
+        need_b += mq_plan(fmt_d, K, N_ff, batch, false).floats();
+    } else {
+        const Plan qa = choose_plan(fmt_gu, N_ff, K, batch, true);
+        const Plan qb = choose_plan(fmt_d, K, N_ff, batch, false);
+        need_a = qa.s.p_out > 1 ? (size_t)qa.s.p_out * batch * 2 * N_ff : 0;
+        need_b += qb.s.p_out > 1 ? (size_t)qb.s.p_out * batch * K : 0;
+    }
     float *h = h_out;
     if (h_floats + std::max(need_a, need_b) > 0) {
         Workspace w;
@@ -1266,6 +1395,14 @@ qd_status qd_plan_q8act(int64_t N, int64_t K, int batch, int32_t *out) {
 qd_status qd_set_walk_override(int rows_per_group) {
     if (rows_per_group < 0 || rows_per_group > 64) return QD_EINVAL;
     g_over_rpg.store(rows_per_group);
+    return QD_OK;
+}
+
+qd_status qd_set_batch_override(int mode, int k_slices) {
+    if (mode != 0 && mode != 1) return QD_EINVAL;
+    if (k_slices < 0 || k_slices > 1024) return QD_EINVAL;
+    g_batch_mode.store(mode);
+    g_mq_pout.store(k_slices);
     return QD_OK;
 }
 

@@ -94,13 +94,14 @@ QD_DEV uint32_t digit_plane(uint32_t y0, uint32_t y1, uint32_t y2, uint32_t y3) 
     return (lo | hi) ^ 0x80808080u;
 }
 
-// Stage activations pos..pos+3 (v, already normalised) of a staged
-// superunit whose bytes start at `su`.  Called by the 8 consecutive threads
-// that hold one run (lane & 7 = the float4 of the run; pos = 32 * run + 4 *
-// (lane & 7), the 8 lanes of a DPP half-row); all 8 must be active.  SX: the
-// format needs the run sums (Q4_K's min term).
+// Digits of one run of 32 activations held by 8 consecutive lanes (lane & 7
+// = the float4 of the run, the 8 lanes of a DPP half-row; all 8 must be
+// active): this lane's four plane dwords (byte e of plane k = digit k of
+// activation e of v) and the run's scale 2^-s and, with SX, its sum of X
+// times 2^-s (exact in fp64; 0 without SX).  A run holding a NaN or an
+// infinity gets a NaN scale.
 template <bool SX>
-QD_DEV void stage_digits(float4 v, uint8_t *su, int pos) {
+QD_DEV void digitize_run(float4 v, uint32_t (&pl)[4], double &scale, double &sxs) {
     // largest |x| of the run, compared as bit patterns (a NaN or an infinity
     // compares above every finite value)
     uint32_t m = max(max(fbits(v.x) & 0x7FFFFFFFu, fbits(v.y) & 0x7FFFFFFFu),
@@ -115,26 +116,39 @@ QD_DEV void stage_digits(float4 v, uint8_t *su, int pos) {
     const int X2 = (int)rintf(ldexpf(v.z, s)), X3 = (int)rintf(ldexpf(v.w, s));
     const uint32_t y0 = (uint32_t)X0 + 0x80808080u, y1 = (uint32_t)X1 + 0x80808080u;
     const uint32_t y2 = (uint32_t)X2 + 0x80808080u, y3 = (uint32_t)X3 + 0x80808080u;
-    const uint32_t p0 = digit_plane<0>(y0, y1, y2, y3), p1 = digit_plane<1>(y0, y1, y2, y3);
-    const uint32_t p2 = digit_plane<2>(y0, y1, y2, y3), p3 = digit_plane<3>(y0, y1, y2, y3);
-    *reinterpret_cast<uint32_t *>(su + dig_at(pos, 0)) = p0;
-    *reinterpret_cast<uint32_t *>(su + dig_at(pos, 1)) = p1;
-    *reinterpret_cast<uint32_t *>(su + dig_at(pos, 2)) = p2;
-    *reinterpret_cast<uint32_t *>(su + dig_at(pos, 3)) = p3;
-    // the run's sum of X, from its digit sums (each below 2^12 in magnitude)
-    int s0 = 0, s1 = 0, s2 = 0, s3 = 0;
+    pl[0] = digit_plane<0>(y0, y1, y2, y3);
+    pl[1] = digit_plane<1>(y0, y1, y2, y3);
+    pl[2] = digit_plane<2>(y0, y1, y2, y3);
+    pl[3] = digit_plane<3>(y0, y1, y2, y3);
+    scale = bad ? __builtin_nan("") : ldexp(1.0, -s);
+    sxs = 0.0;
     if constexpr (SX) {
-        s0 = sum8(dot4(p0, 0x01010101u, 0));
-        s1 = sum8(dot4(p1, 0x01010101u, 0));
-        s2 = sum8(dot4(p2, 0x01010101u, 0));
-        s3 = sum8(dot4(p3, 0x01010101u, 0));
+        // the run's sum of X, from its digit sums (each below 2^12 in magnitude)
+        const int s0 = sum8(dot4(pl[0], 0x01010101u, 0));
+        const int s1 = sum8(dot4(pl[1], 0x01010101u, 0));
+        const int s2 = sum8(dot4(pl[2], 0x01010101u, 0));
+        const int s3 = sum8(dot4(pl[3], 0x01010101u, 0));
+        sxs = fma((double)(s3 * 256 + s2), 65536.0, (double)(s1 * 256 + s0)) * scale;
     }
+}
+
+// Stage activations pos..pos+3 (v, already normalised) of a staged
+// superunit whose bytes start at `su`.  Called by the 8 consecutive threads
+// that hold one run (lane & 7 = the float4 of the run; pos = 32 * run + 4 *
+// (lane & 7), the 8 lanes of a DPP half-row); all 8 must be active.  SX: the
+// format needs the run sums (Q4_K's min term).
+template <bool SX>
+QD_DEV void stage_digits(float4 v, uint8_t *su, int pos) {
+    uint32_t pl[4];
+    double sc, sxs;
+    digitize_run<SX>(v, pl, sc, sxs);
+#pragma unroll
+    for (int k = 0; k < 4; k++) *reinterpret_cast<uint32_t *>(su + dig_at(pos, k)) = pl[k];
     if ((pos & 31) == 0) {
-        const double sc = bad ? __builtin_nan("") : ldexp(1.0, -s);
         RunRec rec;
         rec.scale = (float)sc;
         rec.pad = 0;
-        rec.sxs = fma((double)(s3 * 256 + s2), 65536.0, (double)(s1 * 256 + s0)) * sc;
+        rec.sxs = sxs;
         *reinterpret_cast<RunRec *>(su + kDigRuns + 16 * (pos >> 5)) = rec;
     }
 }

@@ -1,0 +1,787 @@
+// qd_gemv_mfma.hip -- batch 3..64 GEMVs and fused gate/up on the matrix
+// cores, the weights streamed once per call.
+//
+// What is computed is the same y = sum_k w_k x_k as everywhere in this
+// library (larql "Architecture -> Metal shader map": the Q4_K / Q6_K
+// matvec and gate/up rows of the Gemma 3 and Gemma 4 tables; dotLLM PR #320:
+// matmul_q8_0 and the batched ForwardBatch GEMM that streams each weight
+// once for all the tokens of a step).  The arithmetic is the integer form of
+// qd_digits.h, spread over the matrix cores:
+//
+//  * Activations (normalised first when an RMS-norm weight is given) are
+//    written once per call by xdig_kernel as the 31-bit integers X of each
+//    run of 32 (one exponent per run and batch row), split into four signed
+//    byte planes.  The planes of 8 batch rows form the A operand of one
+//    v_mfma_i32_32x32x32_i8: 32 A rows = (batch row bb, plane p) at row
+//    bb + 8p, 32 k = the run's activations.  One 1 KB "fragment" per (group
+//    of 8 batch rows, run), laid out exactly as the 64 lanes read it
+//    (lane l: row l % 32, k = 16 (l / 32) .. +15).
+//  * A wave owns 32 weight rows; its 64 lanes hold the integer quants of
+//    one sub-block of those rows as the B operand (lane l: row l % 32, the
+//    16 quants k = 16 (l / 32) .. +15).  The product is, for every (batch
+//    row, plane, weight row), the exact integer sum of quant x digit over
+//    the sub-block.  The output registers of lane l hold all four planes of
+//    the batch rows 4 (l / 32) .. +3 for its weight row, so the planes are
+//    recombined and the block scales applied in the lane: Q4_K in fp64
+//    (d sc 2^-s I - dmin m 2^-s sum X, no cancellation), Q6_K and Q8_0 in
+//    fp32, as in the batch-1..2 kernels.
+//  * Q6_K sub-blocks hold 16 weights: one instruction takes the two
+//    sub-blocks of a run, A rows 0..15 (4 batch rows x 4 planes) seeing only
+//    k < 16 and rows 16..31 only k >= 16 (the other half of A is zero), so
+//    each lane still loads 16 consecutive quant bytes.
+//
+// A workgroup is 4 waves, 128 weight rows, over a K-slice of superunits;
+// the fragments and run records of the next superunit are loaded into
+// registers while the current one is multiplied and written to the other
+// half of a double-buffered LDS area before a barrier.  Each lane loads its
+// weight bytes straight into registers (16-byte loads; Q6_K and Q8_0
+// blocks are 2-byte aligned, which the hardware reads unaligned), a few
+// superunits ahead.  Split-K slices end in the deterministic last-arriver
+// sum of qd_epilogue.h.
+#include <type_traits>
+
+#include "qd_digits.h"
+#include "qd_epilogue.h"
+#include "qd_lds.h"
+
+namespace qd {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+// ------------------------------------------------------ activation digits ---
+// Bytes of one superunit (8 runs) of one group of 8 batch rows: the 8 runs'
+// fragments, then their records (RR bytes per run: 8 records).  The
+// digits of a call are [group][superunit] of these, the layout the matrix
+// kernel copies to LDS as it is.
+__host__ __device__ constexpr int mq_su_bytes(int rr) { return 8 * kFragRun + 8 * rr; }
+
+// One workgroup of 1024 threads per batch row (ng * 8 rows; rows past
+// `batch`, and runs past K / 32, are written as zeros).  Each thread holds
+// up to kXdF float4 of the row (8 consecutive threads = one run), all loaded
+// before the first is used: the row's mean square (RMS-norm) and its digits
+// come from one pass over x.
+constexpr int kXdThreads = 1024;
+constexpr int kXdF = 8;   // float4 per thread: rows of up to 8 * 1024 * 4 = 32768 activations
+template <bool NORM, bool SX>
+__global__ __launch_bounds__(kXdThreads) void xdig_kernel(XdArgs a) {
+    __shared__ float red[kXdThreads / 64];
+    const int tid = threadIdx.x;
+    const int b = blockIdx.x;
+    const bool live = b < a.batch;
+    const int F = a.R * 8;            // float4 of the row
+    const int Fp = a.nb * 64;         // float4 of the padded row (8 runs per superunit)
+    const float *xb = a.x + (int64_t)b * a.K;
+    float4 v[kXdF];
+#pragma unroll
+    for (int i = 0; i < kXdF; i++) {
+        const int f = tid + kXdThreads * i;
+        v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (live && f < F) v[i] = *reinterpret_cast<const float4 *>(xb + 4 * (int64_t)f);
+    }
+    if (NORM) {
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < kXdF; i++) {
+            ss = fmaf(v[i].x, v[i].x, ss);
+            ss = fmaf(v[i].y, v[i].y, ss);
+            ss = fmaf(v[i].z, v[i].z, ss);
+            ss = fmaf(v[i].w, v[i].w, ss);
+        }
+        ss = block_total<kXdThreads>(ss, red);
+        const float ir = 1.0f / sqrtf(ss / (float)a.K + a.eps);
+#pragma unroll
+        for (int i = 0; i < kXdF; i++) {
+            const int f = tid + kXdThreads * i;
+            if (live && f < F) {
+                const float4 w = *reinterpret_cast<const float4 *>(a.norm_w + 4 * (int64_t)f);
+                v[i].x = v[i].x * ir * w.x;
+                v[i].y = v[i].y * ir * w.y;
+                v[i].z = v[i].z * ir * w.z;
+                v[i].w = v[i].w * ir * w.w;
+            }
+        }
+    }
+    constexpr int RR = SX ? 128 : 32;
+    const int g = b >> 3, bb = b & 7, q = tid & 7;
+#pragma unroll
+    for (int i = 0; i < kXdF; i++) {
+        const int f0 = kXdThreads * i;
+        if (f0 >= Fp) break;  // uniform
+        uint32_t pl[4];
+        double sc, sxs;
+        digitize_run<SX>(v[i], pl, sc, sxs);  // all 8 lanes of every run take part
+        const int run = (f0 + tid) >> 3;
+        if (f0 + tid >= Fp) continue;
+        uint8_t *su = a.dig + ((int64_t)g * a.nb + (run >> 3)) * mq_su_bytes(RR);
+        uint8_t *fr = su + (run & 7) * kFragRun;
+#pragma unroll
+        for (int p = 0; p < 4; p++)
+            *reinterpret_cast<uint32_t *>(fr + 16 * (bb + 8 * p + 32 * (q >> 2)) + 4 * (q & 3)) = pl[p];
+        if (q == 0) {
+            uint8_t *rec = su + 8 * kFragRun + (run & 7) * RR;
+            if constexpr (SX) {
+                double2 r;
+                r.x = sc;
+                r.y = sxs;
+                reinterpret_cast<double2 *>(rec)[bb] = r;
+            } else {
+                reinterpret_cast<float *>(rec)[bb] = (float)sc;
+            }
+        }
+    }
+}
+
+// --------------------------------------------------- per-lane weight bytes ---
+// One lane's bytes of one superunit of its row: lane half h = lane / 32.
+template <int FMT>
+struct MqW;
+// Q4_K: the header, and bytes 16h..16h+15 of each 32-byte quant run c
+// (sub-block 2c in the low nibbles, 2c+1 in the high ones).
+template <>
+struct MqW<kQ4K> {
+    uint4 hd;
+    uint4 q[4];
+};
+// Q6_K: for each half H of the block, ql bytes 64H + 16h .. +15 (A) and
+// 64H + 32 + 16h .. +15 (B), qh bytes 32H + 16h .. +15; the 16 scales and d.
+template <>
+struct MqW<kQ6K> {
+    uint4 ql[2][2];
+    uint4 qh[2];
+    uint4 sc;
+    uint32_t d;
+};
+// Q8_0: quants 16h..16h+15 of each of the 8 blocks, and each block's d.
+template <>
+struct MqW<kQ80> {
+    uint4 q[8];
+    uint32_t d[8];
+};
+
+typedef uint32_t u4_a2 __attribute__((ext_vector_type(4), aligned(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+QD_DEV uint4 ld128u(const uint8_t *p) {  // 16 bytes at a 2-byte-aligned address
+    const u4_a2 v = *reinterpret_cast<const u4_a2 *>(p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+QD_DEV uint32_t ld16(const uint8_t *p) { return *reinterpret_cast<const uint16_t *>(p); }
+
+// ---- a wave's weight tile: 32 rows x one superunit.  Each row's unit is
+// contiguous in memory, so the tile is read as 16-byte pieces with the lanes
+// walking the rows' bytes in order (one instruction covers several whole
+// rows, few cache lines), then written row-major to the wave's own LDS area
+// and read back in the matrix core's B layout.
+//   UB     bytes of one superunit of a row
+//   NPC    16-byte pieces read per row (Q6_K: the last one starts 14 bytes
+//          early, so no piece reads past the unit)
+//   PITCH  LDS bytes per row (Q6_K padded so the 32 rows' reads fall in
+//          distinct banks)
+template <int FMT>
+struct MqGeo;
+template <> struct MqGeo<kQ4K> { static constexpr int UB = 144, NPC = 9, PITCH = 144; };
+template <> struct MqGeo<kQ6K> { static constexpr int UB = 210, NPC = 14, PITCH = 240; };
+template <> struct MqGeo<kQ80> { static constexpr int UB = 272, NPC = 17, PITCH = 272; };
+template <int FMT>
+QD_DEV constexpr int piece_src(int q) { return (FMT == kQ6K && q == 13) ? 194 : 16 * q; }
+template <int FMT>
+QD_DEV constexpr int piece_dst(int q) { return 16 * q; }
+template <int FMT>
+__host__ __device__ constexpr int mq_ni() { return (32 * MqGeo<FMT>::NPC + 63) / 64; }
+template <int FMT>
+__host__ __device__ constexpr int mq_slot() { return 32 * MqGeo<FMT>::PITCH; }
+// Digit buffers in LDS: two (the next superunit's are written while the
+// current one is read) where they fit beside the tiles, else one.
+template <int FMT, int NG>
+__host__ __device__ constexpr int mq_nbuf() {
+    return 2 * NG * mq_su_bytes(FMT == kQ4K ? 128 : 32) + 16 + 4 * mq_slot<FMT>() <= 160 * 1024 ? 2 : 1;
+}
+template <int FMT, int NG>
+__host__ __device__ constexpr int mq_lds() {
+    return mq_nbuf<FMT, NG>() * NG * mq_su_bytes(FMT == kQ4K ? 128 : 32) + 16 + 4 * mq_slot<FMT>();
+}
+template <int FMT>
+struct MqR {
+    u32x4 v[mq_ni<FMT>()];
+};
+
+// Superunits whose loads are in flight while one is multiplied.
+template <int FMT, int NG>
+constexpr int mq_lookahead() {
+    if (NG >= 4) return 1;
+    return FMT == kQ80 ? 1 : 2;
+}
+
+// This lane's bytes of the tile in the B layout (row l % 32, half h = l / 32),
+// read back from the wave's LDS area `scr` (row-major, PITCH per row).
+template <int FMT>
+QD_DEV void mq_read_tile(MqW<FMT> &w, const uint8_t *scr, int j, int h) {
+    const uint8_t *rowp = scr + j * MqGeo<FMT>::PITCH;
+    if constexpr (FMT == kQ4K) {
+        w.hd = ld128(rowp);
+#pragma unroll
+        for (int c = 0; c < 4; c++) w.q[c] = ld128(rowp + 16 + 32 * c + 16 * h);
+    } else if constexpr (FMT == kQ6K) {
+#pragma unroll
+        for (int H = 0; H < 2; H++) {
+            w.ql[H][0] = ld128(rowp + 64 * H + 16 * h);
+            w.ql[H][1] = ld128(rowp + 64 * H + 32 + 16 * h);
+            w.qh[H] = ld128(rowp + 128 + 32 * H + 16 * h);
+        }
+        w.sc = ld128(rowp + 192);
+        w.d = ld16(rowp + 208 + (208 - piece_src<kQ6K>(13)));  // d sits at 208..209 of the unit
+    } else {
+#pragma unroll
+        for (int r = 0; r < 8; r++) {
+            w.q[r] = ld128u(rowp + 34 * r + 2 + 16 * h);
+            w.d[r] = ld16(rowp + 34 * r);
+        }
+    }
+}
+
+QD_DEV uint4 u4and(uint4 v, uint32_t m) { return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m); }
+QD_DEV uint4 u4shr(uint4 v, int s) { return make_uint4(v.x >> s, v.y >> s, v.z >> s, v.w >> s); }
+QD_DEV v4i as_v4i(uint4 v) {
+    v4i r;
+    r[0] = (int)v.x;
+    r[1] = (int)v.y;
+    r[2] = (int)v.z;
+    r[3] = (int)v.w;
+    return r;
+}
+QD_DEV v16i mfma8(v4i a, v4i b) {
+    const v16i z = {};
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, z, 0, 0, 0);
+}
+// Planes p = 0..3 of one batch row sit at output registers base + stride p.
+template <int BASE, int STRIDE>
+QD_DEV double undig64(const v16i &d) {
+    return fma((double)(d[BASE + 3 * STRIDE] * 256 + d[BASE + 2 * STRIDE]), 65536.0,
+               (double)(d[BASE + STRIDE] * 256 + d[BASE]));
+}
+template <int BASE, int STRIDE>
+QD_DEV float undig32(const v16i &d) {
+    return fmaf((float)(d[BASE + 3 * STRIDE] * 256 + d[BASE + 2 * STRIDE]), 65536.f,
+                (float)(d[BASE + STRIDE] * 256 + d[BASE]));
+}
+
+// The accumulators are complete here: an empty asm that reads and writes
+// them, so the compiler cannot sink a sub-block's products past the next
+// one (which would keep every product's registers alive at once).
+template <typename T, int A, int B, int C>
+QD_DEV void pin_acc(T (&acc)[A][B][C]) {
+#pragma unroll
+    for (int i = 0; i < A; i++)
+#pragma unroll
+        for (int j = 0; j < B; j++)
+#pragma unroll
+            for (int k = 0; k < C; k++) asm volatile("" : "+v"(acc[i][j][k]));
+}
+
+// Copy of one superunit's digits (every group, BUF bytes of GB per group)
+// through registers: thread tid moves the 16-byte pieces tid + 256 v.
+// (native vectors, not the uint4 struct, whose copies between address
+// spaces would go through private memory)
+template <int SV, int BUF, int GB>
+QD_DEV void mq_stage_load(u32x4 (&stg)[SV], const uint8_t *dig, int nb, int t, int tid) {
+#pragma unroll
+    for (int v = 0; v < SV; v++) {
+        const int e = min(tid + 256 * v, BUF / 16 - 1);  // repeats past the end are not stored
+        const int g = e / (GB / 16), o = e - g * (GB / 16);
+        stg[v] = reinterpret_cast<const u32x4 *>(dig + ((int64_t)g * nb + t) * GB)[o];
+    }
+}
+template <int SV, int BUF>
+QD_DEV void mq_stage_store(uint8_t *dst, const u32x4 (&stg)[SV], int tid) {
+#pragma unroll
+    for (int v = 0; v < SV; v++)
+        if (v < SV - 1 || tid + 256 * v < BUF / 16) *reinterpret_cast<u32x4 *>(dst + 16 * (tid + 256 * v)) = stg[v];
+}
+
+// ------------------------------------------------------------ the kernel ---
+template <int FMT, int NG, bool FFN>
+__global__ __launch_bounds__(256) void mq_kernel(MqArgs a) {
+    constexpr int NR = 1;                       // one matrix per wave
+    constexpr int TILE = mq_tile_rows(FFN);     // rows per workgroup (of each matrix)
+    constexpr int RR = FMT == kQ4K ? 128 : 32;  // record bytes per run (8 batch rows)
+    constexpr int GB = mq_su_bytes(RR);         // bytes per superunit per group
+    constexpr int BUF = NG * GB;
+    constexpr int SV = (BUF / 16 + 255) / 256;  // staged uint4 per thread
+    using Acc = typename std::conditional<FMT == kQ4K, double, float>::type;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // [NBUF][BUF], 16 zero bytes, 4 tiles
+    __shared__ float red[4];
+    __shared__ int flag;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int h = lane >> 5;
+    const int bx = blockIdx.x, ks = blockIdx.y, p_out = gridDim.y;
+    const int t_beg = ks * a.nk, t_end = min(a.nb, t_beg + a.nk);
+    const int64_t N = a.N;
+    // FFN: waves 0-1 take 64 rows of gate, waves 2-3 the same rows of up
+    const int mi = FFN ? wave >> 1 : 0;
+    const int rloc = (FFN ? (wave & 1) : wave) * 32 + (lane & 31);
+    const int64_t row = (int64_t)bx * TILE + rloc;
+    const bool row_ok = row < N;
+    const int64_t rowc = row_ok ? row : N - 1;
+    (void)rowc;
+
+    // ---- staging: superunit t's fragments and records of every group
+    u32x4 stg[SV];
+    auto stage_load = [&](int t) { mq_stage_load<SV, BUF, GB>(stg, a.dig, a.nb, t, tid); };
+    auto stage_store = [&](int bi) { mq_stage_store<SV, BUF>(lds + bi * BUF, stg, tid); };
+
+    // ---- weight loads, D superunits ahead (ring of D + 1): lane piece p =
+    // 64 i + lane of instruction i is piece p % NPC of the wave's row p / NPC
+    constexpr int D = mq_lookahead<FMT, NG>();
+    constexpr int NI = mq_ni<FMT>(), NPC = MqGeo<FMT>::NPC, UB = MqGeo<FMT>::UB;
+    constexpr int PITCH = MqGeo<FMT>::PITCH;
+    MqR<FMT> wb[D + 1];
+    uint32_t voff[NI];
+    int lpos[NI];
+    bool pv[NI];
+    {
+        const int64_t row0w = (int64_t)bx * TILE + (FFN ? (wave & 1) : wave) * 32;
+#pragma unroll
+        for (int i = 0; i < NI; i++) {
+            const int p = 64 * i + lane;
+            const int r = p / NPC, q = p - (p / NPC) * NPC;
+            pv[i] = p < 32 * NPC;
+            const int64_t rr = min(row0w + r, N - 1);
+            voff[i] = (uint32_t)(rr * a.row_bytes + piece_src<FMT>(q));
+            lpos[i] = r * PITCH + piece_dst<FMT>(q);
+        }
+    }
+    const uint8_t *wbase = mi ? a.W1 : a.W0;
+    auto wload = [&](MqR<FMT> &dst, int t) {
+        t = min(t, t_end - 1);  // past the slice: a repeat of its last superunit, unused
+        const uint8_t *base = wbase + (int64_t)UB * t;
+#pragma unroll
+        for (int i = 0; i < NI; i++) {
+            if (i < NI - 1 || pv[i]) {
+                const u4_a2 v = *reinterpret_cast<const u4_a2 *>(base + voff[i]);
+                dst.v[i] = u32x4{v.x, v.y, v.z, v.w};
+            }
+        }
+    };
+    constexpr int NBUF = mq_nbuf<FMT, NG>();
+    uint8_t *scr = lds + NBUF * BUF + 16 + wave * mq_slot<FMT>();
+    // the tile to the wave's LDS area, then back in the B layout (LDS
+    // accesses of one wave complete in order; the wait orders the lanes'
+    // writes before any lane's read)
+    auto untile = [&](const MqR<FMT> &src, MqW<FMT> &w) {
+#pragma unroll
+        for (int i = 0; i < NI; i++)
+            if (i < NI - 1 || pv[i]) *reinterpret_cast<u32x4 *>(scr + lpos[i]) = src.v[i];
+        lgkm_wait();
+        mq_read_tile<FMT>(w, scr, lane & 31, h);
+    };
+
+    Acc acc[NR][NG][4];
+#pragma unroll
+    for (int i = 0; i < NR; i++)
+#pragma unroll
+        for (int g = 0; g < NG; g++)
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++) acc[i][g][jj] = (Acc)0;
+
+    // Q6_K: A operand offsets of the two half-zero instructions of a run;
+    // lanes whose A row and k half disagree read 16 zero bytes past the
+    // digit buffers instead
+    const int ai = lane & 31;
+    const bool a_live = (ai < 16) == (h == 0);
+    int aoff[2];
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+        const int i16 = ai & 15;
+        const int bb = 4 * ((i16 & 7) >> 2) + 2 * u + (i16 >> 3);
+        aoff[u] = 16 * (bb + 8 * (i16 & 3) + 32 * h);
+    }
+    const uint8_t *zero16 = lds + mq_nbuf<FMT, NG>() * BUF;
+
+    // ---- one superunit, software-pipelined over its steps (sub-block and
+    // group): step n's fragment is read two steps ahead and its product
+    // issued one step ahead, so the matrix core and LDS latencies run under
+    // the previous step's scaling; the accumulators are pinned after each
+    // step so the compiler keeps that order
+    auto compute = [&](const MqR<FMT> &wr, const uint8_t *buf) {
+        MqW<FMT> wv;
+        untile(wr, wv);
+        if constexpr (FMT == kQ4K) {
+            const double dd = (double)f16_lo(wv.hd.x), dm = (double)f16_hi(wv.hd.x);
+            const uint32_t s03 = wv.hd.y, s47 = wv.hd.z, s811 = wv.hd.w;
+            // 6-bit scales / mins of sub-blocks 0..3 and 4..7, a byte each
+            const uint32_t scp[2] = {s03 & 0x3F3F3F3Fu, (s811 & 0x0F0F0F0Fu) | ((s03 >> 2) & 0x30303030u)};
+            const uint32_t mnp[2] = {s47 & 0x3F3F3F3Fu, ((s811 >> 4) & 0x0F0F0F0Fu) | ((s47 >> 2) & 0x30303030u)};
+            constexpr int NS = 8 * NG;  // step n: sub-block n / NG, group n % NG
+            auto bop = [&](int sb) {
+                return as_v4i(u4and((sb & 1) ? u4shr(wv.q[sb >> 1], 4) : wv.q[sb >> 1], 0x0F0F0F0Fu));
+            };
+            auto aload = [&](int n) {
+                return *reinterpret_cast<const v4i *>(buf + (n % NG) * GB + (n / NG) * kFragRun + 16 * lane);
+            };
+            auto rload = [&](int n, double2 (&r)[4]) {
+                const double2 *rc =
+                    reinterpret_cast<const double2 *>(buf + (n % NG) * GB + 8 * kFragRun + (n / NG) * RR + 64 * h);
+#pragma unroll
+                for (int jj = 0; jj < 4; jj++) r[jj] = rc[jj];
+            };
+            v4i Aq[3];
+            v16i Dq[2];
+            double2 Rq[2][4];
+            Aq[0] = aload(0);
+            if (NS > 1) Aq[1] = aload(1);
+            rload(0, Rq[0]);
+            Dq[0] = mfma8(Aq[0], bop(0));
+#pragma unroll
+            for (int n = 0; n < NS; n++) {
+                const int sb = n / NG, g = n % NG;
+                if (n + 2 < NS) Aq[(n + 2) % 3] = aload(n + 2);
+                if (n + 1 < NS) {
+                    rload(n + 1, Rq[(n + 1) & 1]);
+                    Dq[(n + 1) & 1] = mfma8(Aq[(n + 1) % 3], bop((n + 1) / NG));
+                }
+                const double ae = dd * (double)((scp[sb >> 2] >> (8 * (sb & 3))) & 0xFFu);
+                const double be = dm * (double)((mnp[sb >> 2] >> (8 * (sb & 3))) & 0xFFu);
+                const v16i &d = Dq[n & 1];
+                const double2(&r)[4] = Rq[n & 1];
+                acc[0][g][0] = fma(ae * r[0].x, undig64<0, 4>(d), fma(-be, r[0].y, acc[0][g][0]));
+                acc[0][g][1] = fma(ae * r[1].x, undig64<1, 4>(d), fma(-be, r[1].y, acc[0][g][1]));
+                acc[0][g][2] = fma(ae * r[2].x, undig64<2, 4>(d), fma(-be, r[2].y, acc[0][g][2]));
+                acc[0][g][3] = fma(ae * r[3].x, undig64<3, 4>(d), fma(-be, r[3].y, acc[0][g][3]));
+                pin_acc(acc);
+            }
+        } else if constexpr (FMT == kQ6K) {
+            const float d6 = f16_lo(wv.d);
+            const uint32_t sw[4] = {wv.sc.x, wv.sc.y, wv.sc.z, wv.sc.w};
+            // step n: run n / (2 NG), group (n / 2) % NG, half-zero instruction n % 2
+            constexpr int NS = 16 * NG;
+            auto bop = [&](int r) {  // quants q - 32 of sub-blocks 2r (k < 16) and 2r + 1
+                const int H = r >> 2, g4 = r & 3;
+                const uint4 ql = wv.ql[H][g4 & 1];
+                const uint4 nib = u4and(g4 >= 2 ? u4shr(ql, 4) : ql, 0x0F0F0F0Fu);
+                const uint4 hb = u4and(u4shr(wv.qh[H], 2 * g4), 0x03030303u);
+                v4i B;
+                B[0] = (int)(nib.x | byte_lut(kQ6HiTable, hb.x));
+                B[1] = (int)(nib.y | byte_lut(kQ6HiTable, hb.y));
+                B[2] = (int)(nib.z | byte_lut(kQ6HiTable, hb.z));
+                B[3] = (int)(nib.w | byte_lut(kQ6HiTable, hb.w));
+                return B;
+            };
+            auto aload = [&](int n) {
+                const int r = n / (2 * NG), g = (n >> 1) % NG, u = n & 1;
+                const uint8_t *p = a_live ? buf + g * GB + r * kFragRun + aoff[u] : zero16;
+                return *reinterpret_cast<const v4i *>(p);
+            };
+            auto sload = [&](int n) {
+                const int r = n / (2 * NG), g = (n >> 1) % NG;
+                return *reinterpret_cast<const float4 *>(buf + g * GB + 8 * kFragRun + r * RR + 16 * h);
+            };
+            v4i Aq[3];
+            v16i Dq[2];
+            float4 Sq[2];
+            Aq[0] = aload(0);
+            Aq[1] = aload(1);
+            Sq[0] = sload(0);
+            Dq[0] = mfma8(Aq[0], bop(0));
+#pragma unroll
+            for (int n = 0; n < NS; n++) {
+                const int r = n / (2 * NG), g = (n >> 1) % NG, u = n & 1;
+                if (n + 2 < NS) Aq[(n + 2) % 3] = aload(n + 2);
+                if (n + 1 < NS) {
+                    Sq[(n + 1) & 1] = sload(n + 1);
+                    Dq[(n + 1) & 1] = mfma8(Aq[(n + 1) % 3], bop((n + 1) / (2 * NG)));
+                }
+                const v16i &d = Dq[n & 1];
+                const float4 S = Sq[n & 1];
+                const float ds0 = d6 * sbyte(sw[r >> 1], 2 * (r & 1));      // sub-block 2r
+                const float ds1 = d6 * sbyte(sw[r >> 1], 2 * (r & 1) + 1);  // sub-block 2r + 1
+                // registers 4a + p (sub-block 2r) and 8 + 4a + p (2r + 1) hold
+                // batch row 4h + 2u + a
+                const float s0 = u ? S.z : S.x, s1 = u ? S.w : S.y;
+                Acc &a0 = acc[0][g][2 * u], &a1 = acc[0][g][2 * u + 1];
+                a0 = fmaf(ds0 * s0, undig32<0, 1>(d), a0);
+                a0 = fmaf(ds1 * s0, undig32<8, 1>(d), a0);
+                a1 = fmaf(ds0 * s1, undig32<4, 1>(d), a1);
+                a1 = fmaf(ds1 * s1, undig32<12, 1>(d), a1);
+                pin_acc(acc);
+            }
+        } else {
+            constexpr int NS = 8 * NG;  // step n: block n / NG, group n % NG
+            auto aload = [&](int n) {
+                return *reinterpret_cast<const v4i *>(buf + (n % NG) * GB + (n / NG) * kFragRun + 16 * lane);
+            };
+            auto sload = [&](int n) {
+                return *reinterpret_cast<const float4 *>(buf + (n % NG) * GB + 8 * kFragRun + (n / NG) * RR + 16 * h);
+            };
+            v4i Aq[3];
+            v16i Dq[2];
+            float4 Sq[2];
+            Aq[0] = aload(0);
+            if (NS > 1) Aq[1] = aload(1);
+            Sq[0] = sload(0);
+            Dq[0] = mfma8(Aq[0], as_v4i(wv.q[0]));
+#pragma unroll
+            for (int n = 0; n < NS; n++) {
+                const int r = n / NG, g = n % NG;
+                if (n + 2 < NS) Aq[(n + 2) % 3] = aload(n + 2);
+                if (n + 1 < NS) {
+                    Sq[(n + 1) & 1] = sload(n + 1);
+                    Dq[(n + 1) & 1] = mfma8(Aq[(n + 1) % 3], as_v4i(wv.q[(n + 1) / NG]));
+                }
+                const v16i &d = Dq[n & 1];
+                const float4 S = Sq[n & 1];
+                const float dq = f16_lo(wv.d[r]);
+                acc[0][g][0] = fmaf(dq * S.x, undig32<0, 4>(d), acc[0][g][0]);
+                acc[0][g][1] = fmaf(dq * S.y, undig32<1, 4>(d), acc[0][g][1]);
+                acc[0][g][2] = fmaf(dq * S.z, undig32<2, 4>(d), acc[0][g][2]);
+                acc[0][g][3] = fmaf(dq * S.w, undig32<3, 4>(d), acc[0][g][3]);
+                pin_acc(acc);
+            }
+        }
+    };
+
+    // ---- main loop: superunit t multiplied from LDS half (t - t_beg) & 1
+    // while superunit t + 1's fragments are loaded for the other half
+    if (FMT == kQ6K && tid == 0) *reinterpret_cast<uint4 *>(const_cast<uint8_t *>(zero16)) = make_uint4(0u, 0u, 0u, 0u);
+    if (t_beg < t_end) {
+        stage_load(t_beg);
+#pragma unroll
+        for (int d = 0; d < D; d++) wload(wb[d], t_beg + d);
+        stage_store(0);
+        block_sync();
+        for (int t0 = t_beg; t0 < t_end; t0 += D + 1) {
+#pragma unroll
+            for (int s = 0; s <= D; s++) {
+                const int t = t0 + s;
+                if (t >= t_end) break;
+                const int bi = NBUF == 2 ? (t - t_beg) & 1 : 0;
+                const bool more = t + 1 < t_end;
+                if (more) stage_load(t + 1);
+                wload(wb[(s + D) % (D + 1)], t + D);
+                compute(wb[s], lds + bi * BUF);
+                if (more) {
+                    if (NBUF == 1) block_sync();  // every wave is done with the buffer
+                    stage_store(NBUF == 2 ? bi ^ 1 : 0);
+                }
+                block_sync();
+            }
+        }
+    }
+
+    // ---- outputs: lane (row, batch rows 8g + 4h + jj)
+    constexpr int NP = FFN ? 2 : 1;
+    const int B = a.batch;
+    if (p_out == 1) {
+        if constexpr (FFN) {
+            // up (waves 2-3) hands its rows to gate (waves 0-1) through LDS
+            float *ub = reinterpret_cast<float *>(lds);  // [64 rows][8 NG]; the digit buffers are done
+            if (mi == 1) {
+#pragma unroll
+                for (int g = 0; g < NG; g++)
+#pragma unroll
+                    for (int jj = 0; jj < 4; jj++) ub[rloc * 8 * NG + 8 * g + 4 * h + jj] = (float)acc[0][g][jj];
+            }
+            block_sync();
+            if (mi == 0 && row_ok) {
+#pragma unroll
+                for (int g = 0; g < NG; g++)
+#pragma unroll
+                    for (int jj = 0; jj < 4; jj++) {
+                        const int b = 8 * g + 4 * h + jj;
+                        if (b >= B) continue;
+                        const int64_t o = (int64_t)b * N + row;
+                        const float gv = (float)acc[0][g][jj], uv = ub[rloc * 8 * NG + 8 * g + 4 * h + jj];
+                        a.y[o] = act_apply(a.act, gv) * uv;
+                        if (a.g_out) a.g_out[o] = gv;
+                        if (a.u_out) a.u_out[o] = uv;
+                    }
+            }
+        } else {
+            if (row_ok) {
+#pragma unroll
+                for (int g = 0; g < NG; g++)
+#pragma unroll
+                    for (int jj = 0; jj < 4; jj++) {
+                        const int b = 8 * g + 4 * h + jj;
+                        if (b >= B) continue;
+                        const int64_t o = (int64_t)b * N + row;
+                        const float vv = (float)acc[0][g][jj];
+                        if (a.pn.w1) xstore(a.pn.p + o, vv);  // the row epilogue forms y
+                        else a.y[o] = a.res ? vv + a.res[o] : vv;
+                    }
+            }
+            if (a.pn.w1) post_norm_tail<256>(a.pn, a.y, B, N, red, &flag);
+        }
+        return;
+    }
+    if (row_ok) {
+#pragma unroll
+        for (int g = 0; g < NG; g++)
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++) {
+                const int b = 8 * g + 4 * h + jj;
+                if (b >= B) continue;
+                xstore(a.partials + (((int64_t)ks * B + b) * NP + mi) * N + row, (float)acc[0][g][jj]);
+            }
+    }
+    // ---- split-K: the last workgroup of this row tile sums the partials in
+    // slice order (the hand-off of qd_epilogue.h on the tile's counter)
+    if (!arrive_last<256>(a.counters + bx, (unsigned)p_out, &flag)) return;
+    // each thread sums the slices of up to EPT outputs of the tile, with
+    // KC slices per output loaded at once (independent loads in flight,
+    // added in slice order afterwards)
+    constexpr int EPT = TILE * 8 * NG / 256;
+    constexpr int KC = EPT * NP >= 32 ? 1 : 32 / (EPT * NP);
+    const int64_t tile0 = (int64_t)bx * TILE;
+    float s[EPT][NP];
+#pragma unroll
+    for (int m = 0; m < EPT; m++)
+#pragma unroll
+        for (int i = 0; i < NP; i++) s[m][i] = 0.f;
+    for (int k0 = 0; k0 < p_out; k0 += KC) {
+        float v[EPT][NP][KC];
+#pragma unroll
+        for (int m = 0; m < EPT; m++) {
+            const int e = tid + 256 * m;
+            const int b = e / TILE;
+            const int64_t r = tile0 + (e - b * TILE);
+            const bool ok = b < B && r < N;
+#pragma unroll
+            for (int u = 0; u < KC; u++) {
+                const int k = min(k0 + u, p_out - 1);
+                const float *p = a.partials + (((int64_t)k * B + b) * NP) * N + r;
+#pragma unroll
+                for (int i = 0; i < NP; i++) v[m][i][u] = ok ? xload(p + i * N) : 0.f;
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < EPT; m++)
+#pragma unroll
+            for (int u = 0; u < KC; u++)
+                if (k0 + u < p_out)
+#pragma unroll
+                    for (int i = 0; i < NP; i++) s[m][i] += v[m][i][u];
+    }
+#pragma unroll
+    for (int m = 0; m < EPT; m++) {
+        const int e = tid + 256 * m;
+        const int b = e / TILE;
+        const int64_t r = tile0 + (e - b * TILE);
+        if (b >= B || r >= N) continue;
+        const int64_t o = (int64_t)b * N + r;
+        const float s0 = s[m][0];
+        if constexpr (FFN) {
+            const float s1 = s[m][NP - 1];
+            a.y[o] = act_apply(a.act, s0) * s1;
+            if (a.g_out) a.g_out[o] = s0;
+            if (a.u_out) a.u_out[o] = s1;
+        } else {
+            if (a.pn.w1) xstore(a.pn.p + o, s0);
+            else a.y[o] = a.res ? s0 + a.res[o] : s0;
+        }
+    }
+    if (tid == 0)  // ready for the next call
+        __hip_atomic_store(a.counters + bx, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!FFN && a.pn.w1) post_norm_tail<256>(a.pn, a.y, B, N, red, &flag);
+}
+
+// ------------------------------------------------------------- launchers ---
+size_t mq_su_bytes_host(int fmt) { return (size_t)mq_su_bytes(fmt == kQ4K ? 128 : 32); }
+template <int FMT>
+static size_t mq_lds_f(int ng) {
+    switch (ng) {
+    case 1: return mq_lds<FMT, 1>();
+    case 2: return mq_lds<FMT, 2>();
+    case 4: return mq_lds<FMT, 4>();
+    default: return mq_lds<FMT, 8>();
+    }
+}
+size_t mq_lds_bytes(int fmt, int ng) {
+    return fmt == kQ4K ? mq_lds_f<kQ4K>(ng) : fmt == kQ6K ? mq_lds_f<kQ6K>(ng) : mq_lds_f<kQ80>(ng);
+}
+
+// Allow each kernel the dynamic LDS it uses (once per kernel; the static
+// words of the kernel come on top).
+template <auto Kern>
+static hipError_t allow_lds_mq(size_t bytes) {
+    static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(Kern),
+                                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    return e;
+}
+
+int xdig_max_k() { return kXdF * kXdThreads * 4; }
+
+hipError_t launch_xdig(const XdArgs &a, int ng, bool sx, hipStream_t st) {
+    if (a.K > xdig_max_k() || 64 * a.nb > kXdF * kXdThreads) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(ng * 8));
+    const bool norm = a.norm_w != nullptr;
+    const dim3 blk(kXdThreads);
+    if (norm && sx) hipLaunchKernelGGL((xdig_kernel<true, true>), grid, blk, 0, st, a);
+    else if (norm) hipLaunchKernelGGL((xdig_kernel<true, false>), grid, blk, 0, st, a);
+    else if (sx) hipLaunchKernelGGL((xdig_kernel<false, true>), grid, blk, 0, st, a);
+    else hipLaunchKernelGGL((xdig_kernel<false, false>), grid, blk, 0, st, a);
+    return hipGetLastError();
+}
+
+template <int FMT, int NG, bool FFN>
+static hipError_t launch_mq_one(const MqArgs &a, dim3 grid, hipStream_t st) {
+    const size_t lds = mq_lds_bytes(FMT, NG);
+    if (allow_lds_mq<mq_kernel<FMT, NG, FFN>>(lds) != hipSuccess) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((mq_kernel<FMT, NG, FFN>), grid, dim3(256), lds, st, a);
+    return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t launch_mq_f(const MqArgs &a, int ng, bool ffn, dim3 grid, hipStream_t st) {
+    switch (ng) {
+    case 1: return ffn ? launch_mq_one<FMT, 1, true>(a, grid, st) : launch_mq_one<FMT, 1, false>(a, grid, st);
+    case 2: return ffn ? launch_mq_one<FMT, 2, true>(a, grid, st) : launch_mq_one<FMT, 2, false>(a, grid, st);
+    case 4: return ffn ? launch_mq_one<FMT, 4, true>(a, grid, st) : launch_mq_one<FMT, 4, false>(a, grid, st);
+    case 8: return ffn ? launch_mq_one<FMT, 8, true>(a, grid, st) : launch_mq_one<FMT, 8, false>(a, grid, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// Workgroups of a matrix kernel resident per CU (registers and LDS).
+template <int FMT, int NG, bool FFN>
+static int mq_occ() {
+    static const int n = [] {
+        const size_t lds = mq_lds_bytes(FMT, NG);
+        if (allow_lds_mq<mq_kernel<FMT, NG, FFN>>(lds) != hipSuccess) return 1;
+        int wg = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&wg, reinterpret_cast<const void *>(mq_kernel<FMT, NG, FFN>),
+                                                         256, lds) != hipSuccess)
+            return 1;
+        return wg > 0 ? wg : 1;
+    }();
+    return n;
+}
+template <int FMT>
+static int mq_occ_f(int ng, bool ffn) {
+    switch (ng) {
+    case 1: return ffn ? mq_occ<FMT, 1, true>() : mq_occ<FMT, 1, false>();
+    case 2: return ffn ? mq_occ<FMT, 2, true>() : mq_occ<FMT, 2, false>();
+    case 4: return ffn ? mq_occ<FMT, 4, true>() : mq_occ<FMT, 4, false>();
+    default: return ffn ? mq_occ<FMT, 8, true>() : mq_occ<FMT, 8, false>();
+    }
+}
+int mq_wg_per_cu(int fmt, int ng, bool ffn) {
+    switch (fmt) {
+    case kQ4K: return mq_occ_f<kQ4K>(ng, ffn);
+    case kQ6K: return mq_occ_f<kQ6K>(ng, ffn);
+    default: return mq_occ_f<kQ80>(ng, ffn);
+    }
+}
+
+hipError_t launch_mq(int fmt, int ng, bool ffn, const MqArgs &a, unsigned tiles, unsigned p_out,
+                     hipStream_t st) {
+    const dim3 grid(tiles, p_out);
+    switch (fmt) {
+    case kQ4K: return launch_mq_f<kQ4K>(a, ng, ffn, grid, st);
+    case kQ6K: return launch_mq_f<kQ6K>(a, ng, ffn, grid, st);
+    case kQ80: return launch_mq_f<kQ80>(a, ng, ffn, grid, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace qd

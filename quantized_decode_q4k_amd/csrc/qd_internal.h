@@ -143,6 +143,51 @@ int stream_copies_per_step(int fmt, bool ffn);
 hipError_t launch_stream(int fmt, int batch, bool ffn, const StreamArgs &a, unsigned grid,
                          size_t lds, hipStream_t st);
 
+// Batch 3..64 GEMVs on the matrix cores (qd_gemv_mfma.hip).  xdig_kernel
+// writes the activation digits of up to 64 batch rows in groups of 8: per
+// (group, superunit) the A-operand fragments of its 8 runs (1 KB each) and
+// a record per run and batch row ({scale, scale * sum X} as two doubles for
+// Q4_K, the scale as a float otherwise).  mq_kernel streams 128 weight rows
+// per workgroup over a K-slice of nk superunits (gridDim.y slices, split-K
+// partials summed by the last workgroup of a row tile).
+constexpr int kFragRun = 1024;        // bytes of one run's A operand (8 batch rows)
+// Weight rows per workgroup (4 waves of 32 rows): 128 of one matrix, or 64
+// rows of both gate and up for the fused FFN.
+__host__ __device__ constexpr int mq_tile_rows(bool ffn) { return ffn ? 64 : 128; }
+struct XdArgs {
+    const float *x;         // [batch][K], 16-byte aligned
+    const float *norm_w;    // [K] or nullptr
+    float eps;
+    uint8_t *dig;           // [ng][nb] superunits of digits (mq_su_bytes_host each)
+    int64_t K;
+    int R;                  // runs of activations (K / 32)
+    int nb;                 // superunits (ceil(K / 256))
+    int batch;
+};
+struct MqArgs {
+    const uint8_t *W0;      // the matrix (GEMV) or gate (FFN)
+    const uint8_t *W1;      // up (FFN)
+    const uint8_t *dig;     // xdig_kernel's output
+    float *y, *g_out, *u_out;
+    const float *res;       // GEMV: optional [batch][N] added to y (may equal y)
+    float *partials;        // split-K: [p_out][batch][1 or 2][N]
+    unsigned *counters;     // split-K: one per row tile, zero between calls
+    int64_t N, K, row_bytes;
+    int nb;                 // superunits per row
+    int nblk;               // format blocks per row
+    int nk;                 // superunits per K-slice
+    int batch;
+    int act;
+    PostNorm pn;            // GEMV row epilogue (pn.w1 = nullptr: none)
+};
+size_t mq_su_bytes_host(int fmt);      // digits bytes per (group, superunit)
+size_t mq_lds_bytes(int fmt, int ng);
+int xdig_max_k();                      // longest row xdig_kernel takes
+int mq_wg_per_cu(int fmt, int ng, bool ffn);  // resident workgroups per CU
+hipError_t launch_xdig(const XdArgs &a, int ng, bool sx, hipStream_t st);
+hipError_t launch_mq(int fmt, int ng, bool ffn, const MqArgs &a, unsigned tiles, unsigned p_out,
+                     hipStream_t st);
+
 // Prefill GEMM (qd_prefill.hip).  A workgroup owns 32*tm tokens by 256
 // output columns (plain: 256 weight rows; FFN: 128 rows of gate and of up)
 // over K-tiles [kt_per_split*ks, ...) of 128 weights.
