@@ -475,6 +475,71 @@ struct PostArgs {
     float eps = 0.f;
 };
 
+// The activation digits of x (unless `dig` already holds them), then one
+// matrix-core launch.  region: this call's floats of the workspace, holding
+// (in order) its own digits when it forms them, the split-K partials and
+// the post-norm projection.  hd: FFN only, h written as the down
+// projection's digits instead of (or besides, y != nullptr) fp32.
+struct HDigits {
+    uint8_t *dig = nullptr;
+    int nb = 0;
+    int sx = 0;
+};
+qd_status mq_run(const MqPlan &p, int fmt, bool ffn, const void *W0, const void *W1, const float *x,
+                 const uint8_t *dig, const float *norm_w, float eps, int act, float *y, float *g_out,
+                 float *u_out, int64_t N, int64_t K, int batch, hipStream_t hs, const Workspace &w, float *region,
+                 const float *res, const PostArgs &post, const HDigits &hd = HDigits()) {
+    const bool pnorm = post.w1 != nullptr;
+    float *next = region;
+    if (!dig) {
+        qd::XdArgs xa{};
+        xa.x = x;
+        xa.norm_w = norm_w;
+        xa.eps = eps;
+        xa.dig = reinterpret_cast<uint8_t *>(region);
+        xa.K = K;
+        xa.R = (int)(K / 32);
+        xa.nb = p.nb;
+        xa.batch = batch;
+        if (qd::launch_xdig(xa, p.ng, fmt == QD_Q4_K, hs) != hipSuccess) return QD_ELAUNCH;
+        dig = xa.dig;
+        next += p.dig_floats;
+    }
+    qd::MqArgs a{};
+    a.W0 = static_cast<const uint8_t *>(W0);
+    a.W1 = static_cast<const uint8_t *>(W1);
+    a.dig = dig;
+    a.y = y;
+    a.g_out = g_out;
+    a.u_out = u_out;
+    a.res = pnorm ? nullptr : res;
+    a.partials = next;
+    a.counters = w.counters;
+    a.N = N;
+    a.K = K;
+    a.row_bytes = row_bytes(fmt, K);
+    a.nb = (int)((K + qd::kSuper - 1) / qd::kSuper);
+    a.nblk = (int)(K / block_elems(fmt));
+    a.nk = p.nk;
+    a.batch = batch;
+    a.act = act;
+    if (pnorm) {
+        a.pn.w1 = post.w1;
+        a.pn.w2 = post.w2;
+        a.pn.r = res;
+        a.pn.y2 = post.y2;
+        a.pn.p = next + p.part_floats;
+        a.pn.ctr = w.counters + kMaxTiles;  // auxiliary counter 0
+        a.pn.tiles = (unsigned)p.tiles;
+        a.pn.eps = post.eps;
+    }
+    a.hdig = hd.dig;
+    a.hd_nb = hd.nb;
+    a.hd_sx = hd.sx;
+    const hipError_t e = qd::launch_mq(fmt, p.ng, ffn, a, (unsigned)p.tiles, (unsigned)p.p_out, hs);
+    return e == hipSuccess ? QD_OK : QD_ELAUNCH;
+}
+
 qd_status run_mv(int fmt, bool ffn, const void *W0, const void *W1, const float *x,
                  const float *norm_w, float eps, int act, float *y, float *g_out, float *u_out,
                  int64_t N, int64_t K, int batch, void *stream, size_t ws_offset = 0,
@@ -517,47 +582,8 @@ qd_status run_mv(int fmt, bool ffn, const void *W0, const void *W1, const float 
         Workspace w;
         st = acquire_ws(hs, ws_offset + p.floats() + p_floats, fixed, &w);
         if (st != QD_OK) return st;
-        float *base = w.partials + ws_offset;
-        qd::XdArgs xa{};
-        xa.x = x;
-        xa.norm_w = norm_w;
-        xa.eps = eps;
-        xa.dig = reinterpret_cast<uint8_t *>(base);
-        xa.K = K;
-        xa.R = (int)(K / 32);
-        xa.nb = p.nb;
-        xa.batch = batch;
-        if (qd::launch_xdig(xa, p.ng, fmt == QD_Q4_K, hs) != hipSuccess) return QD_ELAUNCH;
-        qd::MqArgs a{};
-        a.W0 = static_cast<const uint8_t *>(W0);
-        a.W1 = static_cast<const uint8_t *>(W1);
-        a.dig = xa.dig;
-        a.y = y;
-        a.g_out = g_out;
-        a.u_out = u_out;
-        a.res = pnorm ? nullptr : res;
-        a.partials = base + p.dig_floats;
-        a.counters = w.counters;
-        a.N = N;
-        a.K = K;
-        a.row_bytes = row_bytes(fmt, K);
-        a.nb = (int)((K + qd::kSuper - 1) / qd::kSuper);
-        a.nblk = (int)(K / block_elems(fmt));
-        a.nk = p.nk;
-        a.batch = batch;
-        a.act = act;
-        if (pnorm) {
-            a.pn.w1 = post.w1;
-            a.pn.w2 = post.w2;
-            a.pn.r = res;
-            a.pn.y2 = post.y2;
-            a.pn.p = base + p.floats();
-            a.pn.ctr = w.counters + kMaxTiles;  // auxiliary counter 0
-            a.pn.tiles = (unsigned)p.tiles;
-            a.pn.eps = post.eps;
-        }
-        const hipError_t e = qd::launch_mq(fmt, p.ng, ffn, a, (unsigned)p.tiles, (unsigned)p.p_out, hs);
-        return e == hipSuccess ? QD_OK : QD_ELAUNCH;
+        return mq_run(p, fmt, ffn, W0, W1, x, nullptr, norm_w, eps, act, y, g_out, u_out, N, K, batch, hs, w,
+                      w.partials + ws_offset, res, post);
     }
     if (batch > QD_BATCH_CHUNK) {
         // successive launches of up to QD_BATCH_CHUNK columns
@@ -697,14 +723,36 @@ qd_status run_ffn_decode(int fmt_gu, const void *Wg, const void *Wu, int fmt_d, 
     }
 
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    if (mq) {
+        // gate/up writes h as the down projection's digits (and as fp32 only
+        // when the caller keeps h): [down digits][gate/up digits + partials,
+        // then down partials + post-norm projection]
+        const MqPlan qa = mq_plan(fmt_gu, N_ff, K, batch, true);
+        const MqPlan qb = mq_plan(fmt_d, K, N_ff, batch, false);
+        const size_t need = qb.dig_floats + std::max(qa.floats(), qb.part_floats + (post.w1 ? (size_t)batch * K : 0));
+        Workspace w;
+        st = acquire_ws(hs, need, fixed, &w);
+        if (st != QD_OK) return st;
+        if (fixed) {
+            hipLaunchKernelGGL(zero_words_kernel, dim3(64), dim3(256), 0, hs, w.counters, kCounterWords);
+            if (hipGetLastError() != hipSuccess) return QD_ELAUNCH;
+        }
+        HDigits hd;
+        hd.dig = reinterpret_cast<uint8_t *>(w.partials);
+        hd.nb = qb.nb;
+        hd.sx = fmt_d == QD_Q4_K;
+        float *region = w.partials + qb.dig_floats;
+        st = mq_run(qa, fmt_gu, true, Wg, Wu, x, nullptr, norm_w, eps, act, h_out, nullptr, nullptr, N_ff, K, batch,
+                    hs, w, region, nullptr, PostArgs(), hd);
+        if (st != QD_OK) return st;
+        return mq_run(qb, fmt_d, false, Wd, nullptr, nullptr, hd.dig, nullptr, 0.f, 0, y, nullptr, nullptr, K, N_ff,
+                      batch, hs, w, region, res, post);
+    }
     const size_t h_floats = h_out ? 0 : (((size_t)batch * N_ff + 63) / 64) * 64;
     // size the workspace once for h and both calls' split-K partials, so
     // that neither call reallocates it under h
     size_t need_a = 0, need_b = post.w1 ? (size_t)batch * K : 0;
-    if (mq) {
-        need_a = mq_plan(fmt_gu, N_ff, K, batch, true).floats();
-        need_b += mq_plan(fmt_d, K, N_ff, batch, false).floats();
-    } else {
+    {
         const Plan qa = choose_plan(fmt_gu, N_ff, K, batch, true);
         const Plan qb = choose_plan(fmt_d, K, N_ff, batch, false);
         need_a = qa.s.p_out > 1 ? (size_t)qa.s.p_out * batch * 2 * N_ff : 0;

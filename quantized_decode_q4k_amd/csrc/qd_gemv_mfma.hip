@@ -132,6 +132,67 @@ __global__ __launch_bounds__(kXdThreads) void xdig_kernel(XdArgs a) {
     }
 }
 
+// The same digits from a run held by the 32 lanes of a half-wave (lane & 31
+// = the activation's index in the run, one value each; all 64 lanes of the
+// wave take part): the run's largest magnitude and plane sums by cross-lane
+// reductions, then each lane writes its four digit bytes, and lane 0 of the
+// half the run's record.  su: the run's superunit of its group; bb: the
+// batch row within the group; r8: the run within the superunit.
+template <typename T>
+QD_DEV T half_max(T m) {
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) m = max(m, (T)__shfl_xor((int)m, o));
+    return m;
+}
+QD_DEV int half_sum(int v) {
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) v += __shfl_xor(v, o);
+    return v;
+}
+template <bool SX>
+QD_DEV void digitize_half(float v, uint8_t *su, int bb, int r8) {
+    const int k = threadIdx.x & 31;
+    const uint32_t m = half_max<uint32_t>(fbits(v) & 0x7FFFFFFFu);
+    const bool bad = m >= 0x7F800000u;
+    const int E = (int)(m >> 23) - 126;
+    const int s = 30 - E;
+    const int X = (int)rintf(ldexpf(v, s));
+    const uint32_t y = (uint32_t)X + 0x80808080u;
+    uint8_t *fr = su + r8 * kFragRun + 16 * (bb + 32 * (k >> 4)) + (k & 15);
+    int ds[4];
+#pragma unroll
+    for (int p = 0; p < 4; p++) {
+        const int dp = (int)((y >> (8 * p)) & 0xFFu) - 128;  // digit p, balanced
+        fr[16 * 8 * p] = (uint8_t)dp;
+        ds[p] = dp;
+    }
+    double sxs = 0.0;
+    const double sc = bad ? __builtin_nan("") : ldexp(1.0, -s);
+    if constexpr (SX) {
+        const int s0 = half_sum(ds[0]), s1 = half_sum(ds[1]), s2 = half_sum(ds[2]), s3 = half_sum(ds[3]);
+        sxs = fma((double)(s3 * 256 + s2), 65536.0, (double)(s1 * 256 + s0)) * sc;
+    }
+    if (k == 0) {
+        uint8_t *rec = su + 8 * kFragRun + r8 * (SX ? 128 : 32);
+        if constexpr (SX) {
+            double2 r;
+            r.x = sc;
+            r.y = sxs;
+            reinterpret_cast<double2 *>(rec)[bb] = r;
+        } else {
+            reinterpret_cast<float *>(rec)[bb] = (float)sc;
+        }
+    }
+}
+// h of gate/up row `row` (the down's activation index) for batch slot b.
+QD_DEV void emit_h_digit(const MqArgs &a, float hv, int b, int64_t row) {
+    const int run = (int)(row >> 5);
+    const int g = b >> 3, bb = b & 7;
+    uint8_t *su = a.hdig + ((int64_t)g * a.hd_nb + (run >> 3)) * mq_su_bytes(a.hd_sx ? 128 : 32);
+    if (a.hd_sx) digitize_half<true>(hv, su, bb, run & 7);
+    else digitize_half<false>(hv, su, bb, run & 7);
+}
+
 // --------------------------------------------------- per-lane weight bytes ---
 // One lane's bytes of one superunit of its row: lane half h = lane / 32.
 template <int FMT>
@@ -403,10 +464,94 @@ __global__ __launch_bounds__(256) void mq_kernel(MqArgs a) {
     // issued one step ahead, so the matrix core and LDS latencies run under
     // the previous step's scaling; the accumulators are pinned after each
     // step so the compiler keeps that order
+    // Four or more groups: one step at a time (the pipelined form's
+    // registers and code do not fit at that size)
+    auto compute_wide = [&](const MqW<FMT> &wv, const uint8_t *buf) {
+        if constexpr (FMT == kQ4K) {
+            const double dd = (double)f16_lo(wv.hd.x), dm = (double)f16_hi(wv.hd.x);
+            const uint32_t s03 = wv.hd.y, s47 = wv.hd.z, s811 = wv.hd.w;
+            const uint32_t scp[2] = {s03 & 0x3F3F3F3Fu, (s811 & 0x0F0F0F0Fu) | ((s03 >> 2) & 0x30303030u)};
+            const uint32_t mnp[2] = {s47 & 0x3F3F3F3Fu, ((s811 >> 4) & 0x0F0F0F0Fu) | ((s47 >> 2) & 0x30303030u)};
+#pragma unroll
+            for (int sb = 0; sb < 8; sb++) {
+                const v4i B = as_v4i(u4and((sb & 1) ? u4shr(wv.q[sb >> 1], 4) : wv.q[sb >> 1], 0x0F0F0F0Fu));
+                const double ae = dd * (double)((scp[sb >> 2] >> (8 * (sb & 3))) & 0xFFu);
+                const double be = dm * (double)((mnp[sb >> 2] >> (8 * (sb & 3))) & 0xFFu);
+#pragma unroll
+                for (int g = 0; g < NG; g++) {
+                    const uint8_t *gb = buf + g * GB;
+                    const v4i A = *reinterpret_cast<const v4i *>(gb + sb * kFragRun + 16 * lane);
+                    const double2 *rc = reinterpret_cast<const double2 *>(gb + 8 * kFragRun + sb * RR + 64 * h);
+                    const v16i d = mfma8(A, B);
+#pragma unroll
+                    for (int jj = 0; jj < 4; jj++) {
+                        const double2 r = rc[jj];
+                        const double I = jj == 0 ? undig64<0, 4>(d) : jj == 1 ? undig64<1, 4>(d)
+                                         : jj == 2 ? undig64<2, 4>(d) : undig64<3, 4>(d);
+                        acc[0][g][jj] = fma(ae * r.x, I, fma(-be, r.y, acc[0][g][jj]));
+                    }
+                    pin_acc(acc);
+                }
+            }
+        } else if constexpr (FMT == kQ6K) {
+            const float d6 = f16_lo(wv.d);
+            const uint32_t sw[4] = {wv.sc.x, wv.sc.y, wv.sc.z, wv.sc.w};
+#pragma unroll
+            for (int r = 0; r < 8; r++) {
+                const int H = r >> 2, g4 = r & 3;
+                const uint4 ql = wv.ql[H][g4 & 1];
+                const uint4 nib = u4and(g4 >= 2 ? u4shr(ql, 4) : ql, 0x0F0F0F0Fu);
+                const uint4 hb = u4and(u4shr(wv.qh[H], 2 * g4), 0x03030303u);
+                v4i B;
+                B[0] = (int)(nib.x | byte_lut(kQ6HiTable, hb.x));
+                B[1] = (int)(nib.y | byte_lut(kQ6HiTable, hb.y));
+                B[2] = (int)(nib.z | byte_lut(kQ6HiTable, hb.z));
+                B[3] = (int)(nib.w | byte_lut(kQ6HiTable, hb.w));
+                const float ds0 = d6 * sbyte(sw[r >> 1], 2 * (r & 1)), ds1 = d6 * sbyte(sw[r >> 1], 2 * (r & 1) + 1);
+#pragma unroll
+                for (int g = 0; g < NG; g++) {
+                    const uint8_t *gb = buf + g * GB;
+                    const float4 S = *reinterpret_cast<const float4 *>(gb + 8 * kFragRun + r * RR + 16 * h);
+#pragma unroll
+                    for (int u = 0; u < 2; u++) {
+                        const v4i A = *reinterpret_cast<const v4i *>(a_live ? gb + r * kFragRun + aoff[u] : zero16);
+                        const v16i d = mfma8(A, B);
+                        const float s0 = u ? S.z : S.x, s1 = u ? S.w : S.y;
+                        Acc &a0 = acc[0][g][2 * u], &a1 = acc[0][g][2 * u + 1];
+                        a0 = fmaf(ds0 * s0, undig32<0, 1>(d), a0);
+                        a0 = fmaf(ds1 * s0, undig32<8, 1>(d), a0);
+                        a1 = fmaf(ds0 * s1, undig32<4, 1>(d), a1);
+                        a1 = fmaf(ds1 * s1, undig32<12, 1>(d), a1);
+                        pin_acc(acc);
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 8; r++) {
+                const v4i B = as_v4i(wv.q[r]);
+                const float dq = f16_lo(wv.d[r]);
+#pragma unroll
+                for (int g = 0; g < NG; g++) {
+                    const uint8_t *gb = buf + g * GB;
+                    const v4i A = *reinterpret_cast<const v4i *>(gb + r * kFragRun + 16 * lane);
+                    const float4 S = *reinterpret_cast<const float4 *>(gb + 8 * kFragRun + r * RR + 16 * h);
+                    const v16i d = mfma8(A, B);
+                    acc[0][g][0] = fmaf(dq * S.x, undig32<0, 4>(d), acc[0][g][0]);
+                    acc[0][g][1] = fmaf(dq * S.y, undig32<1, 4>(d), acc[0][g][1]);
+                    acc[0][g][2] = fmaf(dq * S.z, undig32<2, 4>(d), acc[0][g][2]);
+                    acc[0][g][3] = fmaf(dq * S.w, undig32<3, 4>(d), acc[0][g][3]);
+                    pin_acc(acc);
+                }
+            }
+        }
+    };
     auto compute = [&](const MqR<FMT> &wr, const uint8_t *buf) {
         MqW<FMT> wv;
         untile(wr, wv);
-        if constexpr (FMT == kQ4K) {
+        if constexpr (NG >= 4) {
+            compute_wide(wv, buf);
+        } else if constexpr (FMT == kQ4K) {
             const double dd = (double)f16_lo(wv.hd.x), dm = (double)f16_hi(wv.hd.x);
             const uint32_t s03 = wv.hd.y, s47 = wv.hd.z, s811 = wv.hd.w;
             // 6-bit scales / mins of sub-blocks 0..3 and 4..7, a byte each
@@ -582,16 +727,18 @@ __global__ __launch_bounds__(256) void mq_kernel(MqArgs a) {
                     for (int jj = 0; jj < 4; jj++) ub[rloc * 8 * NG + 8 * g + 4 * h + jj] = (float)acc[0][g][jj];
             }
             block_sync();
-            if (mi == 0 && row_ok) {
+            if (mi == 0) {  // uniform per wave; the rows of an FFN tile are all in the matrix
 #pragma unroll
                 for (int g = 0; g < NG; g++)
 #pragma unroll
                     for (int jj = 0; jj < 4; jj++) {
-                        const int b = 8 * g + 4 * h + jj;
-                        if (b >= B) continue;
-                        const int64_t o = (int64_t)b * N + row;
+                        const int b = 8 * g + 4 * h + jj;  // the same slot for the 32 lanes of a half
                         const float gv = (float)acc[0][g][jj], uv = ub[rloc * 8 * NG + 8 * g + 4 * h + jj];
-                        a.y[o] = act_apply(a.act, gv) * uv;
+                        const float hv = act_apply(a.act, gv) * uv;  // 0 for the zero digits of slots past B
+                        if (a.hdig) emit_h_digit(a, hv, b, row);
+                        if (b >= B || !row_ok) continue;
+                        const int64_t o = (int64_t)b * N + row;
+                        if (a.y) a.y[o] = hv;
                         if (a.g_out) a.g_out[o] = gv;
                         if (a.u_out) a.u_out[o] = uv;
                     }
@@ -667,15 +814,20 @@ __global__ __launch_bounds__(256) void mq_kernel(MqArgs a) {
         const int e = tid + 256 * m;
         const int b = e / TILE;
         const int64_t r = tile0 + (e - b * TILE);
-        if (b >= B || r >= N) continue;
-        const int64_t o = (int64_t)b * N + r;
         const float s0 = s[m][0];
         if constexpr (FFN) {
+            // a wave holds one batch slot's 64 rows: a run in each half
             const float s1 = s[m][NP - 1];
-            a.y[o] = act_apply(a.act, s0) * s1;
+            const float hv = act_apply(a.act, s0) * s1;  // 0 for slots past B
+            if (a.hdig) emit_h_digit(a, hv, b, r);
+            if (b >= B || r >= N) continue;
+            const int64_t o = (int64_t)b * N + r;
+            if (a.y) a.y[o] = hv;
             if (a.g_out) a.g_out[o] = s0;
             if (a.u_out) a.u_out[o] = s1;
         } else {
+            if (b >= B || r >= N) continue;
+            const int64_t o = (int64_t)b * N + r;
             if (a.pn.w1) xstore(a.pn.p + o, s0);
             else a.y[o] = a.res ? s0 + a.res[o] : s0;
         }

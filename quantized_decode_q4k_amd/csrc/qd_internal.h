@@ -179,6 +179,12 @@ struct MqArgs {
     int batch;
     int act;
     PostNorm pn;            // GEMV row epilogue (pn.w1 = nullptr: none)
+    // FFN: h also written as the activation digits of the down projection
+    // (its K is this launch's N), in xdig_kernel's layout; y may then be
+    // nullptr (h not kept in fp32)
+    uint8_t *hdig;          // nullptr: none
+    int hd_nb;              // down superunits per row (N / 256)
+    int hd_sx;              // the down format takes run sums (Q4_K)
 };
 size_t mq_su_bytes_host(int fmt);      // digits bytes per (group, superunit)
 size_t mq_lds_bytes(int fmt, int ng);
