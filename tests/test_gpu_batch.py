@@ -1,8 +1,10 @@
-"""GPU parity for batches above one launch's 8 columns (run as successive
-launches of up to 8 columns): every column of the GEMV, the fused gate/up,
-the decode FFN and the fused Q/K/V projection against the oracle, at batch
-sizes that leave a ragged last chunk (9, 11, 17, 23) and at the 64-column
-limit.  The bar is the oracle bound for every column.
+"""GPU parity for batches above 8 columns: every column of the GEMV, the
+fused gate/up, the decode FFN (one matrix-core launch per projection over
+groups of 8 batch rows, a ragged last group at 9, 17 and 23 columns, the
+64-column limit) and the fused Q/K/V projection (successive launches of up
+to 8 columns) against the oracle.  The bar is the oracle bound for every
+column.  The decode FFN's down projection reads h as the digits the gate/up
+launch wrote: its output must not depend on whether h is also kept.
 """
 import numpy as np
 import pytest
@@ -67,6 +69,24 @@ def test_gate_up_and_ffn_decode_large_batch(qd, batch):
     hh = qd.qffn_gate_up_act("q4_k", dev(Wg), dev(Wu), dev(x), dev(nw), 1e-6, "silu", g_out=g)
     assert_bound("gate b%d" % batch, g.cpu().numpy(), g64, Sg)
     assert np.array_equal(hh.cpu().numpy().view(np.uint32), h.view(np.uint32))
+
+
+@pytest.mark.parametrize("batch", [3, 8, 19])
+def test_ffn_decode_h_kept_or_not(qd, batch):
+    hidden, ff = 768, 2048
+    Wg = synth.quant_weights("q4_k", ff, hidden, SEED, tensor_id=130)
+    Wu = synth.quant_weights("q4_k", ff, hidden, SEED, tensor_id=131)
+    Wd = synth.quant_weights("q6_k", hidden, ff, SEED, tensor_id=132)
+    x = synth.normal((batch, hidden), SEED, tensor_id=133)
+    nw = synth.normal((hidden,), SEED, tensor_id=134, mean=1.0, std=0.1)
+    say(f"ffn decode h kept or not batch={batch}")
+    h = torch.full((batch, ff), float("nan"), device="cuda")
+    y1 = qd.qffn_decode("q4_k", dev(Wg), dev(Wu), "q6_k", dev(Wd), dev(x), dev(nw), 1e-6, "gelu_tanh", h_out=h)
+    y2 = qd.qffn_decode("q4_k", dev(Wg), dev(Wu), "q6_k", dev(Wd), dev(x), dev(nw), 1e-6, "gelu_tanh")
+    y1, y2, h = y1.cpu().numpy(), y2.cpu().numpy(), h.cpu().numpy()
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    y64, Sy = oracle.gemv("q6_k", Wd, h, hidden, ff)
+    assert_bound(f"down b{batch}", y1, y64, Sy)
 
 
 def test_qkv_large_batch(qd):

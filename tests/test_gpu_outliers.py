@@ -1,6 +1,7 @@
-"""Activations with a large dynamic range, through the batch-1..2 paths that
-stage x as per-run digits (an exponent per run of 32 and a 31-bit integer
-per activation), against the oracle.
+"""Activations with a large dynamic range, through the paths that stage x as
+per-run digits (an exponent per run of 32 and a 31-bit integer per
+activation): the batch-1..2 GEMVs and the batch 3..64 matrix-core kernels,
+against the oracle.
 
 Each run of 32 activations carries one outlier 10^4 times the others (and
 some runs 10^5), so every other activation of the run is rounded at 2^-31 of
@@ -8,7 +9,8 @@ the outlier.  Where an outlier meets a zero weight (Q8_0 rows whose quant at
 the outlier's column is zeroed), the output bound 1e-4 * sum|w x| + 1e-6 is
 set by the small activations alone: the rounding must stay below it there
 too.  Shapes: the register GEMV (K = 2560), the LDS-streaming GEMV (K =
-10240) and the fused gate/up; batch 1 and 2.  Also: a run holding an
+10240) and the fused gate/up; batch 1 and 2, and 3, 8 and 19 on the
+matrix cores (one and three groups of 8 batch rows).  Also: a run holding an
 infinity gives a non-finite output on every row, as fp32 arithmetic would.
 """
 import numpy as np
@@ -53,7 +55,7 @@ def zero_q80_columns(W, N, K, cols, rows):
 
 @pytest.mark.parametrize("fmt", ["q4_k", "q6_k", "q8_0"])
 @pytest.mark.parametrize("N,K", [(256, 2560), (64, 10240)])
-@pytest.mark.parametrize("batch", [1, 2])
+@pytest.mark.parametrize("batch", [1, 2, 3, 8, 19])
 def test_gemv_outliers(qd, fmt, N, K, batch):
     say(f"outliers gemv {fmt} {N}x{K} batch={batch}")
     W = synth.quant_weights(fmt, N, K, SEED, tensor_id=301)
@@ -65,7 +67,7 @@ def test_gemv_outliers(qd, fmt, N, K, batch):
     assert_bound(f"{fmt} {N}x{K} b{batch} outliers", y, y64, S)
 
 
-@pytest.mark.parametrize("batch", [1, 2])
+@pytest.mark.parametrize("batch", [1, 2, 8])
 def test_gate_up_outliers(qd, batch):
     ff, hidden = 1024, 2560
     say(f"outliers gate/up q4_k {ff}x{hidden} batch={batch}")
@@ -86,11 +88,15 @@ def test_gate_up_outliers(qd, batch):
 
 @pytest.mark.parametrize("fmt", ["q4_k", "q6_k", "q8_0"])
 @pytest.mark.parametrize("K", [2560, 10240])
-def test_gemv_nonfinite_activation(qd, fmt, K):
+@pytest.mark.parametrize("batch", [1, 4])
+def test_gemv_nonfinite_activation(qd, fmt, K, batch):
     N = 64
-    say(f"non-finite activation {fmt} {N}x{K}")
+    say(f"non-finite activation {fmt} {N}x{K} batch={batch}")
     W = synth.quant_weights(fmt, N, K, SEED, tensor_id=306)
-    x = synth.normal((1, K), SEED, tensor_id=307)
+    x = synth.normal((batch, K), SEED, tensor_id=307)
     x[0, 77] = np.inf
     y = qd.qgemv(fmt, dev(W), dev(x)).cpu().numpy()
-    assert not np.isfinite(y).any(), f"{fmt} K={K}: an infinite activation left finite outputs"
+    assert not np.isfinite(y[0]).any(), f"{fmt} K={K}: an infinite activation left finite outputs"
+    if batch > 1:  # the other batch rows are untouched by row 0's infinity
+        y64, S = oracle.gemv(fmt, W, x[1:], N, K)
+        assert_bound(f"{fmt} {N}x{K} rows 1..{batch - 1}", y[1:], y64, S)

@@ -48,7 +48,7 @@ def _check(name, y, W, x, N, K, zero_rows_exact):
 
 @pytest.mark.parametrize("flip", [0.0, 0.03])
 @pytest.mark.parametrize("N,K", [(300, 2560), (64, 5376), (40, 10240)])
-@pytest.mark.parametrize("batch", [1, 2, 8])
+@pytest.mark.parametrize("batch", [1, 2, 8, 40])
 def test_cancel_gemv_automatic(qd, flip, N, K, batch):
     say(f"q4k cancel gemv N={N} K={K} batch={batch} flip={flip}")
     W = cancelling_q4k(N, K, seed=N + K + batch, flip_frac=flip)
