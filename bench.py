@@ -228,13 +228,13 @@ class Workload:
         c = self.copies[self.i]
         self.i = (self.i + 1) % self.ncopy
         qd, n = self.qd, self.name
-        if n in ("gemma3_ffn", "gemma4_ffn"):
+        if n in ("gemma3_ffn", "gemma4_ffn", "gemma4_ffn_b8"):
             qd.qffn_decode("q4_k", c["gate"], c["up"], "q6_k", c["down"], self.x, self.nw, 1e-6,
                            "gelu_tanh", y=self.y)
         elif n == "gemma4_prefill":
             qd.qgemm_prefill_gate_up_act("q4_k", c["gate"], c["up"], self.X, "gelu_tanh", H=self.H)
             qd.qgemm_prefill("q6_k", c["down"], self.H, Y=self.Y)
-        elif n in ("gemma3_ffn_2k", "gemma4_ffn_2k", "gemma4_ffn_b8", "gate_up_q4k"):
+        elif n in ("gemma3_ffn_2k", "gemma4_ffn_2k", "gate_up_q4k"):
             qd.qffn_gate_up_act("q4_k", c["gate"], c["up"], self.x, self.nw, 1e-6, "gelu_tanh", h=self.h)
             if n != "gate_up_q4k":
                 qd.qgemv_q6k(c["down"], self.h, self.y)
@@ -460,9 +460,10 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         # arithmetic of the path: prefill bf16 MFMA with fp32 accumulation;
-        # batch-1..2 decode: exact int8 x int8 -> int32 dot products on
-        # activation digits, block scales in fp64 (Q4_K) / fp32 (Q6_K, Q8_0)
-        "dtype": "bf16-mfma/f32" if prefill else ("i8-dot-i32/f64-f32" if wl.batch <= 2 else "f32"),
+        # decode: exact int8 x int8 -> int32 products of quants and activation
+        # digits (v_dot4 at batch 1-2, int8 MFMA from batch 3 on), block
+        # scales in fp64 (Q4_K) / fp32 (Q6_K, Q8_0)
+        "dtype": "bf16-mfma/f32" if prefill else ("i8-dot-i32/f64-f32" if wl.batch <= 2 else "i8-mfma-i32/f64-f32"),
         "data": "synthetic",
         "config": {
             "workload": workloads.get(args.workload, args.workload),
