@@ -8,13 +8,15 @@
 // format is handled, and the weights are the bf16 rounding (nearest even) of
 // the exact fp32 dequantised value.
 //
-// Work split.  A workgroup of four waves owns 32*TM tokens by 256
-// accumulator columns.  The waves split the columns only (64 each: two
-// 32-row weight slices, or 32 gate rows and the same 32 up rows), so each
-// weight is decoded once per workgroup, straight from its quantized bytes
-// into the B operand of the MFMA, in registers.  The activations of a
+// Work split.  A workgroup of eight waves (two per SIMD) owns 32*TM tokens
+// by 256 accumulator columns.  The waves split the columns only (32 each:
+// one 32-row weight slice; for the gate/up variant waves 0-3 take 32 gate
+// rows each and waves 4-7 the same rows of up), so each weight is decoded
+// once per workgroup, straight from its quantized bytes into the B operand
+// of the MFMA, in registers.  Two waves per SIMD let one wave's decode (the
+// vector ALU) run while the other's MFMAs execute.  The activations of a
 // K-tile (bf16, 128 per token) are shared through LDS: copied there by
-// global_load_lds_dwordx4, double-buffered, with the sixteen 16-byte chunks
+// global_load_lds_dwordx4, triple-buffered, with the sixteen 16-byte chunks
 // of each token's row XOR-swizzled by the token index so that the operand
 // reads of 16 consecutive tokens hit 16 different bank groups.
 //
@@ -33,6 +35,7 @@
 // last to arrive (device-scope counter) sums the partials in split order, so
 // results do not depend on arrival order.
 #include "qd_decode.h"
+
 
 namespace qd {
 
@@ -63,6 +66,34 @@ QD_DEV int xchunk(int s, int h) {
         // 4p + 2h + 1); step s takes e = 8s..8s+7
         return 8 * h + s;
     }
+}
+
+// Q6_K rows are 210 bytes, so a block starts on a 2-byte boundary; its
+// fields are read as 16-byte (quants), 8-byte (scales) and 2-byte (d) loads
+// at 2-byte-aligned addresses, which the hardware reads unaligned.  Lane
+// c = 2p + h of superunit t: half p, quant run h (as the GEMV kernels split
+// the block).
+typedef uint32_t pf_u4a2 __attribute__((ext_vector_type(4), aligned(2)));
+typedef uint32_t pf_u2a2 __attribute__((ext_vector_type(2), aligned(2)));
+struct RawQ6KU {
+    pf_u4a2 a, b, h;  // ql[64p + 16h ..], ql[64p + 32 + 16h ..], qh[32p + 16h ..]
+    pf_u2a2 s;        // scales 8p .. 8p + 7
+    uint32_t d;       // f16 d in the low half
+};
+QD_DEV void load_q6k_u(RawQ6KU &r, const uint8_t *blk, int p, int h) {
+    const uint8_t *pa = blk + 64 * p + 16 * h;
+    r.a = *reinterpret_cast<const pf_u4a2 *>(pa);
+    r.b = *reinterpret_cast<const pf_u4a2 *>(pa + 32);
+    r.h = *reinterpret_cast<const pf_u4a2 *>(blk + 128 + 32 * p + 16 * h);
+    r.s = *reinterpret_cast<const pf_u2a2 *>(blk + 192 + 8 * p);
+    r.d = *reinterpret_cast<const uint16_t *>(blk + 208);
+}
+template <int FMT> struct PfRaw { using T = typename RawOf<FMT>::T; };
+template <> struct PfRaw<kQ6K> { using T = RawQ6KU; };
+template <int FMT>
+QD_DEV void pf_load(typename PfRaw<FMT>::T &r, const uint8_t *rowp, int t, int c, int nblk) {
+    if constexpr (FMT == kQ6K) load_q6k_u(r, rowp + 210 * t, c >> 1, c & 1);
+    else load_unit<FMT>(r, rowp, t, c, nblk);
 }
 
 // Decoded state of one weight row's share of a K-tile, and the bf16 B
@@ -106,18 +137,22 @@ struct Dec<kQ4K> {
 
 template <>
 struct Dec<kQ6K> {
-    uint32_t qa[4], qb[4], qh[4];  // re-aligned ql (two runs) and qh dwords
+    uint32_t qa[4], qb[4], qh[4];  // ql (two runs) and qh dwords
     float ds[4];                   // d * scale of groups 0..3
 
-    QD_DEV void prep(const RawQ6K &r, int c) {
-        const Q6Scales s = q6k_scales(r, c & 1);
-#pragma unroll
-        for (int g = 0; g < 4; g++) ds[g] = s.d * s.sc[g];
+    QD_DEV void prep(const RawQ6KU &r, int c) {
+        // groups g = 0..3 of run h use scales 8p + h + 2g
+        const int sh = 8 * (c & 1);
+        const float d = f16_lo(r.d);
+        ds[0] = d * sbyte(r.s.x >> sh, 0);
+        ds[1] = d * sbyte(r.s.x >> sh, 2);
+        ds[2] = d * sbyte(r.s.y >> sh, 0);
+        ds[3] = d * sbyte(r.s.y >> sh, 2);
 #pragma unroll
         for (int k = 0; k < 4; k++) {
-            qa[k] = align_bytes(r.a[k + 1], r.a[k], r.sh);
-            qb[k] = align_bytes(r.b[k + 1], r.b[k], r.sh);
-            qh[k] = align_bytes(r.h[k + 1], r.h[k], r.sh);
+            qa[k] = r.a[k];
+            qb[k] = r.b[k];
+            qh[k] = r.h[k];
         }
     }
     template <int S>
@@ -168,17 +203,47 @@ struct Dec<kQ80> {
     }
 };
 
-// One workgroup per CU and so one wave per SIMD: the whole register file is
-// this wave's, which lets the next step's activation operands load while the
-// current step's MFMAs run.
+constexpr int kGemmWaves = 8;
+constexpr int kGemmThreads = 64 * kGemmWaves;
+
+// Loads are issued two K-tiles ahead: K-tile kt's activations and weights
+// are requested while K-tile kt - 2 is multiplied, into the third of three
+// activation buffers and three weight register sets.  Global load
+// instructions per lane for one K-tile's weights (load_unit): the wait at
+// the top of a K-tile leaves the next K-tile's loads in flight.  The count
+// only has to be exact for speed; the activations of the current K-tile are
+// complete for any value up to twice the true count, and the compiler itself
+// waits for weight registers before their first use.
+template <int FMT>
+constexpr int kPfWeightLoads = FMT == kQ4K ? 3 : FMT == kQ6K ? 5 : 6;
+
+// s_waitcnt with vmcnt(n) and no wait on the other counters
+template <int N>
+QD_DEV void pf_vm_wait() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One workgroup per CU, two waves per SIMD (at most 256 registers each).
 template <int FMT, bool FFN, int TM>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_kernel(GemmArgs a) {
     constexpr int BM = 32 * TM;
-    constexpr int XBUF = BM * kXRowBytes;     // bytes per activation buffer
-    constexpr int XLOADS = BM / 16;           // global_load_lds per wave per K-tile
-    constexpr int TILEF = BM * kGemmCols;     // floats per partial tile
-    constexpr int WAVEF = TILEF / 4;
-    __shared__ __attribute__((aligned(1024))) uint8_t xs[2 * XBUF];
+    constexpr int XBUF = BM * kXRowBytes;          // bytes per activation buffer
+    constexpr int XLOADS = BM / (4 * kGemmWaves);  // global_load_lds per wave per K-tile
+    constexpr int TILEF = BM * kGemmCols;          // floats per partial tile
+    constexpr int WAVEF = TILEF / kGemmWaves;
+    static_assert(XLOADS >= 1 && BM % (4 * kGemmWaves) == 0, "token tile");
+    constexpr int NLD = XLOADS + kPfWeightLoads<FMT>;  // load instructions per K-tile
+    static_assert(!FFN || 2 * WAVEF * 4 <= XBUF, "up exchange fits two activation buffers");
+    // one array per buffer, so that the compiler sees that copies into one
+    // cannot alias operand reads of another
+    __shared__ __attribute__((aligned(1024))) uint8_t xs0[XBUF];
+    __shared__ __attribute__((aligned(1024))) uint8_t xs1[XBUF];
+    __shared__ __attribute__((aligned(1024))) uint8_t xs2[XBUF];
+    auto xbuf = [&](auto jc) -> uint8_t * {
+        constexpr int J = decltype(jc)::value;
+        return J == 0 ? xs0 : J == 1 ? xs1 : xs2;
+    };
     __shared__ int s_last;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -194,74 +259,73 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int kt0 = ks * a.kt_per_split;
     const int kt1 = min(a.kt_total, kt0 + a.kt_per_split);
 
-    // weight rows of this lane (rows past N read row N-1; never stored)
-    int64_t nrow[2];
-    const uint8_t *rowp[2];
+    // weight row of this lane (rows past N read row N-1; never stored)
+    int64_t nrow;
+    const uint8_t *rowp;
     if constexpr (FFN) {
-        nrow[0] = nrow[1] = (int64_t)nt * 128 + 32 * w + l32;
-        const int64_t nc = min(nrow[0], N - 1);
-        rowp[0] = a.Wg + nc * a.row_bytes;
-        rowp[1] = a.Wu + nc * a.row_bytes;
+        nrow = (int64_t)nt * 128 + 32 * (w & 3) + l32;
+        rowp = (w < 4 ? a.Wg : a.Wu) + min(nrow, N - 1) * a.row_bytes;
     } else {
-#pragma unroll
-        for (int i = 0; i < 2; i++) {
-            nrow[i] = (int64_t)nt * kGemmCols + 64 * w + 32 * i + l32;
-            rowp[i] = a.Wg + min(nrow[i], N - 1) * a.row_bytes;
-        }
+        nrow = (int64_t)nt * kGemmCols + 32 * w + l32;
+        rowp = a.Wg + min(nrow, N - 1) * a.row_bytes;
     }
 
-    // activation staging: load i of this wave fills LDS rows 16 i + 4 w .. +3;
-    // lane l writes chunk slot l % 16 of row 16 i + 4 w + l / 16, which holds
+    // activation staging: load i of this wave fills LDS rows 32 i + 4 w .. +3;
+    // lane l writes chunk slot l % 16 of row 32 i + 4 w + l / 16, which holds
     // logical chunk kap = slot ^ (row % 16)
     const int srow = 4 * w + (lane >> 4);
     const int kap = (lane & 15) ^ (srow & 15);
     uint32_t xoff[XLOADS];  // element offset of each staged row (rows past M read row M-1)
 #pragma unroll
     for (int i = 0; i < XLOADS; i++)
-        xoff[i] = (uint32_t)(min(m0 + 16 * i + srow, M - 1) * K) + 8 * kap;
+        xoff[i] = (uint32_t)(min(m0 + 4 * kGemmWaves * i + srow, M - 1) * K) + 8 * kap;
 
-    typename RawOf<FMT>::T raw[2][2];  // [buffer][row]
-    Dec<FMT> dec[2];
-    f32x16 acc[TM][2];
+    typename PfRaw<FMT>::T raw[3];  // [buffer]
+    Dec<FMT> dec;
+    f32x16 acc[TM];
 #pragma unroll
-    for (int i = 0; i < TM; i++) acc[i][0] = acc[i][1] = f32x16{};
+    for (int i = 0; i < TM; i++) acc[i] = f32x16{};
 
-    auto issue = [&](int kt, int buf, typename RawOf<FMT>::T (&rw)[2]) {
+    auto issue = [&](int kt, auto jc, typename PfRaw<FMT>::T &rw) {
         const int64_t kbase = (int64_t)kt * kGemmKT;
         const bool kin = kbase + 8 * kap < K;
-        uint8_t *dst = xs + buf * XBUF + w * 1024;
+        uint8_t *dst = xbuf(jc) + w * 1024;
         // a chunk past K reads X[0..7] (always in bounds) and is zeroed in
         // LDS before use, so both arms of the select share one address form
 #pragma unroll
         for (int i = 0; i < XLOADS; i++)
             __builtin_amdgcn_global_load_lds((gbl_void *)(a.X + (kin ? xoff[i] + kbase : 0)),
-                                             (lds_void *)(dst + i * 4096), 16, 0, 0);
+                                             (lds_void *)(dst + i * 1024 * kGemmWaves), 16, 0, 0);
         const int t = kt >> 1, c = 2 * (kt & 1) + h;
-        load_unit<FMT>(rw[0], rowp[0], t, c, a.nblk);
-        load_unit<FMT>(rw[1], rowp[1], t, c, a.nblk);
+        pf_load<FMT>(rw, rowp, t, c, a.nblk);
     };
 
     // A-operand address of token row 32 tm + l32 for chunk kap: the slot is
     // kap ^ (row % 16) = kap ^ (lane % 16)
-    const uint8_t *xa = xs + l32 * kXRowBytes;
+    const int xa = l32 * kXRowBytes;
     const int sw = lane & 15;
 
-    auto body = [&](int kt, int buf, typename RawOf<FMT>::T (&cur)[2],
-                    typename RawOf<FMT>::T (&nxt)[2]) {
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of K-tile kt are complete
+    auto body = [&](int kt, auto jc) {
+        constexpr int buf = decltype(jc)::value, nbuf = (buf + 2) % 3;
+        // K-tile kt's loads are complete; kt + 1's may still be in flight
+        pf_vm_wait<NLD>();
         if ((int64_t)(kt + 1) * kGemmKT > K &&
             (int64_t)kt * kGemmKT + 8 * kap >= K) {  // zero the chunks past K
-            uint8_t *dst = xs + buf * XBUF + w * 1024 + 16 * lane;
+            uint8_t *dst = xbuf(jc) + w * 1024 + 16 * lane;
 #pragma unroll
             for (int i = 0; i < XLOADS; i++)
-                *reinterpret_cast<uint4 *>(dst + i * 4096) = make_uint4(0u, 0u, 0u, 0u);
+                *reinterpret_cast<uint4 *>(dst + i * 1024 * kGemmWaves) = make_uint4(0u, 0u, 0u, 0u);
         }
-        __syncthreads();                // ... and every wave's; buffer buf^1 is free
-        const int c = 2 * (kt & 1) + h;
-        dec[0].prep(cur[0], c);
-        dec[1].prep(cur[1], c);
-        if (kt + 1 < kt1) issue(kt + 1, buf ^ 1, nxt);
-        const uint8_t *xb = xa + buf * XBUF;
+        // ... and every wave's; the buffer of kt - 1 is free.  A plain
+        // barrier: __syncthreads() would also wait for the loads in flight
+        __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        dec.prep(raw[buf], 2 * (kt & 1) + h);
+        // every body issues (the last two repeat the split's last K-tile into
+        // buffers nobody reads), so each buffer keeps its registers and the
+        // count of loads in flight is the same at every wait
+        issue(min(kt + 2, kt1 - 1), std::integral_constant<int, nbuf>{}, raw[nbuf]);
+        const uint8_t *xb = xbuf(jc) + xa;
         // A operands of step S (TM token rows) from LDS
         auto load_a = [&](auto sc, bf16x8 (&A)[TM]) {
             constexpr int S = decltype(sc)::value;
@@ -277,13 +341,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         // other buffer first, so their LDS latency overlaps these MFMAs
         auto mstep = [&](auto sc, const bf16x8 (&A)[TM]) {
             constexpr int S = decltype(sc)::value;
-            const bf16x8 B0 = dec[0].template step<S>();
-            const bf16x8 B1 = dec[1].template step<S>();
+            const bf16x8 B = dec.template step<S>();
 #pragma unroll
-            for (int i = 0; i < TM; i++) {
-                acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[i], B0, acc[i][0], 0, 0, 0);
-                acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[i], B1, acc[i][1], 0, 0, 0);
-            }
+            for (int i = 0; i < TM; i++) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[i], B, acc[i], 0, 0, 0);
         };
         bf16x8 Ae[TM], Ao[TM];
         load_a(std::integral_constant<int, 0>{}, Ae);
@@ -304,11 +364,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         mstep(std::integral_constant<int, 7>{}, Ao);
     };
 
-    if (kt0 < kt1) issue(kt0, 0, raw[0]);
-    for (int kt = kt0; kt < kt1; kt += 2) {
-        body(kt, 0, raw[0], raw[1]);
-        if (kt + 1 < kt1) body(kt + 1, 1, raw[1], raw[0]);
+    if (kt0 < kt1) {
+        issue(kt0, std::integral_constant<int, 0>{}, raw[0]);
+        __builtin_amdgcn_sched_barrier(0);  // K-tile kt0's loads all go first
+        issue(min(kt0 + 1, kt1 - 1), std::integral_constant<int, 1>{}, raw[1]);
     }
+    // whole rounds of three K-tiles, then the one or two left (no path
+    // through the loop skips a stage, so the wait counts above hold on it)
+    int kt = kt0;
+    for (; kt + 2 < kt1; kt += 3) {
+        body(kt, std::integral_constant<int, 0>{});
+        body(kt + 1, std::integral_constant<int, 1>{});
+        body(kt + 2, std::integral_constant<int, 2>{});
+    }
+    if (kt < kt1) body(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < kt1) body(kt + 1, std::integral_constant<int, 1>{});
+    pf_vm_wait<0>();  // the repeated loads have landed before LDS is reused or released
 
     // ---- split-K: publish, then the last workgroup of the tile sums.
     if (a.splits > 1) {
@@ -318,11 +389,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
         for (int i = 0; i < TM; i++)
 #pragma unroll
-            for (int j = 0; j < 2; j++)
-#pragma unroll
-                for (int r = 0; r < 16; r++)
-                    __hip_atomic_store(own + ((i * 2 + j) * 16 + r) * 64, acc[i][j][r],
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int r = 0; r < 16; r++)
+                __hip_atomic_store(own + (i * 16 + r) * 64, acc[i][r], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
         __atomic_signal_fence(__ATOMIC_SEQ_CST);  // keep the stores above the wait
         __builtin_amdgcn_s_waitcnt(0);            // this wave's stores are complete
         __syncthreads();
@@ -336,41 +405,54 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
         for (int i = 0; i < TM; i++)
 #pragma unroll
-            for (int j = 0; j < 2; j++)
-#pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    const float *p = part + ((i * 2 + j) * 16 + r) * 64;
-                    float s = 0.f;
-                    for (int k = 0; k < a.splits; k++)
-                        s += __hip_atomic_load(p + (int64_t)k * TILEF, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-                    acc[i][j][r] = s;
-                }
+            for (int r = 0; r < 16; r++) {
+                const float *p = part + (i * 16 + r) * 64;
+                float s = 0.f;
+                for (int k = 0; k < a.splits; k++)
+                    s += __hip_atomic_load(p + (int64_t)k * TILEF, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                acc[i][r] = s;
+            }
         if (tid == 0)  // ready for the next call
             __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
     // ---- epilogue: accumulator register r of lane l is token
     // 8 (r / 4) + 4 h + r % 4 of the 32-token slice, column l % 32
+    if constexpr (FFN) {
+        // the up waves hand their sums to the gate waves of the same rows
+        // through the (now idle) activation buffers
+        float *ub = reinterpret_cast<float *>((w & 2) ? xs1 : xs0) + (w & 1) * WAVEF + lane;
+        __syncthreads();  // every wave's last operand reads are done
+        if (w >= 4) {
 #pragma unroll
-    for (int i = 0; i < TM; i++)
+            for (int i = 0; i < TM; i++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-            const int64_t m = m0 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (m >= M) continue;
-            if constexpr (FFN) {
-                if (nrow[0] >= N) continue;
-                const float g = acc[i][0][r], u = acc[i][1][r];
-                const int64_t o = m * N + nrow[0];
+                for (int r = 0; r < 16; r++) ub[(i * 16 + r) * 64] = acc[i][r];
+        }
+        __syncthreads();
+        if (w >= 4 || nrow >= N) return;
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int64_t m = m0 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (m >= M) continue;
+                const float g = acc[i][r], u = ub[(i * 16 + r) * 64];
+                const int64_t o = m * N + nrow;
                 a.H[o] = f32_to_bf16(act_apply(a.act, g) * u);
                 if (a.g_out) a.g_out[o] = g;
                 if (a.u_out) a.u_out[o] = u;
-            } else {
-#pragma unroll
-                for (int j = 0; j < 2; j++)
-                    if (nrow[j] < N) a.Y[m * N + nrow[j]] = acc[i][j][r];
             }
-        }
+    } else {
+        if (nrow >= N) return;
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int64_t m = m0 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (m < M) a.Y[m * N + nrow] = acc[i][r];
+            }
+    }
 }
 
 template <int FMT, bool FFN>
@@ -378,9 +460,9 @@ hipError_t launch_f(int tm, const GemmArgs &a, hipStream_t st) {
     const int64_t grid = (int64_t)a.m_tiles * a.n_tiles * a.splits;
     if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidValue;
     if (tm == 4)
-        hipLaunchKernelGGL((gemm_kernel<FMT, FFN, 4>), dim3((unsigned)grid), dim3(kThreads), 0, st, a);
+        hipLaunchKernelGGL((gemm_kernel<FMT, FFN, 4>), dim3((unsigned)grid), dim3(kGemmThreads), 0, st, a);
     else if (tm == 2)
-        hipLaunchKernelGGL((gemm_kernel<FMT, FFN, 2>), dim3((unsigned)grid), dim3(kThreads), 0, st, a);
+        hipLaunchKernelGGL((gemm_kernel<FMT, FFN, 2>), dim3((unsigned)grid), dim3(kGemmThreads), 0, st, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
