@@ -540,6 +540,17 @@ qd_status qd_set_walk_override(int rows_per_group);
 qd_status qd_set_gemm_override(int tm, int splits);
 
 /*
+ * Stream-K scheduling of the prefill GEMMs (process-wide tuning knob).
+ * units_per_wg: 0 = off (whole tiles, or the planned K-split), > 0 = each
+ * workgroup takes that many consecutive (tile, K-tile of 128 weights) units
+ * in tile-major order.  A tile shared by several workgroups is summed by the
+ * last to arrive in workgroup order, so results do not depend on timing
+ * (they differ from the unsplit sums by the order of fp32 additions).
+ * Returns QD_EINVAL below 0.
+ */
+qd_status qd_set_gemm_streamk(int units_per_wg);
+
+/*
  * Shape override of the streaming GEMV path (process-wide; 0 = automatic).
  *   wg_per_cu  workgroups per CU (1..8; LDS is divided between them)
  *   depth      steps of 16 superunits in flight per copying wave (1..32,

@@ -80,6 +80,7 @@ SIGNATURES = {
     "qd_set_launch_override": (_I, [_I, _I, _I]),
     "qd_set_walk_override": (_I, [_I]),
     "qd_set_gemm_override": (_I, [_I, _I]),
+    "qd_set_gemm_streamk": (_I, [_I]),
     "qd_set_stream_override": (_I, [_I, _I, _I, _I]),
     "qd_set_batch_override": (_I, [_I, _I]),
     "qd_plan_q8act": (_I, [_I64, _I64, _I, _P]),
@@ -517,6 +518,11 @@ def qdequant_bf16(fmt, W: torch.Tensor, K: int, out: torch.Tensor | None = None)
 def set_gemm_override(tm: int = 0, splits: int = 0):
     """Prefill tile override (0 = automatic)."""
     _check("qd_set_gemm_override", lib().qd_set_gemm_override(tm, splits))
+
+
+def set_gemm_streamk(units_per_wg: int = 0):
+    """Prefill stream-K: 0 off, > 0 that many (tile, K-tile) units per workgroup."""
+    _check("qd_set_gemm_streamk", lib().qd_set_gemm_streamk(units_per_wg))
 
 
 def set_stream_override(wg_per_cu: int = 0, depth: int = 0, consumers: int = 0, producers: int = 0):

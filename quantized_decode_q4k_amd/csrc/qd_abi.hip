@@ -779,12 +779,17 @@ qd_status run_ffn_decode(int fmt_gu, const void *Wg, const void *Wu, int fmt_d, 
 }
 
 // ------------------------------------------------------------ prefill ---
-std::atomic<int> g_gemm_tm{0}, g_gemm_splits{0};
+std::atomic<int> g_gemm_tm{0}, g_gemm_splits{0}, g_gemm_sk{0};
 constexpr int kGemmTargetWorkgroups = 256;  // one resident workgroup per CU (LDS and registers)
 constexpr int kGemmMinKTiles = 8;          // K-tiles per split, at least
 
 struct GemmPlan {
     int tm, m_tiles, n_tiles, kt_total, kt_per_split, splits;
+    int sk_per;  // stream-K units per workgroup (0: one tile or K-slice each)
+    int64_t grid() const {
+        const int64_t units = (int64_t)m_tiles * n_tiles * kt_total;
+        return sk_per > 0 ? (units + sk_per - 1) / sk_per : (int64_t)m_tiles * n_tiles * splits;
+    }
 };
 
 GemmPlan gemm_plan(bool ffn, int64_t M, int64_t N, int64_t K) {
@@ -807,6 +812,17 @@ GemmPlan gemm_plan(bool ffn, int64_t M, int64_t N, int64_t K) {
     }
     p.kt_per_split = (p.kt_total + s - 1) / s;
     p.splits = (p.kt_total + p.kt_per_split - 1) / p.kt_per_split;  // every split non-empty
+    // stream-K only on request: each workgroup an equal run of (tile,
+    // K-tile) units.  Measured level with whole tiles on the Gemma-4-31B
+    // gate/up (512 tokens: 672 tiles, 2.625 rounds of 256; 298-306 us either
+    // way) and slower on its split-K down (247 against 176 us)
+    p.sk_per = 0;
+    const int sk = g_gemm_sk.load();
+    if (sk > 0 && tiles <= kMaxTiles) p.sk_per = (int)std::min<int64_t>(sk, tiles * p.kt_total);
+    if (p.sk_per > 0) {
+        p.splits = 1;
+        p.kt_per_split = p.kt_total;
+    }
     return p;
 }
 
@@ -856,9 +872,13 @@ qd_status run_gemm(int fmt, bool ffn, const void *Wg, const void *Wu, const uint
     a.m_tiles = p.m_tiles;
     a.n_tiles = p.n_tiles;
     a.act = act;
-    if (p.splits > 1) {
+    a.sk_per = p.sk_per;
+    if (p.grid() <= 0 || p.grid() > 0x7FFFFFFF) return QD_ESHAPE;
+    if (p.splits > 1 || p.sk_per > 0) {
         Workspace w;
-        const size_t need = (size_t)p.m_tiles * p.n_tiles * p.splits * (32 * p.tm) * qd::kGemmCols;
+        const size_t tile_f = (size_t)(32 * p.tm) * qd::kGemmCols;
+        const size_t need = p.sk_per > 0 ? 2 * (size_t)p.grid() * tile_f
+                                         : (size_t)p.m_tiles * p.n_tiles * p.splits * tile_f;
         st = get_workspace(hs, need, &w);
         if (st != QD_OK) return st;
         a.partials = w.partials;
@@ -1407,6 +1427,12 @@ qd_status qgemm_prefill_gate_up_act(qd_format fmt, const void *Wg, const void *W
                                     float *u_out, int64_t M, int64_t N_ff, int64_t K,
                                     void *stream) {
     return run_gemm(fmt, true, Wg, Wu, X, act, nullptr, H, g_out, u_out, M, N_ff, K, stream);
+}
+
+qd_status qd_set_gemm_streamk(int units_per_wg) {
+    if (units_per_wg < 0) return QD_EINVAL;
+    g_gemm_sk.store(units_per_wg);
+    return QD_OK;
 }
 
 qd_status qd_set_gemm_override(int tm, int splits) {

@@ -207,7 +207,7 @@ struct GemmArgs {
     uint16_t *H;            // bf16 [M][N] (FFN variant)
     float *g_out;           // optional fp32 [M][N] (FFN variant)
     float *u_out;
-    float *partials;        // split-K: tiles * splits * 32*tm * kGemmCols floats
+    float *partials;        // split-K: tiles * splits, stream-K: 2 * grid partial tiles of 32*tm * kGemmCols floats
     unsigned *counters;     // split-K: one per output tile, zero between calls
     int64_t M, N, K;
     int64_t row_bytes;
@@ -217,6 +217,7 @@ struct GemmArgs {
     int splits;
     int m_tiles, n_tiles;
     int act;
+    int sk_per;             // stream-K: (tile, K-tile) units per workgroup; 0 = split-K
 };
 hipError_t launch_gemm(int fmt, bool ffn, int tm, const GemmArgs &a, hipStream_t st);
 

@@ -249,215 +249,256 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2,
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int h = lane >> 5, l32 = lane & 31;
 
-    int bid = blockIdx.x;
-    const int mt = bid % a.m_tiles;
-    bid /= a.m_tiles;
-    const int nt = bid % a.n_tiles;
-    const int ks = bid / a.n_tiles;
     const int64_t M = a.M, N = a.N, K = a.K;
-    const int64_t m0 = (int64_t)mt * BM;
-    const int kt0 = ks * a.kt_per_split;
-    const int kt1 = min(a.kt_total, kt0 + a.kt_per_split);
-
-    // weight row of this lane (rows past N read row N-1; never stored)
-    int64_t nrow;
-    const uint8_t *rowp;
-    if constexpr (FFN) {
-        nrow = (int64_t)nt * 128 + 32 * (w & 3) + l32;
-        rowp = (w < 4 ? a.Wg : a.Wu) + min(nrow, N - 1) * a.row_bytes;
-    } else {
-        nrow = (int64_t)nt * kGemmCols + 32 * w + l32;
-        rowp = a.Wg + min(nrow, N - 1) * a.row_bytes;
-    }
+    const int KT = a.kt_total;
 
     // activation staging: load i of this wave fills LDS rows 32 i + 4 w .. +3;
     // lane l writes chunk slot l % 16 of row 32 i + 4 w + l / 16, which holds
     // logical chunk kap = slot ^ (row % 16)
     const int srow = 4 * w + (lane >> 4);
     const int kap = (lane & 15) ^ (srow & 15);
-    uint32_t xoff[XLOADS];  // element offset of each staged row (rows past M read row M-1)
-#pragma unroll
-    for (int i = 0; i < XLOADS; i++)
-        xoff[i] = (uint32_t)(min(m0 + 4 * kGemmWaves * i + srow, M - 1) * K) + 8 * kap;
-
-    typename PfRaw<FMT>::T raw[3];  // [buffer]
-    Dec<FMT> dec;
-    f32x16 acc[TM];
-#pragma unroll
-    for (int i = 0; i < TM; i++) acc[i] = f32x16{};
-
-    auto issue = [&](int kt, auto jc, typename PfRaw<FMT>::T &rw) {
-        const int64_t kbase = (int64_t)kt * kGemmKT;
-        const bool kin = kbase + 8 * kap < K;
-        uint8_t *dst = xbuf(jc) + w * 1024;
-        // a chunk past K reads X[0..7] (always in bounds) and is zeroed in
-        // LDS before use, so both arms of the select share one address form
-#pragma unroll
-        for (int i = 0; i < XLOADS; i++)
-            __builtin_amdgcn_global_load_lds((gbl_void *)(a.X + (kin ? xoff[i] + kbase : 0)),
-                                             (lds_void *)(dst + i * 1024 * kGemmWaves), 16, 0, 0);
-        const int t = kt >> 1, c = 2 * (kt & 1) + h;
-        pf_load<FMT>(rw, rowp, t, c, a.nblk);
-    };
-
     // A-operand address of token row 32 tm + l32 for chunk kap: the slot is
     // kap ^ (row % 16) = kap ^ (lane % 16)
     const int xa = l32 * kXRowBytes;
     const int sw = lane & 15;
 
-    auto body = [&](int kt, auto jc) {
-        constexpr int buf = decltype(jc)::value, nbuf = (buf + 2) % 3;
-        // K-tile kt's loads are complete; kt + 1's may still be in flight
-        pf_vm_wait<NLD>();
-        if ((int64_t)(kt + 1) * kGemmKT > K &&
-            (int64_t)kt * kGemmKT + 8 * kap >= K) {  // zero the chunks past K
-            uint8_t *dst = xbuf(jc) + w * 1024 + 16 * lane;
+    // ---- this workgroup's segments, each a tile and a range of its K-tiles.
+    // Split-K: one segment, K-slice blockIdx / tiles of the tile.  Stream-K
+    // (sk_per > 0): the (tile, K-tile) units numbered tile-major, sk_per
+    // consecutive units per workgroup, cut where a tile ends.  A tile whose
+    // units are shared by nc workgroups is summed by the last of them to
+    // arrive, in contributor order, so results do not depend on timing.
+    const int64_t units = (int64_t)a.m_tiles * a.n_tiles * KT;
+    int64_t u = a.sk_per > 0 ? (int64_t)blockIdx.x * a.sk_per : 0;
+    const int64_t u_end = a.sk_per > 0 ? min(units, u + a.sk_per) : 0;
+    for (bool more = true; more;) {
+        int64_t tile, gf = 0;
+        int kt0, kt1, nc, idx;
+        if (a.sk_per > 0) {
+            if (u >= u_end) break;
+            tile = u / KT;
+            kt0 = (int)(u - tile * KT);
+            kt1 = (int)min<int64_t>(KT, kt0 + (u_end - u));
+            gf = tile * KT / a.sk_per;  // contributors gf .. gl
+            nc = (int)((tile * KT + KT - 1) / a.sk_per - gf + 1);
+            idx = (int)(blockIdx.x - gf);
+            u += kt1 - kt0;
+        } else {
+            more = false;
+            const int tiles = a.m_tiles * a.n_tiles;
+            const int ks = blockIdx.x / tiles;
+            tile = blockIdx.x - (int64_t)ks * tiles;
+            kt0 = ks * a.kt_per_split;
+            kt1 = min(KT, kt0 + a.kt_per_split);
+            nc = a.splits;
+            idx = ks;
+        }
+        // partial-sum slot of contributor c: split-K, tile * splits + c;
+        // stream-K, 2 g (+1 when the tile is not g's first), g = gf + c
+        auto slot_of = [&](int c) -> int64_t {
+            if (a.sk_per <= 0) return tile * a.splits + c;
+            const int64_t g = gf + c;
+            return 2 * g + ((g * a.sk_per) / KT == tile ? 0 : 1);
+        };
+        const int mt = (int)(tile % a.m_tiles), nt = (int)(tile / a.m_tiles);
+        const int64_t m0 = (int64_t)mt * BM;
+
+        // weight row of this lane (rows past N read row N-1; never stored)
+        int64_t nrow;
+        const uint8_t *rowp;
+        if constexpr (FFN) {
+            nrow = (int64_t)nt * 128 + 32 * (w & 3) + l32;
+            rowp = (w < 4 ? a.Wg : a.Wu) + min(nrow, N - 1) * a.row_bytes;
+        } else {
+            nrow = (int64_t)nt * kGemmCols + 32 * w + l32;
+            rowp = a.Wg + min(nrow, N - 1) * a.row_bytes;
+        }
+        uint32_t xoff[XLOADS];  // element offset of each staged row (rows past M read row M-1)
+#pragma unroll
+        for (int i = 0; i < XLOADS; i++)
+            xoff[i] = (uint32_t)(min(m0 + 4 * kGemmWaves * i + srow, M - 1) * K) + 8 * kap;
+
+        typename PfRaw<FMT>::T raw[3];  // [buffer]
+        Dec<FMT> dec;
+        f32x16 acc[TM];
+#pragma unroll
+        for (int i = 0; i < TM; i++) acc[i] = f32x16{};
+
+        auto issue = [&](int kt, auto jc, typename PfRaw<FMT>::T &rw) {
+            const int64_t kbase = (int64_t)kt * kGemmKT;
+            const bool kin = kbase + 8 * kap < K;
+            uint8_t *dst = xbuf(jc) + w * 1024;
+            // a chunk past K reads X[0..7] (always in bounds) and is zeroed in
+            // LDS before use, so both arms of the select share one address form
 #pragma unroll
             for (int i = 0; i < XLOADS; i++)
-                *reinterpret_cast<uint4 *>(dst + i * 1024 * kGemmWaves) = make_uint4(0u, 0u, 0u, 0u);
-        }
-        // ... and every wave's; the buffer of kt - 1 is free.  A plain
-        // barrier: __syncthreads() would also wait for the loads in flight
-        __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
-        __builtin_amdgcn_s_barrier();
-        dec.prep(raw[buf], 2 * (kt & 1) + h);
-        // every body issues (the last two repeat the split's last K-tile into
-        // buffers nobody reads), so each buffer keeps its registers and the
-        // count of loads in flight is the same at every wait
-        issue(min(kt + 2, kt1 - 1), std::integral_constant<int, nbuf>{}, raw[nbuf]);
-        const uint8_t *xb = xbuf(jc) + xa;
-        // A operands of step S (TM token rows) from LDS
-        auto load_a = [&](auto sc, bf16x8 (&A)[TM]) {
-            constexpr int S = decltype(sc)::value;
-            const int off = 16 * (xchunk<FMT>(S, h) ^ sw);
-#pragma unroll
-            for (int i = 0; i < TM; i++)
-                A[i] = *reinterpret_cast<const bf16x8 *>(xb + i * 32 * kXRowBytes + off);
-            // keep these reads ahead of the MFMAs that follow (the scheduler
-            // would otherwise sink them next to their own, later MFMAs)
-            __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_global_load_lds((gbl_void *)(a.X + (kin ? xoff[i] + kbase : 0)),
+                                                 (lds_void *)(dst + i * 1024 * kGemmWaves), 16, 0, 0);
+            const int t = kt >> 1, c = 2 * (kt & 1) + h;
+            pf_load<FMT>(rw, rowp, t, c, a.nblk);
         };
-        // step S's MFMAs on A; the operands of step S + 1 are read into the
-        // other buffer first, so their LDS latency overlaps these MFMAs
-        auto mstep = [&](auto sc, const bf16x8 (&A)[TM]) {
-            constexpr int S = decltype(sc)::value;
-            const bf16x8 B = dec.template step<S>();
-#pragma unroll
-            for (int i = 0; i < TM; i++) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[i], B, acc[i], 0, 0, 0);
-        };
-        bf16x8 Ae[TM], Ao[TM];
-        load_a(std::integral_constant<int, 0>{}, Ae);
-        load_a(std::integral_constant<int, 1>{}, Ao);
-        mstep(std::integral_constant<int, 0>{}, Ae);
-        load_a(std::integral_constant<int, 2>{}, Ae);
-        mstep(std::integral_constant<int, 1>{}, Ao);
-        load_a(std::integral_constant<int, 3>{}, Ao);
-        mstep(std::integral_constant<int, 2>{}, Ae);
-        load_a(std::integral_constant<int, 4>{}, Ae);
-        mstep(std::integral_constant<int, 3>{}, Ao);
-        load_a(std::integral_constant<int, 5>{}, Ao);
-        mstep(std::integral_constant<int, 4>{}, Ae);
-        load_a(std::integral_constant<int, 6>{}, Ae);
-        mstep(std::integral_constant<int, 5>{}, Ao);
-        load_a(std::integral_constant<int, 7>{}, Ao);
-        mstep(std::integral_constant<int, 6>{}, Ae);
-        mstep(std::integral_constant<int, 7>{}, Ao);
-    };
 
-    if (kt0 < kt1) {
+        auto body = [&](int kt, auto jc) {
+            constexpr int buf = decltype(jc)::value, nbuf = (buf + 2) % 3;
+            // K-tile kt's loads are complete; kt + 1's may still be in flight
+            pf_vm_wait<NLD>();
+            if ((int64_t)(kt + 1) * kGemmKT > K &&
+                (int64_t)kt * kGemmKT + 8 * kap >= K) {  // zero the chunks past K
+                uint8_t *dst = xbuf(jc) + w * 1024 + 16 * lane;
+#pragma unroll
+                for (int i = 0; i < XLOADS; i++)
+                    *reinterpret_cast<uint4 *>(dst + i * 1024 * kGemmWaves) = make_uint4(0u, 0u, 0u, 0u);
+            }
+            // ... and every wave's; the buffer of kt - 1 is free.  A plain
+            // barrier: __syncthreads() would also wait for the loads in flight
+            __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+            __builtin_amdgcn_s_barrier();
+            dec.prep(raw[buf], 2 * (kt & 1) + h);
+            // every body issues (the last two repeat the segment's last K-tile
+            // into buffers nobody reads), so each buffer keeps its registers and
+            // the count of loads in flight is the same at every wait
+            issue(min(kt + 2, kt1 - 1), std::integral_constant<int, nbuf>{}, raw[nbuf]);
+            const uint8_t *xb = xbuf(jc) + xa;
+            // A operands of step S (TM token rows) from LDS
+            auto load_a = [&](auto sc, bf16x8 (&A)[TM]) {
+                constexpr int S = decltype(sc)::value;
+                const int off = 16 * (xchunk<FMT>(S, h) ^ sw);
+#pragma unroll
+                for (int i = 0; i < TM; i++)
+                    A[i] = *reinterpret_cast<const bf16x8 *>(xb + i * 32 * kXRowBytes + off);
+                // keep these reads ahead of the MFMAs that follow (the scheduler
+                // would otherwise sink them next to their own, later MFMAs)
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            // step S's MFMAs on A; the operands of step S + 1 are read into the
+            // other buffer first, so their LDS latency overlaps these MFMAs
+            auto mstep = [&](auto sc, const bf16x8 (&A)[TM]) {
+                constexpr int S = decltype(sc)::value;
+                const bf16x8 B = dec.template step<S>();
+#pragma unroll
+                for (int i = 0; i < TM; i++) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[i], B, acc[i], 0, 0, 0);
+            };
+            bf16x8 Ae[TM], Ao[TM];
+            load_a(std::integral_constant<int, 0>{}, Ae);
+            load_a(std::integral_constant<int, 1>{}, Ao);
+            mstep(std::integral_constant<int, 0>{}, Ae);
+            load_a(std::integral_constant<int, 2>{}, Ae);
+            mstep(std::integral_constant<int, 1>{}, Ao);
+            load_a(std::integral_constant<int, 3>{}, Ao);
+            mstep(std::integral_constant<int, 2>{}, Ae);
+            load_a(std::integral_constant<int, 4>{}, Ae);
+            mstep(std::integral_constant<int, 3>{}, Ao);
+            load_a(std::integral_constant<int, 5>{}, Ao);
+            mstep(std::integral_constant<int, 4>{}, Ae);
+            load_a(std::integral_constant<int, 6>{}, Ae);
+            mstep(std::integral_constant<int, 5>{}, Ao);
+            load_a(std::integral_constant<int, 7>{}, Ao);
+            mstep(std::integral_constant<int, 6>{}, Ae);
+            mstep(std::integral_constant<int, 7>{}, Ao);
+        };
+
         issue(kt0, std::integral_constant<int, 0>{}, raw[0]);
         __builtin_amdgcn_sched_barrier(0);  // K-tile kt0's loads all go first
         issue(min(kt0 + 1, kt1 - 1), std::integral_constant<int, 1>{}, raw[1]);
-    }
-    // whole rounds of three K-tiles, then the one or two left (no path
-    // through the loop skips a stage, so the wait counts above hold on it)
-    int kt = kt0;
-    for (; kt + 2 < kt1; kt += 3) {
-        body(kt, std::integral_constant<int, 0>{});
-        body(kt + 1, std::integral_constant<int, 1>{});
-        body(kt + 2, std::integral_constant<int, 2>{});
-    }
-    if (kt < kt1) body(kt, std::integral_constant<int, 0>{});
-    if (kt + 1 < kt1) body(kt + 1, std::integral_constant<int, 1>{});
-    pf_vm_wait<0>();  // the repeated loads have landed before LDS is reused or released
-
-    // ---- split-K: publish, then the last workgroup of the tile sums.
-    if (a.splits > 1) {
-        const int64_t tile = (int64_t)nt * a.m_tiles + mt;
-        float *part = a.partials + tile * a.splits * (int64_t)TILEF + w * WAVEF + lane;
-        float *own = part + (int64_t)ks * TILEF;
-#pragma unroll
-        for (int i = 0; i < TM; i++)
-#pragma unroll
-            for (int r = 0; r < 16; r++)
-                __hip_atomic_store(own + (i * 16 + r) * 64, acc[i][r], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);  // keep the stores above the wait
-        __builtin_amdgcn_s_waitcnt(0);            // this wave's stores are complete
-        __syncthreads();
-        if (tid == 0) {
-            const unsigned prev = __hip_atomic_fetch_add(a.counters + tile, 1u, __ATOMIC_RELAXED,
-                                                         __HIP_MEMORY_SCOPE_AGENT);
-            s_last = prev == (unsigned)a.splits - 1 ? 1 : 0;
+        // whole rounds of three K-tiles, then the one or two left (no path
+        // through the loop skips a stage, so the wait counts above hold on it)
+        int kt = kt0;
+        for (; kt + 2 < kt1; kt += 3) {
+            body(kt, std::integral_constant<int, 0>{});
+            body(kt + 1, std::integral_constant<int, 1>{});
+            body(kt + 2, std::integral_constant<int, 2>{});
         }
-        __syncthreads();
-        if (!s_last) return;
-#pragma unroll
-        for (int i = 0; i < TM; i++)
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const float *p = part + (i * 16 + r) * 64;
-                float s = 0.f;
-                for (int k = 0; k < a.splits; k++)
-                    s += __hip_atomic_load(p + (int64_t)k * TILEF, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                acc[i][r] = s;
-            }
-        if (tid == 0)  // ready for the next call
-            __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+        if (kt < kt1) body(kt, std::integral_constant<int, 0>{});
+        if (kt + 1 < kt1) body(kt + 1, std::integral_constant<int, 1>{});
+        pf_vm_wait<0>();  // the repeated loads have landed before LDS is reused or released
 
-    // ---- epilogue: accumulator register r of lane l is token
-    // 8 (r / 4) + 4 h + r % 4 of the 32-token slice, column l % 32
-    if constexpr (FFN) {
-        // the up waves hand their sums to the gate waves of the same rows
-        // through the (now idle) activation buffers
-        float *ub = reinterpret_cast<float *>((w & 2) ? xs1 : xs0) + (w & 1) * WAVEF + lane;
-        __syncthreads();  // every wave's last operand reads are done
-        if (w >= 4) {
+        // ---- a tile shared by several workgroups: publish, then the last
+        // to arrive sums the partials in contributor order
+        bool owner = true;
+        if (nc > 1) {
+            float *own = a.partials + slot_of(idx) * TILEF + w * WAVEF + lane;
 #pragma unroll
             for (int i = 0; i < TM; i++)
 #pragma unroll
-                for (int r = 0; r < 16; r++) ub[(i * 16 + r) * 64] = acc[i][r];
+                for (int r = 0; r < 16; r++)
+                    __hip_atomic_store(own + (i * 16 + r) * 64, acc[i][r], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);  // keep the stores above the wait
+            __builtin_amdgcn_s_waitcnt(0);            // this wave's stores are complete
+            __syncthreads();
+            if (tid == 0) {
+                const unsigned prev = __hip_atomic_fetch_add(a.counters + tile, 1u, __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_AGENT);
+                s_last = prev == (unsigned)nc - 1 ? 1 : 0;
+            }
+            __syncthreads();
+            owner = s_last != 0;
+            if (owner) {
+#pragma unroll
+                for (int i = 0; i < TM; i++)
+#pragma unroll
+                    for (int r = 0; r < 16; r++) acc[i][r] = 0.f;
+                for (int c = 0; c < nc; c++) {
+                    const float *p = a.partials + slot_of(c) * TILEF + w * WAVEF + lane;
+#pragma unroll
+                    for (int i = 0; i < TM; i++)
+#pragma unroll
+                        for (int r = 0; r < 16; r++)
+                            acc[i][r] += __hip_atomic_load(p + (i * 16 + r) * 64, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT);
+                }
+                if (tid == 0)  // ready for the next call
+                    __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
-        __syncthreads();
-        if (w >= 4 || nrow >= N) return;
+
+        // ---- epilogue: accumulator register r of lane l is token
+        // 8 (r / 4) + 4 h + r % 4 of the 32-token slice, column l % 32
+        if (owner) {
+            if constexpr (FFN) {
+                // the up waves hand their sums to the gate waves of the same rows
+                // through the (now idle) activation buffers
+                float *ub = reinterpret_cast<float *>((w & 2) ? xs1 : xs0) + (w & 1) * WAVEF + lane;
+                __syncthreads();  // every wave's last operand reads are done
+                if (w >= 4) {
 #pragma unroll
-        for (int i = 0; i < TM; i++)
+                    for (int i = 0; i < TM; i++)
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int64_t m = m0 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (m >= M) continue;
-                const float g = acc[i][r], u = ub[(i * 16 + r) * 64];
-                const int64_t o = m * N + nrow;
-                a.H[o] = f32_to_bf16(act_apply(a.act, g) * u);
-                if (a.g_out) a.g_out[o] = g;
-                if (a.u_out) a.u_out[o] = u;
+                        for (int r = 0; r < 16; r++) ub[(i * 16 + r) * 64] = acc[i][r];
+                }
+                __syncthreads();
+                if (w < 4 && nrow < N) {
+#pragma unroll
+                    for (int i = 0; i < TM; i++)
+#pragma unroll
+                        for (int r = 0; r < 16; r++) {
+                            const int64_t m = m0 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                            if (m >= M) continue;
+                            const float g = acc[i][r], uu = ub[(i * 16 + r) * 64];
+                            const int64_t o = m * N + nrow;
+                            a.H[o] = f32_to_bf16(act_apply(a.act, g) * uu);
+                            if (a.g_out) a.g_out[o] = g;
+                            if (a.u_out) a.u_out[o] = uu;
+                        }
+                }
+            } else if (nrow < N) {
+#pragma unroll
+                for (int i = 0; i < TM; i++)
+#pragma unroll
+                    for (int r = 0; r < 16; r++) {
+                        const int64_t m = m0 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                        if (m < M) a.Y[m * N + nrow] = acc[i][r];
+                    }
             }
-    } else {
-        if (nrow >= N) return;
-#pragma unroll
-        for (int i = 0; i < TM; i++)
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int64_t m = m0 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (m < M) a.Y[m * N + nrow] = acc[i][r];
-            }
+        }
+        __syncthreads();  // LDS and s_last free for the next segment
     }
 }
 
 template <int FMT, bool FFN>
 hipError_t launch_f(int tm, const GemmArgs &a, hipStream_t st) {
-    const int64_t grid = (int64_t)a.m_tiles * a.n_tiles * a.splits;
+    const int64_t units = (int64_t)a.m_tiles * a.n_tiles * a.kt_total;
+    const int64_t grid = a.sk_per > 0 ? (units + a.sk_per - 1) / a.sk_per : (int64_t)a.m_tiles * a.n_tiles * a.splits;
     if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidValue;
     if (tm == 4)
         hipLaunchKernelGGL((gemm_kernel<FMT, FFN, 4>), dim3((unsigned)grid), dim3(kGemmThreads), 0, st, a);

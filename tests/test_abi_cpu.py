@@ -262,6 +262,9 @@ def test_gemm_override_validation():
     assert L.qd_set_gemm_override(3, 0) == 1
     assert L.qd_set_gemm_override(0, -1) == 1
     assert L.qd_set_gemm_override(0, 0) == 0
+    assert L.qd_set_gemm_streamk(-1) == 1
+    assert L.qd_set_gemm_streamk(7) == 0
+    assert L.qd_set_gemm_streamk(0) == 0
 
 
 def test_stream_override_validation():

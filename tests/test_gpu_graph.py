@@ -114,6 +114,12 @@ def test_graph_moe_and_prefill(qd):
                       lambda: qd.qgemm_prefill("q6_k", W, X2, Y=Y2))
     finally:
         qd.set_gemm_override(0, 0)
+    qd.set_gemm_streamk(5)
+    try:
+        check_replays("stream-K qgemm_prefill", lambda: qd.qgemm_prefill("q6_k", W, X, Y=Y), [Y],
+                      lambda: qd.qgemm_prefill("q6_k", W, X2, Y=Y2))
+    finally:
+        qd.set_gemm_streamk(0)
 
 
 def test_graph_int8_activations(qd):

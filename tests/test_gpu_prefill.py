@@ -112,6 +112,46 @@ def test_prefill_split_k_deterministic(qd):
     assert_bound("no split", one, y64, S)
 
 
+# ------------------------------------------------------------- stream-K ---
+
+def run_streamk(qd, per, fn, tm=0):
+    qd.set_gemm_streamk(per)
+    qd.set_gemm_override(tm, 0)
+    try:
+        return fn()
+    finally:
+        qd.set_gemm_streamk(0)
+        qd.set_gemm_override(0, 0)
+
+
+@pytest.mark.parametrize("fmt,M,N,K", [("q4_k", 300, 700, 2048), ("q6_k", 130, 513, 1536),
+                                       ("q8_0", 77, 300, 416)])
+@pytest.mark.parametrize("per", [3, 5, 16, 37])
+def test_prefill_streamk(qd, fmt, M, N, K, per):
+    """Stream-K runs of units shorter and longer than a tile's K-tiles (16,
+    12 and 4 of them here): tiles shared by up to six workgroups, workgroups
+    holding only the middle of one tile, several whole tiles, ragged ends and
+    a K-tile past K.  Repeat calls are bitwise equal; every output is within
+    the bound."""
+    say(f"prefill stream-K {fmt} M={M} N={N} K={K} per={per}")
+    W = synth.quant_weights(fmt, N, K, SEED, tensor_id=66)
+    X = synth.normal_bf16((M, K), SEED, tensor_id=67)
+    Wd, Xd = dev(W), xdev(X)
+    runs = [run_streamk(qd, per, lambda: qd.qgemm_prefill(fmt, Wd, Xd).cpu().numpy()) for _ in range(2)]
+    assert np.array_equal(runs[0].view(np.uint32), runs[1].view(np.uint32))
+    y64, S = oracle.gemm_bf16(fmt, W, X, N, K)
+    assert_bound(f"stream-K {fmt}", runs[0], y64, S)
+
+
+@pytest.mark.parametrize("per,tm", [(7, 4), (3, 2)])
+def test_prefill_ffn_streamk(qd, per, tm):
+    qd.set_gemm_streamk(per)
+    try:
+        check_prefill_ffn(qd, "q4_k", 200, 300, 1536, "silu", f"stream-K {per}", tm=tm)
+    finally:
+        qd.set_gemm_streamk(0)
+
+
 # --------------------------------------------------------- gate/up + act ---
 
 def check_prefill_ffn(qd, fmt, M, N, K, act, tag, cols=None, tm=0, splits=0):
