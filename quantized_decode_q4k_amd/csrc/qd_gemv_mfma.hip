@@ -30,14 +30,18 @@
 //    k < 16 and rows 16..31 only k >= 16 (the other half of A is zero), so
 //    each lane still loads 16 consecutive quant bytes.
 //
-// A workgroup is 4 waves, 128 weight rows, over a K-slice of superunits;
-// the fragments and run records of the next superunit are loaded into
-// registers while the current one is multiplied and written to the other
-// half of a double-buffered LDS area before a barrier.  Each lane loads its
-// weight bytes straight into registers (16-byte loads; Q6_K and Q8_0
-// blocks are 2-byte aligned, which the hardware reads unaligned), a few
-// superunits ahead.  Split-K slices end in the deterministic last-arriver
-// sum of qd_epilogue.h.
+// A workgroup is 4 waves, 128 weight rows, over a K-slice of superunits.
+// While one superunit is multiplied the next one's weight tile (32 rows of
+// the wave, whole 16-byte pieces of each row's contiguous block; Q6_K
+// blocks are 2-byte aligned, which the copies read unaligned) is copied
+// straight into the wave's second LDS tile slot by global_load_lds, and its
+// digit fragments and run records into the second digit buffer the same
+// way (or, where only one digit buffer fits beside two resident
+// workgroups, into registers, stored after the multiply); every copy has
+// landed at the end of the iteration (vmcnt 0, then a barrier).  No weight
+// byte passes through vector registers before the B-layout read out of
+// LDS, which keeps a wave at about 110 registers.  Split-K slices end in
+// the deterministic last-arriver sum of qd_epilogue.h.
 #include <type_traits>
 
 #include "qd_digits.h"
@@ -241,7 +245,7 @@ QD_DEV uint32_t ld16(const uint8_t *p) { return *reinterpret_cast<const uint16_t
 template <int FMT>
 struct MqGeo;
 template <> struct MqGeo<kQ4K> { static constexpr int UB = 144, NPC = 9, PITCH = 144; };
-template <> struct MqGeo<kQ6K> { static constexpr int UB = 210, NPC = 14, PITCH = 240; };
+template <> struct MqGeo<kQ6K> { static constexpr int UB = 210, NPC = 14, PITCH = 224; };
 template <> struct MqGeo<kQ80> { static constexpr int UB = 272, NPC = 17, PITCH = 272; };
 template <int FMT>
 QD_DEV constexpr int piece_src(int q) { return (FMT == kQ6K && q == 13) ? 194 : 16 * q; }
@@ -249,28 +253,31 @@ template <int FMT>
 QD_DEV constexpr int piece_dst(int q) { return 16 * q; }
 template <int FMT>
 __host__ __device__ constexpr int mq_ni() { return (32 * MqGeo<FMT>::NPC + 63) / 64; }
+// A wave's weight tile: 32 rows of PITCH = 16 NPC bytes, piece p of the
+// tile (row p / NPC, piece p % NPC) at byte 16 p, so that one LDS copy of
+// the 64 lanes fills 1 KB contiguously.  Two per wave: the next superunit's
+// tile is copied in while the current one is read.
 template <int FMT>
 __host__ __device__ constexpr int mq_slot() { return 32 * MqGeo<FMT>::PITCH; }
-// Digit buffers in LDS: two (the next superunit's are written while the
-// current one is read) where they fit beside the tiles, else one.
+static_assert(MqGeo<kQ4K>::PITCH == 16 * MqGeo<kQ4K>::NPC && MqGeo<kQ6K>::PITCH == 16 * MqGeo<kQ6K>::NPC &&
+                  MqGeo<kQ80>::PITCH == 16 * MqGeo<kQ80>::NPC,
+              "tiles are filled 16 bytes per piece");
+// Digit buffers in LDS: two (the next superunit's are copied in while the
+// current one is read) where two workgroups still fit on a CU with them, or
+// where not even one buffer lets two fit; else one (two workgroups per CU
+// with one buffer measured faster than one with two: lm_head Q8_0 at batch
+// 8, 193 -> 157 us).
 template <int FMT, int NG>
 __host__ __device__ constexpr int mq_nbuf() {
-    return 2 * NG * mq_su_bytes(FMT == kQ4K ? 128 : 32) + 16 + 4 * mq_slot<FMT>() <= 160 * 1024 ? 2 : 1;
+    constexpr int buf = NG * mq_su_bytes(FMT == kQ4K ? 128 : 32), rest = 16 + 8 * mq_slot<FMT>();
+    constexpr int cu = 160 * 1024;
+    if (2 * (2 * buf + rest) <= cu) return 2;
+    if (2 * (buf + rest) <= cu) return 1;
+    return 2 * buf + rest <= cu ? 2 : 1;
 }
 template <int FMT, int NG>
 __host__ __device__ constexpr int mq_lds() {
-    return mq_nbuf<FMT, NG>() * NG * mq_su_bytes(FMT == kQ4K ? 128 : 32) + 16 + 4 * mq_slot<FMT>();
-}
-template <int FMT>
-struct MqR {
-    u32x4 v[mq_ni<FMT>()];
-};
-
-// Superunits whose loads are in flight while one is multiplied.
-template <int FMT, int NG>
-constexpr int mq_lookahead() {
-    if (NG >= 4) return 1;
-    return FMT == kQ80 ? 1 : 2;
+    return mq_nbuf<FMT, NG>() * NG * mq_su_bytes(FMT == kQ4K ? 128 : 32) + 16 + 8 * mq_slot<FMT>();
 }
 
 // This lane's bytes of the tile in the B layout (row l % 32, half h = l / 32),
@@ -386,19 +393,34 @@ __global__ __launch_bounds__(256) void mq_kernel(MqArgs a) {
     const int64_t rowc = row_ok ? row : N - 1;
     (void)rowc;
 
-    // ---- staging: superunit t's fragments and records of every group
-    u32x4 stg[SV];
-    auto stage_load = [&](int t) { mq_stage_load<SV, BUF, GB>(stg, a.dig, a.nb, t, tid); };
-    auto stage_store = [&](int bi) { mq_stage_store<SV, BUF>(lds + bi * BUF, stg, tid); };
+    // ---- digits of superunit t (every group) into a digit buffer: by LDS
+    // copies where there are two buffers, else through registers (loaded
+    // before the current superunit is multiplied, stored after)
+    constexpr int NBUF = mq_nbuf<FMT, NG>();
+    u32x4 stg[NBUF == 1 ? SV : 1];
+    auto stage_load = [&](int t) {
+        if constexpr (NBUF == 1) mq_stage_load<SV, BUF, GB>(stg, a.dig, a.nb, t, tid);
+    };
+    auto stage_store = [&](int bi) {
+        if constexpr (NBUF == 1) mq_stage_store<SV, BUF>(lds + bi * BUF, stg, tid);
+    };
+    auto stage_copy = [&](int t, int bi) {  // thread tid copies pieces tid + 256 v
+#pragma unroll
+        for (int v = 0; v < SV; v++) {
+            const int e = tid + 256 * v;
+            if (v == SV - 1 && 256 * v + 64 * wave >= BUF / 16) break;  // no piece of this wave
+            const int ec = min(e, BUF / 16 - 1);
+            const int g = ec / (GB / 16), o = ec - g * (GB / 16);
+            if (e < BUF / 16)
+                lds_copy16(a.dig + ((int64_t)g * a.nb + t) * GB + 16 * o,
+                           lds_addr(lds + bi * BUF + 16 * (256 * v + 64 * wave)));
+        }
+    };
 
-    // ---- weight loads, D superunits ahead (ring of D + 1): lane piece p =
-    // 64 i + lane of instruction i is piece p % NPC of the wave's row p / NPC
-    constexpr int D = mq_lookahead<FMT, NG>();
+    // ---- weight tiles by LDS copies, one superunit ahead: lane piece p =
+    // 64 i + lane of copy i is piece p % NPC of the wave's row p / NPC
     constexpr int NI = mq_ni<FMT>(), NPC = MqGeo<FMT>::NPC, UB = MqGeo<FMT>::UB;
-    constexpr int PITCH = MqGeo<FMT>::PITCH;
-    MqR<FMT> wb[D + 1];
     uint32_t voff[NI];
-    int lpos[NI];
     bool pv[NI];
     {
         const int64_t row0w = (int64_t)bx * TILE + (FFN ? (wave & 1) : wave) * 32;
@@ -409,32 +431,23 @@ __global__ __launch_bounds__(256) void mq_kernel(MqArgs a) {
             pv[i] = p < 32 * NPC;
             const int64_t rr = min(row0w + r, N - 1);
             voff[i] = (uint32_t)(rr * a.row_bytes + piece_src<FMT>(q));
-            lpos[i] = r * PITCH + piece_dst<FMT>(q);
         }
     }
     const uint8_t *wbase = mi ? a.W1 : a.W0;
-    auto wload = [&](MqR<FMT> &dst, int t) {
-        t = min(t, t_end - 1);  // past the slice: a repeat of its last superunit, unused
-        const uint8_t *base = wbase + (int64_t)UB * t;
-#pragma unroll
-        for (int i = 0; i < NI; i++) {
-            if (i < NI - 1 || pv[i]) {
-                const u4_a2 v = *reinterpret_cast<const u4_a2 *>(base + voff[i]);
-                dst.v[i] = u32x4{v.x, v.y, v.z, v.w};
-            }
-        }
-    };
-    constexpr int NBUF = mq_nbuf<FMT, NG>();
-    uint8_t *scr = lds + NBUF * BUF + 16 + wave * mq_slot<FMT>();
-    // the tile to the wave's LDS area, then back in the B layout (LDS
-    // accesses of one wave complete in order; the wait orders the lanes'
-    // writes before any lane's read)
-    auto untile = [&](const MqR<FMT> &src, MqW<FMT> &w) {
+    uint8_t *scr = lds + NBUF * BUF + 16 + wave * 2 * mq_slot<FMT>();  // [2][32 rows][PITCH]
+    auto wcopy = [&](int t, int sl) {
+        t = min(t, t_end - 1);
+        // the copy's base address and LDS destination in scalar registers
+        const uint64_t b64 = reinterpret_cast<uint64_t>(wbase + (int64_t)UB * t);
+        // (readfirstlane returns int: widen through uint32_t, not by sign)
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b64);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32));
+        const uint64_t bu = ((uint64_t)hi << 32) | (uint64_t)lo;
+        const uint8_t *base = reinterpret_cast<const uint8_t *>(bu);
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(scr + sl * mq_slot<FMT>()));
 #pragma unroll
         for (int i = 0; i < NI; i++)
-            if (i < NI - 1 || pv[i]) *reinterpret_cast<u32x4 *>(scr + lpos[i]) = src.v[i];
-        lgkm_wait();
-        mq_read_tile<FMT>(w, scr, lane & 31, h);
+            if (i < NI - 1 || pv[i]) lds_copy16_s(base, voff[i], dst + 1024 * i);
     };
 
     Acc acc[NR][NG][4];
@@ -546,9 +559,9 @@ __global__ __launch_bounds__(256) void mq_kernel(MqArgs a) {
             }
         }
     };
-    auto compute = [&](const MqR<FMT> &wr, const uint8_t *buf) {
+    auto compute = [&](const uint8_t *tile, const uint8_t *buf) {
         MqW<FMT> wv;
-        untile(wr, wv);
+        mq_read_tile<FMT>(wv, tile, lane & 31, h);
         if constexpr (NG >= 4) {
             compute_wide(wv, buf);
         } else if constexpr (FMT == kQ4K) {
@@ -688,28 +701,34 @@ __global__ __launch_bounds__(256) void mq_kernel(MqArgs a) {
     // ---- main loop: superunit t multiplied from LDS half (t - t_beg) & 1
     // while superunit t + 1's fragments are loaded for the other half
     if (FMT == kQ6K && tid == 0) *reinterpret_cast<uint4 *>(const_cast<uint8_t *>(zero16)) = make_uint4(0u, 0u, 0u, 0u);
+    // ---- main loop: superunit t multiplied out of tile slot (t - t_beg) & 1
+    // and digit buffer (t - t_beg) & 1 (or the one buffer) while superunit
+    // t + 1's tile and digits are copied into the other ones; every copy of
+    // an iteration has landed at its end (vmcnt 0, then the barrier makes the
+    // digits of every wave visible)
     if (t_beg < t_end) {
-        stage_load(t_beg);
-#pragma unroll
-        for (int d = 0; d < D; d++) wload(wb[d], t_beg + d);
+        wcopy(t_beg, 0);
+        if constexpr (NBUF == 2) stage_copy(t_beg, 0);
+        else stage_load(t_beg);
         stage_store(0);
+        vm_wait<0>();
         block_sync();
-        for (int t0 = t_beg; t0 < t_end; t0 += D + 1) {
-#pragma unroll
-            for (int s = 0; s <= D; s++) {
-                const int t = t0 + s;
-                if (t >= t_end) break;
-                const int bi = NBUF == 2 ? (t - t_beg) & 1 : 0;
-                const bool more = t + 1 < t_end;
-                if (more) stage_load(t + 1);
-                wload(wb[(s + D) % (D + 1)], t + D);
-                compute(wb[s], lds + bi * BUF);
-                if (more) {
-                    if (NBUF == 1) block_sync();  // every wave is done with the buffer
-                    stage_store(NBUF == 2 ? bi ^ 1 : 0);
-                }
-                block_sync();
+        for (int t = t_beg; t < t_end; t++) {
+            const int sl = (t - t_beg) & 1;
+            const int bi = NBUF == 2 ? sl : 0;
+            const bool more = t + 1 < t_end;
+            if (more) {
+                wcopy(t + 1, sl ^ 1);
+                if constexpr (NBUF == 2) stage_copy(t + 1, bi ^ 1);
+                else stage_load(t + 1);
             }
+            compute(scr + sl * mq_slot<FMT>(), lds + bi * BUF);
+            if (more && NBUF == 1) {
+                block_sync();  // every wave is done with the buffer
+                stage_store(0);
+            }
+            vm_wait<0>();
+            block_sync();
         }
     }
 
