@@ -306,10 +306,14 @@ MqPlan mq_plan(int fmt, int64_t N, int64_t K, int batch, bool ffn) {
     const int nb = (int)((K + qd::kSuper - 1) / qd::kSuper);
     p.nb = nb;
     p.tiles = (N + qd::mq_tile_rows(ffn) - 1) / qd::mq_tile_rows(ffn);
-    // K-slices: the fewest superunits on the busiest slot, counting the
-    // rounds of workgroups the resident slots take (the fewest slices among
-    // equals: less split-K traffic)
-    const int64_t slots = (int64_t)cu_count() * qd::mq_wg_per_cu(fmt, p.ng, ffn);
+    // K-slices: the least work on the busiest CU.  A CU given w workgroups
+    // of nk superunits runs them about two at a time, or one where only one
+    // is resident (a third resident one adds little: Gemma-4-31B down at
+    // batch 8, 42 tiles x 84 superunits, 12 slices = 2 workgroups on every CU
+    // 42 us, 14 slices = 2 or 3 47 us), so it takes w (nk + 2) / min(w, c);
+    // the fewest slices among equals (less split-K traffic)
+    const int64_t cus = cu_count();
+    const int64_t conc = std::min(2, qd::mq_wg_per_cu(fmt, p.ng, ffn));
     int64_t best = INT64_MAX;
     for (int po = 1; po <= nb; po++) {
         if (po > 1 && p.tiles > kMaxTiles) break;  // a counter per row tile
@@ -319,7 +323,9 @@ MqPlan mq_plan(int fmt, int64_t N, int64_t K, int batch, bool ffn) {
         // a workgroup's start (digits, first loads) costs about two
         // superunits; the last workgroup of a tile reads its slices' partial
         // sums about 8 at a time, each batch about one superunit
-        const int64_t cost = (p.tiles * pp + slots - 1) / slots * (nk + 2) + (pp > 1 ? (pp + 7) / 8 : 0);
+        const int64_t w = (p.tiles * pp + cus - 1) / cus;
+        const int64_t c = std::max<int64_t>(1, std::min(w, conc));
+        const int64_t cost = (2 * w * (nk + 2) + c - 1) / c + 2 * (pp > 1 ? (pp + 7) / 8 : 0);
         if (cost < best) {
             best = cost;
             p.nk = nk;

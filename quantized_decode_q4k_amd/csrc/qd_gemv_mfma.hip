@@ -255,8 +255,9 @@ template <int FMT>
 __host__ __device__ constexpr int mq_ni() { return (32 * MqGeo<FMT>::NPC + 63) / 64; }
 // A wave's weight tile: 32 rows of PITCH = 16 NPC bytes, piece p of the
 // tile (row p / NPC, piece p % NPC) at byte 16 p, so that one LDS copy of
-// the 64 lanes fills 1 KB contiguously.  Two per wave: the next superunit's
-// tile is copied in while the current one is read.
+// the 64 lanes fills 1 KB contiguously.  One per wave: the wave reads its
+// whole tile into registers before it multiplies, and the next superunit's
+// tile is copied into the same slot from then on.
 template <int FMT>
 __host__ __device__ constexpr int mq_slot() { return 32 * MqGeo<FMT>::PITCH; }
 static_assert(MqGeo<kQ4K>::PITCH == 16 * MqGeo<kQ4K>::NPC && MqGeo<kQ6K>::PITCH == 16 * MqGeo<kQ6K>::NPC &&
@@ -269,7 +270,7 @@ static_assert(MqGeo<kQ4K>::PITCH == 16 * MqGeo<kQ4K>::NPC && MqGeo<kQ6K>::PITCH 
 // 8, 193 -> 157 us).
 template <int FMT, int NG>
 __host__ __device__ constexpr int mq_nbuf() {
-    constexpr int buf = NG * mq_su_bytes(FMT == kQ4K ? 128 : 32), rest = 16 + 8 * mq_slot<FMT>();
+    constexpr int buf = NG * mq_su_bytes(FMT == kQ4K ? 128 : 32), rest = 16 + 4 * mq_slot<FMT>();
     constexpr int cu = 160 * 1024;
     if (2 * (2 * buf + rest) <= cu) return 2;
     if (2 * (buf + rest) <= cu) return 1;
@@ -277,7 +278,7 @@ __host__ __device__ constexpr int mq_nbuf() {
 }
 template <int FMT, int NG>
 __host__ __device__ constexpr int mq_lds() {
-    return mq_nbuf<FMT, NG>() * NG * mq_su_bytes(FMT == kQ4K ? 128 : 32) + 16 + 8 * mq_slot<FMT>();
+    return mq_nbuf<FMT, NG>() * NG * mq_su_bytes(FMT == kQ4K ? 128 : 32) + 16 + 4 * mq_slot<FMT>();
 }
 
 // This lane's bytes of the tile in the B layout (row l % 32, half h = l / 32),
@@ -434,8 +435,8 @@ __global__ __launch_bounds__(256) void mq_kernel(MqArgs a) {
         }
     }
     const uint8_t *wbase = mi ? a.W1 : a.W0;
-    uint8_t *scr = lds + NBUF * BUF + 16 + wave * 2 * mq_slot<FMT>();  // [2][32 rows][PITCH]
-    auto wcopy = [&](int t, int sl) {
+    uint8_t *scr = lds + NBUF * BUF + 16 + wave * mq_slot<FMT>();  // [32 rows][PITCH]
+    auto wcopy = [&](int t) {
         t = min(t, t_end - 1);
         // the copy's base address and LDS destination in scalar registers
         const uint64_t b64 = reinterpret_cast<uint64_t>(wbase + (int64_t)UB * t);
@@ -444,7 +445,7 @@ __global__ __launch_bounds__(256) void mq_kernel(MqArgs a) {
         const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32));
         const uint64_t bu = ((uint64_t)hi << 32) | (uint64_t)lo;
         const uint8_t *base = reinterpret_cast<const uint8_t *>(bu);
-        const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(scr + sl * mq_slot<FMT>()));
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(scr));
 #pragma unroll
         for (int i = 0; i < NI; i++)
             if (i < NI - 1 || pv[i]) lds_copy16_s(base, voff[i], dst + 1024 * i);
@@ -559,9 +560,7 @@ __global__ __launch_bounds__(256) void mq_kernel(MqArgs a) {
             }
         }
     };
-    auto compute = [&](const uint8_t *tile, const uint8_t *buf) {
-        MqW<FMT> wv;
-        mq_read_tile<FMT>(wv, tile, lane & 31, h);
+    auto compute = [&](const MqW<FMT> &wv, const uint8_t *buf) {
         if constexpr (NG >= 4) {
             compute_wide(wv, buf);
         } else if constexpr (FMT == kQ4K) {
@@ -701,28 +700,31 @@ __global__ __launch_bounds__(256) void mq_kernel(MqArgs a) {
     // ---- main loop: superunit t multiplied from LDS half (t - t_beg) & 1
     // while superunit t + 1's fragments are loaded for the other half
     if (FMT == kQ6K && tid == 0) *reinterpret_cast<uint4 *>(const_cast<uint8_t *>(zero16)) = make_uint4(0u, 0u, 0u, 0u);
-    // ---- main loop: superunit t multiplied out of tile slot (t - t_beg) & 1
-    // and digit buffer (t - t_beg) & 1 (or the one buffer) while superunit
-    // t + 1's tile and digits are copied into the other ones; every copy of
-    // an iteration has landed at its end (vmcnt 0, then the barrier makes the
-    // digits of every wave visible)
+    // ---- main loop: superunit t's tile read out of the wave's slot into
+    // registers, then superunit t + 1's tile copied into the slot and its
+    // digits into the other digit buffer (or loaded into registers, where
+    // there is one buffer) while t is multiplied; every copy of an iteration
+    // has landed at its end (vmcnt 0, then the barrier makes the digits of
+    // every wave visible)
     if (t_beg < t_end) {
-        wcopy(t_beg, 0);
+        wcopy(t_beg);
         if constexpr (NBUF == 2) stage_copy(t_beg, 0);
         else stage_load(t_beg);
         stage_store(0);
         vm_wait<0>();
         block_sync();
         for (int t = t_beg; t < t_end; t++) {
-            const int sl = (t - t_beg) & 1;
-            const int bi = NBUF == 2 ? sl : 0;
+            const int bi = NBUF == 2 ? (t - t_beg) & 1 : 0;
             const bool more = t + 1 < t_end;
+            MqW<FMT> wv;
+            mq_read_tile<FMT>(wv, scr, lane & 31, h);
+            lgkm_wait();  // the tile is in registers: the slot may be refilled
             if (more) {
-                wcopy(t + 1, sl ^ 1);
+                wcopy(t + 1);
                 if constexpr (NBUF == 2) stage_copy(t + 1, bi ^ 1);
                 else stage_load(t + 1);
             }
-            compute(scr + sl * mq_slot<FMT>(), lds + bi * BUF);
+            compute(wv, lds + bi * BUF);
             if (more && NBUF == 1) {
                 block_sync();  // every wave is done with the buffer
                 stage_store(0);
