@@ -368,10 +368,12 @@ std::atomic<int> g_stream_wpc{0}, g_stream_depth{0}, g_stream_consumers{0}, g_st
 constexpr int64_t kStreamMinK = 8192;       // automatic use of the streaming kernel
 constexpr int64_t kStreamMinRowsTall = 65536;  // ... and for tall Q6_K / Q8_0 matrices at batch 1
 
+// n_sel > 1: the routed slots of a MoE launch share the CUs, each slot
+// taking G workgroups (at least one) over its own matrix.
 void stream_rows(int64_t N, int64_t K, int fmt, int wpc, const float *norm_w, qd::StreamArgs *a,
-                 unsigned *grid) {
+                 unsigned *grid, int n_sel = 1) {
     const int64_t rb = row_bytes(fmt, K);
-    const int G = (int)std::min<int64_t>(N, (int64_t)kCUs * wpc);
+    const int G = (int)std::min<int64_t>(N, std::max<int64_t>(1, (int64_t)kCUs * wpc / n_sel));
     a->N = N;
     a->K = K;
     a->row_bytes = rb;
@@ -381,7 +383,8 @@ void stream_rows(int64_t N, int64_t K, int fmt, int wpc, const float *norm_w, qd
     a->rows_extra = (int)(N % G);
     a->units_max = (a->rows_base + (a->rows_extra > 0 ? 1 : 0)) * a->nb;
     a->norm_w = norm_w;
-    *grid = (unsigned)G;
+    a->wps = G;
+    *grid = (unsigned)(G * n_sel);
 }
 
 // Producer / consumer kernel: as many ring slots as the LDS share holds (a
@@ -391,8 +394,8 @@ void stream_rows(int64_t N, int64_t K, int fmt, int wpc, const float *norm_w, qd
 // copying wave for a free slot finite.  False if it does not fit.
 bool stream_plan_pc(int fmt, bool ffn, int64_t N, int64_t K, int batch, const float *norm_w,
                     int wpc, int consumers, int producers, int lag_default, qd::StreamArgs *a,
-                    unsigned *grid, size_t *lds) {
-    stream_rows(N, K, fmt, wpc, norm_w, a, grid);
+                    unsigned *grid, size_t *lds, int n_sel = 1) {
+    stream_rows(N, K, fmt, wpc, norm_w, a, grid, n_sel);
     a->consumers = consumers;
     a->producers = producers;
     const size_t budget = kLdsPerCU / wpc;
@@ -471,6 +474,22 @@ bool stream_plan(int fmt, bool ffn, int64_t N, int64_t K, int batch, const float
         a->slots * 16 >= a->units_max)
         return true;
     return stream_plan_pc(fmt, ffn, N, K, batch, norm_w, 2, 4, 2, kPcLag, a, grid, lds);
+}
+
+// The routed experts of the MoE decode FFN on the producer / consumer kernel
+// (batch 1): the slots split the CUs, each slot's workgroups a contiguous
+// row range of its expert's matrix, with the batch-1 settings of the plain
+// launches.  False where the register kernel is used instead (rows not of
+// whole 256-weight superunits, an expert matrix not a multiple of 16 bytes,
+// an LDS layout that does not fit).
+bool stream_plan_moe(int fmt, bool ffn, int64_t N, int64_t K, int n_sel, const float *norm_w,
+                     qd::StreamArgs *a, unsigned *grid, size_t *lds) {
+    if (K % qd::kSuper != 0) return false;
+    if ((N * row_bytes(fmt, K)) % 16 != 0) return false;
+    const int64_t G = std::min<int64_t>(N, std::max<int64_t>(1, kCUs / n_sel));
+    const int64_t wg_bytes = (N + G - 1) / G * row_bytes(fmt, K) * (ffn ? 2 : 1);
+    const int prod = wg_bytes >= (int64_t(256) << 10) ? 4 : 2;
+    return stream_plan_pc(fmt, ffn, N, K, 1, norm_w, 1, 8, prod, 4, a, grid, lds, n_sel);
 }
 
 // Row epilogue arguments of a plain GEMV (post-norm, residual, next norm).
@@ -1014,16 +1033,55 @@ qd_status run_moe(int fmt_gu, const void *Wg, const void *Wu, int fmt_d, const v
         if (overlap(y, ybytes, ins[i], insz[i]) || (h_out && overlap(h_out, hbytes, ins[i], insz[i])))
             return QD_EINVAL;
     if (h_out && overlap(y, ybytes, h_out, hbytes)) return QD_EINVAL;
-    // every slot stages its whole activation row in one workgroup
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    const size_t h_floats = h_out ? 0 : (((size_t)n_sel * N_ff + 63) / 64) * 64;
+    if (!launch_forced()) {
+        qd::StreamArgs sa{}, sb{};
+        unsigned ga = 0, gb = 0;
+        size_t la = 0, lb = 0;
+        if (stream_plan_moe(fmt_gu, true, N_ff, K, n_sel, norm_w, &sa, &ga, &la) &&
+            stream_plan_moe(fmt_d, false, K, N_ff, n_sel, nullptr, &sb, &gb, &lb)) {
+            Workspace w;
+            st = get_workspace(hs, h_floats + (size_t)n_sel * K, &w);
+            if (st != QD_OK) return st;
+            float *h = h_out ? h_out : w.partials;
+            sa.W0 = static_cast<const uint8_t *>(Wg);
+            sa.W1 = static_cast<const uint8_t *>(Wu);
+            sa.x = x;
+            sa.y = h;
+            sa.act = act;
+            sa.eps = eps;
+            sa.ids = ids;
+            sa.n_experts = n_experts;
+            sa.n_sel = n_sel;
+            sa.w_estride = N_ff * rb_a;
+            sa.y_sstride = N_ff;
+            hipError_t e = qd::launch_stream_moe(fmt_gu, true, sa, ga, la, hs);
+            if (e != hipSuccess) return QD_ELAUNCH;
+            sb.W0 = static_cast<const uint8_t *>(Wd);
+            sb.x = h;
+            sb.y = y;
+            sb.ids = ids;
+            sb.coef = coef;
+            sb.n_experts = n_experts;
+            sb.n_sel = n_sel;
+            sb.w_estride = K * rb_b;
+            sb.x_sstride = N_ff;
+            sb.part = w.partials + h_floats;
+            sb.counters = w.counters;
+            e = qd::launch_stream_moe(fmt_d, false, sb, gb, lb, hs);
+            return e == hipSuccess ? QD_OK : QD_ELAUNCH;
+        }
+    }
+
+    // register kernel: every slot stages its whole activation row in one
+    // workgroup
     const int nb_a = (int)((K + qd::kSuper - 1) / qd::kSuper);
     const int nb_b = (int)((N_ff + qd::kSuper - 1) / qd::kSuper);
     if (nb_a > lds_units_max(fmt_gu, 1) || nb_b > lds_units_max(fmt_d, 1)) return QD_EUNSUPPORTED;
-
-    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     const Plan pa = make_plan(fmt_gu, N_ff, K, 1, true, Shape{moe_p_in(N_ff, n_sel), 1, 1, 1});
     const Plan pb = make_plan(fmt_d, K, N_ff, 1, false, Shape{moe_p_in(K, n_sel), 1, 1, 1});
     if (pb.tiles > kMaxTiles) return QD_EUNSUPPORTED;
-    const size_t h_floats = h_out ? 0 : (((size_t)n_sel * N_ff + 63) / 64) * 64;
     Workspace w;
     st = get_workspace(hs, h_floats + (size_t)n_sel * K, &w);
     if (st != QD_OK) return st;

@@ -174,8 +174,12 @@ QD_DEV void dot_step(const StepRegs<FMT, NR> &st, const uint8_t *xd, int xsb, co
 //     (the digits stay), stores the number of its steps read so far in
 //     done[c];
 //   * waves NC .. NC + 3 copy the weights (producers; as many as the launch
-//     asks for, 1, 2 or 4, and the others idle).  They issue nothing before x has landed, so
-//     x does not queue behind the weight stream.  Producer p takes the
+//     asks for, 1, 2 or 4, and the others idle).  Where x holds more than
+//     kXFirstSlices slices they issue nothing before it has landed, so x
+//     does not queue behind the weight stream (MI355X, graph replay: the
+//     Gemma-3 down's 40 KB of h lands 0.9 us later without the wait); a
+//     shorter x goes out alongside the first weights (the Gemma-3 gate/up,
+//     10 slices: 10.55 -> 10.28 us with no wait).  Producer p takes the
 //     steps j = p (mod producers), each into ring slot j % slots, keeping up
 //     to `lag` of its steps in flight; once one of its steps has landed (its
 //     own vmcnt) it stores the step number in ready[slot].
@@ -188,8 +192,20 @@ QD_DEV void dot_step(const StepRegs<FMT, NR> &st, const uint8_t *xd, int xsb, co
 // applied to each row's sum at the end (every product is linear in the
 // staged activations).
 constexpr int kPcMaxProducers = 4;
+constexpr int kXFirstSlices = 16;  // longer staged x: the copying waves wait for it
 
-template <int FMT, int B, int NR, bool FFN, int NC>
+//
+// Mixture-of-experts slots (MOE): the launch holds n_sel * wps workgroups,
+// workgroup i serving routed slot z = i / wps with row range i % wps of that
+// slot's expert e = ids[z] (an id outside [0, n_experts) streams expert 0
+// and its result is dropped).  The copying waves read the id while x lands.
+//   * gate/up (FFN): x is shared by the slots; slot z writes h_z at
+//     y + z * y_sstride (zeros for an invalid id);
+//   * down: slot z reads h_z at x + z * x_sstride and stores its rows into
+//     part[z]; the last of the n_sel workgroups of a row range (counter per
+//     range) forms y = sum of coef[z] * part[z] over the valid slots, in slot
+//     order, and returns the counter to zero.
+template <int FMT, int B, int NR, bool FFN, int NC, bool MOE>
 __global__ __launch_bounds__(64 * (NC + kPcMaxProducers)) void stream_pc_kernel(StreamArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr int UB = StreamFmt<FMT>::UB;
@@ -208,7 +224,14 @@ __global__ __launch_bounds__(64 * (NC + kPcMaxProducers)) void stream_pc_kernel(
     const int R = a.slots;
     const int NP = a.producers;
 
-    const int wg = blockIdx.x;
+    int wg = blockIdx.x;
+    int z = 0;                 // routed slot (MOE)
+    const float *xin = a.x;
+    if constexpr (MOE) {
+        z = wg / a.wps;
+        wg -= z * a.wps;
+        if constexpr (!FFN) xin += (int64_t)z * a.x_sstride;
+    }
     const int64_t r0 = (int64_t)wg * a.rows_base + min(wg, a.rows_extra);
     const int cnt = a.rows_base + (wg < a.rows_extra ? 1 : 0);
     const int U = cnt * nb;
@@ -236,7 +259,14 @@ __global__ __launch_bounds__(64 * (NC + kPcMaxProducers)) void stream_pc_kernel(
         const int p = wv - NC;
         if (p < NP) {
             __builtin_amdgcn_s_setprio(3);
-            lds_wait_eq(landed, NC);
+            const uint8_t *W0 = a.W0, *W1 = a.W1;
+            if constexpr (MOE) {
+                int e = a.ids[z];
+                e = (e >= 0 && e < a.n_experts) ? e : 0;
+                W0 += (int64_t)e * a.w_estride;
+                if constexpr (FFN) W1 += (int64_t)e * a.w_estride;
+            }
+            if (B * nb > kXFirstSlices) lds_wait_eq(landed, NC);
             // weight steps j = p + NP * k
             constexpr int SB = kStepUnits * UB;  // bytes per step and matrix
             const int64_t base = wbeg & ~(int64_t)15;
@@ -269,7 +299,7 @@ __global__ __launch_bounds__(64 * (NC + kPcMaxProducers)) void stream_pc_kernel(
                     if (a0 <= safe) {
 #pragma unroll
                         for (int m = 0; m < NR; m++) {
-                            const uint8_t *sp = (m == 0 ? a.W0 : a.W1) + a0;
+                            const uint8_t *sp = (m == 0 ? W0 : W1) + a0;
 #pragma unroll
                             for (int q = 0; q < NI; q++)
                                 if (q < NI - 1 || tail_lane)
@@ -285,7 +315,7 @@ __global__ __launch_bounds__(64 * (NC + kPcMaxProducers)) void stream_pc_kernel(
                             for (int q = 0; q < NI; q++) {
                                 const int64_t off = min(a0 + 16 * (int64_t)(64 * q + lane), last16);
                                 if (q < NI - 1 || tail_lane)
-                                    lds_copy16((m == 0 ? a.W0 : a.W1) + off, dst + m * SLOTM + 1024 * q);
+                                    lds_copy16((m == 0 ? W0 : W1) + off, dst + m * SLOTM + 1024 * q);
                             }
                     }
                     k++;
@@ -323,7 +353,7 @@ __global__ __launch_bounds__(64 * (NC + kPcMaxProducers)) void stream_pc_kernel(
                 if (it < nslices) {  // uniform per wave
                     const int b = it / nb;
                     const int64_t k = (int64_t)(it - b * nb) * kSuper + 4 * lane;
-                    xv[i] = *reinterpret_cast<const float4 *>(a.x + (int64_t)b * K + k);
+                    xv[i] = *reinterpret_cast<const float4 *>(xin + (int64_t)b * K + k);
                     if (norm) nv[i] = *reinterpret_cast<const float4 *>(a.norm_w + k);
                 }
             }
@@ -426,6 +456,16 @@ __global__ __launch_bounds__(64 * (NC + kPcMaxProducers)) void stream_pc_kernel(
             sr[m] = oct_sum(acc) * rinv[b];
         }
         if (!on || l8 != 0) continue;
+        if constexpr (MOE) {
+            if constexpr (FFN) {
+                const int e = a.ids[z];
+                const bool valid = e >= 0 && e < a.n_experts;
+                a.y[(int64_t)z * a.y_sstride + row] = valid ? act_apply(a.act, sr[0]) * sr[1] : 0.f;
+            } else {
+                xstore(a.part + (int64_t)z * N + row, sr[0]);
+            }
+            continue;
+        }
         if constexpr (FFN) {
             a.y[(int64_t)b * N + row] = act_apply(a.act, sr[0]) * sr[1];
             if (a.g_out) a.g_out[(int64_t)b * N + row] = sr[0];
@@ -436,7 +476,30 @@ __global__ __launch_bounds__(64 * (NC + kPcMaxProducers)) void stream_pc_kernel(
             else a.y[o] = a.res ? sr[0] + a.res[o] : sr[0];
         }
     }
-    if constexpr (!FFN) {
+    if constexpr (MOE && !FFN) {
+        // the slots' rows of this range: the last of the n_sel workgroups
+        // sums them (the ring, offset 0, is free once every step is decoded)
+        if (!arrive_last<NT>(a.counters + wg, (unsigned)a.n_sel, reinterpret_cast<int *>(smem))) return;
+        for (int lr = tid; lr < cnt; lr += NT) {
+            const int64_t row = r0 + lr;
+            float s = 0.f;
+            for (int z0 = 0; z0 < a.n_sel; z0 += 8) {
+                float v[8];  // eight slots' loads in flight together
+#pragma unroll
+                for (int i = 0; i < 8; i++)
+                    v[i] = z0 + i < a.n_sel ? xload(a.part + (int64_t)(z0 + i) * N + row) : 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; i++) {
+                    const int zz = z0 + i;
+                    if (zz >= a.n_sel) break;
+                    const int e = a.ids[zz];
+                    if (e >= 0 && e < a.n_experts) s = fmaf(a.coef[zz], v[i], s);
+                }
+            }
+            a.y[row] = s;
+        }
+        if (tid == 0) __hip_atomic_store(a.counters + wg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else if constexpr (!FFN) {
         // the ring (offset 0) is free once every step has been decoded
         if (a.pn.w1)
             post_norm_tail<NT>(a.pn, a.y, B, N, reinterpret_cast<float *>(smem), reinterpret_cast<int *>(smem + 64));
@@ -481,12 +544,12 @@ static hipError_t allow_lds() {
     return e;
 }
 
-template <int FMT, int B, bool FFN, int NC>
+template <int FMT, int B, bool FFN, int NC, bool MOE = false>
 static hipError_t launch_pc(const StreamArgs &a, unsigned grid, size_t lds, hipStream_t st) {
     constexpr int NR = FFN ? 2 : 1;
-    if (allow_lds<stream_pc_kernel<FMT, B, NR, FFN, NC>>() != hipSuccess) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((stream_pc_kernel<FMT, B, NR, FFN, NC>), dim3(grid), dim3(64 * (NC + kPcMaxProducers)), lds,
-                       st, a);
+    if (allow_lds<stream_pc_kernel<FMT, B, NR, FFN, NC, MOE>>() != hipSuccess) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((stream_pc_kernel<FMT, B, NR, FFN, NC, MOE>), dim3(grid), dim3(64 * (NC + kPcMaxProducers)),
+                       lds, st, a);
     return hipGetLastError();
 }
 
@@ -515,6 +578,19 @@ hipError_t launch_stream(int fmt, int batch, bool ffn, const StreamArgs &a, unsi
     case kQ4K: return launch_sf<kQ4K>(a, batch, ffn, grid, lds, st);
     case kQ6K: return launch_sf<kQ6K>(a, batch, ffn, grid, lds, st);
     case kQ80: return launch_sf<kQ80>(a, batch, ffn, grid, lds, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// The routed experts' launches of the MoE decode FFN (batch 1, 8 decoding
+// waves).
+hipError_t launch_stream_moe(int fmt, bool ffn, const StreamArgs &a, unsigned grid, size_t lds,
+                             hipStream_t st) {
+    if (a.consumers != 8) return hipErrorInvalidValue;
+    switch (fmt) {
+    case kQ4K: return ffn ? launch_pc<kQ4K, 1, true, 8, true>(a, grid, lds, st) : launch_pc<kQ4K, 1, false, 8, true>(a, grid, lds, st);
+    case kQ6K: return ffn ? launch_pc<kQ6K, 1, true, 8, true>(a, grid, lds, st) : launch_pc<kQ6K, 1, false, 8, true>(a, grid, lds, st);
+    case kQ80: return ffn ? launch_pc<kQ80, 1, true, 8, true>(a, grid, lds, st) : launch_pc<kQ80, 1, false, 8, true>(a, grid, lds, st);
     default: return hipErrorInvalidValue;
     }
 }

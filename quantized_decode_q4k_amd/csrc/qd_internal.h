@@ -136,12 +136,23 @@ struct StreamArgs {
     int act;
     float eps;
     PostNorm pn;            // GEMV row epilogue (pn.w1 = nullptr: none)
+    // routed experts of the MoE decode FFN (launch_stream_moe): n_sel * wps
+    // workgroups, wps per slot; expert e's matrices at W + e * w_estride
+    const int32_t *ids;
+    const float *coef;
+    int n_experts, n_sel, wps;
+    int64_t w_estride;
+    int64_t x_sstride, y_sstride;  // down: h_z at x + z * x_sstride; gate/up: h_z at y + z * y_sstride
+    float *part;                   // down: [n_sel][N] slot rows
+    unsigned *counters;            // down: [wps], zero between launches
 };
 size_t stream_pc_layout(int fmt, int batch, bool ffn, int nb, int units_max, int slots,
                         StreamArgs *a);
 int stream_copies_per_step(int fmt, bool ffn);
 hipError_t launch_stream(int fmt, int batch, bool ffn, const StreamArgs &a, unsigned grid,
                          size_t lds, hipStream_t st);
+hipError_t launch_stream_moe(int fmt, bool ffn, const StreamArgs &a, unsigned grid, size_t lds,
+                             hipStream_t st);
 
 // Batch 3..64 GEMVs on the matrix cores (qd_gemv_mfma.hip).  xdig_kernel
 // writes the activation digits of up to 64 batch rows in groups of 8: per

@@ -9,6 +9,11 @@ id must hold h_z = 0.  Then y must meet
 with y_z, S_z the oracle's down GEMV of expert e over the GPU's own h_z (fp64)
 and the last term the fp32 rounding of the weighted sum.  Repeated calls must
 agree bit for bit (the slots are summed in slot order).
+
+Rows of whole 256-weight superunits take the streaming kernel (the slots
+share the CUs, and the last workgroup of a down row range sums the slots);
+other rows, and any forced launch shape, take the register kernel, which the
+`register_kernel` cases run on shapes the streaming kernel would take.
 """
 import numpy as np
 import pytest
@@ -30,6 +35,14 @@ def qd(gpu):
 
 
 from helpers import dev, h_tolerance, say  # noqa: E402
+
+
+@pytest.fixture
+def register_kernel(qd):
+    """A forced launch shape keeps the MoE launches on the register kernel."""
+    qd.set_launch_override(2, 0, 0)
+    yield
+    qd.set_launch_override(0, 0, 0)
 
 
 def check_moe(qd, fg, fd, hidden, ff, n_experts, ids, coef, act, with_norm=True, tag=""):
@@ -107,3 +120,36 @@ def test_moe_bench_configuration(qd):
     ids = [int(v) for v in rng.choice(128, 8, replace=False)]
     coef = [float(v) for v in rng.dirichlet(np.ones(8))]
     check_moe(qd, "q4_k", "q6_k", 2560, 1024, 128, ids, coef, "gelu_tanh", tag="bench config")
+
+
+def test_moe_three_slots_ragged_ranges(qd):
+    """Three slots: 85 workgroups per slot, row ranges of unequal length."""
+    check_moe(qd, "q4_k", "q6_k", 2560, 1024, 32, [30, 2, 17], [0.5, 0.3, 0.2], "gelu_tanh",
+              tag="3 slots")
+
+
+def test_moe_sixty_four_slots(qd):
+    """The most slots a call takes: four workgroups per slot."""
+    rng = np.random.default_rng(11)
+    ids = [int(v) for v in rng.integers(0, 40, 64)]
+    ids[5] = 40       # out of range: contributes nothing
+    coef = [float(v) for v in rng.uniform(-0.1, 0.2, 64)]
+    check_moe(qd, "q4_k", "q6_k", 1024, 512, 40, ids, coef, "silu", tag="64 slots")
+
+
+def test_moe_partial_superunit_rows(qd):
+    """Q8_0 rows of 800 weights (not whole superunits): the register kernel."""
+    check_moe(qd, "q8_0", "q8_0", 800, 512, 5, [4, 1, 1], [0.6, 0.3, 0.1], "gelu_tanh",
+              tag="K % 256 != 0")
+
+
+def test_moe_register_kernel_bench_configuration(qd, register_kernel):
+    rng = np.random.default_rng(7)
+    ids = [int(v) for v in rng.choice(128, 8, replace=False)]
+    coef = [float(v) for v in rng.dirichlet(np.ones(8))]
+    check_moe(qd, "q4_k", "q6_k", 2560, 1024, 128, ids, coef, "gelu_tanh", tag="register kernel")
+
+
+def test_moe_register_kernel_invalid_id(qd, register_kernel):
+    check_moe(qd, "q8_0", "q8_0", 512, 512, 6, [5, -1, 6, 0], [0.5, 9.0, 7.0, 0.25], "gelu_tanh",
+              tag="register kernel, invalid ids")
