@@ -369,11 +369,13 @@ constexpr int64_t kStreamMinK = 8192;       // automatic use of the streaming ke
 constexpr int64_t kStreamMinRowsTall = 65536;  // ... and for tall Q6_K / Q8_0 matrices at batch 1
 
 // n_sel > 1: the routed slots of a MoE launch share the CUs, each slot
-// taking G workgroups (at least one) over its own matrix.
+// taking G workgroups (at least one) over its own matrix.  g_set > 0: G
+// workgroups (at most N), the matrix's share of a launch.
 void stream_rows(int64_t N, int64_t K, int fmt, int wpc, const float *norm_w, qd::StreamArgs *a,
-                 unsigned *grid, int n_sel = 1) {
+                 unsigned *grid, int n_sel = 1, int g_set = 0) {
     const int64_t rb = row_bytes(fmt, K);
-    const int G = (int)std::min<int64_t>(N, std::max<int64_t>(1, (int64_t)kCUs * wpc / n_sel));
+    const int G = (int)std::min<int64_t>(
+        N, g_set > 0 ? g_set : std::max<int64_t>(1, (int64_t)kCUs * wpc / n_sel));
     a->N = N;
     a->K = K;
     a->row_bytes = rb;
@@ -394,8 +396,8 @@ void stream_rows(int64_t N, int64_t K, int fmt, int wpc, const float *norm_w, qd
 // copying wave for a free slot finite.  False if it does not fit.
 bool stream_plan_pc(int fmt, bool ffn, int64_t N, int64_t K, int batch, const float *norm_w,
                     int wpc, int consumers, int producers, int lag_default, qd::StreamArgs *a,
-                    unsigned *grid, size_t *lds, int n_sel = 1) {
-    stream_rows(N, K, fmt, wpc, norm_w, a, grid, n_sel);
+                    unsigned *grid, size_t *lds, int n_sel = 1, int g_set = 0) {
+    stream_rows(N, K, fmt, wpc, norm_w, a, grid, n_sel, g_set);
     a->consumers = consumers;
     a->producers = producers;
     const size_t budget = kLdsPerCU / wpc;
@@ -951,6 +953,41 @@ qd_status run_qkv(const int fmt[3], const void *const W[3], const int64_t N[3], 
         return QD_OK;
     }
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    if (batch == 1 && !launch_forced() && K % qd::kSuper == 0) {
+        // batch 1: the three matrices on the streaming kernel in one launch,
+        // the CUs shared in proportion to their bytes (Gemma-3-4B: 115, 57
+        // and 83 workgroups)
+        qd::StreamQkvArgs q{};
+        size_t lds = 0;
+        int64_t bytes[3], total = 0;
+        for (int i = 0; i < 3; i++) {
+            bytes[i] = N[i] * row_bytes(fmt[i], K);
+            total += bytes[i];
+        }
+        bool ok = true;
+        for (int i = 0; i < 3 && ok; i++) {
+            const int G = (int)std::max<int64_t>(1, std::min<int64_t>(N[i], kCUs * bytes[i] / total));
+            const int64_t wg_bytes = (N[i] + G - 1) / G * row_bytes(fmt[i], K);
+            const int prod = wg_bytes >= (int64_t(256) << 10) ? 4 : 2;
+            unsigned g = 0;
+            size_t l = 0;
+            ok = bytes[i] % 16 == 0 &&
+                 stream_plan_pc(fmt[i], false, N[i], K, 1, norm_w, 1, 8, prod, 4, &q.a[i], &g, &l, 1, G);
+            if (!ok) break;
+            qd::StreamArgs &a = q.a[i];
+            a.W0 = static_cast<const uint8_t *>(W[i]);
+            a.x = x;
+            a.y = y[i];
+            a.eps = eps;
+            q.fmt[i] = fmt[i];
+            q.wgs[i] = (int)g;
+            lds = std::max(lds, l);
+        }
+        if (ok) {
+            hipError_t e = qd::launch_stream_qkv(q, lds, hs);
+            return e == hipSuccess ? QD_OK : QD_ELAUNCH;
+        }
+    }
     const int nb = (int)(K / qd::kSuper);
     bool fused = K % qd::kSuper == 0;
     for (int i = 0; i < 3 && fused; i++) fused = nb <= lds_units_max(fmt[i], batch);

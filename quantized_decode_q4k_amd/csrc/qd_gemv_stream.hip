@@ -205,8 +205,9 @@ constexpr int kXFirstSlices = 16;  // longer staged x: the copying waves wait fo
 //     part[z]; the last of the n_sel workgroups of a row range (counter per
 //     range) forms y = sum of coef[z] * part[z] over the valid slots, in slot
 //     order, and returns the counter to zero.
+// wg: the workgroup's index in its launch (or in its matrix's share of one).
 template <int FMT, int B, int NR, bool FFN, int NC, bool MOE>
-__global__ __launch_bounds__(64 * (NC + kPcMaxProducers)) void stream_pc_kernel(StreamArgs a) {
+QD_DEV void stream_pc_body(StreamArgs a, int wg) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr int UB = StreamFmt<FMT>::UB;
     constexpr int NCH = StreamFmt<FMT>::NCH;
@@ -224,7 +225,6 @@ __global__ __launch_bounds__(64 * (NC + kPcMaxProducers)) void stream_pc_kernel(
     const int R = a.slots;
     const int NP = a.producers;
 
-    int wg = blockIdx.x;
     int z = 0;                 // routed slot (MOE)
     const float *xin = a.x;
     if constexpr (MOE) {
@@ -506,6 +506,35 @@ __global__ __launch_bounds__(64 * (NC + kPcMaxProducers)) void stream_pc_kernel(
     }
 }
 
+template <int FMT, int B, int NR, bool FFN, int NC, bool MOE>
+__global__ __launch_bounds__(64 * (NC + kPcMaxProducers)) void stream_pc_kernel(StreamArgs a) {
+    stream_pc_body<FMT, B, NR, FFN, NC, MOE>(a, blockIdx.x);
+}
+
+// Q, K and V projections of one token in one launch (batch 1): workgroup t
+// belongs to matrix 0, 1 or 2 by its index and streams that matrix's share
+// of rows in that matrix's format; every workgroup stages (and
+// RMS-normalises) x itself, so the three matrices' workgroups are
+// independent.
+__global__ __launch_bounds__(64 * (8 + kPcMaxProducers)) void stream_qkv_kernel(StreamQkvArgs q) {
+    int t = (int)blockIdx.x;
+    int s = 0;
+    if (t >= q.wgs[0]) {
+        t -= q.wgs[0];
+        s = 1;
+        if (t >= q.wgs[1]) {
+            t -= q.wgs[1];
+            s = 2;
+        }
+    }
+    const StreamArgs &a = q.a[s];
+    switch (q.fmt[s]) {
+    case kQ4K: stream_pc_body<kQ4K, 1, 1, false, 8, false>(a, t); break;
+    case kQ6K: stream_pc_body<kQ6K, 1, 1, false, 8, false>(a, t); break;
+    default: stream_pc_body<kQ80, 1, 1, false, 8, false>(a, t); break;
+    }
+}
+
 }  // namespace
 
 // LDS layout of the producer / consumer kernel with `slots` ring slots; returns
@@ -580,6 +609,15 @@ hipError_t launch_stream(int fmt, int batch, bool ffn, const StreamArgs &a, unsi
     case kQ80: return launch_sf<kQ80>(a, batch, ffn, grid, lds, st);
     default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_stream_qkv(const StreamQkvArgs &q, size_t lds, hipStream_t st) {
+    for (int i = 0; i < 3; i++)
+        if (q.a[i].consumers != 8) return hipErrorInvalidValue;
+    if (allow_lds<stream_qkv_kernel>() != hipSuccess) return hipErrorInvalidValue;
+    const unsigned grid = (unsigned)(q.wgs[0] + q.wgs[1] + q.wgs[2]);
+    hipLaunchKernelGGL(stream_qkv_kernel, dim3(grid), dim3(64 * (8 + kPcMaxProducers)), lds, st, q);
+    return hipGetLastError();
 }
 
 // The routed experts' launches of the MoE decode FFN (batch 1, 8 decoding

@@ -153,6 +153,14 @@ hipError_t launch_stream(int fmt, int batch, bool ffn, const StreamArgs &a, unsi
                          size_t lds, hipStream_t st);
 hipError_t launch_stream_moe(int fmt, bool ffn, const StreamArgs &a, unsigned grid, size_t lds,
                              hipStream_t st);
+// Q/K/V in one streaming launch (batch 1): wgs[i] workgroups for matrix i
+// (format fmt[i], plain GEMV arguments a[i], each with 8 decoding waves).
+struct StreamQkvArgs {
+    StreamArgs a[3];
+    int fmt[3];
+    int wgs[3];
+};
+hipError_t launch_stream_qkv(const StreamQkvArgs &q, size_t lds, hipStream_t st);
 
 // Batch 3..64 GEMVs on the matrix cores (qd_gemv_mfma.hip).  xdig_kernel
 // writes the activation digits of up to 64 batch rows in groups of 8: per

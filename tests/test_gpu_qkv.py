@@ -7,6 +7,11 @@ over K = 2560) in the Q4_K/Q4_K/Q6_K mix and in Q8_0; small ragged row counts
 that leave partial tiles, batch 1..8, with and without the norm; and the
 shapes that fall back to three GEMV launches (K beyond one workgroup's LDS,
 Q8_0 with K not a multiple of 256).
+
+At batch 1 with rows of whole 256-weight superunits the three matrices run
+on the streaming kernel in one launch; other batches, other rows and any
+forced launch shape take the register kernel, which the `register_kernel`
+cases run on the batch-1 shapes.
 """
 import numpy as np
 import pytest
@@ -28,6 +33,14 @@ def qd(gpu):
 
 
 from helpers import assert_bound, dev, say  # noqa: E402
+
+
+@pytest.fixture
+def register_kernel(qd):
+    """A forced launch shape keeps Q/K/V on the register kernel."""
+    qd.set_launch_override(4, 0, 0)
+    yield
+    qd.set_launch_override(0, 0, 0)
 
 
 def check_qkv(qd, fmts, Ns, K, batch, with_norm=True, tag="", rows=None):
@@ -76,17 +89,40 @@ def test_qkv_gemma4_31b_shapes(qd):
     check_qkv(qd, ("q4_k", "q4_k", "q6_k"), (512, 256, 256), 5376, 1, tag="gemma4 K=5376")
 
 
-@pytest.mark.parametrize("fmts,K", [(("q4_k", "q4_k", "q6_k"), 16384),
-                                    (("q8_0", "q8_0", "q8_0"), 96)])
-def test_qkv_three_launch_fallback(qd, fmts, K):
-    check_qkv(qd, fmts, (40, 24, 24), K, 1, tag="fallback")
+@pytest.mark.parametrize("fmts,K,batch", [(("q4_k", "q4_k", "q6_k"), 16384, 2),
+                                          (("q8_0", "q8_0", "q8_0"), 96, 1)])
+def test_qkv_three_launch_fallback(qd, fmts, K, batch):
+    check_qkv(qd, fmts, (40, 24, 24), K, batch, tag="fallback")
 
 
-def test_qkv_repeatable_bitwise(qd):
+def test_qkv_long_rows_streaming(qd):
+    """K = 16384 at batch 1: beyond the register kernel's staging, on the
+    streaming kernel."""
+    check_qkv(qd, ("q4_k", "q4_k", "q6_k"), (40, 24, 24), 16384, 1, tag="stream K=16384")
+
+
+def test_qkv_more_rows_than_cus(qd):
+    """Fewer rows than workgroups for one matrix, many rows per workgroup for
+    another."""
+    check_qkv(qd, ("q6_k", "q4_k", "q8_0"), (3000, 2, 700), 1024, 1, tag="uneven shares")
+
+
+@pytest.mark.parametrize("variant", ["kquant", "q8_0"])
+def test_qkv_register_kernel_gemma3_4b(qd, register_kernel, variant):
+    fm = ("q4_k", "q4_k", "q6_k") if variant == "kquant" else ("q8_0",) * 3
+    check_qkv(qd, fm, (2048, 1024, 1024), 2560, 1, tag=f"register kernel {variant}")
+
+
+def test_qkv_register_kernel_ragged(qd, register_kernel):
+    check_qkv(qd, ("q6_k", "q8_0", "q4_k"), (37, 5, 130), 512, 1, tag="register kernel ragged")
+
+
+@pytest.mark.parametrize("batch", [1, 2])
+def test_qkv_repeatable_bitwise(qd, batch):
     fm = ("q4_k", "q4_k", "q6_k")
     Ws = [dev(synth.quant_weights(f, n, 2560, SEED, tensor_id=70 + i)) for i, (f, n) in
           enumerate(zip(fm, (300, 100, 100)))]
-    x = dev(synth.normal((2, 2560), SEED, tensor_id=73))
+    x = dev(synth.normal((batch, 2560), SEED, tensor_id=73))
     nw = dev(synth.normal((2560,), SEED, tensor_id=74, mean=1.0, std=0.1))
     a = [t.cpu().numpy() for t in qd.qqkv_proj(fm, *Ws, x, nw)]
     b = [t.cpu().numpy() for t in qd.qqkv_proj(fm, *Ws, x, nw)]
