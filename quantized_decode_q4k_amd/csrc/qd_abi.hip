@@ -131,8 +131,11 @@ Plan choose_plan(int fmt, int64_t N, int64_t K, int batch, bool ffn) {
     //    (Gemma-4-31B FFN at batch 8: gate/up 194-282 -> 114-137 us, down
     //    113 -> 85 us);
     //  * batch 1..2 plain GEMV over many rows: two rows per lane group, two
-    //    row slots (four for Q8_0's longer rows) (lm_head 262144 x 2560:
-    //    Q4_K 82 -> 71-75 us, Q8_0 155 -> 144 us).
+    //    row slots (lm_head 262144 x 2560: Q4_K 82 -> 71-75 us, Q8_0 155 ->
+    //    144 us), four for Q8_0's longer rows and for Q4_K where the rows
+    //    allow (lm_head Q4_K on activation digits, same box: batch 1
+    //    78.9-82.0 -> 75.1-76.3 us, batch 2 101.7-104.6 -> 99.2-101.7 us;
+    //    eight: 74.6-74.9 and 101.9-102.7 us).
     if (batch >= 3) {
         Shape t = p.s;
         t.p_in = 1;
@@ -142,9 +145,14 @@ Plan choose_plan(int fmt, int64_t N, int64_t K, int batch, bool ffn) {
     } else if (!ffn && p.s.p_in == 2) {
         Shape t = p.s;
         t.nr = 2;
-        t.rpg = fmt == qd::kQ80 ? 4 : 2;
-        Plan q = make_plan(fmt, N, K, batch, ffn, t);
-        if (q.tiles * q.s.p_out >= kWalkMinWorkgroups) p = q;
+        for (int rpg = fmt == qd::kQ6K ? 2 : 4; rpg >= 2; rpg /= 2) {
+            t.rpg = rpg;
+            Plan q = make_plan(fmt, N, K, batch, ffn, t);
+            if (q.tiles * q.s.p_out >= kWalkMinWorkgroups) {
+                p = q;
+                break;
+            }
+        }
     }
     // explicit overrides (tuning sweeps)
     const int op = g_over_pin.load(), oq = g_over_pout.load(), onr = g_over_nr.load();
