@@ -60,78 +60,81 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 // kernel copies to LDS as it is.
 __host__ __device__ constexpr int mq_su_bytes(int rr) { return 8 * kFragRun + 8 * rr; }
 
-// One workgroup of 1024 threads per batch row (ng * 8 rows; rows past
-// `batch`, and runs past K / 32, are written as zeros).  Each thread holds
-// up to kXdF float4 of the row (8 consecutive threads = one run), all loaded
-// before the first is used: the row's mean square (RMS-norm) and its digits
-// come from one pass over x.
-constexpr int kXdThreads = 1024;
-constexpr int kXdF = 8;   // float4 per thread: rows of up to 8 * 1024 * 4 = 32768 activations
+// A workgroup of four waves per (batch row, four superunits) of ng * 8 rows
+// by ceil(nb / 4) (rows past `batch`, and runs past K / 32, are written as
+// zeros): wave w takes superunit 4 blockIdx.y + w, lane l its float4 l (8
+// consecutive lanes = one run).  With an RMS-norm weight every workgroup
+// first forms its row's mean square itself (each thread's float4 of the
+// row, all loaded before the first is used, then a fixed-order workgroup
+// sum), so the digit pass is one launch over many CUs with no hand-off.
+constexpr int kXdThreads = 256;
+constexpr int kXdMaxK = 32768;  // longest row the matrix kernel takes
+constexpr int kXdF = kXdMaxK / 4 / kXdThreads;  // float4 of the row per thread
 template <bool NORM, bool SX>
 __global__ __launch_bounds__(kXdThreads) void xdig_kernel(XdArgs a) {
     __shared__ float red[kXdThreads / 64];
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = blockIdx.x;
+    const int t = 4 * blockIdx.y + wave;  // this wave's superunit (uniform)
     const bool live = b < a.batch;
-    const int F = a.R * 8;            // float4 of the row
-    const int Fp = a.nb * 64;         // float4 of the padded row (8 runs per superunit)
+    const int F = a.R * 8;  // float4 of the row
     const float *xb = a.x + (int64_t)b * a.K;
-    float4 v[kXdF];
-#pragma unroll
-    for (int i = 0; i < kXdF; i++) {
-        const int f = tid + kXdThreads * i;
-        v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (live && f < F) v[i] = *reinterpret_cast<const float4 *>(xb + 4 * (int64_t)f);
+    const int f = 64 * t + lane;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 w = make_float4(1.f, 1.f, 1.f, 1.f);
+    if (live && t < a.nb && f < F) {
+        v = *reinterpret_cast<const float4 *>(xb + 4 * (int64_t)f);
+        if (NORM) w = *reinterpret_cast<const float4 *>(a.norm_w + 4 * (int64_t)f);
     }
     if (NORM) {
+        // the row's sum of squares: thread tid adds float4 tid, tid + 256, ...
+        // in order (loaded together, up to kXdF), then the workgroup's fixed
+        // cross-lane and cross-wave order
         float ss = 0.f;
+        if (live) {
+            float4 r[kXdF];
 #pragma unroll
-        for (int i = 0; i < kXdF; i++) {
-            ss = fmaf(v[i].x, v[i].x, ss);
-            ss = fmaf(v[i].y, v[i].y, ss);
-            ss = fmaf(v[i].z, v[i].z, ss);
-            ss = fmaf(v[i].w, v[i].w, ss);
+            for (int i = 0; i < kXdF; i++) {
+                const int ff = tid + kXdThreads * i;
+                r[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (ff < F) r[i] = *reinterpret_cast<const float4 *>(xb + 4 * (int64_t)ff);
+            }
+#pragma unroll
+            for (int i = 0; i < kXdF; i++) {
+                ss = fmaf(r[i].x, r[i].x, ss);
+                ss = fmaf(r[i].y, r[i].y, ss);
+                ss = fmaf(r[i].z, r[i].z, ss);
+                ss = fmaf(r[i].w, r[i].w, ss);
+            }
         }
         ss = block_total<kXdThreads>(ss, red);
         const float ir = 1.0f / sqrtf(ss / (float)a.K + a.eps);
-#pragma unroll
-        for (int i = 0; i < kXdF; i++) {
-            const int f = tid + kXdThreads * i;
-            if (live && f < F) {
-                const float4 w = *reinterpret_cast<const float4 *>(a.norm_w + 4 * (int64_t)f);
-                v[i].x = v[i].x * ir * w.x;
-                v[i].y = v[i].y * ir * w.y;
-                v[i].z = v[i].z * ir * w.z;
-                v[i].w = v[i].w * ir * w.w;
-            }
-        }
+        v.x = v.x * ir * w.x;
+        v.y = v.y * ir * w.y;
+        v.z = v.z * ir * w.z;
+        v.w = v.w * ir * w.w;
     }
+    if (t >= a.nb) return;  // uniform per wave, after the workgroup's barriers
     constexpr int RR = SX ? 128 : 32;
-    const int g = b >> 3, bb = b & 7, q = tid & 7;
+    const int g = b >> 3, bb = b & 7, q = lane & 7;
+    uint32_t pl[4];
+    double sc, sxs;
+    digitize_run<SX>(v, pl, sc, sxs);  // all 8 lanes of every run take part
+    const int run = f >> 3;
+    uint8_t *su = a.dig + ((int64_t)g * a.nb + t) * mq_su_bytes(RR);
+    uint8_t *fr = su + (run & 7) * kFragRun;
 #pragma unroll
-    for (int i = 0; i < kXdF; i++) {
-        const int f0 = kXdThreads * i;
-        if (f0 >= Fp) break;  // uniform
-        uint32_t pl[4];
-        double sc, sxs;
-        digitize_run<SX>(v[i], pl, sc, sxs);  // all 8 lanes of every run take part
-        const int run = (f0 + tid) >> 3;
-        if (f0 + tid >= Fp) continue;
-        uint8_t *su = a.dig + ((int64_t)g * a.nb + (run >> 3)) * mq_su_bytes(RR);
-        uint8_t *fr = su + (run & 7) * kFragRun;
-#pragma unroll
-        for (int p = 0; p < 4; p++)
-            *reinterpret_cast<uint32_t *>(fr + 16 * (bb + 8 * p + 32 * (q >> 2)) + 4 * (q & 3)) = pl[p];
-        if (q == 0) {
-            uint8_t *rec = su + 8 * kFragRun + (run & 7) * RR;
-            if constexpr (SX) {
-                double2 r;
-                r.x = sc;
-                r.y = sxs;
-                reinterpret_cast<double2 *>(rec)[bb] = r;
-            } else {
-                reinterpret_cast<float *>(rec)[bb] = (float)sc;
-            }
+    for (int p = 0; p < 4; p++)
+        *reinterpret_cast<uint32_t *>(fr + 16 * (bb + 8 * p + 32 * (q >> 2)) + 4 * (q & 3)) = pl[p];
+    if (q == 0) {
+        uint8_t *rec = su + 8 * kFragRun + (run & 7) * RR;
+        if constexpr (SX) {
+            double2 rr;
+            rr.x = sc;
+            rr.y = sxs;
+            reinterpret_cast<double2 *>(rec)[bb] = rr;
+        } else {
+            reinterpret_cast<float *>(rec)[bb] = (float)sc;
         }
     }
 }
@@ -882,11 +885,11 @@ static hipError_t allow_lds_mq(size_t bytes) {
     return e;
 }
 
-int xdig_max_k() { return kXdF * kXdThreads * 4; }
+int xdig_max_k() { return kXdMaxK; }
 
 hipError_t launch_xdig(const XdArgs &a, int ng, bool sx, hipStream_t st) {
-    if (a.K > xdig_max_k() || 64 * a.nb > kXdF * kXdThreads) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)(ng * 8));
+    if (a.K > xdig_max_k() || a.nb < 1 || 256 * (int64_t)a.nb < a.K) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(ng * 8), (unsigned)((a.nb + 3) / 4));
     const bool norm = a.norm_w != nullptr;
     const dim3 blk(kXdThreads);
     if (norm && sx) hipLaunchKernelGGL((xdig_kernel<true, true>), grid, blk, 0, st, a);
