@@ -433,8 +433,9 @@ qd_status qffn_decode_post_norm_residual(qd_format fmt_gu, const void *Wg, const
  * Errors: QD_ESHAPE (shapes, n_experts < 1, n_sel outside 1..64),
  * QD_EINVAL (NULL pointers, bad act, outputs overlapping inputs),
  * QD_EALIGN, QD_EUNSUPPORTED when K or N_ff does not fit one workgroup's
- * LDS (K or N_ff up to 14592 in Q4_K).  Calls that overlap on one stream's
- * workspace race.
+ * LDS (rows of whole 256-weight superunits: the streaming kernel's staged
+ * digits and ring; other rows: K or N_ff up to 14592 in Q4_K).  Calls that
+ * overlap on one stream's workspace race.
  */
 qd_status qmoe_ffn_decode(qd_format fmt_gu, const void *Wg, const void *Wu, qd_format fmt_down,
                           const void *Wd, int n_experts, const int32_t *ids, const float *coef,

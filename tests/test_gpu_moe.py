@@ -153,3 +153,9 @@ def test_moe_register_kernel_bench_configuration(qd, register_kernel):
 def test_moe_register_kernel_invalid_id(qd, register_kernel):
     check_moe(qd, "q8_0", "q8_0", 512, 512, 6, [5, -1, 6, 0], [0.5, 9.0, 7.0, 0.25], "gelu_tanh",
               tag="register kernel, invalid ids")
+
+
+def test_moe_long_rows_streaming(qd):
+    """Hidden 16384: beyond the register kernel's staging (which would refuse
+    it), on the streaming kernel."""
+    check_moe(qd, "q4_k", "q6_k", 16384, 512, 3, [2, 0], [0.7, 0.3], "gelu_tanh", tag="hidden 16384")
