@@ -111,8 +111,20 @@ def test_ffn_decode_guard_bands(qd):
     h.check("qffn_decode h")
 
 
-def test_qkv_and_moe_guard_bands(qd):
-    say("guard qkv and moe")
+@pytest.mark.parametrize("kernel", ["stream", "register"])
+def test_qkv_and_moe_guard_bands(qd, kernel):
+    """Batch 1 runs on the streaming kernel; a forced launch shape keeps the
+    register kernel."""
+    say(f"guard qkv and moe ({kernel} kernel)")
+    if kernel == "register":
+        qd.set_launch_override(4, 0, 0)
+    try:
+        _qkv_and_moe(qd)
+    finally:
+        qd.set_launch_override(0, 0, 0)
+
+
+def _qkv_and_moe(qd):
     fm, Ns, K = ("q4_k", "q4_k", "q6_k"), (2048, 1024, 1024), 2560
     Ws = [dev(synth.quant_weights(f, n, K, SEED, tensor_id=143 + i)) for i, (f, n) in enumerate(zip(fm, Ns))]
     x = dev(synth.normal((1, K), SEED, tensor_id=146))
