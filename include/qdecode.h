@@ -288,10 +288,12 @@ qd_status qgemv_post_norm_residual(qd_format fmt, const void *W, const float *x,
  *                   overlap each other or any input
  *   K               a multiple of 256 when any matrix is Q4_K or Q6_K (of 32
  *                   when all are Q8_0)
- * Accuracy: each output meets the GEMV bound for xn.  One launch when every
- * matrix's activation slice fits one workgroup's LDS (K up to 14592 at
- * batch 1 in Q4_K) and K is a multiple of 256; otherwise the same results
- * from three GEMV launches.  Needs no workspace.
+ * Accuracy: each output meets the GEMV bound for xn.  One launch when K is
+ * a multiple of 256 and every matrix's staged activations fit one
+ * workgroup's LDS (at batch 1 on the streaming kernel, the CUs shared in
+ * proportion to the matrices' bytes; at batch 2-8 K up to 14592 in Q4_K on
+ * the register kernel); otherwise the same bound from three GEMV launches.
+ * Needs no workspace.
  * Errors: as qgemv for each matrix (QD_ESHAPE, QD_EALIGN, QD_EINVAL).
  */
 qd_status qqkv_proj(qd_format fmt_q, const void *Wq, int64_t Nq, qd_format fmt_k,
