@@ -22,6 +22,10 @@
 //  * x is multiplied by the RMS-norm weight and staged once per workgroup
 //    as activation digits (qd_digits.h: exact integer products); the
 //    inverse RMS is applied to each row's sum at the end.
+//  * The same body serves the routed experts of the MoE decode FFN (the
+//    slots share the CUs, each workgroup a row range of one slot's expert)
+//    and the Q, K and V projections in one launch (the CUs shared by the
+//    three matrices, each workgroup in its own matrix's format).
 // The copies are ordered by explicit waits (qd_lds.h).
 #include "qd_decode.h"
 #include "qd_digits.h"
@@ -194,7 +198,6 @@ QD_DEV void dot_step(const StepRegs<FMT, NR> &st, const uint8_t *xd, int xsb, co
 constexpr int kPcMaxProducers = 4;
 constexpr int kXFirstSlices = 16;  // longer staged x: the copying waves wait for it
 
-//
 // Mixture-of-experts slots (MOE): the launch holds n_sel * wps workgroups,
 // workgroup i serving routed slot z = i / wps with row range i % wps of that
 // slot's expert e = ids[z] (an id outside [0, n_experts) streams expert 0
