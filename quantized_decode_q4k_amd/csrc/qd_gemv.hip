@@ -587,6 +587,8 @@ __global__ __launch_bounds__(kThreads) void mv_kernel(MvArgs a) {
 // the experts' outputs summed with their routing weights.  The expert ids
 // and weights stay on the device (no host round trip): slot z of the launch
 // reads ids[z] and offsets the weight pointers by that expert's matrix.
+// This register-kernel form runs rows that are not whole superunits and
+// forced launch shapes; the streaming kernel runs the rest.
 //  * gate/up (FFN = true, grid (tiles, 1, n_sel)): slot z = blockIdx.z
 //    writes its h rows at y + z * y_sstride; an id outside [0, n_experts)
 //    writes zeros (the slot contributes nothing);
@@ -644,7 +646,9 @@ hipError_t launch_moe(int fmt, bool ffn, const MvArgs &a, int64_t tiles, int n_s
 // ------------------------------------------------ fused Q/K/V projection ---
 // The larql Gemma 3 table runs the input RMS-norm and the Q, K and V
 // projections of attention as one fused dispatch (Q and K in Q4_K, V in
-// Q6_K).  Here the three projections share one launch: workgroup t belongs
+// Q6_K).  This register-kernel form serves batch 2-8 (and rows that are not
+// whole superunits, and forced launch shapes; batch 1 runs on the streaming
+// kernel).  The three projections share one launch: workgroup t belongs
 // to matrix 0, 1 or 2 by its index, and runs that matrix's row tile in that
 // matrix's format.  Every tile stages (and RMS-normalises) the activation
 // rows itself, so the tiles are independent and the launch needs no
