@@ -105,33 +105,53 @@ QD_DEV Q4Nibbles q4k_nibbles(uint32_t v) {
 // (g = 0..3, l = 0..15): low 4 bits from ql[64h + 16j + l] (g = 0: low
 // nibble, g = 2: high nibble) and ql[64h + 32 + 16j + l] (g = 1, 3); high 2
 // bits from qh[32h + 16j + l] (bits 2g, 2g+1); scale sc[8h + 2g + j].
-// Blocks start on 2-byte boundaries, so every field is read as whole dwords
-// from the 4-byte-aligned address at or below it and re-aligned by `sh`
-// bytes.  Each dword read overlaps the block, so no read leaves the matrix.
+// Blocks start on 2-byte boundaries.  Read out of LDS (the streaming
+// kernel), every field is taken as whole dwords from the 4-byte-aligned
+// address at or below it and re-aligned by `sh` bytes (RawQ6K); read from
+// global memory (the register kernels), each field is one 16-byte (quants),
+// 8-byte (scales) or 2-byte (d) load at its own address, which global
+// memory takes unaligned (RawQ6KA).  No read leaves the block.
 struct RawQ6K {
     uint32_t a[5], b[5], h[5];  // ql[64h+16j..], ql[64h+32+16j..], qh[32h+16j..] (+1 dword)
     uint32_t s[3];              // scales of half h (+ slack)
     uint32_t d;                 // dword holding d
     uint32_t sh;                // block start & 3
 };
+struct RawQ6KA {
+    uint32_t a[4], b[4], h[4];  // ql[64h+16j..], ql[64h+32+16j..], qh[32h+16j..]
+    uint32_t s[2];              // scales 8h .. 8h + 7
+    uint32_t d;                 // f16 d in the low half
+};
 
-QD_DEV void load_q6k(RawQ6K &r, const uint8_t *blk, int h, int j) {
-    const uintptr_t addr = reinterpret_cast<uintptr_t>(blk);
-    r.sh = (uint32_t)(addr & 3u);
-    const uint8_t *bp = blk - r.sh;
-    const uint8_t *pa = bp + 64 * h + 16 * j;
-    const uint8_t *pb = pa + 32;
-    const uint8_t *ph = bp + 128 + 32 * h + 16 * j;
-    const uint8_t *ps = bp + 192 + 8 * h;
+typedef uint32_t q6_u4a2 __attribute__((ext_vector_type(4), aligned(2)));
+typedef uint32_t q6_u2a2 __attribute__((ext_vector_type(2), aligned(2)));
+QD_DEV void load_q6k(RawQ6KA &r, const uint8_t *blk, int h, int j) {
+    const uint8_t *pa = blk + 64 * h + 16 * j;
+    const q6_u4a2 A = *reinterpret_cast<const q6_u4a2 *>(pa);
+    const q6_u4a2 Bq = *reinterpret_cast<const q6_u4a2 *>(pa + 32);
+    const q6_u4a2 H = *reinterpret_cast<const q6_u4a2 *>(blk + 128 + 32 * h + 16 * j);
+    const q6_u2a2 S = *reinterpret_cast<const q6_u2a2 *>(blk + 192 + 8 * h);
 #pragma unroll
-    for (int k = 0; k < 5; k++) {
-        r.a[k] = ld32(pa + 4 * k);
-        r.b[k] = ld32(pb + 4 * k);
-        r.h[k] = ld32(ph + 4 * k);
+    for (int k = 0; k < 4; k++) {
+        r.a[k] = A[k];
+        r.b[k] = Bq[k];
+        r.h[k] = H[k];
     }
-#pragma unroll
-    for (int k = 0; k < 3; k++) r.s[k] = ld32(ps + 4 * k);
-    r.d = ld32(bp + 208);
+    r.s[0] = S[0];
+    r.s[1] = S[1];
+    r.d = *reinterpret_cast<const uint16_t *>(blk + 208);
+}
+
+// The ql (a, b) and qh dwords k of a lane's share.
+QD_DEV void q6k_dwords(const RawQ6K &r, int k, uint32_t &av, uint32_t &bv, uint32_t &hv) {
+    av = align_bytes(r.a[k + 1], r.a[k], r.sh);
+    bv = align_bytes(r.b[k + 1], r.b[k], r.sh);
+    hv = align_bytes(r.h[k + 1], r.h[k], r.sh);
+}
+QD_DEV void q6k_dwords(const RawQ6KA &r, int k, uint32_t &av, uint32_t &bv, uint32_t &hv) {
+    av = r.a[k];
+    bv = r.b[k];
+    hv = r.h[k];
 }
 
 // Byte lookup of the high bits: hi (0..3) -> (hi - 2) << 4 as a two's
@@ -139,10 +159,10 @@ QD_DEV void load_q6k(RawQ6K &r, const uint8_t *blk, int h, int j) {
 constexpr uint32_t kQ6HiTable = 0x1000F0E0u;
 
 // Signed bytes (q - 32) of group g = 0..3 for dword k (weights l = 4k..4k+3).
-QD_DEV void q6k_qbytes(const RawQ6K &r, int k, uint32_t (&q)[4]) {
-    const uint32_t av = align_bytes(r.a[k + 1], r.a[k], r.sh);
-    const uint32_t bv = align_bytes(r.b[k + 1], r.b[k], r.sh);
-    const uint32_t hv = align_bytes(r.h[k + 1], r.h[k], r.sh);
+template <class R>
+QD_DEV void q6k_qbytes(const R &r, int k, uint32_t (&q)[4]) {
+    uint32_t av, bv, hv;
+    q6k_dwords(r, k, av, bv, hv);
     q[0] = (av & 0x0F0F0F0Fu) | byte_lut(kQ6HiTable, hv & 0x03030303u);
     q[1] = (bv & 0x0F0F0F0Fu) | byte_lut(kQ6HiTable, (hv >> 2) & 0x03030303u);
     q[2] = ((av >> 4) & 0x0F0F0F0Fu) | byte_lut(kQ6HiTable, (hv >> 4) & 0x03030303u);
@@ -163,6 +183,17 @@ QD_DEV Q6Scales q6k_scales(const RawQ6K &r, int j) {
     s.sc[2] = sbyte(s23, 0);
     s.sc[3] = sbyte(s23, 2);
     s.d = f16_lo(align_bytes(r.d, r.d, r.sh));
+    return s;
+}
+QD_DEV Q6Scales q6k_scales(const RawQ6KA &r, int j) {
+    const uint32_t s01 = r.s[0] >> (8 * j);  // sc[8h+j], sc[8h+2+j]
+    const uint32_t s23 = r.s[1] >> (8 * j);  // sc[8h+4+j], sc[8h+6+j]
+    Q6Scales s;
+    s.sc[0] = sbyte(s01, 0);
+    s.sc[1] = sbyte(s01, 2);
+    s.sc[2] = sbyte(s23, 0);
+    s.sc[3] = sbyte(s23, 2);
+    s.d = f16_lo(r.d);
     return s;
 }
 
@@ -225,7 +256,7 @@ QD_DEV uint2 q80_qdwords(const RawQ80 &r, int k) {
 template <int FMT>
 struct RawOf;
 template <> struct RawOf<kQ4K> { using T = RawQ4K; };
-template <> struct RawOf<kQ6K> { using T = RawQ6K; };
+template <> struct RawOf<kQ6K> { using T = RawQ6KA; };
 template <> struct RawOf<kQ80> { using T = RawQ80; };
 
 // Load lane c's share of superunit t of the row starting at rowp.

@@ -288,19 +288,15 @@ QD_DEV void q6k_group_dig(const uint32_t (&av)[NR][4], const uint32_t (&bv)[NR][
     }
 }
 
-template <int NR, int B>
-QD_DEV void q6k_step_dig(const RawQ6K (&r)[NR], const uint8_t *__restrict__ xd, int xsb, int h, int j,
+template <int NR, int B, class R>
+QD_DEV void q6k_step_dig(const R (&r)[NR], const uint8_t *__restrict__ xd, int xsb, int h, int j,
                          float (&y)[NR][B]) {
     uint32_t av[NR][4], bv[NR][4], hv[NR][4];
     Q6Scales s[NR];
 #pragma unroll
     for (int i = 0; i < NR; i++) {
 #pragma unroll
-        for (int k4 = 0; k4 < 4; k4++) {
-            av[i][k4] = align_bytes(r[i].a[k4 + 1], r[i].a[k4], r[i].sh);
-            bv[i][k4] = align_bytes(r[i].b[k4 + 1], r[i].b[k4], r[i].sh);
-            hv[i][k4] = align_bytes(r[i].h[k4 + 1], r[i].h[k4], r[i].sh);
-        }
+        for (int k4 = 0; k4 < 4; k4++) q6k_dwords(r[i], k4, av[i][k4], bv[i][k4], hv[i][k4]);
         s[i] = q6k_scales(r[i], j);
     }
     q6k_group_dig<0, NR, B>(av, bv, hv, s, xd, xsb, h, j, y);

@@ -122,8 +122,8 @@ QD_DEV void q4k_step(const RawQ4K (&r)[NR], const float *__restrict__ xp, int xs
 }
 
 // Q6_K.  xg0..xg3: this lane's four runs of 16 activations (groups g).
-template <int NR, int B>
-QD_DEV void q6k_step(const RawQ6K (&r)[NR], const float *__restrict__ xg0,
+template <int NR, int B, class R>
+QD_DEV void q6k_step(const R (&r)[NR], const float *__restrict__ xg0,
                      const float *__restrict__ xg1, const float *__restrict__ xg2,
                      const float *__restrict__ xg3, int xstride, int j, float (&y)[NR][B]) {
     float acc[NR][B][4];

@@ -130,9 +130,14 @@ QD_DEV void lds_q80(RawQ80 &r, const uint8_t *blk, int c) {
 // ------------------------------------------------------ one step ---
 // A lane's share of one superunit (per row stream) out of the ring; the
 // activations are read as digits (qd_digits.h) while multiplying.
+// Q6_K out of LDS keeps the re-aligned dword form (LDS takes no unaligned
+// 16-byte reads).
+template <int FMT>
+struct LdsRaw { using T = typename RawOf<FMT>::T; };
+template <> struct LdsRaw<kQ6K> { using T = RawQ6K; };
 template <int FMT, int NR>
 struct StepRegs {
-    typename RawOf<FMT>::T raw[NR];
+    typename LdsRaw<FMT>::T raw[NR];
 };
 
 // blk0: the lane group's superunit in row stream 0 (stream m is m * mstride
