@@ -77,6 +77,7 @@ std::atomic<int> g_over_pin{0}, g_over_pout{0}, g_over_nr{0}, g_over_rpg{0};
 constexpr int kTargetWorkgroups = 400;   // enough to keep every CU streaming
 constexpr int kWalkMinWorkgroups = 1000; // batch 1-2 row walk only with rows to spare
 constexpr int kMaxTiles = 1 << 16;       // split-K counters per workspace
+constexpr int64_t kStreamMinK = 8192;    // automatic use of the streaming kernel
 constexpr int kAuxWords = 4096;          // counters after the tile counters: row epilogues, FFN flags
 
 int lds_units_max(int fmt, int batch) {
@@ -113,7 +114,14 @@ Plan choose_plan(int fmt, int64_t N, int64_t K, int batch, bool ffn) {
     // chip, and only then across workgroups.
     Shape s{2, p_lds, 1};
     Plan p = make_plan(fmt, N, K, batch, ffn, s);
-    for (int iter = 0; iter < 16; iter++) {
+    // Batch 2 over rows of K >= kStreamMinK, few of them (the streaming
+    // kernel takes the rest): four K-slices across workgroups and no more
+    // lane groups per row (Gemma-3 down 2560 x 10240, graph replay, p_in /
+    // p_out 2/4 against 2/2, 4/4, 2/8: Q6_K 15.4 against 17.8, 17.9, 17.8 us;
+    // Q4_K 13.0 against 15.8, 12.6, 13.2; Q8_0 17.1 against 20.9, 16.7, 17.4).
+    const bool long_b2 = batch == 2 && !ffn && K >= kStreamMinK;
+    if (long_b2) p = make_plan(fmt, N, K, batch, ffn, Shape{2, std::max(p_lds, 4), 1});
+    for (int iter = 0; iter < 16 && !long_b2; iter++) {
         const int64_t wgs = p.tiles * p.s.p_out;
         if (wgs >= kTargetWorkgroups) break;
         Shape t = p.s;
@@ -373,8 +381,8 @@ constexpr size_t kLdsPerCU = 160 * 1024;    // gfx950 LDS per CU
 constexpr int kStreamMaxWait = 63;          // vmcnt limit: copies in flight per wave
 // tuning overrides (0 = automatic)
 std::atomic<int> g_stream_wpc{0}, g_stream_depth{0}, g_stream_consumers{0}, g_stream_producers{0};
-constexpr int64_t kStreamMinK = 8192;       // automatic use of the streaming kernel
-constexpr int64_t kStreamMinRowsTall = 65536;  // ... and for tall Q6_K / Q8_0 matrices at batch 1
+constexpr int64_t kStreamMinRowsTall = 65536;  // streaming kernel for tall Q6_K / Q8_0 matrices at batch 1
+constexpr int64_t kStreamMinRowsB2 = 4096;     // ... and at batch 2 only from this many rows
 
 // n_sel > 1: the routed slots of a MoE launch share the CUs, each slot
 // taking G workgroups (at least one) over its own matrix.  g_set > 0: G
@@ -479,6 +487,11 @@ bool stream_plan(int fmt, bool ffn, int64_t N, int64_t K, int batch, const float
         const int prod = wg_bytes >= (int64_t(256) << 10) ? 4 : 2;
         return stream_plan_pc(fmt, ffn, N, K, batch, norm_w, 1, 8, prod, kPcLag1, a, grid, lds);
     }
+    // batch 2 over few rows: the register kernel's K split across
+    // workgroups fills the chip better (Gemma-3 down 2560 x 10240, graph
+    // replay: Q6_K 21.5-22.0 -> 15.4 us, Q4_K 18.3-19.0 -> 13.0 us, Q8_0
+    // 18.2-18.6 -> 17.1 us; 5376 x 21504 about even)
+    if (!ffn && N < kStreamMinRowsB2) return false;
     // 8 decoding waves spill registers at batch 2
     if (stream_plan_pc(fmt, ffn, N, K, batch, norm_w, 1, 4, 2, kPcLag, a, grid, lds) &&
         a->slots * 16 >= a->units_max)

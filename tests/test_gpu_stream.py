@@ -2,7 +2,8 @@
 one workgroup per row range) against the oracle.
 
 The path applies to batch 1 and 2 when the matrix is a whole number of
-16-byte chunks; it is taken automatically for long rows (K >= 8192) and
+16-byte chunks; it is taken automatically for long rows (K >= 8192; at
+batch 2 only from 4096 rows, fewer go to the register kernel) and
 forced here with the stream override on shapes chosen to split rows
 unevenly over workgroups, leave partial last steps and run fewer rows than
 workgroups, with 4 and 8 decoding waves and one, two or four copying waves
@@ -156,3 +157,22 @@ def test_stream_ring_reuse_gate_up(qd, consumers, depth, producers):
         assert_bound(f"up wpc={wpc}", u.cpu().numpy(), u64, Su)
         err = np.abs(h - href)
         assert (err <= tol).all(), f"h wpc={wpc}: worst {np.max(err / tol):.3f} of tolerance"
+
+
+# Batch 2 over long rows and few of them (the Gemma-3 down shape, 2560 rows
+# of K = 10240) runs on the register kernel with four K-slices across
+# workgroups, the automatic choice there; 4096 rows stay on the streaming
+# kernel.  Every output row is checked.
+@pytest.mark.parametrize("fmt", ["q4_k", "q6_k", "q8_0"])
+@pytest.mark.parametrize("N", [2560, 4096])
+def test_long_rows_batch2_automatic(qd, fmt, N):
+    K, batch = 10240, 2
+    say(f"automatic gemv {fmt} N={N} K={K} batch={batch}")
+    W = synth.quant_weights(fmt, N, K, SEED, tensor_id=83)
+    x = synth.normal((batch, K), SEED, tensor_id=84)
+    Wd, xd = dev(W), dev(x)
+    y64, S = oracle.gemv(fmt, W, x, N, K)
+    y = qd.qgemv(fmt, Wd, xd).cpu().numpy()
+    assert_bound(f"automatic {fmt} N={N}", y, y64, S)
+    again = qd.qgemv(fmt, Wd, xd).cpu().numpy()
+    assert np.array_equal(y.view(np.uint32), again.view(np.uint32))
