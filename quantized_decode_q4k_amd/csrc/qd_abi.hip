@@ -78,6 +78,7 @@ constexpr int kTargetWorkgroups = 400;   // enough to keep every CU streaming
 constexpr int kWalkMinWorkgroups = 1000; // batch 1-2 row walk only with rows to spare
 constexpr int kMaxTiles = 1 << 16;       // split-K counters per workspace
 constexpr int64_t kStreamMinK = 8192;    // automatic use of the streaming kernel
+constexpr int64_t kRegisterMinKFfnB2 = 4096;  // fused gate/up at batch 2: register kernel from this K
 constexpr int kAuxWords = 4096;          // counters after the tile counters: row epilogues, FFN flags
 
 int lds_units_max(int fmt, int batch) {
@@ -119,9 +120,15 @@ Plan choose_plan(int fmt, int64_t N, int64_t K, int batch, bool ffn) {
     // lane groups per row (Gemma-3 down 2560 x 10240, graph replay, p_in /
     // p_out 2/4 against 2/2, 4/4, 2/8: Q6_K 15.4 against 17.8, 17.9, 17.8 us;
     // Q4_K 13.0 against 15.8, 12.6, 13.2; Q8_0 17.1 against 20.9, 16.7, 17.4).
+    // The fused gate/up at batch 2 over rows of K >= 4096: one lane group per
+    // row and two K-slices across workgroups (graph replay, against the
+    // streaming kernel: Gemma-4 21504 x 5376 62.7-66.1 -> 54.7-57.9 us,
+    // 14336 x 4096 32.9-39.3 -> 27.3-30.4 us; p_out 3 and 4 no better).
     const bool long_b2 = batch == 2 && !ffn && K >= kStreamMinK;
+    const bool ffn_b2 = batch == 2 && ffn && K >= kRegisterMinKFfnB2;
     if (long_b2) p = make_plan(fmt, N, K, batch, ffn, Shape{2, std::max(p_lds, 4), 1});
-    for (int iter = 0; iter < 16 && !long_b2; iter++) {
+    if (ffn_b2) p = make_plan(fmt, N, K, batch, ffn, Shape{1, std::max(p_lds, 2), 1});
+    for (int iter = 0; iter < 16 && !long_b2 && !ffn_b2; iter++) {
         const int64_t wgs = p.tiles * p.s.p_out;
         if (wgs >= kTargetWorkgroups) break;
         Shape t = p.s;
@@ -492,6 +499,8 @@ bool stream_plan(int fmt, bool ffn, int64_t N, int64_t K, int batch, const float
     // replay: Q6_K 21.5-22.0 -> 15.4 us, Q4_K 18.3-19.0 -> 13.0 us, Q8_0
     // 18.2-18.6 -> 17.1 us; 5376 x 21504 about even)
     if (!ffn && N < kStreamMinRowsB2) return false;
+    // ... and the fused gate/up over rows of K >= 4096 (choose_plan)
+    if (ffn && K >= kRegisterMinKFfnB2) return false;
     // 8 decoding waves spill registers at batch 2
     if (stream_plan_pc(fmt, ffn, N, K, batch, norm_w, 1, 4, 2, kPcLag, a, grid, lds) &&
         a->slots * 16 >= a->units_max)

@@ -176,3 +176,31 @@ def test_long_rows_batch2_automatic(qd, fmt, N):
     assert_bound(f"automatic {fmt} N={N}", y, y64, S)
     again = qd.qgemv(fmt, Wd, xd).cpu().numpy()
     assert np.array_equal(y.view(np.uint32), again.view(np.uint32))
+
+
+# The fused gate/up at batch 2 over rows of K >= 4096 runs on the register
+# kernel (one lane group per row, two K-slices across workgroups), the
+# automatic choice there; K = 2560 stays on the streaming kernel.
+@pytest.mark.parametrize("fmt,N,K", [("q4_k", 1500, 5376), ("q4_k", 700, 4096), ("q6_k", 300, 4096),
+                                     ("q8_0", 333, 4096), ("q4_k", 1024, 2560)])
+def test_gate_up_batch2_automatic(qd, fmt, N, K):
+    batch, act = 2, "gelu_tanh"
+    say(f"automatic gate/up {fmt} N={N} K={K} batch={batch}")
+    Wg = synth.quant_weights(fmt, N, K, SEED, tensor_id=88)
+    Wu = synth.quant_weights(fmt, N, K, SEED, tensor_id=89)
+    x = synth.normal((batch, K), SEED, tensor_id=90)
+    nw = synth.normal((K,), SEED, tensor_id=91, mean=1.0, std=0.1)
+    g = torch.empty((batch, N), device="cuda")
+    u = torch.empty((batch, N), device="cuda")
+    h = qd.qffn_gate_up_act(fmt, dev(Wg), dev(Wu), dev(x), dev(nw), 1e-6, act,
+                            g_out=g, u_out=u).cpu().numpy()
+    g, u = g.cpu().numpy(), u.cpu().numpy()
+    xn = oracle.rmsnorm(x, nw, 1e-6).astype(np.float32)
+    g64, Sg = oracle.gemv(fmt, Wg, xn, N, K)
+    u64, Su = oracle.gemv(fmt, Wu, xn, N, K)
+    assert_bound("gate", g, g64, Sg)
+    assert_bound("up", u, u64, Su)
+    href = oracle.act_vec(oracle.ACT_GELU_TANH, g64) * u64
+    tol = h_tolerance(g64, u64, Sg, Su, oracle.ACT_GELU_TANH)
+    err = np.abs(h - href)
+    assert (err <= tol).all(), f"h: worst {np.max(err / tol):.3f} of tolerance"
